@@ -1,0 +1,283 @@
+/*
+ * bitlinear_oracle.c -- plain, slow CPU oracle of the BitNet b1.58 BitLinear path.
+ *
+ * TEST INFRASTRUCTURE. This is the independent reference that the HIP path is
+ * checked against. Only the tests, the smoke check and the benchmark's CPU
+ * baseline leg may load it. The product library neither links nor calls it,
+ * and the two share no code, header, table or constant.
+ *
+ * Pages this follows (title, then section):
+ *  [BN] "BitNet Model - Complete Inference Pipeline" (Hesper API, Models.BitNet):
+ *       "Model Configurations", "Memory Footprint (BitNet-3B with TQ2_0)",
+ *       "Text Generation / Greedy Decoding", "GPU Argmax" (argmaxKernel).
+ *  [TB] "Transformer Block" (Hesper API, Layers.TransformerBlock):
+ *       "Feed-Forward Network (FFN)", "Memory Layout", "Layer Structure"
+ *       (ffnNorm, ffnGate, ffnUp, ffnSubNorm, ffnDown), "Forward Pass" steps 4-8.
+ *  [CA] "Add Support for BitNet Architecture Inference" (candle PR 2664): the
+ *       reply that lists the changes -- an RMSNorm in front of every BitLinear,
+ *       and the activation_quant / weight_quant pair.
+ *  The pages name the quantizers but print no formula. They follow the BitNet
+ *  b1.58 method that [BN] and [TB] reference (arXiv 2402.17764): one absmean
+ *  scale per weight tensor with weights rounded to {-1, 0, +1}, and per-token
+ *  absmax scaling of activations to 8-bit integers, integer accumulation, one
+ *  float rescale at the end.
+ *
+ * Readings where the pages are silent (each is listed with its reason in the
+ * design notes of the repository):
+ *  - Rounding is round-half-to-even (nearbyint in the default FP mode).
+ *  - Activation codes are clamped to [-128, 127]; the absmax element lands on
+ *    +-127, so -128 never occurs.
+ *  - The floor on absmax and on mean|W| is 1e-5.
+ *  - TQ2_0 byte layout: code c = t + 1 in {0, 1, 2}, four 2-bit fields per byte,
+ *    least significant field first; byte i of a row holds k = 4i .. 4i+3.
+ *    Code 3 is invalid. Weights are stored W[N_out][K_in], K contiguous.
+ *  - RMSNorm: y = fl32(fl32(x * r) * g), r = fl32(1 / sqrt(ss / K + eps)) taken
+ *    in fp64; ss is the fp64 sum of squares in one fixed order: 256 strided
+ *    partials (partial l sums k = l, l+256, ... ascending), then a pairwise
+ *    xor-butterfly over the partials with offsets 128, 64, ..., 1.
+ *  - Dequant: inv = fl32(1 / fl32(s_a * s_w)) once per (token, tensor), then
+ *    y = fl32((float)acc * inv).
+ *  - FFN: h = fl32(fl32(relu(gate) * relu(gate)) * up), then the sub-norm and
+ *    activation quant of h, then the down projection. No residual inside.
+ *  - Argmax ties go to the lowest index.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fopenmp (OpenMP only splits independent
+ * rows/tokens; every result is the same for any thread count).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_EPS_FLOOR 1e-5
+#define ORACLE_PARTIALS 256
+
+int ref_abi_version(void) { return 1; }
+
+/* ------------------------------------------------------------------------ */
+/* weight_quant ([CA] weight_quant; absmean ternary rounding of the b1.58
+ * method): s_w = 1 / mean|W| over the whole tensor, t = clamp(rne(W * s_w)).
+ * mean|W| is an fp64 sum in row-major order divided by N*K; s_w is the fp64
+ * reciprocal rounded once to fp32; each W*s_w is an fp32 product.           */
+int ref_weight_quant(const float *w, int64_t n, int64_t k, int8_t *t, float *s_w)
+{
+    if (n <= 0 || k <= 0) return -2;
+    double sum = 0.0;
+    for (int64_t i = 0; i < n * k; i++) {
+        if (!isfinite(w[i])) return -4;
+        sum += fabs((double)w[i]);
+    }
+    double mean = sum / (double)(n * k);
+    if (mean < ORACLE_EPS_FLOOR) mean = ORACLE_EPS_FLOOR;
+    float scale = (float)(1.0 / mean);
+    *s_w = scale;
+    for (int64_t i = 0; i < n * k; i++) {
+        float v = w[i] * scale;
+        float r = nearbyintf(v);
+        if (r > 1.0f) r = 1.0f;
+        if (r < -1.0f) r = -1.0f;
+        t[i] = (int8_t)r;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* TQ2_0 codec ([BN] "Memory Footprint": 0.25 byte per weight; layout is the
+ * reading stated in the header). pack: P[n][i] = sum_j (t[n][4i+j] + 1) << 2j. */
+int ref_pack(const int8_t *t, int64_t n, int64_t k, uint8_t *packed)
+{
+    if (n <= 0 || k <= 0) return -2;
+    if (k % 4 != 0) return -2;
+    for (int64_t i = 0; i < n * k; i++)
+        if (t[i] < -1 || t[i] > 1) return -4;
+    int64_t kb = k / 4;
+    for (int64_t r = 0; r < n; r++) {
+        for (int64_t i = 0; i < kb; i++) {
+            unsigned byte = 0;
+            for (int j = 0; j < 4; j++) {
+                unsigned code = (unsigned)(t[r * k + 4 * i + j] + 1);
+                byte |= code << (2 * j);
+            }
+            packed[r * kb + i] = (uint8_t)byte;
+        }
+    }
+    return 0;
+}
+
+/* unpack: inverse of ref_pack; a field holding code 3 is rejected (-4). */
+int ref_unpack(const uint8_t *packed, int64_t n, int64_t k, int8_t *t)
+{
+    if (n <= 0 || k <= 0 || k % 4 != 0) return -2;
+    int64_t kb = k / 4;
+    for (int64_t r = 0; r < n; r++) {
+        for (int64_t i = 0; i < kb; i++) {
+            unsigned byte = packed[r * kb + i];
+            for (int j = 0; j < 4; j++) {
+                unsigned code = (byte >> (2 * j)) & 3u;
+                if (code == 3u) return -4;
+                t[r * k + 4 * i + j] = (int8_t)((int)code - 1);
+            }
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* RMSNorm sum of squares in the fixed order stated in the header. Each x^2 is
+ * exact in fp64 (a 24-bit significand squared fits in 53 bits).              */
+double ref_sumsq(const float *x, int64_t k)
+{
+    double p[ORACLE_PARTIALS], c[ORACLE_PARTIALS];
+    for (int l = 0; l < ORACLE_PARTIALS; l++) p[l] = 0.0;
+    for (int64_t i = 0; i < k; i++) {
+        double v = (double)x[i];
+        p[i % ORACLE_PARTIALS] += v * v;
+    }
+    for (int off = ORACLE_PARTIALS / 2; off >= 1; off /= 2) {
+        memcpy(c, p, sizeof p);
+        for (int l = 0; l < ORACLE_PARTIALS; l++) p[l] = c[l] + c[l ^ off];
+    }
+    return p[0];
+}
+
+/* RMSNorm ([TB] "Layer Structure": attnNorm/ffnNorm/ffnSubNorm; [CA]: a norm in
+ * front of every BitLinear). y[m][k] = fl32(fl32(x * r) * g[k]). g == NULL is
+ * not allowed here (the caller skips the norm instead).                       */
+int ref_rmsnorm(const float *x, const float *g, float eps, int64_t m, int64_t k, float *y)
+{
+    if (m <= 0 || k <= 0 || !g) return -2;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t row = 0; row < m; row++) {
+        const float *xr = x + row * k;
+        for (int64_t i = 0; i < k; i++)
+            if (!isfinite(xr[i])) bad = 1;
+        double ss = ref_sumsq(xr, k);
+        double r64 = 1.0 / sqrt(ss / (double)k + (double)eps);
+        float r = (float)r64;
+        for (int64_t i = 0; i < k; i++) {
+            float a = xr[i] * r;
+            y[row * k + i] = a * g[i];
+        }
+    }
+    return bad ? -4 : 0;
+}
+
+/* activation_quant ([CA]; per-token absmax of the b1.58 method):
+ * s_a = fl32(127 / max(absmax, 1e-5)), q = clamp(rne(fl32(y * s_a)), -128, 127),
+ * qsum = sum of q in int32.                                                   */
+int ref_activation_quant(const float *y, int64_t m, int64_t k, int8_t *q, float *s_a, int32_t *qsum)
+{
+    if (m <= 0 || k <= 0) return -2;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t row = 0; row < m; row++) {
+        const float *yr = y + row * k;
+        float amax = 0.0f;
+        for (int64_t i = 0; i < k; i++) {
+            if (!isfinite(yr[i])) bad = 1;
+            float a = fabsf(yr[i]);
+            if (a > amax) amax = a;
+        }
+        float floor_ = (float)ORACLE_EPS_FLOOR;
+        float scale = 127.0f / (amax > floor_ ? amax : floor_);
+        s_a[row] = scale;
+        int32_t sum = 0;
+        for (int64_t i = 0; i < k; i++) {
+            float v = yr[i] * scale;
+            float r = nearbyintf(v);
+            if (r > 127.0f) r = 127.0f;
+            if (r < -128.0f) r = -128.0f;
+            int8_t qi = (int8_t)r;
+            q[row * k + i] = qi;
+            sum += qi;
+        }
+        if (qsum) qsum[row] = sum;
+    }
+    return bad ? -4 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Ternary x int8 matmul: acc[m][n] = sum_k t[n][k] * q[m][k], exact in int32
+ * (|acc| <= 127 K < 2^31 for every K this path sees).                        */
+int ref_matmul_i32(const int8_t *t, const int8_t *q, int64_t m, int64_t n, int64_t k, int32_t *acc)
+{
+    if (m <= 0 || n <= 0 || k <= 0) return -2;
+#pragma omp parallel for schedule(static)
+    for (int64_t col = 0; col < n; col++) {
+        const int8_t *tr = t + col * k;
+        for (int64_t row = 0; row < m; row++) {
+            const int8_t *qr = q + row * k;
+            int32_t s = 0;
+            for (int64_t i = 0; i < k; i++) s += (int32_t)tr[i] * (int32_t)qr[i];
+            acc[row * n + col] = s;
+        }
+    }
+    return 0;
+}
+
+/* Dequant: one float rescale by 1/(s_a * s_w) per (token, tensor).           */
+int ref_dequant(const int32_t *acc, const float *s_a, float s_w, int64_t m, int64_t n, float *y)
+{
+    if (m <= 0 || n <= 0) return -2;
+    for (int64_t row = 0; row < m; row++) {
+        float prod = s_a[row] * s_w;
+        float inv = 1.0f / prod;
+        for (int64_t col = 0; col < n; col++) y[row * n + col] = (float)acc[row * n + col] * inv;
+    }
+    return 0;
+}
+
+/* One BitLinear on quantized activations: unpack, exact matmul, dequant.
+ * acc may be NULL.                                                            */
+int ref_bitlinear(const uint8_t *packed, float s_w, int64_t n, int64_t k, const int8_t *q,
+                  const float *s_a, int64_t m, float *y, int32_t *acc)
+{
+    if (m <= 0 || n <= 0 || k <= 0 || k % 4 != 0) return -2;
+    int8_t *t = (int8_t *)malloc((size_t)(n * k));
+    int32_t *a = acc ? acc : (int32_t *)malloc((size_t)(m * n) * sizeof(int32_t));
+    if (!t || !a) {
+        free(t);
+        if (!acc) free(a);
+        return -7;
+    }
+    int rc = ref_unpack(packed, n, k, t);
+    if (rc == 0) rc = ref_matmul_i32(t, q, m, n, k, a);
+    if (rc == 0) rc = ref_dequant(a, s_a, s_w, m, n, y);
+    free(t);
+    if (!acc) free(a);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* FFN gating ([TB] "Feed-Forward Network (FFN)": the gate goes through a
+ * squared ReLU, then multiplies the up projection elementwise).             */
+void ref_relu2_mul(const float *gate, const float *up, int64_t count, float *h)
+{
+    for (int64_t i = 0; i < count; i++) {
+        float g = gate[i] > 0.0f ? gate[i] : 0.0f;
+        float g2 = g * g;
+        h[i] = g2 * up[i];
+    }
+}
+
+/* Residual add ([TB] "Forward Pass" steps 3 and 9): x = fl32(x + d).        */
+void ref_residual_add(float *x, const float *d, int64_t count)
+{
+    for (int64_t i = 0; i < count; i++) x[i] = x[i] + d[i];
+}
+
+/* Greedy token choice ([BN] "Greedy Decoding", "GPU Argmax"): per row, the
+ * lowest index holding the maximum accumulator.                              */
+int ref_argmax_rows(const int32_t *acc, int64_t m, int64_t n, int32_t *idx)
+{
+    if (m <= 0 || n <= 0) return -2;
+    for (int64_t row = 0; row < m; row++) {
+        const int32_t *a = acc + row * n;
+        int64_t best = 0;
+        for (int64_t col = 1; col < n; col++)
+            if (a[col] > a[best]) best = col;
+        idx[row] = (int32_t)best;
+    }
+    return 0;
+}

@@ -1,0 +1,635 @@
+"""Pins of the CPU oracle: checks against facts that do not come from the oracle.
+
+Each pin is a function ``pin_x(o, lib)`` of an oracle module ``o`` and its C
+library ``lib``; it raises AssertionError when the oracle is wrong. The
+mutation test reuses them against copies of the oracle with planted mistakes.
+
+Sources of truth used here (never the oracle itself):
+  * hand-worked fixtures under tests/golden/ (each cites its page and section);
+  * the pages' packed-size arithmetic ("Memory Footprint" on the Hesper
+    BitNet page, "Memory Layout" on the Hesper TransformerBlock page);
+  * closed forms: identity / sign-flip / permutation weights, one-hot inputs,
+    power-of-two scalings, constant vectors;
+  * exact rational arithmetic (fractions, decimal) within a stated error bound;
+  * numpy's int64 matmul and argmax on tiny cases (library routines).
+"""
+import decimal
+import os
+from fractions import Fraction
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _ulp32(v):
+    v = abs(np.float32(v))
+    return float(np.spacing(v)) if v != 0 else float(np.finfo(np.float32).tiny)
+
+
+def _read_fixture(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as fh:
+        for line in fh:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line)
+    return rows
+
+
+# --- TQ2_0 codec ----------------------------------------------------------------
+
+def pin_codec_golden(o, lib):
+    """Hand-derived bytes for the stated layout (tests/golden/tq2_codec.txt)."""
+    for row in _read_fixture("tq2_codec.txt"):
+        lhs, rhs = row.split("->")
+        t = np.array([int(v) for v in lhs.split()], np.int8).reshape(1, 4)
+        byte = int(rhs.strip(), 16)
+        p = o.pack(t, lib)
+        assert p.shape == (1, 1) and int(p[0, 0]) == byte, (t, p, byte)
+        assert (o.unpack(p, 4, lib) == t).all()
+
+
+def pin_codec_exhaustive(o, lib):
+    """All 81 ternary 4-tuples map to 81 distinct bytes with no code-3 field, and
+    back; the 175 bytes holding a code-3 field are rejected."""
+    import itertools
+    tuples = np.array(list(itertools.product((-1, 0, 1), repeat=4)), np.int8)
+    p = o.pack(tuples, lib)  # 81 rows of K=4 -> one byte each
+    vals = [int(b) for b in p[:, 0]]
+    assert len(set(vals)) == 81
+    for b in vals:
+        assert all(((b >> (2 * j)) & 3) != 3 for j in range(4))
+    assert (o.unpack(p, 4, lib) == tuples).all()
+    good = set(vals)
+    for b in range(256):
+        if b in good:
+            continue
+        try:
+            o.unpack(np.array([[b]], np.uint8), 4, lib)
+        except o.OracleError:
+            continue
+        raise AssertionError(f"byte {b:#x} with a code-3 field was accepted")
+
+
+def pin_codec_value_range(o, lib):
+    """Values outside {-1, 0, 1} are rejected; K not a multiple of 4 is rejected."""
+    for bad in (2, -2, 127, -128):
+        t = np.zeros((1, 4), np.int8)
+        t[0, 2] = bad
+        try:
+            o.pack(t, lib)
+        except o.OracleError:
+            continue
+        raise AssertionError(f"value {bad} accepted")
+    try:
+        o.pack(np.zeros((1, 6), np.int8), lib)
+    except o.OracleError:
+        pass
+    else:
+        raise AssertionError("k % 4 != 0 accepted")
+
+
+def pin_codec_row_layout(o, lib):
+    """Byte i of row n covers weights 4i..4i+3 of that row (a single +1 at (n, k)
+    lands in byte k//4 of row n, field k%4, and nowhere else)."""
+    n, k = 5, 24
+    for (r, c) in ((0, 0), (2, 7), (4, 23), (3, 12)):
+        t = np.full((n, k), -1, np.int8)
+        t[r, c] = 1
+        p = o.pack(t, lib)
+        assert p.shape == (n, k // 4)
+        expect = np.zeros((n, k // 4), np.uint8)
+        expect[r, c // 4] = 2 << (2 * (c % 4))
+        assert (p == expect).all(), (r, c)
+
+
+def pin_packed_sizes(o, lib):
+    """The pages' packed-size arithmetic: count * n * k * 0.25 bytes, matching the
+    printed MB figure to the printed precision. Every output byte is written (a
+    valid code byte is never 0xff) and nothing past the end."""
+    for row in _read_fixture("packed_sizes.txt"):
+        n, k, count, mb, _src = row.split()
+        n, k, count, mb = int(n), int(k), int(count), float(mb)
+        exact = count * n * k // 4
+        digits = len(repr(mb).split(".")[1]) if repr(mb).split(".")[1] != "0" else 0
+        assert abs(exact / 1e6 - mb) < 10.0 ** (-digits), (row, exact)
+        t = np.zeros((n, k), np.int8)
+        buf = np.full(n * k // 4 + 64, 0xFF, np.uint8)
+        view = buf[: n * k // 4].reshape(n, k // 4)
+        rc = lib.ref_pack(t.ctypes.data_as(o._i8p), n, k, view.ctypes.data_as(o._u8p))
+        assert rc == 0
+        assert (buf[n * k // 4:] == 0xFF).all(), "wrote past the end"
+        assert (view == 0x55).all(), "zero weights must pack to 0x55 everywhere"
+
+
+def pin_layer_bytes(o, lib):
+    """One BitNet-3B layer is 26,214,400 packed bytes and 32 layers 838,860,800
+    ("Memory Layout": ~26 MB per layer, ~832 MB for 32 layers; "Memory
+    Footprint": 32 x 26 MB). Pack one of each shape and sum."""
+    d, f = 2560, 10240
+    shapes = [(d, d)] * 4 + [(f, d), (f, d), (d, f)]
+    total = 0
+    for n, k in shapes:
+        total += o.pack(np.zeros((n, k), np.int8), lib).nbytes
+    assert total == 26_214_400
+    assert round(total / 1e6) == 26
+    assert 32 * total == 838_860_800
+    assert abs(32 * round(total / 1e6) - 832) == 0
+
+
+# --- activation quant -----------------------------------------------------------
+
+def pin_quant_golden(o, lib):
+    """Hand-worked absmax/round-half-even cases (tests/golden/quant_cases.txt)."""
+    for row in _read_fixture("quant_cases.txt"):
+        ys, sa, qs, qsum = [s.strip() for s in row.split("|")]
+        y = np.array([float(v) for v in ys.split()], np.float32).reshape(1, -1)
+        q, s, qsm = o.activation_quant(y, lib)
+        assert float(s[0]) == float(sa), (row, s)
+        assert q[0].tolist() == [int(v) for v in qs.split()], (row, q)
+        assert int(qsm[0]) == int(qsum), (row, qsm)
+
+
+def pin_quant_bounds(o, lib):
+    """The absmax element maps to +-127, |q| <= 127 and q never hits -128;
+    qsum is the integer sum of q (checked with numpy int64)."""
+    g = _rng(11)
+    for k in (1, 4, 64, 257, 2560):
+        x = g.standard_normal((7, k)).astype(np.float32) * np.float32(g.uniform(1e-3, 1e3))
+        q, s, qs = o.activation_quant(x, lib)
+        for r in range(7):
+            j = int(np.argmax(np.abs(x[r])))
+            assert abs(int(q[r, j])) == 127 and np.sign(q[r, j]) == np.sign(x[r, j])
+            assert np.abs(q[r].astype(np.int64)).max() == 127
+        assert q.min() > -128
+        assert (qs.astype(np.int64) == q.astype(np.int64).sum(1)).all()
+
+
+def pin_quant_pow2_scaling(o, lib):
+    """Multiplying a token by 2^e leaves q unchanged and divides s_a by 2^e (all
+    products are exact in binary floating point)."""
+    g = _rng(12)
+    x = g.standard_normal((5, 300)).astype(np.float32)
+    q0, s0, _ = o.activation_quant(x, lib)
+    for e in (-7, -1, 3, 10):
+        q1, s1, _ = o.activation_quant(x * np.float32(2.0 ** e), lib)
+        assert (q1 == q0).all()
+        assert (s1 == s0 * np.float32(2.0 ** -e)).all()
+
+
+def pin_quant_scale_value(o, lib):
+    """s_a is the correctly rounded fp32 of 127/absmax (checked with Fraction)."""
+    g = _rng(13)
+    x = g.standard_normal((20, 100)).astype(np.float32)
+    _, s, _ = o.activation_quant(x, lib)
+    for r in range(20):
+        amax = Fraction(float(np.abs(x[r]).max()))
+        exact = Fraction(127) / amax
+        assert abs(Fraction(float(s[r])) - exact) <= Fraction(_ulp32(s[r])) / 2
+
+
+def pin_quant_error_bound(o, lib):
+    """q / s_a reconstructs y within half a quantization step (plus one fp32
+    rounding of y*s_a): the defining property of round-to-nearest codes."""
+    g = _rng(14)
+    x = g.standard_normal((6, 512)).astype(np.float32)
+    q, s, _ = o.activation_quant(x, lib)
+    for r in range(6):
+        err = np.abs(q[r].astype(np.float64) / float(s[r]) - x[r].astype(np.float64))
+        bound = (0.5 + 127 * 2.0 ** -23) / float(s[r])
+        assert err.max() <= bound
+
+
+# --- RMSNorm ----------------------------------------------------------------------
+
+def _exact_r(x, eps):
+    """1/sqrt(mean(x^2) + eps) with 60 significant digits, from an exact sum."""
+    ss = sum(Fraction(float(v)) ** 2 for v in x)
+    mean = ss / len(x) + Fraction(float(np.float32(eps)))
+    ctx = decimal.Context(prec=60)
+    dm = ctx.divide(decimal.Decimal(mean.numerator), decimal.Decimal(mean.denominator))
+    return ctx.divide(decimal.Decimal(1), ctx.sqrt(dm))
+
+
+def pin_sumsq_exact_bound(o, lib):
+    """The fixed-order fp64 sum of squares is the exact sum of all K squares
+    within the fp64 summation bound K * 2^-53 * sum."""
+    g = _rng(21)
+    for k in (1, 3, 64, 255, 256, 257, 1000, 2560):
+        x = (g.standard_normal(k) * g.uniform(0.01, 100)).astype(np.float32)
+        exact = sum(Fraction(float(v)) ** 2 for v in x)
+        got = Fraction(o.sumsq(x, lib))
+        assert abs(got - exact) <= exact * Fraction(k + 8, 2 ** 53), k
+
+
+def pin_sumsq_order(o, lib):
+    """The sum of squares follows the stated order exactly: 256 strided partials,
+    then a pairwise xor-butterfly with offsets 128, 64, ..., 1. Two hand-worked
+    cases with squares 2^52 and 1 (fp64 spacing is 2 above 2^53, so where a 1
+    meets 2^53 alone it is lost to round-half-even):
+      A: x[0] = x[256] = 2^26, x[64] = x[128] = 1. Partial 0 = 2^52 + 2^52 = 2^53;
+         the butterfly then adds each 1 to 2^53 on its own -> 2^53.
+         (64 or 128 partials, or a left-to-right sum, give 2^53 + 2.)
+      B: x[0] = x[128] = 2^26, x[256] = x[384] = 1. Partials 0 and 128 are each
+         2^52 + 1 (exact); the offset-128 step adds them -> 2^53 + 2.
+         (128 partials or a left-to-right sum give 2^53.)"""
+    big = np.float32(2.0 ** 26)
+    xa = np.zeros(512, np.float32)
+    xa[[0, 256]] = big
+    xa[[64, 128]] = 1.0
+    assert o.sumsq(xa, lib) == 2.0 ** 53
+    xb = np.zeros(512, np.float32)
+    xb[[0, 128]] = big
+    xb[[256, 384]] = 1.0
+    assert o.sumsq(xb, lib) == 2.0 ** 53 + 2.0
+
+
+def pin_rmsnorm_closed_form(o, lib):
+    """y = x * r * g with r = 1/sqrt(mean(x^2) + eps): each y is within 1.5 fp32
+    ulps of the exact product (one rounding of r, two of the products)."""
+    g = _rng(22)
+    for k, eps in ((4, 0.0), (64, 1e-5), (300, 1e-5), (2560, 1e-6), (16, 1.0)):
+        x = g.standard_normal((1, k)).astype(np.float32)
+        gain = g.uniform(0.5, 1.5, k).astype(np.float32)
+        y = o.rmsnorm(x, gain, eps, lib)[0]
+        r = _exact_r(x[0], eps)
+        for i in range(0, k, max(1, k // 37)):
+            exact = decimal.Decimal(float(x[0, i])) * r * decimal.Decimal(float(gain[i]))
+            err = abs(decimal.Decimal(float(y[i])) - exact)
+            assert err <= decimal.Decimal(2.0 * _ulp32(y[i])), (k, eps, i)
+
+
+def pin_rmsnorm_constant(o, lib):
+    """A constant vector c with unit gains and eps = 0 normalises to sign(c),
+    so activation_quant gives 127 * sign(c) everywhere."""
+    for c in (3.0, -0.125, 1e-3, 77.5):
+        for k in (4, 100, 2560):
+            x = np.full((1, k), c, np.float32)
+            q, s, qs = o.quant_act(x, np.ones(k, np.float32), 0.0, lib)
+            assert (q == 127 * int(np.sign(c))).all()
+            assert int(qs[0]) == 127 * int(np.sign(c)) * k
+
+
+def pin_rmsnorm_pow2(o, lib):
+    """With eps = 0, scaling x by 2^e leaves the normalised y unchanged exactly."""
+    g = _rng(23)
+    x = g.standard_normal((3, 640)).astype(np.float32)
+    gain = g.uniform(0.5, 1.5, 640).astype(np.float32)
+    y0 = o.rmsnorm(x, gain, 0.0, lib)
+    for e in (-5, 4, 20):
+        y1 = o.rmsnorm(x * np.float32(2.0 ** e), gain, 0.0, lib)
+        assert (y1 == y0).all()
+
+
+def pin_rmsnorm_eps(o, lib):
+    """eps enters under the root: with x = 0 except one element a, K = 1 and
+    eps = 3 a^2, r = 1/(2|a|) exactly, so y = g/2 * sign(a)."""
+    for a in (0.5, -2.0, 8.0):
+        x = np.array([[a]], np.float32)
+        y = o.rmsnorm(x, np.array([3.0], np.float32), 3.0 * a * a, lib)
+        assert float(y[0, 0]) == 1.5 * np.sign(a), y
+
+
+# --- weight quant -----------------------------------------------------------------
+
+def pin_weight_quant_closed_form(o, lib):
+    """absmean scale: W = [a, -a, 3a, -3a, 0, 0, 0, 0] has mean|W| = a, so
+    s_w = 1/a and t = [1, -1, 1, -1, 0, 0, 0, 0] (3 clamps to 1). An absmax
+    scale would give s_w = 1/(3a) and zeros in the first two places."""
+    for a in (0.125, 2.0, 1.0 / 64):
+        w = np.array([[a, -a, 3 * a, -3 * a, 0, 0, 0, 0]], np.float32)
+        t, s = o.weight_quant(w, lib)
+        assert float(s) == 1.0 / a
+        assert t[0].tolist() == [1, -1, 1, -1, 0, 0, 0, 0]
+
+
+def pin_weight_quant_ties(o, lib):
+    """W = [a, -a, 3a, -3a] has mean 2a, s_w = 1/(2a): W*s_w = [.5, -.5, 1.5, -1.5]
+    rounds half to even to [0, 0, 2, -2] and clamps to [0, 0, 1, -1]."""
+    a = 0.125
+    w = np.array([[a, -a, 3 * a, -3 * a]], np.float32)
+    t, s = o.weight_quant(w, lib)
+    assert float(s) == 4.0
+    assert t[0].tolist() == [0, 0, 1, -1]
+
+
+def pin_weight_quant_recovers_ternary(o, lib):
+    """W = c * t for a ternary t with half its entries nonzero: mean|W| = c/2,
+    s_w = 2/c and t is recovered exactly (W*s_w = 2t clamps to t)."""
+    g = _rng(31)
+    t0 = np.zeros((16, 64), np.int8)
+    idx = g.permutation(16 * 64)[: 16 * 32]
+    t0.flat[idx] = g.choice(np.array([-1, 1], np.int8), size=idx.size)
+    for c in (0.25, 4.0):
+        t, s = o.weight_quant(t0.astype(np.float32) * np.float32(c), lib)
+        assert float(s) == 2.0 / c
+        assert (t == t0).all()
+
+
+def pin_weight_quant_mean(o, lib):
+    """s_w is 1/mean|W| (numpy's float64 mean, within fp32 rounding)."""
+    g = _rng(32)
+    w = (g.standard_normal((33, 96)) * 0.02).astype(np.float32)
+    _, s = o.weight_quant(w, lib)
+    ref = 1.0 / np.mean(np.abs(w.astype(np.float64)))
+    assert abs(float(s) - ref) <= 1.0 * _ulp32(s)
+
+
+# --- matmul / dequant ----------------------------------------------------------------
+
+def pin_matmul_bruteforce(o, lib):
+    """Exact int32 products against numpy's int64 matmul on small random shapes
+    (non-square, so a transposed operand or output fails)."""
+    g = _rng(41)
+    for _ in range(40):
+        m, n, k = int(g.integers(1, 17)), int(g.integers(1, 17)), 4 * int(g.integers(1, 5))
+        t = g.integers(-1, 2, (n, k)).astype(np.int8)
+        q = g.integers(-127, 128, (m, k)).astype(np.int8)
+        acc = o.matmul_i32(t, q, lib)
+        assert acc.shape == (m, n)
+        assert (acc.astype(np.int64) == q.astype(np.int64) @ t.astype(np.int64).T).all()
+
+
+def pin_matmul_k4_exhaustive_rows(o, lib):
+    """Every ternary row of K=4 against sampled int8 vectors, through the packed
+    path (pack -> bitlinear), against numpy."""
+    import itertools
+    t = np.array(list(itertools.product((-1, 0, 1), repeat=4)), np.int8)
+    g = _rng(42)
+    q = g.integers(-127, 128, (64, 4)).astype(np.int8)
+    p = o.pack(t, lib)
+    s_a = np.ones(64, np.float32)
+    _, acc = o.bitlinear(p, np.float32(1.0), 4, q, s_a, lib)
+    assert (acc.astype(np.int64) == q.astype(np.int64) @ t.astype(np.int64).T).all()
+
+
+def pin_matmul_invariants(o, lib):
+    """Identity gives q, -I gives -q, a permutation permutes q, zero rows give 0,
+    all-(+1) rows give sum(q) and all-(-1) rows give -sum(q)."""
+    g = _rng(43)
+    k = 64
+    q = g.integers(-127, 128, (3, k)).astype(np.int8)
+    eye = np.eye(k, dtype=np.int8)
+    assert (o.matmul_i32(eye, q, lib) == q).all()
+    assert (o.matmul_i32(-eye, q, lib) == -q.astype(np.int32)).all()
+    perm = g.permutation(k)
+    assert (o.matmul_i32(eye[perm], q, lib) == q[:, perm]).all()
+    special = np.stack([np.zeros(k, np.int8), np.ones(k, np.int8), -np.ones(k, np.int8)])
+    acc = o.matmul_i32(special, q, lib)
+    s = q.astype(np.int64).sum(1)
+    assert (acc[:, 0] == 0).all() and (acc[:, 1] == s).all() and (acc[:, 2] == -s).all()
+
+
+def pin_int32_bound(o, lib):
+    """x = +-c everywhere gives q = +-127; with t = sign(q), acc = 127 K exactly
+    (1,300,480 at K = 10240) and the fp32 conversion is exact."""
+    k = 10240
+    g = _rng(44)
+    sgn = g.choice(np.array([-1, 1], np.int8), size=k)
+    x = (sgn.astype(np.float32) * np.float32(3.5)).reshape(1, k)
+    q, s, _ = o.activation_quant(x, lib)
+    assert (q[0] == 127 * sgn).all()
+    p = o.pack(sgn.reshape(1, k), lib)
+    y, acc = o.bitlinear(p, np.float32(1.0), k, q, s, lib)
+    assert int(acc[0, 0]) == 1_300_480
+    assert float(y[0, 0]) == float(np.float32(1_300_480) * (np.float32(1.0) / s[0]))
+
+
+def pin_dequant_pow2(o, lib):
+    """Power-of-two scales make the dequant exact: s_a = 2^a, s_w = 2^b gives
+    y = acc * 2^-(a+b)."""
+    g = _rng(45)
+    acc = g.integers(-2 ** 20, 2 ** 20, (4, 9)).astype(np.int32)
+    for a, b in ((3, 5), (-2, 7), (0, 0)):
+        s_a = np.full(4, 2.0 ** a, np.float32)
+        y = o.dequant(acc, s_a, np.float32(2.0 ** b), lib)
+        assert (y.astype(np.float64) == acc.astype(np.float64) * 2.0 ** -(a + b)).all()
+
+
+def pin_dequant_per_row(o, lib):
+    """Each row uses its own s_a: rows with s_a = 1, 2, 4 differ by exactly 2x."""
+    acc = np.tile(np.arange(-5, 6, dtype=np.int32), (3, 1))
+    y = o.dequant(acc, np.array([1, 2, 4], np.float32), np.float32(1.0), lib)
+    assert (y[0] == 2 * y[1]).all() and (y[1] == 2 * y[2]).all()
+
+
+def pin_bitlinear_onehot(o, lib):
+    """x = v e_j: q = 127 sign(v) e_j, s_a = 127/|v|, so y[n] = t[n][j] v / s_w
+    within a few fp32 ulps (the float matmul the quantization approximates)."""
+    g = _rng(46)
+    n, k = 24, 64
+    t = g.integers(-1, 2, (n, k)).astype(np.int8)
+    p = o.pack(t, lib)
+    s_w = np.float32(37.0)
+    for j, v in ((0, 2.5), (17, -0.3), (63, 1000.0)):
+        x = np.zeros((1, k), np.float32)
+        x[0, j] = v
+        q, s, _ = o.activation_quant(x, lib)
+        y, _ = o.bitlinear(p, s_w, k, q, s, lib)
+        exact = t[:, j].astype(np.float64) * v / float(s_w)
+        assert np.all(np.abs(y[0] - exact) <= 4 * np.abs(exact) * 2.0 ** -24), (j, y[0], exact)
+
+
+def pin_bitlinear_error_bound(o, lib):
+    """The whole BitLinear approximates the float product (t/s_w) x: the error
+    is at most sum_k |t[n][k]| * (0.5 + eps) / (s_a s_w), the activation
+    quantization step, plus fp32 rounding of the dequant."""
+    g = _rng(47)
+    n, k, m = 40, 256, 3
+    t = g.integers(-1, 2, (n, k)).astype(np.int8)
+    p = o.pack(t, lib)
+    s_w = np.float32(29.5)
+    x = g.standard_normal((m, k)).astype(np.float32)
+    q, s, _ = o.activation_quant(x, lib)
+    y, _ = o.bitlinear(p, s_w, k, q, s, lib)
+    exact = x.astype(np.float64) @ t.astype(np.float64).T / float(s_w)
+    for r in range(m):
+        bound = np.abs(t).sum(1) * (0.5 + 1e-4) / (float(s[r]) * float(s_w)) + 4 * np.abs(y[r]) * 2.0 ** -24
+        assert np.all(np.abs(y[r] - exact[r]) <= bound + 1e-12), r
+
+
+# --- argmax ------------------------------------------------------------------------
+
+def pin_argmax(o, lib):
+    """Lowest index wins ties; agrees with numpy's argmax (first occurrence)."""
+    acc = np.array([[1, 5, 5, 2], [7, 7, 7, 7], [-3, -1, -2, -1], [0, 0, 0, 9]], np.int32)
+    assert o.argmax_rows(acc, lib).tolist() == [1, 0, 1, 3]
+    g = _rng(51)
+    a = g.integers(-5, 5, (50, 30)).astype(np.int32)
+    assert (o.argmax_rows(a, lib) == np.argmax(a, axis=1)).all()
+
+
+# --- FFN ------------------------------------------------------------------------------
+
+def pin_relu2_mul(o, lib):
+    """h = relu(gate)^2 * up, elementwise: the gate is squared after the ReLU, the
+    up projection passes through unchanged."""
+    gate = np.array([-2.0, 0.0, 3.0, 0.5, 1.0], np.float32)
+    up = np.array([5.0, 7.0, 2.0, -4.0, -1.5], np.float32)
+    h = o.relu2_mul(gate, up, lib)
+    assert h.tolist() == [0.0, 0.0, 18.0, -1.0, -1.5]
+
+
+def _ffn_onehot_expect(tg, tu, td, sg, su, sd, d, j, sv):
+    """Closed form of the FFN for a one-hot input with sign sv at j, unit gains and
+    eps = 0 (see pin_ffn_onehot). Returns gate, up, h, out and the bound on
+    |out - exact| set by the quantization step of q2."""
+    gate = tg[:, j] * sv * np.sqrt(d) / float(sg)
+    up = tu[:, j] * sv * np.sqrt(d) / float(su)
+    h = np.maximum(gate, 0) ** 2 * up
+    if not np.any(h != 0):
+        return gate, up, h, np.zeros(td.shape[0]), np.zeros(td.shape[0])
+    hn = h / np.sqrt(np.mean(h * h))
+    out = td.astype(np.float64) @ hn / float(sd)
+    step = np.abs(td).sum(1) * 0.5 / (127.0 / np.abs(hn).max()) / float(sd)
+    return gate, up, h, out, step
+
+
+def pin_ffn_onehot(o, lib):
+    """Closed form of the FFN for a one-hot input x = v e_j with unit gains and
+    eps = 0: the norm maps x to sqrt(D) sign(v) e_j, so q1 = 127 sign(v) e_j and
+    gate[f] = T_g[f][j] sign(v) sqrt(D)/s_g, up[f] = T_u[f][j] sign(v) sqrt(D)/s_u,
+    h = relu(gate)^2 up; the sub-norm and down projection then give
+    out = (t_d/s_d) * rmsnorm(h) up to the quantization step of q2."""
+    g = _rng(61)
+    d, f = 16, 32
+    tg = g.integers(-1, 2, (f, d)).astype(np.int8)
+    tu = g.integers(-1, 2, (f, d)).astype(np.int8)
+    td = g.integers(-1, 2, (d, f)).astype(np.int8)
+    sg, su, sd = np.float32(2.0), np.float32(8.0), np.float32(2.0)
+    ones_d, ones_f = np.ones(d, np.float32), np.ones(f, np.float32)
+    for j, v in ((3, 1.75), (10, -0.5)):
+        x = np.zeros((1, d), np.float32)
+        x[0, j] = v
+        r = o.ffn(x, ones_d, ones_f, 0.0, o.pack(tg, lib), sg, o.pack(tu, lib), su, o.pack(td, lib), sd, lib)
+        gate, up, h, out, step = _ffn_onehot_expect(tg, tu, td, sg, su, sd, d, j, np.sign(v))
+        assert np.allclose(r["gate"][0], gate, rtol=1e-6, atol=0)
+        assert np.allclose(r["up"][0], up, rtol=1e-6, atol=0)
+        assert np.allclose(r["h"][0], h, rtol=1e-5, atol=1e-7)
+        assert np.all(np.abs(r["out"][0] - out) <= step + 1e-5), (r["out"][0], out)
+
+
+def pin_layer_closed_form(o, lib):
+    """One layer in closed form: x = 0, the stand-in z = v e_0 and W_o with a single
+    +1 at (j, 0). Then a (the attention-norm quant of x) is 0, so q/k/v are 0;
+    the o projection gives y_o = sign(v) sqrt(D)/s_o e_j; the FFN reads
+    x' = x + y_o (one-hot) and adds its one-hot closed form:
+    x_next = y_o + out(x'). (A tiny eps keeps the norm of x = 0 finite.)"""
+    g = _rng(64)
+    d, f = 16, 32
+    tg = g.integers(-1, 2, (f, d)).astype(np.int8)
+    tu = g.integers(-1, 2, (f, d)).astype(np.int8)
+    td = g.integers(-1, 2, (d, f)).astype(np.int8)
+    for j, v in ((5, 0.75), (12, -3.0)):
+        to = np.zeros((d, d), np.int8)
+        to[j, 0] = 1
+        lw = {"wq": o.pack(g.integers(-1, 2, (d, d)).astype(np.int8), lib), "sq": np.float32(30.0),
+              "wk": o.pack(g.integers(-1, 2, (d, d)).astype(np.int8), lib), "sk": np.float32(31.0),
+              "wv": o.pack(g.integers(-1, 2, (d, d)).astype(np.int8), lib), "sv": np.float32(32.0),
+              "wo": o.pack(to, lib), "so": np.float32(2.0),
+              "wg": o.pack(tg, lib), "sg": np.float32(2.0), "wu": o.pack(tu, lib), "su": np.float32(8.0),
+              "wd": o.pack(td, lib), "sd": np.float32(2.0),
+              "g_attn": np.ones(d, np.float32), "g_attn_sub": np.ones(d, np.float32),
+              "g_ffn": np.ones(d, np.float32), "g_ffn_sub": np.ones(f, np.float32)}
+        z = np.zeros((1, d), np.float32)
+        z[0, 0] = v
+        lw["z"] = z
+        # eps = 1e-12 keeps r finite for x = 0 and moves the closed form by ~1e-11.
+        x_next, qkv = o.layer(np.zeros((1, d), np.float32), lw, 1e-12, lib)
+        assert (qkv == 0).all()
+        yo = np.zeros(d)
+        yo[j] = np.sign(v) * np.sqrt(d) / 2.0
+        _, _, _, out, step = _ffn_onehot_expect(tg, tu, td, 2.0, 8.0, 2.0, d, j, np.sign(v))
+        assert np.all(np.abs(x_next[0] - (yo + out)) <= step + 1e-5), (x_next[0], yo + out)
+
+
+def pin_ffn_zero_paths(o, lib):
+    """Zero up weights (or a gate that is never positive) give h = 0 and out = 0."""
+    g = _rng(62)
+    d, f = 16, 32
+    x = g.standard_normal((2, d)).astype(np.float32)
+    tg = g.integers(-1, 2, (f, d)).astype(np.int8)
+    td = g.integers(-1, 2, (d, f)).astype(np.int8)
+    gd, gf = np.ones(d, np.float32), np.ones(f, np.float32)
+    r = o.ffn(x, gd, gf, 1e-5, o.pack(tg, lib), 10.0, o.pack(np.zeros((f, d), np.int8), lib), 10.0,
+              o.pack(td, lib), 10.0, lib)
+    assert (r["h"] == 0).all() and (r["out"] == 0).all()
+    xpos = np.abs(x)
+    r = o.ffn(xpos, gd, gf, 1e-5, o.pack(-np.ones((f, d), np.int8), lib), 10.0, o.pack(tg, lib), 10.0,
+              o.pack(td, lib), 10.0, lib)
+    assert (r["gate"] < 0).all() and (r["h"] == 0).all() and (r["out"] == 0).all()
+
+
+def pin_ffn_subnorm_present(o, lib):
+    """The sub-norm gain scales h before its quantization: doubling the sub-norm
+    gain leaves q2 unchanged and doubles out exactly (s2 halves), while a gain that zeroes
+    half of h changes q2 (the norm sits between the gating and the down
+    projection)."""
+    g = _rng(63)
+    d, f = 16, 64
+    x = g.standard_normal((1, d)).astype(np.float32)
+    w = [o.pack(g.integers(-1, 2, s).astype(np.int8), lib) for s in ((f, d), (f, d), (d, f))]
+    gd = np.ones(d, np.float32)
+    r1 = o.ffn(x, gd, np.ones(f, np.float32), 0.0, w[0], 3.0, w[1], 3.0, w[2], 3.0, lib)
+    r2 = o.ffn(x, gd, np.full(f, 2.0, np.float32), 0.0, w[0], 3.0, w[1], 3.0, w[2], 3.0, lib)
+    assert (r1["q2"] == r2["q2"]).all() and (r2["out"] == 2 * r1["out"]).all()
+    half = np.ones(f, np.float32)
+    half[: f // 2] = 0.0
+    r3 = o.ffn(x, gd, half, 0.0, w[0], 3.0, w[1], 3.0, w[2], 3.0, lib)
+    hz = r1["h"][0].copy()
+    if np.any(hz[: f // 2] != 0):
+        assert (r3["q2"][0, : f // 2] == 0).all()
+        assert not (r3["q2"] == r1["q2"]).all()
+
+
+# --- layer chain ------------------------------------------------------------------------
+
+def _layer_weights(o, lib, g, d, f, zero=()):
+    lw = {}
+    for name, (n, k) in zip(("wq", "wk", "wv", "wo", "wg", "wu", "wd"),
+                            [(d, d)] * 4 + [(f, d), (f, d), (d, f)]):
+        t = np.zeros((n, k), np.int8) if name in zero else g.integers(-1, 2, (n, k)).astype(np.int8)
+        lw[name] = o.pack(t, lib)
+        lw["s" + name[1]] = np.float32(g.uniform(20, 60))
+    lw["z"] = g.standard_normal((1, d)).astype(np.float32)
+    for key, k in (("g_attn", d), ("g_attn_sub", d), ("g_ffn", d), ("g_ffn_sub", f)):
+        lw[key] = g.uniform(0.5, 1.5, k).astype(np.float32)
+    return lw
+
+
+def pin_chain_zero_weights(o, lib):
+    """With zero o, gate, up and down weights every residual adds +0 and x passes
+    through the stream unchanged; q/k/v still read the attention norm of x."""
+    g = _rng(71)
+    d, f = 16, 32
+    x = g.standard_normal((1, d)).astype(np.float32)
+    layers = [_layer_weights(o, lib, g, d, f, zero=("wo", "wg", "wu", "wd")) for _ in range(3)]
+    x2, qkvs = o.chain(x, layers, 1e-5, lib)
+    assert (x2 == x).all()
+    for lw, qkv in zip(layers, qkvs):
+        a, sa, _ = o.quant_act(x, lw["g_attn"], 1e-5, lib)
+        tq = o.unpack(lw["wq"], d, lib)
+        q_ref = a.astype(np.int64) @ tq.astype(np.int64).T
+        assert (np.round(qkv[0, :d].astype(np.float64) * float(sa[0]) * float(lw["sq"])) == q_ref[0]).all()
+
+
+def pin_chain_residual(o, lib):
+    """The o projection output and the FFN output are each added to x once: with
+    only wo nonzero, x_next - x equals the o projection of the stand-in z."""
+    g = _rng(72)
+    d, f = 16, 32
+    x = g.standard_normal((1, d)).astype(np.float32)
+    lw = _layer_weights(o, lib, g, d, f, zero=("wg", "wu", "wd"))
+    x2, _ = o.layer(x, lw, 1e-5, lib)
+    zq, zs, _ = o.quant_act(lw["z"], lw["g_attn_sub"], 1e-5, lib)
+    to = o.unpack(lw["wo"], d, lib).astype(np.int64)
+    yo = (zq.astype(np.int64) @ to.T)[0] / (float(zs[0]) * float(lw["so"]))
+    assert np.allclose(x2[0] - x[0], yo, rtol=1e-5, atol=1e-6)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

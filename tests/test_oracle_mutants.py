@@ -1,0 +1,103 @@
+"""The pins catch plausible mistakes: each mutant below plants one mistake in a
+temporary copy of the oracle (C source or Python composition) and at least one
+pin must fail on it. Runs on the CPU only; the real oracle is never modified."""
+import importlib.util
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+C_SRC = os.path.join(ROOT, "oracle", "bitlinear_oracle.c")
+PY_SRC = os.path.join(ROOT, "oracle", "__init__.py")
+
+# (name, original text, planted text) in bitlinear_oracle.c
+C_MUTANTS = [
+    ("pack_code_flip", "(unsigned)(t[r * k + 4 * i + j] + 1)", "(unsigned)(1 - t[r * k + 4 * i + j])"),
+    ("pack_field_order", "byte |= code << (2 * j);", "byte |= code << (6 - 2 * j);"),
+    ("unpack_sign", "(int8_t)((int)code - 1)", "(int8_t)(1 - (int)code)"),
+    ("unpack_accepts_code3", "if (code == 3u) return -4;", "if (code == 4u) return -4;"),
+    ("aq_round_half_away", "float r = nearbyintf(v);\n            if (r > 127.0f)",
+     "float r = roundf(v);\n            if (r > 127.0f)"),
+    ("aq_scale_128", "float scale = 127.0f /", "float scale = 128.0f /"),
+    ("aq_no_abs", "float a = fabsf(yr[i]);", "float a = yr[i];"),
+    ("aq_qsum_positive_only", "sum += qi;", "sum += (qi > 0 ? qi : 0);"),
+    ("aq_floor_missing", "float scale = 127.0f / (amax > floor_ ? amax : floor_);",
+     "float scale = 127.0f / (amax > 0.0f ? amax : 1.0f);"),
+    ("sumsq_drop_last", "for (int64_t i = 0; i < k; i++) {\n        double v",
+     "for (int64_t i = 0; i + 1 < k; i++) {\n        double v"),
+    ("sumsq_64_partials", "p[i % ORACLE_PARTIALS] += v * v;", "p[i % 64] += v * v;"),
+    ("rms_no_mean", "sqrt(ss / (double)k + (double)eps)", "sqrt(ss + (double)eps)"),
+    ("rms_no_eps", "sqrt(ss / (double)k + (double)eps)", "sqrt(ss / (double)k)"),
+    ("rms_no_sqrt", "1.0 / sqrt(ss / (double)k + (double)eps)", "1.0 / (ss / (double)k + (double)eps)"),
+    ("rms_no_gain", "y[row * k + i] = a * g[i];", "y[row * k + i] = a;"),
+    ("wq_absmax", "sum += fabs((double)w[i]);", "sum = fmax(sum, fabs((double)w[i]));"),
+    ("wq_no_clamp", "if (r > 1.0f) r = 1.0f;", "if (r > 2.0f) r = 2.0f;"),
+    ("wq_round_half_away", "float r = nearbyintf(v);\n        if (r > 1.0f)", "float r = roundf(v);\n        if (r > 1.0f)"),
+    ("mm_transposed_out", "acc[row * n + col] = s;", "acc[col * m + row] = s;"),
+    ("mm_wrong_k", "s += (int32_t)tr[i] * (int32_t)qr[i];", "s += (int32_t)tr[i] * (int32_t)qr[k - 1 - i];"),
+    ("dq_inverted", "float inv = 1.0f / prod;", "float inv = prod;"),
+    ("dq_no_sw", "float prod = s_a[row] * s_w;", "float prod = s_a[row];"),
+    ("dq_row0_scale", "float prod = s_a[row] * s_w;", "float prod = s_a[0] * s_w;"),
+    ("relu_not_squared", "float g2 = g * g;", "float g2 = g;"),
+    ("relu_on_up", "h[i] = g2 * up[i];", "h[i] = g2 * (up[i] > 0.0f ? up[i] : 0.0f);"),
+    ("relu_missing", "float g = gate[i] > 0.0f ? gate[i] : 0.0f;", "float g = gate[i];"),
+    ("argmax_last_tie", "if (a[col] > a[best]) best = col;", "if (a[col] >= a[best]) best = col;"),
+    ("residual_sub", "x[i] = x[i] + d[i];", "x[i] = x[i] - d[i];"),
+]
+
+# (name, original, planted) in oracle/__init__.py
+PY_MUTANTS = [
+    ("ffn_no_subnorm", "q2, s2, qs2 = quant_act(h, sub_norm_gain, eps, lib)", "q2, s2, qs2 = quant_act(h, None, eps, lib)"),
+    ("ffn_gate_up_swapped", "h = relu2_mul(gate, up, lib)", "h = relu2_mul(up, gate, lib)"),
+    ("ffn_up_uses_gate_w", "up, acc_up = bitlinear(w_up, s_up, d, q1, s1, lib)",
+     "up, acc_up = bitlinear(w_gate, s_up, d, q1, s1, lib)"),
+    ("ffn_no_norm", "q1, s1, qs1 = quant_act(x, norm_gain, eps, lib)", "q1, s1, qs1 = quant_act(x, None, eps, lib)"),
+    ("layer_no_residual_o", "    x = residual_add(x, yo, lib)\n", "    x = x\n"),
+    ("layer_o_reads_x", "o_in, so, _ = quant_act(lw[\"z\"], lw[\"g_attn_sub\"], eps, lib)",
+     "o_in, so, _ = quant_act(x, lw[\"g_attn_sub\"], eps, lib)"),
+    ("layer_ffn_from_old_x", "    f = ffn(x, lw[\"g_ffn\"]", "    f = ffn(x - yo, lw[\"g_ffn\"]"),
+    ("layer_q_uses_wk", "yq, _ = bitlinear(lw[\"wq\"], lw[\"sq\"], d, a, sa, lib)",
+     "yq, _ = bitlinear(lw[\"wk\"], lw[\"sq\"], d, a, sa, lib)"),
+]
+
+
+def _any_pin_fails(o, lib):
+    for pin in ALL_PINS:
+        try:
+            pin(o, lib)
+        except Exception:  # AssertionError, or an error the mistake provokes
+            return pin.__name__
+    return None
+
+
+@pytest.mark.parametrize("name,old,new", C_MUTANTS, ids=[m[0] for m in C_MUTANTS])
+def test_c_mutant_caught(name, old, new, tmp_path):
+    src = open(C_SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mut = tmp_path / "mut.c"
+    mut.write_text(src.replace(old, new))
+    so = tmp_path / "libmut.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared", str(mut),
+                    "-o", str(so), "-lm"], check=True)
+    lib = oracle.load(str(so))
+    caught = _any_pin_fails(oracle, lib)
+    assert caught, f"no pin caught mutant {name}"
+
+
+@pytest.mark.parametrize("name,old,new", PY_MUTANTS, ids=[m[0] for m in PY_MUTANTS])
+def test_py_mutant_caught(name, old, new, olib):
+    src = open(PY_SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    modname = f"oracle_mutant_{name}"
+    spec = importlib.util.spec_from_loader(modname, loader=None)
+    mod = importlib.util.module_from_spec(spec)
+    mod.__dict__["__file__"] = PY_SRC
+    exec(compile(src.replace(old, new), f"<{modname}>", "exec"), mod.__dict__)
+    sys.modules.pop(modname, None)
+    caught = _any_pin_fails(mod, olib)
+    assert caught, f"no pin caught mutant {name}"
