@@ -1,0 +1,285 @@
+#!/usr/bin/env python3
+"""Benchmark of the BitNet b1.58 BitLinear hot path on one MI355X.
+
+Timed step: one decode token through the full BitNet-3B BitLinear stream --
+32 layers x 7 BitLinears (q, k, v, o 2560x2560; gate, up 2560->10240; down
+10240->2560), each behind its RMSNorm + activation quant, with the ReLU^2 x up
+gating and the residual adds; attention math is left out (the o projection
+reads a seeded stand-in). 838,860,800 bytes of packed ternary weights are
+streamed per step, so the headline value is the weight-stream rate in GB/s
+(with ms/token beside it).
+
+Also reported in the same JSON line:
+  prefill  : activation quant of 2048 x 2560 fp32 tokens (1% outliers x20), then
+             the int8-MFMA GEMM against 10240 x 2560 ternary weights -> fp32;
+             int8 TOPS of the GEMM (2 M N K per call) and of quant + GEMM.
+  batched  : BitNet-1.3B stream at 32 tokens (24 layers x 7 BitLinears), then
+             the final norm + quant and the ternary LM head 2048 -> 50000 with
+             the fused per-row argmax.
+  gemv     : one 2560 -> 2560 BitLinear (quant + GEMV) at 1 token.
+  ffn      : the BitNet-3B FFN sub-layer at 1 token.
+  roofline : the dominant kernel against HBM or MFMA peak.
+  cpu_baseline : the CPU oracle on a bounded sample of the same workload.
+
+Inputs are synthetic and seeded (workloads.py): ternary weights with
+P(-1) = P(+1) = 0.3, scales U(20, 60), activations N(0, 1), unit gains.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, TOP/s
+METRIC = "BitLinear decode weight-stream GB/s + ms/token (3B shapes); prefill int8 TOPS"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def ensure_built():
+    lib = os.path.join(ROOT, "bitlinear_amd", "libbitlinear.so")
+    olib = os.path.join(ROOT, "oracle", "liboracle.so")
+    if not (os.path.exists(lib) and os.path.exists(olib)):
+        import __graft_entry__
+        __graft_entry__.build()
+
+
+class Timer:
+    """HIP events on the stream the library launches on (torch's current stream)."""
+
+    def __init__(self):
+        import torch
+        self.torch = torch
+        self.s = torch.cuda.Event(enable_timing=True)
+        self.e = torch.cuda.Event(enable_timing=True)
+
+    def __enter__(self):
+        self.s.record()
+        return self
+
+    def __exit__(self, *a):
+        self.e.record()
+        self.e.synchronize()
+        self.ms = self.s.elapsed_time(self.e)
+
+
+def build_stream(bl, workload, n_layers, d, f, m, T):
+    """Seeded layers packed with the library's host packer and uploaded as one
+    resident blob. Returns host copies for the oracle too."""
+    blobs, scales, gains, zs, host_layers = [], [], [], [], []
+    for l in range(n_layers):
+        raw = W.layer_inputs(workload, l, d, f, m, bench_gains=True)
+        lw = {}
+        for name, sname in zip(W.LINEAR_NAMES, W.SCALE_NAMES):
+            lw[name] = bl.bitlinear_pack(raw[name])
+            lw[sname] = raw[sname]
+            blobs.append(lw[name].reshape(-1))
+        for key in ("g_attn", "g_attn_sub", "g_ffn", "g_ffn_sub", "z"):
+            lw[key] = raw[key]
+        scales.append(np.array([raw[s] for s in W.SCALE_NAMES], np.float32))
+        gains.append(np.concatenate([raw["g_attn"], raw["g_attn_sub"], raw["g_ffn"], raw["g_ffn_sub"]]))
+        zs.append(raw["z"])
+        host_layers.append(lw)
+        del raw
+    dev = dict(weights=T(np.concatenate(blobs)), scales=T(np.stack(scales)), gains=T(np.stack(gains)),
+               z=T(np.stack(zs)))
+    return dev, host_layers
+
+
+def run_stream_step(bl, dev, n_layers, m, d, f, x, qkv, ws):
+    bl.bitnet_decode_stream(dev["weights"], dev["scales"], dev["gains"], dev["z"], n_layers, m, d, f, 1e-5, x, qkv, ws)
+
+
+def omp_threads():
+    v = os.environ.get("OMP_NUM_THREADS")
+    return int(v) if v and v.isdigit() else os.cpu_count()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extra", action="store_true", help="only the headline decode stream")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    ensure_built()
+    import torch
+    import bitlinear_amd as bl
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev0 = torch.device("cuda:0")
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev0)
+
+    # ---- headline: BitNet-3B decode stream, 1 token ------------------------------------
+    cfg = W.BITNET_3B
+    L, d, f, m = cfg["layers"], cfg["dim"], cfg["ffn"], 1
+    t0 = time.perf_counter()
+    dev, host_layers = build_stream(bl, W.W_STREAM, L, d, f, m, T)
+    weight_bytes = L * bl.bitnet_layer_bytes(d, f)
+    log(f"3B stream inputs ready in {time.perf_counter() - t0:.1f}s ({weight_bytes} packed weight bytes)")
+    x0 = W.activations(W.rng(W.W_STREAM, 999, W.T_X), m, d)
+    x = T(x0)
+    qkv = torch.empty((L, m, 3 * d), dtype=torch.float32, device=dev0)
+    ws = torch.empty(bl.bitnet_stream_workspace_bytes(m, d, f), dtype=torch.uint8, device=dev0)
+
+    # first step from x0, checked against the oracle below (same inputs)
+    run_stream_step(bl, dev, L, m, d, f, x, qkv, ws)
+    torch.cuda.synchronize()
+    x_first = x.cpu().numpy()
+    qkv_first = qkv.cpu().numpy()
+
+    for _ in range(args.warmup):
+        run_stream_step(bl, dev, L, m, d, f, x, qkv, ws)
+    torch.cuda.synchronize()
+    tw0 = time.perf_counter()
+    with Timer() as tm:
+        for _ in range(args.steps):
+            run_stream_step(bl, dev, L, m, d, f, x, qkv, ws)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - tw0) * 1e3
+    ms_per_step = wall_ms / args.steps
+    ev_ms_per_step = tm.ms / args.steps
+    value = weight_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"decode stream: {ms_per_step:.4f} ms/token wall, {ev_ms_per_step:.4f} ms/token events, {value:.1f} GB/s")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded ternary weights, N(0,1) activations)",
+        "config": {"workload": "BitNet-3B decode weight stream: 32 layers x 7 BitLinears, 1 token, "
+                               "attention math excluded", "layers": L, "dim": d, "ffn": f, "tokens": m,
+                   "weight_bytes_per_step": weight_bytes},
+        "ms_per_token": round(ms_per_step, 5),
+    }
+
+    # roofline of the dominant kernel: the stream as launched per step
+    result["roofline"] = {"kernel": "bitnet_decode_stream step (all launches of one token)", "bound": "hbm",
+                          "achieved": round(weight_bytes / (ev_ms_per_step * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": round(weight_bytes / (ev_ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "traffic": None}
+
+    # ---- CPU oracle baseline + parity of the first step ----------------------------------
+    if not args.no_cpu:
+        import oracle
+        olib = oracle.load()
+        tc0 = time.perf_counter()
+        ox, oqkv = oracle.chain(x0, host_layers, 1e-5, olib)
+        cpu_s = time.perf_counter() - tc0
+        exact = bool(np.array_equal(ox.view(np.uint32), x_first.view(np.uint32)) and
+                     all(np.array_equal(oqkv[l].view(np.uint32), qkv_first[l].view(np.uint32)) for l in range(L)))
+        rel = float(np.max(np.abs(ox.astype(np.float64) - x_first) / np.maximum(np.abs(ox), 1e-30)))
+        result["cpu_baseline"] = {"value": round(weight_bytes / cpu_s / 1e9, 4), "unit": "GB/s",
+                                  "cores": omp_threads(), "kind": "oracle",
+                                  "sample": "one full token of the same 32-layer stream (all 224 BitLinears), "
+                                            f"{cpu_s:.2f} s"}
+        result["parity_first_step"] = {"bit_exact": exact, "max_rel_err_x": rel}
+        log(f"oracle: {cpu_s:.2f}s for one token; first GPU step bit-exact: {exact}")
+    del host_layers
+
+    if not args.no_extra:
+        result.update(extra_measurements(bl, torch, T, dev0))
+    print(json.dumps(result), flush=True)
+
+
+def extra_measurements(bl, torch, T, dev0):
+    out = {}
+    # ---- prefill GEMM 2048 x 2560 -> 10240 ----
+    M, K, N = 2048, 2560, 10240
+    g = W.rng(W.W_PREFILL, 0, W.T_GATE)
+    t = W.ternary(g, N, K)
+    sw = W.weight_scale(g)
+    p = T(bl.bitlinear_pack(t))
+    del t
+    x = T(W.activations(W.rng(W.W_PREFILL, 0, W.T_X), M, K, outliers=True))
+    q = torch.empty((M, K), dtype=torch.int8, device=dev0)
+    s = torch.empty(M, dtype=torch.float32, device=dev0)
+    qs = torch.empty(M, dtype=torch.int32, device=dev0)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev0)
+    bl.bitlinear_quant_act(x, None, 1e-5, q, s, qs)
+    for _ in range(3):
+        bl.bitlinear_gemm(p, sw, N, K, q, s, qs, M, None, y)
+    iters = 20
+    with Timer() as tg:
+        for _ in range(iters):
+            bl.bitlinear_gemm(p, sw, N, K, q, s, qs, M, None, y)
+    with Timer() as tq:
+        for _ in range(iters):
+            bl.bitlinear_quant_act(x, None, 1e-5, q, s, qs)
+            bl.bitlinear_gemm(p, sw, N, K, q, s, qs, M, None, y)
+    ops = 2.0 * M * N * K
+    gemm_ms = tg.ms / iters
+    out["prefill"] = {"workload": "quant 2048x2560 fp32 (1% outliers x20) + GEMM vs 10240x2560 ternary -> fp32",
+                      "gemm_ms": round(gemm_ms, 4), "gemm_tops": round(ops / (gemm_ms * 1e-3) / 1e12, 1),
+                      "quant_plus_gemm_ms": round(tq.ms / iters, 4),
+                      "quant_plus_gemm_tops": round(ops / (tq.ms / iters * 1e-3) / 1e12, 1),
+                      "peak_tops": INT8_PEAK_TOPS,
+                      "gemm_frac": round(ops / (gemm_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)}
+    log(f"prefill: GEMM {gemm_ms:.4f} ms = {out['prefill']['gemm_tops']} TOPS")
+    del p, x, q, y
+
+    # ---- batched decode, 1.3B, 32 tokens, + LM head argmax ----
+    cfg = W.BITNET_1P3B
+    L, d, f, m, V = cfg["layers"], cfg["dim"], cfg["ffn"], 32, cfg["vocab"]
+    dev, _ = build_stream(bl, W.W_BATCHED, L, d, f, m, T)
+    gh = W.rng(W.W_BATCHED, 0, W.T_HEAD)
+    head = T(bl.bitlinear_pack(W.ternary(gh, V, d)))
+    sh = W.weight_scale(gh)
+    gfin = T(np.ones(d, np.float32))
+    xb = T(W.activations(W.rng(W.W_BATCHED, 999, W.T_X), m, d))
+    qkv = torch.empty((L, m, 3 * d), dtype=torch.float32, device=dev0)
+    ws = torch.empty(bl.bitnet_stream_workspace_bytes(m, d, f), dtype=torch.uint8, device=dev0)
+    qf = torch.empty((m, d), dtype=torch.int8, device=dev0)
+    sf = torch.empty(m, dtype=torch.float32, device=dev0)
+    qsf = torch.empty(m, dtype=torch.int32, device=dev0)
+    idx = torch.empty(m, dtype=torch.int32, device=dev0)
+    wsh = torch.empty(bl.bitlinear_gemm_workspace_bytes(m, V, d, 1), dtype=torch.uint8, device=dev0)
+
+    def batched_step():
+        run_stream_step(bl, dev, L, m, d, f, xb, qkv, wsh_dummy := ws)
+        bl.bitlinear_quant_act(xb, gfin, 1e-5, qf, sf, qsf)
+        bl.bitlinear_gemm(head, sh, V, d, qf, sf, qsf, m, None, None, None, idx, wsh)
+
+    for _ in range(2):
+        batched_step()
+    iters = 10
+    with Timer() as tb:
+        for _ in range(iters):
+            batched_step()
+    bytes_b = L * bl.bitnet_layer_bytes(d, f) + V * d // 4
+    ms_b = tb.ms / iters
+    out["batched"] = {"workload": "BitNet-1.3B stream, 32 tokens, 24 layers x 7 BitLinears + LM head 2048->50000 "
+                                  "with fused argmax", "ms_per_step": round(ms_b, 4),
+                      "weight_gbs": round(bytes_b / (ms_b * 1e-3) / 1e9, 1),
+                      "us_per_token": round(ms_b * 1e3 / m, 3), "weight_bytes": bytes_b,
+                      "frac_hbm": round(bytes_b / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    log(f"batched: {ms_b:.4f} ms per 32-token step")
+    del dev, head
+    return out
+
+
+if __name__ == "__main__":
+    main()

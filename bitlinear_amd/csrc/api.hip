@@ -1,0 +1,276 @@
+// api.hip -- the device entry points of the C ABI: argument checks on the host,
+// then launches on the caller's stream. No allocation, no synchronisation, no
+// host reads of device memory.
+#include "internal.h"
+
+namespace {
+
+using bl::aligned;
+
+constexpr int64_t kMaxGemvM = 8;
+constexpr int64_t kMaxGemvK = 32768;
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+inline bool dim_ok(int64_t v) { return v > 0 && v <= kMaxDim; }
+
+// k must be a positive multiple of 64 (whole 16-byte packed chunks).
+inline bool k_ok(int64_t k) { return dim_ok(k) && (k % 64) == 0; }
+
+struct Layout {
+    size_t off[BITNET_FFN_WS_COUNT];
+    size_t total;
+};
+
+Layout ffn_layout(int64_t m, int64_t d, int64_t f)
+{
+    const size_t sz[BITNET_FFN_WS_COUNT] = {
+        (size_t)(m * d),     (size_t)m * 4,     (size_t)m * 4, (size_t)(m * f) * 4,
+        (size_t)(m * f),     (size_t)m * 4,     (size_t)m * 4, (size_t)(m * f) * 4,
+        (size_t)(m * f) * 4, (size_t)(m * d) * 4, (size_t)(m * f) * 4, (size_t)(m * f) * 4,
+    };
+    Layout l{};
+    size_t at = 0;
+    for (int i = 0; i < BITNET_FFN_WS_COUNT; ++i) {
+        l.off[i] = at;
+        at = align_up(at + sz[i], 256);
+    }
+    l.total = at;
+    return l;
+}
+
+// Stream workspace: a (q, s, qs) for d, o_in for d, the FFN workspace, the
+// q/k/v scratch when the caller passes none.
+struct StreamLayout {
+    size_t q_a, s_a, qs_a, q_o, s_o, qs_o, ffn, qkv, total;
+};
+
+StreamLayout stream_layout(int64_t m, int64_t d, int64_t f)
+{
+    StreamLayout l{};
+    size_t at = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = at;
+        at = align_up(at + bytes, 256);
+        return o;
+    };
+    l.q_a = take((size_t)(m * d));
+    l.s_a = take((size_t)m * 4);
+    l.qs_a = take((size_t)m * 4);
+    l.q_o = take((size_t)(m * d));
+    l.s_o = take((size_t)m * 4);
+    l.qs_o = take((size_t)m * 4);
+    l.ffn = take(ffn_layout(m, d, f).total);
+    l.qkv = take((size_t)(m * 3 * d) * 4);
+    l.total = at;
+    return l;
+}
+
+template <typename T>
+inline T* at(void* base, size_t off)
+{
+    return reinterpret_cast<T*>(static_cast<uint8_t*>(base) + off);
+}
+
+int ffn_impl(const float* x, int64_t m, int64_t d, int64_t f, const float* g_ffn, const float* g_sub, float eps,
+             const uint8_t* w_gate, float s_gate, const uint8_t* w_up, float s_up, const uint8_t* w_down,
+             float s_down, const float* scale_ptr /* [gate, up, down] or null */, const float* residual, float* out,
+             void* ws, int flags, hipStream_t s)
+{
+    const Layout L = ffn_layout(m, d, f);
+    int8_t* q1 = at<int8_t>(ws, L.off[BITNET_FFN_WS_Q1]);
+    float* s1 = at<float>(ws, L.off[BITNET_FFN_WS_S1]);
+    int32_t* qs1 = at<int32_t>(ws, L.off[BITNET_FFN_WS_QS1]);
+    float* h = at<float>(ws, L.off[BITNET_FFN_WS_H]);
+    int8_t* q2 = at<int8_t>(ws, L.off[BITNET_FFN_WS_Q2]);
+    float* s2 = at<float>(ws, L.off[BITNET_FFN_WS_S2]);
+    int32_t* qs2 = at<int32_t>(ws, L.off[BITNET_FFN_WS_QS2]);
+    const bool keep = (flags & BITNET_FFN_WRITE_ACC) != 0;
+    int32_t* acc_g = keep ? at<int32_t>(ws, L.off[BITNET_FFN_WS_ACC_GATE]) : nullptr;
+    int32_t* acc_u = keep ? at<int32_t>(ws, L.off[BITNET_FFN_WS_ACC_UP]) : nullptr;
+    int32_t* acc_d = keep ? at<int32_t>(ws, L.off[BITNET_FFN_WS_ACC_DOWN]) : nullptr;
+    const int M = (int)m, D = (int)d, F = (int)f;
+
+    int rc = bl::launch_quant_act(x, g_ffn, eps, M, D, q1, s1, qs1, s);
+    if (rc) return rc;
+    if (m <= kMaxGemvM) {
+        rc = bl::launch_gateup(w_gate, s_gate, w_up, s_up, scale_ptr, F, D, q1, s1, qs1, M, h, acc_g, acc_u, s);
+    } else {
+        float* gate = at<float>(ws, L.off[BITNET_FFN_WS_GATE]);
+        float* up = at<float>(ws, L.off[BITNET_FFN_WS_UP]);
+        rc = bl::launch_gemm(w_gate, s_gate, scale_ptr, F, D, q1, s1, qs1, M, nullptr, gate, F, acc_g, nullptr,
+                             nullptr, s);
+        if (!rc)
+            rc = bl::launch_gemm(w_up, s_up, scale_ptr ? scale_ptr + 1 : nullptr, F, D, q1, s1, qs1, M, nullptr, up, F,
+                                 acc_u, nullptr, nullptr, s);
+        if (!rc) rc = bl::launch_relu2_mul(gate, up, (int64_t)m * f, h, s);
+    }
+    if (rc) return rc;
+    rc = bl::launch_quant_act(h, g_sub, eps, M, F, q2, s2, qs2, s);
+    if (rc) return rc;
+    const float* sdp = scale_ptr ? scale_ptr + 2 : nullptr;
+    if (m <= kMaxGemvM)
+        return bl::launch_gemv(w_down, s_down, sdp, D, F, q2, s2, qs2, M, residual, out, acc_d, s);
+    return bl::launch_gemm(w_down, s_down, sdp, D, F, q2, s2, qs2, M, residual, out, D, acc_d, nullptr, nullptr, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int bitlinear_quant_act(const float* x, const float* gain, float eps, int64_t m, int64_t k, int8_t* q,
+                        float* act_scale, int32_t* act_sum, void* stream)
+{
+    if (!x || !q || !act_scale) return BL_ERR_NULL;
+    if (!dim_ok(m) || !k_ok(k) || m > 0x7fffffff) return BL_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(q, 16) || (gain && !aligned(gain, 16)) || !aligned(act_scale, 4) ||
+        (act_sum && !aligned(act_sum, 4)))
+        return BL_ERR_ALIGN;
+    return bl::launch_quant_act(x, gain, eps, (int)m, (int)k, q, act_scale, act_sum, as_stream(stream));
+}
+
+int bitlinear_gemv(const uint8_t* packed, float w_scale, int64_t n, int64_t k, const int8_t* q,
+                   const float* act_scale, const int32_t* act_sum, int64_t m, const float* residual, float* y,
+                   int32_t* acc_out, void* stream)
+{
+    if (!packed || !q || !act_scale || !act_sum || !y) return BL_ERR_NULL;
+    if (m < 1 || m > kMaxGemvM || !dim_ok(n) || !k_ok(k) || k > kMaxGemvK) return BL_ERR_SHAPE;
+    if (!aligned(packed, 16) || !aligned(q, 16) || !aligned(act_scale, 4) || !aligned(act_sum, 4) ||
+        !aligned(y, 4) || (residual && !aligned(residual, 4)) || (acc_out && !aligned(acc_out, 4)))
+        return BL_ERR_ALIGN;
+    if (!(w_scale > 0.0f) || !(w_scale < INFINITY)) return BL_ERR_VALUE;
+    return bl::launch_gemv(packed, w_scale, nullptr, (int)n, (int)k, q, act_scale, act_sum, (int)m, residual, y,
+                           acc_out, as_stream(stream));
+}
+
+size_t bitlinear_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int with_argmax)
+{
+    (void)n;
+    (void)k;
+    if (!with_argmax || m <= 0) return 0;
+    return align_up((size_t)m * 8, 256);
+}
+
+int bitlinear_gemm(const uint8_t* packed, float w_scale, int64_t n, int64_t k, const int8_t* q,
+                   const float* act_scale, const int32_t* act_sum, int64_t m, const float* residual, float* y,
+                   int32_t* acc_out, int32_t* row_argmax, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!packed || !q || !act_scale || !act_sum) return BL_ERR_NULL;
+    if (!y && !row_argmax) return BL_ERR_NULL;
+    if (row_argmax && !workspace) return BL_ERR_NULL;
+    if (!dim_ok(m) || !dim_ok(n) || !k_ok(k) || m > 0x7fffffff || n > 0x7fffffff || m * n > ((int64_t)1 << 40))
+        return BL_ERR_SHAPE;
+    if (!aligned(packed, 16) || !aligned(q, 16) || !aligned(act_scale, 4) || !aligned(act_sum, 4) ||
+        (y && !aligned(y, 4)) || (residual && !aligned(residual, 4)) || (acc_out && !aligned(acc_out, 4)) ||
+        (row_argmax && !aligned(row_argmax, 4)) || (workspace && !aligned(workspace, 8)))
+        return BL_ERR_ALIGN;
+    if (!(w_scale > 0.0f) || !(w_scale < INFINITY)) return BL_ERR_VALUE;
+    if (row_argmax && workspace_bytes < bitlinear_gemm_workspace_bytes(m, n, k, 1)) return BL_ERR_WORKSPACE;
+    return bl::launch_gemm(packed, w_scale, nullptr, (int)n, (int)k, q, act_scale, act_sum, (int)m, residual, y,
+                           (int)n, acc_out, row_argmax, static_cast<unsigned long long*>(workspace),
+                           as_stream(stream));
+}
+
+size_t bitnet_ffn_workspace_bytes(int64_t m, int64_t d, int64_t f)
+{
+    if (m <= 0 || d <= 0 || f <= 0) return 0;
+    return ffn_layout(m, d, f).total;
+}
+
+size_t bitnet_ffn_workspace_offset(int64_t m, int64_t d, int64_t f, int segment)
+{
+    if (m <= 0 || d <= 0 || f <= 0 || segment < 0 || segment >= BITNET_FFN_WS_COUNT) return (size_t)-1;
+    return ffn_layout(m, d, f).off[segment];
+}
+
+int bitnet_ffn(const float* x, int64_t m, int64_t d, int64_t f, const float* norm_gain, const float* sub_norm_gain,
+               float eps, const uint8_t* w_gate, float s_gate, const uint8_t* w_up, float s_up,
+               const uint8_t* w_down, float s_down, const float* residual, float* out, void* workspace,
+               size_t workspace_bytes, int flags, void* stream)
+{
+    if (!x || !norm_gain || !sub_norm_gain || !w_gate || !w_up || !w_down || !out || !workspace) return BL_ERR_NULL;
+    if (!dim_ok(m) || !k_ok(d) || !k_ok(f) || m > 0x7fffffff || f > kMaxGemvK || d > kMaxGemvK)
+        return BL_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(norm_gain, 16) || !aligned(sub_norm_gain, 16) || !aligned(w_gate, 16) ||
+        !aligned(w_up, 16) || !aligned(w_down, 16) || !aligned(out, 4) || (residual && !aligned(residual, 4)) ||
+        !aligned(workspace, 256))
+        return BL_ERR_ALIGN;
+    if (!(s_gate > 0.0f) || !(s_up > 0.0f) || !(s_down > 0.0f) || !(s_gate < INFINITY) || !(s_up < INFINITY) ||
+        !(s_down < INFINITY))
+        return BL_ERR_VALUE;
+    if (workspace_bytes < bitnet_ffn_workspace_bytes(m, d, f)) return BL_ERR_WORKSPACE;
+    return ffn_impl(x, m, d, f, norm_gain, sub_norm_gain, eps, w_gate, s_gate, w_up, s_up, w_down, s_down, nullptr,
+                    residual, out, workspace, flags, as_stream(stream));
+}
+
+size_t bitnet_layer_bytes(int64_t d, int64_t f)
+{
+    if (d <= 0 || f <= 0) return 0;
+    return (size_t)(d * d) + (size_t)(3 * d * f) / 4;
+}
+
+size_t bitnet_stream_workspace_bytes(int64_t m, int64_t d, int64_t f)
+{
+    if (m <= 0 || d <= 0 || f <= 0) return 0;
+    return stream_layout(m, d, f).total;
+}
+
+int bitnet_decode_stream(const uint8_t* weights, const float* scales, const float* gains, const float* z,
+                         int64_t n_layers, int64_t m, int64_t d, int64_t f, float eps, float* x, float* qkv,
+                         void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!weights || !scales || !gains || !z || !x || !workspace) return BL_ERR_NULL;
+    if (!dim_ok(n_layers) || !dim_ok(m) || !k_ok(d) || !k_ok(f) || d > kMaxGemvK || f > kMaxGemvK ||
+        m > 0x7fffffff)
+        return BL_ERR_SHAPE;
+    if (!aligned(weights, 16) || !aligned(scales, 4) || !aligned(gains, 16) || !aligned(z, 16) || !aligned(x, 16) ||
+        (qkv && !aligned(qkv, 16)) || !aligned(workspace, 256))
+        return BL_ERR_ALIGN;
+    if (workspace_bytes < bitnet_stream_workspace_bytes(m, d, f)) return BL_ERR_WORKSPACE;
+    const hipStream_t s = as_stream(stream);
+    const StreamLayout L = stream_layout(m, d, f);
+    int8_t* qa = at<int8_t>(workspace, L.q_a);
+    float* sa = at<float>(workspace, L.s_a);
+    int32_t* qsa = at<int32_t>(workspace, L.qs_a);
+    int8_t* qo = at<int8_t>(workspace, L.q_o);
+    float* so = at<float>(workspace, L.s_o);
+    int32_t* qso = at<int32_t>(workspace, L.qs_o);
+    void* ffn_ws = at<void>(workspace, L.ffn);
+    const int M = (int)m, D = (int)d;
+    const size_t blob = bitnet_layer_bytes(d, f);
+    const size_t dd = (size_t)(d * d) / 4, fd = (size_t)(f * d) / 4;
+    const size_t gstride = (size_t)(3 * d + f);
+    for (int64_t l = 0; l < n_layers; ++l) {
+        const uint8_t* wl = weights + (size_t)l * blob;
+        const float* sl = scales + 7 * l;
+        const float* gl = gains + l * gstride;
+        float* qkv_l = qkv ? qkv + (size_t)l * m * 3 * d : at<float>(workspace, L.qkv);
+        int rc = bl::launch_quant_act(x, gl, eps, M, D, qa, sa, qsa, s);
+        if (rc) return rc;
+        if (m <= kMaxGemvM) {
+            const uint8_t* qkv_w[3] = {wl, wl + dd, wl + 2 * dd};
+            rc = bl::launch_gemv_multi(3, qkv_w, sl, D, D, qa, sa, qsa, M, qkv_l, 3 * D, s);
+        } else {
+            for (int j = 0; j < 3 && !rc; ++j)  // column block j of qkv[m][3d]
+                rc = bl::launch_gemm(wl + j * dd, 0.0f, sl + j, D, D, qa, sa, qsa, M, nullptr, qkv_l + (size_t)j * d,
+                                     3 * D, nullptr, nullptr, nullptr, s);
+        }
+        if (rc) return rc;
+        rc = bl::launch_quant_act(z + (size_t)l * m * d, gl + d, eps, M, D, qo, so, qso, s);
+        if (rc) return rc;
+        if (m <= kMaxGemvM)
+            rc = bl::launch_gemv(wl + 3 * dd, 0.0f, sl + 3, D, D, qo, so, qso, M, x, x, nullptr, s);
+        else
+            rc = bl::launch_gemm(wl + 3 * dd, 0.0f, sl + 3, D, D, qo, so, qso, M, x, x, D, nullptr, nullptr, nullptr, s);
+        if (rc) return rc;
+        rc = ffn_impl(x, m, d, f, gl + 2 * d, gl + 3 * d, eps, wl + 4 * dd, 0.0f, wl + 4 * dd + fd, 0.0f,
+                      wl + 4 * dd + 2 * fd, 0.0f, sl + 4, x, x, ffn_ws, 0, s);
+        if (rc) return rc;
+    }
+    return BL_OK;
+}
+
+}  // extern "C"

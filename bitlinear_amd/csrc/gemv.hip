@@ -1,0 +1,343 @@
+// gemv.hip -- decode BitLinear GEMV (a few tokens) on packed ternary weights.
+//
+// The decode step of a BitNet layer is a weight stream: every packed byte of a
+// BitLinear is read once per token ("Transformer Block", Hesper API, "Memory
+// Layout": ~26 MB of TQ2_0 weights per BitNet-3B layer). Each group of L lanes
+// owns one output row; lane j of the group reads the row's 16-byte chunks
+// j, j+L, j+2L, ... with 128-bit loads (a chunk is 64 weights), so a load
+// instruction of the wave covers 64/L rows x L consecutive chunks.
+//
+// Unpack: a packed dword holds the codes c = t+1 of 16 consecutive weights,
+// field j of byte b being weight 4b+j. (w >> 2j) & 0x03030303 therefore yields
+// the codes of weights {j, 4+j, 8+j, 12+j} as four bytes, which one
+// v_dot4_i32_i8 multiplies with the activations taken in the same order. The
+// activations are put in that order once per lane (a 4x4 byte transpose with
+// v_perm_b32), so the inner loop is 3 shifts, 4 ANDs and 4 dot4 per 16 weights.
+// Since c = t + 1, sum_k t*q = sum_k c*q - sum_k q: the act_sum of the token is
+// subtracted once per row. The partial sums are reduced across the L lanes with
+// xor shuffles, and the group's first lane applies the single fp32 rescale.
+#include "internal.h"
+
+namespace bl {
+namespace {
+
+constexpr uint32_t kCodeMask = 0x03030303u;
+constexpr int kMaxChunksPerLane = 8;
+
+// 4x4 byte transpose of 16 activations a[0..15] (given as 4 dwords, natural
+// order) into the order the shifted code masks produce: out[j] holds
+// a[j], a[4+j], a[8+j], a[12+j].
+__device__ __forceinline__ void permute16(const uint4 v, uint32_t out[4])
+{
+    const uint32_t t01lo = __builtin_amdgcn_perm(v.y, v.x, 0x05010400u);  // a0 a4 a1 a5
+    const uint32_t t01hi = __builtin_amdgcn_perm(v.y, v.x, 0x07030602u);  // a2 a6 a3 a7
+    const uint32_t t23lo = __builtin_amdgcn_perm(v.w, v.z, 0x05010400u);  // a8 a12 a9 a13
+    const uint32_t t23hi = __builtin_amdgcn_perm(v.w, v.z, 0x07030602u);  // a10 a14 a11 a15
+    out[0] = __builtin_amdgcn_perm(t23lo, t01lo, 0x05040100u);            // a0 a4 a8 a12
+    out[1] = __builtin_amdgcn_perm(t23lo, t01lo, 0x07060302u);            // a1 a5 a9 a13
+    out[2] = __builtin_amdgcn_perm(t23hi, t01hi, 0x05040100u);            // a2 a6 a10 a14
+    out[3] = __builtin_amdgcn_perm(t23hi, t01hi, 0x07060302u);            // a3 a7 a11 a15
+}
+
+// The 64 activations of chunk `ch` of token row qr, permuted (16 dwords).
+__device__ __forceinline__ void load_q_chunk(const int8_t* qr, int ch, uint32_t out[16])
+{
+    const uint4* src = reinterpret_cast<const uint4*>(qr + (size_t)ch * 64);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) permute16(src[g], out + 4 * g);
+}
+
+// sum over one 16-byte chunk (64 weights) of code * activation.
+__device__ __forceinline__ int dot_chunk(const uint4 w, const uint32_t* qp, int acc)
+{
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t c = (wd[g] >> (2 * j)) & kCodeMask;
+            acc = __builtin_amdgcn_sdot4((int)c, (int)qp[4 * g + j], acc, false);
+        }
+    }
+    return acc;
+}
+
+template <int L>
+__device__ __forceinline__ int group_sum(int v)
+{
+#pragma unroll
+    for (int off = L / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__device__ __forceinline__ float dequant(int acc, int qsum, float inv) { return (float)(acc - qsum) * inv; }
+
+// Loads of one packed row: lane j of the group takes chunks j, j+L, ...
+template <int L>
+__device__ __forceinline__ void load_row(const uint8_t* rowp, bool valid, int lane_in_group, int chunks,
+                                         uint4 w[kMaxChunksPerLane])
+{
+#pragma unroll
+    for (int c = 0; c < kMaxChunksPerLane; ++c) {
+        const int ch = lane_in_group + c * L;
+        w[c] = (valid && ch < chunks) ? *reinterpret_cast<const uint4*>(rowp + (size_t)ch * 16) : make_uint4(0, 0, 0, 0);
+    }
+}
+
+// Per-lane partial sums of code * activation over the loaded chunks, for all
+// m tokens. For m == 1 the activations live in registers (qreg, loaded once
+// per lane); otherwise they are read and permuted per row.
+template <int L, int M>
+__device__ __forceinline__ void dot_row(const uint4 w[kMaxChunksPerLane], int lane_in_group, int chunks,
+                                        const int8_t* q, int k, const uint32_t (*qreg)[16], int acc[M])
+{
+#pragma unroll
+    for (int mm = 0; mm < M; ++mm) acc[mm] = 0;
+#pragma unroll
+    for (int c = 0; c < kMaxChunksPerLane; ++c) {
+        const int ch = lane_in_group + c * L;
+        if (ch < chunks) {
+            if (M == 1) {
+                acc[0] = dot_chunk(w[c], qreg[c], acc[0]);
+            } else {
+#pragma unroll
+                for (int mm = 0; mm < M; ++mm) {
+                    uint32_t qp[16];
+                    load_q_chunk(q + (size_t)mm * k, ch, qp);
+                    acc[mm] = dot_chunk(w[c], qp, acc[mm]);
+                }
+            }
+        }
+    }
+}
+
+template <int L, int M>
+__device__ __forceinline__ void load_qreg(const int8_t* q, int lane_in_group, int chunks, uint32_t qreg[][16])
+{
+    if (M != 1) return;
+#pragma unroll
+    for (int c = 0; c < kMaxChunksPerLane; ++c) {
+        const int ch = lane_in_group + c * L;
+        if (ch < chunks) load_q_chunk(q, ch, qreg[c]);
+    }
+}
+
+// ---- single matrix ---------------------------------------------------------
+template <int L, int M>
+__global__ __launch_bounds__(64) void gemv_kernel(const uint8_t* __restrict__ packed, float w_scale,
+                                                  const float* __restrict__ w_scale_ptr, int n, int k,
+                                                  const int8_t* __restrict__ q, const float* __restrict__ act_scale,
+                                                  const int32_t* __restrict__ act_sum,
+                                                  const float* residual, float* y, int32_t* __restrict__ acc_out)
+{
+    constexpr int R = 64 / L;
+    const int lane = threadIdx.x;
+    const int g = lane / L, j = lane % L;
+    const int chunks = k / 64;
+    const size_t row_bytes = (size_t)k / 4;
+    uint32_t qreg[M == 1 ? kMaxChunksPerLane : 1][16];
+    load_qreg<L, M>(q, j, chunks, qreg);
+    const float ws = w_scale_ptr ? *w_scale_ptr : w_scale;
+    for (int base = blockIdx.x * R; base < n; base += gridDim.x * R) {
+        const int row = base + g;
+        const bool valid = row < n;
+        uint4 w[kMaxChunksPerLane];
+        load_row<L>(packed + (size_t)row * row_bytes, valid, j, chunks, w);
+        int acc[M];
+        dot_row<L, M>(w, j, chunks, q, k, qreg, acc);
+#pragma unroll
+        for (int mm = 0; mm < M; ++mm) acc[mm] = group_sum<L>(acc[mm]);
+        if (valid && j == 0) {
+#pragma unroll
+            for (int mm = 0; mm < M; ++mm) {
+                const int total = acc[mm] - act_sum[mm];
+                const float inv = 1.0f / (act_scale[mm] * ws);
+                float v = (float)total * inv;
+                const size_t o = (size_t)mm * n + row;
+                if (residual) v = residual[o] + v;
+                y[o] = v;
+                if (acc_out) acc_out[o] = total;
+            }
+        }
+    }
+}
+
+// ---- several matrices of equal shape sharing the activations (q, k, v) ----
+struct MultiPtrs {
+    const uint8_t* p[4];
+};
+
+template <int L, int M>
+__global__ __launch_bounds__(64) void gemv_multi_kernel(MultiPtrs mats, int count, const float* __restrict__ w_scale_ptr,
+                                                        int n, int k, const int8_t* __restrict__ q,
+                                                        const float* __restrict__ act_scale,
+                                                        const int32_t* __restrict__ act_sum, float* __restrict__ y,
+                                                        int ldy)
+{
+    constexpr int R = 64 / L;
+    const int lane = threadIdx.x;
+    const int g = lane / L, j = lane % L;
+    const int chunks = k / 64;
+    const size_t row_bytes = (size_t)k / 4;
+    const int total_rows = n * count;
+    uint32_t qreg[M == 1 ? kMaxChunksPerLane : 1][16];
+    load_qreg<L, M>(q, j, chunks, qreg);
+    for (int base = blockIdx.x * R; base < total_rows; base += gridDim.x * R) {
+        const int r = base + g;
+        const bool valid = r < total_rows;
+        const int mat = valid ? r / n : 0;
+        const int row = valid ? r - mat * n : 0;
+        const uint8_t* P = mats.p[0];
+#pragma unroll
+        for (int i = 1; i < 4; ++i)
+            if (mat == i) P = mats.p[i];
+        uint4 w[kMaxChunksPerLane];
+        load_row<L>(P + (size_t)row * row_bytes, valid, j, chunks, w);
+        int acc[M];
+        dot_row<L, M>(w, j, chunks, q, k, qreg, acc);
+#pragma unroll
+        for (int mm = 0; mm < M; ++mm) acc[mm] = group_sum<L>(acc[mm]);
+        if (valid && j == 0) {
+            const float ws = w_scale_ptr[mat];
+#pragma unroll
+            for (int mm = 0; mm < M; ++mm) {
+                const float inv = 1.0f / (act_scale[mm] * ws);
+                y[(size_t)mm * ldy + (size_t)mat * n + row] = dequant(acc[mm], act_sum[mm], inv);
+            }
+        }
+    }
+}
+
+// ---- fused gate/up with relu(gate)^2 * up --------------------------------------
+template <int L, int M>
+__global__ __launch_bounds__(64) void gateup_kernel(const uint8_t* __restrict__ w_gate, float s_gate,
+                                                    const uint8_t* __restrict__ w_up, float s_up,
+                                                    const float* __restrict__ scale_ptr, int f, int d,
+                                                    const int8_t* __restrict__ q, const float* __restrict__ act_scale,
+                                                    const int32_t* __restrict__ act_sum, float* __restrict__ h,
+                                                    int32_t* __restrict__ acc_gate, int32_t* __restrict__ acc_up)
+{
+    constexpr int R = 64 / L;
+    const int lane = threadIdx.x;
+    const int g = lane / L, j = lane % L;
+    const int chunks = d / 64;
+    const size_t row_bytes = (size_t)d / 4;
+    uint32_t qreg[M == 1 ? kMaxChunksPerLane : 1][16];
+    load_qreg<L, M>(q, j, chunks, qreg);
+    const float sg = scale_ptr ? scale_ptr[0] : s_gate;
+    const float su = scale_ptr ? scale_ptr[1] : s_up;
+    for (int base = blockIdx.x * R; base < f; base += gridDim.x * R) {
+        const int row = base + g;
+        const bool valid = row < f;
+        uint4 wg[kMaxChunksPerLane], wu[kMaxChunksPerLane];
+        load_row<L>(w_gate + (size_t)row * row_bytes, valid, j, chunks, wg);
+        load_row<L>(w_up + (size_t)row * row_bytes, valid, j, chunks, wu);
+        int ag[M], au[M];
+        dot_row<L, M>(wg, j, chunks, q, d, qreg, ag);
+        dot_row<L, M>(wu, j, chunks, q, d, qreg, au);
+#pragma unroll
+        for (int mm = 0; mm < M; ++mm) {
+            ag[mm] = group_sum<L>(ag[mm]);
+            au[mm] = group_sum<L>(au[mm]);
+        }
+        if (valid && j == 0) {
+#pragma unroll
+            for (int mm = 0; mm < M; ++mm) {
+                const int tg = ag[mm] - act_sum[mm], tu = au[mm] - act_sum[mm];
+                const float gate = (float)tg * (1.0f / (act_scale[mm] * sg));
+                const float up = (float)tu * (1.0f / (act_scale[mm] * su));
+                const float gp = gate > 0.0f ? gate : 0.0f;
+                const float g2 = gp * gp;
+                const size_t o = (size_t)mm * f + row;
+                h[o] = g2 * up;
+                if (acc_gate) acc_gate[o] = tg;
+                if (acc_up) acc_up[o] = tu;
+            }
+        }
+    }
+}
+
+// Lanes per row so that every lane holds at most kMaxChunksPerLane chunks.
+inline int pick_lanes(int k)
+{
+    const int chunks = k / 64;
+    if (chunks <= 8 * kMaxChunksPerLane) return 8;
+    if (chunks <= 16 * kMaxChunksPerLane) return 16;
+    if (chunks <= 32 * kMaxChunksPerLane) return 32;
+    return 64;
+}
+
+inline int grid_for(int rows, int lanes)
+{
+    const int per_block = 64 / lanes;
+    const int blocks = (rows + per_block - 1) / per_block;
+    return blocks < 8192 ? blocks : 8192;
+}
+
+#define BL_DISPATCH_M(MACRO, LVAL)                     \
+    switch (m) {                                      \
+    case 1: MACRO(LVAL, 1); break;                    \
+    case 2: MACRO(LVAL, 2); break;                    \
+    case 3: MACRO(LVAL, 3); break;                    \
+    case 4: MACRO(LVAL, 4); break;                    \
+    case 5: MACRO(LVAL, 5); break;                    \
+    case 6: MACRO(LVAL, 6); break;                    \
+    case 7: MACRO(LVAL, 7); break;                    \
+    default: MACRO(LVAL, 8); break;                   \
+    }
+
+#define BL_DISPATCH_L(MACRO)                           \
+    switch (lanes) {                                  \
+    case 8: BL_DISPATCH_M(MACRO, 8); break;            \
+    case 16: BL_DISPATCH_M(MACRO, 16); break;          \
+    case 32: BL_DISPATCH_M(MACRO, 32); break;          \
+    default: BL_DISPATCH_M(MACRO, 64); break;          \
+    }
+
+}  // namespace
+
+int launch_gemv(const uint8_t* packed, float w_scale, const float* w_scale_ptr, int n, int k, const int8_t* q,
+                const float* act_scale, const int32_t* act_sum, int m, const float* residual, float* y,
+                int32_t* acc_out, hipStream_t s)
+{
+    const int lanes = pick_lanes(k);
+    const int grid = grid_for(n, lanes);
+#define BL_LAUNCH(LV, MV)                                                                                    \
+    gemv_kernel<LV, MV><<<grid, 64, 0, s>>>(packed, w_scale, w_scale_ptr, n, k, q, act_scale, act_sum, residual, \
+                                            y, acc_out)
+    BL_DISPATCH_L(BL_LAUNCH)
+#undef BL_LAUNCH
+    return hipGetLastError() == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
+}
+
+int launch_gemv_multi(int count, const uint8_t* const* packed, const float* w_scale_ptr, int n_each, int k,
+                      const int8_t* q, const float* act_scale, const int32_t* act_sum, int m, float* y, int ldy,
+                      hipStream_t s)
+{
+    MultiPtrs mats{};
+    for (int i = 0; i < 4; ++i) mats.p[i] = packed[i < count ? i : 0];
+    const int lanes = pick_lanes(k);
+    const int grid = grid_for(n_each * count, lanes);
+#define BL_LAUNCH(LV, MV)                                                                                 \
+    gemv_multi_kernel<LV, MV><<<grid, 64, 0, s>>>(mats, count, w_scale_ptr, n_each, k, q, act_scale, act_sum, \
+                                                  y, ldy)
+    BL_DISPATCH_L(BL_LAUNCH)
+#undef BL_LAUNCH
+    return hipGetLastError() == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
+}
+
+int launch_gateup(const uint8_t* w_gate, float s_gate, const uint8_t* w_up, float s_up, const float* scale_ptr, int f,
+                  int d, const int8_t* q, const float* act_scale, const int32_t* act_sum, int m, float* h,
+                  int32_t* acc_gate, int32_t* acc_up, hipStream_t s)
+{
+    const int lanes = pick_lanes(d);
+    const int grid = grid_for(f, lanes);
+#define BL_LAUNCH(LV, MV)                                                                                    \
+    gateup_kernel<LV, MV><<<grid, 64, 0, s>>>(w_gate, s_gate, w_up, s_up, scale_ptr, f, d, q, act_scale, act_sum, \
+                                              h, acc_gate, acc_up)
+    BL_DISPATCH_L(BL_LAUNCH)
+#undef BL_LAUNCH
+    return hipGetLastError() == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
+}
+
+}  // namespace bl

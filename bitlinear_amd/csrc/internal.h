@@ -1,0 +1,49 @@
+// internal.h -- shared declarations of the HIP library (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/bitlinear.h"
+
+namespace bl {
+
+// Launchers (defined in the .hip files). They assume validated arguments and
+// return BL_OK or BL_ERR_LAUNCH.
+
+// [RMSNorm +] activation quant, one workgroup per token.
+int launch_quant_act(const float* x, const float* gain, float eps, int m, int k, int8_t* q,
+                     float* act_scale, int32_t* act_sum, hipStream_t s);
+
+// Decode GEMV, m in [1, 8]. The weight scale is read from w_scale_ptr when it
+// is non-null, else w_scale is used.
+int launch_gemv(const uint8_t* packed, float w_scale, const float* w_scale_ptr, int n, int k, const int8_t* q,
+                const float* act_scale, const int32_t* act_sum, int m, const float* residual, float* y,
+                int32_t* acc_out, hipStream_t s);
+
+// Several GEMVs sharing one activation vector, in one launch (used for q/k/v):
+// matrix j has n_rows[j] rows starting at packed[j]; outputs go to
+// y + j * n_rows[0] (row stride ldy per token).
+int launch_gemv_multi(int count, const uint8_t* const* packed, const float* w_scale_ptr, int n_each, int k,
+                      const int8_t* q, const float* act_scale, const int32_t* act_sum, int m, float* y,
+                      int ldy, hipStream_t s);
+
+// Fused gate/up GEMV with the relu(gate)^2 * up epilogue, m in [1, 8].
+int launch_gateup(const uint8_t* w_gate, float s_gate, const uint8_t* w_up, float s_up,
+                  const float* scale_ptr /* [2] or null */, int f, int d, const int8_t* q,
+                  const float* act_scale, const int32_t* act_sum, int m, float* h, int32_t* acc_gate,
+                  int32_t* acc_up, hipStream_t s);
+
+// MFMA GEMM. y, residual and acc_out have row stride ldy (>= n). key_ws: m
+// uint64 argmax keys (only with row_argmax).
+int launch_gemm(const uint8_t* packed, float w_scale, const float* w_scale_ptr, int n, int k, const int8_t* q,
+                const float* act_scale, const int32_t* act_sum, int m, const float* residual, float* y, int ldy,
+                int32_t* acc_out, int32_t* row_argmax, unsigned long long* key_ws, hipStream_t s);
+
+// h = relu(gate)^2 * up, elementwise.
+int launch_relu2_mul(const float* gate, const float* up, int64_t count, float* h, hipStream_t s);
+
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace bl

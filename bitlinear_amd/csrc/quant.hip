@@ -1,0 +1,122 @@
+// quant.hip -- fused RMSNorm + per-token absmax activation quant.
+//
+// RMSNorm in front of every BitLinear ("Add Support for BitNet Architecture
+// Inference", candle PR 2664) and the per-token absmax int8 quantizer of the
+// b1.58 method that the same PR names activation_quant. One 256-thread
+// workgroup per token:
+//   pass 1 (with a gain): thread t accumulates x[k]^2 in fp64 for k = t, t+256, ...
+//          in ascending k, then the 256 partials are combined by an
+//          xor-butterfly (offsets 128 and 64 through LDS, 32..1 inside the wave):
+//          the fixed order every implementation of this ABI uses;
+//          r = fl32(1 / sqrt(ss / k + eps)) in fp64.
+//   pass 2: y = fl32(fl32(x * r) * g) and absmax over the row.
+//   pass 3: s_a = fl32(127 / max(absmax, 1e-5)), q = clamp(rne(y * s_a)), sum(q).
+// Passes 2 and 3 each re-read the row (an L2 hit after pass 1) and recompute y
+// identically, so no fp32 row has to be stored.
+#include "internal.h"
+
+namespace bl {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ int quant_one(float y, float scale)
+{
+    const float r = rintf(y * scale);
+    return (int)fminf(fmaxf(r, -128.0f), 127.0f);
+}
+
+template <bool kNorm>
+__device__ __forceinline__ float4 normed(const float* xr, const float* gain, float r, int i)
+{
+    const float4 xv = *reinterpret_cast<const float4*>(xr + i);
+    if (!kNorm) return xv;
+    const float4 gv = *reinterpret_cast<const float4*>(gain + i);
+    float4 y;
+    y.x = (xv.x * r) * gv.x;
+    y.y = (xv.y * r) * gv.y;
+    y.z = (xv.z * r) * gv.z;
+    y.w = (xv.w * r) * gv.w;
+    return y;
+}
+
+template <bool kNorm>
+__global__ __launch_bounds__(kThreads) void quant_act_kernel(const float* __restrict__ x,
+                                                             const float* __restrict__ gain, float eps, int k,
+                                                             int8_t* __restrict__ q, float* __restrict__ act_scale,
+                                                             int32_t* __restrict__ act_sum)
+{
+    const int row = blockIdx.x;
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = t >> 6;
+    const float* xr = x + (size_t)row * k;
+    __shared__ double part[kThreads];
+    __shared__ float wmax[kThreads / 64];
+    __shared__ int wsum[kThreads / 64];
+
+    float r = 1.0f;
+    if (kNorm) {
+        double p = 0.0;
+        for (int i = t; i < k; i += kThreads) {
+            const double v = (double)xr[i];
+            p += v * v;  // exact square; any fusion rounds the same way
+        }
+        part[t] = p;
+        __syncthreads();
+        p = p + part[t ^ 128];
+        __syncthreads();
+        part[t] = p;
+        __syncthreads();
+        p = p + part[t ^ 64];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) p = p + __shfl_xor(p, off, 64);
+        r = (float)(1.0 / sqrt(p / (double)k + (double)eps));
+    }
+
+    float amax = 0.0f;
+    for (int i = 4 * t; i < k; i += 4 * kThreads) {
+        const float4 y = normed<kNorm>(xr, gain, r, i);
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(y.x), fabsf(y.y)), fmaxf(fabsf(y.z), fabsf(y.w))));
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    if (lane == 0) wmax[wave] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    const float scale = 127.0f / fmaxf(amax, 1e-5f);
+
+    int sum = 0;
+    int8_t* qr = q + (size_t)row * k;
+    for (int i = 4 * t; i < k; i += 4 * kThreads) {
+        const float4 y = normed<kNorm>(xr, gain, r, i);
+        const int q0 = quant_one(y.x, scale), q1 = quant_one(y.y, scale);
+        const int q2 = quant_one(y.z, scale), q3 = quant_one(y.w, scale);
+        sum += q0 + q1 + q2 + q3;
+        const uint32_t packed = (uint32_t)(q0 & 0xff) | ((uint32_t)(q1 & 0xff) << 8) |
+                                ((uint32_t)(q2 & 0xff) << 16) | ((uint32_t)(q3 & 0xff) << 24);
+        *reinterpret_cast<uint32_t*>(qr + i) = packed;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+    if (lane == 0) wsum[wave] = sum;
+    __syncthreads();
+    if (t == 0) {
+        act_scale[row] = scale;
+        if (act_sum) act_sum[row] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    }
+}
+
+}  // namespace
+
+int launch_quant_act(const float* x, const float* gain, float eps, int m, int k, int8_t* q, float* act_scale,
+                     int32_t* act_sum, hipStream_t s)
+{
+    if (gain)
+        quant_act_kernel<true><<<m, kThreads, 0, s>>>(x, gain, eps, k, q, act_scale, act_sum);
+    else
+        quant_act_kernel<false><<<m, kThreads, 0, s>>>(x, gain, eps, k, q, act_scale, act_sum);
+    return hipGetLastError() == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
+}
+
+}  // namespace bl

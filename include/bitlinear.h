@@ -1,0 +1,226 @@
+/*
+ * bitlinear.h -- C ABI of the BitNet b1.58 BitLinear hot path on MI355X (gfx950).
+ *
+ * A BitLinear multiplies ternary weights t in {-1, 0, +1} by 8-bit activations:
+ *   - weights are stored 2-bit packed, four per byte (the TQ2_0 size of 0.25 byte
+ *     per weight: "BitNet Model - Complete Inference Pipeline", Hesper API,
+ *     section "Memory Footprint (BitNet-3B with TQ2_0)"), with one fp32 scale
+ *     s_w = 1/mean|W| per tensor (the weight_quant of "Add Support for BitNet
+ *     Architecture Inference", candle PR 2664);
+ *   - activations are quantized per token: an optional RMSNorm (the same PR puts
+ *     one in front of every BitLinear), then absmax scaling to 127, rounding and
+ *     clamping to int8 (its activation_quant);
+ *   - the product is accumulated exactly in int32 and rescaled once in fp32 by
+ *     1/(s_a * s_w).
+ * The FFN entry point follows "Transformer Block" (Hesper API,
+ * Layers.TransformerBlock), sections "Feed-Forward Network (FFN)" and
+ * "Forward Pass" steps 4-8, with the ffnSubNorm of "Layer Structure".
+ *
+ * Layouts (row-major, no padding):
+ *   W       : t[n][k], n = output features, k = input features (k contiguous).
+ *   packed  : uint8 [n][k/4]; byte i of row r holds weights k = 4i..4i+3 as
+ *             2-bit codes c = t + 1 in {0, 1, 2}, least significant field first
+ *             (field j at bits 2j..2j+1). Code 3 never appears.
+ *   x, y    : fp32 [m][k] / [m][n], one row per token.
+ *   q       : int8 [m][k]; act_scale fp32 [m] (= 127/absmax of the normed row);
+ *   act_sum : int32 [m], the sum of the row's q (the kernels use it: they
+ *             multiply codes c = t + 1 and subtract act_sum).
+ *
+ * Numerics (identical on every entry point):
+ *   RMSNorm  r = fl32(1 / sqrt(ss/k + eps)) in fp64, ss = fp64 sum of x^2 in a
+ *            fixed order (256 strided partials, then an xor-butterfly over the
+ *            partials with offsets 128, 64, ..., 1); y = fl32(fl32(x * r) * g).
+ *   quant    s_a = fl32(127 / max(absmax(y), 1e-5)); q = clamp(rne(fl32(y*s_a)),
+ *            -128, 127) with round-half-to-even.
+ *   dequant  inv = fl32(1 / fl32(s_a * s_w)); y = fl32((float)acc * inv);
+ *            with a residual: y = fl32(residual + fl32((float)acc * inv)).
+ *   FFN      h = fl32(fl32(relu(gate)^2) * up).
+ *
+ * Conventions:
+ *   - Every pointer marked "device" is caller-owned device memory (for example
+ *     a torch tensor's data pointer). The library never allocates, frees or
+ *     retains memory, never synchronises, and never reads device memory on the
+ *     host. Host pointers are read/written only during the call.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Device
+ *     calls are asynchronous on it and may be captured into a HIP graph; the
+ *     pointers must then stay valid for the life of the graph.
+ *   - Status codes: 0 = BL_OK, negative = error. All argument checks happen on
+ *     the host before any launch; on an error nothing is launched or written.
+ *     A kernel launch failure returns BL_ERR_LAUNCH; faults inside a kernel
+ *     surface at the caller's next synchronisation.
+ *   - Device calls need k % 64 == 0 (packed rows are whole 16-byte chunks),
+ *     16-byte aligned packed/q pointers and 4-byte aligned fp32/int32 pointers.
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BL_OK 0
+#define BL_ERR_NULL (-1)      /* a required pointer is NULL */
+#define BL_ERR_SHAPE (-2)     /* a size is <= 0, not a multiple of what the call needs, or too large */
+#define BL_ERR_ALIGN (-3)     /* a pointer is not aligned as stated above */
+#define BL_ERR_VALUE (-4)     /* a value is out of range (a weight outside {-1,0,1}, a non-finite input) */
+#define BL_ERR_WORKSPACE (-5) /* the workspace is smaller than the matching *_workspace_bytes() */
+#define BL_ERR_LAUNCH (-6)    /* a kernel launch failed (hipGetLastError after the launch) */
+#define BL_ERR_DEVICE (-7)    /* no usable gfx950 device, or a HIP runtime call failed */
+
+/* ABI version of this header (bumped on any incompatible change). */
+int bitlinear_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char *bitlinear_strerror(int status);
+
+/* ---------------------------------------------------------------- host --- */
+
+/* Ternary packer (TQ2_0, layout above). Host memory only.
+ *   t      : host int8 [n][k], every value in {-1, 0, 1}.
+ *   packed : host uint8 [n][k/4], written in full on success.
+ * Errors: BL_ERR_NULL; BL_ERR_SHAPE if n <= 0, k <= 0 or k % 4 != 0;
+ *         BL_ERR_VALUE if any t is outside {-1, 0, 1} (nothing is written). */
+int bitlinear_pack(const int8_t *t, int64_t n, int64_t k, uint8_t *packed);
+
+/* weight_quant of the b1.58 method on the host: s_w = fl32(1 / max(mean|W|, 1e-5))
+ * with mean|W| an fp64 sum in row-major order over n*k, then
+ * t = clamp(rne(fl32(W * s_w)), -1, 1).
+ *   w : host fp32 [n][k]; t : host int8 [n][k]; w_scale : host fp32 [1].
+ * Errors: BL_ERR_NULL; BL_ERR_SHAPE (n, k <= 0); BL_ERR_VALUE (non-finite W). */
+int bitlinear_weight_quant(const float *w, int64_t n, int64_t k, int8_t *t, float *w_scale);
+
+/* -------------------------------------------------------------- device --- */
+
+/* [RMSNorm(gain, eps) +] per-token absmax activation quant.
+ *   x         : device fp32 [m][k].
+ *   gain      : device fp32 [k], or NULL for no RMSNorm (q quantizes x itself).
+ *   eps       : RMSNorm epsilon (ignored when gain is NULL), widened to fp64.
+ *   q         : device int8 [m][k]; act_scale : device fp32 [m];
+ *   act_sum   : device int32 [m] or NULL.
+ * One workgroup per token. Errors: NULL, SHAPE (m, k <= 0, k % 64 != 0),
+ * ALIGN, LAUNCH. Non-finite x is out of contract (results unspecified). */
+int bitlinear_quant_act(const float *x, const float *gain, float eps, int64_t m, int64_t k,
+                        int8_t *q, float *act_scale, int32_t *act_sum, void *stream);
+
+/* Decode GEMV, m in [1, 8]: y[m][n] = [residual +] dequant(P . q).
+ *   packed    : device uint8 [n][k/4], 16-byte aligned.
+ *   w_scale   : the tensor's s_w (> 0).
+ *   q, act_scale, act_sum : from bitlinear_quant_act (act_sum is required).
+ *   residual  : device fp32 [m][n] or NULL; may alias y.
+ *   y         : device fp32 [m][n].
+ *   acc_out   : device int32 [m][n] (the exact accumulators) or NULL.
+ * Streams the packed weights with 16-byte loads; codes are unpacked in
+ * registers and multiplied with 4-way int8 dot products, reduced across lanes.
+ * Errors: NULL, SHAPE (m outside [1, 8], n <= 0, k % 64 != 0, k > 32768),
+ * ALIGN, VALUE (w_scale not > 0), LAUNCH. */
+int bitlinear_gemv(const uint8_t *packed, float w_scale, int64_t n, int64_t k,
+                   const int8_t *q, const float *act_scale, const int32_t *act_sum, int64_t m,
+                   const float *residual, float *y, int32_t *acc_out, void *stream);
+
+/* Workspace bytes bitlinear_gemm needs (0 unless a per-row argmax is asked for). */
+size_t bitlinear_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int with_argmax);
+
+/* GEMM on int8 matrix cores (prefill, batched decode, ternary LM head):
+ * y[m][n] = [residual +] dequant(q . P^T), optional fused per-row argmax.
+ *   packed, w_scale, q, act_scale, act_sum : as bitlinear_gemv; any m >= 1.
+ *   residual   : device fp32 [m][n] or NULL (may alias y).
+ *   y          : device fp32 [m][n], or NULL when row_argmax is given (logits
+ *                are then not written).
+ *   acc_out    : device int32 [m][n] or NULL.
+ *   row_argmax : device int32 [m] or NULL: per row, the lowest n holding the
+ *                largest accumulator (the same as the first argmax of y, since
+ *                the rescale is monotone and exact on distinct integers).
+ *   workspace  : device memory of bitlinear_gemm_workspace_bytes(m, n, k, 1)
+ *                bytes (8-byte aligned) when row_argmax is given, else unused.
+ * Ternary tiles are unpacked in registers from a packed LDS tile; the int8
+ * activation tile is staged in LDS; products run on v_mfma_i32_32x32x32_i8.
+ * Errors: NULL (y and row_argmax both NULL, ...), SHAPE, ALIGN, VALUE,
+ * WORKSPACE, LAUNCH. */
+int bitlinear_gemm(const uint8_t *packed, float w_scale, int64_t n, int64_t k,
+                   const int8_t *q, const float *act_scale, const int32_t *act_sum, int64_t m,
+                   const float *residual, float *y, int32_t *acc_out, int32_t *row_argmax,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* BitNet FFN sub-layer without the residual of the block (pass `residual` to
+ * add one):
+ *   q1  = quant(rmsnorm(x, norm_gain))                       [m][d]
+ *   gate, up = dequant(W_gate . q1), dequant(W_up . q1)       [m][f]
+ *   h   = relu(gate)^2 * up                                   [m][f]
+ *   q2  = quant(rmsnorm(h, sub_norm_gain))                    [m][f]
+ *   out = [residual +] dequant(W_down . q2)                   [m][d]
+ *   x           : device fp32 [m][d].
+ *   norm_gain   : device fp32 [d];  sub_norm_gain : device fp32 [f].
+ *   w_gate, w_up: device packed [f][d/4];  w_down : device packed [d][f/4].
+ *   s_gate, s_up, s_down : weight scales.
+ *   residual    : device fp32 [m][d] or NULL (may alias out).
+ *   out         : device fp32 [m][d].
+ *   workspace   : device, >= bitnet_ffn_workspace_bytes(m, d, f), 256-byte
+ *                 aligned; holds every intermediate at the offsets given by
+ *                 bitnet_ffn_workspace_offset().
+ *   flags       : BITNET_FFN_WRITE_ACC also stores acc_gate, acc_up, acc_down.
+ * For m <= 8 gate and up run in one launch that streams both weight matrices
+ * and applies relu(gate)^2 * up in its epilogue. d and f must be multiples
+ * of 64. Errors: NULL, SHAPE, ALIGN, VALUE, WORKSPACE, LAUNCH. */
+#define BITNET_FFN_WRITE_ACC 1
+enum bitnet_ffn_ws_segment {
+    BITNET_FFN_WS_Q1 = 0,    /* int8  [m][d] */
+    BITNET_FFN_WS_S1,        /* fp32  [m]    */
+    BITNET_FFN_WS_QS1,       /* int32 [m]    */
+    BITNET_FFN_WS_H,         /* fp32  [m][f] */
+    BITNET_FFN_WS_Q2,        /* int8  [m][f] */
+    BITNET_FFN_WS_S2,        /* fp32  [m]    */
+    BITNET_FFN_WS_QS2,       /* int32 [m]    */
+    BITNET_FFN_WS_ACC_GATE,  /* int32 [m][f] (with BITNET_FFN_WRITE_ACC) */
+    BITNET_FFN_WS_ACC_UP,    /* int32 [m][f] (with BITNET_FFN_WRITE_ACC) */
+    BITNET_FFN_WS_ACC_DOWN,  /* int32 [m][d] (with BITNET_FFN_WRITE_ACC) */
+    BITNET_FFN_WS_GATE,      /* fp32  [m][f] (used when m > 8) */
+    BITNET_FFN_WS_UP,        /* fp32  [m][f] (used when m > 8) */
+    BITNET_FFN_WS_COUNT
+};
+size_t bitnet_ffn_workspace_bytes(int64_t m, int64_t d, int64_t f);
+/* Byte offset of a segment inside the FFN workspace; (size_t)-1 for a bad segment. */
+size_t bitnet_ffn_workspace_offset(int64_t m, int64_t d, int64_t f, int segment);
+int bitnet_ffn(const float *x, int64_t m, int64_t d, int64_t f,
+               const float *norm_gain, const float *sub_norm_gain, float eps,
+               const uint8_t *w_gate, float s_gate, const uint8_t *w_up, float s_up,
+               const uint8_t *w_down, float s_down,
+               const float *residual, float *out, void *workspace, size_t workspace_bytes,
+               int flags, void *stream);
+
+/* Decoder-layer stream of BitLinears with attention math left out: for each
+ * layer l in order ("Transformer Block", "Forward Pass"; "Memory Layout" for
+ * the seven projections):
+ *   a      = quant(rmsnorm(x, g_attn))
+ *   q,k,v  = dequant(W_q . a), dequant(W_k . a), dequant(W_v . a)  -> qkv[l]
+ *   o_in   = quant(rmsnorm(z[l], g_attn_sub))   (z: stand-in for attention)
+ *   x      = x + dequant(W_o . o_in)
+ *   x      = x + ffn(x)                         (as bitnet_ffn)
+ * The projections run in that order, each after the one before it.
+ *   weights : device, n_layers consecutive layer blobs of bitnet_layer_bytes(d, f)
+ *             bytes; inside a blob the packed tensors W_q, W_k, W_v, W_o
+ *             ([d][d/4] each), W_gate, W_up ([f][d/4] each), W_down ([d][f/4])
+ *             follow each other with no gap.
+ *   scales  : device fp32 [n_layers][7] (q, k, v, o, gate, up, down).
+ *   gains   : device fp32 [n_layers][3d + f]: g_attn, g_attn_sub, g_ffn ([d]
+ *             each), g_ffn_sub ([f]).
+ *   z       : device fp32 [n_layers][m][d].
+ *   x       : device fp32 [m][d], updated in place.
+ *   qkv     : device fp32 [n_layers][m][3d] or NULL (then written to the
+ *             workspace and overwritten layer by layer).
+ *   workspace: device, >= bitnet_stream_workspace_bytes(m, d, f), 256-aligned.
+ * d and f must be multiples of 64; m >= 1.
+ * Errors: NULL, SHAPE, ALIGN, WORKSPACE, LAUNCH. */
+size_t bitnet_layer_bytes(int64_t d, int64_t f);
+size_t bitnet_stream_workspace_bytes(int64_t m, int64_t d, int64_t f);
+int bitnet_decode_stream(const uint8_t *weights, const float *scales, const float *gains, const float *z,
+                         int64_t n_layers, int64_t m, int64_t d, int64_t f, float eps,
+                         float *x, float *qkv, void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITLINEAR_H */

@@ -1,0 +1,209 @@
+"""C ABI on the CPU: the library loads without a GPU, exports every symbol of
+include/bitlinear.h, its host packer and weight_quant match the oracle bit for
+bit, and every argument check of the device entry points fires on the host
+before any launch (no device memory is touched: the pointers below are never
+dereferenced)."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bitlinear_amd as bl
+import oracle
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitlinear.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(\w+)\s*\(", text, flags=re.M)) - {"defined"})
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 14
+    for name in names:
+        assert hasattr(bl._lib, name), name
+    assert sorted(bl.EXPORTS) == names
+
+
+def test_abi_version_and_strerror():
+    assert bl.abi_version() == 1
+    for code in range(-7, 1):
+        assert bl.strerror(code) and bl.strerror(code) != "unknown status"
+    assert bl.strerror(-99) == "unknown status"
+
+
+# ---- packer / weight_quant vs oracle -----------------------------------------------
+
+@pytest.mark.parametrize("n,k,seed", [(1, 4, 0), (3, 8, 1), (17, 64, 2), (256, 2560, 3), (5, 10244, 4)])
+def test_pack_matches_oracle(n, k, seed, olib):
+    t = W.ternary(W.rng(90, seed, 0), n, k)
+    assert (bl.bitlinear_pack(t) == oracle.pack(t, olib)).all()
+
+
+def test_pack_adversarial_rows(olib):
+    import itertools
+    tuples = np.array(list(itertools.product((-1, 0, 1), repeat=4)), np.int8)
+    assert (bl.bitlinear_pack(tuples) == oracle.pack(tuples, olib)).all()
+    for fill in (-1, 0, 1):
+        t = np.full((7, 128), fill, np.int8)
+        assert (bl.bitlinear_pack(t) == oracle.pack(t, olib)).all()
+
+
+def test_pack_rejects_bad_input():
+    t = np.zeros((2, 8), np.int8)
+    t[1, 5] = 2
+    out = np.full((2, 2), 0xEE, np.uint8)
+    with pytest.raises(bl.BitlinearError) as e:
+        bl.bitlinear_pack(t, out)
+    assert e.value.status == bl.BL_ERR_VALUE
+    assert (out == 0xEE).all(), "nothing may be written on error"
+    with pytest.raises(bl.BitlinearError) as e:
+        bl.bitlinear_pack(np.zeros((2, 6), np.int8), np.zeros((2, 1), np.uint8))
+    assert e.value.status == bl.BL_ERR_SHAPE
+    assert bl._lib.bitlinear_pack(None, 1, 4, 16) == bl.BL_ERR_NULL
+
+
+@pytest.mark.parametrize("seed,sigma", [(0, 0.02), (1, 1.0), (2, 1e-3)])
+def test_weight_quant_matches_oracle(seed, sigma, olib):
+    w = W.random_fp32_weights(W.rng(91, seed, 0), 96, 320, sigma)
+    t1, s1 = bl.bitlinear_weight_quant(w)
+    t2, s2 = oracle.weight_quant(w, olib)
+    assert s1 == s2
+    assert (t1 == t2).all()
+
+
+def test_weight_quant_ties_and_zero(olib):
+    a = np.float32(0.125)
+    w = np.array([[a, -a, 3 * a, -3 * a]], np.float32)
+    for arr in (w, np.zeros((4, 8), np.float32)):
+        t1, s1 = bl.bitlinear_weight_quant(arr)
+        t2, s2 = oracle.weight_quant(arr, olib)
+        assert s1 == s2 and (t1 == t2).all()
+    bad = np.ones((2, 2), np.float32)
+    bad[0, 1] = np.nan
+    with pytest.raises(bl.BitlinearError) as e:
+        bl.bitlinear_weight_quant(bad)
+    assert e.value.status == bl.BL_ERR_VALUE
+
+
+# ---- argument checks of the device entry points (host only) -------------------------
+
+A = 1 << 20       # a 256-aligned fake address, never dereferenced
+U = A + 1         # misaligned
+S = None          # null stream
+
+
+def test_quant_act_checks():
+    f = bl._lib.bitlinear_quant_act
+    assert f(None, None, 1e-5, 1, 64, A, A, A, S) == bl.BL_ERR_NULL
+    assert f(A, None, 1e-5, 1, 64, None, A, A, S) == bl.BL_ERR_NULL
+    assert f(A, None, 1e-5, 1, 64, A, None, A, S) == bl.BL_ERR_NULL
+    assert f(A, None, 1e-5, 0, 64, A, A, A, S) == bl.BL_ERR_SHAPE
+    assert f(A, None, 1e-5, 1, 96, A, A, A, S) == bl.BL_ERR_SHAPE
+    assert f(A, None, 1e-5, 1, 0, A, A, A, S) == bl.BL_ERR_SHAPE
+    assert f(U, None, 1e-5, 1, 64, A, A, A, S) == bl.BL_ERR_ALIGN
+    assert f(A, A + 4, 1e-5, 1, 64, A, A, A, S) == bl.BL_ERR_ALIGN
+    assert f(A, None, 1e-5, 1, 64, A + 8, A, A, S) == bl.BL_ERR_ALIGN
+
+
+def test_gemv_checks():
+    f = bl._lib.bitlinear_gemv
+    ok = dict(p=A, s=40.0, n=16, k=64, q=A, sa=A, qs=A, m=1, r=None, y=A, acc=None)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return f(a["p"], a["s"], a["n"], a["k"], a["q"], a["sa"], a["qs"], a["m"], a["r"], a["y"], a["acc"], S)
+
+    assert call(p=None) == bl.BL_ERR_NULL
+    assert call(qs=None) == bl.BL_ERR_NULL
+    assert call(y=None) == bl.BL_ERR_NULL
+    assert call(m=0) == bl.BL_ERR_SHAPE
+    assert call(m=9) == bl.BL_ERR_SHAPE
+    assert call(k=100) == bl.BL_ERR_SHAPE
+    assert call(k=65536) == bl.BL_ERR_SHAPE
+    assert call(n=0) == bl.BL_ERR_SHAPE
+    assert call(p=A + 4) == bl.BL_ERR_ALIGN
+    assert call(q=A + 8) == bl.BL_ERR_ALIGN
+    assert call(y=U) == bl.BL_ERR_ALIGN
+    assert call(s=0.0) == bl.BL_ERR_VALUE
+    assert call(s=-3.0) == bl.BL_ERR_VALUE
+    assert call(s=float("inf")) == bl.BL_ERR_VALUE
+    assert call(s=float("nan")) == bl.BL_ERR_VALUE
+
+
+def test_gemm_checks():
+    f = bl._lib.bitlinear_gemm
+    ok = dict(p=A, s=40.0, n=16, k=64, q=A, sa=A, qs=A, m=3, r=None, y=A, acc=None, am=None, ws=None, wsb=0)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return f(a["p"], a["s"], a["n"], a["k"], a["q"], a["sa"], a["qs"], a["m"], a["r"], a["y"], a["acc"], a["am"],
+                 a["ws"], a["wsb"], S)
+
+    assert call(y=None) == bl.BL_ERR_NULL
+    assert call(am=A) == bl.BL_ERR_NULL           # argmax without workspace
+    assert call(am=A, ws=A, wsb=8) == bl.BL_ERR_WORKSPACE
+    assert bl.bitlinear_gemm_workspace_bytes(3, 16, 64, 1) >= 24
+    assert bl.bitlinear_gemm_workspace_bytes(3, 16, 64, 0) == 0
+    assert call(m=0) == bl.BL_ERR_SHAPE
+    assert call(k=32) == bl.BL_ERR_SHAPE
+    assert call(am=A, ws=A + 4, wsb=256) == bl.BL_ERR_ALIGN
+    assert call(s=0.0) == bl.BL_ERR_VALUE
+
+
+def test_ffn_checks():
+    f = bl._lib.bitnet_ffn
+    m, d, f_ = 1, 64, 128
+    need = bl.bitnet_ffn_workspace_bytes(m, d, f_)
+    ok = dict(x=A, m=m, d=d, f=f_, g=A, gs=A, eps=1e-5, wg=A, sg=1.0, wu=A, su=1.0, wd=A, sd=1.0, r=None, out=A,
+              ws=A, wsb=need, flags=0)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return f(a["x"], a["m"], a["d"], a["f"], a["g"], a["gs"], a["eps"], a["wg"], a["sg"], a["wu"], a["su"],
+                 a["wd"], a["sd"], a["r"], a["out"], a["ws"], a["wsb"], a["flags"], S)
+
+    assert call(g=None) == bl.BL_ERR_NULL
+    assert call(ws=None) == bl.BL_ERR_NULL
+    assert call(d=96) == bl.BL_ERR_SHAPE
+    assert call(f=100) == bl.BL_ERR_SHAPE
+    assert call(ws=A + 16) == bl.BL_ERR_ALIGN
+    assert call(wd=A + 4) == bl.BL_ERR_ALIGN
+    assert call(su=0.0) == bl.BL_ERR_VALUE
+    assert call(wsb=need - 1) == bl.BL_ERR_WORKSPACE
+
+
+def test_ffn_workspace_layout():
+    m, d, f = 3, 2560, 10240
+    total = bl.bitnet_ffn_workspace_bytes(m, d, f)
+    sizes = {"q1": m * d, "s1": 4 * m, "qs1": 4 * m, "h": 4 * m * f, "q2": m * f, "s2": 4 * m, "qs2": 4 * m,
+             "acc_gate": 4 * m * f, "acc_up": 4 * m * f, "acc_down": 4 * m * d, "gate": 4 * m * f, "up": 4 * m * f}
+    spans = []
+    for seg in bl.FFN_WS_SEGMENTS:
+        off = bl.bitnet_ffn_workspace_offset(m, d, f, seg)
+        assert off % 256 == 0
+        spans.append((off, off + sizes[seg]))
+    spans.sort()
+    for (a0, a1), (b0, _) in zip(spans, spans[1:]):
+        assert a1 <= b0, "segments overlap"
+    assert spans[-1][1] <= total
+    assert bl.bitnet_ffn_workspace_offset(m, d, f, 99) == 2 ** 64 - 1
+
+
+def test_stream_checks():
+    f = bl._lib.bitnet_decode_stream
+    m, d, ff = 1, 64, 128
+    need = bl.bitnet_stream_workspace_bytes(m, d, ff)
+    assert bl.bitnet_layer_bytes(2560, 10240) == 26_214_400
+    assert bl.bitnet_layer_bytes(2048, 8192) == 402_653_184 // 24
+    assert f(A, A, A, A, 2, m, d, ff, 1e-5, A, None, A, need - 1, S) == bl.BL_ERR_WORKSPACE
+    assert f(A, A, A, None, 2, m, d, ff, 1e-5, A, None, A, need, S) == bl.BL_ERR_NULL
+    assert f(A, A, A, A, 0, m, d, ff, 1e-5, A, None, A, need, S) == bl.BL_ERR_SHAPE
+    assert f(A, A, A, A, 2, m, 80, ff, 1e-5, A, None, A, need, S) == bl.BL_ERR_SHAPE
+    assert f(A + 8, A, A, A, 2, m, d, ff, 1e-5, A, None, A, need, S) == bl.BL_ERR_ALIGN

@@ -1,0 +1,234 @@
+"""HIP path vs the CPU oracle, element by element, through the C ABI.
+
+Sizes span several tiles with ragged tails; the full configurations of the
+benchmark are covered in test_gpu_full.py."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_helpers import assert_exact, assert_f32, log, pack_both, to_dev, to_host, torch_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def bl():
+    import bitlinear_amd
+    return bitlinear_amd
+
+
+def quant_gpu(bl, x, gain, eps):
+    import torch
+    m, k = x.shape
+    dev = torch_dev()
+    xd = to_dev(x)
+    gd = to_dev(gain) if gain is not None else None
+    q = torch.empty((m, k), dtype=torch.int8, device=dev)
+    s = torch.empty(m, dtype=torch.float32, device=dev)
+    qs = torch.empty(m, dtype=torch.int32, device=dev)
+    bl.bitlinear_quant_act(xd, gd, eps, q, s, qs)
+    return to_host(q), to_host(s), to_host(qs)
+
+
+# ---- activation quant ------------------------------------------------------------------
+
+QUANT_CASES = [(1, 64), (1, 2560), (1, 10240), (3, 192), (7, 640), (33, 2560), (5, 16384)]
+
+
+@pytest.mark.parametrize("norm", [False, True])
+@pytest.mark.parametrize("m,k", QUANT_CASES)
+def test_quant_act(bl, olib, m, k, norm):
+    log(f"quant_act m={m} k={k} norm={norm}")
+    g = W.rng(100, m, k)
+    x = W.activations(g, m, k, outliers=True) * np.float32(g.uniform(0.01, 50))
+    gain = W.gains(g, k) if norm else None
+    q, s, qs = quant_gpu(bl, x, gain, 1e-5)
+    oq, os_, oqs = oracle.quant_act(x, gain, 1e-5, olib)
+    assert_exact(q, oq, "q")
+    assert_exact(s.view(np.uint32), os_.view(np.uint32), "act_scale bits")
+    assert_exact(qs, oqs, "act_sum")
+
+
+def test_quant_act_special_rows(bl, olib):
+    """Ties at +-0.5 of a code, an all-zero row, a constant row, one huge outlier,
+    tiny values near the absmax floor."""
+    k = 256
+    rows = []
+    r = np.zeros(k, np.float32)
+    r[0] = 127.0
+    r[1:128] = np.arange(127, dtype=np.float32) + np.float32(0.5)   # every x.5 tie (s_a = 1)
+    r[128:255] = -(np.arange(127, dtype=np.float32) + np.float32(0.5))
+    rows.append(r)
+    rows.append(np.zeros(k, np.float32))
+    rows.append(np.full(k, -3.25, np.float32))
+    r = np.full(k, 1e-3, np.float32)
+    r[77] = 1e6
+    rows.append(r)
+    rows.append(np.full(k, 3e-6, np.float32))
+    x = np.stack(rows)
+    for gain in (None, np.ones(k, np.float32)):
+        q, s, qs = quant_gpu(bl, x, gain, 1e-5)
+        oq, os_, oqs = oracle.quant_act(x, gain, 1e-5, olib)
+        assert_exact(q, oq, "q")
+        assert_exact(s.view(np.uint32), os_.view(np.uint32), "act_scale bits")
+        assert_exact(qs, oqs, "act_sum")
+    assert q.min() > -128
+
+
+# ---- GEMV ---------------------------------------------------------------------------------
+
+GEMV_CASES = [(16, 64, 1), (40, 192, 1), (2560, 2560, 1), (10240, 2560, 1), (2560, 10240, 1), (7, 640, 1),
+              (13, 32768, 1), (100, 2048, 2), (333, 8192, 3), (64, 640, 5), (129, 2560, 8)]
+
+
+def _gemv_inputs(case_id, n, k, m, olib):
+    g = W.rng(101, case_id, 0)
+    t = W.ternary(g, n, k)
+    sw = W.weight_scale(g)
+    x = W.activations(g, m, k)
+    res = W.activations(g, m, n)
+    p = pack_both(t, olib)
+    q, s, qs = oracle.quant_act(x, None, 1e-5, olib)
+    return p, sw, q, s, qs, res
+
+
+@pytest.mark.parametrize("n,k,m", GEMV_CASES)
+def test_gemv(bl, olib, n, k, m):
+    import torch
+    log(f"gemv n={n} k={k} m={m}")
+    p, sw, q, s, qs, res = _gemv_inputs(n * 7 + k + m, n, k, m, olib)
+    dev = torch_dev()
+    y = torch.empty((m, n), dtype=torch.float32, device=dev)
+    acc = torch.empty((m, n), dtype=torch.int32, device=dev)
+    bl.bitlinear_gemv(to_dev(p), sw, n, k, to_dev(q), to_dev(s), to_dev(qs), m, None, y, acc)
+    oy, oacc = oracle.bitlinear(p, sw, k, q, s, olib)
+    assert_exact(to_host(acc), oacc, "acc")
+    assert_f32(to_host(y), oy, "y")
+    # residual, in place (y aliases the residual)
+    yr = to_dev(res)
+    bl.bitlinear_gemv(to_dev(p), sw, n, k, to_dev(q), to_dev(s), to_dev(qs), m, yr, yr, None)
+    assert_f32(to_host(yr), oracle.residual_add(res, oy, olib), "y + residual")
+
+
+# ---- GEMM ------------------------------------------------------------------------------------
+
+GEMM_CASES = [(1, 16, 64), (5, 100, 192), (32, 2048, 2048), (130, 200, 640), (256, 384, 2560), (37, 2560, 10240),
+              (300, 129, 128), (32, 8192, 2048), (64, 50000, 2048)]
+
+
+@pytest.mark.parametrize("m,n,k", GEMM_CASES)
+def test_gemm(bl, olib, m, n, k):
+    import torch
+    log(f"gemm m={m} n={n} k={k}")
+    g = W.rng(102, m + n, k)
+    t = W.ternary(g, n, k)
+    sw = W.weight_scale(g)
+    x = W.activations(g, m, k, outliers=True)
+    p = pack_both(t, olib)
+    q, s, qs = oracle.quant_act(x, None, 1e-5, olib)
+    dev = torch_dev()
+    y = torch.empty((m, n), dtype=torch.float32, device=dev)
+    acc = torch.empty((m, n), dtype=torch.int32, device=dev)
+    am = torch.empty(m, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(bl.bitlinear_gemm_workspace_bytes(m, n, k, 1), 8), dtype=torch.uint8, device=dev)
+    bl.bitlinear_gemm(to_dev(p), sw, n, k, to_dev(q), to_dev(s), to_dev(qs), m, None, y, acc, am, ws)
+    oy, oacc = oracle.bitlinear(p, sw, k, q, s, olib)
+    assert_exact(to_host(acc), oacc, "acc")
+    assert_f32(to_host(y), oy, "y")
+    assert_exact(to_host(am), oracle.argmax_rows(oacc, olib), "row argmax")
+    assert_exact(to_host(am), np.argmax(oy, axis=1).astype(np.int32), "argmax of logits")
+
+
+def test_gemm_argmax_ties_no_logits(bl, olib):
+    """Duplicated weight rows make ties; the lowest index must win, without y."""
+    import torch
+    m, n, k = 7, 300, 128
+    g = W.rng(103, 0, 0)
+    t = W.ternary(g, n, k)
+    t[250] = t[3]
+    t[299] = t[3]
+    t[17] = t[200]
+    x = W.activations(g, m, k)
+    x[2] = t[3].astype(np.float32) * np.float32(2.0)   # row 2 maximal at 3, 250, 299
+    p = pack_both(t, olib)
+    q, s, qs = oracle.quant_act(x, None, 1e-5, olib)
+    dev = torch_dev()
+    am = torch.empty(m, dtype=torch.int32, device=dev)
+    ws = torch.empty(bl.bitlinear_gemm_workspace_bytes(m, n, k, 1), dtype=torch.uint8, device=dev)
+    bl.bitlinear_gemm(to_dev(p), 30.0, n, k, to_dev(q), to_dev(s), to_dev(qs), m, None, None, None, am, ws)
+    oacc = oracle.matmul_i32(oracle.unpack(p, k, olib), q, olib)
+    got = to_host(am)
+    assert_exact(got, oracle.argmax_rows(oacc, olib), "row argmax")
+    assert got[2] == 3
+
+
+def test_gemm_residual_and_stride(bl, olib):
+    import torch
+    m, n, k = 40, 96, 256
+    g = W.rng(104, 0, 0)
+    t = W.ternary(g, n, k)
+    x = W.activations(g, m, k)
+    res = W.activations(g, m, n)
+    p = pack_both(t, olib)
+    q, s, qs = oracle.quant_act(x, None, 1e-5, olib)
+    y = to_dev(res)
+    bl.bitlinear_gemm(to_dev(p), 25.0, n, k, to_dev(q), to_dev(s), to_dev(qs), m, y, y)
+    oy, _ = oracle.bitlinear(p, np.float32(25.0), k, q, s, olib)
+    assert_f32(to_host(y), oracle.residual_add(res, oy, olib), "y + residual")
+
+
+# ---- FFN -----------------------------------------------------------------------------------------
+
+def _ffn_case(bl, olib, m, d, f, seed, with_residual):
+    import torch
+    log(f"ffn m={m} d={d} f={f}")
+    g = W.rng(105, seed, 0)
+    tg, tu, td = W.ternary(g, f, d), W.ternary(g, f, d), W.ternary(g, d, f)
+    sg, su, sd = W.weight_scale(g), W.weight_scale(g), W.weight_scale(g)
+    x = W.activations(g, m, d)
+    gn, gs = W.gains(g, d), W.gains(g, f)
+    pg, pu, pd = pack_both(tg, olib), pack_both(tu, olib), pack_both(td, olib)
+    res = W.activations(g, m, d) if with_residual else None
+    dev = torch_dev()
+    out = torch.empty((m, d), dtype=torch.float32, device=dev)
+    ws = torch.zeros(bl.bitnet_ffn_workspace_bytes(m, d, f), dtype=torch.uint8, device=dev)
+    bl.bitnet_ffn(to_dev(x), m, d, f, to_dev(gn), to_dev(gs), 1e-5, to_dev(pg), sg, to_dev(pu), su, to_dev(pd), sd,
+                  to_dev(res) if res is not None else None, out, ws, flags=bl.BITNET_FFN_WRITE_ACC)
+    r = oracle.ffn(x, gn, gs, 1e-5, pg, sg, pu, su, pd, sd, olib)
+    view = lambda seg: to_host(bl.ffn_workspace_view(ws, m, d, f, seg))
+    assert_exact(view("q1"), r["q1"], "q1")
+    assert_exact(view("s1").view(np.uint32), r["s1"].view(np.uint32), "s1 bits")
+    assert_exact(view("qs1"), r["qs1"], "qs1")
+    assert_exact(view("acc_gate"), r["acc_gate"], "acc_gate")
+    assert_exact(view("acc_up"), r["acc_up"], "acc_up")
+    assert_f32(view("h"), r["h"], "h")
+    assert_exact(view("q2"), r["q2"], "q2")
+    assert_exact(view("s2").view(np.uint32), r["s2"].view(np.uint32), "s2 bits")
+    assert_exact(view("qs2"), r["qs2"], "qs2")
+    assert_exact(view("acc_down"), r["acc_down"], "acc_down")
+    want = r["out"] if res is None else oracle.residual_add(res, r["out"], olib)
+    assert_f32(to_host(out), want, "out")
+
+
+@pytest.mark.parametrize("m,d,f,res", [(1, 64, 128, False), (1, 192, 640, True), (3, 256, 1024, False),
+                                        (1, 2560, 10240, False), (8, 640, 2560, True), (12, 320, 640, False),
+                                        (40, 256, 512, True)])
+def test_ffn(bl, olib, m, d, f, res):
+    _ffn_case(bl, olib, m, d, f, m * 1000 + d + f, res)
+
+
+# ---- layer stream ------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n_layers,m,d,f", [(2, 1, 128, 512), (3, 2, 256, 640), (2, 1, 2560, 10240),
+                                            (2, 12, 192, 384), (2, 32, 2048, 8192)])
+def test_decode_stream(bl, olib, n_layers, m, d, f):
+    from gpu_helpers import make_layers, run_stream
+    log(f"stream layers={n_layers} m={m} d={d} f={f}")
+    layers, dev = make_layers(W.W_STREAM, n_layers, d, f, m, olib)
+    x0 = W.activations(W.rng(W.W_STREAM, 999, W.T_X), m, d)
+    x, qkv = run_stream(dev, n_layers, m, d, f, 1e-5, x0)
+    ox, oqkv = oracle.chain(x0, layers, 1e-5, olib)
+    for l in range(n_layers):
+        assert_f32(qkv[l], oqkv[l], f"qkv layer {l}")
+    assert_f32(x, ox, "x after the stream")
