@@ -135,7 +135,7 @@ def main():
     x0 = W.activations(W.rng(W.W_STREAM, 999, W.T_X), m, d)
     x = T(x0)
     qkv = torch.empty((L, m, 3 * d), dtype=torch.float32, device=dev0)
-    ws = torch.empty(bl.bitnet_stream_workspace_bytes(m, d, f), dtype=torch.uint8, device=dev0)
+    ws = torch.zeros(bl.bitnet_stream_workspace_bytes(m, d, f), dtype=torch.uint8, device=dev0)
 
     # first step from x0, checked against the oracle below (same inputs)
     run_stream_step(bl, dev, L, m, d, f, x, qkv, ws)
@@ -251,7 +251,7 @@ def extra_measurements(bl, torch, T, dev0):
     gfin = T(np.ones(d, np.float32))
     xb = T(W.activations(W.rng(W.W_BATCHED, 999, W.T_X), m, d))
     qkv = torch.empty((L, m, 3 * d), dtype=torch.float32, device=dev0)
-    ws = torch.empty(bl.bitnet_stream_workspace_bytes(m, d, f), dtype=torch.uint8, device=dev0)
+    ws = torch.zeros(bl.bitnet_stream_workspace_bytes(m, d, f), dtype=torch.uint8, device=dev0)
     qf = torch.empty((m, d), dtype=torch.int8, device=dev0)
     sf = torch.empty(m, dtype=torch.float32, device=dev0)
     qsf = torch.empty(m, dtype=torch.int32, device=dev0)
@@ -259,7 +259,7 @@ def extra_measurements(bl, torch, T, dev0):
     wsh = torch.empty(bl.bitlinear_gemm_workspace_bytes(m, V, d, 1), dtype=torch.uint8, device=dev0)
 
     def batched_step():
-        run_stream_step(bl, dev, L, m, d, f, xb, qkv, wsh_dummy := ws)
+        run_stream_step(bl, dev, L, m, d, f, xb, qkv, ws)
         bl.bitlinear_quant_act(xb, gfin, 1e-5, qf, sf, qsf)
         bl.bitlinear_gemm(head, sh, V, d, qf, sf, qsf, m, None, None, None, idx, wsh)
 

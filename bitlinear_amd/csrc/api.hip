@@ -42,10 +42,11 @@ Layout ffn_layout(int64_t m, int64_t d, int64_t f)
     return l;
 }
 
-// Stream workspace: a (q, s, qs) for d, o_in for d, the FFN workspace, the
-// q/k/v scratch when the caller passes none.
+// Stream workspace: control words {epoch, status} and the published vectors of
+// the persistent one-token kernel, then a (q, s, qs) for d, o_in for d, the
+// FFN workspace and the q/k/v scratch of the launch-per-step path.
 struct StreamLayout {
-    size_t q_a, s_a, qs_a, q_o, s_o, qs_o, ffn, qkv, total;
+    size_t ctrl, ll, q_a, s_a, qs_a, q_o, s_o, qs_o, ffn, qkv, total;
 };
 
 StreamLayout stream_layout(int64_t m, int64_t d, int64_t f)
@@ -57,6 +58,8 @@ StreamLayout stream_layout(int64_t m, int64_t d, int64_t f)
         at = align_up(at + bytes, 256);
         return o;
     };
+    l.ctrl = take(256);
+    l.ll = take(bl::stream_ll_words((int)d, (int)f) * 8);
     l.q_a = take((size_t)(m * d));
     l.s_a = take((size_t)m * 4);
     l.qs_a = take((size_t)m * 4);
@@ -232,6 +235,12 @@ int bitnet_decode_stream(const uint8_t* weights, const float* scales, const floa
     if (workspace_bytes < bitnet_stream_workspace_bytes(m, d, f)) return BL_ERR_WORKSPACE;
     const hipStream_t s = as_stream(stream);
     const StreamLayout L = stream_layout(m, d, f);
+    if (bl::stream_persistent_fits((int)m, (int)d, (int)f)) {
+        float* qkv_out = qkv ? qkv : at<float>(workspace, L.qkv);
+        return bl::launch_stream_persistent(weights, scales, gains, z, (int)n_layers, (int)d, (int)f, eps, x, qkv_out,
+                                            qkv ? 3 * d : 0, at<void>(workspace, L.ll),
+                                            at<uint32_t>(workspace, L.ctrl), s);
+    }
     int8_t* qa = at<int8_t>(workspace, L.q_a);
     float* sa = at<float>(workspace, L.s_a);
     int32_t* qsa = at<int32_t>(workspace, L.qs_a);

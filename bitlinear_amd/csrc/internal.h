@@ -41,6 +41,15 @@ int launch_gemm(const uint8_t* packed, float w_scale, const float* w_scale_ptr, 
                 const float* act_scale, const int32_t* act_sum, int m, const float* residual, float* y, int ldy,
                 int32_t* acc_out, int32_t* row_argmax, unsigned long long* key_ws, hipStream_t s);
 
+// Persistent one-token layer stream (stream.hip). fits() tells whether the
+// shapes and the device suit it; ll_region holds stream_ll_words(d, f) 64-bit
+// words and ctrl two 32-bit words, all zero before the first call.
+bool stream_persistent_fits(int m, int d, int f);
+size_t stream_ll_words(int d, int f);
+int launch_stream_persistent(const uint8_t* weights, const float* scales, const float* gains, const float* z,
+                             int n_layers, int d, int f, float eps, float* x, float* qkv, long long qkv_stride,
+                             void* ll_region, uint32_t* ctrl, hipStream_t s);
+
 // h = relu(gate)^2 * up, elementwise.
 int launch_relu2_mul(const float* gate, const float* up, int64_t count, float* h, hipStream_t s);
 

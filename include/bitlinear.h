@@ -210,8 +210,20 @@ int bitnet_ffn(const float *x, int64_t m, int64_t d, int64_t f,
  *   x       : device fp32 [m][d], updated in place.
  *   qkv     : device fp32 [n_layers][m][3d] or NULL (then written to the
  *             workspace and overwritten layer by layer).
- *   workspace: device, >= bitnet_stream_workspace_bytes(m, d, f), 256-aligned.
+ *   workspace: device, >= bitnet_stream_workspace_bytes(m, d, f), 256-aligned,
+ *             zero-filled before its first use and then kept between calls:
+ *             its first 8 bytes are two uint32 words {phase counter, status}.
  * d and f must be multiples of 64; m >= 1.
+ * At m == 1 (when the device supports cooperative launch and the shapes fit:
+ * d, f <= 10240 with at most 64 rows of any projection per CU) the whole stream
+ * runs as one persistent kernel, one workgroup per CU, that hands each step's
+ * output vector to the next step through flag-tagged words in the workspace.
+ * Every wait in it is bounded (2 s); on a timeout the kernel stops early and
+ * sets status = 1 (status = 2: the phase counter is exhausted after about 2^31
+ * steps). A nonzero status stays set, and further calls do nothing, until the
+ * workspace is zero-filled again; the caller reads it after synchronising.
+ * Calls that share a workspace must not overlap. Other shapes run one launch
+ * per step, with the same results.
  * Errors: NULL, SHAPE, ALIGN, WORKSPACE, LAUNCH. */
 size_t bitnet_layer_bytes(int64_t d, int64_t f);
 size_t bitnet_stream_workspace_bytes(int64_t m, int64_t d, int64_t f);

@@ -95,12 +95,28 @@ def make_layers(workload, n_layers, d, f, m, olib, bench_gains=False):
     return layers, dev
 
 
-def run_stream(dev, n_layers, m, d, f, eps, x0):
-    """Run bitnet_decode_stream on the GPU; returns (x, qkv) on the host."""
+def new_stream_workspace(m, d, f):
+    """A zero-filled stream workspace (the persistent path keeps a phase counter in it)."""
+    import torch
+    import bitlinear_amd as bl
+    return torch.zeros(bl.bitnet_stream_workspace_bytes(m, d, f), dtype=torch.uint8, device=torch_dev())
+
+
+def stream_ctrl(ws):
+    """(phase counter, status) words at the start of a stream workspace."""
+    import torch
+    torch.cuda.synchronize()
+    c = ws[:8].view(torch.int32).cpu().numpy()
+    return int(c[0]), int(c[1])
+
+
+def run_stream(dev, n_layers, m, d, f, eps, x0, ws=None):
+    """Run bitnet_decode_stream on the GPU; returns (x, qkv, workspace)."""
     import torch
     import bitlinear_amd as bl
     x = to_dev(x0)
     qkv = torch.empty((n_layers, m, 3 * d), dtype=torch.float32, device=torch_dev())
-    ws = torch.empty(bl.bitnet_stream_workspace_bytes(m, d, f), dtype=torch.uint8, device=torch_dev())
+    if ws is None:
+        ws = new_stream_workspace(m, d, f)
     bl.bitnet_decode_stream(dev["weights"], dev["scales"], dev["gains"], dev["z"], n_layers, m, d, f, eps, x, qkv, ws)
-    return to_host(x), to_host(qkv)
+    return to_host(x), to_host(qkv), ws

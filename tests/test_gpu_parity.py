@@ -1,7 +1,7 @@
 """HIP path vs the CPU oracle, element by element, through the C ABI.
 
-Sizes span several tiles with ragged tails; the full configurations of the
-benchmark are covered in test_gpu_full.py."""
+Sizes span several tiles with ragged tails, up to the full shapes of the
+benchmark for single projections."""
 import numpy as np
 import pytest
 
@@ -220,15 +220,37 @@ def test_ffn(bl, olib, m, d, f, res):
 
 # ---- layer stream ------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("n_layers,m,d,f", [(2, 1, 128, 512), (3, 2, 256, 640), (2, 1, 2560, 10240),
-                                            (2, 12, 192, 384), (2, 32, 2048, 8192)])
+@pytest.mark.parametrize("n_layers,m,d,f", [(2, 1, 128, 512), (3, 2, 256, 640), (3, 1, 256, 1024),
+                                            (2, 1, 2560, 10240), (2, 1, 2048, 8192), (2, 12, 192, 384),
+                                            (2, 32, 2048, 8192)])
 def test_decode_stream(bl, olib, n_layers, m, d, f):
-    from gpu_helpers import make_layers, run_stream
+    from gpu_helpers import make_layers, run_stream, stream_ctrl
     log(f"stream layers={n_layers} m={m} d={d} f={f}")
     layers, dev = make_layers(W.W_STREAM, n_layers, d, f, m, olib)
     x0 = W.activations(W.rng(W.W_STREAM, 999, W.T_X), m, d)
-    x, qkv = run_stream(dev, n_layers, m, d, f, 1e-5, x0)
+    x, qkv, ws = run_stream(dev, n_layers, m, d, f, 1e-5, x0)
+    assert stream_ctrl(ws)[1] == 0, "stream status word"
     ox, oqkv = oracle.chain(x0, layers, 1e-5, olib)
     for l in range(n_layers):
         assert_f32(qkv[l], oqkv[l], f"qkv layer {l}")
     assert_f32(x, ox, "x after the stream")
+
+
+@pytest.mark.parametrize("d,f", [(256, 1024), (2560, 10240)])
+def test_decode_stream_repeated_calls(bl, olib, d, f):
+    """Three tokens through one workspace: each call continues the phase counter
+    and reads the previous call's output; every result matches the oracle."""
+    from gpu_helpers import make_layers, run_stream, stream_ctrl
+    n_layers = 3
+    log(f"stream repeated d={d} f={f}")
+    layers, dev = make_layers(W.W_STREAM, n_layers, d, f, 1, olib)
+    x = W.activations(W.rng(W.W_STREAM, 998, W.T_X), 1, d)
+    ws = None
+    for call in range(3):
+        gx, _, ws = run_stream(dev, n_layers, 1, d, f, 1e-5, x, ws)
+        epoch, status = stream_ctrl(ws)
+        assert status == 0
+        x, _ = oracle.chain(x, layers, 1e-5, olib)
+        assert_f32(gx, x, f"x after call {call}")
+        x = gx
+    assert epoch == 3 * 4 * n_layers, "one-token calls of these shapes run the persistent kernel"
