@@ -2,23 +2,25 @@
 //
 // RMSNorm in front of every BitLinear ("Add Support for BitNet Architecture
 // Inference", candle PR 2664) and the per-token absmax int8 quantizer of the
-// b1.58 method that the same PR names activation_quant. One 256-thread
+// b1.58 method that the same PR names activation_quant. One 512-thread
 // workgroup per token:
-//   pass 1 (with a gain): thread t accumulates x[k]^2 in fp64 for k = t, t+256, ...
-//          in ascending k, then the 256 partials are combined by an
-//          xor-butterfly (offsets 128 and 64 through LDS, 32..1 inside the wave):
-//          the fixed order every implementation of this ABI uses;
-//          r = fl32(1 / sqrt(ss / k + eps)) in fp64.
+//   pass 1 (with a gain): thread t accumulates x[k]^2 in fp64 for k = t, t+512,
+//          ... in ascending k (512 partials), then the partials are combined by
+//          an xor-butterfly with offsets 1, 2, ..., 32 inside each wave and 64,
+//          128, 256 across the 8 waves -- the fixed order every implementation
+//          of this ABI uses; r = fl32(1 / sqrt(ss / k + eps)) in fp64.
 //   pass 2: y = fl32(fl32(x * r) * g) and absmax over the row.
 //   pass 3: s_a = fl32(127 / max(absmax, 1e-5)), q = clamp(rne(y * s_a)), sum(q).
 // Passes 2 and 3 each re-read the row (an L2 hit after pass 1) and recompute y
 // identically, so no fp32 row has to be stored.
 #include "internal.h"
+#include "wave.h"
 
 namespace bl {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;  // = the number of RMSNorm partial sums
+constexpr int kWaves = kThreads / 64;
 
 __device__ __forceinline__ int quant_one(float y, float scale)
 {
@@ -51,9 +53,9 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(const float* __rest
     const int lane = t & 63;
     const int wave = t >> 6;
     const float* xr = x + (size_t)row * k;
-    __shared__ double part[kThreads];
-    __shared__ float wmax[kThreads / 64];
-    __shared__ int wsum[kThreads / 64];
+    __shared__ double wsum_d[kWaves];
+    __shared__ float wmax[kWaves];
+    __shared__ int wsum[kWaves];
 
     float r = 1.0f;
     if (kNorm) {
@@ -62,16 +64,10 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(const float* __rest
             const double v = (double)xr[i];
             p += v * v;  // exact square; any fusion rounds the same way
         }
-        part[t] = p;
+        p = wave_butterfly_sum(p);
+        if (lane == 0) wsum_d[wave] = p;
         __syncthreads();
-        p = p + part[t ^ 128];
-        __syncthreads();
-        part[t] = p;
-        __syncthreads();
-        p = p + part[t ^ 64];
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) p = p + __shfl_xor(p, off, 64);
-        r = (float)(1.0 / sqrt(p / (double)k + (double)eps));
+        r = (float)(1.0 / sqrt(cross_wave_sum8(wsum_d) / (double)k + (double)eps));
     }
 
     float amax = 0.0f;
@@ -79,11 +75,12 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(const float* __rest
         const float4 y = normed<kNorm>(xr, gain, r, i);
         amax = fmaxf(amax, fmaxf(fmaxf(fabsf(y.x), fabsf(y.y)), fmaxf(fabsf(y.z), fabsf(y.w))));
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    amax = wave_max(amax);
     if (lane == 0) wmax[wave] = amax;
     __syncthreads();
-    amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    amax = wmax[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) amax = fmaxf(amax, wmax[w]);
     const float scale = 127.0f / fmaxf(amax, 1e-5f);
 
     int sum = 0;
@@ -97,13 +94,15 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(const float* __rest
                                 ((uint32_t)(q2 & 0xff) << 16) | ((uint32_t)(q3 & 0xff) << 24);
         *reinterpret_cast<uint32_t*>(qr + i) = packed;
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+    sum = wave_sum(sum);
     if (lane == 0) wsum[wave] = sum;
     __syncthreads();
     if (t == 0) {
         act_scale[row] = scale;
-        if (act_sum) act_sum[row] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+        int total = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) total += wsum[w];
+        if (act_sum) act_sum[row] = total;
     }
 }
 

@@ -24,14 +24,18 @@
 //     Value and flag travel in one single-copy-atomic store, so no fence or
 //     separate barrier is needed;
 //   - every workgroup then computes the RMSNorm + activation quant of the full
-//     vector itself, in the fixed fp64 order (thread t sums the squares of
-//     k = t, t+256, ... in ascending k; then an xor-butterfly over the 256
-//     partials, offsets 128 and 64 through LDS and 32..1 with exact lane
-//     exchanges), so no extra round trip is spent on broadcasting q;
+//     vector itself, so no extra round trip is spent on broadcasting q. The
+//     sum of squares keeps the fixed fp64 order of quant.hip: with the vector
+//     staged in LDS, thread l < 256 sums x[k]^2 for k = l, l+256, ... in
+//     ascending k, then an xor-butterfly combines the 256 partials (offsets 128
+//     and 64 through LDS, 32..1 with exact lane exchanges);
 //   - the dot products are those of gemv.hip (dot4 on shifted code masks
 //     against activations permuted once into LDS). Each row of a step gets
-//     floor(256 / rows) lanes, and the lanes' partial sums meet in LDS through
+//     floor(1024 / rows) lanes, and the lanes' partial sums meet in LDS through
 //     int32 atomic adds, which are exact in any order.
+// A workgroup has 1024 threads (4 waves per SIMD), so the vector work of a step
+// is spread over 4x the lanes of a one-wave-per-SIMD layout and its latencies
+// overlap.
 // The P2/P4 rows of a workgroup are the same, so the residual x of its rows
 // stays in registers across the whole stream.
 //
@@ -44,7 +48,8 @@
 namespace bl {
 namespace {
 
-constexpr int kT = 256;      // threads per workgroup (= RMSNorm partial count)
+constexpr int kT = 512;      // threads per workgroup: 8 waves, 2 per SIMD; also the
+                             // number of RMSNorm partial sums of the fixed order
 constexpr int kGrid = 256;   // workgroups: one per CU of an MI355X
 constexpr uint32_t kCodeMask = 0x03030303u;
 constexpr long long kTimeoutTicks = 200000000LL;  // 2 s at 100 MHz
@@ -61,6 +66,7 @@ struct Step {
     static constexpr int C = K / 64;          // chunks per row
     static constexpr int CL = cdiv(C, Lr);    // chunks per lane
     static_assert(R >= 1 && R <= 64, "rows per workgroup");
+    static_assert(Lr >= 1, "lanes per row");
     static_assert(K % 64 == 0 && K <= kMaxK, "K");
 };
 
@@ -97,7 +103,7 @@ __device__ __forceinline__ uint32_t status_load(const uint32_t* ctrl)
     return __hip_atomic_load(ctrl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Loads the words k = t, t + 256, ... < N of buf until every one carries epoch
+// Loads the words k = t, t + 1024, ... < N of buf until every one carries epoch
 // e (all loads of a round are issued before any is checked); v receives the
 // fp32 payloads. Returns false, for the whole workgroup, on a timeout or when
 // another workgroup gave up.
@@ -109,9 +115,10 @@ __device__ bool poll_vec(const unsigned long long* buf, uint32_t e, float* v, ui
     unsigned long long w[NI];
     bool failed = false;
     for (int spin = 0;; ++spin) {
+        // every load is unconditional (clamped address) so that the whole batch
+        // is in flight before the first wait
 #pragma unroll
-        for (int i = 0; i < NI; ++i)
-            w[i] = (t + kT * i < N) ? ll_load(buf + t + kT * i) : ((unsigned long long)e << 32);
+        for (int i = 0; i < NI; ++i) w[i] = ll_load(buf + min(t + kT * i, N - 1));
         bool ready = true;
 #pragma unroll
         for (int i = 0; i < NI; ++i) ready = ready && (uint32_t)(w[i] >> 32) == e;
@@ -124,7 +131,7 @@ __device__ bool poll_vec(const unsigned long long* buf, uint32_t e, float* v, ui
         __builtin_amdgcn_s_sleep(2);
     }
 #pragma unroll
-    for (int i = 0; i < NI; ++i) v[i] = __uint_as_float((uint32_t)w[i]);
+    for (int i = 0; i < NI; ++i) v[i] = (t + kT * i < N) ? __uint_as_float((uint32_t)w[i]) : 0.0f;
     if (__syncthreads_or(failed ? 1 : 0)) {
         if (t == 0) __hip_atomic_fetch_or(ctrl + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return false;
@@ -137,7 +144,10 @@ __device__ __forceinline__ void load_strided(const float* src, float* out)
 {
     const int t = threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < cdiv(N, kT); ++i) out[i] = (t + kT * i < N) ? src[t + kT * i] : 0.0f;
+    for (int i = 0; i < cdiv(N, kT); ++i) out[i] = src[min(t + kT * i, N - 1)];
+#pragma unroll
+    for (int i = 0; i < cdiv(N, kT); ++i)
+        if (t + kT * i >= N) out[i] = 0.0f;
 }
 
 __device__ __forceinline__ int quant_one(float y, float scale)
@@ -152,19 +162,23 @@ __device__ __forceinline__ int perm_pos(int k) { return (k & ~15) | ((k & 3) << 
 
 struct Shared {
     __attribute__((aligned(16))) uint8_t q[kMaxK];  // quantized input vector, permuted
-    double part1[kT], part2[kT];
+    double red_d[kT / 64];
     float red_f[kT / 64];
     int red_i[kT / 64];
     int acc[128];  // per-row accumulators of a step (gate rows, then up rows)
 };
 
-// RMSNorm (gains g[i] = gain[t + 256 i]) + activation quant of the N values
-// held as v[i] = x[t + 256 i] into the permuted int8 vector sh.q; returns s_a
-// and sum(q) to every thread.
+// RMSNorm (gains g[i] = gain[t + 512 i]) + activation quant of the N values
+// held as v[i] = x[t + 512 i] into the permuted int8 vector sh.q; returns s_a
+// and sum(q) to every thread. Thread t's own values form partial t of the sum
+// of squares (k = t, t + 512, ... ascending); the butterfly then runs inside
+// each wave (offsets 1..32) and across the 8 waves (64, 128, 256).
 template <int N>
 __device__ void norm_quant(const float* v, const float* g, float eps, Shared& sh, float& s_out, int& qsum_out)
 {
+    static_assert(kT == 512, "the sum of squares is defined over 512 partials");
     constexpr int NI = cdiv(N, kT);
+    constexpr int W = kT / 64;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     double p = 0.0;
 #pragma unroll
@@ -172,14 +186,10 @@ __device__ void norm_quant(const float* v, const float* g, float eps, Shared& sh
         const double xv = (double)v[i];
         p += xv * xv;  // v is zero beyond N
     }
-    sh.part1[t] = p;
-    __syncthreads();
-    p = p + sh.part1[t ^ 128];
-    sh.part2[t] = p;
-    __syncthreads();
-    p = p + sh.part2[t ^ 64];
     p = wave_butterfly_sum(p);
-    const float r = (float)(1.0 / sqrt(p / (double)N + (double)eps));
+    if (lane == 0) sh.red_d[wave] = p;
+    __syncthreads();
+    const float r = (float)(1.0 / sqrt(cross_wave_sum8(sh.red_d) / (double)N + (double)eps));
 
     float y[NI];
     float amax = 0.0f;
@@ -191,7 +201,9 @@ __device__ void norm_quant(const float* v, const float* g, float eps, Shared& sh
     amax = wave_max(amax);
     if (lane == 0) sh.red_f[wave] = amax;
     __syncthreads();
-    amax = fmaxf(fmaxf(sh.red_f[0], sh.red_f[1]), fmaxf(sh.red_f[2], sh.red_f[3]));
+    amax = sh.red_f[0];
+#pragma unroll
+    for (int i = 1; i < W; ++i) amax = fmaxf(amax, sh.red_f[i]);
     const float scale = 127.0f / fmaxf(amax, 1e-5f);
     int sum = 0;
 #pragma unroll
@@ -207,7 +219,10 @@ __device__ void norm_quant(const float* v, const float* g, float eps, Shared& sh
     if (lane == 0) sh.red_i[wave] = sum;
     __syncthreads();
     s_out = scale;
-    qsum_out = sh.red_i[0] + sh.red_i[1] + sh.red_i[2] + sh.red_i[3];
+    int total = 0;
+#pragma unroll
+    for (int i = 0; i < W; ++i) total += sh.red_i[i];
+    qsum_out = total;
 }
 
 __device__ __forceinline__ int dot16(uint32_t p, const uint4 q, int acc)
@@ -233,14 +248,17 @@ struct Lane {
     }
 };
 
+// rowp must point at a valid row even for inactive lanes (the caller clamps
+// the row); chunks past the row end re-read its last chunk. Loads are
+// unconditional so that they all issue before the first wait; dot_row ignores
+// what inactive lanes and excess chunks loaded.
 template <class S>
 __device__ __forceinline__ void load_row(const uint8_t* rowp, const Lane<S>& ln, uint4* w)
 {
 #pragma unroll
     for (int c = 0; c < S::CL; ++c) {
-        const int ch = ln.j + c * S::Lr;
-        w[c] = (ln.active && ch < S::C) ? *reinterpret_cast<const uint4*>(rowp + (size_t)ch * 16)
-                                       : make_uint4(0, 0, 0, 0);
+        const int ch = min(ln.j + c * S::Lr, S::C - 1);
+        w[c] = *reinterpret_cast<const uint4*>(rowp + (size_t)ch * 16);
     }
 }
 
@@ -251,7 +269,7 @@ __device__ __forceinline__ int dot_row(const uint4* w, const Lane<S>& ln, const 
 #pragma unroll
     for (int c = 0; c < S::CL; ++c) {
         const int ch = ln.j + c * S::Lr;
-        if (ch < S::C) {
+        if (S::CL * S::Lr <= S::C || ch < S::C) {  // the test folds away when every lane's chunks exist
             const uint4* qp = reinterpret_cast<const uint4*>(q + (size_t)ch * 64);
             acc = dot16(w[c].x, qp[0], acc);
             acc = dot16(w[c].y, qp[1], acc);
@@ -298,37 +316,61 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
     float s_a;
     int qsum;
 
+    // The weight rows, gains and stand-in input of a step are loaded when the
+    // step starts, before its wait: the fetch overlaps the hand-over. (Loading
+    // a step earlier does not pay: a wave's loads complete in issue order, so
+    // every later wait would also wait for the early loads.)
+    uint4 w1[S1::CL], w2[S2::CL], wg[S3::CL], wu[S3::CL], w4[S4::CL];
+    float g1[ND], g2[ND], g3[ND], g4[NF], zv[ND];
+    auto fetch1 = [&](int l) {
+        const uint8_t* W = a.weights + (size_t)l * blob;
+        const int row = l1.active ? r1 + l1.ri : 0;
+        const int mat = row / D, rin = row - mat * D;
+        load_row<S1>(W + mat * dd + (size_t)rin * (D / 4), l1, w1);
+        load_strided<D>(a.gains + (size_t)l * (3 * D + F), g1);
+    };
+    auto fetch2 = [&](int l) {
+        const uint8_t* W = a.weights + (size_t)l * blob;
+        load_row<S2>(W + 3 * dd + (size_t)(l2.active ? r2 + l2.ri : 0) * (D / 4), l2, w2);
+        load_strided<D>(a.gains + (size_t)l * (3 * D + F) + D, g2);
+        load_strided<D>(a.z + (size_t)l * D, zv);
+    };
+    auto fetch3 = [&](int l) {
+        const uint8_t* W = a.weights + (size_t)l * blob;
+        const size_t ro = (size_t)(l3.active ? r3 + l3.ri : 0) * (D / 4);
+        load_row<S3>(W + 4 * dd + ro, l3, wg);
+        load_row<S3>(W + 4 * dd + fd + ro, l3, wu);
+        load_strided<D>(a.gains + (size_t)l * (3 * D + F) + 2 * D, g3);
+    };
+    auto fetch4 = [&](int l) {
+        const uint8_t* W = a.weights + (size_t)l * blob;
+        load_row<S4>(W + 4 * dd + 2 * fd + (size_t)(l4.active ? r2 + l4.ri : 0) * (F / 4), l4, w4);
+        load_strided<F>(a.gains + (size_t)l * (3 * D + F) + 3 * D, g4);
+    };
     for (int l = 0; l < a.n_layers; ++l) {
         const uint32_t E = base + 4u * (uint32_t)l;
-        const uint8_t* W = a.weights + (size_t)l * blob;
-        const float* sl = a.scales + 7 * l;
-        const float* gl = a.gains + (size_t)l * (3 * D + F);
+        float sw[7];  // this layer's weight scales
+#pragma unroll
+        for (int i = 0; i < 7; ++i) sw[i] = a.scales[7 * l + i];
         float* qkv = a.qkv + (size_t)l * a.qkv_layer_stride;
 
         // ---- P1: q, k, v ----
         {
             if (t < S1::R) sh.acc[t] = 0;
-            uint4 wr[S1::CL];
-            {
-                const int row = r1 + l1.ri;
-                const int mat = l1.active ? row / D : 0;
-                const int rin = l1.active ? row - mat * D : 0;
-                load_row<S1>(W + mat * dd + (size_t)rin * (D / 4), l1, wr);
-            }
-            float v[ND], gv[ND];
-            load_strided<D>(gl, gv);
+            fetch1(l);
+            float v[ND];
             if (l == 0) {
                 load_strided<D>(a.x, v);
             } else if (!poll_vec<D>(a.xa, E, v, a.ctrl, t_start)) {
                 return;
             }
-            norm_quant<D>(v, gv, a.eps, sh, s_a, qsum);
-            const int acc = dot_row<S1>(wr, l1, sh.q);
+            norm_quant<D>(v, g1, a.eps, sh, s_a, qsum);
+            const int acc = dot_row<S1>(w1, l1, sh.q);
             if (l1.active) atomicAdd(&sh.acc[l1.ri], acc);
             __syncthreads();
             if (e1) {
                 const int row = r1 + t, mat = row / D;
-                const float inv = 1.0f / (s_a * sl[mat]);
+                const float inv = 1.0f / (s_a * (mat == 0 ? sw[0] : (mat == 1 ? sw[1] : sw[2])));
                 qkv[row] = (float)(sh.acc[t] - qsum) * inv;
             }
             if (t == 0) ll_store(a.done + w, 0.0f, E + 1);
@@ -336,21 +378,18 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
         // ---- P2: o projection of the stand-in z, residual ----
         {
             if (t < S2::R) sh.acc[t] = 0;
-            uint4 wr[S2::CL];
-            load_row<S2>(W + 3 * dd + (size_t)(r2 + l2.ri) * (D / 4), l2, wr);
-            float zv[ND], gv[ND], fl[1];
-            load_strided<D>(a.z + (size_t)l * D, zv);
-            load_strided<D>(gl + D, gv);
+            fetch2(l);
+            float fl[1];
             if (!poll_vec<kGrid>(a.done, E + 1, fl, a.ctrl, t_start)) return;
             if (l == 0 && w == 0 && t == 0)  // every workgroup has read the base by now
                 __hip_atomic_store(a.ctrl, base + 4u * (uint32_t)a.n_layers, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
-            norm_quant<D>(zv, gv, a.eps, sh, s_a, qsum);
-            const int acc = dot_row<S2>(wr, l2, sh.q);
+            norm_quant<D>(zv, g2, a.eps, sh, s_a, qsum);
+            const int acc = dot_row<S2>(w2, l2, sh.q);
             if (l2.active) atomicAdd(&sh.acc[l2.ri], acc);
             __syncthreads();
             if (e2) {
-                const float inv = 1.0f / (s_a * sl[3]);
+                const float inv = 1.0f / (s_a * sw[3]);
                 xres = xres + (float)(sh.acc[t] - qsum) * inv;
                 ll_store(a.xb + r2 + t, xres, E + 2);
             }
@@ -361,14 +400,10 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
                 sh.acc[t] = 0;
                 sh.acc[S3::R + t] = 0;
             }
-            uint4 wg[S3::CL], wu[S3::CL];
-            const size_t ro = (size_t)(r3 + l3.ri) * (D / 4);
-            load_row<S3>(W + 4 * dd + ro, l3, wg);
-            load_row<S3>(W + 4 * dd + fd + ro, l3, wu);
-            float v[ND], gv[ND];
-            load_strided<D>(gl + 2 * D, gv);
+            fetch3(l);
+            float v[ND];
             if (!poll_vec<D>(a.xb, E + 2, v, a.ctrl, t_start)) return;
-            norm_quant<D>(v, gv, a.eps, sh, s_a, qsum);
+            norm_quant<D>(v, g3, a.eps, sh, s_a, qsum);
             const int ag = dot_row<S3>(wg, l3, sh.q);
             const int au = dot_row<S3>(wu, l3, sh.q);
             if (l3.active) {
@@ -377,27 +412,25 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
             }
             __syncthreads();
             if (e3) {
-                const float gate = (float)(sh.acc[t] - qsum) * (1.0f / (s_a * sl[4]));
-                const float up = (float)(sh.acc[S3::R + t] - qsum) * (1.0f / (s_a * sl[5]));
+                const float gate = (float)(sh.acc[t] - qsum) * (1.0f / (s_a * sw[4]));
+                const float up = (float)(sh.acc[S3::R + t] - qsum) * (1.0f / (s_a * sw[5]));
                 const float gp = gate > 0.0f ? gate : 0.0f;
-                const float g2 = gp * gp;
-                ll_store(a.hh + r3 + t, g2 * up, E + 3);
+                const float g2v = gp * gp;
+                ll_store(a.hh + r3 + t, g2v * up, E + 3);
             }
         }
         // ---- P4: down projection of h, residual ----
         {
             if (t < S4::R) sh.acc[t] = 0;
-            uint4 wr[S4::CL];
-            load_row<S4>(W + 4 * dd + 2 * fd + (size_t)(r2 + l4.ri) * (F / 4), l4, wr);
-            float v[NF], gv[NF];
-            load_strided<F>(gl + 3 * D, gv);
+            fetch4(l);
+            float v[NF];
             if (!poll_vec<F>(a.hh, E + 3, v, a.ctrl, t_start)) return;
-            norm_quant<F>(v, gv, a.eps, sh, s_a, qsum);
-            const int acc = dot_row<S4>(wr, l4, sh.q);
+            norm_quant<F>(v, g4, a.eps, sh, s_a, qsum);
+            const int acc = dot_row<S4>(w4, l4, sh.q);
             if (l4.active) atomicAdd(&sh.acc[l4.ri], acc);
             __syncthreads();
             if (e2) {
-                const float inv = 1.0f / (s_a * sl[6]);
+                const float inv = 1.0f / (s_a * sw[6]);
                 xres = xres + (float)(sh.acc[t] - qsum) * inv;
                 ll_store(a.xa + r2 + t, xres, E + 4);
                 if (l == a.n_layers - 1) a.x[r2 + t] = xres;

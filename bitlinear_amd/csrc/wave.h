@@ -57,17 +57,25 @@ __device__ __forceinline__ double xor_lane(double v)
     return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
-// p + p(lane ^ M) for M = 32, 16, ..., 1: the in-wave part of the fixed
-// xor-butterfly (every lane ends with the same value).
+// p + p(lane ^ M) for M = 1, 2, ..., 32: the in-wave part of the fixed
+// xor-butterfly over the RMSNorm partial sums (every lane ends with the sum
+// of its wave, combined in exactly this order).
 __device__ __forceinline__ double wave_butterfly_sum(double p)
 {
-    p = p + xor_lane<32>(p);
-    p = p + xor_lane<16>(p);
-    p = p + xor_lane<8>(p);
-    p = p + xor_lane<4>(p);
-    p = p + xor_lane<2>(p);
     p = p + xor_lane<1>(p);
+    p = p + xor_lane<2>(p);
+    p = p + xor_lane<4>(p);
+    p = p + xor_lane<8>(p);
+    p = p + xor_lane<16>(p);
+    p = p + xor_lane<32>(p);
     return p;
+}
+
+// The cross-wave part of the butterfly over 8 wave sums s[0..7] (offsets 64,
+// 128, 256 between partials): ((s0+s1)+(s2+s3)) + ((s4+s5)+(s6+s7)).
+__device__ __forceinline__ double cross_wave_sum8(const double* s)
+{
+    return ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
 }
 
 __device__ __forceinline__ float wave_max(float v)

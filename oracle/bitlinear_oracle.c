@@ -32,9 +32,9 @@
  *    least significant field first; byte i of a row holds k = 4i .. 4i+3.
  *    Code 3 is invalid. Weights are stored W[N_out][K_in], K contiguous.
  *  - RMSNorm: y = fl32(fl32(x * r) * g), r = fl32(1 / sqrt(ss / K + eps)) taken
- *    in fp64; ss is the fp64 sum of squares in one fixed order: 256 strided
- *    partials (partial l sums k = l, l+256, ... ascending), then a pairwise
- *    xor-butterfly over the partials with offsets 128, 64, ..., 1.
+ *    in fp64; ss is the fp64 sum of squares in one fixed order: 512 strided
+ *    partials (partial l sums k = l, l+512, ... ascending), then a pairwise
+ *    xor-butterfly over the partials with offsets 1, 2, 4, ..., 256.
  *  - Dequant: inv = fl32(1 / fl32(s_a * s_w)) once per (token, tensor), then
  *    y = fl32((float)acc * inv).
  *  - FFN: h = fl32(fl32(relu(gate) * relu(gate)) * up), then the sub-norm and
@@ -50,7 +50,7 @@
 #include <string.h>
 
 #define ORACLE_EPS_FLOOR 1e-5
-#define ORACLE_PARTIALS 256
+#define ORACLE_PARTIALS 512
 
 int ref_abi_version(void) { return 1; }
 
@@ -133,7 +133,7 @@ double ref_sumsq(const float *x, int64_t k)
         double v = (double)x[i];
         p[i % ORACLE_PARTIALS] += v * v;
     }
-    for (int off = ORACLE_PARTIALS / 2; off >= 1; off /= 2) {
+    for (int off = 1; off < ORACLE_PARTIALS; off *= 2) {
         memcpy(c, p, sizeof p);
         for (int l = 0; l < ORACLE_PARTIALS; l++) p[l] = c[l] + c[l ^ off];
     }

@@ -228,25 +228,33 @@ def pin_sumsq_exact_bound(o, lib):
 
 
 def pin_sumsq_order(o, lib):
-    """The sum of squares follows the stated order exactly: 256 strided partials,
-    then a pairwise xor-butterfly with offsets 128, 64, ..., 1. Two hand-worked
-    cases with squares 2^52 and 1 (fp64 spacing is 2 above 2^53, so where a 1
-    meets 2^53 alone it is lost to round-half-even):
-      A: x[0] = x[256] = 2^26, x[64] = x[128] = 1. Partial 0 = 2^52 + 2^52 = 2^53;
-         the butterfly then adds each 1 to 2^53 on its own -> 2^53.
+    """The sum of squares follows the stated order exactly: 512 strided partials
+    (partial l sums x[k]^2 for k = l, l+512, ... ascending), then a pairwise
+    xor-butterfly with offsets 1, 2, 4, ..., 256. Hand-worked cases with squares
+    2^52 and 1 (fp64 spacing is 2 above 2^53, so a 1 that meets 2^53 alone is
+    lost to round-half-even); K = 1024, x = 0 elsewhere:
+      A: x[0] = x[512] = 2^26, x[64] = x[128] = 1. Partial 0 = 2^53; the 1s in
+         partials 64 and 128 each meet 2^53 alone -> 2^53.
          (64 or 128 partials, or a left-to-right sum, give 2^53 + 2.)
-      B: x[0] = x[128] = 2^26, x[256] = x[384] = 1. Partials 0 and 128 are each
-         2^52 + 1 (exact); the offset-128 step adds them -> 2^53 + 2.
-         (128 partials or a left-to-right sum give 2^53.)"""
+      B: x[0] = x[128] = 2^26, x[512] = x[640] = 1. Partials 0 and 128 are each
+         2^52 + 1 (exact) and meet at offset 128 -> 2^53 + 2.
+         (128 or 256 partials, or a left-to-right sum, give 2^53.)
+      C: x[0] = x[512] = 2^26, x[1] = x[257] = 1. Ascending offsets add partial 1
+         to 2^53 first (lost), then partial 257 alone (lost) -> 2^53.
+         (Descending offsets pair the two 1s first -> 2^53 + 2.)"""
     big = np.float32(2.0 ** 26)
-    xa = np.zeros(512, np.float32)
-    xa[[0, 256]] = big
+    xa = np.zeros(1024, np.float32)
+    xa[[0, 512]] = big
     xa[[64, 128]] = 1.0
     assert o.sumsq(xa, lib) == 2.0 ** 53
-    xb = np.zeros(512, np.float32)
+    xb = np.zeros(1024, np.float32)
     xb[[0, 128]] = big
-    xb[[256, 384]] = 1.0
+    xb[[512, 640]] = 1.0
     assert o.sumsq(xb, lib) == 2.0 ** 53 + 2.0
+    xc = np.zeros(1024, np.float32)
+    xc[[0, 512]] = big
+    xc[[1, 257]] = 1.0
+    assert o.sumsq(xc, lib) == 2.0 ** 53
 
 
 def pin_rmsnorm_closed_form(o, lib):

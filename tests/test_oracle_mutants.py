@@ -31,6 +31,8 @@ C_MUTANTS = [
     ("sumsq_drop_last", "for (int64_t i = 0; i < k; i++) {\n        double v",
      "for (int64_t i = 0; i + 1 < k; i++) {\n        double v"),
     ("sumsq_64_partials", "p[i % ORACLE_PARTIALS] += v * v;", "p[i % 64] += v * v;"),
+    ("sumsq_descending_butterfly", "for (int off = 1; off < ORACLE_PARTIALS; off *= 2) {",
+     "for (int off = ORACLE_PARTIALS / 2; off >= 1; off /= 2) {"),
     ("rms_no_mean", "sqrt(ss / (double)k + (double)eps)", "sqrt(ss + (double)eps)"),
     ("rms_no_eps", "sqrt(ss / (double)k + (double)eps)", "sqrt(ss / (double)k)"),
     ("rms_no_sqrt", "1.0 / sqrt(ss / (double)k + (double)eps)", "1.0 / (ss / (double)k + (double)eps)"),
