@@ -100,6 +100,55 @@ def run_stream_step(bl, dev, n_layers, m, d, f, x, qkv, ws):
     bl.bitnet_decode_stream(dev["weights"], dev["scales"], dev["gains"], dev["z"], n_layers, m, d, f, 1e-5, x, qkv, ws)
 
 
+# HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, each scaled by the
+# factor the same counter gives for a plain 512 MiB device copy (FETCH_SIZE x 2.0,
+# WRITE_SIZE x 1.0); summaries in profiles/. Each entry holds the sha256 of the
+# kernel sources it was measured on: once they change the figure no longer
+# describes the kernel and is reported as null.
+TRAFFIC_BYTES_PER_LAUNCH = {
+    "stream_3b": {"bytes": 903725094,
+                  "sources": {"bitlinear_amd/csrc/stream.hip":
+                              "82bddba15d7bad7126fe140ec396377f1eee9a5883473c76b1db60ad616b2a62",
+                              "bitlinear_amd/csrc/wave.h":
+                              "c69e873099defc85d5684275fbfcce86285892ceef0209e5a6afd9ff57cb9c81"}},
+}
+
+
+def traffic_bytes(key):
+    """Counter-derived bytes for `key`, or None if its sources changed since."""
+    import hashlib
+    e = TRAFFIC_BYTES_PER_LAUNCH.get(key)
+    if e is None:
+        return None
+    for rel, digest in e["sources"].items():
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            if hashlib.sha256(fh.read()).hexdigest() != digest:
+                return None
+    return e["bytes"]
+
+
+def stream_is_persistent(ws):
+    """The persistent one-token path advances the phase counter in the workspace."""
+    import torch
+    torch.cuda.synchronize()
+    return int(ws[:4].view(torch.int32).item()) != 0
+
+
+def copy_probe():
+    import torch
+    n = 512 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    with Timer() as tm:
+        for _ in range(20):
+            dst.copy_(src)
+    print(json.dumps({"copy_bytes_each_way": n, "ms_per_copy": tm.ms / 20,
+                      "gbs_read_plus_write": 2 * n / (tm.ms / 20 * 1e-3) / 1e9}), flush=True)
+
+
 def omp_threads():
     v = os.environ.get("OMP_NUM_THREADS")
     return int(v) if v and v.isdigit() else os.cpu_count()
@@ -112,12 +161,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extra", action="store_true", help="only the headline decode stream")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 512 MiB device copy (calibrates rocprof byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr, flush=True)
         sys.exit(2)
 
+    if args.copy_probe:
+        copy_probe()
+        return
     ensure_built()
     import torch
     import bitlinear_amd as bl
@@ -152,6 +206,9 @@ def main():
             run_stream_step(bl, dev, L, m, d, f, x, qkv, ws)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - tw0) * 1e3
+    status = int(ws[4:8].view(torch.int32).item())
+    if status != 0:
+        raise RuntimeError(f"decode stream status word {status}: the persistent kernel gave up; timing is void")
     ms_per_step = wall_ms / args.steps
     ev_ms_per_step = tm.ms / args.steps
     value = weight_bytes / (ms_per_step * 1e-3) / 1e9
@@ -176,11 +233,15 @@ def main():
         "ms_per_token": round(ms_per_step, 5),
     }
 
-    # roofline of the dominant kernel: the stream as launched per step
-    result["roofline"] = {"kernel": "bitnet_decode_stream step (all launches of one token)", "bound": "hbm",
+    # roofline of the dominant kernel: at one token the whole stream is one
+    # launch of the persistent kernel, so the per-step event time is its duration
+    persistent = bl._lib.bitnet_stream_workspace_bytes(m, d, f) > 0 and stream_is_persistent(ws)
+    kname = ("stream_kernel<2560, 10240> (one persistent launch per token)" if persistent
+             else "bitnet_decode_stream launches of one token")
+    result["roofline"] = {"kernel": kname, "bound": "hbm",
                           "achieved": round(weight_bytes / (ev_ms_per_step * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
                           "unit": "GB/s", "frac": round(weight_bytes / (ev_ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                          "traffic": None}
+                          "traffic": traffic_bytes("stream_3b")}
 
     # ---- CPU oracle baseline + parity of the first step ----------------------------------
     if not args.no_cpu:
@@ -188,16 +249,21 @@ def main():
         olib = oracle.load()
         tc0 = time.perf_counter()
         ox, oqkv = oracle.chain(x0, host_layers, 1e-5, olib)
-        cpu_s = time.perf_counter() - tc0
+        first_s = time.perf_counter() - tc0
         exact = bool(np.array_equal(ox.view(np.uint32), x_first.view(np.uint32)) and
                      all(np.array_equal(oqkv[l].view(np.uint32), qkv_first[l].view(np.uint32)) for l in range(L)))
         rel = float(np.max(np.abs(ox.astype(np.float64) - x_first) / np.maximum(np.abs(ox), 1e-30)))
-        result["cpu_baseline"] = {"value": round(weight_bytes / cpu_s / 1e9, 4), "unit": "GB/s",
+        tokens, xo = 1, ox
+        while time.perf_counter() - tc0 < 10.0 and tokens < 64:  # about 10 s of CPU work
+            xo, _ = oracle.chain(xo, host_layers, 1e-5, olib)
+            tokens += 1
+        cpu_s = time.perf_counter() - tc0
+        result["cpu_baseline"] = {"value": round(tokens * weight_bytes / cpu_s / 1e9, 4), "unit": "GB/s",
                                   "cores": omp_threads(), "kind": "oracle",
-                                  "sample": "one full token of the same 32-layer stream (all 224 BitLinears), "
-                                            f"{cpu_s:.2f} s"}
+                                  "sample": f"{tokens} consecutive tokens of the same 32-layer stream (all 224 "
+                                            f"BitLinears each), {cpu_s:.2f} s"}
         result["parity_first_step"] = {"bit_exact": exact, "max_rel_err_x": rel}
-        log(f"oracle: {cpu_s:.2f}s for one token; first GPU step bit-exact: {exact}")
+        log(f"oracle: {first_s:.2f}s for one token, {tokens} tokens in {cpu_s:.2f}s; first GPU step bit-exact: {exact}")
     del host_layers
 
     if not args.no_extra:
@@ -207,6 +273,58 @@ def main():
 
 def extra_measurements(bl, torch, T, dev0):
     out = {}
+    # ---- single BitLinear decode GEMV 2560 -> 2560 (quant + GEMV), weights rotated
+    # over > 512 MiB of copies so that they stream from HBM, not the 256 MB MALL ----
+    d = 2560
+    g = W.rng(W.W_GEMV, 0, W.T_Q)
+    p0 = bl.bitlinear_pack(W.ternary(g, d, d))
+    sw = W.weight_scale(g)
+    copies = 320
+    pw = T(np.ascontiguousarray(np.broadcast_to(p0, (copies,) + p0.shape)))
+    x1 = T(W.activations(W.rng(W.W_GEMV, 0, W.T_X), 1, d))
+    q1 = torch.empty((1, d), dtype=torch.int8, device=dev0)
+    s1 = torch.empty(1, dtype=torch.float32, device=dev0)
+    qs1 = torch.empty(1, dtype=torch.int32, device=dev0)
+    y1 = torch.empty((1, d), dtype=torch.float32, device=dev0)
+    for i in range(8):
+        bl.bitlinear_quant_act(x1, None, 1e-5, q1, s1, qs1)
+        bl.bitlinear_gemv(pw[i], sw, d, d, q1, s1, qs1, 1, None, y1)
+    with Timer() as tg:
+        for i in range(copies):
+            bl.bitlinear_quant_act(x1, None, 1e-5, q1, s1, qs1)
+            bl.bitlinear_gemv(pw[i], sw, d, d, q1, s1, qs1, 1, None, y1)
+    ms = tg.ms / copies
+    out["gemv"] = {"workload": "quant 1x2560 + GEMV 2560->2560 (1,638,400 packed B), weights rotated over 320 copies",
+                   "us_per_call": round(ms * 1e3, 3), "weight_gbs": round(d * d / 4 / (ms * 1e-3) / 1e9, 1),
+                   "frac_hbm": round(d * d / 4 / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del pw
+    # ---- BitNet-3B FFN at one token, weights rotated over 27 copies (531 MB) ----
+    f = 10240
+    gg = [W.rng(W.W_FFN, 0, tid) for tid in (W.T_GATE, W.T_UP, W.T_DOWN)]
+    shapes = ((f, d), (f, d), (d, f))
+    packs = [bl.bitlinear_pack(W.ternary(gx, n, k)) for gx, (n, k) in zip(gg, shapes)]
+    scales = [float(W.weight_scale(gx)) for gx in gg]
+    fcopies = 27
+    fw = [T(np.ascontiguousarray(np.broadcast_to(pk, (fcopies,) + pk.shape))) for pk in packs]
+    xf = T(W.activations(W.rng(W.W_FFN, 0, W.T_X), 1, d))
+    gn = T(np.ones(d, np.float32))
+    gs = T(np.ones(f, np.float32))
+    of = torch.empty((1, d), dtype=torch.float32, device=dev0)
+    wsf = torch.empty(bl.bitnet_ffn_workspace_bytes(1, d, f), dtype=torch.uint8, device=dev0)
+    for i in range(3):
+        bl.bitnet_ffn(xf, 1, d, f, gn, gs, 1e-5, fw[0][i], scales[0], fw[1][i], scales[1], fw[2][i], scales[2],
+                      None, of, wsf)
+    with Timer() as tf:
+        for i in range(fcopies):
+            bl.bitnet_ffn(xf, 1, d, f, gn, gs, 1e-5, fw[0][i], scales[0], fw[1][i], scales[1], fw[2][i],
+                          scales[2], None, of, wsf)
+    ms = tf.ms / fcopies
+    fb = 3 * d * f // 4
+    out["ffn"] = {"workload": "BitNet-3B FFN at 1 token (19,660,800 packed B), weights rotated over 27 copies",
+                  "us_per_call": round(ms * 1e3, 3), "weight_gbs": round(fb / (ms * 1e-3) / 1e9, 1),
+                  "frac_hbm": round(fb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    log(f"gemv {out['gemv']['us_per_call']} us, ffn {out['ffn']['us_per_call']} us")
+    del fw
     # ---- prefill GEMM 2048 x 2560 -> 10240 ----
     M, K, N = 2048, 2560, 10240
     g = W.rng(W.W_PREFILL, 0, W.T_GATE)

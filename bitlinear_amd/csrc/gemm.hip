@@ -3,8 +3,10 @@
 //
 // acc[m][n] = sum_k q[m][k] * t[n][k] is a dense int8 contraction, so it runs on
 // v_mfma_i32_32x32x32_i8 (32x32 output tile, 32-deep K per instruction, exact
-// int32 accumulation). The weights stay 2-bit packed in HBM and in LDS; each
-// wave unpacks its B operand in registers: the packed dword of 16 consecutive
+// int32 accumulation). Tiles are staged through double-buffered LDS: the next K
+// step's global loads are in flight while the current step's MFMAs run, and
+// one barrier per K step separates the buffers. The weights stay 2-bit packed
+// in HBM and in LDS; each wave unpacks its B operand in registers: the packed dword of 16 consecutive
 // weights of column n gives, through (w >> 2j) & 0x03030303 for j = 0..3, the
 // codes c = t + 1 of weights {j, 4+j, 8+j, 12+j}. The activation tile is staged
 // in LDS already transposed into that order (4x4 byte transpose per 16 bytes),
@@ -27,12 +29,6 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr uint32_t kCodeMask = 0x03030303u;
-constexpr int kBM = 128, kBN = 128, kBK = 64;
-constexpr int kThreads = 256;
-constexpr int kWaveM = 64, kWaveN = 64;       // wave tile
-constexpr int kTM = kWaveM / 32, kTN = kWaveN / 32;
-constexpr int kStrideA = kBK + 16;             // bytes per A row in LDS (padding against bank conflicts)
-constexpr int kStrideB = kBK / 4 + 4;          // bytes per packed B row in LDS
 
 __device__ __forceinline__ uint4 permute16(const uint4 v)
 {
@@ -48,96 +44,151 @@ __device__ __forceinline__ uint4 permute16(const uint4 v)
     return o;
 }
 
-__global__ __launch_bounds__(kThreads) void gemm_kernel(const uint8_t* __restrict__ packed, float w_scale,
-                                                        const float* __restrict__ w_scale_ptr, int n, int k,
-                                                        const int8_t* __restrict__ q,
-                                                        const float* __restrict__ act_scale,
-                                                        const int32_t* __restrict__ act_sum, int m,
-                                                        const float* residual, float* y, int ldy,
-                                                        int32_t* __restrict__ acc_out,
-                                                        unsigned long long* __restrict__ keys)
+constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Tile configuration: a BM x BN block tile, WAVES_M x WAVES_N waves, each
+// owning a (BM/WAVES_M) x (BN/WAVES_N) wave tile of 32x32 MFMA tiles; BK-deep
+// K steps. The packed weight tile holds BK/4 bytes per row.
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_;
+    static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+    static constexpr int kThreads = 64 * WAVES_M * WAVES_N;
+    static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+    static constexpr int TM = WM / 32, TN = WN / 32;
+    static constexpr int SA = BK + 16;     // LDS bytes per activation row (padded against bank conflicts)
+    static constexpr int SB = BK / 4 + 4;  // LDS bytes per packed weight row (5 dwords: conflict-free reads)
+    static constexpr int A_CHUNKS = BM * BK / 16, B_CHUNKS = BN * BK / 64;  // 16-byte chunks per K step
+    static constexpr int A_PER_T = cdiv(A_CHUNKS, kThreads), B_PER_T = cdiv(B_CHUNKS, kThreads);
+    static_assert(WM % 32 == 0 && WN % 32 == 0 && BK % 64 == 0, "tile shape");
+};
+
+// Large M (prefill): 128 x 320 tiles -- 512 tiles for 2048 x 10240, two per CU.
+using CfgLarge = Cfg<128, 320, 2, 2, 64>;
+// Small M (batched decode, LM head): 32 x 256 tiles.
+using CfgSmall = Cfg<32, 256, 1, 4, 64>;
+
+template <class C>
+__global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(2))) void gemm_kernel(const uint8_t* __restrict__ packed, float w_scale,
+                                                           const float* __restrict__ w_scale_ptr, int n, int k,
+                                                           const int8_t* __restrict__ q,
+                                                           const float* __restrict__ act_scale,
+                                                           const int32_t* __restrict__ act_sum, int m,
+                                                           const float* residual, float* y, int ldy,
+                                                           int32_t* __restrict__ acc_out,
+                                                           unsigned long long* __restrict__ keys)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t lds_a[kBM * kStrideA];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_b[kBN * kStrideB];
-    __shared__ float lds_inv[kBM];
-    __shared__ int lds_qsum[kBM];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][C::BM * C::SA];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][C::BN * C::SB];
+    __shared__ float lds_inv[C::BM];
+    __shared__ int lds_qsum[C::BM];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = (wave >> 1) * kWaveM;   // wave row offset inside the block tile
-    const int wn = (wave & 1) * kWaveN;    // wave column offset
-    const int n0 = blockIdx.x * kBN;
-    const int m0 = blockIdx.y * kBM;
+    const int wm = (wave / C::WAVES_N) * C::WM;  // wave row offset inside the block tile
+    const int wn = (wave % C::WAVES_N) * C::WN;  // wave column offset
+    const int n0 = blockIdx.x * C::BN;
+    const int m0 = blockIdx.y * C::BM;
     const size_t kb = (size_t)k / 4;
+    const int nk = k / C::BK;
 
     const float ws = w_scale_ptr ? *w_scale_ptr : w_scale;
-    if (tid < kBM) {
-        const int row = m0 + tid;
-        lds_inv[tid] = row < m ? 1.0f / (act_scale[row] * ws) : 0.0f;
-        lds_qsum[tid] = row < m ? act_sum[row] : 0;
+    for (int r = tid; r < C::BM; r += C::kThreads) {
+        const int row = m0 + r;
+        lds_inv[r] = row < m ? 1.0f / (act_scale[row] * ws) : 0.0f;
+        lds_qsum[r] = row < m ? act_sum[row] : 0;
     }
 
-    v16i acc[kTM][kTN];
+    // Global -> register staging of one K step: activation chunks (16 bytes of
+    // one row) and packed weight chunks (16 bytes of one weight row). Rows past
+    // m / n read row 0 (in bounds); their results are never stored.
+    uint4 ga[C::A_PER_T], gb[C::B_PER_T];
+    auto load_global = [&](int s) {
+        const int k0 = s * C::BK;
 #pragma unroll
-    for (int i = 0; i < kTM; ++i)
+        for (int c = 0; c < C::A_PER_T; ++c) {
+            const int chunk = tid + c * C::kThreads;
+            const int row = chunk / (C::BK / 16), kg = chunk % (C::BK / 16);
+            const int grow = (chunk < C::A_CHUNKS && m0 + row < m) ? m0 + row : 0;
+            ga[c] = *reinterpret_cast<const uint4*>(q + (size_t)grow * k + k0 + kg * 16);
+        }
 #pragma unroll
-        for (int j = 0; j < kTN; ++j)
+        for (int c = 0; c < C::B_PER_T; ++c) {
+            const int chunk = tid + c * C::kThreads;
+            const int row = chunk / (C::BK / 64), kg = chunk % (C::BK / 64);
+            const int gcol = (chunk < C::B_CHUNKS && n0 + row < n) ? n0 + row : 0;
+            gb[c] = *reinterpret_cast<const uint4*>(packed + (size_t)gcol * kb + k0 / 4 + kg * 16);
+        }
+    };
+    auto store_lds = [&](int buf) {
+#pragma unroll
+        for (int c = 0; c < C::A_PER_T; ++c) {
+            const int chunk = tid + c * C::kThreads;
+            if (C::A_CHUNKS % C::kThreads == 0 || chunk < C::A_CHUNKS) {
+                const int row = chunk / (C::BK / 16), kg = chunk % (C::BK / 16);
+                *reinterpret_cast<uint4*>(lds_a[buf] + row * C::SA + kg * 16) = permute16(ga[c]);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < C::B_PER_T; ++c) {
+            const int chunk = tid + c * C::kThreads;
+            if (C::B_CHUNKS % C::kThreads == 0 || chunk < C::B_CHUNKS) {
+                const int row = chunk / (C::BK / 64), kg = chunk % (C::BK / 64);
+                uint32_t* dst = reinterpret_cast<uint32_t*>(lds_b[buf] + row * C::SB + kg * 16);
+                dst[0] = gb[c].x;
+                dst[1] = gb[c].y;
+                dst[2] = gb[c].z;
+                dst[3] = gb[c].w;
+            }
+        }
+    };
+
+    v16i acc[C::TM][C::TN];
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-    for (int k0 = 0; k0 < k; k0 += kBK) {
-        // stage A: kBM rows x 64 bytes = 512 chunks of 16 bytes, 2 per thread
+    load_global(0);
+    store_lds(0);
+    __syncthreads();
+    for (int s = 0; s < nk; ++s) {
+        const int buf = s & 1;
+        if (s + 1 < nk) load_global(s + 1);  // in flight during this step's MFMAs
 #pragma unroll
-        for (int c = 0; c < (kBM * kBK / 16) / kThreads; ++c) {
-            const int chunk = tid + c * kThreads;
-            const int row = chunk >> 2, kg = chunk & 3;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (m0 + row < m) v = *reinterpret_cast<const uint4*>(q + (size_t)(m0 + row) * k + k0 + kg * 16);
-            *reinterpret_cast<uint4*>(lds_a + row * kStrideA + kg * 16) = permute16(v);
-        }
-        // stage B: kBN packed rows x 16 bytes
-        if (tid < kBN) {
-            const int col = n0 + tid;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (col < n) v = *reinterpret_cast<const uint4*>(packed + (size_t)col * kb + k0 / 4);
-            uint32_t* dst = reinterpret_cast<uint32_t*>(lds_b + tid * kStrideB);
-            dst[0] = v.x;
-            dst[1] = v.y;
-            dst[2] = v.z;
-            dst[3] = v.w;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int ks = 0; ks < kBK / 32; ++ks) {
+        for (int ks = 0; ks < C::BK / 32; ++ks) {
             const int kofs = ks * 32 + (lane >> 5) * 16;  // this lane's 16 K values
-            v4i a[kTM], b[kTN];
+            v4i a[C::TM], b[C::TN];
 #pragma unroll
-            for (int i = 0; i < kTM; ++i) {
+            for (int i = 0; i < C::TM; ++i) {
                 const uint4 v =
-                    *reinterpret_cast<const uint4*>(lds_a + (wm + i * 32 + (lane & 31)) * kStrideA + kofs);
+                    *reinterpret_cast<const uint4*>(lds_a[buf] + (wm + i * 32 + (lane & 31)) * C::SA + kofs);
                 a[i] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
             }
 #pragma unroll
-            for (int j = 0; j < kTN; ++j) {
+            for (int j = 0; j < C::TN; ++j) {
                 const uint32_t p =
-                    *reinterpret_cast<const uint32_t*>(lds_b + (wn + j * 32 + (lane & 31)) * kStrideB + kofs / 4);
+                    *reinterpret_cast<const uint32_t*>(lds_b[buf] + (wn + j * 32 + (lane & 31)) * C::SB + kofs / 4);
                 b[j] = v4i{(int)(p & kCodeMask), (int)((p >> 2) & kCodeMask), (int)((p >> 4) & kCodeMask),
                            (int)((p >> 6) & kCodeMask)};
             }
 #pragma unroll
-            for (int i = 0; i < kTM; ++i)
+            for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-                for (int j = 0; j < kTN; ++j)
+                for (int j = 0; j < C::TN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
         }
+        if (s + 1 < nk) store_lds(buf ^ 1);  // the other buffer: last read before the previous barrier
         __syncthreads();
     }
 
     // epilogue: lane holds column (lane & 31) of each 32x32 tile; register r
     // holds row 8 (r / 4) + 4 (lane / 32) + (r % 4).
 #pragma unroll
-    for (int i = 0; i < kTM; ++i) {
+    for (int i = 0; i < C::TM; ++i) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int lrow = wm + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -146,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint8_t* __restric
             const float inv = lds_inv[lrow];
             unsigned long long best = 0;
 #pragma unroll
-            for (int j = 0; j < kTN; ++j) {
+            for (int j = 0; j < C::TN; ++j) {
                 const int col = n0 + wn + j * 32 + (lane & 31);
                 const int total = acc[i][j][r] - qs;
                 if (row < m && col < n) {
@@ -210,9 +261,15 @@ int launch_gemm(const uint8_t* packed, float w_scale, const float* w_scale_ptr, 
         argmax_init_kernel<<<(m + 255) / 256, 256, 0, s>>>(keys, m);
         if (hipGetLastError() != hipSuccess) return BL_ERR_LAUNCH;
     }
-    dim3 grid((n + kBN - 1) / kBN, (m + kBM - 1) / kBM);
-    gemm_kernel<<<grid, kThreads, 0, s>>>(packed, w_scale, w_scale_ptr, n, k, q, act_scale, act_sum, m, residual, y,
-                                          ldy, acc_out, keys);
+    if (m <= CfgSmall::BM) {
+        dim3 grid((n + CfgSmall::BN - 1) / CfgSmall::BN, (m + CfgSmall::BM - 1) / CfgSmall::BM);
+        gemm_kernel<CfgSmall><<<grid, CfgSmall::kThreads, 0, s>>>(packed, w_scale, w_scale_ptr, n, k, q, act_scale,
+                                                                  act_sum, m, residual, y, ldy, acc_out, keys);
+    } else {
+        dim3 grid((n + CfgLarge::BN - 1) / CfgLarge::BN, (m + CfgLarge::BM - 1) / CfgLarge::BM);
+        gemm_kernel<CfgLarge><<<grid, CfgLarge::kThreads, 0, s>>>(packed, w_scale, w_scale_ptr, n, k, q, act_scale,
+                                                                  act_sum, m, residual, y, ldy, acc_out, keys);
+    }
     if (hipGetLastError() != hipSuccess) return BL_ERR_LAUNCH;
     if (keys) {
         argmax_finish_kernel<<<(m + 255) / 256, 256, 0, s>>>(keys, m, row_argmax);
