@@ -328,12 +328,13 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
         const int mat = row / D, rin = row - mat * D;
         load_row<S1>(W + mat * dd + (size_t)rin * (D / 4), l1, w1);
         load_strided<D>(a.gains + (size_t)l * (3 * D + F), g1);
+        // P2's gains and stand-in input: its norm + quant runs right after P1
+        load_strided<D>(a.gains + (size_t)l * (3 * D + F) + D, g2);
+        load_strided<D>(a.z + (size_t)l * D, zv);
     };
     auto fetch2 = [&](int l) {
         const uint8_t* W = a.weights + (size_t)l * blob;
         load_row<S2>(W + 3 * dd + (size_t)(l2.active ? r2 + l2.ri : 0) * (D / 4), l2, w2);
-        load_strided<D>(a.gains + (size_t)l * (3 * D + F) + D, g2);
-        load_strided<D>(a.z + (size_t)l * D, zv);
     };
     auto fetch3 = [&](int l) {
         const uint8_t* W = a.weights + (size_t)l * blob;
@@ -377,6 +378,9 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
         }
         // ---- P2: o projection of the stand-in z, residual ----
         {
+            // z does not depend on the stream: its norm + quant runs before the
+            // wait for P1 to finish everywhere
+            norm_quant<D>(zv, g2, a.eps, sh, s_a, qsum);
             if (t < S2::R) sh.acc[t] = 0;
             fetch2(l);
             float fl[1];
@@ -384,7 +388,6 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
             if (l == 0 && w == 0 && t == 0)  // every workgroup has read the base by now
                 __hip_atomic_store(a.ctrl, base + 4u * (uint32_t)a.n_layers, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
-            norm_quant<D>(zv, g2, a.eps, sh, s_a, qsum);
             const int acc = dot_row<S2>(w2, l2, sh.q);
             if (l2.active) atomicAdd(&sh.acc[l2.ri], acc);
             __syncthreads();
