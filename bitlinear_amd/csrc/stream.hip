@@ -17,7 +17,8 @@
 // one workgroup per CU (256 on an MI355X) stays resident for the whole token:
 //   - each workgroup owns fixed output rows of every step and issues the loads
 //     of those weight rows (and of the step's RMSNorm gains) before it waits
-//     for the step's input, so the weight fetch overlaps the hand-over;
+//     for the step's input, so the weight fetch overlaps the hand-over. The
+//     rows go straight into registers in the layout of the MFMA B operand;
 //   - a step's output vector is published as 64-bit words {fp32 value, epoch}
 //     written with device-scope atomic stores; a consumer loads all words of
 //     the vector it needs in one batch and repeats until every epoch matches.
@@ -25,17 +26,21 @@
 //     separate barrier is needed;
 //   - every workgroup then computes the RMSNorm + activation quant of the full
 //     vector itself, so no extra round trip is spent on broadcasting q. The
-//     sum of squares keeps the fixed fp64 order of quant.hip: with the vector
-//     staged in LDS, thread l < 256 sums x[k]^2 for k = l, l+256, ... in
-//     ascending k, then an xor-butterfly combines the 256 partials (offsets 128
-//     and 64 through LDS, 32..1 with exact lane exchanges);
-//   - the dot products are those of gemv.hip (dot4 on shifted code masks
-//     against activations permuted once into LDS). Each row of a step gets
-//     floor(1024 / rows) lanes, and the lanes' partial sums meet in LDS through
-//     int32 atomic adds, which are exact in any order.
-// A workgroup has 1024 threads (4 waves per SIMD), so the vector work of a step
-// is spread over 4x the lanes of a one-wave-per-SIMD layout and its latencies
-// overlap.
+//     sum of squares keeps the fixed fp64 order of quant.hip: thread t sums
+//     x[k]^2 for k = t, t + 512, ... in ascending k, and an xor-butterfly
+//     combines the 512 partials (offsets 1..32 with exact lane exchanges,
+//     64..256 through LDS). P2's input does not depend on the stream, so its
+//     norm + quant runs before the wait for P1;
+//   - dot products: v_mfma_i32_16x16x64_i8 with the token in row 0 of A and
+//     16 weight rows as the columns of B (rows 1..15 of A are zero). A lane
+//     of B holds 16 weights of one row; from a packed 16-byte chunk (64
+//     weights) the masks 0x03, 0x0C, 0x30 per byte select the codes of weights
+//     4i+0, 4i+1, 4i+2 scaled by 1, 4, 16, and (w >> 2) & 0x30 those of 4i+3
+//     scaled by 16, so one AND (two for the last class) yields each operand.
+//     The activation vector sits in LDS in the matching byte order. The
+//     scaled accumulators are exact multiples of their scales and are shifted
+//     back exactly; the code offset (c = t + 1) is removed with sum(q).
+// A workgroup has 512 threads (8 waves, 2 per SIMD).
 // The P2/P4 rows of a workgroup are the same, so the residual x of its rows
 // stays in registers across the whole stream.
 //
@@ -57,17 +62,23 @@ constexpr int kMaxK = 10240;
 
 constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 
-// Geometry of one step: N output rows of K inputs spread over kGrid
-// workgroups; lanes per row and 16-byte chunks per lane.
-template <int N, int K>
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// One step: N output rows per stacked matrix (MATS matrices), K inputs. A
+// workgroup owns R consecutive rows of each matrix, RT = MATS * R in all. Its
+// dot products are ITEMS items (tile, s): rows 16 tile .. +15 against inputs
+// 256 s .. +255; wave w takes the contiguous items [w P, (w + 1) P).
+template <int N, int K, int MATS>
 struct Step {
-    static constexpr int R = cdiv(N, kGrid);  // rows per workgroup
-    static constexpr int Lr = kT / R;         // lanes per row
-    static constexpr int C = K / 64;          // chunks per row
-    static constexpr int CL = cdiv(C, Lr);    // chunks per lane
-    static_assert(R >= 1 && R <= 64, "rows per workgroup");
-    static_assert(Lr >= 1, "lanes per row");
-    static_assert(K % 64 == 0 && K <= kMaxK, "K");
+    static constexpr int R = N / kGrid;
+    static constexpr int RT = MATS * R;
+    static constexpr int TILES = cdiv(RT, 16);
+    static constexpr int KSTEPS = K / 256;
+    static constexpr int ITEMS = TILES * KSTEPS;
+    static constexpr int P = cdiv(ITEMS, kT / 64);
+    static_assert(N % kGrid == 0 && R >= 1, "rows per workgroup");
+    static_assert(K % 256 == 0 && K <= kMaxK, "K");
+    static_assert(RT <= 128, "LDS accumulators");
 };
 
 struct StreamArgs {
@@ -156,12 +167,17 @@ __device__ __forceinline__ int quant_one(float y, float scale)
     return (int)fminf(fmaxf(r, -128.0f), 127.0f);
 }
 
-// Byte position of activation k in the permuted LDS layout (per 16 values,
-// dword j holds k0+j, k0+4+j, k0+8+j, k0+12+j).
-__device__ __forceinline__ int perm_pos(int k) { return (k & ~15) | ((k & 3) << 2) | ((k >> 2) & 3); }
+// Byte position of activation k in LDS: within each 64 values, the 16 bytes at
+// 16 j hold k = 16 g + 4 i + j at byte 4 g + i (the order of the B operand
+// built from mask class j).
+__device__ __forceinline__ int q_pos(int k)
+{
+    return (k & ~63) | ((k & 3) << 4) | (((k >> 4) & 3) << 2) | ((k >> 2) & 3);
+}
 
 struct Shared {
-    __attribute__((aligned(16))) uint8_t q[kMaxK];  // quantized input vector, permuted
+    __attribute__((aligned(16))) uint8_t q[kMaxK];  // quantized input vector (q_pos order)
+    __attribute__((aligned(16))) uint8_t zero[64];  // A rows 1..15
     double red_d[kT / 64];
     float red_f[kT / 64];
     int red_i[kT / 64];
@@ -212,7 +228,7 @@ __device__ void norm_quant(const float* v, const float* g, float eps, Shared& sh
         if (k < N) {
             const int qv = quant_one(y[i], scale);
             sum += qv;
-            sh.q[perm_pos(k)] = (uint8_t)(qv & 0xff);
+            sh.q[q_pos(k)] = (uint8_t)(qv & 0xff);
         }
     }
     sum = wave_sum(sum);
@@ -225,70 +241,84 @@ __device__ void norm_quant(const float* v, const float* g, float eps, Shared& sh
     qsum_out = total;
 }
 
-__device__ __forceinline__ int dot16(uint32_t p, const uint4 q, int acc)
+__device__ __forceinline__ v4i mask4(const uint4 p, uint32_t m)
 {
-    acc = __builtin_amdgcn_sdot4((int)(p & kCodeMask), (int)q.x, acc, false);
-    acc = __builtin_amdgcn_sdot4((int)((p >> 2) & kCodeMask), (int)q.y, acc, false);
-    acc = __builtin_amdgcn_sdot4((int)((p >> 4) & kCodeMask), (int)q.z, acc, false);
-    acc = __builtin_amdgcn_sdot4((int)((p >> 6) & kCodeMask), (int)q.w, acc, false);
-    return acc;
+    return v4i{(int)(p.x & m), (int)(p.y & m), (int)(p.z & m), (int)(p.w & m)};
 }
 
-// One lane's part of a step: row ri = t / Lr of the workgroup's rows, chunks
-// j, j + Lr, ... of that row (j = t % Lr).
-template <class S>
-struct Lane {
-    int ri, j;
-    bool active;
-    __device__ Lane(int row0, int n_rows)
-    {
-        ri = threadIdx.x / S::Lr;
-        j = threadIdx.x % S::Lr;
-        active = ri < S::R && row0 + ri < n_rows;
-    }
-};
-
-// rowp must point at a valid row even for inactive lanes (the caller clamps
-// the row); chunks past the row end re-read its last chunk. Loads are
-// unconditional so that they all issue before the first wait; dot_row ignores
-// what inactive lanes and excess chunks loaded.
-template <class S>
-__device__ __forceinline__ void load_row(const uint8_t* rowp, const Lane<S>& ln, uint4* w)
+// Loads the B operands of this wave's items: lane (n, b) = (lane % 16,
+// lane / 16) takes bytes 64 s + 16 b .. +15 of slot row 16 tile + n (clamped to
+// the last row; items past the end repeat the last one, so every load is
+// unconditional and all issue before the first wait). row_ptr(r) is the
+// packed row r of the step.
+template <class S, class RowPtr>
+__device__ __forceinline__ void load_items(uint4* wr, RowPtr row_ptr)
 {
+    const int lane = threadIdx.x & 63, n = lane & 15, b = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
-    for (int c = 0; c < S::CL; ++c) {
-        const int ch = min(ln.j + c * S::Lr, S::C - 1);
-        w[c] = *reinterpret_cast<const uint4*>(rowp + (size_t)ch * 16);
+    for (int j = 0; j < S::P; ++j) {
+        const int it = min(wave * S::P + j, S::ITEMS - 1);
+        const int tile = it / S::KSTEPS, s = it - tile * S::KSTEPS;
+        const int row = min(16 * tile + n, S::RT - 1);
+        wr[j] = *reinterpret_cast<const uint4*>(row_ptr(row) + 64 * s + 16 * b);
     }
 }
 
+// The wave's items: one MFMA accumulator per mask class; when the tile
+// changes, and at the end, the row sums of codes x q (row 0 of C: lanes 0..15,
+// register 0) go to acc[] through LDS atomics, exact in any order.
 template <class S>
-__device__ __forceinline__ int dot_row(const uint4* w, const Lane<S>& ln, const uint8_t* q)
+__device__ __forceinline__ void dots(const uint4* wr, const uint8_t* q, const uint8_t* zero, int* acc)
 {
-    int acc = 0;
+    const int lane = threadIdx.x & 63, n = lane & 15, b = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint8_t* a_base = n == 0 ? q + 64 * b : zero;
+    const int a_step = n == 0 ? 256 : 0;
+    const v4i zc = {0, 0, 0, 0};
+    v4i c0 = zc, c1 = zc, c2 = zc, c3 = zc;
+    int tile = -1;
+    auto flush = [&]() {
+        const int v = c0[0] + (c1[0] >> 2) + ((c2[0] + c3[0]) >> 4);
+        if (lane < 16 && 16 * tile + lane < S::RT) atomicAdd(acc + 16 * tile + lane, v);
+        c0 = zc;
+        c1 = zc;
+        c2 = zc;
+        c3 = zc;
+    };
 #pragma unroll
-    for (int c = 0; c < S::CL; ++c) {
-        const int ch = ln.j + c * S::Lr;
-        if (S::CL * S::Lr <= S::C || ch < S::C) {  // the test folds away when every lane's chunks exist
-            const uint4* qp = reinterpret_cast<const uint4*>(q + (size_t)ch * 64);
-            acc = dot16(w[c].x, qp[0], acc);
-            acc = dot16(w[c].y, qp[1], acc);
-            acc = dot16(w[c].z, qp[2], acc);
-            acc = dot16(w[c].w, qp[3], acc);
+    for (int j = 0; j < S::P; ++j) {
+        const int it = wave * S::P + j;
+        if (it < S::ITEMS) {
+            const int tl = it / S::KSTEPS, s = it - tl * S::KSTEPS;
+            if (tl != tile) {
+                if (tile >= 0) flush();
+                tile = tl;
+            }
+            const uint8_t* ap = a_base + a_step * s;
+            const v4i a0 = *reinterpret_cast<const v4i*>(ap);
+            const v4i a1 = *reinterpret_cast<const v4i*>(ap + 16);
+            const v4i a2 = *reinterpret_cast<const v4i*>(ap + 32);
+            const v4i a3 = *reinterpret_cast<const v4i*>(ap + 48);
+            const uint4 p = wr[j];
+            const uint4 p3 = make_uint4(p.x >> 2, p.y >> 2, p.z >> 2, p.w >> 2);
+            c0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, mask4(p, kCodeMask), c0, 0, 0, 0);
+            c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, mask4(p, kCodeMask << 2), c1, 0, 0, 0);
+            c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a2, mask4(p, kCodeMask << 4), c2, 0, 0, 0);
+            c3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a3, mask4(p3, kCodeMask << 4), c3, 0, 0, 0);
         }
     }
-    return acc;
+    if (tile >= 0) flush();
 }
 
 template <int D, int F>
 __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
 {
-    using S1 = Step<3 * D, D>;  // q, k, v
-    using S2 = Step<D, D>;      // o (and the rows of x this workgroup owns)
-    using S3 = Step<F, D>;      // gate / up
-    using S4 = Step<D, F>;      // down
+    using S1 = Step<3 * D, D, 1>;  // q, k, v stacked
+    using S2 = Step<D, D, 1>;      // o (and the rows of x this workgroup owns)
+    using S3 = Step<F, D, 2>;      // gate rows, then up rows
+    using S4 = Step<D, F, 1>;      // down
     static_assert(S2::R == S4::R, "o and down share their rows");
-    static_assert(2 * S3::R <= 128 && S1::R <= 128, "LDS accumulators");
     constexpr int ND = cdiv(D, kT), NF = cdiv(F, kT);
     constexpr size_t dd = (size_t)D * D / 4, fd = (size_t)F * D / 4;
     constexpr size_t blob = 4 * dd + 3 * fd;
@@ -305,12 +335,9 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
     }
 
     const int r1 = w * S1::R, r2 = w * S2::R, r3 = w * S3::R;
-    const Lane<S1> l1(r1, 3 * D);
-    const Lane<S2> l2(r2, D);
-    const Lane<S3> l3(r3, F);
-    const Lane<S4> l4(r2, D);
     // epilogue thread t < R owns row t of the step
-    const bool e1 = t < S1::R && r1 + t < 3 * D, e2 = t < S2::R && r2 + t < D, e3 = t < S3::R && r3 + t < F;
+    const bool e1 = t < S1::R, e2 = t < S2::R, e3 = t < S3::R;
+    if (t < 16) reinterpret_cast<uint32_t*>(sh.zero)[t] = 0u;  // visible after the first barrier
 
     float xres = e2 ? a.x[r2 + t] : 0.0f;  // residual x of this workgroup's rows
     float s_a;
@@ -320,32 +347,31 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
     // step starts, before its wait: the fetch overlaps the hand-over. (Loading
     // a step earlier does not pay: a wave's loads complete in issue order, so
     // every later wait would also wait for the early loads.)
-    uint4 w1[S1::CL], w2[S2::CL], wg[S3::CL], wu[S3::CL], w4[S4::CL];
+    uint4 w1[S1::P], w2[S2::P], w3[S3::P], w4[S4::P];
     float g1[ND], g2[ND], g3[ND], g4[NF], zv[ND];
     auto fetch1 = [&](int l) {
-        const uint8_t* W = a.weights + (size_t)l * blob;
-        const int row = l1.active ? r1 + l1.ri : 0;
-        const int mat = row / D, rin = row - mat * D;
-        load_row<S1>(W + mat * dd + (size_t)rin * (D / 4), l1, w1);
+        // q, k, v are consecutive D x D/4 matrices: stacked row r is at r * D/4
+        const uint8_t* W = a.weights + (size_t)l * blob + (size_t)r1 * (D / 4);
+        load_items<S1>(w1, [&](int r) { return W + (size_t)r * (D / 4); });
         load_strided<D>(a.gains + (size_t)l * (3 * D + F), g1);
         // P2's gains and stand-in input: its norm + quant runs right after P1
         load_strided<D>(a.gains + (size_t)l * (3 * D + F) + D, g2);
         load_strided<D>(a.z + (size_t)l * D, zv);
     };
     auto fetch2 = [&](int l) {
-        const uint8_t* W = a.weights + (size_t)l * blob;
-        load_row<S2>(W + 3 * dd + (size_t)(l2.active ? r2 + l2.ri : 0) * (D / 4), l2, w2);
+        const uint8_t* W = a.weights + (size_t)l * blob + 3 * dd + (size_t)r2 * (D / 4);
+        load_items<S2>(w2, [&](int r) { return W + (size_t)r * (D / 4); });
     };
     auto fetch3 = [&](int l) {
-        const uint8_t* W = a.weights + (size_t)l * blob;
-        const size_t ro = (size_t)(l3.active ? r3 + l3.ri : 0) * (D / 4);
-        load_row<S3>(W + 4 * dd + ro, l3, wg);
-        load_row<S3>(W + 4 * dd + fd + ro, l3, wu);
+        const uint8_t* W = a.weights + (size_t)l * blob + 4 * dd + (size_t)r3 * (D / 4);
+        load_items<S3>(w3, [&](int r) {
+            return r < S3::R ? W + (size_t)r * (D / 4) : W + fd + (size_t)(r - S3::R) * (D / 4);
+        });
         load_strided<D>(a.gains + (size_t)l * (3 * D + F) + 2 * D, g3);
     };
     auto fetch4 = [&](int l) {
-        const uint8_t* W = a.weights + (size_t)l * blob;
-        load_row<S4>(W + 4 * dd + 2 * fd + (size_t)(l4.active ? r2 + l4.ri : 0) * (F / 4), l4, w4);
+        const uint8_t* W = a.weights + (size_t)l * blob + 4 * dd + 2 * fd + (size_t)r2 * (F / 4);
+        load_items<S4>(w4, [&](int r) { return W + (size_t)r * (F / 4); });
         load_strided<F>(a.gains + (size_t)l * (3 * D + F) + 3 * D, g4);
     };
     for (int l = 0; l < a.n_layers; ++l) {
@@ -366,8 +392,7 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
                 return;
             }
             norm_quant<D>(v, g1, a.eps, sh, s_a, qsum);
-            const int acc = dot_row<S1>(w1, l1, sh.q);
-            if (l1.active) atomicAdd(&sh.acc[l1.ri], acc);
+            dots<S1>(w1, sh.q, sh.zero, sh.acc);
             __syncthreads();
             if (e1) {
                 const int row = r1 + t, mat = row / D;
@@ -388,8 +413,7 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
             if (l == 0 && w == 0 && t == 0)  // every workgroup has read the base by now
                 __hip_atomic_store(a.ctrl, base + 4u * (uint32_t)a.n_layers, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
-            const int acc = dot_row<S2>(w2, l2, sh.q);
-            if (l2.active) atomicAdd(&sh.acc[l2.ri], acc);
+            dots<S2>(w2, sh.q, sh.zero, sh.acc);
             __syncthreads();
             if (e2) {
                 const float inv = 1.0f / (s_a * sw[3]);
@@ -407,12 +431,7 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
             float v[ND];
             if (!poll_vec<D>(a.xb, E + 2, v, a.ctrl, t_start)) return;
             norm_quant<D>(v, g3, a.eps, sh, s_a, qsum);
-            const int ag = dot_row<S3>(wg, l3, sh.q);
-            const int au = dot_row<S3>(wu, l3, sh.q);
-            if (l3.active) {
-                atomicAdd(&sh.acc[l3.ri], ag);
-                atomicAdd(&sh.acc[S3::R + l3.ri], au);
-            }
+            dots<S3>(w3, sh.q, sh.zero, sh.acc);
             __syncthreads();
             if (e3) {
                 const float gate = (float)(sh.acc[t] - qsum) * (1.0f / (s_a * sw[4]));
@@ -429,8 +448,7 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
             float v[NF];
             if (!poll_vec<F>(a.hh, E + 3, v, a.ctrl, t_start)) return;
             norm_quant<F>(v, g4, a.eps, sh, s_a, qsum);
-            const int acc = dot_row<S4>(w4, l4, sh.q);
-            if (l4.active) atomicAdd(&sh.acc[l4.ri], acc);
+            dots<S4>(w4, sh.q, sh.zero, sh.acc);
             __syncthreads();
             if (e2) {
                 const float inv = 1.0f / (s_a * sw[6]);
