@@ -3,9 +3,9 @@
 //
 // acc[m][n] = sum_k q[m][k] * t[n][k] is a dense int8 contraction, so it runs on
 // v_mfma_i32_32x32x32_i8 (32x32 output tile, 32-deep K per instruction, exact
-// int32 accumulation). Tiles are staged through double-buffered LDS: the next K
-// step's global loads are in flight while the current step's MFMAs run, and
-// one barrier per K step separates the buffers. The weights stay 2-bit packed
+// int32 accumulation). Tiles are staged through double-buffered LDS; the global
+// loads run two K steps ahead (two register staging sets), so each has a whole
+// step to land, and one barrier per K step separates the LDS buffers. The weights stay 2-bit packed
 // in HBM and in LDS; each wave unpacks its B operand in registers: the packed dword of 16 consecutive
 // weights of column n gives, through (w >> 2j) & 0x03030303 for j = 0..3, the
 // codes c = t + 1 of weights {j, 4+j, 8+j, 12+j}. The activation tile is staged
@@ -47,37 +47,66 @@ __device__ __forceinline__ uint4 permute16(const uint4 v)
 constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 // Tile configuration: a BM x BN block tile, WAVES_M x WAVES_N waves, each
-// owning a (BM/WAVES_M) x (BN/WAVES_N) wave tile of 32x32 MFMA tiles; BK-deep
-// K steps. The packed weight tile holds BK/4 bytes per row.
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_>
+// owning a (BM/WAVES_M) x (BN/WAVES_N) wave tile of MT x MT MFMA tiles; BK-deep
+// K steps. MT = 32: v_mfma_i32_32x32x32_i8 (32 inputs per instruction); MT = 16:
+// v_mfma_i32_16x16x64_i8 (64 inputs). Either way lane l of an operand holds the
+// 16 inputs 16 (l / MT) .. +15 of row / column l % MT, so the packed weight tile
+// holds BK/4 bytes per row and every lane unpacks one packed dword per operand.
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int MT_>
 struct Cfg {
-    static constexpr int BM = BM_, BN = BN_, BK = BK_;
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, MT = MT_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
     static constexpr int kThreads = 64 * WAVES_M * WAVES_N;
     static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
-    static constexpr int TM = WM / 32, TN = WN / 32;
+    static constexpr int TM = WM / MT, TN = WN / MT;
+    static constexpr int KT = 1024 / MT;   // inputs per MFMA
+    static constexpr int NACC = MT * MT / 64;  // accumulator registers per tile and lane
     static constexpr int SA = BK + 16;     // LDS bytes per activation row (padded against bank conflicts)
     static constexpr int SB = BK / 4 + 4;  // LDS bytes per packed weight row (5 dwords: conflict-free reads)
     static constexpr int A_CHUNKS = BM * BK / 16, B_CHUNKS = BN * BK / 64;  // 16-byte chunks per K step
     static constexpr int A_PER_T = cdiv(A_CHUNKS, kThreads), B_PER_T = cdiv(B_CHUNKS, kThreads);
-    static_assert(WM % 32 == 0 && WN % 32 == 0 && BK % 64 == 0, "tile shape");
+    static_assert(MT == 16 || MT == 32, "MFMA shape");
+    static_assert(WM % MT == 0 && WN % MT == 0 && BK % 64 == 0 && BK % KT == 0, "tile shape");
+};
+
+template <int MT>
+struct Mfma;
+template <>
+struct Mfma<32> {
+    typedef v16i acc_t;
+    static __device__ __forceinline__ acc_t run(v4i a, v4i b, acc_t c)
+    {
+        return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+    }
+    // register r of lane l holds row 8 (r / 4) + 4 (l / 32) + r % 4 of the tile
+    static __device__ __forceinline__ int row(int lane, int r) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+};
+template <>
+struct Mfma<16> {
+    typedef v4i acc_t;
+    static __device__ __forceinline__ acc_t run(v4i a, v4i b, acc_t c)
+    {
+        return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+    }
+    // register r of lane l holds row 4 (l / 16) + r of the tile
+    static __device__ __forceinline__ int row(int lane, int r) { return 4 * (lane >> 4) + r; }
 };
 
 // Large M (prefill): 128 x 320 tiles -- 512 tiles for 2048 x 10240, two per CU.
-using CfgLarge = Cfg<128, 320, 2, 2, 64>;
+// The four waves split the columns (128 x 80 each, 8 x 5 tiles of 16x16x64),
+// so every packed weight column is unpacked by one wave only.
+using CfgLarge = Cfg<128, 320, 1, 4, 64, 16>;
 // Small M (batched decode, LM head): 32 x 256 tiles.
-using CfgSmall = Cfg<32, 256, 1, 4, 64>;
+using CfgSmall = Cfg<32, 256, 1, 4, 64, 32>;
 
 template <class C>
-__global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(2))) void gemm_kernel(const uint8_t* __restrict__ packed, float w_scale,
-                                                           const float* __restrict__ w_scale_ptr, int n, int k,
-                                                           const int8_t* __restrict__ q,
-                                                           const float* __restrict__ act_scale,
-                                                           const int32_t* __restrict__ act_sum, int m,
-                                                           const float* residual, float* y, int ldy,
-                                                           int32_t* __restrict__ acc_out,
-                                                           unsigned long long* __restrict__ keys)
+__global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(2))) void gemm_kernel(
+    const uint8_t* __restrict__ packed, float w_scale, const float* __restrict__ w_scale_ptr, int n, int k,
+    const int8_t* __restrict__ q, const float* __restrict__ act_scale, const int32_t* __restrict__ act_sum, int m,
+    const float* residual, float* y, int ldy, int32_t* __restrict__ acc_out, unsigned long long* __restrict__ keys)
 {
+    using M = Mfma<C::MT>;
+    constexpr int MT = C::MT;
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][C::BM * C::SA];
     __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][C::BN * C::SB];
     __shared__ float lds_inv[C::BM];
@@ -103,31 +132,32 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(2))
     // Global -> register staging of one K step: activation chunks (16 bytes of
     // one row) and packed weight chunks (16 bytes of one weight row). Rows past
     // m / n read row 0 (in bounds); their results are never stored.
-    uint4 ga[C::A_PER_T], gb[C::B_PER_T];
-    auto load_global = [&](int s) {
+    uint4 ga[2][C::A_PER_T], gb[2][C::B_PER_T];  // two K steps in flight
+    // st: the staging set (a constant at every call, so the arrays stay in registers)
+    auto load_global = [&](int s, int st) __attribute__((always_inline)) {
         const int k0 = s * C::BK;
 #pragma unroll
         for (int c = 0; c < C::A_PER_T; ++c) {
             const int chunk = tid + c * C::kThreads;
             const int row = chunk / (C::BK / 16), kg = chunk % (C::BK / 16);
             const int grow = (chunk < C::A_CHUNKS && m0 + row < m) ? m0 + row : 0;
-            ga[c] = *reinterpret_cast<const uint4*>(q + (size_t)grow * k + k0 + kg * 16);
+            ga[st][c] = *reinterpret_cast<const uint4*>(q + (size_t)grow * k + k0 + kg * 16);
         }
 #pragma unroll
         for (int c = 0; c < C::B_PER_T; ++c) {
             const int chunk = tid + c * C::kThreads;
             const int row = chunk / (C::BK / 64), kg = chunk % (C::BK / 64);
             const int gcol = (chunk < C::B_CHUNKS && n0 + row < n) ? n0 + row : 0;
-            gb[c] = *reinterpret_cast<const uint4*>(packed + (size_t)gcol * kb + k0 / 4 + kg * 16);
+            gb[st][c] = *reinterpret_cast<const uint4*>(packed + (size_t)gcol * kb + k0 / 4 + kg * 16);
         }
     };
-    auto store_lds = [&](int buf) {
+    auto store_lds = [&](int buf, int st) __attribute__((always_inline)) {
 #pragma unroll
         for (int c = 0; c < C::A_PER_T; ++c) {
             const int chunk = tid + c * C::kThreads;
             if (C::A_CHUNKS % C::kThreads == 0 || chunk < C::A_CHUNKS) {
                 const int row = chunk / (C::BK / 16), kg = chunk % (C::BK / 16);
-                *reinterpret_cast<uint4*>(lds_a[buf] + row * C::SA + kg * 16) = permute16(ga[c]);
+                *reinterpret_cast<uint4*>(lds_a[buf] + row * C::SA + kg * 16) = permute16(ga[st][c]);
             }
         }
 #pragma unroll
@@ -136,69 +166,77 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(2))
             if (C::B_CHUNKS % C::kThreads == 0 || chunk < C::B_CHUNKS) {
                 const int row = chunk / (C::BK / 64), kg = chunk % (C::BK / 64);
                 uint32_t* dst = reinterpret_cast<uint32_t*>(lds_b[buf] + row * C::SB + kg * 16);
-                dst[0] = gb[c].x;
-                dst[1] = gb[c].y;
-                dst[2] = gb[c].z;
-                dst[3] = gb[c].w;
+                dst[0] = gb[st][c].x;
+                dst[1] = gb[st][c].y;
+                dst[2] = gb[st][c].z;
+                dst[3] = gb[st][c].w;
             }
         }
     };
 
-    v16i acc[C::TM][C::TN];
+    typename M::acc_t acc[C::TM][C::TN];
 #pragma unroll
     for (int i = 0; i < C::TM; ++i)
 #pragma unroll
         for (int j = 0; j < C::TN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+            for (int r = 0; r < C::NACC; ++r) acc[i][j][r] = 0;
 
-    load_global(0);
-    store_lds(0);
-    __syncthreads();
-    for (int s = 0; s < nk; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < nk) load_global(s + 1);  // in flight during this step's MFMAs
+    // One K step: loads for step s + 2 go out, the MFMAs of step s run from LDS
+    // buffer s & 1, and step s + 1 (loaded one step earlier) is stored into the
+    // other buffer. Steps alternate staging sets and buffers, so the loop is
+    // unrolled by two with constant set indices.
+    auto k_step = [&](int s, int cur) __attribute__((always_inline)) {
+        if (s + 2 < nk) load_global(s + 2, cur);  // two steps ahead: a whole step to land
 #pragma unroll
-        for (int ks = 0; ks < C::BK / 32; ++ks) {
-            const int kofs = ks * 32 + (lane >> 5) * 16;  // this lane's 16 K values
+        for (int ks = 0; ks < C::BK / C::KT; ++ks) {
+            const int kofs = ks * C::KT + (lane / MT) * 16;  // this lane's 16 K values
             v4i a[C::TM], b[C::TN];
 #pragma unroll
             for (int i = 0; i < C::TM; ++i) {
                 const uint4 v =
-                    *reinterpret_cast<const uint4*>(lds_a[buf] + (wm + i * 32 + (lane & 31)) * C::SA + kofs);
+                    *reinterpret_cast<const uint4*>(lds_a[cur] + (wm + i * MT + (lane % MT)) * C::SA + kofs);
                 a[i] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
             }
 #pragma unroll
             for (int j = 0; j < C::TN; ++j) {
                 const uint32_t p =
-                    *reinterpret_cast<const uint32_t*>(lds_b[buf] + (wn + j * 32 + (lane & 31)) * C::SB + kofs / 4);
+                    *reinterpret_cast<const uint32_t*>(lds_b[cur] + (wn + j * MT + (lane % MT)) * C::SB + kofs / 4);
                 b[j] = v4i{(int)(p & kCodeMask), (int)((p >> 2) & kCodeMask), (int)((p >> 4) & kCodeMask),
                            (int)((p >> 6) & kCodeMask)};
             }
 #pragma unroll
             for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-                for (int j = 0; j < C::TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < C::TN; ++j) acc[i][j] = M::run(a[i], b[j], acc[i][j]);
         }
-        if (s + 1 < nk) store_lds(buf ^ 1);  // the other buffer: last read before the previous barrier
+        // the other buffer was last read before the previous barrier
+        if (s + 1 < nk) store_lds(cur ^ 1, cur ^ 1);
         __syncthreads();
+    };
+    load_global(0, 0);
+    if (nk > 1) load_global(1, 1);
+    store_lds(0, 0);
+    __syncthreads();
+    for (int s = 0; s < nk; s += 2) {
+        k_step(s, 0);
+        if (s + 1 < nk) k_step(s + 1, 1);
     }
 
-    // epilogue: lane holds column (lane & 31) of each 32x32 tile; register r
-    // holds row 8 (r / 4) + 4 (lane / 32) + (r % 4).
+    // epilogue: lane holds column lane % MT of each tile, register r the row
+    // M::row(lane, r). For the argmax, the MT lanes of a row reduce their keys.
 #pragma unroll
     for (int i = 0; i < C::TM; ++i) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int lrow = wm + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        for (int r = 0; r < C::NACC; ++r) {
+            const int lrow = wm + i * MT + M::row(lane, r);
             const int row = m0 + lrow;
             const int qs = lds_qsum[lrow];
             const float inv = lds_inv[lrow];
             unsigned long long best = 0;
 #pragma unroll
             for (int j = 0; j < C::TN; ++j) {
-                const int col = n0 + wn + j * 32 + (lane & 31);
+                const int col = n0 + wn + j * MT + (lane % MT);
                 const int total = acc[i][j][r] - qs;
                 if (row < m && col < n) {
                     const size_t o = (size_t)row * ldy + col;
@@ -218,11 +256,11 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(2))
             }
             if (keys) {
 #pragma unroll
-                for (int off = 16; off >= 1; off >>= 1) {
+                for (int off = MT / 2; off >= 1; off >>= 1) {
                     const unsigned long long other = __shfl_xor(best, off, 64);
                     best = other > best ? other : best;
                 }
-                if ((lane & 31) == 0 && row < m && best != 0) atomicMax(keys + row, best);
+                if ((lane % MT) == 0 && row < m && best != 0) atomicMax(keys + row, best);
             }
         }
     }
