@@ -8,6 +8,7 @@ namespace {
 using bl::aligned;
 
 constexpr int64_t kMaxGemvM = 8;
+constexpr int64_t kMaxSkinnyM = 32;
 constexpr int64_t kMaxGemvK = 32768;
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
 
@@ -248,10 +249,38 @@ int bitnet_decode_stream(const uint8_t* weights, const float* scales, const floa
     float* so = at<float>(workspace, L.s_o);
     int32_t* qso = at<int32_t>(workspace, L.qs_o);
     void* ffn_ws = at<void>(workspace, L.ffn);
-    const int M = (int)m, D = (int)d;
+    const int M = (int)m, D = (int)d, F = (int)f;
     const size_t blob = bitnet_layer_bytes(d, f);
     const size_t dd = (size_t)(d * d) / 4, fd = (size_t)(f * d) / 4;
     const size_t gstride = (size_t)(3 * d + f);
+    if (m > kMaxGemvM && m <= kMaxSkinnyM) {
+        // 9..32 tokens: every projection is one skinny MFMA launch over
+        // activations quantised straight into its operand order
+        const Layout FL = ffn_layout(m, d, f);
+        int8_t* q1 = at<int8_t>(ffn_ws, FL.off[BITNET_FFN_WS_Q1]);
+        float* s1 = at<float>(ffn_ws, FL.off[BITNET_FFN_WS_S1]);
+        int32_t* qs1 = at<int32_t>(ffn_ws, FL.off[BITNET_FFN_WS_QS1]);
+        float* h = at<float>(ffn_ws, FL.off[BITNET_FFN_WS_H]);
+        int8_t* q2 = at<int8_t>(ffn_ws, FL.off[BITNET_FFN_WS_Q2]);
+        float* s2 = at<float>(ffn_ws, FL.off[BITNET_FFN_WS_S2]);
+        int32_t* qs2 = at<int32_t>(ffn_ws, FL.off[BITNET_FFN_WS_QS2]);
+        for (int64_t l = 0; l < n_layers; ++l) {
+            const uint8_t* wl = weights + (size_t)l * blob;
+            const float* sl = scales + 7 * l;
+            const float* gl = gains + l * gstride;
+            float* qkv_l = qkv ? qkv + (size_t)l * m * 3 * d : at<float>(workspace, L.qkv);
+            int rc = bl::launch_quant_act(x, gl, eps, M, D, qa, sa, qsa, s, true);
+            if (!rc) rc = bl::launch_skinny(wl, sl, D, 3 * D, D, qa, sa, qsa, M, nullptr, qkv_l, 3 * D, s);
+            if (!rc) rc = bl::launch_quant_act(z + (size_t)l * m * d, gl + d, eps, M, D, qo, so, qso, s, true);
+            if (!rc) rc = bl::launch_skinny(wl + 3 * dd, sl + 3, D, D, D, qo, so, qso, M, x, x, D, s);
+            if (!rc) rc = bl::launch_quant_act(x, gl + 2 * d, eps, M, D, q1, s1, qs1, s, true);
+            if (!rc) rc = bl::launch_skinny_gateup(wl + 4 * dd, wl + 4 * dd + fd, sl + 4, F, D, q1, s1, qs1, M, h, s);
+            if (!rc) rc = bl::launch_quant_act(h, gl + 3 * d, eps, M, F, q2, s2, qs2, s, true);
+            if (!rc) rc = bl::launch_skinny(wl + 4 * dd + 2 * fd, sl + 6, D, D, F, q2, s2, qs2, M, x, x, D, s);
+            if (rc) return rc;
+        }
+        return BL_OK;
+    }
     for (int64_t l = 0; l < n_layers; ++l) {
         const uint8_t* wl = weights + (size_t)l * blob;
         const float* sl = scales + 7 * l;

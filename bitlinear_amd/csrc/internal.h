@@ -12,9 +12,11 @@ namespace bl {
 // Launchers (defined in the .hip files). They assume validated arguments and
 // return BL_OK or BL_ERR_LAUNCH.
 
-// [RMSNorm +] activation quant, one workgroup per token.
+// [RMSNorm +] activation quant, one workgroup per token. With perm16, q is
+// written with each 16 values 4x4 byte-transposed (byte 4 j + g of a group
+// holds value 4 g + j), the operand order of the skinny MFMA kernels.
 int launch_quant_act(const float* x, const float* gain, float eps, int m, int k, int8_t* q,
-                     float* act_scale, int32_t* act_sum, hipStream_t s);
+                     float* act_scale, int32_t* act_sum, hipStream_t s, bool perm16 = false);
 
 // Decode GEMV, m in [1, 8]. The weight scale is read from w_scale_ptr when it
 // is non-null, else w_scale is used.
@@ -49,6 +51,21 @@ size_t stream_ll_words(int d, int f);
 int launch_stream_persistent(const uint8_t* weights, const float* scales, const float* gains, const float* z,
                              int n_layers, int d, int f, float eps, float* x, float* qkv, long long qkv_stride,
                              void* ll_region, uint32_t* ctrl, hipStream_t s);
+
+// Skinny MFMA GEMM for m <= 32 tokens whose activations are in the perm16
+// layout: y[m][n] = (acc - act_sum) / (act_scale * s_w) (+ residual), with
+// n / n_per_scale selecting the weight scale w_scale_ptr[.] of consecutive
+// stacked matrices. Row stride ldy for y and residual.
+int launch_skinny(const uint8_t* packed, const float* w_scale_ptr, int n_per_scale, int n, int k, const int8_t* q,
+                  const float* act_scale, const int32_t* act_sum, int m, const float* residual, float* y, int ldy,
+                  hipStream_t s);
+
+// Fused gate/up for m <= 32 tokens (perm16 activations): h[m][f] =
+// relu(gate)^2 * up, gate / up from the f x d matrices w_gate / w_up with
+// scales scale_ptr[0] / scale_ptr[1].
+int launch_skinny_gateup(const uint8_t* w_gate, const uint8_t* w_up, const float* scale_ptr, int f, int d,
+                         const int8_t* q, const float* act_scale, const int32_t* act_sum, int m, float* h,
+                         hipStream_t s);
 
 // h = relu(gate)^2 * up, elementwise.
 int launch_relu2_mul(const float* gate, const float* up, int64_t count, float* h, hipStream_t s);

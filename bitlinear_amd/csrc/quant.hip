@@ -11,6 +11,9 @@
 //          of this ABI uses; r = fl32(1 / sqrt(ss / k + eps)) in fp64.
 //   pass 2: y = fl32(fl32(x * r) * g) and absmax over the row.
 //   pass 3: s_a = fl32(127 / max(absmax, 1e-5)), q = clamp(rne(y * s_a)), sum(q).
+//          Optionally q is written with each 16 values 4x4 byte-transposed, the
+//          order in which the MFMA kernels unpack ternary weights (an internal
+//          layout of the batched layer stream).
 // Passes 2 and 3 each re-read the row (an L2 hit after pass 1) and recompute y
 // identically, so no fp32 row has to be stored.
 #include "internal.h"
@@ -42,7 +45,7 @@ __device__ __forceinline__ float4 normed(const float* xr, const float* gain, flo
     return y;
 }
 
-template <bool kNorm>
+template <bool kNorm, bool kPerm>
 __global__ __launch_bounds__(kThreads) void quant_act_kernel(const float* __restrict__ x,
                                                              const float* __restrict__ gain, float eps, int k,
                                                              int8_t* __restrict__ q, float* __restrict__ act_scale,
@@ -90,9 +93,19 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(const float* __rest
         const int q0 = quant_one(y.x, scale), q1 = quant_one(y.y, scale);
         const int q2 = quant_one(y.z, scale), q3 = quant_one(y.w, scale);
         sum += q0 + q1 + q2 + q3;
-        const uint32_t packed = (uint32_t)(q0 & 0xff) | ((uint32_t)(q1 & 0xff) << 8) |
-                                ((uint32_t)(q2 & 0xff) << 16) | ((uint32_t)(q3 & 0xff) << 24);
-        *reinterpret_cast<uint32_t*>(qr + i) = packed;
+        if (kPerm) {
+            // within each 16 values, byte 4 j + g holds value 4 g + j (k = i + j
+            // sits at (i & ~15) + 4 j + ((i >> 2) & 3))
+            int8_t* b = qr + (i & ~15) + ((i >> 2) & 3);
+            b[0] = (int8_t)q0;
+            b[4] = (int8_t)q1;
+            b[8] = (int8_t)q2;
+            b[12] = (int8_t)q3;
+        } else {
+            const uint32_t packed = (uint32_t)(q0 & 0xff) | ((uint32_t)(q1 & 0xff) << 8) |
+                                    ((uint32_t)(q2 & 0xff) << 16) | ((uint32_t)(q3 & 0xff) << 24);
+            *reinterpret_cast<uint32_t*>(qr + i) = packed;
+        }
     }
     sum = wave_sum(sum);
     if (lane == 0) wsum[wave] = sum;
@@ -109,12 +122,18 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(const float* __rest
 }  // namespace
 
 int launch_quant_act(const float* x, const float* gain, float eps, int m, int k, int8_t* q, float* act_scale,
-                     int32_t* act_sum, hipStream_t s)
+                     int32_t* act_sum, hipStream_t s, bool perm16)
 {
-    if (gain)
-        quant_act_kernel<true><<<m, kThreads, 0, s>>>(x, gain, eps, k, q, act_scale, act_sum);
-    else
-        quant_act_kernel<false><<<m, kThreads, 0, s>>>(x, gain, eps, k, q, act_scale, act_sum);
+    if (perm16) {
+        if (gain)
+            quant_act_kernel<true, true><<<m, kThreads, 0, s>>>(x, gain, eps, k, q, act_scale, act_sum);
+        else
+            quant_act_kernel<false, true><<<m, kThreads, 0, s>>>(x, gain, eps, k, q, act_scale, act_sum);
+    } else if (gain) {
+        quant_act_kernel<true, false><<<m, kThreads, 0, s>>>(x, gain, eps, k, q, act_scale, act_sum);
+    } else {
+        quant_act_kernel<false, false><<<m, kThreads, 0, s>>>(x, gain, eps, k, q, act_scale, act_sum);
+    }
     return hipGetLastError() == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
 }
 

@@ -222,7 +222,8 @@ def test_ffn(bl, olib, m, d, f, res):
 
 @pytest.mark.parametrize("n_layers,m,d,f", [(2, 1, 128, 512), (3, 2, 256, 640), (3, 1, 256, 1024),
                                             (2, 1, 2560, 10240), (2, 1, 2048, 8192), (2, 12, 192, 384),
-                                            (2, 32, 2048, 8192)])
+                                            (2, 9, 320, 1088), (2, 25, 512, 1536), (2, 32, 2048, 8192),
+                                            (2, 33, 256, 512), (1, 16, 256, 8448)])
 def test_decode_stream(bl, olib, n_layers, m, d, f):
     from gpu_helpers import make_layers, run_stream, stream_ctrl
     log(f"stream layers={n_layers} m={m} d={d} f={f}")
