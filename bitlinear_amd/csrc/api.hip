@@ -79,6 +79,42 @@ inline T* at(void* base, size_t off)
     return reinterpret_cast<T*>(static_cast<uint8_t*>(base) + off);
 }
 
+// A skinny product of one matrix (or of stacked matrices with per-matrix
+// scales from w_scale_ptr, n_per_scale rows each).
+bl::SkinnyArgs skinny(const uint8_t* w, const float* w_scale_ptr, float w_scale, int n_per_scale, int n, int k,
+                      const int8_t* q, const float* act_scale, const int32_t* act_sum, int m, const float* residual,
+                      float* y, int ldy, int32_t* acc = nullptr)
+{
+    bl::SkinnyArgs a;
+    a.w0 = w;
+    a.w_scale_ptr = w_scale_ptr;
+    a.w_scale0 = w_scale;
+    a.n_per_scale = n_per_scale;
+    a.n = n;
+    a.k = k;
+    a.q = q;
+    a.act_scale = act_scale;
+    a.act_sum = act_sum;
+    a.m = m;
+    a.residual = residual;
+    a.y = y;
+    a.ldy = ldy;
+    a.acc0 = acc;
+    return a;
+}
+
+// The fused gate/up of f rows over d inputs: h[m][f] = relu(gate)^2 * up.
+bl::SkinnyArgs skinny_gateup(const uint8_t* w_gate, float s_gate, const uint8_t* w_up, float s_up,
+                             const float* scale_ptr, int f, int d, const int8_t* q, const float* act_scale,
+                             const int32_t* act_sum, int m, float* h, int32_t* acc_gate, int32_t* acc_up)
+{
+    bl::SkinnyArgs a = skinny(w_gate, scale_ptr, s_gate, f, f, d, q, act_scale, act_sum, m, nullptr, h, f, acc_gate);
+    a.w1 = w_up;
+    a.w_scale1 = s_up;
+    a.acc1 = acc_up;
+    return a;
+}
+
 int ffn_impl(const float* x, int64_t m, int64_t d, int64_t f, const float* g_ffn, const float* g_sub, float eps,
              const uint8_t* w_gate, float s_gate, const uint8_t* w_up, float s_up, const uint8_t* w_down,
              float s_down, const float* scale_ptr /* [gate, up, down] or null */, const float* residual, float* out,
@@ -102,6 +138,10 @@ int ffn_impl(const float* x, int64_t m, int64_t d, int64_t f, const float* g_ffn
     if (rc) return rc;
     if (m <= kMaxGemvM) {
         rc = bl::launch_gateup(w_gate, s_gate, w_up, s_up, scale_ptr, F, D, q1, s1, qs1, M, h, acc_g, acc_u, s);
+    } else if (m <= kMaxSkinnyM) {
+        rc = bl::launch_skinny(skinny_gateup(w_gate, s_gate, w_up, s_up, scale_ptr, F, D, q1, s1, qs1, M, h, acc_g,
+                                             acc_u),
+                               true, s);
     } else {
         float* gate = at<float>(ws, L.off[BITNET_FFN_WS_GATE]);
         float* up = at<float>(ws, L.off[BITNET_FFN_WS_UP]);
@@ -118,6 +158,9 @@ int ffn_impl(const float* x, int64_t m, int64_t d, int64_t f, const float* g_ffn
     const float* sdp = scale_ptr ? scale_ptr + 2 : nullptr;
     if (m <= kMaxGemvM)
         return bl::launch_gemv(w_down, s_down, sdp, D, F, q2, s2, qs2, M, residual, out, acc_d, s);
+    if (m <= kMaxSkinnyM)
+        return bl::launch_skinny(skinny(w_down, sdp, s_down, D, D, F, q2, s2, qs2, M, residual, out, D, acc_d), true,
+                                 s);
     return bl::launch_gemm(w_down, s_down, sdp, D, F, q2, s2, qs2, M, residual, out, D, acc_d, nullptr, nullptr, s);
 }
 
@@ -152,9 +195,10 @@ int bitlinear_gemv(const uint8_t* packed, float w_scale, int64_t n, int64_t k, c
 
 size_t bitlinear_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int with_argmax)
 {
-    (void)n;
     (void)k;
-    if (!with_argmax || m <= 0) return 0;
+    if (!with_argmax || m <= 0 || n <= 0) return 0;
+    if (m <= kMaxSkinnyM)  // one key per token and 32-column tile
+        return align_up((size_t)m * (size_t)((n + 31) / 32) * 8, 256);
     return align_up((size_t)m * 8, 256);
 }
 
@@ -173,6 +217,16 @@ int bitlinear_gemm(const uint8_t* packed, float w_scale, int64_t n, int64_t k, c
         return BL_ERR_ALIGN;
     if (!(w_scale > 0.0f) || !(w_scale < INFINITY)) return BL_ERR_VALUE;
     if (row_argmax && workspace_bytes < bitlinear_gemm_workspace_bytes(m, n, k, 1)) return BL_ERR_WORKSPACE;
+    if (m <= kMaxSkinnyM) {
+        bl::SkinnyArgs a = skinny(packed, nullptr, w_scale, 1, (int)n, (int)k, q, act_scale, act_sum, (int)m, residual,
+                                  y, (int)n, acc_out);
+        unsigned long long* keys = row_argmax ? static_cast<unsigned long long*>(workspace) : nullptr;
+        a.tile_keys = keys;
+        int rc = bl::launch_skinny(a, true, as_stream(stream));
+        if (!rc && keys)
+            rc = bl::launch_tile_argmax(keys, bl::skinny_tiles((int)n, false), (int)m, row_argmax, as_stream(stream));
+        return rc;
+    }
     return bl::launch_gemm(packed, w_scale, nullptr, (int)n, (int)k, q, act_scale, act_sum, (int)m, residual, y,
                            (int)n, acc_out, row_argmax, static_cast<unsigned long long*>(workspace),
                            as_stream(stream));
@@ -269,14 +323,22 @@ int bitnet_decode_stream(const uint8_t* weights, const float* scales, const floa
             const float* sl = scales + 7 * l;
             const float* gl = gains + l * gstride;
             float* qkv_l = qkv ? qkv + (size_t)l * m * 3 * d : at<float>(workspace, L.qkv);
+            const uint8_t* wg = wl + 4 * dd;
             int rc = bl::launch_quant_act(x, gl, eps, M, D, qa, sa, qsa, s, true);
-            if (!rc) rc = bl::launch_skinny(wl, sl, D, 3 * D, D, qa, sa, qsa, M, nullptr, qkv_l, 3 * D, s);
+            if (!rc)
+                rc = bl::launch_skinny(skinny(wl, sl, 0.0f, D, 3 * D, D, qa, sa, qsa, M, nullptr, qkv_l, 3 * D), false,
+                                       s);
             if (!rc) rc = bl::launch_quant_act(z + (size_t)l * m * d, gl + d, eps, M, D, qo, so, qso, s, true);
-            if (!rc) rc = bl::launch_skinny(wl + 3 * dd, sl + 3, D, D, D, qo, so, qso, M, x, x, D, s);
+            if (!rc)
+                rc = bl::launch_skinny(skinny(wl + 3 * dd, sl + 3, 0.0f, D, D, D, qo, so, qso, M, x, x, D), false, s);
             if (!rc) rc = bl::launch_quant_act(x, gl + 2 * d, eps, M, D, q1, s1, qs1, s, true);
-            if (!rc) rc = bl::launch_skinny_gateup(wl + 4 * dd, wl + 4 * dd + fd, sl + 4, F, D, q1, s1, qs1, M, h, s);
+            if (!rc)
+                rc = bl::launch_skinny(skinny_gateup(wg, 0.0f, wg + fd, 0.0f, sl + 4, F, D, q1, s1, qs1, M, h, nullptr,
+                                                     nullptr),
+                                       false, s);
             if (!rc) rc = bl::launch_quant_act(h, gl + 3 * d, eps, M, F, q2, s2, qs2, s, true);
-            if (!rc) rc = bl::launch_skinny(wl + 4 * dd + 2 * fd, sl + 6, D, D, F, q2, s2, qs2, M, x, x, D, s);
+            if (!rc)
+                rc = bl::launch_skinny(skinny(wg + 2 * fd, sl + 6, 0.0f, D, D, F, q2, s2, qs2, M, x, x, D), false, s);
             if (rc) return rc;
         }
         return BL_OK;

@@ -2,8 +2,9 @@
 // the ternary LM head with a fused per-row argmax).
 //
 // acc[m][n] = sum_k q[m][k] * t[n][k] is a dense int8 contraction, so it runs on
-// v_mfma_i32_32x32x32_i8 (32x32 output tile, 32-deep K per instruction, exact
-// int32 accumulation). Tiles are staged through double-buffered LDS; the global
+// int8 MFMA with exact int32 accumulation: v_mfma_i32_16x16x64_i8 for large M,
+// v_mfma_i32_32x32x32_i8 for small M (m <= 32 goes to the skinny kernels of
+// skinny.hip instead). Tiles are staged through double-buffered LDS; the global
 // loads run two K steps ahead (two register staging sets), so each has a whole
 // step to land, and one barrier per K step separates the LDS buffers. The weights stay 2-bit packed
 // in HBM and in LDS; each wave unpacks its B operand in registers: the packed dword of 16 consecutive
@@ -21,28 +22,10 @@
 // one 64-bit key per row, (acc + 2^31) << 32 | (2^32 - 1 - n), and merges it with
 // a 64-bit atomicMax, so equal accumulators resolve to the lowest n.
 #include "internal.h"
+#include "ternary.h"
 
 namespace bl {
 namespace {
-
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
-
-constexpr uint32_t kCodeMask = 0x03030303u;
-
-__device__ __forceinline__ uint4 permute16(const uint4 v)
-{
-    const uint32_t t01lo = __builtin_amdgcn_perm(v.y, v.x, 0x05010400u);
-    const uint32_t t01hi = __builtin_amdgcn_perm(v.y, v.x, 0x07030602u);
-    const uint32_t t23lo = __builtin_amdgcn_perm(v.w, v.z, 0x05010400u);
-    const uint32_t t23hi = __builtin_amdgcn_perm(v.w, v.z, 0x07030602u);
-    uint4 o;
-    o.x = __builtin_amdgcn_perm(t23lo, t01lo, 0x05040100u);
-    o.y = __builtin_amdgcn_perm(t23lo, t01lo, 0x07060302u);
-    o.z = __builtin_amdgcn_perm(t23hi, t01hi, 0x05040100u);
-    o.w = __builtin_amdgcn_perm(t23hi, t01hi, 0x07060302u);
-    return o;
-}
 
 constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 
@@ -96,7 +79,7 @@ struct Mfma<16> {
 // The four waves split the columns (128 x 80 each, 8 x 5 tiles of 16x16x64),
 // so every packed weight column is unpacked by one wave only.
 using CfgLarge = Cfg<128, 320, 1, 4, 64, 16>;
-// Small M (batched decode, LM head): 32 x 256 tiles.
+// Small M (up to 64 tokens; fewer run the skinny kernels): 32 x 256 tiles.
 using CfgSmall = Cfg<32, 256, 1, 4, 64, 32>;
 
 template <class C>
@@ -202,8 +185,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(2))
             for (int j = 0; j < C::TN; ++j) {
                 const uint32_t p =
                     *reinterpret_cast<const uint32_t*>(lds_b[cur] + (wn + j * MT + (lane % MT)) * C::SB + kofs / 4);
-                b[j] = v4i{(int)(p & kCodeMask), (int)((p >> 2) & kCodeMask), (int)((p >> 4) & kCodeMask),
-                           (int)((p >> 6) & kCodeMask)};
+                b[j] = ternary_codes(p);
             }
 #pragma unroll
             for (int i = 0; i < C::TM; ++i)
@@ -247,9 +229,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(2))
                     }
                     if (acc_out) acc_out[o] = total;
                     if (keys) {
-                        const unsigned long long key =
-                            ((unsigned long long)((uint32_t)total ^ 0x80000000u) << 32) |
-                            (unsigned long long)(0xFFFFFFFFu - (uint32_t)col);
+                        const unsigned long long key = argmax_key(total, col);
                         best = key > best ? key : best;
                     }
                 }
@@ -299,7 +279,7 @@ int launch_gemm(const uint8_t* packed, float w_scale, const float* w_scale_ptr, 
         argmax_init_kernel<<<(m + 255) / 256, 256, 0, s>>>(keys, m);
         if (hipGetLastError() != hipSuccess) return BL_ERR_LAUNCH;
     }
-    if (m <= CfgSmall::BM) {
+    if (m <= 2 * CfgSmall::BM) {
         dim3 grid((n + CfgSmall::BN - 1) / CfgSmall::BN, (m + CfgSmall::BM - 1) / CfgSmall::BM);
         gemm_kernel<CfgSmall><<<grid, CfgSmall::kThreads, 0, s>>>(packed, w_scale, w_scale_ptr, n, k, q, act_scale,
                                                                   act_sum, m, residual, y, ldy, acc_out, keys);

@@ -52,20 +52,36 @@ int launch_stream_persistent(const uint8_t* weights, const float* scales, const 
                              int n_layers, int d, int f, float eps, float* x, float* qkv, long long qkv_stride,
                              void* ll_region, uint32_t* ctrl, hipStream_t s);
 
-// Skinny MFMA GEMM for m <= 32 tokens whose activations are in the perm16
-// layout: y[m][n] = (acc - act_sum) / (act_scale * s_w) (+ residual), with
-// n / n_per_scale selecting the weight scale w_scale_ptr[.] of consecutive
-// stacked matrices. Row stride ldy for y and residual.
-int launch_skinny(const uint8_t* packed, const float* w_scale_ptr, int n_per_scale, int n, int k, const int8_t* q,
-                  const float* act_scale, const int32_t* act_sum, int m, const float* residual, float* y, int ldy,
-                  hipStream_t s);
-
-// Fused gate/up for m <= 32 tokens (perm16 activations): h[m][f] =
-// relu(gate)^2 * up, gate / up from the f x d matrices w_gate / w_up with
-// scales scale_ptr[0] / scale_ptr[1].
-int launch_skinny_gateup(const uint8_t* w_gate, const uint8_t* w_up, const float* scale_ptr, int f, int d,
-                         const int8_t* q, const float* act_scale, const int32_t* act_sum, int m, float* h,
-                         hipStream_t s);
+// Skinny MFMA products for m <= 32 tokens (skinny.hip). Without w1:
+// y[m][n] = [residual +] (acc - act_sum) / (act_scale * s_w), with s_w =
+// w_scale_ptr[col / n_per_scale] (stacked matrices) or w_scale0; acc0 gets the
+// exact acc - act_sum; tile_keys, if set, gets per token and workgroup the
+// argmax key of its columns ([m][skinny_tiles(n, false)]), reduced by
+// launch_tile_argmax. With w1 (paired mode): w0 / w1 are the gate / up
+// matrices (scales w_scale_ptr[0..1] or w_scale0 / w_scale1), y = relu(gate)^2
+// * up, acc0 / acc1 the exact gate / up accumulators. y, residual, acc0 and
+// acc1 share the row stride ldy. q is in the perm16 layout, or in natural
+// order when natural_q is set.
+struct SkinnyArgs {
+    const uint8_t* w0 = nullptr;
+    const uint8_t* w1 = nullptr;
+    const float* w_scale_ptr = nullptr;
+    float w_scale0 = 0.0f, w_scale1 = 0.0f;
+    int n_per_scale = 1, n = 0, k = 0;
+    const int8_t* q = nullptr;
+    const float* act_scale = nullptr;
+    const int32_t* act_sum = nullptr;
+    int m = 0;
+    const float* residual = nullptr;
+    float* y = nullptr;
+    int ldy = 0;
+    int32_t* acc0 = nullptr;
+    int32_t* acc1 = nullptr;
+    unsigned long long* tile_keys = nullptr;
+};
+int launch_skinny(const SkinnyArgs& a, bool natural_q, hipStream_t s);
+int skinny_tiles(int n, bool pair);
+int launch_tile_argmax(const unsigned long long* tile_keys, int tiles, int m, int32_t* idx, hipStream_t s);
 
 // h = relu(gate)^2 * up, elementwise.
 int launch_relu2_mul(const float* gate, const float* up, int64_t count, float* h, hipStream_t s);

@@ -14,8 +14,9 @@
 //          Optionally q is written with each 16 values 4x4 byte-transposed, the
 //          order in which the MFMA kernels unpack ternary weights (an internal
 //          layout of the batched layer stream).
-// Passes 2 and 3 each re-read the row (an L2 hit after pass 1) and recompute y
-// identically, so no fp32 row has to be stored.
+// Rows of up to 16384 values are held in registers (one load per value); for
+// longer rows passes 2 and 3 each re-read the row (an L2 hit after pass 1) and
+// recompute y identically.
 #include "internal.h"
 #include "wave.h"
 
@@ -119,6 +120,107 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(const float* __rest
     }
 }
 
+// The same three steps with the row held in registers: thread t loads x[k]
+// (and g[k]) for k = t, t + 512, ... < NPT * 512 once, up front, so the row
+// costs one trip to memory instead of three. The sum of squares runs over the
+// same values in the same order as above, and y is recomputed identically.
+template <bool kNorm, bool kPerm, int NPT>
+__global__ __launch_bounds__(kThreads) void quant_act_reg_kernel(const float* __restrict__ x,
+                                                                 const float* __restrict__ gain, float eps, int k,
+                                                                 int8_t* __restrict__ q, float* __restrict__ act_scale,
+                                                                 int32_t* __restrict__ act_sum)
+{
+    const int row = blockIdx.x;
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = t >> 6;
+    const float* xr = x + (size_t)row * k;
+    __shared__ double wsum_d[kWaves];
+    __shared__ float wmax[kWaves];
+    __shared__ int wsum[kWaves];
+
+    float xv[NPT], gv[NPT];
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+        const int i = t + j * kThreads;
+        xv[j] = i < k ? xr[i] : 0.0f;
+        gv[j] = kNorm && i < k ? gain[i] : 0.0f;
+    }
+
+    float r = 1.0f;
+    if (kNorm) {
+        double p = 0.0;
+#pragma unroll
+        for (int j = 0; j < NPT; ++j) {
+            const double v = (double)xv[j];
+            if (t + j * kThreads < k) p += v * v;
+        }
+        p = wave_butterfly_sum(p);
+        if (lane == 0) wsum_d[wave] = p;
+        __syncthreads();
+        r = (float)(1.0 / sqrt(cross_wave_sum8(wsum_d) / (double)k + (double)eps));
+    }
+
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+        const float y = kNorm ? (xv[j] * r) * gv[j] : xv[j];
+        if (t + j * kThreads < k) amax = fmaxf(amax, fabsf(y));
+    }
+    amax = wave_max(amax);
+    if (lane == 0) wmax[wave] = amax;
+    __syncthreads();
+    amax = wmax[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) amax = fmaxf(amax, wmax[w]);
+    const float scale = 127.0f / fmaxf(amax, 1e-5f);
+
+    int sum = 0;
+    int8_t* qr = q + (size_t)row * k;
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+        const int i = t + j * kThreads;
+        if (i < k) {
+            const float y = kNorm ? (xv[j] * r) * gv[j] : xv[j];
+            const int qv = quant_one(y, scale);
+            sum += qv;
+            // perm16: value 4 g + j' of each 16 sits at byte 4 j' + g
+            qr[kPerm ? (i & ~15) + 4 * (i & 3) + ((i >> 2) & 3) : i] = (int8_t)qv;
+        }
+    }
+    sum = wave_sum(sum);
+    if (lane == 0) wsum[wave] = sum;
+    __syncthreads();
+    if (t == 0) {
+        act_scale[row] = scale;
+        int total = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) total += wsum[w];
+        if (act_sum) act_sum[row] = total;
+    }
+}
+
+template <bool kNorm, bool kPerm>
+void launch_kind(const float* x, const float* gain, float eps, int m, int k, int8_t* q, float* act_scale,
+                 int32_t* act_sum, hipStream_t s)
+{
+    const int per = (k + kThreads - 1) / kThreads;  // values per thread
+#define BL_QREG(N) quant_act_reg_kernel<kNorm, kPerm, N><<<m, kThreads, 0, s>>>(x, gain, eps, k, q, act_scale, act_sum)
+    if (per <= 4)
+        BL_QREG(4);
+    else if (per <= 8)
+        BL_QREG(8);
+    else if (per <= 16)
+        BL_QREG(16);
+    else if (per <= 20)
+        BL_QREG(20);
+    else if (per <= 32)
+        BL_QREG(32);
+    else
+        quant_act_kernel<kNorm, kPerm><<<m, kThreads, 0, s>>>(x, gain, eps, k, q, act_scale, act_sum);
+#undef BL_QREG
+}
+
 }  // namespace
 
 int launch_quant_act(const float* x, const float* gain, float eps, int m, int k, int8_t* q, float* act_scale,
@@ -126,13 +228,13 @@ int launch_quant_act(const float* x, const float* gain, float eps, int m, int k,
 {
     if (perm16) {
         if (gain)
-            quant_act_kernel<true, true><<<m, kThreads, 0, s>>>(x, gain, eps, k, q, act_scale, act_sum);
+            launch_kind<true, true>(x, gain, eps, m, k, q, act_scale, act_sum, s);
         else
-            quant_act_kernel<false, true><<<m, kThreads, 0, s>>>(x, gain, eps, k, q, act_scale, act_sum);
+            launch_kind<false, true>(x, gain, eps, m, k, q, act_scale, act_sum, s);
     } else if (gain) {
-        quant_act_kernel<true, false><<<m, kThreads, 0, s>>>(x, gain, eps, k, q, act_scale, act_sum);
+        launch_kind<true, false>(x, gain, eps, m, k, q, act_scale, act_sum, s);
     } else {
-        quant_act_kernel<false, false><<<m, kThreads, 0, s>>>(x, gain, eps, k, q, act_scale, act_sum);
+        launch_kind<false, false>(x, gain, eps, m, k, q, act_scale, act_sum, s);
     }
     return hipGetLastError() == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
 }

@@ -1,80 +1,89 @@
 // skinny.hip -- BitLinear products for a few tokens (m <= 32) on int8 matrix
-// cores: the batched-decode projections of a layer, including the fused
-// gate/up with the relu(gate)^2 * up epilogue ("Transformer Block", Hesper
-// API, "Forward Pass"; the FFN of "Memory Layout").
+// cores: the batched-decode projections, the fused gate/up with the
+// relu(gate)^2 * up epilogue ("Transformer Block", Hesper API, "Forward Pass";
+// the FFN of "Memory Layout") and the ternary LM head with its per-token argmax
+// ("BitNet Model - Complete Inference Pipeline", Hesper API, "Greedy Decoding").
 //
 // At m <= 32 a projection is a pure weight stream of a few MB, so its time is
 // set by how many dependent trips to memory a wave makes, not by bandwidth:
 // every wave issues all of its loads at once and there is no loop-carried
-// wait. A workgroup owns 16 output columns (weight rows) for all tokens, as the
-// two 16-row tiles of v_mfma_i32_16x16x64_i8 (A: tokens, B: weight rows); its
-// S waves split K into runs of KW super-steps of 256 inputs, and the exact
-// int32 partials meet in LDS (integer sums, so the order does not matter).
+// wait. All 32 tokens are the 32 rows of one v_mfma_i32_32x32x32_i8 A tile; a
+// wave holds NB B tiles of 32 weight rows (consecutive rows, or the gate and
+// up rows of the same 32 outputs). The S waves of a workgroup split K into runs
+// of KW super-steps of 128 inputs, and their exact int32 partials meet through
+// LDS integer atomics (so the order does not matter).
 //
-// Within a super-step lane (n, b) = (lane % 16, lane / 16) takes inputs
-// 64 b .. 64 b + 63: one 16-byte load of packed weights (64 weights of row n)
-// and, per token tile, four 16-byte loads of activations. MFMA t (of 4) uses
-// inputs 64 b + 16 t .. +15 of every lane; the packed dword t unpacks with
-// (w >> 2 j) & 0x03030303 into the codes c = t + 1 of weights {j, 4+j, 8+j,
-// 12+j} of the 16, which is why the activations come in the perm16 layout
-// (each 16 values 4x4 byte-transposed). The code offset is removed with sum(q),
-// and the fp32 dequant 1 / (s_a s_w) is applied per token.
+// Within a super-step lane (c, h) = (lane % 32, lane / 32) takes inputs
+// 64 h .. 64 h + 63: one 16-byte load of packed weights per B tile (64 weights
+// of row c) and, for MFMA t (of 4), inputs 64 h + 16 t .. +15 of token c.
+// Packed dword t unpacks into the 4x4-transposed code order (ternary_codes),
+// and the activations meet it in the same order -- stored that way by the
+// quantizer (perm16), or transposed in registers when they come in natural
+// order. The activations are loaded row-contiguous (eight lanes cover a
+// token's 128 bytes, so a load touches 8 cache lines instead of 32) and pass
+// through the wave's own LDS rows into operand order. The code offset is
+// removed with sum(q), and the fp32 dequant 1 / (s_a s_w) is applied per
+// token.
 #include "internal.h"
+#include "ternary.h"
 
 namespace bl {
 namespace {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
-constexpr uint32_t kCodeMask = 0x03030303u;
 constexpr int kMaxWaves = 16;  // waves per workgroup (K split)
 
-__device__ __forceinline__ v4i codes(uint32_t p)
-{
-    return v4i{(int)(p & kCodeMask), (int)((p >> 2) & kCodeMask), (int)((p >> 4) & kCodeMask),
-               (int)((p >> 6) & kCodeMask)};
-}
-
-__device__ __forceinline__ v4i as_v4i(const uint4 v) { return v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w}; }
-
-// Operands of one super-step for one lane: the packed weights of NB rows
-// (gate and up in the paired mode) and the activations of both token tiles.
+// Operands of one super-step for one lane: the packed weights of its B tiles,
+// and 4 x 16 bytes of the activations in the row-contiguous load order (lane l
+// of load u holds bytes 16 (l % 8) .. +15 of token 8 u + l / 8).
 template <int NB>
 struct Ops {
     uint4 w[NB];
-    uint4 a[2][4];
+    uint4 a[4];
 };
 
-// PAIR = false: y = dequant(W q) (+ residual) for the rows of w0.
-// PAIR = true: rows of w0 (gate) and w1 (up) together, y = relu(gate)^2 * up.
+// Activations of one super-step in LDS, per wave: 32 token rows of 128 bytes,
+// rows 144 bytes apart so the 16-byte operand reads of a wave fall in distinct
+// banks.
+constexpr int kRowA = 144;
+constexpr int kStageA = 32 * kRowA;
+
+// register r of lane l holds token 8 (r / 4) + 4 (l / 32) + r % 4 of the tile
+__device__ __forceinline__ int tile_row(int lane, int r) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
 // Wave w of S takes super-steps (round * S + w) * KW + i, i < KW.
-template <bool PAIR, int KW>
-__global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint8_t* __restrict__ w0,
-                                                                 const uint8_t* __restrict__ w1,
-                                                                 const float* __restrict__ w_scale_ptr,
-                                                                 int n_per_scale, int n, int k,
-                                                                 const int8_t* __restrict__ q,
-                                                                 const float* __restrict__ act_scale,
-                                                                 const int32_t* __restrict__ act_sum, int m,
-                                                                 const float* residual, float* y, int ldy)
+template <int NB, bool PAIR, int KW, bool NAT>
+__global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyArgs a)
 {
-    constexpr int NB = PAIR ? 2 : 1;
-    extern __shared__ int red[];  // [S][NB * 8][64] int32 partials
+    static_assert(!PAIR || NB == 2, "paired mode: gate and up tiles");
+    extern __shared__ int red[];  // [NB][16][64] int32 totals, then the waves' activation rows
+    constexpr int COLS = PAIR ? 32 : 32 * NB;
     const int lane = threadIdx.x & 63;
     const int S = blockDim.x >> 6;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int n0 = blockIdx.x * 16;
-    const int ln = lane & 15, b = lane >> 4;
-    const size_t kb = (size_t)k / 4;
-    const int row = min(n0 + ln, n - 1);
-    const uint8_t* wr0 = w0 + (size_t)row * kb + 16 * b;
-    const uint8_t* wr1 = PAIR ? w1 + (size_t)row * kb + 16 * b : nullptr;
-    const int8_t* ar0 = q + (size_t)min(ln, m - 1) * k + 64 * b;       // token tile 0
-    const int8_t* ar1 = q + (size_t)min(16 + ln, m - 1) * k + 64 * b;  // token tile 1
-    const int nss = (k + 255) / 256;                                   // the last may be partial
-
-    v4i acc[NB][2];
+    const int n0 = blockIdx.x * COLS;
+    const int lc = lane & 31, h = lane >> 5;
+    const size_t kb = (size_t)a.k / 4;
+    const uint8_t* wr[NB];
 #pragma unroll
-    for (int i = 0; i < NB; ++i) acc[i][0] = acc[i][1] = v4i{0, 0, 0, 0};
+    for (int j = 0; j < NB; ++j) {
+        const int row = min(PAIR ? n0 + lc : n0 + 32 * j + lc, a.n - 1);
+        wr[j] = (PAIR && j == 1 ? a.w1 : a.w0) + (size_t)row * kb + 16 * h;
+    }
+    // row-contiguous activation loads: lane l of load u reads 16 bytes of token 8 u + l / 8
+    const int c8 = lane & 7;
+    const int8_t* ar[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) ar[u] = a.q + (size_t)min(8 * u + (lane >> 3), a.m - 1) * a.k + 16 * c8;
+    int8_t* stage = reinterpret_cast<int8_t*>(red + NB * 16 * 64) + wave * kStageA;
+    const int nss = (a.k + 127) / 128;  // the last may be partial
+
+    for (int i = threadIdx.x; i < NB * 16 * 64; i += blockDim.x) red[i] = 0;
+
+    v16i acc[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[j][r] = 0;
     for (int base = wave * KW; base < nss; base += S * KW) {
         Ops<NB> o[KW];
         const uint4 z = {0u, 0u, 0u, 0u};
@@ -84,124 +93,186 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint8_t* _
 #pragma unroll
             for (int j = 0; j < NB; ++j) o[i].w[j] = z;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) o[i].a[0][t] = o[i].a[1][t] = z;
-            // k is a multiple of 64, so a lane's 64 inputs are all in range or none
-            if (ss * 256 + 64 * b < k) {
-                o[i].w[0] = *reinterpret_cast<const uint4*>(wr0 + (size_t)ss * 64);
-                if (PAIR) o[i].w[NB - 1] = *reinterpret_cast<const uint4*>(wr1 + (size_t)ss * 64);
+            for (int u = 0; u < 4; ++u) o[i].a[u] = z;
+            // k is a multiple of 64, so a lane's 64 weights are all in range or none
+            if (ss * 128 + 64 * h < a.k) {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    o[i].a[0][t] = *reinterpret_cast<const uint4*>(ar0 + (size_t)ss * 256 + 16 * t);
-                    o[i].a[1][t] = *reinterpret_cast<const uint4*>(ar1 + (size_t)ss * 256 + 16 * t);
-                }
+                for (int j = 0; j < NB; ++j) o[i].w[j] = *reinterpret_cast<const uint4*>(wr[j] + (size_t)ss * 32);
+            }
+            if (ss * 128 + 16 * c8 < a.k) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) o[i].a[u] = *reinterpret_cast<const uint4*>(ar[u] + (size_t)ss * 128);
             }
         }
 #pragma unroll
         for (int i = 0; i < KW; ++i) {
+            // through this wave's LDS rows into the operand order: lane (c, h)
+            // takes bytes 64 h + 16 t .. +15 of token c for MFMA t. A wave's LDS
+            // accesses complete in order, so the rows are reused without a wait.
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                *reinterpret_cast<uint4*>(stage + (8 * u + (lane >> 3)) * kRowA + 16 * c8) = o[i].a[u];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
+                const uint4 raw = *reinterpret_cast<const uint4*>(stage + lc * kRowA + 64 * h + 16 * t);
+                const v4i av = as_v4i(NAT ? permute16(raw) : raw);
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
                     const uint4& w = o[i].w[j];
                     const uint32_t p = t == 0 ? w.x : t == 1 ? w.y : t == 2 ? w.z : w.w;
-                    const v4i bw = codes(p);
-                    acc[j][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_v4i(o[i].a[0][t]), bw, acc[j][0], 0, 0, 0);
-                    acc[j][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_v4i(o[i].a[1][t]), bw, acc[j][1], 0, 0, 0);
+                    acc[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, ternary_codes(p), acc[j], 0, 0, 0);
                 }
             }
         }
     }
 
-    // slot (tt, r): C row 4 b + r of token tile tt, column ln (MFMA C layout)
+    __syncthreads();  // the zeroed totals are visible
+    if (wave * KW < nss) {
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
+        for (int j = 0; j < NB; ++j)
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) red[(wave * NB * 8 + (j * 2 + tt) * 4 + r) * 64 + lane] = acc[j][tt][r];
+            for (int r = 0; r < 16; ++r) atomicAdd(&red[(j * 16 + r) * 64 + lane], acc[j][r]);
+    }
     __syncthreads();
 
-    const int col = n0 + ln;
-    for (int slot = wave; slot < 8; slot += S) {
-        const int tt = slot >> 2, r = slot & 3;
-        const int tok = 16 * tt + 4 * b + r;
+    const int tiles = gridDim.x;
+    for (int r = wave; r < 16; r += S) {
+        const int tok = tile_row(lane, r);
+        const int tokc = min(tok, a.m - 1);
+        const int qs = a.act_sum[tokc];
+        const float sa = a.act_scale[tokc];
         int tot[NB];
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            int sum = 0;
-            for (int w = 0; w < S; ++w) sum += red[(w * NB * 8 + j * 8 + slot) * 64 + lane];
-            tot[j] = sum;
-        }
-        if (tok >= m || col >= n) continue;
-        const int qs = act_sum[tok];
-        const float sa = act_scale[tok];
-        const size_t o = (size_t)tok * ldy + col;
+        for (int j = 0; j < NB; ++j) tot[j] = red[(j * 16 + r) * 64 + lane] - qs;
         if (PAIR) {
-            const float gate = (float)(tot[0] - qs) * (1.0f / (sa * w_scale_ptr[0]));
-            const float up = (float)(tot[NB - 1] - qs) * (1.0f / (sa * w_scale_ptr[1]));
-            const float gp = gate > 0.0f ? gate : 0.0f;
-            const float g2 = gp * gp;
-            y[o] = g2 * up;
+            const int col = n0 + lc;
+            if (tok < a.m && col < a.n) {
+                const float sg = a.w_scale_ptr ? a.w_scale_ptr[0] : a.w_scale0;
+                const float su = a.w_scale_ptr ? a.w_scale_ptr[1] : a.w_scale1;
+                const float gate = (float)tot[0] * (1.0f / (sa * sg));
+                const float up = (float)tot[1] * (1.0f / (sa * su));
+                const float gp = gate > 0.0f ? gate : 0.0f;
+                const float g2 = gp * gp;
+                const size_t o = (size_t)tok * a.ldy + col;
+                a.y[o] = g2 * up;
+                if (a.acc0) a.acc0[o] = tot[0];
+                if (a.acc1) a.acc1[o] = tot[1];
+            }
         } else {
-            const float inv = 1.0f / (sa * w_scale_ptr[col / n_per_scale]);
-            float v = (float)(tot[0] - qs) * inv;
-            if (residual) v = residual[o] + v;
-            y[o] = v;
+            unsigned long long best = 0;
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const int col = n0 + 32 * j + lc;
+                if (tok < a.m && col < a.n) {
+                    const size_t o = (size_t)tok * a.ldy + col;
+                    if (a.y) {
+                        const float sw = a.w_scale_ptr ? a.w_scale_ptr[col / a.n_per_scale] : a.w_scale0;
+                        float v = (float)tot[j] * (1.0f / (sa * sw));
+                        if (a.residual) v = a.residual[o] + v;
+                        a.y[o] = v;
+                    }
+                    if (a.acc0) a.acc0[o] = tot[j];
+                    const unsigned long long key = argmax_key(tot[j], col);
+                    best = key > best ? key : best;
+                }
+            }
+            if (a.tile_keys) {  // uniform branch: every lane takes part in the exchange
+#pragma unroll
+                for (int off = 16; off >= 1; off >>= 1) {
+                    const unsigned long long other = __shfl_xor(best, off, 64);
+                    best = other > best ? other : best;
+                }
+                if (lc == 0 && tok < a.m) a.tile_keys[(size_t)tok * tiles + blockIdx.x] = best;
+            }
         }
     }
 }
 
-// Super-steps per wave and waves per workgroup for a K of nss super-steps:
-// up to 16 waves of one or two super-steps each (at 16 waves a lane has 128
-// VGPRs, room for two super-steps of operands); a longer K takes several rounds.
+// Per token, the largest of the workgroups' keys; its low word gives the column.
+__global__ __launch_bounds__(256) void tile_argmax_kernel(const unsigned long long* __restrict__ keys, int tiles,
+                                                          int32_t* __restrict__ idx)
+{
+    __shared__ unsigned long long wbest[4];
+    const int tok = blockIdx.x;
+    unsigned long long best = 0;
+    for (int i = threadIdx.x; i < tiles; i += 256) {
+        const unsigned long long v = keys[(size_t)tok * tiles + i];
+        best = v > best ? v : best;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const unsigned long long other = __shfl_xor(best, off, 64);
+        best = other > best ? other : best;
+    }
+    if ((threadIdx.x & 63) == 0) wbest[threadIdx.x >> 6] = best;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int w = 1; w < 4; ++w) best = wbest[w] > best ? wbest[w] : best;
+        idx[tok] = (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
+    }
+}
+
 struct Split {
     int kw, waves;
 };
 
-inline Split pick_split(int k)
+// Super-steps per wave (1, 2 or 4) and waves per workgroup for nss
+// super-steps: up to 16 waves of as few super-steps as fit in one round, at
+// most kw_max each (the
+// operands of a lane at 16 waves must fit its 128 VGPRs); a longer K takes
+// several rounds.
+inline Split pick_split(int k, int kw_max)
 {
-    const int nss = (k + 255) / 256;
+    const int nss = (k + 127) / 128;
     int kw = (nss + kMaxWaves - 1) / kMaxWaves;
-    if (kw > 2) kw = 2;
+    if (kw == 3) kw = 4;
+    if (kw > kw_max) kw = kw_max;
+    if (kw < 1) kw = 1;
     int waves = (nss + kw - 1) / kw;
     if (waves > kMaxWaves) waves = kMaxWaves;
     return {kw, waves};
 }
 
-template <bool PAIR>
-int launch(const uint8_t* w0, const uint8_t* w1, const float* w_scale_ptr, int n_per_scale, int n, int k,
-           const int8_t* q, const float* act_scale, const int32_t* act_sum, int m, const float* residual, float* y,
-           int ldy, hipStream_t s)
+template <int NB, bool PAIR, bool NAT>
+int launch_nb(const SkinnyArgs& a, hipStream_t s)
 {
-    const Split sp = pick_split(k);
-    const dim3 grid((n + 15) / 16), block(64 * sp.waves);
-    const size_t lds = (size_t)sp.waves * (PAIR ? 2 : 1) * 8 * 64 * sizeof(int);
-#define BL_SKINNY(KW)                                                                                              \
-    skinny_kernel<PAIR, KW><<<grid, block, lds, s>>>(w0, w1, w_scale_ptr, n_per_scale, n, k, q, act_scale, act_sum, \
-                                                   m, residual, y, ldy)
+    constexpr int cols = PAIR ? 32 : 32 * NB;
+    constexpr int kw_max = NB == 1 ? 4 : 2;
+    const Split sp = pick_split(a.k, kw_max);
+    const dim3 grid((a.n + cols - 1) / cols), block(64 * sp.waves);
+    const size_t lds = (size_t)NB * 16 * 64 * sizeof(int) + (size_t)sp.waves * kStageA;
     if (sp.kw == 1)
-        BL_SKINNY(1);
+        skinny_kernel<NB, PAIR, 1, NAT><<<grid, block, lds, s>>>(a);
+    else if (sp.kw == 2)
+        skinny_kernel<NB, PAIR, 2, NAT><<<grid, block, lds, s>>>(a);
     else
-        BL_SKINNY(2);
-#undef BL_SKINNY
+        skinny_kernel<NB, PAIR, kw_max, NAT><<<grid, block, lds, s>>>(a);
     return hipGetLastError() == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
 }
 
+// Two 32-row tiles per wave where that still leaves a workgroup per CU.
+inline bool two_tiles(int n) { return n >= 64 * 256; }
+
 }  // namespace
 
-int launch_skinny(const uint8_t* packed, const float* w_scale_ptr, int n_per_scale, int n, int k, const int8_t* q,
-                  const float* act_scale, const int32_t* act_sum, int m, const float* residual, float* y, int ldy,
-                  hipStream_t s)
+int skinny_tiles(int n, bool pair)
 {
-    return launch<false>(packed, nullptr, w_scale_ptr, n_per_scale, n, k, q, act_scale, act_sum, m, residual, y, ldy,
-                         s);
+    if (pair) return (n + 31) / 32;
+    return two_tiles(n) ? (n + 63) / 64 : (n + 31) / 32;
 }
 
-int launch_skinny_gateup(const uint8_t* w_gate, const uint8_t* w_up, const float* scale_ptr, int f, int d,
-                         const int8_t* q, const float* act_scale, const int32_t* act_sum, int m, float* h,
-                         hipStream_t s)
+int launch_skinny(const SkinnyArgs& a, bool natural_q, hipStream_t s)
 {
-    return launch<true>(w_gate, w_up, scale_ptr, f, f, d, q, act_scale, act_sum, m, nullptr, h, f, s);
+    if (a.w1) return natural_q ? launch_nb<2, true, true>(a, s) : launch_nb<2, true, false>(a, s);
+    if (two_tiles(a.n)) return natural_q ? launch_nb<2, false, true>(a, s) : launch_nb<2, false, false>(a, s);
+    return natural_q ? launch_nb<1, false, true>(a, s) : launch_nb<1, false, false>(a, s);
+}
+
+int launch_tile_argmax(const unsigned long long* tile_keys, int tiles, int m, int32_t* idx, hipStream_t s)
+{
+    tile_argmax_kernel<<<m, 256, 0, s>>>(tile_keys, tiles, idx);
+    return hipGetLastError() == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
 }
 
 }  // namespace bl

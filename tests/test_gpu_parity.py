@@ -33,7 +33,10 @@ def quant_gpu(bl, x, gain, eps):
 
 # ---- activation quant ------------------------------------------------------------------
 
-QUANT_CASES = [(1, 64), (1, 2560), (1, 10240), (3, 192), (7, 640), (33, 2560), (5, 16384)]
+# rows up to 16384 values run register-resident (4, 8, 16, 20 or 32 values per
+# thread); longer rows the three-pass kernel
+QUANT_CASES = [(1, 64), (1, 2560), (1, 10240), (3, 192), (7, 640), (33, 2560), (5, 16384), (4, 8192), (2, 4160),
+               (2, 16448)]
 
 
 @pytest.mark.parametrize("norm", [False, True])
@@ -113,8 +116,11 @@ def test_gemv(bl, olib, n, k, m):
 
 # ---- GEMM ------------------------------------------------------------------------------------
 
+# m <= 32 runs the skinny kernels (one or two 32-row tiles per wave, K split
+# over up to 16 waves, ragged K tails); larger m the tiled GEMM.
 GEMM_CASES = [(1, 16, 64), (5, 100, 192), (32, 2048, 2048), (130, 200, 640), (256, 384, 2560), (37, 2560, 10240),
-              (300, 129, 128), (32, 8192, 2048), (64, 50000, 2048)]
+              (300, 129, 128), (32, 8192, 2048), (64, 50000, 2048), (32, 50000, 2048), (17, 16448, 320),
+              (9, 33, 4160), (24, 700, 8448)]
 
 
 @pytest.mark.parametrize("m,n,k", GEMM_CASES)
@@ -140,10 +146,11 @@ def test_gemm(bl, olib, m, n, k):
     assert_exact(to_host(am), np.argmax(oy, axis=1).astype(np.int32), "argmax of logits")
 
 
-def test_gemm_argmax_ties_no_logits(bl, olib):
+@pytest.mark.parametrize("m", [7, 40])
+def test_gemm_argmax_ties_no_logits(bl, olib, m):
     """Duplicated weight rows make ties; the lowest index must win, without y."""
     import torch
-    m, n, k = 7, 300, 128
+    n, k = 300, 128
     g = W.rng(103, 0, 0)
     t = W.ternary(g, n, k)
     t[250] = t[3]
@@ -163,10 +170,11 @@ def test_gemm_argmax_ties_no_logits(bl, olib):
     assert got[2] == 3
 
 
-def test_gemm_residual_and_stride(bl, olib):
+@pytest.mark.parametrize("m", [40, 20])
+def test_gemm_residual_and_stride(bl, olib, m):
     import torch
-    m, n, k = 40, 96, 256
-    g = W.rng(104, 0, 0)
+    n, k = 96, 256
+    g = W.rng(104, 0, m)
     t = W.ternary(g, n, k)
     x = W.activations(g, m, k)
     res = W.activations(g, m, n)
