@@ -106,9 +106,9 @@ def run_stream_step(bl, dev, n_layers, m, d, f, x, qkv, ws):
 # kernel sources it was measured on: once they change the figure no longer
 # describes the kernel and is reported as null.
 TRAFFIC_BYTES_PER_LAUNCH = {
-    "stream_3b": {"bytes": 903725094,
+    "stream_3b": {"bytes": 899344394,
                   "sources": {"bitlinear_amd/csrc/stream.hip":
-                              "82bddba15d7bad7126fe140ec396377f1eee9a5883473c76b1db60ad616b2a62",
+                              "f365328739db0021f2680c1df769edfc7a454a4444779f0557303d684716ad44",
                               "bitlinear_amd/csrc/wave.h":
                               "c69e873099defc85d5684275fbfcce86285892ceef0209e5a6afd9ff57cb9c81"}},
 }
@@ -165,7 +165,7 @@ def main():
                     help="only run a plain 512 MiB device copy (calibrates rocprof byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+        print("bench.py measures one GPU only; there is no multi-GPU path (run with --gpus 1)",
               file=sys.stderr, flush=True)
         sys.exit(2)
 

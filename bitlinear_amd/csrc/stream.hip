@@ -114,7 +114,7 @@ __device__ __forceinline__ uint32_t status_load(const uint32_t* ctrl)
     return __hip_atomic_load(ctrl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Loads the words k = t, t + 1024, ... < N of buf until every one carries epoch
+// Loads the words k = t, t + 512, ... < N of buf until every one carries epoch
 // e (all loads of a round are issued before any is checked); v receives the
 // fp32 payloads. Returns false, for the whole workgroup, on a timeout or when
 // another workgroup gave up.

@@ -120,7 +120,8 @@ int bitlinear_gemv(const uint8_t *packed, float w_scale, int64_t n, int64_t k,
                    const int8_t *q, const float *act_scale, const int32_t *act_sum, int64_t m,
                    const float *residual, float *y, int32_t *acc_out, void *stream);
 
-/* Workspace bytes bitlinear_gemm needs (0 unless a per-row argmax is asked for). */
+/* Workspace bytes bitlinear_gemm needs (0 unless a per-row argmax is asked for):
+ * 8 bytes per token and 32-column tile for m <= 32, 8 bytes per token above. */
 size_t bitlinear_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int with_argmax);
 
 /* GEMM on int8 matrix cores (prefill, batched decode, ternary LM head):
@@ -135,8 +136,12 @@ size_t bitlinear_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int with_
  *                the rescale is monotone and exact on distinct integers).
  *   workspace  : device memory of bitlinear_gemm_workspace_bytes(m, n, k, 1)
  *                bytes (8-byte aligned) when row_argmax is given, else unused.
- * Ternary tiles are unpacked in registers from a packed LDS tile; the int8
- * activation tile is staged in LDS; products run on v_mfma_i32_32x32x32_i8.
+ * m <= 32: every token is a row of one v_mfma_i32_32x32x32_i8 A tile, K is
+ * split across the waves of a workgroup, and the argmax goes through one key
+ * per token and 32-column tile in the workspace plus a reduction kernel.
+ * m > 32: block tiles staged in LDS (ternary tiles unpacked in registers from
+ * a packed LDS tile) on v_mfma_i32_16x16x64_i8 / 32x32x32_i8, argmax by a
+ * 64-bit atomicMax key per row. Results are identical either way.
  * Errors: NULL (y and row_argmax both NULL, ...), SHAPE, ALIGN, VALUE,
  * WORKSPACE, LAUNCH. */
 int bitlinear_gemm(const uint8_t *packed, float w_scale, int64_t n, int64_t k,
@@ -214,16 +219,18 @@ int bitnet_ffn(const float *x, int64_t m, int64_t d, int64_t f,
  *             zero-filled before its first use and then kept between calls:
  *             its first 8 bytes are two uint32 words {phase counter, status}.
  * d and f must be multiples of 64; m >= 1.
- * At m == 1 (when the device supports cooperative launch and the shapes fit:
- * d, f <= 10240 with at most 64 rows of any projection per CU) the whole stream
- * runs as one persistent kernel, one workgroup per CU, that hands each step's
- * output vector to the next step through flag-tagged words in the workspace.
+ * At m == 1, for the compiled shapes (d, f) = (2560, 10240), (2048, 8192) and
+ * (256, 1024) on a device with cooperative launch and at least 256 CUs, the
+ * whole stream runs as one persistent kernel, one workgroup per CU, that hands
+ * each step's output vector to the next step through flag-tagged words in the
+ * workspace.
  * Every wait in it is bounded (2 s); on a timeout the kernel stops early and
  * sets status = 1 (status = 2: the phase counter is exhausted after about 2^31
  * steps). A nonzero status stays set, and further calls do nothing, until the
  * workspace is zero-filled again; the caller reads it after synchronising.
  * Calls that share a workspace must not overlap. Other shapes run one launch
- * per step, with the same results.
+ * per step (at 9..32 tokens one MFMA launch per projection, q/k/v together and
+ * gate/up fused), with the same results.
  * Errors: NULL, SHAPE, ALIGN, WORKSPACE, LAUNCH. */
 size_t bitnet_layer_bytes(int64_t d, int64_t f);
 size_t bitnet_stream_workspace_bytes(int64_t m, int64_t d, int64_t f);
