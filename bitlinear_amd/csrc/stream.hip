@@ -17,8 +17,9 @@
 // one workgroup per CU (256 on an MI355X) stays resident for the whole token:
 //   - each workgroup owns fixed output rows of every step and issues the loads
 //     of those weight rows (and of the step's RMSNorm gains) before it waits
-//     for the step's input, so the weight fetch overlaps the hand-over. The
-//     rows go straight into registers in the layout of the MFMA B operand;
+//     for the step's input, so the weight fetch overlaps the hand-over (the o
+//     rows go out with P1's, ahead of P2's short wait). The rows go straight
+//     into registers in the layout of the MFMA B operand;
 //   - a step's output vector is published as 64-bit words {fp32 value, epoch}
 //     written with device-scope atomic stores; a consumer loads all words of
 //     the vector it needs in one batch and repeats until every epoch matches.
@@ -29,8 +30,9 @@
 //     sum of squares keeps the fixed fp64 order of quant.hip: thread t sums
 //     x[k]^2 for k = t, t + 512, ... in ascending k, and an xor-butterfly
 //     combines the 512 partials (offsets 1..32 with exact lane exchanges,
-//     64..256 through LDS). P2's input does not depend on the stream, so its
-//     norm + quant runs before the wait for P1;
+//     64..256 through LDS). P2's input stands in for the attention output,
+//     so its norm + quant runs after the wait for P1, where the real one
+//     would become available;
 //   - dot products: v_mfma_i32_16x16x64_i8 with the token in row 0 of A and
 //     16 weight rows as the columns of B (rows 1..15 of A are zero). A lane
 //     of B holds 16 weights of one row; from a packed 16-byte chunk (64
@@ -59,6 +61,7 @@ constexpr int kGrid = 256;   // workgroups: one per CU of an MI355X
 constexpr uint32_t kCodeMask = 0x03030303u;
 constexpr long long kTimeoutTicks = 200000000LL;  // 2 s at 100 MHz
 constexpr int kMaxK = 10240;
+constexpr int kFlagStride = 16;  // words between the "P1 finished" flags: one per 128-byte line
 
 constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 
@@ -118,7 +121,7 @@ __device__ __forceinline__ uint32_t status_load(const uint32_t* ctrl)
 // e (all loads of a round are issued before any is checked); v receives the
 // fp32 payloads. Returns false, for the whole workgroup, on a timeout or when
 // another workgroup gave up.
-template <int N>
+template <int N, int STRIDE = 1>
 __device__ bool poll_vec(const unsigned long long* buf, uint32_t e, float* v, uint32_t* ctrl, long long t_start)
 {
     constexpr int NI = cdiv(N, kT);
@@ -129,7 +132,7 @@ __device__ bool poll_vec(const unsigned long long* buf, uint32_t e, float* v, ui
         // every load is unconditional (clamped address) so that the whole batch
         // is in flight before the first wait
 #pragma unroll
-        for (int i = 0; i < NI; ++i) w[i] = ll_load(buf + min(t + kT * i, N - 1));
+        for (int i = 0; i < NI; ++i) w[i] = ll_load(buf + STRIDE * min(t + kT * i, N - 1));
         bool ready = true;
 #pragma unroll
         for (int i = 0; i < NI; ++i) ready = ready && (uint32_t)(w[i] >> 32) == e;
@@ -139,7 +142,7 @@ __device__ bool poll_vec(const unsigned long long* buf, uint32_t e, float* v, ui
             failed = true;
             break;
         }
-        __builtin_amdgcn_s_sleep(2);
+        __builtin_amdgcn_s_sleep(10);
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i) v[i] = (t + kT * i < N) ? __uint_as_float((uint32_t)w[i]) : 0.0f;
@@ -344,23 +347,27 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
     int qsum;
 
     // The weight rows, gains and stand-in input of a step are loaded when the
-    // step starts, before its wait: the fetch overlaps the hand-over. (Loading
-    // a step earlier does not pay: a wave's loads complete in issue order, so
-    // every later wait would also wait for the early loads.)
+    // step starts, before its wait: the fetch overlaps the hand-over. A wave's
+    // loads complete in issue order, so a poll also waits for every load issued
+    // before it: loading P3's or P4's rows a step earlier measured slower, while
+    // the o rows (6.4 KB per workgroup) ride with P1's and spare P2's wait.
     uint4 w1[S1::P], w2[S2::P], w3[S3::P], w4[S4::P];
     float g1[ND], g2[ND], g3[ND], g4[NF], zv[ND];
+    auto fetch2 = [&](int l) {
+        const uint8_t* W = a.weights + (size_t)l * blob + 3 * dd + (size_t)r2 * (D / 4);
+        load_items<S2>(w2, [&](int r) { return W + (size_t)r * (D / 4); });
+    };
     auto fetch1 = [&](int l) {
         // q, k, v are consecutive D x D/4 matrices: stacked row r is at r * D/4
         const uint8_t* W = a.weights + (size_t)l * blob + (size_t)r1 * (D / 4);
         load_items<S1>(w1, [&](int r) { return W + (size_t)r * (D / 4); });
         load_strided<D>(a.gains + (size_t)l * (3 * D + F), g1);
-        // P2's gains and stand-in input: its norm + quant runs right after P1
+        // P2's gains and stand-in input (its norm + quant follows the wait for P1)
         load_strided<D>(a.gains + (size_t)l * (3 * D + F) + D, g2);
         load_strided<D>(a.z + (size_t)l * D, zv);
-    };
-    auto fetch2 = [&](int l) {
-        const uint8_t* W = a.weights + (size_t)l * blob + 3 * dd + (size_t)r2 * (D / 4);
-        load_items<S2>(w2, [&](int r) { return W + (size_t)r * (D / 4); });
+        // the o rows too: a poll waits for every load issued before it, and
+        // P2's wait is the shortest, so its weights go out with P1's
+        fetch2(l);
     };
     auto fetch3 = [&](int l) {
         const uint8_t* W = a.weights + (size_t)l * blob + 4 * dd + (size_t)r3 * (D / 4);
@@ -399,20 +406,19 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
                 const float inv = 1.0f / (s_a * (mat == 0 ? sw[0] : (mat == 1 ? sw[1] : sw[2])));
                 qkv[row] = (float)(sh.acc[t] - qsum) * inv;
             }
-            if (t == 0) ll_store(a.done + w, 0.0f, E + 1);
+            if (t == 0) ll_store(a.done + kFlagStride * w, 0.0f, E + 1);
         }
         // ---- P2: o projection of the stand-in z, residual ----
         {
-            // z does not depend on the stream: its norm + quant runs before the
-            // wait for P1 to finish everywhere
-            norm_quant<D>(zv, g2, a.eps, sh, s_a, qsum);
+            // z stands in for the attention output, which exists only once
+            // every workgroup has finished P1: its norm + quant follows the wait
             if (t < S2::R) sh.acc[t] = 0;
-            fetch2(l);
             float fl[1];
-            if (!poll_vec<kGrid>(a.done, E + 1, fl, a.ctrl, t_start)) return;
+            if (!poll_vec<kGrid, kFlagStride>(a.done, E + 1, fl, a.ctrl, t_start)) return;
             if (l == 0 && w == 0 && t == 0)  // every workgroup has read the base by now
                 __hip_atomic_store(a.ctrl, base + 4u * (uint32_t)a.n_layers, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
+            norm_quant<D>(zv, g2, a.eps, sh, s_a, qsum);
             dots<S2>(w2, sh.q, sh.zero, sh.acc);
             __syncthreads();
             if (e2) {
@@ -531,6 +537,6 @@ int launch_stream_persistent(const uint8_t* weights, const float* scales, const 
     return e == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
 }
 
-size_t stream_ll_words(int d, int f) { return (size_t)2 * d + f + kGrid; }
+size_t stream_ll_words(int d, int f) { return (size_t)2 * d + f + (size_t)kGrid * kFlagStride; }
 
 }  // namespace bl
