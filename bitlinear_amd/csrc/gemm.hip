@@ -82,6 +82,17 @@ using CfgLarge = Cfg<128, 320, 1, 4, 64, 16>;
 // Small M (up to 64 tokens; fewer run the skinny kernels): 32 x 256 tiles.
 using CfgSmall = Cfg<32, 256, 1, 4, 64, 32>;
 
+// Workgroup barrier over LDS only: this wave's LDS accesses complete, then
+// s_barrier. Unlike __syncthreads it does not wait for outstanding global
+// loads, so the loads issued for later K steps stay in flight across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unconstrained
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 template <class C>
 __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(2))) void gemm_kernel(
     const uint8_t* __restrict__ packed, float w_scale, const float* __restrict__ w_scale_ptr, int n, int k,
@@ -194,16 +205,21 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(2))
         }
         // the other buffer was last read before the previous barrier
         if (s + 1 < nk) store_lds(cur ^ 1, cur ^ 1);
-        __syncthreads();
+        lds_barrier();
     };
     load_global(0, 0);
     if (nk > 1) load_global(1, 1);
     store_lds(0, 0);
     __syncthreads();
-    for (int s = 0; s < nk; s += 2) {
+    // pairs of steps, then an odd last one: one path through the loop, so the
+    // accumulators stay in place (a conditional second step made the compiler
+    // copy all of them at the back edge)
+    int s = 0;
+    for (; s + 1 < nk; s += 2) {
         k_step(s, 0);
-        if (s + 1 < nk) k_step(s + 1, 1);
+        k_step(s + 1, 1);
     }
+    if (s < nk) k_step(s, 0);
 
     // epilogue: lane holds column lane % MT of each tile, register r the row
     // M::row(lane, r). For the argmax, the MT lanes of a row reduce their keys.
