@@ -33,10 +33,12 @@ def quant_gpu(bl, x, gain, eps):
 
 # ---- activation quant ------------------------------------------------------------------
 
-# rows up to 16384 values run register-resident (4, 8, 16, 20 or 32 values per
-# thread); longer rows the three-pass kernel
+# few rows: up to 16384 values register-resident in a 512-thread workgroup (4,
+# 8, 16, 20 or 32 values per thread), longer rows the three-pass kernel; from
+# 256 rows one wave per row (2 .. 32 float4 chunks per lane, ragged tails)
 QUANT_CASES = [(1, 64), (1, 2560), (1, 10240), (3, 192), (7, 640), (33, 2560), (5, 16384), (4, 8192), (2, 4160),
-               (2, 16448)]
+               (2, 16448), (300, 2560), (256, 192), (256, 640), (256, 2048), (259, 4096), (257, 8192), (260, 4160),
+               (258, 10240)]
 
 
 @pytest.mark.parametrize("norm", [False, True])
