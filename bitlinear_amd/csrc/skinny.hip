@@ -218,19 +218,19 @@ struct Split {
 };
 
 // Super-steps per wave (1, 2 or 4) and waves per workgroup for nss
-// super-steps: up to 16 waves of as few super-steps as fit in one round, at
-// most kw_max each (the
+// super-steps: up to max_waves waves of as few super-steps as fit in one round,
+// at most kw_max each (the
 // operands of a lane at 16 waves must fit its 128 VGPRs); a longer K takes
 // several rounds.
-inline Split pick_split(int k, int kw_max)
+inline Split pick_split(int k, int kw_max, int max_waves)
 {
     const int nss = (k + 127) / 128;
-    int kw = (nss + kMaxWaves - 1) / kMaxWaves;
+    int kw = (nss + max_waves - 1) / max_waves;
     if (kw == 3) kw = 4;
     if (kw > kw_max) kw = kw_max;
     if (kw < 1) kw = 1;
     int waves = (nss + kw - 1) / kw;
-    if (waves > kMaxWaves) waves = kMaxWaves;
+    if (waves > max_waves) waves = max_waves;
     return {kw, waves};
 }
 
@@ -239,8 +239,11 @@ int launch_nb(const SkinnyArgs& a, hipStream_t s)
 {
     constexpr int cols = PAIR ? 32 : 32 * NB;
     constexpr int kw_max = NB == 1 ? 4 : 2;
-    const Split sp = pick_split(a.k, kw_max);
-    const dim3 grid((a.n + cols - 1) / cols), block(64 * sp.waves);
+    const int tiles = (a.n + cols - 1) / cols;
+    // More workgroups than CUs (the LM head): at most 8 waves each, so two fit
+    // on a CU (LDS and registers) and the grid runs in fewer rounds.
+    const Split sp = pick_split(a.k, kw_max, tiles > 256 ? kMaxWaves / 2 : kMaxWaves);
+    const dim3 grid(tiles), block(64 * sp.waves);
     const size_t lds = (size_t)NB * 16 * 64 * sizeof(int) + (size_t)sp.waves * kStageA;
     if (sp.kw == 1)
         skinny_kernel<NB, PAIR, 1, NAT><<<grid, block, lds, s>>>(a);
