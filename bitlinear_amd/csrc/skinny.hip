@@ -31,6 +31,7 @@ namespace bl {
 namespace {
 
 constexpr int kMaxWaves = 16;  // waves per workgroup (K split)
+constexpr int kPreSlots = 1;   // epilogue slots per wave whose inputs are loaded up front
 
 // Operands of one super-step for one lane: the packed weights of its B tiles,
 // and 4 x 16 bytes of the activations in the row-contiguous load order (lane l
@@ -78,6 +79,32 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyArgs a)
     const int nss = (a.k + 127) / 128;  // the last may be partial
 
     for (int i = threadIdx.x; i < NB * 16 * 64; i += blockDim.x) red[i] = 0;
+
+    // Epilogue inputs of this wave's slots, loaded with the operands when a
+    // wave has at most kPreSlots slots (16 / S): they travel in the same trip.
+    int pre_qs[kPreSlots];
+    float pre_sa[kPreSlots], pre_sw[kPreSlots][NB], pre_res[kPreSlots][NB];
+    if (S * kPreSlots >= 16) {
+#pragma unroll
+        for (int i = 0; i < kPreSlots; ++i) {
+            const int r = min(wave + S * i, 15);  // slots past 15 load slot 15 again (unused)
+            const int tok = tile_row(lane, r);
+            const int tokc = min(tok, a.m - 1);
+            pre_qs[i] = a.act_sum[tokc];
+            pre_sa[i] = a.act_scale[tokc];
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const int col = PAIR ? n0 + lc : n0 + 32 * j + lc;
+                if (PAIR)
+                    pre_sw[i][j] = a.w_scale_ptr ? a.w_scale_ptr[j] : (j == 0 ? a.w_scale0 : a.w_scale1);
+                else
+                    pre_sw[i][j] = a.w_scale_ptr ? a.w_scale_ptr[min(col, a.n - 1) / a.n_per_scale] : a.w_scale0;
+                pre_res[i][j] = (!PAIR && a.residual && a.y && tok < a.m && col < a.n)
+                                    ? a.residual[(size_t)tok * a.ldy + col]
+                                    : 0.0f;
+            }
+        }
+    }
 
     v16i acc[NB];
 #pragma unroll
@@ -136,21 +163,18 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyArgs a)
     __syncthreads();
 
     const int tiles = gridDim.x;
-    for (int r = wave; r < 16; r += S) {
+    // Epilogue of slot r (C row 4 b + r of the tile, see tile_row) with the
+    // slot's per-token and per-column inputs.
+    auto emit = [&](int r, int qs, float sa, const float* sw, const float* res) __attribute__((always_inline)) {
         const int tok = tile_row(lane, r);
-        const int tokc = min(tok, a.m - 1);
-        const int qs = a.act_sum[tokc];
-        const float sa = a.act_scale[tokc];
         int tot[NB];
 #pragma unroll
         for (int j = 0; j < NB; ++j) tot[j] = red[(j * 16 + r) * 64 + lane] - qs;
         if (PAIR) {
             const int col = n0 + lc;
             if (tok < a.m && col < a.n) {
-                const float sg = a.w_scale_ptr ? a.w_scale_ptr[0] : a.w_scale0;
-                const float su = a.w_scale_ptr ? a.w_scale_ptr[1] : a.w_scale1;
-                const float gate = (float)tot[0] * (1.0f / (sa * sg));
-                const float up = (float)tot[1] * (1.0f / (sa * su));
+                const float gate = (float)tot[0] * (1.0f / (sa * sw[0]));
+                const float up = (float)tot[1] * (1.0f / (sa * sw[1]));
                 const float gp = gate > 0.0f ? gate : 0.0f;
                 const float g2 = gp * gp;
                 const size_t o = (size_t)tok * a.ldy + col;
@@ -166,9 +190,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyArgs a)
                 if (tok < a.m && col < a.n) {
                     const size_t o = (size_t)tok * a.ldy + col;
                     if (a.y) {
-                        const float sw = a.w_scale_ptr ? a.w_scale_ptr[col / a.n_per_scale] : a.w_scale0;
-                        float v = (float)tot[j] * (1.0f / (sa * sw));
-                        if (a.residual) v = a.residual[o] + v;
+                        float v = (float)tot[j] * (1.0f / (sa * sw[j]));
+                        if (a.residual) v = res[j] + v;
                         a.y[o] = v;
                     }
                     if (a.acc0) a.acc0[o] = tot[j];
@@ -184,6 +207,38 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyArgs a)
                 }
                 if (lc == 0 && tok < a.m) a.tile_keys[(size_t)tok * tiles + blockIdx.x] = best;
             }
+        }
+    };
+    // the slot's inputs: sum(q), s_a of its token, the weight scale and the
+    // residual of its columns
+    auto fetch = [&](int r, int& qs, float& sa, float* sw, float* res) __attribute__((always_inline)) {
+        const int tok = tile_row(lane, r);
+        const int tokc = min(tok, a.m - 1);
+        qs = a.act_sum[tokc];
+        sa = a.act_scale[tokc];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const int col = PAIR ? n0 + lc : n0 + 32 * j + lc;
+            if (PAIR)
+                sw[j] = a.w_scale_ptr ? a.w_scale_ptr[j] : (j == 0 ? a.w_scale0 : a.w_scale1);
+            else
+                sw[j] = a.w_scale_ptr ? a.w_scale_ptr[min(col, a.n - 1) / a.n_per_scale] : a.w_scale0;
+            res[j] = (!PAIR && a.residual && a.y && tok < a.m && col < a.n) ? a.residual[(size_t)tok * a.ldy + col]
+                                                                          : 0.0f;
+        }
+    };
+    if (S * kPreSlots >= 16) {
+        // at most kPreSlots slots per wave: their inputs were loaded with the
+        // operands (pre_* below), one trip to memory fewer
+#pragma unroll
+        for (int i = 0; i < kPreSlots; ++i)
+            if (wave + S * i < 16) emit(wave + S * i, pre_qs[i], pre_sa[i], pre_sw[i], pre_res[i]);
+    } else {
+        for (int r = wave; r < 16; r += S) {
+            int qs;
+            float sa, sw[NB], res[NB];
+            fetch(r, qs, sa, sw, res);
+            emit(r, qs, sa, sw, res);
         }
     }
 }
