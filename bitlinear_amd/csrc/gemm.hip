@@ -222,7 +222,26 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(2))
     if (s < nk) k_step(s, 0);
 
     // epilogue: lane holds column lane % MT of each tile, register r the row
-    // M::row(lane, r). For the argmax, the MT lanes of a row reduce their keys.
+    // M::row(lane, r). An interior tile that only writes y takes a path with
+    // no per-element bounds or pointer checks (they are uniform there; the
+    // general path below unrolls into hundreds of branches).
+    if (y && !residual && !acc_out && !keys && m0 + C::BM <= m && n0 + C::BN <= n) {
+        float* yb = y + (size_t)(m0 + wm) * ldy + n0 + wn + (lane % MT);
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i) {
+#pragma unroll
+            for (int r = 0; r < C::NACC; ++r) {
+                const int lrow = wm + i * MT + M::row(lane, r);
+                const int qs = lds_qsum[lrow];
+                const float inv = lds_inv[lrow];
+                float* yr = yb + (size_t)(i * MT + M::row(lane, r)) * ldy;
+#pragma unroll
+                for (int j = 0; j < C::TN; ++j) yr[j * MT] = (float)(acc[i][j][r] - qs) * inv;
+            }
+        }
+        return;
+    }
+    // General path; for the argmax, the MT lanes of a row reduce their keys.
 #pragma unroll
     for (int i = 0; i < C::TM; ++i) {
 #pragma unroll
