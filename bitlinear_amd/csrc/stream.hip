@@ -20,11 +20,19 @@
 //     for the step's input, so the weight fetch overlaps the hand-over (the o
 //     rows go out with P1's, ahead of P2's short wait). The rows go straight
 //     into registers in the layout of the MFMA B operand;
-//   - a step's output vector is published as 64-bit words {fp32 value, epoch}
-//     written with device-scope atomic stores; a consumer loads all words of
-//     the vector it needs in one batch and repeats until every epoch matches.
-//     Value and flag travel in one single-copy-atomic store, so no fence or
-//     separate barrier is needed;
+//   - a step's output vector is published as fp32 words written with
+//     device-scope atomic stores, the word's value doubling as its flag: 0
+//     (+0.0) means "not written yet" (+0.0 itself is published as -0.0).
+//     Each vector has two copies that alternate by layer; a producer clears
+//     its words of the other copy when it writes, which every consumer has
+//     finished reading by then. A consumer loads all words of the vector it
+//     needs in one batch and repeats until none reads 0. Value and flag
+//     travel in one single-copy-atomic store, so no fence or separate
+//     barrier is needed, and a poll moves 4 bytes per value (an epoch-tagged
+//     8-byte word measured 4 % slower: the hand-overs are sensitive to the
+//     poll traffic). P2's wait uses epoch-tagged 8-byte flags, one per
+//     workgroup, four per 128-byte line (one per line doubles the poll
+//     traffic, sixteen per line makes the writers contend);
 //   - every workgroup then computes the RMSNorm + activation quant of the full
 //     vector itself, so no extra round trip is spent on broadcasting q. The
 //     sum of squares keeps the fixed fp64 order of quant.hip: thread t sums
@@ -61,7 +69,7 @@ constexpr int kGrid = 256;   // workgroups: one per CU of an MI355X
 constexpr uint32_t kCodeMask = 0x03030303u;
 constexpr long long kTimeoutTicks = 200000000LL;  // 2 s at 100 MHz
 constexpr int kMaxK = 10240;
-constexpr int kFlagStride = 16;  // words between the "P1 finished" flags: one per 128-byte line
+constexpr int kFlagStride = 4;   // words between the "P1 finished" flags: four per 128-byte line
 
 constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 
@@ -92,9 +100,9 @@ struct StreamArgs {
     float* x;
     float* qkv;
     long long qkv_layer_stride;  // elements between layers (0: scratch reused)
-    unsigned long long* xa;      // x at layer start (published by P4)
-    unsigned long long* xb;      // x after the o residual (published by P2)
-    unsigned long long* hh;      // h (published by P3)
+    uint32_t* xa;                // x at layer start (published by P4), two copies
+    uint32_t* xb;                // x after the o residual (published by P2), two copies
+    uint32_t* hh;                // h (published by P3), two copies
     unsigned long long* done;    // per-workgroup "P1 finished" flags
     uint32_t* ctrl;              // [0] epoch base, [1] status
     int n_layers;
@@ -110,6 +118,22 @@ __device__ __forceinline__ void ll_store(unsigned long long* p, float v, uint32_
 __device__ __forceinline__ unsigned long long ll_load(const unsigned long long* p)
 {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Published vector words are plain fp32 bit patterns with 0x00000000 (+0.0)
+// meaning "not written yet": a producer publishes +0.0 as -0.0 (the values
+// are only squared, scaled and rounded by the consumer, where the two agree)
+// and clears its word of the vector's other copy, which is read again only
+// two hand-overs later, after every consumer has finished with it.
+__device__ __forceinline__ void val_store(uint32_t* p, float v)
+{
+    const uint32_t b = __float_as_uint(v);
+    __hip_atomic_store(p, b == 0u ? 0x80000000u : b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void val_clear(uint32_t* p)
+{
+    __hip_atomic_store(p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ uint32_t status_load(const uint32_t* ctrl)
@@ -146,6 +170,38 @@ __device__ bool poll_vec(const unsigned long long* buf, uint32_t e, float* v, ui
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i) v[i] = (t + kT * i < N) ? __uint_as_float((uint32_t)w[i]) : 0.0f;
+    if (__syncthreads_or(failed ? 1 : 0)) {
+        if (t == 0) __hip_atomic_fetch_or(ctrl + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return false;
+    }
+    return true;
+}
+
+// As poll_vec for a published fp32 vector: repeats until no word reads 0.
+template <int N>
+__device__ bool poll_val(const uint32_t* buf, float* v, uint32_t* ctrl, long long t_start)
+{
+    constexpr int NI = cdiv(N, kT);
+    const int t = threadIdx.x;
+    uint32_t w[NI];
+    bool failed = false;
+    for (int spin = 0;; ++spin) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            w[i] = __hip_atomic_load(buf + min(t + kT * i, N - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        bool ready = true;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) ready = ready && w[i] != 0u;
+        if (ready) break;
+        if ((spin & 15) == 15 &&
+            (status_load(ctrl) != 0 || (long long)__builtin_amdgcn_s_memrealtime() - t_start > kTimeoutTicks)) {
+            failed = true;
+            break;
+        }
+        __builtin_amdgcn_s_sleep(10);
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) v[i] = (t + kT * i < N) ? __uint_as_float(w[i]) : 0.0f;
     if (__syncthreads_or(failed ? 1 : 0)) {
         if (t == 0) __hip_atomic_fetch_or(ctrl + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return false;
@@ -387,6 +443,15 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
 #pragma unroll
         for (int i = 0; i < 7; ++i) sw[i] = a.scales[7 * l + i];
         float* qkv = a.qkv + (size_t)l * a.qkv_layer_stride;
+        // copy of the published vectors written in this layer (the phase
+        // counter makes the alternation continue across calls)
+        const int cp = (int)(((base >> 2) + (uint32_t)l) & 1u);
+        uint32_t* xa_in = a.xa + (cp ^ 1) * D;  // written by the previous layer's P4
+        uint32_t* xa_out = a.xa + cp * D;
+        uint32_t* xb_cur = a.xb + cp * D;
+        uint32_t* xb_old = a.xb + (cp ^ 1) * D;
+        uint32_t* hh_cur = a.hh + cp * F;
+        uint32_t* hh_old = a.hh + (cp ^ 1) * F;
 
         // ---- P1: q, k, v ----
         {
@@ -395,7 +460,7 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
             float v[ND];
             if (l == 0) {
                 load_strided<D>(a.x, v);
-            } else if (!poll_vec<D>(a.xa, E, v, a.ctrl, t_start)) {
+            } else if (!poll_val<D>(xa_in, v, a.ctrl, t_start)) {
                 return;
             }
             norm_quant<D>(v, g1, a.eps, sh, s_a, qsum);
@@ -424,7 +489,8 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
             if (e2) {
                 const float inv = 1.0f / (s_a * sw[3]);
                 xres = xres + (float)(sh.acc[t] - qsum) * inv;
-                ll_store(a.xb + r2 + t, xres, E + 2);
+                val_store(xb_cur + r2 + t, xres);
+                val_clear(xb_old + r2 + t);
             }
         }
         // ---- P3: gate/up with relu(gate)^2 * up ----
@@ -435,7 +501,7 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
             }
             fetch3(l);
             float v[ND];
-            if (!poll_vec<D>(a.xb, E + 2, v, a.ctrl, t_start)) return;
+            if (!poll_val<D>(xb_cur, v, a.ctrl, t_start)) return;
             norm_quant<D>(v, g3, a.eps, sh, s_a, qsum);
             dots<S3>(w3, sh.q, sh.zero, sh.acc);
             __syncthreads();
@@ -444,7 +510,8 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
                 const float up = (float)(sh.acc[S3::R + t] - qsum) * (1.0f / (s_a * sw[5]));
                 const float gp = gate > 0.0f ? gate : 0.0f;
                 const float g2v = gp * gp;
-                ll_store(a.hh + r3 + t, g2v * up, E + 3);
+                val_store(hh_cur + r3 + t, g2v * up);
+                val_clear(hh_old + r3 + t);
             }
         }
         // ---- P4: down projection of h, residual ----
@@ -452,14 +519,15 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
             if (t < S4::R) sh.acc[t] = 0;
             fetch4(l);
             float v[NF];
-            if (!poll_vec<F>(a.hh, E + 3, v, a.ctrl, t_start)) return;
+            if (!poll_val<F>(hh_cur, v, a.ctrl, t_start)) return;
             norm_quant<F>(v, g4, a.eps, sh, s_a, qsum);
             dots<S4>(w4, sh.q, sh.zero, sh.acc);
             __syncthreads();
             if (e2) {
                 const float inv = 1.0f / (s_a * sw[6]);
                 xres = xres + (float)(sh.acc[t] - qsum) * inv;
-                ll_store(a.xa + r2 + t, xres, E + 4);
+                val_store(xa_out + r2 + t, xres);
+                val_clear(xa_in + r2 + t);
                 if (l == a.n_layers - 1) a.x[r2 + t] = xres;
             }
         }
@@ -523,11 +591,13 @@ int launch_stream_persistent(const uint8_t* weights, const float* scales, const 
     a.x = x;
     a.qkv = qkv;
     a.qkv_layer_stride = qkv_stride;
+    // 8-byte flag words first, then two copies of each published vector
     unsigned long long* ll = static_cast<unsigned long long*>(ll_region);
-    a.xa = ll;
-    a.xb = ll + d;
-    a.hh = ll + 2 * d;
-    a.done = ll + 2 * d + f;
+    a.done = ll;
+    uint32_t* vec = reinterpret_cast<uint32_t*>(ll + (size_t)kGrid * kFlagStride);
+    a.xa = vec;
+    a.xb = vec + 2 * d;
+    a.hh = vec + 4 * d;
     a.ctrl = ctrl;
     a.n_layers = n_layers;
     a.eps = eps;
