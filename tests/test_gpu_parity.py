@@ -248,6 +248,32 @@ def test_decode_stream(bl, olib, n_layers, m, d, f):
 
 
 @pytest.mark.parametrize("d,f", [(256, 1024), (2560, 10240)])
+def test_decode_stream_all_zero_vectors(bl, olib, d, f):
+    """x = 0 and z = 0: every vector the persistent kernel hands over (x, x
+    after o, h) is +-0 in every word, which is the encoding's "not written"
+    value once negated. Three layers, two calls (both copies of each vector
+    carry zeros); the results must still come out, all zero, like the oracle's."""
+    from gpu_helpers import make_layers, run_stream, stream_ctrl
+    n_layers = 3
+    log(f"stream zeros d={d} f={f}")
+    layers, dev = make_layers(W.W_STREAM, n_layers, d, f, 1, olib)
+    dev["z"].zero_()
+    for lw in layers:
+        lw["z"] = np.zeros_like(lw["z"])
+    x = np.zeros((1, d), np.float32)
+    ws = None
+    for call in range(2):
+        gx, gqkv, ws = run_stream(dev, n_layers, 1, d, f, 1e-5, x, ws)
+        assert stream_ctrl(ws)[1] == 0, "stream status word"
+        ox, oqkv = oracle.chain(x, layers, 1e-5, olib)
+        for l in range(n_layers):
+            assert_f32(gqkv[l], oqkv[l], f"qkv layer {l} call {call}")
+        assert_f32(gx, ox, f"x after call {call}")
+        assert not np.any(gx), "all-zero stream stays zero"
+        x = gx
+
+
+@pytest.mark.parametrize("d,f", [(256, 1024), (2560, 10240)])
 def test_decode_stream_repeated_calls(bl, olib, d, f):
     """Three tokens through one workspace: each call continues the phase counter
     and reads the previous call's output; every result matches the oracle."""
