@@ -271,6 +271,25 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def graph_ms(torch, calls, outputs):
+    """Time `calls` replayed from a HIP graph (the launches only, without the
+    per-call Python and ctypes cost). Returns (ms per replay, whether the
+    replay's outputs equal those of the eager run just before it)."""
+    calls()
+    torch.cuda.synchronize()
+    want = [o.clone() for o in outputs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    g.replay()
+    torch.cuda.synchronize()
+    same = all(bool(torch.equal(o.view(torch.uint8), w.view(torch.uint8))) for o, w in zip(outputs, want))
+    with Timer() as t:
+        g.replay()
+    del g
+    return t.ms, same
+
+
 def extra_measurements(bl, torch, T, dev0):
     out = {}
     # ---- single BitLinear decode GEMV 2560 -> 2560 (quant + GEMV), weights rotated
@@ -294,9 +313,19 @@ def extra_measurements(bl, torch, T, dev0):
             bl.bitlinear_quant_act(x1, None, 1e-5, q1, s1, qs1)
             bl.bitlinear_gemv(pw[i], sw, d, d, q1, s1, qs1, 1, None, y1)
     ms = tg.ms / copies
+
+    def gemv_calls():
+        for i in range(copies):
+            bl.bitlinear_quant_act(x1, None, 1e-5, q1, s1, qs1)
+            bl.bitlinear_gemv(pw[i], sw, d, d, q1, s1, qs1, 1, None, y1)
+    gms, gsame = graph_ms(torch, gemv_calls, [q1, s1, qs1, y1])
+    gms /= copies
     out["gemv"] = {"workload": "quant 1x2560 + GEMV 2560->2560 (1,638,400 packed B), weights rotated over 320 copies",
                    "us_per_call": round(ms * 1e3, 3), "weight_gbs": round(d * d / 4 / (ms * 1e-3) / 1e9, 1),
-                   "frac_hbm": round(d * d / 4 / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                   "frac_hbm": round(d * d / 4 / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                   "us_per_call_graph": round(gms * 1e3, 3),
+                   "weight_gbs_graph": round(d * d / 4 / (gms * 1e-3) / 1e9, 1),
+                   "graph_matches_eager": gsame}
     del pw
     # ---- BitNet-3B FFN at one token, weights rotated over 27 copies (531 MB) ----
     f = 10240
@@ -320,10 +349,21 @@ def extra_measurements(bl, torch, T, dev0):
                           scales[2], None, of, wsf)
     ms = tf.ms / fcopies
     fb = 3 * d * f // 4
+
+    def ffn_calls():
+        for i in range(fcopies):
+            bl.bitnet_ffn(xf, 1, d, f, gn, gs, 1e-5, fw[0][i], scales[0], fw[1][i], scales[1], fw[2][i],
+                          scales[2], None, of, wsf)
+    gms, gsame = graph_ms(torch, ffn_calls, [of])
+    gms /= fcopies
     out["ffn"] = {"workload": "BitNet-3B FFN at 1 token (19,660,800 packed B), weights rotated over 27 copies",
                   "us_per_call": round(ms * 1e3, 3), "weight_gbs": round(fb / (ms * 1e-3) / 1e9, 1),
-                  "frac_hbm": round(fb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    log(f"gemv {out['gemv']['us_per_call']} us, ffn {out['ffn']['us_per_call']} us")
+                  "frac_hbm": round(fb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "us_per_call_graph": round(gms * 1e3, 3), "weight_gbs_graph": round(fb / (gms * 1e-3) / 1e9, 1),
+                  "frac_hbm_graph": round(fb / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "graph_matches_eager": gsame}
+    log(f"gemv {out['gemv']['us_per_call']} us ({out['gemv']['us_per_call_graph']} us from a graph), "
+        f"ffn {out['ffn']['us_per_call']} us ({out['ffn']['us_per_call_graph']} us from a graph)")
     del fw
     # ---- prefill GEMM 2048 x 2560 -> 10240 ----
     M, K, N = 2048, 2560, 10240
@@ -389,12 +429,22 @@ def extra_measurements(bl, torch, T, dev0):
             batched_step()
     bytes_b = L * bl.bitnet_layer_bytes(d, f) + V * d // 4
     ms_b = tb.ms / iters
+    # x is updated in place, so the eager/graph comparison restarts both from one x
+    x_start = xb.clone()
+
+    def batched_from_start():
+        xb.copy_(x_start)
+        batched_step()
+    gms, gsame = graph_ms(torch, batched_from_start, [xb, idx])
     out["batched"] = {"workload": "BitNet-1.3B stream, 32 tokens, 24 layers x 7 BitLinears + LM head 2048->50000 "
                                   "with fused argmax", "ms_per_step": round(ms_b, 4),
                       "weight_gbs": round(bytes_b / (ms_b * 1e-3) / 1e9, 1),
                       "us_per_token": round(ms_b * 1e3 / m, 3), "weight_bytes": bytes_b,
-                      "frac_hbm": round(bytes_b / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    log(f"batched: {ms_b:.4f} ms per 32-token step")
+                      "frac_hbm": round(bytes_b / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                      "ms_per_step_graph": round(gms, 4),
+                      "weight_gbs_graph": round(bytes_b / (gms * 1e-3) / 1e9, 1),
+                      "graph_matches_eager": gsame}
+    log(f"batched: {ms_b:.4f} ms per 32-token step ({gms:.4f} ms from a graph)")
     del dev, head
     return out
 
