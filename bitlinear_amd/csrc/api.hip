@@ -115,6 +115,16 @@ bl::SkinnyArgs skinny_gateup(const uint8_t* w_gate, float s_gate, const uint8_t*
     return a;
 }
 
+// True while s records into a graph (or the query fails): the persistent
+// stream kernel needs a cooperative launch, so a capture takes the
+// launch-per-step path (same results).
+bool capturing(hipStream_t s)
+{
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &st) != hipSuccess) return true;
+    return st != hipStreamCaptureStatusNone;
+}
+
 int ffn_impl(const float* x, int64_t m, int64_t d, int64_t f, const float* g_ffn, const float* g_sub, float eps,
              const uint8_t* w_gate, float s_gate, const uint8_t* w_up, float s_up, const uint8_t* w_down,
              float s_down, const float* scale_ptr /* [gate, up, down] or null */, const float* residual, float* out,
@@ -290,7 +300,7 @@ int bitnet_decode_stream(const uint8_t* weights, const float* scales, const floa
     if (workspace_bytes < bitnet_stream_workspace_bytes(m, d, f)) return BL_ERR_WORKSPACE;
     const hipStream_t s = as_stream(stream);
     const StreamLayout L = stream_layout(m, d, f);
-    if (bl::stream_persistent_fits((int)m, (int)d, (int)f)) {
+    if (bl::stream_persistent_fits((int)m, (int)d, (int)f) && !capturing(s)) {
         float* qkv_out = qkv ? qkv : at<float>(workspace, L.qkv);
         return bl::launch_stream_persistent(weights, scales, gains, z, (int)n_layers, (int)d, (int)f, eps, x, qkv_out,
                                             qkv ? 3 * d : 0, at<void>(workspace, L.ll),

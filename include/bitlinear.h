@@ -228,8 +228,9 @@ int bitnet_ffn(const float *x, int64_t m, int64_t d, int64_t f,
  * sets status = 1 (status = 2: the phase counter is exhausted after about 2^31
  * steps). A nonzero status stays set, and further calls do nothing, until the
  * workspace is zero-filled again; the caller reads it after synchronising.
- * Calls that share a workspace must not overlap. Other shapes run one launch
- * per step (at 9..32 tokens one MFMA launch per projection, q/k/v together and
+ * Calls that share a workspace must not overlap. Other shapes, and any call
+ * made while the stream is being captured into a graph, run one launch per
+ * step (at 9..32 tokens one MFMA launch per projection, q/k/v together and
  * gate/up fused), with the same results.
  * Errors: NULL, SHAPE, ALIGN, WORKSPACE, LAUNCH. */
 size_t bitnet_layer_bytes(int64_t d, int64_t f);

@@ -202,7 +202,8 @@ def _ffn_case(bl, olib, m, d, f, seed, with_residual):
     res = W.activations(g, m, d) if with_residual else None
     dev = torch_dev()
     out = torch.empty((m, d), dtype=torch.float32, device=dev)
-    ws = torch.zeros(bl.bitnet_ffn_workspace_bytes(m, d, f), dtype=torch.uint8, device=dev)
+    # the workspace's content on entry is unspecified: start from garbage
+    ws = torch.full((bl.bitnet_ffn_workspace_bytes(m, d, f),), 0x5A, dtype=torch.uint8, device=dev)
     bl.bitnet_ffn(to_dev(x), m, d, f, to_dev(gn), to_dev(gs), 1e-5, to_dev(pg), sg, to_dev(pu), su, to_dev(pd), sd,
                   to_dev(res) if res is not None else None, out, ws, flags=bl.BITNET_FFN_WRITE_ACC)
     r = oracle.ffn(x, gn, gs, 1e-5, pg, sg, pu, su, pd, sd, olib)
@@ -223,7 +224,8 @@ def _ffn_case(bl, olib, m, d, f, seed, with_residual):
 
 @pytest.mark.parametrize("m,d,f,res", [(1, 64, 128, False), (1, 192, 640, True), (3, 256, 1024, False),
                                         (1, 2560, 10240, False), (8, 640, 2560, True), (12, 320, 640, False),
-                                        (40, 256, 512, True)])
+                                        (40, 256, 512, True), (1, 256, 1024, True), (1, 2048, 8192, True),
+                                        (1, 2560, 10240, True)])
 def test_ffn(bl, olib, m, d, f, res):
     _ffn_case(bl, olib, m, d, f, m * 1000 + d + f, res)
 

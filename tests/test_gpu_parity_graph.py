@@ -116,3 +116,24 @@ def test_graph_layer_stream_and_head(bl, olib, m):
         bl.bitlinear_gemm(head, sh, vocab, d, qf, sf, qsf, m, None, None, None, idx, wsh)
 
     _replay_check(torch, calls, [x, qkv, qf, sf, qsf, idx], lambda: x.copy_(x0))
+
+
+def test_graph_one_token_stream(bl, olib):
+    """One token of a shape with a persistent kernel: the eager call runs the
+    persistent kernel, the captured one the launch-per-step path (a cooperative
+    launch is not recorded); the replays must equal the eager result bit for bit."""
+    import torch
+    dev = torch.device("cuda", 0)
+    n_layers, d, f, m = 2, 256, 1024, 1
+    log("graph one-token stream")
+    layers, dw = make_layers(W.W_STREAM, n_layers, d, f, m, olib)
+    x0 = to_dev(W.activations(W.rng(W.W_STREAM, 996, W.T_X), m, d))
+    x = x0.clone()
+    qkv = torch.empty((n_layers, m, 3 * d), dtype=torch.float32, device=dev)
+    ws = torch.zeros(bl.bitnet_stream_workspace_bytes(m, d, f), dtype=torch.uint8, device=dev)
+
+    def calls():
+        bl.bitnet_decode_stream(dw["weights"], dw["scales"], dw["gains"], dw["z"], n_layers, m, d, f, 1e-5, x, qkv,
+                                ws)
+
+    _replay_check(torch, calls, [x, qkv], lambda: x.copy_(x0))
