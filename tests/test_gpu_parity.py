@@ -55,6 +55,73 @@ def test_quant_act(bl, olib, m, k, norm):
     assert_exact(qs, oqs, "act_sum")
 
 
+def midpoint_row(k, seed, eps=1e-5):
+    """A row x of k fp32 values whose RMSNorm scale in fp64, 1 / sqrt(ss / k + eps)
+    with ss the fixed-order sum of squares, lies within 2^-47 (relative) of the
+    midpoint between two fp32 values, so that any error above about 2^-47 in
+    the divide, square root or reciprocal flips the fp32 scale. The last
+    element is scanned over 2^23 fp32 values whose squares step ss by about
+    2^-46 (relative); the sum follows the same 512-partial butterfly tree."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(k).astype(np.float32)
+    x[0] = 1.0  # its normalised value (gain 1) is the scale itself
+    f = k - 1
+    sq = x.astype(np.float64) ** 2
+    parts = np.zeros(512)
+    for p_ in range(512):
+        acc = 0.0
+        for j in range(p_, k, 512):
+            if j != f:
+                acc += sq[j]
+        parts[p_] = acc
+    pf = f % 512
+    ss_approx = float(np.sum(sq[:-1]))
+    x0 = np.float32(np.sqrt(ss_approx) * 2.0 ** -12)
+    cand = (np.float64(x0) * (1.0 + np.arange(1 << 23, dtype=np.float64) * 2.0 ** -23)).astype(np.float32)
+    # leaf pf of the butterfly tree, then its sibling subtree at each level
+    node = parts[pf] + cand.astype(np.float64) ** 2
+    lo_idx = pf
+    for lev in range(9):
+        size = 1 << lev
+        sib_start = (lo_idx ^ size) & ~(size - 1)
+        sib = parts[sib_start:sib_start + size]
+        # the sibling subtree's own sum in the same butterfly order
+        t = sib.copy()
+        while t.size > 1:
+            t = t[0::2] + t[1::2]
+        node = node + t[0]
+        lo_idx &= ~size
+    r64 = 1.0 / np.sqrt(node / k + eps)
+    r32 = r64.astype(np.float32)
+    b = r32.view(np.uint32)
+    lo = 0.5 * (r32.astype(np.float64) + (b - 1).view(np.float32).astype(np.float64))
+    hi = 0.5 * (r32.astype(np.float64) + (b + 1).view(np.float32).astype(np.float64))
+    dist = np.minimum(r64 - lo, hi - r64) / r64
+    j = int(np.argmin(dist))
+    assert dist[j] < 2.0 ** -47, dist[j]
+    x[f] = cand[j]
+    return x
+
+
+@pytest.mark.parametrize("m,k", [(1, 64), (1, 2560), (3, 10240), (256, 2048), (1, 20480)])
+def test_quant_act_rms_scale_near_fp32_midpoint(bl, olib, m, k):
+    """Rows whose RMSNorm scale sits next to an fp32 rounding boundary (for
+    k = 64, exactly on it: a tie to even): only correctly rounded fp64 divide
+    and square root give the oracle's fp32 scale. Every kernel of the quant
+    dispatch gets one (one workgroup per row, one wave per row at 256 rows,
+    three passes above 16384)."""
+    log(f"quant_act midpoint rows m={m} k={k}")
+    g = W.rng(100, 7000 + m, k)
+    x = W.activations(g, m, k)
+    x[m // 2] = midpoint_row(k, 11 + k)
+    gain = np.ones(k, np.float32)
+    q, s, qs = quant_gpu(bl, x, gain, 1e-5)
+    oq, os_, oqs = oracle.quant_act(x, gain, 1e-5, olib)
+    assert_exact(q, oq, "q")
+    assert_exact(s.view(np.uint32), os_.view(np.uint32), "act_scale bits")
+    assert_exact(qs, oqs, "act_sum")
+
+
 def test_quant_act_special_rows(bl, olib):
     """Ties at +-0.5 of a code, an all-zero row, a constant row, one huge outlier,
     tiny values near the absmax floor."""
