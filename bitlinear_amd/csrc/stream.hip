@@ -17,9 +17,20 @@
 // one workgroup per CU (256 on an MI355X) stays resident for the whole token:
 //   - each workgroup owns fixed output rows of every step and issues the loads
 //     of those weight rows (and of the step's RMSNorm gains) before it waits
-//     for the step's input, so the weight fetch overlaps the hand-over (the o
-//     rows go out with P1's, ahead of P2's short wait). The rows go straight
-//     into registers in the layout of the MFMA B operand;
+//     for the step's input, so the weight fetch overlaps the hand-over. The
+//     rows go straight into registers in the layout of the MFMA B operand;
+//   - a wave's loads complete in issue order, so a wait for a hand-over also
+//     waits for every weight row issued before it, and a step whose rows come
+//     from HBM (13 MB for gate/up) holds its wait until they have streamed
+//     in. Each workgroup therefore pulls its rows of a later step into L2
+//     one step or two ahead, right after a wait has ended, while HBM is
+//     otherwise idle: gate/up after P2's wait, down and the next layer's o
+//     rows after P3's, the next layer's q/k/v rows after P4's. The prefetch
+//     is one dword per 128-byte line, loaded straight into a scratch area of
+//     LDS (global_load_lds_dword), so it needs no register, and the compiler,
+//     which does not see it, adds no wait for it; the wave's next poll waits
+//     for it like for any older load. Every prefetch is followed by a poll
+//     before the workgroup can leave, so none is in flight at the end;
 //   - a step's output vector is published as fp32 words written with
 //     device-scope atomic stores, the word's value doubling as its flag: 0
 //     (+0.0) means "not written yet" (+0.0 itself is published as -0.0).
@@ -241,7 +252,32 @@ struct Shared {
     float red_f[kT / 64];
     int red_i[kT / 64];
     int acc[128];  // per-row accumulators of a step (gate rows, then up rows)
+    uint32_t trash[64];  // written by the L2 prefetch loads, never read
 };
+
+// One dword of the line at p straight into LDS at lds_off + 4 lane: the load
+// only brings the line into L2 (and this CU's L1). m0 holds the LDS address
+// for the instruction and is restored afterwards.
+__device__ __forceinline__ void prefetch_line(const void* p, uint32_t lds_off)
+{
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\t"
+                 "s_mov_b32 m0, %2\n\t"
+                 "global_load_lds_dword %1, off\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "v"(p), "s"(lds_off));
+}
+
+// Every 128-byte line of [p, p + BYTES), one per thread. BYTES is a multiple
+// of 64 (whole packed rows, K % 256 == 0), so the dword read at the start of
+// the last line lies inside the span.
+template <int BYTES>
+__device__ __forceinline__ void prefetch_span(const uint8_t* p, uint32_t lds_off)
+{
+    static_assert(BYTES % 64 == 0, "whole 64-byte chunks");
+    for (int i = threadIdx.x; i < cdiv(BYTES, 128); i += kT) prefetch_line(p + 128 * i, lds_off);
+}
 
 // RMSNorm (gains g[i] = gain[t + 512 i]) + activation quant of the N values
 // held as v[i] = x[t + 512 i] into the permuted int8 vector sh.q; returns s_a
@@ -405,8 +441,8 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
     // The weight rows, gains and stand-in input of a step are loaded when the
     // step starts, before its wait: the fetch overlaps the hand-over. A wave's
     // loads complete in issue order, so a poll also waits for every load issued
-    // before it: loading P3's or P4's rows a step earlier measured slower, while
-    // the o rows (6.4 KB per workgroup) ride with P1's and spare P2's wait.
+    // before it: loading P3's or P4's rows into registers a step earlier
+    // measured slower; their lines are prefetched into L2 instead (pf*).
     uint4 w1[S1::P], w2[S2::P], w3[S3::P], w4[S4::P];
     float g1[ND], g2[ND], g3[ND], g4[NF], zv[ND];
     auto fetch2 = [&](int l) {
@@ -421,9 +457,6 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
         // P2's gains and stand-in input (its norm + quant follows the wait for P1)
         load_strided<D>(a.gains + (size_t)l * (3 * D + F) + D, g2);
         load_strided<D>(a.z + (size_t)l * D, zv);
-        // the o rows too: a poll waits for every load issued before it, and
-        // P2's wait is the shortest, so its weights go out with P1's
-        fetch2(l);
     };
     auto fetch3 = [&](int l) {
         const uint8_t* W = a.weights + (size_t)l * blob + 4 * dd + (size_t)r3 * (D / 4);
@@ -436,6 +469,21 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
         const uint8_t* W = a.weights + (size_t)l * blob + 4 * dd + 2 * fd + (size_t)r2 * (F / 4);
         load_items<S4>(w4, [&](int r) { return W + (size_t)r * (F / 4); });
         load_strided<F>(a.gains + (size_t)l * (3 * D + F) + 3 * D, g4);
+    };
+    const uint32_t trash = (uint32_t)(uintptr_t)&sh.trash[0];
+    auto pf1q = [&](int l) {  // q, k, v rows of layer l
+        prefetch_span<S1::R * (D / 4)>(a.weights + (size_t)l * blob + (size_t)r1 * (D / 4), trash);
+    };
+    auto pf1o = [&](int l) {  // o rows of layer l
+        prefetch_span<S2::R * (D / 4)>(a.weights + (size_t)l * blob + 3 * dd + (size_t)r2 * (D / 4), trash);
+    };
+    auto pf3 = [&](int l) {  // gate and up rows of layer l
+        const uint8_t* W = a.weights + (size_t)l * blob + 4 * dd + (size_t)r3 * (D / 4);
+        prefetch_span<S3::R * (D / 4)>(W, trash);
+        prefetch_span<S3::R * (D / 4)>(W + fd, trash);
+    };
+    auto pf4 = [&](int l) {  // down rows of layer l
+        prefetch_span<S4::R * (F / 4)>(a.weights + (size_t)l * blob + 4 * dd + 2 * fd + (size_t)r2 * (F / 4), trash);
     };
     for (int l = 0; l < a.n_layers; ++l) {
         const uint32_t E = base + 4u * (uint32_t)l;
@@ -479,7 +527,9 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
             // every workgroup has finished P1: its norm + quant follows the wait
             if (t < S2::R) sh.acc[t] = 0;
             float fl[1];
+            fetch2(l);
             if (!poll_vec<kGrid, kFlagStride>(a.done, E + 1, fl, a.ctrl, t_start)) return;
+            pf3(l);
             if (l == 0 && w == 0 && t == 0)  // every workgroup has read the base by now
                 __hip_atomic_store(a.ctrl, base + 4u * (uint32_t)a.n_layers, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
@@ -502,6 +552,8 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
             fetch3(l);
             float v[ND];
             if (!poll_val<D>(xb_cur, v, a.ctrl, t_start)) return;
+            pf4(l);
+            if (l + 1 < a.n_layers) pf1o(l + 1);
             norm_quant<D>(v, g3, a.eps, sh, s_a, qsum);
             dots<S3>(w3, sh.q, sh.zero, sh.acc);
             __syncthreads();
@@ -520,6 +572,7 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
             fetch4(l);
             float v[NF];
             if (!poll_val<F>(hh_cur, v, a.ctrl, t_start)) return;
+            if (l + 1 < a.n_layers) pf1q(l + 1);
             norm_quant<F>(v, g4, a.eps, sh, s_a, qsum);
             dots<S4>(w4, sh.q, sh.zero, sh.acc);
             __syncthreads();
