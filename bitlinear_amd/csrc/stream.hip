@@ -177,7 +177,7 @@ __device__ bool poll_vec(const unsigned long long* buf, uint32_t e, float* v, ui
             failed = true;
             break;
         }
-        __builtin_amdgcn_s_sleep(10);
+        __builtin_amdgcn_s_sleep(3);  // about 190 cycles between rounds
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i) v[i] = (t + kT * i < N) ? __uint_as_float((uint32_t)w[i]) : 0.0f;
@@ -209,7 +209,7 @@ __device__ bool poll_val(const uint32_t* buf, float* v, uint32_t* ctrl, long lon
             failed = true;
             break;
         }
-        __builtin_amdgcn_s_sleep(10);
+        __builtin_amdgcn_s_sleep(3);  // about 190 cycles between rounds
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i) v[i] = (t + kT * i < N) ? __uint_as_float(w[i]) : 0.0f;
