@@ -2,6 +2,7 @@
 // then launches on the caller's stream. No allocation, no synchronisation, no
 // host reads of device memory.
 #include "internal.h"
+#include "prefetch.h"
 
 namespace {
 
@@ -143,8 +144,18 @@ int ffn_impl(const float* x, int64_t m, int64_t d, int64_t f, const float* g_ffn
     int32_t* acc_u = keep ? at<int32_t>(ws, L.off[BITNET_FFN_WS_ACC_UP]) : nullptr;
     int32_t* acc_d = keep ? at<int32_t>(ws, L.off[BITNET_FFN_WS_ACC_DOWN]) : nullptr;
     const int M = (int)m, D = (int)d, F = (int)f;
+    // Up to 32 tokens the products are short, latency-bound weight streams:
+    // each norm + quant launch also pulls the next product's weight lines
+    // into L2 (extra workgroups, no effect on results).
+    const bool pre = m <= kMaxSkinnyM;
+    const bool gemv = m <= kMaxGemvM;
+    const uint32_t wb = (uint32_t)((size_t)f * d / 4);
+    const uint32_t ch_gu = (uint32_t)(gemv ? bl::gemv_rows_per_block(D) : bl::skinny_rows_per_tile(F, true)) * (D / 4);
+    const uint32_t ch_dn = (uint32_t)(gemv ? bl::gemv_rows_per_block(F) : bl::skinny_rows_per_tile(D, false)) * (F / 4);
+    const bl::Prefetch pf_gu = {{w_gate, w_up}, {wb, wb}, ch_gu};
+    const bl::Prefetch pf_dn = {{w_down, nullptr}, {wb, 0u}, ch_dn};
 
-    int rc = bl::launch_quant_act(x, g_ffn, eps, M, D, q1, s1, qs1, s);
+    int rc = bl::launch_quant_act(x, g_ffn, eps, M, D, q1, s1, qs1, s, false, pre ? &pf_gu : nullptr);
     if (rc) return rc;
     if (m <= kMaxGemvM) {
         rc = bl::launch_gateup(w_gate, s_gate, w_up, s_up, scale_ptr, F, D, q1, s1, qs1, M, h, acc_g, acc_u, s);
@@ -163,7 +174,7 @@ int ffn_impl(const float* x, int64_t m, int64_t d, int64_t f, const float* g_ffn
         if (!rc) rc = bl::launch_relu2_mul(gate, up, (int64_t)m * f, h, s);
     }
     if (rc) return rc;
-    rc = bl::launch_quant_act(h, g_sub, eps, M, F, q2, s2, qs2, s);
+    rc = bl::launch_quant_act(h, g_sub, eps, M, F, q2, s2, qs2, s, false, pre ? &pf_dn : nullptr);
     if (rc) return rc;
     const float* sdp = scale_ptr ? scale_ptr + 2 : nullptr;
     if (m <= kMaxGemvM)
@@ -334,19 +345,29 @@ int bitnet_decode_stream(const uint8_t* weights, const float* scales, const floa
             const float* gl = gains + l * gstride;
             float* qkv_l = qkv ? qkv + (size_t)l * m * 3 * d : at<float>(workspace, L.qkv);
             const uint8_t* wg = wl + 4 * dd;
-            int rc = bl::launch_quant_act(x, gl, eps, M, D, qa, sa, qsa, s, true);
+            // each norm + quant also pulls the next product's weight lines into L2
+            const uint32_t rd = (uint32_t)(D / 4), rf = (uint32_t)(F / 4);
+            const bl::Prefetch pf_qkv = {{wl, nullptr}, {(uint32_t)(3 * dd), 0u},
+                                         (uint32_t)bl::skinny_rows_per_tile(3 * D, false) * rd};
+            const bl::Prefetch pf_o = {{wl + 3 * dd, nullptr}, {(uint32_t)dd, 0u},
+                                       (uint32_t)bl::skinny_rows_per_tile(D, false) * rd};
+            const bl::Prefetch pf_gu = {{wg, wg + fd}, {(uint32_t)fd, (uint32_t)fd},
+                                        (uint32_t)bl::skinny_rows_per_tile(F, true) * rd};
+            const bl::Prefetch pf_dn = {{wg + 2 * fd, nullptr}, {(uint32_t)fd, 0u},
+                                        (uint32_t)bl::skinny_rows_per_tile(D, false) * rf};
+            int rc = bl::launch_quant_act(x, gl, eps, M, D, qa, sa, qsa, s, true, &pf_qkv);
             if (!rc)
                 rc = bl::launch_skinny(skinny(wl, sl, 0.0f, D, 3 * D, D, qa, sa, qsa, M, nullptr, qkv_l, 3 * D), false,
                                        s);
-            if (!rc) rc = bl::launch_quant_act(z + (size_t)l * m * d, gl + d, eps, M, D, qo, so, qso, s, true);
+            if (!rc) rc = bl::launch_quant_act(z + (size_t)l * m * d, gl + d, eps, M, D, qo, so, qso, s, true, &pf_o);
             if (!rc)
                 rc = bl::launch_skinny(skinny(wl + 3 * dd, sl + 3, 0.0f, D, D, D, qo, so, qso, M, x, x, D), false, s);
-            if (!rc) rc = bl::launch_quant_act(x, gl + 2 * d, eps, M, D, q1, s1, qs1, s, true);
+            if (!rc) rc = bl::launch_quant_act(x, gl + 2 * d, eps, M, D, q1, s1, qs1, s, true, &pf_gu);
             if (!rc)
                 rc = bl::launch_skinny(skinny_gateup(wg, 0.0f, wg + fd, 0.0f, sl + 4, F, D, q1, s1, qs1, M, h, nullptr,
                                                      nullptr),
                                        false, s);
-            if (!rc) rc = bl::launch_quant_act(h, gl + 3 * d, eps, M, F, q2, s2, qs2, s, true);
+            if (!rc) rc = bl::launch_quant_act(h, gl + 3 * d, eps, M, F, q2, s2, qs2, s, true, &pf_dn);
             if (!rc)
                 rc = bl::launch_skinny(skinny(wg + 2 * fd, sl + 6, 0.0f, D, D, F, q2, s2, qs2, M, x, x, D), false, s);
             if (rc) return rc;
@@ -358,7 +379,12 @@ int bitnet_decode_stream(const uint8_t* weights, const float* scales, const floa
         const float* sl = scales + 7 * l;
         const float* gl = gains + l * gstride;
         float* qkv_l = qkv ? qkv + (size_t)l * m * 3 * d : at<float>(workspace, L.qkv);
-        int rc = bl::launch_quant_act(x, gl, eps, M, D, qa, sa, qsa, s);
+        // m <= 8 here: q/k/v and o are GEMV launches over D inputs
+        const uint32_t ch = (uint32_t)bl::gemv_rows_per_block(D) * (uint32_t)(D / 4);
+        const bl::Prefetch pf_qkv = {{wl, nullptr}, {(uint32_t)(3 * dd), 0u}, ch};
+        const bl::Prefetch pf_o = {{wl + 3 * dd, nullptr}, {(uint32_t)dd, 0u}, ch};
+        const bool pre = m <= kMaxGemvM;
+        int rc = bl::launch_quant_act(x, gl, eps, M, D, qa, sa, qsa, s, false, pre ? &pf_qkv : nullptr);
         if (rc) return rc;
         if (m <= kMaxGemvM) {
             const uint8_t* qkv_w[3] = {wl, wl + dd, wl + 2 * dd};
@@ -369,7 +395,7 @@ int bitnet_decode_stream(const uint8_t* weights, const float* scales, const floa
                                      3 * D, nullptr, nullptr, nullptr, s);
         }
         if (rc) return rc;
-        rc = bl::launch_quant_act(z + (size_t)l * m * d, gl + d, eps, M, D, qo, so, qso, s);
+        rc = bl::launch_quant_act(z + (size_t)l * m * d, gl + d, eps, M, D, qo, so, qso, s, false, pre ? &pf_o : nullptr);
         if (rc) return rc;
         if (m <= kMaxGemvM)
             rc = bl::launch_gemv(wl + 3 * dd, 0.0f, sl + 3, D, D, qo, so, qso, M, x, x, nullptr, s);

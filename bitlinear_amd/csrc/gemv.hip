@@ -296,6 +296,8 @@ inline int grid_for(int rows, int lanes)
 
 }  // namespace
 
+int gemv_rows_per_block(int k) { return 64 / pick_lanes(k); }
+
 int launch_gemv(const uint8_t* packed, float w_scale, const float* w_scale_ptr, int n, int k, const int8_t* q,
                 const float* act_scale, const int32_t* act_sum, int m, const float* residual, float* y,
                 int32_t* acc_out, hipStream_t s)

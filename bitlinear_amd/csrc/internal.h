@@ -12,11 +12,23 @@ namespace bl {
 // Launchers (defined in the .hip files). They assume validated arguments and
 // return BL_OK or BL_ERR_LAUNCH.
 
+struct Prefetch;
+
 // [RMSNorm +] activation quant, one workgroup per token. With perm16, q is
 // written with each 16 values 4x4 byte-transposed (byte 4 j + g of a group
-// holds value 4 g + j), the operand order of the skinny MFMA kernels.
+// holds value 4 g + j), the operand order of the skinny MFMA kernels. With pf
+// (and fewer rows than the one-wave-per-row kernel takes), extra workgroups of
+// the same launch pull the weight lines of pf into L2 for the kernel that
+// follows; they change no result.
 int launch_quant_act(const float* x, const float* gain, float eps, int m, int k, int8_t* q,
-                     float* act_scale, int32_t* act_sum, hipStream_t s, bool perm16 = false);
+                     float* act_scale, int32_t* act_sum, hipStream_t s, bool perm16 = false,
+                     const Prefetch* pf = nullptr);
+
+// Weight rows read by workgroup b of a GEMV-family launch over k inputs (rows
+// [b R, (b + 1) R) of the stacked matrices), and by workgroup b of a skinny
+// launch over n outputs (rows [b R, (b + 1) R) of each of its matrices).
+int gemv_rows_per_block(int k);
+int skinny_rows_per_tile(int n, bool pair);
 
 // Decode GEMV, m in [1, 8]. The weight scale is read from w_scale_ptr when it
 // is non-null, else w_scale is used.

@@ -18,7 +18,10 @@
 // (quant_act_wave_kernel); rows up to 16384 values are held in the registers
 // of a 512-thread workgroup (one load per value); for longer rows passes 2 and
 // 3 each re-read the row (an L2 hit after pass 1) and recompute y identically.
+#include <algorithm>
+
 #include "internal.h"
+#include "prefetch.h"
 #include "wave.h"
 
 namespace bl {
@@ -127,13 +130,19 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(const float* __rest
 // (and g[k]) for k = t, t + 512, ... < NPT * 512 once, up front, so the row
 // costs one trip to memory instead of three. The sum of squares runs over the
 // same values in the same order as above, and y is recomputed identically.
+// Workgroups past the last row (if any) only prefetch the weight lines of pf.
 template <bool kNorm, bool kPerm, int NPT>
 __global__ __launch_bounds__(kThreads) void quant_act_reg_kernel(const float* __restrict__ x,
                                                                  const float* __restrict__ gain, float eps, int k,
                                                                  int8_t* __restrict__ q, float* __restrict__ act_scale,
-                                                                 int32_t* __restrict__ act_sum)
+                                                                 int32_t* __restrict__ act_sum, int rows, Prefetch pf)
 {
     const int row = blockIdx.x;
+    if (row >= rows) {  // the whole workgroup: no barrier is skipped
+        __shared__ uint32_t trash[64];
+        prefetch_chunks(pf, row, row - rows, (int)gridDim.x - rows, kThreads, (uint32_t)(uintptr_t)&trash[0]);
+        return;
+    }
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = t >> 6;
@@ -306,7 +315,7 @@ __global__ __launch_bounds__(256) void quant_act_wave_kernel(const float* __rest
 
 template <bool kNorm, bool kPerm>
 void launch_kind(const float* x, const float* gain, float eps, int m, int k, int8_t* q, float* act_scale,
-                 int32_t* act_sum, hipStream_t s)
+                 int32_t* act_sum, hipStream_t s, const Prefetch& pf, int pf_blocks)
 {
     // Many rows: one wave per row where a lane can hold its share of the row (x
     // and gains in registers) -- 4.15 vs 3.63 TB/s at 2048 x 2560. Few rows run
@@ -345,7 +354,9 @@ void launch_kind(const float* x, const float* gain, float eps, int m, int k, int
     }
 #undef BL_QWAVE
     const int per = (k + kThreads - 1) / kThreads;  // values per thread
-#define BL_QREG(N) quant_act_reg_kernel<kNorm, kPerm, N><<<m, kThreads, 0, s>>>(x, gain, eps, k, q, act_scale, act_sum)
+#define BL_QREG(N)                                                                         \
+    quant_act_reg_kernel<kNorm, kPerm, N><<<m + pf_blocks, kThreads, 0, s>>>(x, gain, eps, k, q, act_scale, \
+                                                                              act_sum, m, pf)
     if (per <= 4)
         BL_QREG(4);
     else if (per <= 8)
@@ -364,17 +375,32 @@ void launch_kind(const float* x, const float* gain, float eps, int m, int k, int
 }  // namespace
 
 int launch_quant_act(const float* x, const float* gain, float eps, int m, int k, int8_t* q, float* act_scale,
-                     int32_t* act_sum, hipStream_t s, bool perm16)
+                     int32_t* act_sum, hipStream_t s, bool perm16, const Prefetch* pf)
 {
+    // one extra workgroup per chunk of the next launch (a multiple of 8, at
+    // most 256); spans that are not 4-byte aligned are not prefetched
+    Prefetch p = {{nullptr, nullptr}, {0u, 0u}, 0u};
+    int pf_blocks = 0;
+    if (pf && pf->chunk && (pf->chunk & 3) == 0) {
+        for (int i = 0; i < 2; ++i)
+            if (pf->p[i] && pf->bytes[i] && (reinterpret_cast<uintptr_t>(pf->p[i]) & 3) == 0 && (pf->bytes[i] & 3) == 0) {
+                p.p[i] = pf->p[i];
+                p.bytes[i] = pf->bytes[i];
+            }
+        p.chunk = pf->chunk;
+        const uint64_t top = std::max(p.bytes[0], p.bytes[1]);
+        const uint64_t chunks = (top + p.chunk - 1) / p.chunk;
+        pf_blocks = (int)std::min<uint64_t>(256, (chunks + 7) / 8 * 8);
+    }
     if (perm16) {
         if (gain)
-            launch_kind<true, true>(x, gain, eps, m, k, q, act_scale, act_sum, s);
+            launch_kind<true, true>(x, gain, eps, m, k, q, act_scale, act_sum, s, p, pf_blocks);
         else
-            launch_kind<false, true>(x, gain, eps, m, k, q, act_scale, act_sum, s);
+            launch_kind<false, true>(x, gain, eps, m, k, q, act_scale, act_sum, s, p, pf_blocks);
     } else if (gain) {
-        launch_kind<true, false>(x, gain, eps, m, k, q, act_scale, act_sum, s);
+        launch_kind<true, false>(x, gain, eps, m, k, q, act_scale, act_sum, s, p, pf_blocks);
     } else {
-        launch_kind<false, false>(x, gain, eps, m, k, q, act_scale, act_sum, s);
+        launch_kind<false, false>(x, gain, eps, m, k, q, act_scale, act_sum, s, p, pf_blocks);
     }
     return hipGetLastError() == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
 }

@@ -320,6 +320,8 @@ int skinny_tiles(int n, bool pair)
     return two_tiles(n) ? (n + 63) / 64 : (n + 31) / 32;
 }
 
+int skinny_rows_per_tile(int n, bool pair) { return pair || !two_tiles(n) ? 32 : 64; }
+
 int launch_skinny(const SkinnyArgs& a, bool natural_q, hipStream_t s)
 {
     if (a.w1) return natural_q ? launch_nb<2, true, true>(a, s) : launch_nb<2, true, false>(a, s);

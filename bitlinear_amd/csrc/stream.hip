@@ -69,6 +69,7 @@
 // 100 MHz) and by a shared status word; a workgroup that gives up sets the
 // status, every other one sees it and leaves, so the grid always drains.
 #include "internal.h"
+#include "prefetch.h"
 #include "wave.h"
 
 namespace bl {
@@ -254,20 +255,6 @@ struct Shared {
     int acc[128];  // per-row accumulators of a step (gate rows, then up rows)
     uint32_t trash[64];  // written by the L2 prefetch loads, never read
 };
-
-// One dword of the line at p straight into LDS at lds_off + 4 lane: the load
-// only brings the line into L2 (and this CU's L1). m0 holds the LDS address
-// for the instruction and is restored afterwards.
-__device__ __forceinline__ void prefetch_line(const void* p, uint32_t lds_off)
-{
-    uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\t"
-                 "s_mov_b32 m0, %2\n\t"
-                 "global_load_lds_dword %1, off\n\t"
-                 "s_mov_b32 m0, %0"
-                 : "=&s"(saved)
-                 : "v"(p), "s"(lds_off));
-}
 
 // Every 128-byte line of [p, p + BYTES), one per thread. BYTES is a multiple
 // of 64 (whole packed rows, K % 256 == 0), so the dword read at the start of
