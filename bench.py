@@ -16,7 +16,7 @@ Also reported in the same JSON line:
   batched  : BitNet-1.3B stream at 32 tokens (24 layers x 7 BitLinears), then
              the final norm + quant and the ternary LM head 2048 -> 50000 with
              the fused per-row argmax.
-  gemv     : one 2560 -> 2560 BitLinear (quant + GEMV) at 1 token.
+  gemv     : one 2560 -> 2560 BitLinear (quant + GEMV, bitlinear_forward) at 1 token.
   ffn      : the BitNet-3B FFN sub-layer at 1 token.
   roofline : the dominant kernel against HBM or MFMA peak.
   cpu_baseline : the CPU oracle on a bounded sample of the same workload.
@@ -306,26 +306,40 @@ def extra_measurements(bl, torch, T, dev0):
     qs1 = torch.empty(1, dtype=torch.int32, device=dev0)
     y1 = torch.empty((1, d), dtype=torch.float32, device=dev0)
     for i in range(8):
-        bl.bitlinear_quant_act(x1, None, 1e-5, q1, s1, qs1)
-        bl.bitlinear_gemv(pw[i], sw, d, d, q1, s1, qs1, 1, None, y1)
+        bl.bitlinear_forward(x1, None, 1e-5, pw[i], sw, d, q1, s1, qs1, y1)
+    # one call of bitlinear_forward (one launch: every workgroup quantizes x itself)
     with Timer() as tg:
         for i in range(copies):
-            bl.bitlinear_quant_act(x1, None, 1e-5, q1, s1, qs1)
-            bl.bitlinear_gemv(pw[i], sw, d, d, q1, s1, qs1, 1, None, y1)
+            bl.bitlinear_forward(x1, None, 1e-5, pw[i], sw, d, q1, s1, qs1, y1)
     ms = tg.ms / copies
 
-    def gemv_calls():
+    def fwd_calls():
+        for i in range(copies):
+            bl.bitlinear_forward(x1, None, 1e-5, pw[i], sw, d, q1, s1, qs1, y1)
+    gms, gsame = graph_ms(torch, fwd_calls, [q1, s1, qs1, y1])
+    gms /= copies
+    # for context: the same as two calls, bitlinear_quant_act then bitlinear_gemv
+    with Timer() as t2:
         for i in range(copies):
             bl.bitlinear_quant_act(x1, None, 1e-5, q1, s1, qs1)
             bl.bitlinear_gemv(pw[i], sw, d, d, q1, s1, qs1, 1, None, y1)
-    gms, gsame = graph_ms(torch, gemv_calls, [q1, s1, qs1, y1])
-    gms /= copies
-    out["gemv"] = {"workload": "quant 1x2560 + GEMV 2560->2560 (1,638,400 packed B), weights rotated over 320 copies",
+    ms2 = t2.ms / copies
+
+    def two_calls():
+        for i in range(copies):
+            bl.bitlinear_quant_act(x1, None, 1e-5, q1, s1, qs1)
+            bl.bitlinear_gemv(pw[i], sw, d, d, q1, s1, qs1, 1, None, y1)
+    gms2, _ = graph_ms(torch, two_calls, [q1, s1, qs1, y1])
+    gms2 /= copies
+    out["gemv"] = {"workload": "BitLinear 2560 -> 2560 at 1 token (quant + GEMV, 1,638,400 packed B) through "
+                               "bitlinear_forward, weights rotated over 320 copies",
                    "us_per_call": round(ms * 1e3, 3), "weight_gbs": round(d * d / 4 / (ms * 1e-3) / 1e9, 1),
                    "frac_hbm": round(d * d / 4 / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                    "us_per_call_graph": round(gms * 1e3, 3),
                    "weight_gbs_graph": round(d * d / 4 / (gms * 1e-3) / 1e9, 1),
-                   "graph_matches_eager": gsame}
+                   "graph_matches_eager": gsame,
+                   "us_per_call_quant_then_gemv": round(ms2 * 1e3, 3),
+                   "us_per_call_quant_then_gemv_graph": round(gms2 * 1e3, 3)}
     del pw
     # ---- BitNet-3B FFN at one token, weights rotated over 27 copies (531 MB) ----
     f = 10240
@@ -362,7 +376,8 @@ def extra_measurements(bl, torch, T, dev0):
                   "us_per_call_graph": round(gms * 1e3, 3), "weight_gbs_graph": round(fb / (gms * 1e-3) / 1e9, 1),
                   "frac_hbm_graph": round(fb / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                   "graph_matches_eager": gsame}
-    log(f"gemv {out['gemv']['us_per_call']} us ({out['gemv']['us_per_call_graph']} us from a graph), "
+    log(f"gemv {out['gemv']['us_per_call']} us ({out['gemv']['us_per_call_graph']} us from a graph; two calls "
+        f"{out['gemv']['us_per_call_quant_then_gemv']} / {out['gemv']['us_per_call_quant_then_gemv_graph']} us), "
         f"ffn {out['ffn']['us_per_call']} us ({out['ffn']['us_per_call_graph']} us from a graph)")
     del fw
     # ---- prefill GEMM 2048 x 2560 -> 10240 ----

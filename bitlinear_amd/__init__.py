@@ -32,7 +32,7 @@ FFN_WS_SEGMENTS = ("q1", "s1", "qs1", "h", "q2", "s2", "qs2", "acc_gate", "acc_u
 # Every symbol the header declares (checked by the CPU tests).
 EXPORTS = (
     "bitlinear_abi_version", "bitlinear_strerror", "bitlinear_pack", "bitlinear_weight_quant",
-    "bitlinear_quant_act", "bitlinear_gemv", "bitlinear_gemm_workspace_bytes", "bitlinear_gemm",
+    "bitlinear_quant_act", "bitlinear_gemv", "bitlinear_forward", "bitlinear_gemm_workspace_bytes", "bitlinear_gemm",
     "bitnet_ffn_workspace_bytes", "bitnet_ffn_workspace_offset", "bitnet_ffn", "bitnet_layer_bytes",
     "bitnet_stream_workspace_bytes", "bitnet_decode_stream",
 )
@@ -73,6 +73,7 @@ _SIGS = {
     "bitlinear_weight_quant": ([_P, _I64, _I64, _P, _P], _I),
     "bitlinear_quant_act": ([_P, _P, _F, _I64, _I64, _P, _P, _P, _P], _I),
     "bitlinear_gemv": ([_P, _F, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P, _P], _I),
+    "bitlinear_forward": ([_P, _P, _F, _P, _F, _I64, _I64, _I64, _P, _P, _P, _P, _P], _I),
     "bitlinear_gemm_workspace_bytes": ([_I64, _I64, _I64, _I], _SZ),
     "bitlinear_gemm": ([_P, _F, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "bitnet_ffn_workspace_bytes": ([_I64, _I64, _I64], _SZ),
@@ -175,6 +176,17 @@ def bitlinear_gemv(packed, w_scale, n, k, q, act_scale, act_sum, m, residual, y,
                                _dev(act_scale, torch.float32, "act_scale"), _dev(act_sum, torch.int32, "act_sum"), m,
                                _dev(residual, torch.float32, "residual", True), _dev(y, torch.float32, "y"),
                                _dev(acc_out, torch.int32, "acc_out", True), _stream(stream)), "bitlinear_gemv")
+
+
+def bitlinear_forward(x, gain, eps, packed, w_scale, n, q, act_scale, act_sum, y, stream=None):
+    """[RMSNorm +] quant + GEMV of x[m][k] (fp32, GPU) into y[m][n]; q, act_scale, act_sum receive the quant."""
+    import torch
+    m, k = x.shape
+    _check(_lib.bitlinear_forward(_dev(x, torch.float32, "x"), _dev(gain, torch.float32, "gain", True), eps,
+                                  _dev(packed, torch.uint8, "packed"), float(w_scale), n, k, m,
+                                  _dev(q, torch.int8, "q"), _dev(act_scale, torch.float32, "act_scale"),
+                                  _dev(act_sum, torch.int32, "act_sum"), _dev(y, torch.float32, "y"),
+                                  _stream(stream)), "bitlinear_forward")
 
 
 def bitlinear_gemm_workspace_bytes(m, n, k, with_argmax):

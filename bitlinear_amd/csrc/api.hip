@@ -1,6 +1,8 @@
 // api.hip -- the device entry points of the C ABI: argument checks on the host,
 // then launches on the caller's stream. No allocation, no synchronisation, no
 // host reads of device memory.
+#include <algorithm>
+
 #include "internal.h"
 #include "prefetch.h"
 
@@ -212,6 +214,27 @@ int bitlinear_gemv(const uint8_t* packed, float w_scale, int64_t n, int64_t k, c
     if (!(w_scale > 0.0f) || !(w_scale < INFINITY)) return BL_ERR_VALUE;
     return bl::launch_gemv(packed, w_scale, nullptr, (int)n, (int)k, q, act_scale, act_sum, (int)m, residual, y,
                            acc_out, as_stream(stream));
+}
+
+int bitlinear_forward(const float* x, const float* gain, float eps, const uint8_t* packed, float w_scale, int64_t n,
+                      int64_t k, int64_t m, int8_t* q, float* act_scale, int32_t* act_sum, float* y, void* stream)
+{
+    if (!x || !packed || !q || !act_scale || !act_sum || !y) return BL_ERR_NULL;
+    if (m < 1 || m > kMaxGemvM || !dim_ok(n) || !k_ok(k) || k > kMaxGemvK) return BL_ERR_SHAPE;
+    if (!aligned(x, 16) || (gain && !aligned(gain, 16)) || !aligned(packed, 16) || !aligned(q, 16) ||
+        !aligned(act_scale, 4) || !aligned(act_sum, 4) || !aligned(y, 4))
+        return BL_ERR_ALIGN;
+    if (!(w_scale > 0.0f) || !(w_scale < INFINITY)) return BL_ERR_VALUE;
+    const hipStream_t s = as_stream(stream);
+    if (bl::fwd_fits((int)m, (int)k))
+        return bl::launch_fwd(x, gain, eps, packed, w_scale, (int)n, (int)k, y, q, act_scale, act_sum, s);
+    const uint64_t wbytes = std::min<uint64_t>((uint64_t)n * (uint64_t)k / 4, 0xfffffffcull);
+    const bl::Prefetch pf = {{packed, nullptr}, {(uint32_t)wbytes, 0u},
+                             (uint32_t)bl::gemv_rows_per_block((int)k) * (uint32_t)(k / 4)};
+    const int rc = bl::launch_quant_act(x, gain, eps, (int)m, (int)k, q, act_scale, act_sum, s, false, &pf);
+    if (rc) return rc;
+    return bl::launch_gemv(packed, w_scale, nullptr, (int)n, (int)k, q, act_scale, act_sum, (int)m, nullptr, y,
+                           nullptr, s);
 }
 
 size_t bitlinear_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int with_argmax)

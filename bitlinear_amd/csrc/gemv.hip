@@ -17,12 +17,14 @@
 // subtracted once per row. The partial sums are reduced across the L lanes with
 // xor shuffles, and the group's first lane applies the single fp32 rescale.
 #include "internal.h"
+#include "wave_quant.h"
 
 namespace bl {
 namespace {
 
 constexpr uint32_t kCodeMask = 0x03030303u;
 constexpr int kMaxChunksPerLane = 8;
+constexpr int kFwdMaxK = 4096;  // longest row of the one-launch quant + GEMV
 
 // 4x4 byte transpose of 16 activations a[0..15] (given as 4 dwords, natural
 // order) into the order the shifted code masks produce: out[j] holds
@@ -111,6 +113,18 @@ __device__ __forceinline__ void dot_row(const uint4 w[kMaxChunksPerLane], int la
     }
 }
 
+// dot_row for one token with the activations in registers.
+template <int L>
+__device__ __forceinline__ int dot_row_one(const uint4 w[kMaxChunksPerLane], int lane_in_group, int chunks,
+                                           const uint32_t (*qreg)[16])
+{
+    int acc = 0;
+#pragma unroll
+    for (int c = 0; c < kMaxChunksPerLane; ++c)
+        if (lane_in_group + c * L < chunks) acc = dot_chunk(w[c], qreg[c], acc);
+    return acc;
+}
+
 template <int L, int M>
 __device__ __forceinline__ void load_qreg(const int8_t* q, int lane_in_group, int chunks, uint32_t qreg[][16])
 {
@@ -159,6 +173,66 @@ __global__ __launch_bounds__(64) void gemv_kernel(const uint8_t* __restrict__ pa
                 if (acc_out) acc_out[o] = total;
             }
         }
+    }
+}
+
+// ---- [RMSNorm +] quant + GEMV of one token in one launch -------------------
+// Every workgroup (one wave) quantizes the whole input row itself with the
+// one-wave quant (wave_quant_row: the same operations in the same order as
+// the quant kernel, so every workgroup holds the same q, s_a and sum(q)) into
+// LDS, and then runs its rows as gemv_kernel does. The input row is read by
+// every workgroup, from L2 after the first; the workgroup's first weight rows
+// are loaded before the row, so their fetch overlaps the quant. Workgroup 0
+// also writes q, s_a and sum(q) where asked.
+template <int V, bool kNorm>
+__global__ __launch_bounds__(64) void fwd_kernel(const float* __restrict__ x, const float* __restrict__ gain, float eps,
+                                                 const uint8_t* __restrict__ packed, float w_scale, int n, int k,
+                                                 float* __restrict__ y, int8_t* __restrict__ q_out,
+                                                 float* __restrict__ scale_out, int32_t* __restrict__ sum_out)
+{
+    constexpr int L = 8, R = 64 / L;
+    static_assert(64 * 4 * V <= kFwdMaxK, "row held in LDS");
+    __shared__ __attribute__((aligned(16))) int8_t qs[kFwdMaxK];
+    const int lane = threadIdx.x;
+    const int g = lane / L, j = lane % L;
+    const int chunks = k / 64;
+    const size_t row_bytes = (size_t)k / 4;
+
+    uint4 w[kMaxChunksPerLane];
+    int base = blockIdx.x * R;
+    load_row<L>(packed + (size_t)(base + g) * row_bytes, base + g < n, j, chunks, w);
+    float4 xv[V], gv[V];
+    wave_quant_load<kNorm, V>(x, gain, k, lane, xv, gv);
+    float s_a;
+    int qsum;
+    wave_quant_compute<kNorm, false, V>(xv, gv, eps, k, lane, qs, s_a, qsum);
+    __syncthreads();  // q complete in LDS
+
+    uint32_t qreg[kMaxChunksPerLane][16];
+#pragma unroll
+    for (int c = 0; c < kMaxChunksPerLane; ++c) {
+        const int ch = j + c * L;
+        if (ch < chunks) load_q_chunk(qs, ch, qreg[c]);
+    }
+    if (blockIdx.x == 0) {
+        if (q_out)
+            for (int i = lane; i < k / 16; i += 64)
+                reinterpret_cast<uint4*>(q_out)[i] = reinterpret_cast<const uint4*>(qs)[i];
+        if (lane == 0) {
+            if (scale_out) *scale_out = s_a;
+            if (sum_out) *sum_out = qsum;
+        }
+    }
+    const float inv = 1.0f / (s_a * w_scale);
+    for (;;) {
+        const int row = base + g;
+        int acc = 0;
+        const int acc0 = dot_row_one<L>(w, j, chunks, qreg);
+        acc = group_sum<L>(acc0);
+        if (row < n && j == 0) y[row] = (float)(acc - qsum) * inv;
+        base += gridDim.x * R;
+        if (base >= n) break;
+        load_row<L>(packed + (size_t)(base + g) * row_bytes, base + g < n, j, chunks, w);
     }
 }
 
@@ -298,6 +372,8 @@ inline int grid_for(int rows, int lanes)
 
 int gemv_rows_per_block(int k) { return 64 / pick_lanes(k); }
 
+bool fwd_fits(int m, int k) { return m == 1 && k >= 64 && k <= kFwdMaxK && k % 64 == 0 && pick_lanes(k) == 8; }
+
 int launch_gemv(const uint8_t* packed, float w_scale, const float* w_scale_ptr, int n, int k, const int8_t* q,
                 const float* act_scale, const int32_t* act_sum, int m, const float* residual, float* y,
                 int32_t* acc_out, hipStream_t s)
@@ -309,6 +385,31 @@ int launch_gemv(const uint8_t* packed, float w_scale, const float* w_scale_ptr, 
                                             y, acc_out)
     BL_DISPATCH_L(BL_LAUNCH)
 #undef BL_LAUNCH
+    return hipGetLastError() == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
+}
+
+int launch_fwd(const float* x, const float* gain, float eps, const uint8_t* packed, float w_scale, int n, int k,
+               float* y, int8_t* q_out, float* scale_out, int32_t* sum_out, hipStream_t s)
+{
+    if (!fwd_fits(1, k)) return BL_ERR_SHAPE;
+    const int grid = grid_for(n, 8);
+    const int v = (k / 4 + 63) / 64;  // float4 chunks per lane
+#define BL_FWD(V)                                                                                          \
+    (gain ? fwd_kernel<V, true><<<grid, 64, 0, s>>>(x, gain, eps, packed, w_scale, n, k, y, q_out, scale_out, \
+                                                     sum_out)                                              \
+          : fwd_kernel<V, false><<<grid, 64, 0, s>>>(x, gain, eps, packed, w_scale, n, k, y, q_out, scale_out, \
+                                                      sum_out))
+    if (v <= 2)
+        BL_FWD(2);
+    else if (v <= 4)
+        BL_FWD(4);
+    else if (v <= 8)
+        BL_FWD(8);
+    else if (v <= 10)
+        BL_FWD(10);
+    else
+        BL_FWD(16);
+#undef BL_FWD
     return hipGetLastError() == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
 }
 

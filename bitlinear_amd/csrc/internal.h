@@ -30,6 +30,12 @@ int launch_quant_act(const float* x, const float* gain, float eps, int m, int k,
 int gemv_rows_per_block(int k);
 int skinny_rows_per_tile(int n, bool pair);
 
+// [RMSNorm +] quant + GEMV of one token in one launch (fwd_fits(m, k): m == 1,
+// 64 <= k <= 4096, k % 64 == 0). q_out, scale_out, sum_out may be null.
+bool fwd_fits(int m, int k);
+int launch_fwd(const float* x, const float* gain, float eps, const uint8_t* packed, float w_scale, int n, int k,
+               float* y, int8_t* q_out, float* scale_out, int32_t* sum_out, hipStream_t s);
+
 // Decode GEMV, m in [1, 8]. The weight scale is read from w_scale_ptr when it
 // is non-null, else w_scale is used.
 int launch_gemv(const uint8_t* packed, float w_scale, const float* w_scale_ptr, int n, int k, const int8_t* q,

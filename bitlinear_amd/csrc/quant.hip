@@ -23,6 +23,7 @@
 #include "internal.h"
 #include "prefetch.h"
 #include "wave.h"
+#include "wave_quant.h"
 
 namespace bl {
 namespace {
@@ -32,11 +33,6 @@ constexpr int kWaveRowsMin = 256;   // rows from which the one-wave-per-row kern
 constexpr int kMaxWaveChunks = 32;  // float4 chunks per lane it holds at most
 constexpr int kWaves = kThreads / 64;
 
-__device__ __forceinline__ int quant_one(float y, float scale)
-{
-    const float r = rintf(y * scale);
-    return (int)fminf(fmaxf(r, -128.0f), 127.0f);
-}
 
 template <bool kNorm>
 __device__ __forceinline__ float4 normed(const float* xr, const float* gain, float r, int i)
@@ -212,14 +208,7 @@ __global__ __launch_bounds__(kThreads) void quant_act_reg_kernel(const float* __
     }
 }
 
-// One wave per row, for rows of up to 64 * 4 * V values: lane t loads the
-// float4 chunks t, t + 64, ... (coalesced), so no LDS and no barrier is needed.
-// The fixed order of the sum of squares still holds: chunk u of lane t holds
-// x[4 t + c + 256 u] (c = 0..3), i.e. members of partials 4 t + c (u even) and
-// 256 + 4 t + c (u odd), accumulated in ascending u -- ascending k within each
-// partial. The butterfly over the 512 partials then runs with offsets 1 and 2
-// inside the lane, 4 .. 128 across lanes (xor 1 .. 32) and 256 inside the lane
-// again, in that (ascending) order.
+// One wave per row, for rows of up to 64 * 4 * V values (wave_quant_row).
 template <bool kNorm, bool kPerm, int V>
 __global__ __launch_bounds__(256) void quant_act_wave_kernel(const float* __restrict__ x,
                                                              const float* __restrict__ gain, float eps, int k, int m,
@@ -229,84 +218,9 @@ __global__ __launch_bounds__(256) void quant_act_wave_kernel(const float* __rest
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= m) return;  // no barriers in this kernel
-    const int k4 = k >> 2;  // float4 chunks per row
-    const float4* xr = reinterpret_cast<const float4*>(x + (size_t)row * k);
-    const float4* gr = reinterpret_cast<const float4*>(gain);
-    float4 xv[V], gv[V];
-#pragma unroll
-    for (int u = 0; u < V; ++u) {
-        const int i = lane + 64 * u;
-        xv[u] = i < k4 ? xr[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        if (kNorm) gv[u] = i < k4 ? gr[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    }
-
-    float r = 1.0f;
-    if (kNorm) {
-        double s[2][4] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};  // [u odd][c]
-#pragma unroll
-        for (int u = 0; u < V; ++u) {
-            const float4 v = xv[u];
-            const double a = v.x, b = v.y, c = v.z, d = v.w;
-            s[u & 1][0] += a * a;  // exact squares; zero beyond k
-            s[u & 1][1] += b * b;
-            s[u & 1][2] += c * c;
-            s[u & 1][3] += d * d;
-        }
-        double h[2];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const double p01 = s[hh][0] + s[hh][1];  // offset 1
-            const double p23 = s[hh][2] + s[hh][3];
-            h[hh] = wave_butterfly_sum(p01 + p23);  // offset 2, then 4 .. 128
-        }
-        const double ss = h[0] + h[1];  // offset 256
-        r = (float)(1.0 / sqrt(ss / (double)k + (double)eps));
-    }
-
-    auto normed = [&](int u) __attribute__((always_inline)) {
-        float4 y = xv[u];
-        if (kNorm) {
-            y.x = (y.x * r) * gv[u].x;
-            y.y = (y.y * r) * gv[u].y;
-            y.z = (y.z * r) * gv[u].z;
-            y.w = (y.w * r) * gv[u].w;
-        }
-        return y;
-    };
-    float amax = 0.0f;
-#pragma unroll
-    for (int u = 0; u < V; ++u) {
-        const float4 y = normed(u);
-        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(y.x), fabsf(y.y)), fmaxf(fabsf(y.z), fabsf(y.w))));
-    }
-    amax = wave_max(amax);
-    const float scale = 127.0f / fmaxf(amax, 1e-5f);
-
-    int sum = 0;
-    int8_t* qr = q + (size_t)row * k;
-#pragma unroll
-    for (int u = 0; u < V; ++u) {
-        const int i = lane + 64 * u;
-        if (i < k4) {
-            const float4 y = normed(u);
-            const int q0 = quant_one(y.x, scale), q1 = quant_one(y.y, scale);
-            const int q2 = quant_one(y.z, scale), q3 = quant_one(y.w, scale);
-            sum += q0 + q1 + q2 + q3;
-            if (kPerm) {
-                // within each 16 values, byte 4 j + g holds value 4 g + j
-                int8_t* b = qr + ((4 * i) & ~15) + (i & 3);
-                b[0] = (int8_t)q0;
-                b[4] = (int8_t)q1;
-                b[8] = (int8_t)q2;
-                b[12] = (int8_t)q3;
-            } else {
-                const uint32_t packed = (uint32_t)(q0 & 0xff) | ((uint32_t)(q1 & 0xff) << 8) |
-                                        ((uint32_t)(q2 & 0xff) << 16) | ((uint32_t)(q3 & 0xff) << 24);
-                *reinterpret_cast<uint32_t*>(qr + 4 * i) = packed;
-            }
-        }
-    }
-    sum = wave_sum(sum);
+    float scale;
+    int sum;
+    wave_quant_row<kNorm, kPerm, V>(x + (size_t)row * k, gain, eps, k, lane, q + (size_t)row * k, scale, sum);
     if (lane == 0) {
         act_scale[row] = scale;
         if (act_sum) act_sum[row] = sum;

@@ -120,6 +120,26 @@ int bitlinear_gemv(const uint8_t *packed, float w_scale, int64_t n, int64_t k,
                    const int8_t *q, const float *act_scale, const int32_t *act_sum, int64_t m,
                    const float *residual, float *y, int32_t *acc_out, void *stream);
 
+/* Decode BitLinear in one call, m in [1, 8]: y[m][n] = dequant(P . quant([RMSNorm](x))),
+ * the composition of bitlinear_quant_act and bitlinear_gemv (no residual), with the same
+ * results bit for bit. A BitLinear applied to a token: the layer of the pages'
+ * "BitLinear" (candle PR 2664 "Add Support for BitNet Architecture Inference": norm,
+ * activation_quant, ternary matmul, one rescale; [BN] "Transformer Block" forward pass).
+ *   x, gain, eps : as bitlinear_quant_act (x [m][k], gain [k] or NULL).
+ *   packed, w_scale, n, k : as bitlinear_gemv.
+ *   q, act_scale, act_sum : device int8 [m][k], fp32 [m], int32 [m], caller-allocated; they
+ *               receive the quantized activations exactly as bitlinear_quant_act writes them.
+ *   y         : device fp32 [m][n].
+ * For m == 1 and k <= 4096 this is one launch: every workgroup quantizes x itself (the
+ * same operations in the same order as the quant kernel) and then runs its weight rows,
+ * so the quant adds no launch and no round trip through memory. Otherwise the quant
+ * launch also pulls P into L2 for the GEMV launch that follows it.
+ * Errors: NULL, SHAPE (m outside [1, 8], n <= 0, k % 64 != 0, k > 32768), ALIGN (x, gain,
+ * packed, q 16-byte; act_scale, act_sum, y 4-byte), VALUE (w_scale not > 0), LAUNCH. */
+int bitlinear_forward(const float *x, const float *gain, float eps, const uint8_t *packed, float w_scale,
+                      int64_t n, int64_t k, int64_t m, int8_t *q, float *act_scale, int32_t *act_sum,
+                      float *y, void *stream);
+
 /* Workspace bytes bitlinear_gemm needs (0 unless a per-row argmax is asked for):
  * 8 bytes per token and 32-column tile for m <= 32, 8 bytes per token above. */
 size_t bitlinear_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int with_argmax);

@@ -137,6 +137,35 @@ def test_gemv_checks():
     assert call(s=float("nan")) == bl.BL_ERR_VALUE
 
 
+def test_forward_checks():
+    f = bl._lib.bitlinear_forward
+    ok = dict(x=A, g=None, p=A, s=40.0, n=16, k=64, m=1, q=A, sa=A, qs=A, y=A)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return f(a["x"], a["g"], 1e-5, a["p"], a["s"], a["n"], a["k"], a["m"], a["q"], a["sa"], a["qs"], a["y"], S)
+
+    assert call(x=None) == bl.BL_ERR_NULL
+    assert call(p=None) == bl.BL_ERR_NULL
+    assert call(q=None) == bl.BL_ERR_NULL
+    assert call(sa=None) == bl.BL_ERR_NULL
+    assert call(qs=None) == bl.BL_ERR_NULL
+    assert call(y=None) == bl.BL_ERR_NULL
+    assert call(m=0) == bl.BL_ERR_SHAPE
+    assert call(m=9) == bl.BL_ERR_SHAPE
+    assert call(k=96) == bl.BL_ERR_SHAPE
+    assert call(k=65536) == bl.BL_ERR_SHAPE
+    assert call(n=0) == bl.BL_ERR_SHAPE
+    assert call(x=A + 4) == bl.BL_ERR_ALIGN
+    assert call(g=A + 8) == bl.BL_ERR_ALIGN
+    assert call(p=A + 4) == bl.BL_ERR_ALIGN
+    assert call(q=A + 8) == bl.BL_ERR_ALIGN
+    assert call(sa=U) == bl.BL_ERR_ALIGN
+    assert call(y=U) == bl.BL_ERR_ALIGN
+    assert call(s=0.0) == bl.BL_ERR_VALUE
+    assert call(s=float("nan")) == bl.BL_ERR_VALUE
+
+
 def test_gemm_checks():
     f = bl._lib.bitlinear_gemm
     ok = dict(p=A, s=40.0, n=16, k=64, q=A, sa=A, qs=A, m=3, r=None, y=A, acc=None, am=None, ws=None, wsb=0)
