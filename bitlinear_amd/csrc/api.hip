@@ -157,9 +157,14 @@ int ffn_impl(const float* x, int64_t m, int64_t d, int64_t f, const float* g_ffn
     const bl::Prefetch pf_gu = {{w_gate, w_up}, {wb, wb}, ch_gu};
     const bl::Prefetch pf_dn = {{w_down, nullptr}, {wb, 0u}, ch_dn};
 
-    int rc = bl::launch_quant_act(x, g_ffn, eps, M, D, q1, s1, qs1, s, false, pre ? &pf_gu : nullptr);
-    if (rc) return rc;
-    if (m <= kMaxGemvM) {
+    int rc;
+    if (bl::fwd_fits(M, D)) {
+        // one token: the norm + quant of x runs inside the gate/up launch
+        rc = bl::launch_fwd_gateup(x, g_ffn, eps, w_gate, s_gate, w_up, s_up, scale_ptr, F, D, h, q1, s1, qs1, acc_g,
+                                   acc_u, s);
+    } else if ((rc = bl::launch_quant_act(x, g_ffn, eps, M, D, q1, s1, qs1, s, false, pre ? &pf_gu : nullptr))) {
+        return rc;
+    } else if (m <= kMaxGemvM) {
         rc = bl::launch_gateup(w_gate, s_gate, w_up, s_up, scale_ptr, F, D, q1, s1, qs1, M, h, acc_g, acc_u, s);
     } else if (m <= kMaxSkinnyM) {
         rc = bl::launch_skinny(skinny_gateup(w_gate, s_gate, w_up, s_up, scale_ptr, F, D, q1, s1, qs1, M, h, acc_g,

@@ -331,6 +331,75 @@ __global__ __launch_bounds__(64) void gateup_kernel(const uint8_t* __restrict__ 
     }
 }
 
+// gateup_kernel for one token with the [RMSNorm +] quant of its input fused
+// in, as fwd_kernel does for a single matrix: every workgroup quantizes x into
+// LDS itself, its first gate and up rows already in flight.
+template <int V, bool kNorm>
+__global__ __launch_bounds__(64) void fwd_gateup_kernel(const float* __restrict__ x, const float* __restrict__ gain,
+                                                        float eps, const uint8_t* __restrict__ w_gate, float s_gate,
+                                                        const uint8_t* __restrict__ w_up, float s_up,
+                                                        const float* __restrict__ scale_ptr, int f, int d,
+                                                        float* __restrict__ h, int8_t* __restrict__ q_out,
+                                                        float* __restrict__ scale_out, int32_t* __restrict__ sum_out,
+                                                        int32_t* __restrict__ acc_gate, int32_t* __restrict__ acc_up)
+{
+    constexpr int L = 8, R = 64 / L;
+    static_assert(64 * 4 * V <= kFwdMaxK, "row held in LDS");
+    __shared__ __attribute__((aligned(16))) int8_t qs[kFwdMaxK];
+    const int lane = threadIdx.x;
+    const int g = lane / L, j = lane % L;
+    const int chunks = d / 64;
+    const size_t row_bytes = (size_t)d / 4;
+
+    uint4 wg[kMaxChunksPerLane], wu[kMaxChunksPerLane];
+    int base = blockIdx.x * R;
+    load_row<L>(w_gate + (size_t)(base + g) * row_bytes, base + g < f, j, chunks, wg);
+    load_row<L>(w_up + (size_t)(base + g) * row_bytes, base + g < f, j, chunks, wu);
+    float4 xv[V], gv[V];
+    wave_quant_load<kNorm, V>(x, gain, d, lane, xv, gv);
+    float s_a;
+    int qsum;
+    wave_quant_compute<kNorm, false, V>(xv, gv, eps, d, lane, qs, s_a, qsum);
+    __syncthreads();  // q complete in LDS
+
+    uint32_t qreg[kMaxChunksPerLane][16];
+#pragma unroll
+    for (int c = 0; c < kMaxChunksPerLane; ++c) {
+        const int ch = j + c * L;
+        if (ch < chunks) load_q_chunk(qs, ch, qreg[c]);
+    }
+    if (blockIdx.x == 0) {
+        if (q_out)
+            for (int i = lane; i < d / 16; i += 64)
+                reinterpret_cast<uint4*>(q_out)[i] = reinterpret_cast<const uint4*>(qs)[i];
+        if (lane == 0) {
+            if (scale_out) *scale_out = s_a;
+            if (sum_out) *sum_out = qsum;
+        }
+    }
+    const float sg = scale_ptr ? scale_ptr[0] : s_gate;
+    const float su = scale_ptr ? scale_ptr[1] : s_up;
+    for (;;) {
+        const int row = base + g;
+        const int ag = group_sum<L>(dot_row_one<L>(wg, j, chunks, qreg));
+        const int au = group_sum<L>(dot_row_one<L>(wu, j, chunks, qreg));
+        if (row < f && j == 0) {
+            const int tg = ag - qsum, tu = au - qsum;
+            const float gate = (float)tg * (1.0f / (s_a * sg));
+            const float up = (float)tu * (1.0f / (s_a * su));
+            const float gp = gate > 0.0f ? gate : 0.0f;
+            const float g2 = gp * gp;
+            h[row] = g2 * up;
+            if (acc_gate) acc_gate[row] = tg;
+            if (acc_up) acc_up[row] = tu;
+        }
+        base += gridDim.x * R;
+        if (base >= f) break;
+        load_row<L>(w_gate + (size_t)(base + g) * row_bytes, base + g < f, j, chunks, wg);
+        load_row<L>(w_up + (size_t)(base + g) * row_bytes, base + g < f, j, chunks, wu);
+    }
+}
+
 // Lanes per row so that every lane holds at most kMaxChunksPerLane chunks.
 inline int pick_lanes(int k)
 {
@@ -440,6 +509,38 @@ int launch_gateup(const uint8_t* w_gate, float s_gate, const uint8_t* w_up, floa
                                               h, acc_gate, acc_up)
     BL_DISPATCH_L(BL_LAUNCH)
 #undef BL_LAUNCH
+    return hipGetLastError() == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
+}
+
+int launch_fwd_gateup(const float* x, const float* gain, float eps, const uint8_t* w_gate, float s_gate,
+                      const uint8_t* w_up, float s_up, const float* scale_ptr, int f, int d, float* h,
+                      int8_t* q_out, float* scale_out, int32_t* sum_out, int32_t* acc_gate, int32_t* acc_up,
+                      hipStream_t s)
+{
+    if (!fwd_fits(1, d)) return BL_ERR_SHAPE;
+    const int grid = grid_for(f, 8);
+    const int v = (d / 4 + 63) / 64;
+#define BL_FWDGU(V, N)                                                                                       \
+    fwd_gateup_kernel<V, N><<<grid, 64, 0, s>>>(x, gain, eps, w_gate, s_gate, w_up, s_up, scale_ptr, f, d, h, \
+                                                q_out, scale_out, sum_out, acc_gate, acc_up)
+#define BL_FWDGU_V(V)       \
+    if (gain)               \
+        BL_FWDGU(V, true);  \
+    else                    \
+        BL_FWDGU(V, false)
+    if (v <= 2) {
+        BL_FWDGU_V(2);
+    } else if (v <= 4) {
+        BL_FWDGU_V(4);
+    } else if (v <= 8) {
+        BL_FWDGU_V(8);
+    } else if (v <= 10) {
+        BL_FWDGU_V(10);
+    } else {
+        BL_FWDGU_V(16);
+    }
+#undef BL_FWDGU_V
+#undef BL_FWDGU
     return hipGetLastError() == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
 }
 

@@ -36,6 +36,12 @@ bool fwd_fits(int m, int k);
 int launch_fwd(const float* x, const float* gain, float eps, const uint8_t* packed, float w_scale, int n, int k,
                float* y, int8_t* q_out, float* scale_out, int32_t* sum_out, hipStream_t s);
 
+// launch_gateup for one token with the [RMSNorm +] quant of x fused in (fwd_fits(1, d)).
+int launch_fwd_gateup(const float* x, const float* gain, float eps, const uint8_t* w_gate, float s_gate,
+                      const uint8_t* w_up, float s_up, const float* scale_ptr, int f, int d, float* h,
+                      int8_t* q_out, float* scale_out, int32_t* sum_out, int32_t* acc_gate, int32_t* acc_up,
+                      hipStream_t s);
+
 // Decode GEMV, m in [1, 8]. The weight scale is read from w_scale_ptr when it
 // is non-null, else w_scale is used.
 int launch_gemv(const uint8_t* packed, float w_scale, const float* w_scale_ptr, int n, int k, const int8_t* q,
