@@ -113,14 +113,29 @@ __device__ __forceinline__ void dot_row(const uint4 w[kMaxChunksPerLane], int la
     }
 }
 
+// load_row with a fixed number of loads: the row index is clamped to the last
+// row and the chunk index to the last chunk (those lanes re-read a line that is
+// being fetched anyway; dot_row_one skips their chunks), so no load sits under a
+// branch and a later wait can name exactly the loads it needs.
+template <int L, int CPL>
+__device__ __forceinline__ void load_row_fixed(const uint8_t* rowp, int lane_in_group, int chunks,
+                                               uint4 w[kMaxChunksPerLane])
+{
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const int ch = min(lane_in_group + c * L, chunks - 1);
+        w[c] = *reinterpret_cast<const uint4*>(rowp + (size_t)ch * 16);
+    }
+}
+
 // dot_row for one token with the activations in registers.
-template <int L>
+template <int L, int CPL>
 __device__ __forceinline__ int dot_row_one(const uint4 w[kMaxChunksPerLane], int lane_in_group, int chunks,
                                            const uint32_t (*qreg)[16])
 {
     int acc = 0;
 #pragma unroll
-    for (int c = 0; c < kMaxChunksPerLane; ++c)
+    for (int c = 0; c < CPL; ++c)
         if (lane_in_group + c * L < chunks) acc = dot_chunk(w[c], qreg[c], acc);
     return acc;
 }
@@ -182,7 +197,7 @@ __global__ __launch_bounds__(64) void gemv_kernel(const uint8_t* __restrict__ pa
 // the quant kernel, so every workgroup holds the same q, s_a and sum(q)) into
 // LDS, and then runs its rows as gemv_kernel does. The input row is read by
 // every workgroup, from L2 after the first; the workgroup's first weight rows
-// are loaded before the row, so their fetch overlaps the quant. Workgroup 0
+// are loaded right behind it, so their fetch overlaps the quant. Workgroup 0
 // also writes q, s_a and sum(q) where asked.
 template <int V, bool kNorm>
 __global__ __launch_bounds__(64) void fwd_kernel(const float* __restrict__ x, const float* __restrict__ gain, float eps,
@@ -198,11 +213,15 @@ __global__ __launch_bounds__(64) void fwd_kernel(const float* __restrict__ x, co
     const int chunks = k / 64;
     const size_t row_bytes = (size_t)k / 4;
 
-    uint4 w[kMaxChunksPerLane];
-    int base = blockIdx.x * R;
-    load_row<L>(packed + (size_t)(base + g) * row_bytes, base + g < n, j, chunks, w);
+    // x first: a wave's loads complete in issue order, so the quant waits
+    // only for x while the weight rows stream in behind it
     float4 xv[V], gv[V];
     wave_quant_load<kNorm, V>(x, gain, k, lane, xv, gv);
+    constexpr int CPL = (V + 1) / 2;  // chunks per lane: k <= 256 V
+    uint4 w[kMaxChunksPerLane];
+    int base = blockIdx.x * R;
+    load_row_fixed<L, CPL>(packed + (size_t)min(base + g, n - 1) * row_bytes, j, chunks, w);
+    __builtin_amdgcn_sched_barrier(0);  // keep the weight loads ahead of the quant
     float s_a;
     int qsum;
     wave_quant_compute<kNorm, false, V>(xv, gv, eps, k, lane, qs, s_a, qsum);
@@ -210,7 +229,7 @@ __global__ __launch_bounds__(64) void fwd_kernel(const float* __restrict__ x, co
 
     uint32_t qreg[kMaxChunksPerLane][16];
 #pragma unroll
-    for (int c = 0; c < kMaxChunksPerLane; ++c) {
+    for (int c = 0; c < CPL; ++c) {
         const int ch = j + c * L;
         if (ch < chunks) load_q_chunk(qs, ch, qreg[c]);
     }
@@ -227,12 +246,12 @@ __global__ __launch_bounds__(64) void fwd_kernel(const float* __restrict__ x, co
     for (;;) {
         const int row = base + g;
         int acc = 0;
-        const int acc0 = dot_row_one<L>(w, j, chunks, qreg);
+        const int acc0 = dot_row_one<L, CPL>(w, j, chunks, qreg);
         acc = group_sum<L>(acc0);
         if (row < n && j == 0) y[row] = (float)(acc - qsum) * inv;
         base += gridDim.x * R;
         if (base >= n) break;
-        load_row<L>(packed + (size_t)(base + g) * row_bytes, base + g < n, j, chunks, w);
+        load_row_fixed<L, CPL>(packed + (size_t)min(base + g, n - 1) * row_bytes, j, chunks, w);
     }
 }
 
@@ -333,7 +352,7 @@ __global__ __launch_bounds__(64) void gateup_kernel(const uint8_t* __restrict__ 
 
 // gateup_kernel for one token with the [RMSNorm +] quant of its input fused
 // in, as fwd_kernel does for a single matrix: every workgroup quantizes x into
-// LDS itself, its first gate and up rows already in flight.
+// LDS itself while its first gate and up rows stream in.
 template <int V, bool kNorm>
 __global__ __launch_bounds__(64) void fwd_gateup_kernel(const float* __restrict__ x, const float* __restrict__ gain,
                                                         float eps, const uint8_t* __restrict__ w_gate, float s_gate,
@@ -351,12 +370,14 @@ __global__ __launch_bounds__(64) void fwd_gateup_kernel(const float* __restrict_
     const int chunks = d / 64;
     const size_t row_bytes = (size_t)d / 4;
 
+    float4 xv[V], gv[V];
+    wave_quant_load<kNorm, V>(x, gain, d, lane, xv, gv);  // first: see fwd_kernel
+    constexpr int CPL = (V + 1) / 2;  // chunks per lane: d <= 256 V
     uint4 wg[kMaxChunksPerLane], wu[kMaxChunksPerLane];
     int base = blockIdx.x * R;
-    load_row<L>(w_gate + (size_t)(base + g) * row_bytes, base + g < f, j, chunks, wg);
-    load_row<L>(w_up + (size_t)(base + g) * row_bytes, base + g < f, j, chunks, wu);
-    float4 xv[V], gv[V];
-    wave_quant_load<kNorm, V>(x, gain, d, lane, xv, gv);
+    load_row_fixed<L, CPL>(w_gate + (size_t)min(base + g, f - 1) * row_bytes, j, chunks, wg);
+    load_row_fixed<L, CPL>(w_up + (size_t)min(base + g, f - 1) * row_bytes, j, chunks, wu);
+    __builtin_amdgcn_sched_barrier(0);  // keep the weight loads ahead of the quant
     float s_a;
     int qsum;
     wave_quant_compute<kNorm, false, V>(xv, gv, eps, d, lane, qs, s_a, qsum);
@@ -364,7 +385,7 @@ __global__ __launch_bounds__(64) void fwd_gateup_kernel(const float* __restrict_
 
     uint32_t qreg[kMaxChunksPerLane][16];
 #pragma unroll
-    for (int c = 0; c < kMaxChunksPerLane; ++c) {
+    for (int c = 0; c < CPL; ++c) {
         const int ch = j + c * L;
         if (ch < chunks) load_q_chunk(qs, ch, qreg[c]);
     }
@@ -381,8 +402,8 @@ __global__ __launch_bounds__(64) void fwd_gateup_kernel(const float* __restrict_
     const float su = scale_ptr ? scale_ptr[1] : s_up;
     for (;;) {
         const int row = base + g;
-        const int ag = group_sum<L>(dot_row_one<L>(wg, j, chunks, qreg));
-        const int au = group_sum<L>(dot_row_one<L>(wu, j, chunks, qreg));
+        const int ag = group_sum<L>(dot_row_one<L, CPL>(wg, j, chunks, qreg));
+        const int au = group_sum<L>(dot_row_one<L, CPL>(wu, j, chunks, qreg));
         if (row < f && j == 0) {
             const int tg = ag - qsum, tu = au - qsum;
             const float gate = (float)tg * (1.0f / (s_a * sg));
@@ -395,8 +416,8 @@ __global__ __launch_bounds__(64) void fwd_gateup_kernel(const float* __restrict_
         }
         base += gridDim.x * R;
         if (base >= f) break;
-        load_row<L>(w_gate + (size_t)(base + g) * row_bytes, base + g < f, j, chunks, wg);
-        load_row<L>(w_up + (size_t)(base + g) * row_bytes, base + g < f, j, chunks, wu);
+        load_row_fixed<L, CPL>(w_gate + (size_t)min(base + g, f - 1) * row_bytes, j, chunks, wg);
+        load_row_fixed<L, CPL>(w_up + (size_t)min(base + g, f - 1) * row_bytes, j, chunks, wu);
     }
 }
 
