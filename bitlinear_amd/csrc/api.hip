@@ -181,9 +181,11 @@ int ffn_impl(const float* x, int64_t m, int64_t d, int64_t f, const float* g_ffn
         if (!rc) rc = bl::launch_relu2_mul(gate, up, (int64_t)m * f, h, s);
     }
     if (rc) return rc;
+    const float* sdp = scale_ptr ? scale_ptr + 2 : nullptr;
+    if (bl::fwd_block_fits(M, F))  // one token: the sub-norm + quant of h runs inside the down launch
+        return bl::launch_fwd_block(h, g_sub, eps, w_down, s_down, sdp, D, F, residual, out, acc_d, q2, s2, qs2, s);
     rc = bl::launch_quant_act(h, g_sub, eps, M, F, q2, s2, qs2, s, false, pre ? &pf_dn : nullptr);
     if (rc) return rc;
-    const float* sdp = scale_ptr ? scale_ptr + 2 : nullptr;
     if (m <= kMaxGemvM)
         return bl::launch_gemv(w_down, s_down, sdp, D, F, q2, s2, qs2, M, residual, out, acc_d, s);
     if (m <= kMaxSkinnyM)
@@ -233,6 +235,9 @@ int bitlinear_forward(const float* x, const float* gain, float eps, const uint8_
     const hipStream_t s = as_stream(stream);
     if (bl::fwd_fits((int)m, (int)k))
         return bl::launch_fwd(x, gain, eps, packed, w_scale, (int)n, (int)k, y, q, act_scale, act_sum, s);
+    if (bl::fwd_block_fits((int)m, (int)k))
+        return bl::launch_fwd_block(x, gain, eps, packed, w_scale, nullptr, (int)n, (int)k, nullptr, y, nullptr, q,
+                                    act_scale, act_sum, s);
     const uint64_t wbytes = std::min<uint64_t>((uint64_t)n * (uint64_t)k / 4, 0xfffffffcull);
     const bl::Prefetch pf = {{packed, nullptr}, {(uint32_t)wbytes, 0u},
                              (uint32_t)bl::gemv_rows_per_block((int)k) * (uint32_t)(k / 4)};

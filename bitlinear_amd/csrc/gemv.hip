@@ -24,7 +24,8 @@ namespace {
 
 constexpr uint32_t kCodeMask = 0x03030303u;
 constexpr int kMaxChunksPerLane = 8;
-constexpr int kFwdMaxK = 4096;  // longest row of the one-launch quant + GEMV
+constexpr int kFwdMaxK = 4096;         // longest row of the one-wave quant + GEMV
+constexpr int kFwdBlockMaxK = 16384;   // ... and of the 512-thread form
 
 // 4x4 byte transpose of 16 activations a[0..15] (given as 4 dwords, natural
 // order) into the order the shifted code masks produce: out[j] holds
@@ -255,6 +256,71 @@ __global__ __launch_bounds__(64) void fwd_kernel(const float* __restrict__ x, co
     }
 }
 
+// fwd_kernel for rows longer than one wave can hold (4096 < k <= 512 NPT): a
+// 512-thread workgroup quantizes x with the workgroup quant of the quant kernel
+// (block_quant_compute: same operations, same order, so every workgroup holds
+// the same q, s_a and sum(q)) into LDS, then each wave runs one row with all 64
+// lanes. Optional residual (may alias y) and exact accumulators, as gemv_kernel.
+template <int NPT, bool kNorm>
+__global__ __launch_bounds__(512) void fwd_block_kernel(const float* __restrict__ x, const float* __restrict__ gain,
+                                                        float eps, const uint8_t* __restrict__ packed, float w_scale,
+                                                        const float* __restrict__ w_scale_ptr, int n, int k,
+                                                        const float* residual, float* y, int32_t* __restrict__ acc_out,
+                                                        int8_t* __restrict__ q_out, float* __restrict__ scale_out,
+                                                        int32_t* __restrict__ sum_out)
+{
+    constexpr int L = 64, RW = 8;                // a row per wave, 8 per workgroup
+    constexpr int CPL = (8 * NPT + L - 1) / L;   // chunks per lane: k <= 512 NPT
+    static_assert(CPL <= kMaxChunksPerLane && 512 * NPT <= kFwdBlockMaxK, "row size");
+    __shared__ __attribute__((aligned(16))) int8_t qs[512 * NPT];
+    __shared__ BlockQuantShared sh;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int chunks = k / 64;
+    const size_t row_bytes = (size_t)k / 4;
+
+    float xv[NPT], gv[NPT];
+    block_quant_load<kNorm, NPT>(x, gain, k, xv, gv);  // first: a wave's loads complete in issue order
+    uint4 w[kMaxChunksPerLane];
+    int base = blockIdx.x * RW;
+    load_row_fixed<L, CPL>(packed + (size_t)min(base + wave, n - 1) * row_bytes, lane, chunks, w);
+    __builtin_amdgcn_sched_barrier(0);  // keep the weight loads ahead of the quant
+    float s_a;
+    int qsum;
+    block_quant_compute<kNorm, false, NPT>(xv, gv, eps, k, qs, sh, s_a, qsum);  // ends with a barrier
+
+    uint32_t qreg[kMaxChunksPerLane][16];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const int ch = lane + c * L;
+        if (ch < chunks) load_q_chunk(qs, ch, qreg[c]);
+    }
+    if (blockIdx.x == 0) {
+        if (q_out)
+            for (int i = threadIdx.x; i < k / 16; i += 512)
+                reinterpret_cast<uint4*>(q_out)[i] = reinterpret_cast<const uint4*>(qs)[i];
+        if (threadIdx.x == 0) {
+            if (scale_out) *scale_out = s_a;
+            if (sum_out) *sum_out = qsum;
+        }
+    }
+    const float ws = w_scale_ptr ? *w_scale_ptr : w_scale;
+    const float inv = 1.0f / (s_a * ws);
+    for (;;) {
+        const int row = base + wave;
+        const int acc = group_sum<L>(dot_row_one<L, CPL>(w, lane, chunks, qreg));
+        if (row < n && lane == 0) {
+            const int total = acc - qsum;
+            float v = (float)total * inv;
+            if (residual) v = residual[row] + v;
+            y[row] = v;
+            if (acc_out) acc_out[row] = total;
+        }
+        base += gridDim.x * RW;
+        if (base >= n) break;
+        load_row_fixed<L, CPL>(packed + (size_t)min(base + wave, n - 1) * row_bytes, lane, chunks, w);
+    }
+}
+
 // ---- several matrices of equal shape sharing the activations (q, k, v) ----
 struct MultiPtrs {
     const uint8_t* p[4];
@@ -464,6 +530,8 @@ int gemv_rows_per_block(int k) { return 64 / pick_lanes(k); }
 
 bool fwd_fits(int m, int k) { return m == 1 && k >= 64 && k <= kFwdMaxK && k % 64 == 0 && pick_lanes(k) == 8; }
 
+bool fwd_block_fits(int m, int k) { return m == 1 && k > kFwdMaxK && k <= kFwdBlockMaxK && k % 64 == 0; }
+
 int launch_gemv(const uint8_t* packed, float w_scale, const float* w_scale_ptr, int n, int k, const int8_t* q,
                 const float* act_scale, const int32_t* act_sum, int m, const float* residual, float* y,
                 int32_t* acc_out, hipStream_t s)
@@ -500,6 +568,33 @@ int launch_fwd(const float* x, const float* gain, float eps, const uint8_t* pack
     else
         BL_FWD(16);
 #undef BL_FWD
+    return hipGetLastError() == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
+}
+
+int launch_fwd_block(const float* x, const float* gain, float eps, const uint8_t* packed, float w_scale,
+                     const float* w_scale_ptr, int n, int k, const float* residual, float* y, int32_t* acc_out,
+                     int8_t* q_out, float* scale_out, int32_t* sum_out, hipStream_t s)
+{
+    if (!fwd_block_fits(1, k)) return BL_ERR_SHAPE;
+    const int grid = (n + 7) / 8 < 8192 ? (n + 7) / 8 : 8192;
+    const int per = (k + 511) / 512;  // values per thread
+#define BL_FWDB(N, G)                                                                                              \
+    fwd_block_kernel<N, G><<<grid, 512, 0, s>>>(x, gain, eps, packed, w_scale, w_scale_ptr, n, k, residual, y, acc_out, \
+                                                q_out, scale_out, sum_out)
+#define BL_FWDB_N(N)      \
+    if (gain)             \
+        BL_FWDB(N, true); \
+    else                  \
+        BL_FWDB(N, false)
+    if (per <= 16) {
+        BL_FWDB_N(16);
+    } else if (per <= 20) {
+        BL_FWDB_N(20);
+    } else {
+        BL_FWDB_N(32);
+    }
+#undef BL_FWDB_N
+#undef BL_FWDB
     return hipGetLastError() == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
 }
 

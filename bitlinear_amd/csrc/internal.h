@@ -36,6 +36,13 @@ bool fwd_fits(int m, int k);
 int launch_fwd(const float* x, const float* gain, float eps, const uint8_t* packed, float w_scale, int n, int k,
                float* y, int8_t* q_out, float* scale_out, int32_t* sum_out, hipStream_t s);
 
+// The same for longer rows (fwd_block_fits(m, k): m == 1, 4096 < k <= 16384,
+// k % 64 == 0), with an optional residual (may alias y) and exact accumulators.
+bool fwd_block_fits(int m, int k);
+int launch_fwd_block(const float* x, const float* gain, float eps, const uint8_t* packed, float w_scale,
+                     const float* w_scale_ptr, int n, int k, const float* residual, float* y, int32_t* acc_out,
+                     int8_t* q_out, float* scale_out, int32_t* sum_out, hipStream_t s);
+
 // launch_gateup for one token with the [RMSNorm +] quant of x fused in (fwd_fits(1, d)).
 int launch_fwd_gateup(const float* x, const float* gain, float eps, const uint8_t* w_gate, float s_gate,
                       const uint8_t* w_up, float s_up, const float* scale_ptr, int f, int d, float* h,

@@ -139,71 +139,14 @@ __global__ __launch_bounds__(kThreads) void quant_act_reg_kernel(const float* __
         prefetch_chunks(pf, row, row - rows, (int)gridDim.x - rows, kThreads, (uint32_t)(uintptr_t)&trash[0]);
         return;
     }
-    const int t = threadIdx.x;
-    const int lane = t & 63;
-    const int wave = t >> 6;
-    const float* xr = x + (size_t)row * k;
-    __shared__ double wsum_d[kWaves];
-    __shared__ float wmax[kWaves];
-    __shared__ int wsum[kWaves];
-
+    __shared__ BlockQuantShared sh;
     float xv[NPT], gv[NPT];
-#pragma unroll
-    for (int j = 0; j < NPT; ++j) {
-        const int i = t + j * kThreads;
-        xv[j] = i < k ? xr[i] : 0.0f;
-        gv[j] = kNorm && i < k ? gain[i] : 0.0f;
-    }
-
-    float r = 1.0f;
-    if (kNorm) {
-        double p = 0.0;
-#pragma unroll
-        for (int j = 0; j < NPT; ++j) {
-            const double v = (double)xv[j];
-            if (t + j * kThreads < k) p += v * v;
-        }
-        p = wave_butterfly_sum(p);
-        if (lane == 0) wsum_d[wave] = p;
-        __syncthreads();
-        r = (float)(1.0 / sqrt(cross_wave_sum8(wsum_d) / (double)k + (double)eps));
-    }
-
-    float amax = 0.0f;
-#pragma unroll
-    for (int j = 0; j < NPT; ++j) {
-        const float y = kNorm ? (xv[j] * r) * gv[j] : xv[j];
-        if (t + j * kThreads < k) amax = fmaxf(amax, fabsf(y));
-    }
-    amax = wave_max(amax);
-    if (lane == 0) wmax[wave] = amax;
-    __syncthreads();
-    amax = wmax[0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) amax = fmaxf(amax, wmax[w]);
-    const float scale = 127.0f / fmaxf(amax, 1e-5f);
-
-    int sum = 0;
-    int8_t* qr = q + (size_t)row * k;
-#pragma unroll
-    for (int j = 0; j < NPT; ++j) {
-        const int i = t + j * kThreads;
-        if (i < k) {
-            const float y = kNorm ? (xv[j] * r) * gv[j] : xv[j];
-            const int qv = quant_one(y, scale);
-            sum += qv;
-            // perm16: value 4 g + j' of each 16 sits at byte 4 j' + g
-            qr[kPerm ? (i & ~15) + 4 * (i & 3) + ((i >> 2) & 3) : i] = (int8_t)qv;
-        }
-    }
-    sum = wave_sum(sum);
-    if (lane == 0) wsum[wave] = sum;
-    __syncthreads();
-    if (t == 0) {
+    block_quant_load<kNorm, NPT>(x + (size_t)row * k, gain, k, xv, gv);
+    float scale;
+    int total;
+    block_quant_compute<kNorm, kPerm, NPT>(xv, gv, eps, k, q + (size_t)row * k, sh, scale, total);
+    if (threadIdx.x == 0) {
         act_scale[row] = scale;
-        int total = 0;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) total += wsum[w];
         if (act_sum) act_sum[row] = total;
     }
 }

@@ -1,9 +1,9 @@
 // wave_quant.h -- [RMSNorm +] per-token absmax activation quant of one row
-// by one wave (RMSNorm in front of every BitLinear, "Add Support for BitNet
-// Architecture Inference", candle PR 2664; activation_quant of the same PR),
-// for rows of up to 64 * 4 * V values. Used by the one-wave-per-row quant
-// kernel and by the fused quant + GEMV kernel, so both compute the same q,
-// s_a and sum(q) with the same operations in the same order.
+// (RMSNorm in front of every BitLinear, "Add Support for BitNet Architecture
+// Inference", candle PR 2664; activation_quant of the same PR) by one wave, for
+// rows of up to 64 * 4 * V values, or by one 512-thread workgroup. Used by the
+// quant kernels and by the fused quant + GEMV kernels, so all of them compute
+// the same q, s_a and sum(q) with the same operations in the same order.
 //
 // Lane t loads the float4 chunks t, t + 64, ... (coalesced), so no LDS and no
 // barrier is needed. The fixed order of the sum of squares still holds: chunk
@@ -129,6 +129,90 @@ __device__ __forceinline__ void wave_quant_row(const float* __restrict__ xrow, c
     float4 xv[V], gv[V];
     wave_quant_load<kNorm, V>(xrow, gain, k, lane, xv, gv);
     wave_quant_compute<kNorm, kPerm, V>(xv, gv, eps, k, lane, qr, scale_out, sum_out);
+}
+
+// The same quant by a 512-thread workgroup, for rows of up to 512 * NPT values:
+// thread t holds x[t + 512 j] (one load per value) and forms partial t of the
+// fixed order itself (ascending k); the butterfly runs over offsets 1 .. 32
+// inside each wave and 64, 128, 256 across the 8 waves. Three barriers.
+struct BlockQuantShared {
+    double wsum_d[8];
+    float wmax[8];
+    int wsum[8];
+};
+
+template <bool kNorm, int NPT>
+__device__ __forceinline__ void block_quant_load(const float* __restrict__ xr, const float* __restrict__ gain, int k,
+                                                 float (&xv)[NPT], float (&gv)[NPT])
+{
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+        const int i = t + j * 512;
+        xv[j] = i < k ? xr[i] : 0.0f;
+        gv[j] = kNorm && i < k ? gain[i] : 0.0f;
+    }
+}
+
+// Quantizes the loaded row into qr (natural or perm16 order; global memory or
+// LDS); every thread returns s_a (scale_out) and sum(q) (sum_out). All 512
+// threads of the workgroup must call it.
+template <bool kNorm, bool kPerm, int NPT>
+__device__ __forceinline__ void block_quant_compute(const float (&xv)[NPT], const float (&gv)[NPT], float eps, int k,
+                                                    int8_t* qr, BlockQuantShared& sh, float& scale_out, int& sum_out)
+{
+    constexpr int kThreads = 512, kWaves = 8;
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = t >> 6;
+    float r = 1.0f;
+    if (kNorm) {
+        double p = 0.0;
+#pragma unroll
+        for (int j = 0; j < NPT; ++j) {
+            const double v = (double)xv[j];
+            if (t + j * kThreads < k) p += v * v;
+        }
+        p = wave_butterfly_sum(p);
+        if (lane == 0) sh.wsum_d[wave] = p;
+        __syncthreads();
+        r = (float)(1.0 / sqrt(cross_wave_sum8(sh.wsum_d) / (double)k + (double)eps));
+    }
+
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+        const float y = kNorm ? (xv[j] * r) * gv[j] : xv[j];
+        if (t + j * kThreads < k) amax = fmaxf(amax, fabsf(y));
+    }
+    amax = wave_max(amax);
+    if (lane == 0) sh.wmax[wave] = amax;
+    __syncthreads();
+    amax = sh.wmax[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) amax = fmaxf(amax, sh.wmax[w]);
+    const float scale = 127.0f / fmaxf(amax, 1e-5f);
+
+    int sum = 0;
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+        const int i = t + j * kThreads;
+        if (i < k) {
+            const float y = kNorm ? (xv[j] * r) * gv[j] : xv[j];
+            const int qv = quant_one(y, scale);
+            sum += qv;
+            // perm16: value 4 g + j' of each 16 sits at byte 4 j' + g
+            qr[kPerm ? (i & ~15) + 4 * (i & 3) + ((i >> 2) & 3) : i] = (int8_t)qv;
+        }
+    }
+    sum = wave_sum(sum);
+    if (lane == 0) sh.wsum[wave] = sum;
+    __syncthreads();
+    int total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) total += sh.wsum[w];
+    scale_out = scale;
+    sum_out = total;
 }
 
 }  // namespace bl
