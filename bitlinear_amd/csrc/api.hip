@@ -148,7 +148,7 @@ int ffn_impl(const float* x, int64_t m, int64_t d, int64_t f, const float* g_ffn
     const int M = (int)m, D = (int)d, F = (int)f;
     // Up to 32 tokens the products are short, latency-bound weight streams:
     // each norm + quant launch also pulls the next product's weight lines
-    // into L2 (extra workgroups, no effect on results).
+    // into the memory-side cache (extra workgroups, no effect on results).
     const bool pre = m <= kMaxSkinnyM;
     const bool gemv = m <= kMaxGemvM;
     const uint32_t wb = (uint32_t)((size_t)f * d / 4);
@@ -378,7 +378,8 @@ int bitnet_decode_stream(const uint8_t* weights, const float* scales, const floa
             const float* gl = gains + l * gstride;
             float* qkv_l = qkv ? qkv + (size_t)l * m * 3 * d : at<float>(workspace, L.qkv);
             const uint8_t* wg = wl + 4 * dd;
-            // each norm + quant also pulls the next product's weight lines into L2
+            // each norm + quant also pulls the next product's weight lines into the
+            // memory-side cache
             const uint32_t rd = (uint32_t)(D / 4), rf = (uint32_t)(F / 4);
             const bl::Prefetch pf_qkv = {{wl, nullptr}, {(uint32_t)(3 * dd), 0u},
                                          (uint32_t)bl::skinny_rows_per_tile(3 * D, false) * rd};

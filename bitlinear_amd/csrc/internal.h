@@ -18,7 +18,7 @@ struct Prefetch;
 // written with each 16 values 4x4 byte-transposed (byte 4 j + g of a group
 // holds value 4 g + j), the operand order of the skinny MFMA kernels. With pf
 // (and fewer rows than the one-wave-per-row kernel takes), extra workgroups of
-// the same launch pull the weight lines of pf into L2 for the kernel that
+// the same launch pull the weight lines of pf toward the CUs for the kernel that
 // follows; they change no result.
 int launch_quant_act(const float* x, const float* gain, float eps, int m, int k, int8_t* q,
                      float* act_scale, int32_t* act_sum, hipStream_t s, bool perm16 = false,

@@ -1,4 +1,4 @@
-// prefetch.h -- pulling weight lines into L2 ahead of the loads that use them.
+// prefetch.h -- pulling weight lines toward the CUs ahead of the loads that use them.
 //
 // At one token (or a few) a BitLinear step is a short weight stream whose time
 // is mostly load latency. A wave's vector loads complete in issue order, so
@@ -6,10 +6,12 @@
 // between. Instead a line is touched with one dword loaded straight into a
 // scratch area of LDS (global_load_lds_dword): no register is held, and the
 // compiler, which does not see the load, inserts no wait for it. The line
-// lands in L2 of the issuing CU's XCD and in the memory-side cache; the
-// instruction still counts in the wave's vmcnt, so the wave's next wait for a
-// vector load also waits for it, and a wave must wait for it (wait_loads)
-// before it ends while the LDS target is still its own.
+// lands in L2 of the issuing CU's XCD and in the memory-side cache. Inside one
+// launch a later load of the same XCD hits L2; across a launch boundary only
+// the memory-side cache keeps it (the L2 traffic counters of the next launch
+// do not drop). The instruction still counts in the wave's vmcnt, so the
+// wave's next wait for a vector load also waits for it, and a wave must wait
+// for it (wait_loads) before it ends while the LDS target is still its own.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -33,12 +35,14 @@ __device__ __forceinline__ void prefetch_line(const void* p, uint32_t lds_off)
 // Waits until every vector load of the wave, prefetches included, has landed.
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Weights for a launch to pull into L2 on behalf of the launch that follows
-// it: up to two byte spans (4-byte aligned, sizes multiples of 4) of which
-// workgroup b of the next launch reads bytes [b chunk, (b + 1) chunk) of each
-// (chunk a multiple of 4). Workgroup i of a launch runs on XCD i mod 8 (the
-// round-robin dispatch of an MI355X, measured at every launch), so a line is
-// prefetched by a workgroup on the XCD whose L2 the reader will look in.
+// Weights for a launch to pull toward the CUs on behalf of the launch that
+// follows it: up to two byte spans (4-byte aligned, sizes multiples of 4) of
+// which workgroup b of the next launch reads bytes [b chunk, (b + 1) chunk) of
+// each (chunk a multiple of 4). Workgroup i of a launch runs on XCD i mod 8
+// (the round-robin dispatch of an MI355X, measured at every launch); chunks
+// are handed out so that a line is prefetched on the XCD that will read it,
+// which costs nothing, although the gain measured comes from the memory-side
+// cache (see above).
 struct Prefetch {
     const uint8_t* p[2];
     uint32_t bytes[2];

@@ -133,8 +133,8 @@ int bitlinear_gemv(const uint8_t *packed, float w_scale, int64_t n, int64_t k,
  * For m == 1 and k <= 16384 this is one launch: every workgroup quantizes x itself (the
  * same operations in the same order as the quant kernel; one wave per workgroup up to
  * k = 4096, 512 threads above) and then runs its weight rows, so the quant adds no launch
- * and no round trip through memory. Otherwise the quant launch also pulls P into L2 for
- * the GEMV launch that follows it.
+ * and no round trip through memory. Otherwise the quant launch also pulls P into the
+ * memory-side cache for the GEMV launch that follows it.
  * Errors: NULL, SHAPE (m outside [1, 8], n <= 0, k % 64 != 0, k > 32768), ALIGN (x, gain,
  * packed, q 16-byte; act_scale, act_sum, y 4-byte), VALUE (w_scale not > 0), LAUNCH. */
 int bitlinear_forward(const float *x, const float *gain, float eps, const uint8_t *packed, float w_scale,
@@ -192,7 +192,7 @@ int bitlinear_gemm(const uint8_t *packed, float w_scale, int64_t n, int64_t k,
  * 4096 < f <= 16384 for the second half) each norm + quant runs inside the
  * launch of the product it feeds, so the FFN is two launches; the workspace
  * still receives q1, s1, qs1, h, q2, s2, qs2. Up to 32 tokens each norm + quant
- * launch also pulls the next product's weights into L2. d and f must be
+ * launch also pulls the next product's weights into the memory-side cache. d and f must be
  * multiples of 64. Errors: NULL, SHAPE, ALIGN, VALUE, WORKSPACE, LAUNCH. */
 #define BITNET_FFN_WRITE_ACC 1
 enum bitnet_ffn_ws_segment {
