@@ -64,6 +64,30 @@ def test_graph_quant_gemv(bl):
     _replay_check(torch, calls, [q, s, qs, y], lambda: None)
 
 
+@pytest.mark.parametrize("m,k,norm", [(1, 2560, False), (1, 10240, True), (3, 2048, True)])
+def test_graph_forward(bl, m, k, norm):
+    """bitlinear_forward in a graph: the one-launch forms (one wave per workgroup,
+    512 threads) and the quant launch with prefetch workgroups + GEMV."""
+    import torch
+    dev = torch.device("cuda", 0)
+    n = 1000
+    log(f"graph forward m={m} k={k} norm={norm}")
+    g = W.rng(W.W_GEMV, 8, k)
+    p = to_dev(bl.bitlinear_pack(W.ternary(g, n, k)))
+    sw = W.weight_scale(g)
+    x = to_dev(W.activations(W.rng(W.W_GEMV, 8, W.T_X), m, k))
+    gain = to_dev(W.gains(g, k)) if norm else None
+    q = torch.empty((m, k), dtype=torch.int8, device=dev)
+    s = torch.empty(m, dtype=torch.float32, device=dev)
+    qs = torch.empty(m, dtype=torch.int32, device=dev)
+    y = torch.empty((m, n), dtype=torch.float32, device=dev)
+
+    def calls():
+        bl.bitlinear_forward(x, gain, 1e-5, p, sw, n, q, s, qs, y)
+
+    _replay_check(torch, calls, [q, s, qs, y], lambda: None)
+
+
 @pytest.mark.parametrize("m", [1, 20])
 def test_graph_ffn(bl, m):
     import torch
