@@ -215,6 +215,41 @@ def test_gemm(bl, olib, m, n, k):
     assert_exact(to_host(am), np.argmax(oy, axis=1).astype(np.int32), "argmax of logits")
 
 
+def test_gemm_prefill_full_size_sampled_rows(bl, olib):
+    """The prefill product at the benchmark's size and launch configuration
+    (2048 tokens x K = 2560 -> N = 10240, 128 x 320 block tiles, activations with
+    1 % outliers x20): the quant of all rows against the oracle, then the exact
+    int32 accumulators and the outputs of 24 rows -- the first and last of
+    block tiles and halves, and random ones -- against the oracle's product of
+    those rows, every column."""
+    import torch
+    m, k, n = 2048, 2560, 10240
+    log(f"gemm full size m={m} n={n} k={k}")
+    g = W.rng(103, m, n)
+    t = W.ternary(g, n, k)
+    sw = W.weight_scale(g)
+    x = W.activations(g, m, k, outliers=True)
+    p = pack_both(t, olib)
+    dev = torch_dev()
+    q = torch.empty((m, k), dtype=torch.int8, device=dev)
+    s = torch.empty(m, dtype=torch.float32, device=dev)
+    qs = torch.empty(m, dtype=torch.int32, device=dev)
+    bl.bitlinear_quant_act(to_dev(x), None, 1e-5, q, s, qs)
+    oq, os_, oqs = oracle.quant_act(x, None, 1e-5, olib)
+    assert_exact(to_host(q), oq, "q")
+    assert_exact(to_host(s).view(np.uint32), os_.view(np.uint32), "act_scale bits")
+    assert_exact(to_host(qs), oqs, "act_sum")
+    y = torch.empty((m, n), dtype=torch.float32, device=dev)
+    acc = torch.empty((m, n), dtype=torch.int32, device=dev)
+    bl.bitlinear_gemm(to_dev(p), sw, n, k, q, s, qs, m, None, y, acc, None, None)
+    rows = sorted(set([0, 1, 63, 64, 127, 128, 129, 1023, 1024, 1151, 2046, 2047] +
+                      list(W.rng(103, 1, 1).choice(m, 12, replace=False))))
+    oy, oacc = oracle.bitlinear(p, sw, k, oq[rows], os_[rows], olib)
+    ya, acca = to_host(y), to_host(acc)
+    assert_exact(acca[rows], oacc, "acc (sampled rows)")
+    assert_f32(ya[rows], oy, "y (sampled rows)")
+
+
 @pytest.mark.parametrize("m", [7, 40])
 def test_gemm_argmax_ties_no_logits(bl, olib, m):
     """Duplicated weight rows make ties; the lowest index must win, without y."""
