@@ -106,7 +106,6 @@ def _dev(t, dtype=None, name="tensor", optional=False):
         if optional:
             return None
         raise BitlinearError(BL_ERR_NULL, f"{name} is required")
-    import torch
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{name} must be a torch tensor on the GPU")
     if dtype is not None and t.dtype != dtype:
@@ -125,7 +124,6 @@ def _host(a, dtype, name):
 def _stream(stream):
     if stream is not None:
         return stream
-    import torch
     return torch.cuda.current_stream().cuda_stream
 
 
@@ -162,7 +160,6 @@ def bitlinear_weight_quant(w):
 
 def bitlinear_quant_act(x, gain, eps, q, act_scale, act_sum, stream=None):
     """[RMSNorm +] activation quant of x[m][k] (fp32, GPU) into q, act_scale, act_sum."""
-    import torch
     m, k = x.shape
     _check(_lib.bitlinear_quant_act(_dev(x, torch.float32, "x"), _dev(gain, torch.float32, "gain", True), eps, m, k,
                                     _dev(q, torch.int8, "q"), _dev(act_scale, torch.float32, "act_scale"),
@@ -171,7 +168,6 @@ def bitlinear_quant_act(x, gain, eps, q, act_scale, act_sum, stream=None):
 
 
 def bitlinear_gemv(packed, w_scale, n, k, q, act_scale, act_sum, m, residual, y, acc_out=None, stream=None):
-    import torch
     _check(_lib.bitlinear_gemv(_dev(packed, torch.uint8, "packed"), float(w_scale), n, k, _dev(q, torch.int8, "q"),
                                _dev(act_scale, torch.float32, "act_scale"), _dev(act_sum, torch.int32, "act_sum"), m,
                                _dev(residual, torch.float32, "residual", True), _dev(y, torch.float32, "y"),
@@ -180,7 +176,6 @@ def bitlinear_gemv(packed, w_scale, n, k, q, act_scale, act_sum, m, residual, y,
 
 def bitlinear_forward(x, gain, eps, packed, w_scale, n, q, act_scale, act_sum, y, stream=None):
     """[RMSNorm +] quant + GEMV of x[m][k] (fp32, GPU) into y[m][n]; q, act_scale, act_sum receive the quant."""
-    import torch
     m, k = x.shape
     _check(_lib.bitlinear_forward(_dev(x, torch.float32, "x"), _dev(gain, torch.float32, "gain", True), eps,
                                   _dev(packed, torch.uint8, "packed"), float(w_scale), n, k, m,
@@ -195,7 +190,6 @@ def bitlinear_gemm_workspace_bytes(m, n, k, with_argmax):
 
 def bitlinear_gemm(packed, w_scale, n, k, q, act_scale, act_sum, m, residual, y, acc_out=None, row_argmax=None,
                    workspace=None, stream=None):
-    import torch
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_lib.bitlinear_gemm(_dev(packed, torch.uint8, "packed"), float(w_scale), n, k, _dev(q, torch.int8, "q"),
                                _dev(act_scale, torch.float32, "act_scale"), _dev(act_sum, torch.int32, "act_sum"), m,
@@ -217,7 +211,6 @@ def bitnet_ffn_workspace_offset(m, d, f, segment):
 
 def bitnet_ffn(x, m, d, f, norm_gain, sub_norm_gain, eps, w_gate, s_gate, w_up, s_up, w_down, s_down, residual, out,
                workspace, flags=0, stream=None):
-    import torch
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(_lib.bitnet_ffn(_dev(x, torch.float32, "x"), m, d, f, _dev(norm_gain, torch.float32, "norm_gain"),
                            _dev(sub_norm_gain, torch.float32, "sub_norm_gain"), eps,
@@ -236,7 +229,6 @@ def bitnet_stream_workspace_bytes(m, d, f):
 
 
 def bitnet_decode_stream(weights, scales, gains, z, n_layers, m, d, f, eps, x, qkv, workspace, stream=None):
-    import torch
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(_lib.bitnet_decode_stream(_dev(weights, torch.uint8, "weights"), _dev(scales, torch.float32, "scales"),
                                      _dev(gains, torch.float32, "gains"), _dev(z, torch.float32, "z"), n_layers, m,
@@ -247,7 +239,6 @@ def bitnet_decode_stream(weights, scales, gains, z, n_layers, m, d, f, eps, x, q
 
 def ffn_workspace_view(workspace, m, d, f, segment):
     """A typed view of one FFN workspace segment (for inspecting intermediates)."""
-    import torch
     shapes = {"q1": ((m, d), torch.int8), "s1": ((m,), torch.float32), "qs1": ((m,), torch.int32),
               "h": ((m, f), torch.float32), "q2": ((m, f), torch.int8), "s2": ((m,), torch.float32),
               "qs2": ((m,), torch.int32), "acc_gate": ((m, f), torch.int32), "acc_up": ((m, f), torch.int32),
