@@ -156,6 +156,57 @@ def omp_threads():
     return int(v) if v and v.isdigit() else os.cpu_count()
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def per_call_stats(torch, fn, iters):
+    """fn() run iters times with a HIP event pair around each call on the
+    current stream (the one the library launches on). Returns the per-call
+    median and the 10th / 90th percentiles in ms."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for s, e in evs:
+        s.record()
+        fn()
+        e.record()
+    torch.cuda.synchronize()
+    t = np.array([s.elapsed_time(e) for s, e in evs])
+    return {"median_ms": round(float(np.median(t)), 5), "p10_ms": round(float(np.percentile(t, 10)), 5),
+            "p90_ms": round(float(np.percentile(t, 90)), 5), "calls": iters}
+
+
+def probe_peaks(bl, torch, dev0):
+    """Measured ceilings: the HBM read-stream probe over 4 GiB and the
+    int8-MFMA-only probe (best of a few runs each)."""
+    sink = torch.zeros(1, dtype=torch.int32, device=dev0)
+    buf = torch.ones(4 << 30, dtype=torch.uint8, device=dev0)
+    bl.bitlinear_probe_read(buf, sink)
+    best = 0.0
+    for _ in range(5):
+        with Timer() as t:
+            nb = bl.bitlinear_probe_read(buf, sink)
+        best = max(best, nb / (t.ms * 1e-3) / 1e9)
+    del buf
+    iters = 20000
+    bl.bitlinear_probe_mfma_i8(100, sink)
+    best_ops = 0.0
+    for _ in range(3):
+        with Timer() as t:
+            ops = bl.bitlinear_probe_mfma_i8(iters, sink)
+        best_ops = max(best_ops, ops / (t.ms * 1e-3) / 1e12)
+    torch.cuda.synchronize()
+    return {"hbm_read_gbs": round(best, 1), "int8_mfma_tops": round(best_ops, 1),
+            "how": "bitlinear_probe_read over 4 GiB (best of 5); bitlinear_probe_mfma_i8, 2 waves per SIMD x "
+                   "8 independent v_mfma_i32_16x16x64_i8 chains (best of 3)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -202,12 +253,19 @@ def main():
     for _ in range(args.warmup):
         run_stream_step(bl, dev, L, m, d, f, x, qkv, ws)
     torch.cuda.synchronize()
+    # one event pair per step inside the timed region (recording an event is
+    # an asynchronous stream operation) for the per-step distribution
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
     tw0 = time.perf_counter()
     with Timer() as tm:
-        for _ in range(args.steps):
+        for i in range(args.steps):
+            step_ev[i][0].record()
             run_stream_step(bl, dev, L, m, d, f, x, qkv, ws)
+            step_ev[i][1].record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - tw0) * 1e3
+    step_ms = np.array([a.elapsed_time(b) for a, b in step_ev])
     status = int(ws[4:8].view(torch.int32).item())
     if status != 0:
         raise RuntimeError(f"decode stream status word {status}: the persistent kernel gave up; timing is void")
@@ -233,6 +291,9 @@ def main():
                                "attention math excluded", "layers": L, "dim": d, "ffn": f, "tokens": m,
                    "weight_bytes_per_step": weight_bytes},
         "ms_per_token": round(ms_per_step, 5),
+        "ms_per_step_events": {"mean": round(ev_ms_per_step, 5), "median": round(float(np.median(step_ms)), 5),
+                               "p10": round(float(np.percentile(step_ms, 10)), 5),
+                               "p90": round(float(np.percentile(step_ms, 90)), 5)},
     }
 
     # roofline of the dominant kernel: at one token the whole stream is one
@@ -240,10 +301,15 @@ def main():
     persistent = bl._lib.bitnet_stream_workspace_bytes(m, d, f) > 0 and stream_is_persistent(ws)
     kname = ("stream_kernel<2560, 10240> (one persistent launch per token)" if persistent
              else "bitnet_decode_stream launches of one token")
-    result["roofline"] = {"kernel": kname, "bound": "hbm",
-                          "achieved": round(weight_bytes / (ev_ms_per_step * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
-                          "unit": "GB/s", "frac": round(weight_bytes / (ev_ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                          "traffic": traffic_bytes("stream_3b")}
+    achieved = weight_bytes / (ev_ms_per_step * 1e-3) / 1e9
+    peaks = probe_peaks(bl, torch, dev0)
+    log(f"probes: HBM read {peaks['hbm_read_gbs']} GB/s, int8 MFMA {peaks['int8_mfma_tops']} TOP/s")
+    result["roofline"] = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                          "traffic": traffic_bytes("stream_3b"),
+                          "algorithmic_bytes": weight_bytes,
+                          "probe_peak": peaks["hbm_read_gbs"], "frac_of_probe": round(achieved / peaks["hbm_read_gbs"], 4)}
+    result["probe_peaks"] = peaks
 
     # ---- CPU oracle baseline + parity of the first step ----------------------------------
     if not args.no_cpu:
@@ -261,16 +327,93 @@ def main():
             tokens += 1
         cpu_s = time.perf_counter() - tc0
         result["cpu_baseline"] = {"value": round(tokens * weight_bytes / cpu_s / 1e9, 4), "unit": "GB/s",
-                                  "cores": omp_threads(), "kind": "oracle",
+                                  "cores": oracle.set_threads(0, olib), "kind": "oracle",
                                   "sample": f"{tokens} consecutive tokens of the same 32-layer stream (all 224 "
-                                            f"BitLinears each), {cpu_s:.2f} s"}
+                                            f"BitLinears each), {cpu_s:.2f} s",
+                                  "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
         result["parity_first_step"] = {"bit_exact": exact, "max_rel_err_x": rel}
         log(f"oracle: {first_s:.2f}s for one token, {tokens} tokens in {cpu_s:.2f}s; first GPU step bit-exact: {exact}")
     del host_layers
 
     if not args.no_extra:
-        result.update(extra_measurements(bl, torch, T, dev0))
+        result.update(extra_measurements(bl, torch, T, dev0, check=not args.no_cpu))
+    if not args.no_cpu:
+        result["cpu_single_core"] = single_core_oracle()
     print(json.dumps(result), flush=True)
+
+
+def single_core_oracle():
+    """The oracle on one thread: in full for the one-token workloads (2560 -> 2560
+    quant + GEMV, the 3B FFN, one 3B stream token), and on a stated slice scaled
+    linearly for prefill (128 of 2048 rows) and the 1.3B 32-token step (one
+    token of 32 through 24 layers and the LM head)."""
+    import oracle
+    olib = oracle.load()
+    prev = oracle.set_threads(0, olib)
+    oracle.set_threads(1, olib)
+    out = {"threads": 1, "cpu_model": cpu_model()}
+    try:
+        d, f = 2560, 10240
+        g = W.rng(W.W_GEMV, 0, W.T_Q)
+        p = oracle.pack(W.ternary(g, d, d), olib)
+        x = W.activations(W.rng(W.W_GEMV, 0, W.T_X), 1, d)
+        t0 = time.perf_counter()
+        q, s, _ = oracle.quant_act(x, None, 1e-5, olib)
+        oracle.bitlinear(p, np.float32(30.0), d, q, s, olib)
+        out["gemv_2560_ms"] = round((time.perf_counter() - t0) * 1e3, 2)
+        gg = [W.rng(W.W_FFN, 0, tid) for tid in (W.T_GATE, W.T_UP, W.T_DOWN)]
+        pk = [oracle.pack(W.ternary(gx, n, k), olib) for gx, (n, k) in zip(gg, ((f, d), (f, d), (d, f)))]
+        xf = W.activations(W.rng(W.W_FFN, 0, W.T_X), 1, d)
+        t0 = time.perf_counter()
+        oracle.ffn(xf, np.ones(d, np.float32), np.ones(f, np.float32), 1e-5, pk[0], 30.0, pk[1], 30.0, pk[2], 30.0,
+                   olib)
+        out["ffn_3b_1token_ms"] = round((time.perf_counter() - t0) * 1e3, 2)
+        layers = []
+        for l in range(32):
+            raw = W.layer_inputs(W.W_STREAM, l, d, f, 1, bench_gains=True)
+            lw = {k: raw[k] for k in ("g_attn", "g_attn_sub", "g_ffn", "g_ffn_sub", "z")}
+            for name, sname in zip(W.LINEAR_NAMES, W.SCALE_NAMES):
+                lw[name] = oracle.pack(raw[name], olib)
+                lw[sname] = raw[sname]
+            layers.append(lw)
+        x0 = W.activations(W.rng(W.W_STREAM, 999, W.T_X), 1, d)
+        t0 = time.perf_counter()
+        oracle.chain(x0, layers, 1e-5, olib)
+        out["stream_3b_1token_s"] = round(time.perf_counter() - t0, 3)
+        del layers
+        M, K, N, rows = 2048, 2560, 10240, 128
+        gp = W.rng(W.W_PREFILL, 0, W.T_GATE)
+        pp = oracle.pack(W.ternary(gp, N, K), olib)
+        xp = W.activations(W.rng(W.W_PREFILL, 0, W.T_X), rows, K, outliers=True)
+        t0 = time.perf_counter()
+        q, s, _ = oracle.quant_act(xp, None, 1e-5, olib)
+        oracle.bitlinear(pp, np.float32(30.0), K, q, s, olib)
+        ts = time.perf_counter() - t0
+        out["prefill_2048x2560x10240_s"] = {"value": round(ts * M / rows, 2), "extrapolated": True,
+                                            "measured": f"{rows} of {M} rows in {ts:.2f} s, scaled by {M // rows}"}
+        cfg = W.BITNET_1P3B
+        d1, f1, V = cfg["dim"], cfg["ffn"], cfg["vocab"]
+        layers = []
+        for l in range(cfg["layers"]):
+            raw = W.layer_inputs(W.W_BATCHED, l, d1, f1, 1, bench_gains=True)
+            lw = {k: raw[k] for k in ("g_attn", "g_attn_sub", "g_ffn", "g_ffn_sub", "z")}
+            for name, sname in zip(W.LINEAR_NAMES, W.SCALE_NAMES):
+                lw[name] = oracle.pack(raw[name], olib)
+                lw[sname] = raw[sname]
+            layers.append(lw)
+        gh = W.rng(W.W_BATCHED, 0, W.T_HEAD)
+        head = oracle.pack(W.ternary(gh, V, d1), olib)
+        x1 = W.activations(W.rng(W.W_BATCHED, 999, W.T_X), 1, d1)
+        t0 = time.perf_counter()
+        xo, _ = oracle.chain(x1, layers, 1e-5, olib)
+        oracle.lm_head_argmax(xo, np.ones(d1, np.float32), 1e-5, head, 30.0, olib)
+        ts = time.perf_counter() - t0
+        out["batched_1p3b_32tokens_s"] = {"value": round(ts * 32, 2), "extrapolated": True,
+                                          "measured": f"1 of 32 tokens in {ts:.2f} s, scaled by 32"}
+    finally:
+        oracle.set_threads(prev, olib)
+    log(f"single-core oracle: {out}")
+    return out
 
 
 def graph_ms(torch, calls, outputs):
@@ -292,7 +435,7 @@ def graph_ms(torch, calls, outputs):
     return t.ms, same
 
 
-def extra_measurements(bl, torch, T, dev0):
+def extra_measurements(bl, torch, T, dev0, check=True):
     out = {}
     # ---- single BitLinear decode GEMV 2560 -> 2560 (quant + GEMV), weights rotated
     # over > 512 MiB of copies so that they stream from HBM, not the 256 MB MALL ----
@@ -333,8 +476,16 @@ def extra_measurements(bl, torch, T, dev0):
             bl.bitlinear_gemv(pw[i], sw, d, d, q1, s1, qs1, 1, None, y1)
     gms2, _ = graph_ms(torch, two_calls, [q1, s1, qs1, y1])
     gms2 /= copies
+    rot = [0]
+
+    def one_fwd():
+        i = rot[0] % copies
+        rot[0] += 1
+        bl.bitlinear_forward(x1, None, 1e-5, pw[i], sw, d, q1, s1, qs1, y1)
+    gemv_stats = per_call_stats(torch, one_fwd, copies)
     out["gemv"] = {"workload": "BitLinear 2560 -> 2560 at 1 token (quant + GEMV, 1,638,400 packed B) through "
                                "bitlinear_forward, weights rotated over 320 copies",
+                   "per_call": gemv_stats,
                    "us_per_call": round(ms * 1e3, 3), "weight_gbs": round(d * d / 4 / (ms * 1e-3) / 1e9, 1),
                    "frac_hbm": round(d * d / 4 / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                    "us_per_call_graph": round(gms * 1e3, 3),
@@ -372,7 +523,16 @@ def extra_measurements(bl, torch, T, dev0):
                           scales[2], None, of, wsf)
     gms, gsame = graph_ms(torch, ffn_calls, [of])
     gms /= fcopies
+    rotf = [0]
+
+    def one_ffn():
+        i = rotf[0] % fcopies
+        rotf[0] += 1
+        bl.bitnet_ffn(xf, 1, d, f, gn, gs, 1e-5, fw[0][i], scales[0], fw[1][i], scales[1], fw[2][i], scales[2],
+                      None, of, wsf)
+    ffn_stats = per_call_stats(torch, one_ffn, 4 * fcopies)
     out["ffn"] = {"workload": "BitNet-3B FFN at 1 token (19,660,800 packed B), weights rotated over 27 copies",
+                  "per_call": ffn_stats,
                   "us_per_call": round(ms * 1e3, 3), "weight_gbs": round(fb / (ms * 1e-3) / 1e9, 1),
                   "frac_hbm": round(fb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                   "us_per_call_graph": round(gms * 1e3, 3), "weight_gbs_graph": round(fb / (gms * 1e-3) / 1e9, 1),
@@ -407,13 +567,35 @@ def extra_measurements(bl, torch, T, dev0):
             bl.bitlinear_gemm(p, sw, N, K, q, s, qs, M, None, y)
     ops = 2.0 * M * N * K
     gemm_ms = tg.ms / iters
+    gemm_stats = per_call_stats(torch, lambda: bl.bitlinear_gemm(p, sw, N, K, q, s, qs, M, None, y), iters)
+    tops = ops / (gemm_ms * 1e-3) / 1e12
     out["prefill"] = {"workload": "quant 2048x2560 fp32 (1% outliers x20) + GEMM vs 10240x2560 ternary -> fp32",
-                      "gemm_ms": round(gemm_ms, 4), "gemm_tops": round(ops / (gemm_ms * 1e-3) / 1e12, 1),
+                      "gemm_ms": round(gemm_ms, 4), "gemm_tops": round(tops, 1),
+                      "gemm_per_call": gemm_stats,
                       "quant_plus_gemm_ms": round(tq.ms / iters, 4),
                       "quant_plus_gemm_tops": round(ops / (tq.ms / iters * 1e-3) / 1e12, 1),
                       "peak_tops": INT8_PEAK_TOPS,
-                      "gemm_frac": round(ops / (gemm_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)}
+                      "gemm_frac": round(tops / INT8_PEAK_TOPS, 4),
+                      "roofline": {"kernel": "gemm_kernel<128x320 tiles> (int8 MFMA 16x16x64)", "bound": "mfma",
+                                   "achieved": round(tops, 1), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
+                                   "frac": round(tops / INT8_PEAK_TOPS, 4), "algorithmic_ops": int(ops),
+                                   "traffic": None}}
     log(f"prefill: GEMM {gemm_ms:.4f} ms = {out['prefill']['gemm_tops']} TOPS")
+    if check:
+        # the timed call's y against the oracle: one random row in every
+        # 128-row block tile, plus the first and last rows, every column
+        import oracle
+        olib = oracle.load()
+        pick = W.rng(W.W_PREFILL, 1, 1)
+        rows = sorted({0, M - 1} | {int(tt * 128 + pick.integers(0, 128)) for tt in range(M // 128)})
+        xh = x.cpu().numpy()[rows]
+        oq, os_, _ = oracle.quant_act(xh, None, 1e-5, olib)
+        oy, _ = oracle.bitlinear(p.cpu().numpy(), sw, K, oq, os_, olib)
+        got = y.cpu().numpy()[rows]
+        err = np.abs(got.astype(np.float64) - oy) / np.maximum(np.abs(oy.astype(np.float64)), 1e-30)
+        out["prefill"]["parity_sampled_rows"] = {"rows": len(rows), "bit_exact": bool(np.array_equal(
+            got.view(np.uint32), oy.view(np.uint32))), "max_rel_err": float(err.max())}
+        log(f"prefill parity on {len(rows)} rows: {out['prefill']['parity_sampled_rows']}")
     del p, x, q, y
 
     # ---- batched decode, 1.3B, 32 tokens, + LM head argmax ----
@@ -446,6 +628,7 @@ def extra_measurements(bl, torch, T, dev0):
             batched_step()
     bytes_b = L * bl.bitnet_layer_bytes(d, f) + V * d // 4
     ms_b = tb.ms / iters
+    batched_stats = per_call_stats(torch, batched_step, iters)
     # x is updated in place, so the eager/graph comparison restarts both from one x
     x_start = xb.clone()
 
@@ -460,7 +643,12 @@ def extra_measurements(bl, torch, T, dev0):
                       "frac_hbm": round(bytes_b / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                       "ms_per_step_graph": round(gms, 4),
                       "weight_gbs_graph": round(bytes_b / (gms * 1e-3) / 1e9, 1),
-                      "graph_matches_eager": gsame}
+                      "graph_matches_eager": gsame, "per_step": batched_stats,
+                      "roofline": {"kernel": "the step's launches (skinny MFMA products, quant, LM head argmax)",
+                                   "bound": "hbm", "achieved": round(bytes_b / (ms_b * 1e-3) / 1e9, 1),
+                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": round(bytes_b / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                   "algorithmic_bytes": bytes_b, "traffic": None}}
     log(f"batched: {ms_b:.4f} ms per 32-token step ({gms:.4f} ms from a graph)")
     del dev, head
     return out

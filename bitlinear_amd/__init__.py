@@ -35,6 +35,7 @@ EXPORTS = (
     "bitlinear_quant_act", "bitlinear_gemv", "bitlinear_forward", "bitlinear_gemm_workspace_bytes", "bitlinear_gemm",
     "bitnet_ffn_workspace_bytes", "bitnet_ffn_workspace_offset", "bitnet_ffn", "bitnet_layer_bytes",
     "bitnet_stream_workspace_bytes", "bitnet_decode_stream",
+    "bitlinear_probe_read", "bitlinear_probe_mfma_ops", "bitlinear_probe_mfma_i8",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -82,6 +83,9 @@ _SIGS = {
     "bitnet_layer_bytes": ([_I64, _I64], _SZ),
     "bitnet_stream_workspace_bytes": ([_I64, _I64, _I64], _SZ),
     "bitnet_decode_stream": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _P, _P, _P, _SZ, _P], _I),
+    "bitlinear_probe_read": ([_P, _SZ, _P, _P], _I),
+    "bitlinear_probe_mfma_ops": ([_I64], _I64),
+    "bitlinear_probe_mfma_i8": ([_I64, _P, _P], _I),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -247,3 +251,20 @@ def ffn_workspace_view(workspace, m, d, f, segment):
     off = bitnet_ffn_workspace_offset(m, d, f, segment)
     nbytes = int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()
     return workspace[off:off + nbytes].view(dtype).view(shape)
+
+
+# ---- roofline probes (measurement tools) -----------------------------------------------
+
+def bitlinear_probe_read(buf, sink, stream=None):
+    """Read every byte of the GPU tensor buf once (the HBM read-stream probe)."""
+    nbytes = buf.numel() * buf.element_size()
+    _check(_lib.bitlinear_probe_read(_dev(buf, None, "buf"), nbytes, _dev(sink, torch.int32, "sink"),
+                                     _stream(stream)), "bitlinear_probe_read")
+    return nbytes
+
+
+def bitlinear_probe_mfma_i8(iters, sink, stream=None):
+    """int8 MFMA-only probe; returns the int8 operations of the call."""
+    _check(_lib.bitlinear_probe_mfma_i8(int(iters), _dev(sink, torch.int32, "sink"), _stream(stream)),
+           "bitlinear_probe_mfma_i8")
+    return _lib.bitlinear_probe_mfma_ops(int(iters))

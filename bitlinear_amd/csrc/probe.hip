@@ -1,0 +1,123 @@
+// probe.hip -- roofline probes: the measured ceilings that the benchmark
+// reports beside the nominal MI355X peaks (8 TB/s HBM, 5.0 POP/s dense int8).
+//
+//   read probe: every byte of a caller buffer is read once with 16-byte loads,
+//     eight loads in flight per thread, two 1024-thread workgroups per CU;
+//     the loaded words are folded into one word per workgroup and
+//     xor-ed into a sink, so the loads cannot be dropped.
+//   MFMA probe: waves that issue only v_mfma_i32_16x16x64_i8 on register
+//     operands, eight independent accumulators per wave (enough to cover the
+//     instruction's latency), two waves per SIMD on every CU.
+// Neither touches anything but its arguments; both are plain launches on the
+// caller's stream.
+#include <algorithm>
+
+#include "internal.h"
+#include "ternary.h"
+
+namespace bl {
+namespace {
+
+constexpr int kReadThreads = 1024;
+constexpr int kReadUnroll = 8;
+
+__global__ __launch_bounds__(kReadThreads) void read_probe_kernel(const uint4* __restrict__ p, uint64_t n16,
+                                                                  uint32_t* sink)
+{
+    const uint64_t stride = (uint64_t)gridDim.x * kReadThreads;
+    uint64_t i = (uint64_t)blockIdx.x * kReadThreads + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + (kReadUnroll - 1) * stride < n16; i += kReadUnroll * stride) {
+        uint4 v[kReadUnroll];
+#pragma unroll
+        for (int u = 0; u < kReadUnroll; ++u) v[u] = p[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < kReadUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < n16; i += stride) {
+        const uint4 v = p[i];
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    // fold the workgroup into one word
+    for (int off = 32; off >= 1; off >>= 1) acc ^= __shfl_xor(acc, off, 64);
+    __shared__ uint32_t part[kReadThreads / 64];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t t = 0;
+        for (int w = 0; w < kReadThreads / 64; ++w) t ^= part[w];
+        atomicXor(sink, t);
+    }
+}
+
+constexpr int kMfmaThreads = 256;
+constexpr int kMfmaChains = 8;
+
+__global__ __launch_bounds__(kMfmaThreads) void mfma_probe_kernel(int64_t iters, uint32_t* sink)
+{
+    const int lane = threadIdx.x & 63;
+    v4i a = {lane, lane * 3, lane * 5, lane * 7};
+    v4i b = {lane ^ 1, lane ^ 2, lane ^ 3, lane ^ 4};
+    v4i c[kMfmaChains];
+#pragma unroll
+    for (int j = 0; j < kMfmaChains; ++j) c[j] = v4i{j, 0, 0, 0};
+    for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < kMfmaChains; ++j) c[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c[j], 0, 0, 0);
+    }
+    uint32_t acc = 0;
+#pragma unroll
+    for (int j = 0; j < kMfmaChains; ++j) acc ^= (uint32_t)(c[j][0] ^ c[j][1] ^ c[j][2] ^ c[j][3]);
+    if (acc == 0x9e3779b9u) atomicXor(sink, acc);  // practically never taken; keeps the chain alive
+}
+
+int cu_count()
+{
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    return cus;
+}
+
+}  // namespace
+}  // namespace bl
+
+extern "C" {
+
+int bitlinear_probe_read(const void* buf, size_t bytes, uint32_t* sink, void* stream)
+{
+    if (!buf || !sink) return BL_ERR_NULL;
+    if (bytes == 0 || bytes % 16 != 0) return BL_ERR_SHAPE;
+    if (!bl::aligned(buf, 16) || !bl::aligned(sink, 4)) return BL_ERR_ALIGN;
+    const int cus = bl::cu_count();
+    if (cus <= 0) return BL_ERR_DEVICE;
+    const uint64_t n16 = bytes / 16;
+    // two 1024-thread workgroups per CU, but no more workgroups than 16-byte words
+    const uint64_t want = (uint64_t)cus * 2;
+    const uint64_t grid = std::min<uint64_t>(want, (n16 + bl::kReadThreads - 1) / bl::kReadThreads);
+    bl::read_probe_kernel<<<(unsigned)grid, bl::kReadThreads, 0, reinterpret_cast<hipStream_t>(stream)>>>(
+        static_cast<const uint4*>(buf), n16, sink);
+    return hipGetLastError() == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
+}
+
+int64_t bitlinear_probe_mfma_ops(int64_t iters)
+{
+    const int cus = bl::cu_count();
+    if (iters <= 0 || cus <= 0) return 0;
+    // waves x MFMAs per wave x (16 x 16 x 64 multiply-adds = 32768 ops)
+    return (int64_t)cus * 8 * iters * bl::kMfmaChains * 32768;
+}
+
+int bitlinear_probe_mfma_i8(int64_t iters, uint32_t* sink, void* stream)
+{
+    if (!sink) return BL_ERR_NULL;
+    if (iters <= 0 || iters > ((int64_t)1 << 40)) return BL_ERR_SHAPE;
+    if (!bl::aligned(sink, 4)) return BL_ERR_ALIGN;
+    const int cus = bl::cu_count();
+    if (cus <= 0) return BL_ERR_DEVICE;
+    // two waves per SIMD: 8 waves per CU, as 2 workgroups of 4 waves
+    bl::mfma_probe_kernel<<<cus * 2, bl::kMfmaThreads, 0, reinterpret_cast<hipStream_t>(stream)>>>(iters, sink);
+    return hipGetLastError() == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -65,9 +65,10 @@
 // The P2/P4 rows of a workgroup are the same, so the residual x of its rows
 // stays in registers across the whole stream.
 //
-// Termination: every wait is bounded by a wall-clock limit (s_memrealtime,
-// 100 MHz) and by a shared status word; a workgroup that gives up sets the
-// status, every other one sees it and leaves, so the grid always drains.
+// Termination: every wait is bounded by a wall-clock limit of 2 s from the
+// start of that wait (s_memrealtime, 100 MHz) and by a shared status word; a
+// workgroup that gives up sets the status, every other one sees it and leaves,
+// so the grid always drains.
 #include "internal.h"
 #include "prefetch.h"
 #include "wave.h"
@@ -155,13 +156,14 @@ __device__ __forceinline__ uint32_t status_load(const uint32_t* ctrl)
 
 // Loads the words k = t, t + 512, ... < N of buf until every one carries epoch
 // e (all loads of a round are issued before any is checked); v receives the
-// fp32 payloads. Returns false, for the whole workgroup, on a timeout or when
-// another workgroup gave up.
+// fp32 payloads. Returns false, for the whole workgroup, on a timeout (2 s from
+// the start of this wait) or when another workgroup gave up.
 template <int N, int STRIDE = 1>
-__device__ bool poll_vec(const unsigned long long* buf, uint32_t e, float* v, uint32_t* ctrl, long long t_start)
+__device__ bool poll_vec(const unsigned long long* buf, uint32_t e, float* v, uint32_t* ctrl)
 {
     constexpr int NI = cdiv(N, kT);
     const int t = threadIdx.x;
+    const long long t_start = (long long)__builtin_amdgcn_s_memrealtime();
     unsigned long long w[NI];
     bool failed = false;
     for (int spin = 0;; ++spin) {
@@ -191,10 +193,11 @@ __device__ bool poll_vec(const unsigned long long* buf, uint32_t e, float* v, ui
 
 // As poll_vec for a published fp32 vector: repeats until no word reads 0.
 template <int N>
-__device__ bool poll_val(const uint32_t* buf, float* v, uint32_t* ctrl, long long t_start)
+__device__ bool poll_val(const uint32_t* buf, float* v, uint32_t* ctrl)
 {
     constexpr int NI = cdiv(N, kT);
     const int t = threadIdx.x;
+    const long long t_start = (long long)__builtin_amdgcn_s_memrealtime();
     uint32_t w[NI];
     bool failed = false;
     for (int spin = 0;; ++spin) {
@@ -407,7 +410,6 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
 
     __shared__ Shared sh;
     const int w = blockIdx.x, t = threadIdx.x;
-    const long long t_start = (long long)__builtin_amdgcn_s_memrealtime();
 
     const uint32_t base = __hip_atomic_load(a.ctrl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (status_load(a.ctrl) != 0) return;  // a failed call left stale flags: the workspace must be re-zeroed
@@ -495,7 +497,7 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
             float v[ND];
             if (l == 0) {
                 load_strided<D>(a.x, v);
-            } else if (!poll_val<D>(xa_in, v, a.ctrl, t_start)) {
+            } else if (!poll_val<D>(xa_in, v, a.ctrl)) {
                 return;
             }
             norm_quant<D>(v, g1, a.eps, sh, s_a, qsum);
@@ -515,7 +517,7 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
             if (t < S2::R) sh.acc[t] = 0;
             float fl[1];
             fetch2(l);
-            if (!poll_vec<kGrid, kFlagStride>(a.done, E + 1, fl, a.ctrl, t_start)) return;
+            if (!poll_vec<kGrid, kFlagStride>(a.done, E + 1, fl, a.ctrl)) return;
             pf3(l);
             if (l == 0 && w == 0 && t == 0)  // every workgroup has read the base by now
                 __hip_atomic_store(a.ctrl, base + 4u * (uint32_t)a.n_layers, __ATOMIC_RELAXED,
@@ -538,7 +540,7 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
             }
             fetch3(l);
             float v[ND];
-            if (!poll_val<D>(xb_cur, v, a.ctrl, t_start)) return;
+            if (!poll_val<D>(xb_cur, v, a.ctrl)) return;
             pf4(l);
             if (l + 1 < a.n_layers) pf1o(l + 1);
             norm_quant<D>(v, g3, a.eps, sh, s_a, qsum);
@@ -558,7 +560,7 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
             if (t < S4::R) sh.acc[t] = 0;
             fetch4(l);
             float v[NF];
-            if (!poll_val<F>(hh_cur, v, a.ctrl, t_start)) return;
+            if (!poll_val<F>(hh_cur, v, a.ctrl)) return;
             if (l + 1 < a.n_layers) pf1q(l + 1);
             norm_quant<F>(v, g4, a.eps, sh, s_a, qsum);
             dots<S4>(w4, sh.q, sh.zero, sh.acc);

@@ -1,8 +1,10 @@
 // ternary.h -- operand helpers shared by the int8 MFMA kernels.
 //
 // Packed ternary weights hold four 2-bit codes c = t + 1 per byte, weight i of
-// a row at bits 2 (i % 4) of byte i / 4 ("Memory Layout", Hesper API; the
-// TQ2_0 packing of candle PR 2664). A dword holds weights 0..15 of a 16-run.
+// a row at bits 2 (i % 4) of byte i / 4. The pages give TQ2_0 only its name and
+// its size of 0.25 byte per weight ("BitNet Model - Complete Inference
+// Pipeline", section "Memory Footprint (BitNet-3B with TQ2_0)"); this layout is
+// the one the ABI header states. A dword holds weights 0..15 of a 16-run.
 #pragma once
 
 #include <hip/hip_runtime.h>

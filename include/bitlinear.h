@@ -27,14 +27,20 @@
  *             multiply codes c = t + 1 and subtract act_sum).
  *
  * Numerics (identical on every entry point):
- *   RMSNorm  r = fl32(1 / sqrt(ss/k + eps)) in fp64, ss = fp64 sum of x^2 in a
- *            fixed order (256 strided partials, then an xor-butterfly over the
- *            partials with offsets 128, 64, ..., 1); y = fl32(fl32(x * r) * g).
+ *   RMSNorm  ss = fp64 sum of x^2 in one fixed order: 512 strided partials
+ *            (partial l sums x[i]^2 for i = l, l + 512, l + 1024, ... in
+ *            ascending i), then an xor-butterfly over the 512 partials with
+ *            offsets 1, 2, 4, ..., 256 in that ascending order (at each offset
+ *            every partial l becomes p[l] + p[l ^ offset]); ss = p[0].
+ *            Then, each step rounded in fp64: w = 1 / sqrt(ss / k + eps),
+ *            r = fl32(w); y = fl32(fl32(x * r) * g).
  *   quant    s_a = fl32(127 / max(absmax(y), 1e-5)); q = clamp(rne(fl32(y*s_a)),
  *            -128, 127) with round-half-to-even.
- *   dequant  inv = fl32(1 / fl32(s_a * s_w)); y = fl32((float)acc * inv);
+ *   dequant  p = fl32(s_a * s_w); inv = fl32(1 / p); y = fl32((float)acc * inv);
  *            with a residual: y = fl32(residual + fl32((float)acc * inv)).
- *   FFN      h = fl32(fl32(relu(gate)^2) * up).
+ *   FFN      g = max(gate, 0); h = fl32(fl32(g * g) * up).
+ *   Every fp32 / fp64 operation above rounds on its own (no fused multiply-add),
+ *   and division and square root are correctly rounded.
  *
  * Conventions:
  *   - Every pointer marked "device" is caller-owned device memory (for example
@@ -100,12 +106,20 @@ int bitlinear_weight_quant(const float *w, int64_t n, int64_t k, int8_t *t, floa
  *   eps       : RMSNorm epsilon (ignored when gain is NULL), widened to fp64.
  *   q         : device int8 [m][k]; act_scale : device fp32 [m];
  *   act_sum   : device int32 [m] or NULL.
- * One workgroup per token. Errors: NULL, SHAPE (m, k <= 0, k % 64 != 0),
- * ALIGN, LAUNCH. Non-finite x is out of contract (results unspecified). */
+ * Launch forms (results are identical): from 256 tokens on, one wave per token
+ * with the row in registers (k <= 4096 with a gain, k <= 8192 without); else
+ * one 512-thread workgroup per token, the row in registers up to k = 16384 and
+ * read three times (sum of squares, absmax, codes) above that.
+ * Errors: NULL, SHAPE (m, k <= 0, k % 64 != 0), ALIGN, LAUNCH. Non-finite x is
+ * out of contract (results unspecified). */
 int bitlinear_quant_act(const float *x, const float *gain, float eps, int64_t m, int64_t k,
                         int8_t *q, float *act_scale, int32_t *act_sum, void *stream);
 
-/* Decode GEMV, m in [1, 8]: y[m][n] = [residual +] dequant(P . q).
+/* Decode GEMV, m in [1, 8]: y[m][n] = [residual +] dequant(P . q). At decode
+ * the time goes into the layers' BitLinear weights ("BitNet Model - Complete
+ * Inference Pipeline", Hesper API, section "Performance (BitNet-3B on A100)";
+ * the per-layer weights of "Transformer Block", section "Memory Layout"), so
+ * this product is a stream of the packed weights.
  *   packed    : device uint8 [n][k/4], 16-byte aligned.
  *   w_scale   : the tensor's s_w (> 0).
  *   q, act_scale, act_sum : from bitlinear_quant_act (act_sum is required).
@@ -123,8 +137,9 @@ int bitlinear_gemv(const uint8_t *packed, float w_scale, int64_t n, int64_t k,
 /* Decode BitLinear in one call, m in [1, 8]: y[m][n] = dequant(P . quant([RMSNorm](x))),
  * the composition of bitlinear_quant_act and bitlinear_gemv (no residual), with the same
  * results bit for bit. A BitLinear applied to a token: the layer of the pages'
- * "BitLinear" (candle PR 2664 "Add Support for BitNet Architecture Inference": norm,
- * activation_quant, ternary matmul, one rescale; [BN] "Transformer Block" forward pass).
+ * "BitLinear" ("Add Support for BitNet Architecture Inference", candle PR 2664: an
+ * RMSNorm before the BitLinear, activation_quant, ternary matmul, one rescale; and
+ * "Transformer Block", Hesper API, section "Forward Pass").
  *   x, gain, eps : as bitlinear_quant_act (x [m][k], gain [k] or NULL).
  *   packed, w_scale, n, k : as bitlinear_gemv.
  *   q, act_scale, act_sum : device int8 [m][k], fp32 [m], int32 [m], caller-allocated; they
@@ -147,6 +162,12 @@ size_t bitlinear_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int with_
 
 /* GEMM on int8 matrix cores (prefill, batched decode, ternary LM head):
  * y[m][n] = [residual +] dequant(q . P^T), optional fused per-row argmax.
+ * The prefill product is the "Tiled matmul" step of "BitNet Model - Complete
+ * Inference Pipeline" (section "Performance (BitNet-3B on A100)", "With
+ * optimizations"); the LM head projects to the vocabulary ("Architecture"), and
+ * row_argmax is the greedy choice of "Text Generation / Greedy Decoding" done
+ * on the device as the page's "GPU Argmax" does (argmaxKernel, gpuArgmax: only
+ * the index comes back).
  *   packed, w_scale, q, act_scale, act_sum : as bitlinear_gemv; any m >= 1.
  *   residual   : device fp32 [m][n] or NULL (may alias y).
  *   y          : device fp32 [m][n], or NULL when row_argmax is given (logits
@@ -249,7 +270,8 @@ int bitnet_ffn(const float *x, int64_t m, int64_t d, int64_t f,
  * whole stream runs as one persistent kernel, one workgroup per CU, that hands
  * each step's output vector to the next step through flag-tagged words in the
  * workspace.
- * Every wait in it is bounded (2 s); on a timeout the kernel stops early and
+ * Every wait in it is bounded (2 s from the start of that wait, so the bound
+ * does not grow with n_layers); on a timeout the kernel stops early and
  * sets status = 1 (status = 2: the phase counter is exhausted after about 2^31
  * steps). A nonzero status stays set, and further calls do nothing, until the
  * workspace is zero-filled again; the caller reads it after synchronising.
@@ -263,6 +285,26 @@ size_t bitnet_stream_workspace_bytes(int64_t m, int64_t d, int64_t f);
 int bitnet_decode_stream(const uint8_t *weights, const float *scales, const float *gains, const float *z,
                          int64_t n_layers, int64_t m, int64_t d, int64_t f, float eps,
                          float *x, float *qkv, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------- roofline probes --- */
+/* Measurement tools, not part of the method: they give the measured ceilings
+ * that throughput is reported against next to the nominal MI355X peaks.
+ *
+ * bitlinear_probe_read: reads every byte of buf once (16-byte loads, eight in
+ * flight per thread, two 1024-thread workgroups per CU) and xors a fold of
+ * the data into *sink (device uint32). Bytes read = bytes.
+ *   buf : device, 16-byte aligned; bytes : > 0, a multiple of 16.
+ * Errors: NULL, SHAPE, ALIGN, DEVICE, LAUNCH. */
+int bitlinear_probe_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+
+/* bitlinear_probe_mfma_i8: every wave (two per SIMD on every CU) issues
+ * iters x 8 independent v_mfma_i32_16x16x64_i8 on register operands and
+ * nothing else; *sink (device uint32) is touched only to keep the results
+ * alive. bitlinear_probe_mfma_ops(iters) is the number of int8 operations
+ * (2 per multiply-add) one call performs on the current device (0 on error).
+ * Errors: NULL, SHAPE (iters <= 0 or > 2^40), ALIGN, DEVICE, LAUNCH. */
+int64_t bitlinear_probe_mfma_ops(int64_t iters);
+int bitlinear_probe_mfma_i8(int64_t iters, uint32_t *sink, void *stream);
 
 #ifdef __cplusplus
 }

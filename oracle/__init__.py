@@ -60,9 +60,17 @@ def load(path=None):
     lib.ref_residual_add.argtypes = [_f32p, _f32p, _i64]
     lib.ref_residual_add.restype = None
     lib.ref_argmax_rows.argtypes = [_i32p, _i64, _i64, _i32p]
+    lib.ref_set_threads.argtypes = [ctypes.c_int]
+    lib.ref_set_threads.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
+
+
+def set_threads(n, lib=None):
+    """Threads of the oracle's row-parallel loops (n <= 0: unchanged); returns the setting."""
+    lib = lib or load()
+    return int(lib.ref_set_threads(int(n)))
 
 
 def _ptr(a, ty):

@@ -45,6 +45,9 @@
  * rows/tokens; every result is the same for any thread count).
  */
 #include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -53,6 +56,19 @@
 #define ORACLE_PARTIALS 512
 
 int ref_abi_version(void) { return 1; }
+
+/* Threads of the row-parallel loops (OpenMP); results do not depend on it.
+ * n <= 0 leaves the current setting. Returns the setting in effect. */
+int ref_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
+}
 
 /* ------------------------------------------------------------------------ */
 /* weight_quant ([CA] weight_quant; absmean ternary rounding of the b1.58

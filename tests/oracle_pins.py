@@ -640,4 +640,157 @@ def pin_chain_residual(o, lib):
     assert np.allclose(x2[0] - x[0], yo, rtol=1e-5, atol=1e-6)
 
 
+# --- floating-point operation order, derived with exact rational arithmetic -------------
+#
+# The pages fix no fp32 operation order, so the oracle states one (the numerics
+# contract of the ABI header, the same readings on both sides). The pins below
+# derive the bits that order must give with exact rational arithmetic and one
+# explicit IEEE rounding per operation (tests/exact_fp.py, no floating-point
+# hardware), on inputs where the plausible other orders round differently. Each
+# pin also checks that its inputs tell the stated order from those others, so it
+# cannot pass by accident on inputs where every order agrees.
+
+def _differs(counts, name, got, want):
+    if got != want:
+        counts[name] = counts.get(name, 0) + 1
+
+
+def _require_discrimination(counts, names, what):
+    missing = [n for n in names if counts.get(n, 0) == 0]
+    assert not missing, f"{what}: the inputs do not tell the stated order from {missing}"
+
+
+def pin_dequant_order_exact(o, lib):
+    """Dequant rounds three times, in this order: p = fl32(s_a * s_w),
+    inv = fl32(1 / p), y = fl32(acc * inv). Seeded accumulators over the whole
+    int32 range a BitLinear reaches (|acc| <= 127 * 10240) and scales of the
+    sizes the path sees; expected bits from exact rationals. Ruled out by the
+    same inputs: acc / p, acc * fl32(fl32(1/s_a) * fl32(1/s_w)), and an inverse
+    taken from the exact product fl32(1 / (s_a s_w))."""
+    from exact_fp import f32, fl32
+    g = _rng(81)
+    m, n = 48, 12
+    counts = {}
+    for s_w in (np.float32(23.75), np.float32(g.uniform(20, 60)), np.float32(g.uniform(20, 60))):
+        acc = g.integers(-1_300_480, 1_300_481, (m, n)).astype(np.int32)
+        s_a = g.uniform(0.5, 400.0, m).astype(np.float32)
+        y = o.dequant(acc, s_a, s_w, lib)
+        sw = f32(s_w)
+        for r in range(m):
+            sa = f32(s_a[r])
+            p = fl32(sa * sw)
+            inv = fl32(1 / p)
+            inv_split = fl32(fl32(1 / sa) * fl32(1 / sw))
+            inv_exact = fl32(1 / (sa * sw))
+            for c in range(n):
+                a = Fraction(int(acc[r, c]))
+                want = fl32(a * inv)
+                assert Fraction(float(y[r, c])) == want, (r, c, float(y[r, c]), float(want))
+                _differs(counts, "acc / p", fl32(a / p), want)
+                _differs(counts, "(1/s_a)(1/s_w)", fl32(a * inv_split), want)
+                _differs(counts, "1/(s_a s_w) exact", fl32(a * inv_exact), want)
+    _require_discrimination(counts, ("acc / p", "(1/s_a)(1/s_w)", "1/(s_a s_w) exact"), "dequant")
+
+
+def pin_rmsnorm_apply_exact(o, lib):
+    """RMSNorm: w = fl64(1 / fl64(sqrt(fl64(fl64(ss / K) + eps)))), r = fl32(w),
+    y = fl32(fl32(x * r) * g). The inputs have at most 12 significant bits, so
+    every x^2 and their sum are exact in fp64 whatever the summation order, and
+    ss is the exact sum of squares; every other step is derived with one exact
+    IEEE rounding. Ruled out by the same inputs: x * fl32(r * g), one rounding
+    of the exact x r g, and x * w taken before r is rounded to fp32."""
+    from exact_fp import f32, fl32, fl64, sqrt64
+    g = _rng(82)
+    counts = {}
+    for k, eps in ((64, 1e-5), (640, 1e-6), (1024, 0.0), (96, 0.25)):
+        x = (g.integers(-2047, 2048, (3, k)) / 256.0).astype(np.float32)
+        gain = g.uniform(0.5, 1.5, k).astype(np.float32)
+        y = o.rmsnorm(x, gain, eps, lib)
+        eps_q = f32(np.float32(eps))
+        for row in range(3):
+            ss = sum(f32(v) ** 2 for v in x[row])
+            assert fl64(ss) == ss
+            w = fl64(1 / sqrt64(fl64(fl64(ss / k) + eps_q)))
+            r = fl32(w)
+            for i in range(k):
+                xi, gi = f32(x[row, i]), f32(gain[i])
+                want = fl32(fl32(xi * r) * gi)
+                assert Fraction(float(y[row, i])) == want, (k, row, i)
+                _differs(counts, "x (r g)", fl32(xi * fl32(r * gi)), want)
+                _differs(counts, "x r g rounded once", fl32(xi * r * gi), want)
+                _differs(counts, "x w before rounding r", fl32(fl32(xi * w) * gi), want)
+    _require_discrimination(counts, ("x (r g)", "x r g rounded once", "x w before rounding r"), "rmsnorm")
+
+
+def pin_quant_order_exact(o, lib):
+    """activation_quant: s_a = fl32(127 / absmax), v = fl32(y * s_a),
+    q = rne(v). Rows hold values placed within a few fp32 ulps of a half-integer
+    step y s_a = j + 1/2, where the order of roundings decides the code. Expected
+    codes from exact rationals. Ruled out by the same rows: fl32(fl32(y / absmax)
+    * 127), rounding the exact product y s_a, and a product with the fp64 scale
+    127 / absmax (unrounded to fp32)."""
+    from exact_fp import f32, fl32, fl64, rne_int
+    g = _rng(83)
+    counts = {}
+    for amax in (np.float32(1.0), np.float32(g.uniform(0.3, 30)), np.float32(g.uniform(0.3, 30)),
+                 np.float32(g.uniform(0.3, 30)), np.float32(g.uniform(30, 3000))):
+        A = f32(amax)
+        s_a = fl32(Fraction(127) / A)
+        vals = [float(amax)]
+        for _ in range(60):
+            j = int(g.integers(0, 126))
+            sign = 1 if g.random() < 0.5 else -1
+            y0 = np.float32(float(Fraction(2 * j + 1, 2) / s_a)) * np.float32(sign)
+            for step in range(-2, 3):
+                v = y0
+                for _ in range(abs(step)):
+                    v = np.nextafter(v, np.float32(np.inf) if step > 0 else np.float32(-np.inf))
+                if abs(float(v)) < float(amax):
+                    vals.append(float(v))
+        row = np.array(vals, np.float32).reshape(1, -1)
+        q, s, _ = o.activation_quant(row, lib)
+        assert Fraction(float(s[0])) == s_a
+        for i, v in enumerate(row[0]):
+            y = f32(v)
+            want = max(-128, min(127, rne_int(fl32(y * s_a))))
+            assert int(q[0, i]) == want, (float(amax), i, float(v), int(q[0, i]), want)
+            _differs(counts, "y / absmax * 127", max(-128, min(127, rne_int(fl32(fl32(y / A) * 127)))), want)
+            _differs(counts, "exact y s_a", max(-128, min(127, rne_int(y * s_a))), want)
+            _differs(counts, "fp64 scale", max(-128, min(127, rne_int(fl32(fl64(y * fl64(Fraction(127) / A)))))),
+                     want)
+    _require_discrimination(counts, ("y / absmax * 127", "exact y s_a", "fp64 scale"), "activation_quant")
+
+
+def pin_relu2_order_exact(o, lib):
+    """The FFN gating rounds twice, square first: h = fl32(fl32(g g) * up) with
+    g = max(gate, 0). Expected bits from exact rationals on seeded gate / up
+    values. Ruled out by the same inputs: fl32(fl32(g up) g) and one rounding of
+    the exact g^2 up."""
+    from exact_fp import f32, fl32
+    g = _rng(84)
+    gate = (g.standard_normal(600) * 3).astype(np.float32)
+    up = (g.standard_normal(600) * 3).astype(np.float32)
+    h = o.relu2_mul(gate, up, lib)
+    counts = {}
+    for i in range(gate.size):
+        gg = max(f32(gate[i]), Fraction(0))
+        u = f32(up[i])
+        want = fl32(fl32(gg * gg) * u)
+        assert Fraction(float(h[i])) == want, (i, float(gate[i]), float(up[i]))
+        _differs(counts, "(g up) g", fl32(fl32(gg * u) * gg), want)
+        _differs(counts, "g^2 up rounded once", fl32(gg * gg * u), want)
+    _require_discrimination(counts, ("(g up) g", "g^2 up rounded once"), "relu2_mul")
+
+
+def pin_residual_exact(o, lib):
+    """The residual add is one fp32 addition: x + d rounded once."""
+    from exact_fp import f32, fl32
+    g = _rng(85)
+    x = (g.standard_normal(300) * 10).astype(np.float32)
+    d = (g.standard_normal(300) * 1e-3).astype(np.float32)
+    out = o.residual_add(x, d, lib)
+    for i in range(x.size):
+        assert Fraction(float(out[i])) == fl32(f32(x[i]) + f32(d[i])), i
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

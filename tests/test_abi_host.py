@@ -236,3 +236,20 @@ def test_stream_checks():
     assert f(A, A, A, A, 0, m, d, ff, 1e-5, A, None, A, need, S) == bl.BL_ERR_SHAPE
     assert f(A, A, A, A, 2, m, 80, ff, 1e-5, A, None, A, need, S) == bl.BL_ERR_SHAPE
     assert f(A + 8, A, A, A, 2, m, d, ff, 1e-5, A, None, A, need, S) == bl.BL_ERR_ALIGN
+
+
+def test_header_states_the_oracle_partial_order():
+    """The numerics contract of the header names the same RMSNorm summation
+    order as the oracle: the partial count, and ascending butterfly offsets
+    from 1 up to half the partial count."""
+    text = re.sub(r"\s+", " ", open(HEADER).read())
+    m = re.search(r"(\d+) strided partials", text)
+    assert m, "the header does not state the partial count"
+    header_partials = int(m.group(1))
+    src = open(os.path.join(ROOT, "oracle", "bitlinear_oracle.c")).read()
+    oracle_partials = int(re.search(r"#define ORACLE_PARTIALS (\d+)", src).group(1))
+    assert header_partials == oracle_partials
+    m = re.search(r"offsets 1, 2, 4, \.\.\., (\d+) in that ascending order", text)
+    assert m, "the header does not state ascending butterfly offsets"
+    assert int(m.group(1)) == oracle_partials // 2
+    assert "for (int off = 1; off < ORACLE_PARTIALS; off *= 2)" in src

@@ -218,10 +218,11 @@ def test_gemm(bl, olib, m, n, k):
 def test_gemm_prefill_full_size_sampled_rows(bl, olib):
     """The prefill product at the benchmark's size and launch configuration
     (2048 tokens x K = 2560 -> N = 10240, 128 x 320 block tiles, activations with
-    1 % outliers x20): the quant of all rows against the oracle, then the exact
-    int32 accumulators and the outputs of 24 rows -- the first and last of
-    block tiles and halves, and random ones -- against the oracle's product of
-    those rows, every column."""
+    1 % outliers x20). The quant of all rows is checked against the oracle. Then
+    the call the benchmark times -- y only, no residual, accumulators or argmax,
+    so every tile takes the branch-free epilogue -- is checked on sampled rows
+    (at least one in every 128-row block tile, plus tile and half edges), every
+    column; a second call that also writes the accumulators checks them exactly."""
     import torch
     m, k, n = 2048, 2560, 10240
     log(f"gemm full size m={m} n={n} k={k}")
@@ -239,15 +240,45 @@ def test_gemm_prefill_full_size_sampled_rows(bl, olib):
     assert_exact(to_host(q), oq, "q")
     assert_exact(to_host(s).view(np.uint32), os_.view(np.uint32), "act_scale bits")
     assert_exact(to_host(qs), oqs, "act_sum")
-    y = torch.empty((m, n), dtype=torch.float32, device=dev)
-    acc = torch.empty((m, n), dtype=torch.int32, device=dev)
-    bl.bitlinear_gemm(to_dev(p), sw, n, k, q, s, qs, m, None, y, acc, None, None)
-    rows = sorted(set([0, 1, 63, 64, 127, 128, 129, 1023, 1024, 1151, 2046, 2047] +
-                      list(W.rng(103, 1, 1).choice(m, 12, replace=False))))
+    pick = W.rng(103, 1, 1)
+    rows = set([0, 1, 63, 64, 127, 128, 129, 1023, 1024, 1151, 2046, 2047])
+    rows |= {int(tile * 128 + pick.integers(0, 128)) for tile in range(m // 128)}
+    rows = sorted(rows)
     oy, oacc = oracle.bitlinear(p, sw, k, oq[rows], os_[rows], olib)
-    ya, acca = to_host(y), to_host(acc)
+    pd = to_dev(p)
+    y = torch.full((m, n), float("nan"), dtype=torch.float32, device=dev)
+    bl.bitlinear_gemm(pd, sw, n, k, q, s, qs, m, None, y)
+    assert_f32(to_host(y)[rows], oy, "y, y-only call (sampled rows)")
+    y2 = torch.empty((m, n), dtype=torch.float32, device=dev)
+    acc = torch.empty((m, n), dtype=torch.int32, device=dev)
+    bl.bitlinear_gemm(pd, sw, n, k, q, s, qs, m, None, y2, acc, None, None)
+    acca = to_host(acc)
     assert_exact(acca[rows], oacc, "acc (sampled rows)")
-    assert_f32(ya[rows], oy, "y (sampled rows)")
+    assert_f32(to_host(y2)[rows], oy, "y with acc (sampled rows)")
+    assert_exact(to_host(y2).view(np.uint32), to_host(y).view(np.uint32), "y-only call == general call, all rows")
+
+
+# (m, n, k): tiles that all take the branch-free y-only epilogue, and ragged
+# shapes where interior tiles take it and edge tiles the general one, for both
+# block-tile configurations (m <= 64 and m > 64).
+GEMM_Y_ONLY_CASES = [(256, 640, 256), (300, 1000, 320), (129, 330, 2560), (64, 512, 128), (65, 700, 192),
+                     (40, 257, 64), (2048, 640, 64)]
+
+
+@pytest.mark.parametrize("m,n,k", GEMM_Y_ONLY_CASES)
+def test_gemm_y_only(bl, olib, m, n, k):
+    import torch
+    log(f"gemm y-only m={m} n={n} k={k}")
+    g = W.rng(106, m + n, k)
+    t = W.ternary(g, n, k)
+    sw = W.weight_scale(g)
+    x = W.activations(g, m, k, outliers=True)
+    p = pack_both(t, olib)
+    q, s, qs = oracle.quant_act(x, None, 1e-5, olib)
+    y = torch.full((m, n), float("nan"), dtype=torch.float32, device=torch_dev())
+    bl.bitlinear_gemm(to_dev(p), sw, n, k, to_dev(q), to_dev(s), to_dev(qs), m, None, y)
+    oy, _ = oracle.bitlinear(p, sw, k, q, s, olib)
+    assert_f32(to_host(y), oy, "y")
 
 
 @pytest.mark.parametrize("m", [7, 40])

@@ -50,7 +50,30 @@ C_MUTANTS = [
     ("relu_missing", "float g = gate[i] > 0.0f ? gate[i] : 0.0f;", "float g = gate[i];"),
     ("argmax_last_tie", "if (a[col] > a[best]) best = col;", "if (a[col] >= a[best]) best = col;"),
     ("residual_sub", "x[i] = x[i] + d[i];", "x[i] = x[i] - d[i];"),
+    # floating-point operation order (caught by the exact-rational pins)
+    ("dq_recip_product", "float inv = 1.0f / prod;", "float inv = (1.0f / s_a[row]) * (1.0f / s_w);"),
+    ("dq_divide", "y[row * n + col] = (float)acc[row * n + col] * inv;",
+     "y[row * n + col] = (float)acc[row * n + col] / prod;"),
+    ("dq_inv_fp64", "float inv = 1.0f / prod;", "float inv = (float)(1.0 / ((double)s_a[row] * (double)s_w));"),
+    ("rms_r_times_g", "float a = xr[i] * r;\n            y[row * k + i] = a * g[i];",
+     "y[row * k + i] = xr[i] * (r * g[i]);"),
+    ("rms_xr_fp64", "float a = xr[i] * r;", "float a = (float)((double)xr[i] * r64);"),
+    ("rms_apply_fp64", "float a = xr[i] * r;\n            y[row * k + i] = a * g[i];",
+     "y[row * k + i] = (float)((double)xr[i] * (double)r * (double)g[i]);"),
+    ("relu2_order", "float g2 = g * g;\n        h[i] = g2 * up[i];", "h[i] = (g * up[i]) * g;"),
+    ("relu2_fp64", "float g2 = g * g;\n        h[i] = g2 * up[i];", "h[i] = (float)((double)g * g * up[i]);"),
+    ("aq_scale_fp64_in_product", "float v = yr[i] * scale;",
+     "float v = (float)((double)yr[i] * (127.0 / (double)(amax > floor_ ? amax : floor_)));"),
+    ("aq_round_exact_product", "float r = nearbyintf(v);\n            if (r > 127.0f)",
+     "float r = (float)nearbyint((double)yr[i] * (double)scale);\n            if (r > 127.0f)"),
+    ("aq_div_then_mul", "float v = yr[i] * scale;", "float v = yr[i] / (amax > floor_ ? amax : floor_) * 127.0f;"),
 ]
+
+# Equivalent rewrites, not mutants: they give the same bits on every input, so
+# no pin can (or should) tell them apart. s_a = (float)(127.0 / (double)amax) is
+# the correctly rounded fp32 quotient (a double-precision quotient rounded to
+# single is exact-rounded: 53 >= 2 * 24 + 2), and (double)y * (double)s_a is the
+# exact product of two floats, so rounding it to float equals the fp32 product.
 
 # (name, original, planted) in oracle/__init__.py
 PY_MUTANTS = [
