@@ -36,6 +36,7 @@ EXPORTS = (
     "bitnet_ffn_workspace_bytes", "bitnet_ffn_workspace_offset", "bitnet_ffn", "bitnet_layer_bytes",
     "bitnet_stream_workspace_bytes", "bitnet_decode_stream",
     "bitlinear_probe_read", "bitlinear_probe_mfma_ops", "bitlinear_probe_mfma_i8",
+    "bitlinear_gemm_noalloc", "bitlinear_gemm_noalloc_max_scratch_bytes",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -83,6 +84,8 @@ _SIGS = {
     "bitnet_layer_bytes": ([_I64, _I64], _SZ),
     "bitnet_stream_workspace_bytes": ([_I64, _I64, _I64], _SZ),
     "bitnet_decode_stream": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _P, _P, _P, _SZ, _P], _I),
+    "bitlinear_gemm_noalloc": ([_P, _F, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P, _P, _P], _I),
+    "bitlinear_gemm_noalloc_max_scratch_bytes": ([], _SZ),
     "bitlinear_probe_read": ([_P, _SZ, _P, _P], _I),
     "bitlinear_probe_mfma_ops": ([_I64], _I64),
     "bitlinear_probe_mfma_i8": ([_I64, _P, _P], _I),
@@ -201,6 +204,22 @@ def bitlinear_gemm(packed, w_scale, n, k, q, act_scale, act_sum, m, residual, y,
                                _dev(y, torch.float32, "y", True), _dev(acc_out, torch.int32, "acc_out", True),
                                _dev(row_argmax, torch.int32, "row_argmax", True),
                                _dev(workspace, None, "workspace", True), ws_bytes, _stream(stream)), "bitlinear_gemm")
+
+
+def bitlinear_gemm_noalloc(packed, w_scale, n, k, q, act_scale, act_sum, m, residual, y, acc_out=None,
+                           row_argmax=None, stream=None):
+    """bitlinear_gemm with the argmax keys in the library's static device array (no workspace)."""
+    _check(_lib.bitlinear_gemm_noalloc(_dev(packed, torch.uint8, "packed"), float(w_scale), n, k,
+                                       _dev(q, torch.int8, "q"), _dev(act_scale, torch.float32, "act_scale"),
+                                       _dev(act_sum, torch.int32, "act_sum"), m,
+                                       _dev(residual, torch.float32, "residual", True),
+                                       _dev(y, torch.float32, "y", True), _dev(acc_out, torch.int32, "acc_out", True),
+                                       _dev(row_argmax, torch.int32, "row_argmax", True), _stream(stream)),
+           "bitlinear_gemm_noalloc")
+
+
+def bitlinear_gemm_noalloc_max_scratch_bytes():
+    return _lib.bitlinear_gemm_noalloc_max_scratch_bytes()
 
 
 def bitnet_ffn_workspace_bytes(m, d, f):

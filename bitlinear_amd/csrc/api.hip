@@ -2,6 +2,7 @@
 // then launches on the caller's stream. No allocation, no synchronisation, no
 // host reads of device memory.
 #include <algorithm>
+#include <mutex>
 
 #include "internal.h"
 #include "prefetch.h"
@@ -194,6 +195,47 @@ int ffn_impl(const float* x, int64_t m, int64_t d, int64_t f, const float* g_ffn
     return bl::launch_gemm(w_down, s_down, sdp, D, F, q2, s2, qs2, M, residual, out, D, acc_d, nullptr, nullptr, s);
 }
 
+// ---- library-owned scratch for callers that cannot allocate -------------------
+//
+// A static device array: each GPU the library runs on holds its own copy until
+// the process ends. Host code never passes the array's name to a kernel (on
+// the host it names a stand-in, not device memory): the device address of the
+// current GPU's copy is looked up once per device with hipGetSymbolAddress and
+// only that address is used.
+constexpr size_t kStaticScratchBytes = (size_t)1 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+    std::once_flag once;
+    void* ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// Device address of the current GPU's scratch copy (looked up on the first call
+// on that GPU, with that GPU current), or an error status.
+int static_scratch(void** out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BL_ERR_DEVICE;
+    ScratchSlot& slot = g_scratch[dev];
+    std::call_once(slot.once, [&]() { slot.err = hipGetSymbolAddress(&slot.ptr, HIP_SYMBOL(scratch)); });
+    if (slot.err != hipSuccess || slot.ptr == nullptr) return BL_ERR_DEVICE;
+    *out = slot.ptr;
+    return BL_OK;
+}
+
+// Argument checks of bitlinear_gemm, then its launches. ws_given: the call has
+// a workspace (the caller's, or the library's static array, passed as
+// workspace == NULL); a caller's workspace must be 8-byte aligned.
+int gemm_check(const uint8_t* packed, float w_scale, int64_t n, int64_t k, const int8_t* q, const float* act_scale,
+               const int32_t* act_sum, int64_t m, const float* residual, const float* y, const int32_t* acc_out,
+               const int32_t* row_argmax, const void* workspace, bool ws_given, size_t workspace_bytes);
+int gemm_launch(const uint8_t* packed, float w_scale, int64_t n, int64_t k, const int8_t* q, const float* act_scale,
+                const int32_t* act_sum, int64_t m, const float* residual, float* y, int32_t* acc_out,
+                int32_t* row_argmax, void* workspace, hipStream_t s);
+
 }  // namespace
 
 extern "C" {
@@ -260,9 +302,45 @@ int bitlinear_gemm(const uint8_t* packed, float w_scale, int64_t n, int64_t k, c
                    const float* act_scale, const int32_t* act_sum, int64_t m, const float* residual, float* y,
                    int32_t* acc_out, int32_t* row_argmax, void* workspace, size_t workspace_bytes, void* stream)
 {
+    if (row_argmax && !workspace) return BL_ERR_NULL;
+    const int rc = gemm_check(packed, w_scale, n, k, q, act_scale, act_sum, m, residual, y, acc_out, row_argmax,
+                              workspace, workspace != nullptr, workspace_bytes);
+    if (rc != BL_OK) return rc;
+    return gemm_launch(packed, w_scale, n, k, q, act_scale, act_sum, m, residual, y, acc_out, row_argmax, workspace,
+                       as_stream(stream));
+}
+
+int bitlinear_gemm_noalloc(const uint8_t* packed, float w_scale, int64_t n, int64_t k, const int8_t* q,
+                           const float* act_scale, const int32_t* act_sum, int64_t m, const float* residual,
+                           float* y, int32_t* acc_out, int32_t* row_argmax, void* stream)
+{
+    // every argument check first (an argmax needing more than the static array
+    // fails as BL_ERR_WORKSPACE), then the device address of the array
+    const int rc = gemm_check(packed, w_scale, n, k, q, act_scale, act_sum, m, residual, y, acc_out, row_argmax,
+                              nullptr, true, kStaticScratchBytes);
+    if (rc != BL_OK) return rc;
+    void* ws = nullptr;
+    if (row_argmax) {
+        const int src = static_scratch(&ws);
+        if (src != BL_OK) return src;
+    }
+    return gemm_launch(packed, w_scale, n, k, q, act_scale, act_sum, m, residual, y, acc_out, row_argmax, ws,
+                       as_stream(stream));
+}
+
+size_t bitlinear_gemm_noalloc_max_scratch_bytes(void) { return kStaticScratchBytes; }
+
+}  // extern "C"
+
+namespace {
+
+int gemm_check(const uint8_t* packed, float w_scale, int64_t n, int64_t k, const int8_t* q, const float* act_scale,
+               const int32_t* act_sum, int64_t m, const float* residual, const float* y, const int32_t* acc_out,
+               const int32_t* row_argmax, const void* workspace, bool ws_given, size_t workspace_bytes)
+{
     if (!packed || !q || !act_scale || !act_sum) return BL_ERR_NULL;
     if (!y && !row_argmax) return BL_ERR_NULL;
-    if (row_argmax && !workspace) return BL_ERR_NULL;
+    if (row_argmax && !ws_given) return BL_ERR_NULL;
     if (!dim_ok(m) || !dim_ok(n) || !k_ok(k) || m > 0x7fffffff || n > 0x7fffffff || m * n > ((int64_t)1 << 40))
         return BL_ERR_SHAPE;
     if (!aligned(packed, 16) || !aligned(q, 16) || !aligned(act_scale, 4) || !aligned(act_sum, 4) ||
@@ -271,20 +349,29 @@ int bitlinear_gemm(const uint8_t* packed, float w_scale, int64_t n, int64_t k, c
         return BL_ERR_ALIGN;
     if (!(w_scale > 0.0f) || !(w_scale < INFINITY)) return BL_ERR_VALUE;
     if (row_argmax && workspace_bytes < bitlinear_gemm_workspace_bytes(m, n, k, 1)) return BL_ERR_WORKSPACE;
+    return BL_OK;
+}
+
+int gemm_launch(const uint8_t* packed, float w_scale, int64_t n, int64_t k, const int8_t* q, const float* act_scale,
+                const int32_t* act_sum, int64_t m, const float* residual, float* y, int32_t* acc_out,
+                int32_t* row_argmax, void* workspace, hipStream_t s)
+{
     if (m <= kMaxSkinnyM) {
         bl::SkinnyArgs a = skinny(packed, nullptr, w_scale, 1, (int)n, (int)k, q, act_scale, act_sum, (int)m, residual,
                                   y, (int)n, acc_out);
         unsigned long long* keys = row_argmax ? static_cast<unsigned long long*>(workspace) : nullptr;
         a.tile_keys = keys;
-        int rc = bl::launch_skinny(a, true, as_stream(stream));
-        if (!rc && keys)
-            rc = bl::launch_tile_argmax(keys, bl::skinny_tiles((int)n, false), (int)m, row_argmax, as_stream(stream));
+        int rc = bl::launch_skinny(a, true, s);
+        if (!rc && keys) rc = bl::launch_tile_argmax(keys, bl::skinny_tiles((int)n, false), (int)m, row_argmax, s);
         return rc;
     }
     return bl::launch_gemm(packed, w_scale, nullptr, (int)n, (int)k, q, act_scale, act_sum, (int)m, residual, y,
-                           (int)n, acc_out, row_argmax, static_cast<unsigned long long*>(workspace),
-                           as_stream(stream));
+                           (int)n, acc_out, row_argmax, static_cast<unsigned long long*>(workspace), s);
 }
+
+}  // namespace
+
+extern "C" {
 
 size_t bitnet_ffn_workspace_bytes(int64_t m, int64_t d, int64_t f)
 {

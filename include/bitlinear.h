@@ -191,6 +191,31 @@ int bitlinear_gemm(const uint8_t *packed, float w_scale, int64_t n, int64_t k,
                    const float *residual, float *y, int32_t *acc_out, int32_t *row_argmax,
                    void *workspace, size_t workspace_bytes, void *stream);
 
+/* bitlinear_gemm for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * The same computation and results as bitlinear_gemm, but the argmax keys live
+ * in a library-owned static device array of
+ * bitlinear_gemm_noalloc_max_scratch_bytes() bytes (1 MiB) instead of a
+ * workspace argument; each GPU the library runs on holds its own copy of the
+ * array until the process ends. The call allocates and frees nothing; on its
+ * first use on a GPU it looks up that GPU's copy (hipGetSymbolAddress).
+ *   Arguments : as bitlinear_gemm, without workspace / workspace_bytes.
+ *   Limit     : with row_argmax, bitlinear_gemm_workspace_bytes(m, n, k, 1)
+ *               must not exceed the array (m <= 32: m * ceil(n / 32) * 8 bytes,
+ *               e.g. 32 tokens x 50000 columns = 400,128 B; m > 32: 8 bytes per
+ *               token); larger requests fail with BL_ERR_WORKSPACE before any
+ *               device call. Without row_argmax the array is not used.
+ * Every call on one GPU shares that GPU's array, so calls that overlap in time
+ * on one GPU (different streams, or concurrent host threads) race on it and
+ * must be serialised by the caller. The array keeps the last call's contents;
+ * each call writes every key it reads, so nothing needs clearing between calls.
+ * Errors: as bitlinear_gemm; BL_ERR_DEVICE if the array cannot be located. */
+size_t bitlinear_gemm_noalloc_max_scratch_bytes(void);
+int bitlinear_gemm_noalloc(const uint8_t *packed, float w_scale, int64_t n, int64_t k,
+                           const int8_t *q, const float *act_scale, const int32_t *act_sum, int64_t m,
+                           const float *residual, float *y, int32_t *acc_out, int32_t *row_argmax,
+                           void *stream);
+
 /* BitNet FFN sub-layer without the residual of the block (pass `residual` to
  * add one):
  *   q1  = quant(rmsnorm(x, norm_gain))                       [m][d]

@@ -186,6 +186,35 @@ def test_gemm_checks():
     assert call(s=0.0) == bl.BL_ERR_VALUE
 
 
+def test_gemm_noalloc_checks():
+    """Every check of bitlinear_gemm_noalloc fires on the host before any device
+    call (this container has no GPU: a call that got past them would fail with
+    BL_ERR_DEVICE instead)."""
+    f = bl._lib.bitlinear_gemm_noalloc
+    ok = dict(p=A, s=40.0, n=16, k=64, q=A, sa=A, qs=A, m=3, r=None, y=A, acc=None, am=None)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return f(a["p"], a["s"], a["n"], a["k"], a["q"], a["sa"], a["qs"], a["m"], a["r"], a["y"], a["acc"], a["am"],
+                 S)
+
+    cap = bl.bitlinear_gemm_noalloc_max_scratch_bytes()
+    assert cap == 1 << 20
+    assert call(p=None) == bl.BL_ERR_NULL
+    assert call(y=None) == bl.BL_ERR_NULL
+    assert call(m=0) == bl.BL_ERR_SHAPE
+    assert call(k=96) == bl.BL_ERR_SHAPE
+    assert call(p=A + 4) == bl.BL_ERR_ALIGN
+    assert call(am=U) == bl.BL_ERR_ALIGN
+    assert call(s=float("nan")) == bl.BL_ERR_VALUE
+    # the LM head of the pages (32 tokens x 50000) fits; beyond the array it is refused
+    assert bl.bitlinear_gemm_workspace_bytes(32, 50000, 2048, 1) <= cap
+    n_big = 32 * (cap // (32 * 8)) + 64
+    assert bl.bitlinear_gemm_workspace_bytes(32, n_big, 2048, 1) > cap
+    assert call(m=32, n=n_big, k=2048, am=A) == bl.BL_ERR_WORKSPACE
+    assert call(m=cap // 8 + 64, n=16, k=64, am=A) == bl.BL_ERR_WORKSPACE
+
+
 def test_ffn_checks():
     f = bl._lib.bitnet_ffn
     m, d, f_ = 1, 64, 128
