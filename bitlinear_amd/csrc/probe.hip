@@ -53,23 +53,36 @@ __global__ __launch_bounds__(kReadThreads) void read_probe_kernel(const uint4* _
 constexpr int kMfmaThreads = 256;
 constexpr int kMfmaChains = 8;
 
+// One MFMA accumulating in place: the compiler's own form of a loop-carried
+// accumulator is moved between registers every iteration, which the probe
+// would then measure instead of the matrix cores.
+#define BL_MFMA_INPLACE(c) asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b))
+
 __global__ __launch_bounds__(kMfmaThreads) void mfma_probe_kernel(int64_t iters, uint32_t* sink)
 {
     const int lane = threadIdx.x & 63;
-    v4i a = {lane, lane * 3, lane * 5, lane * 7};
-    v4i b = {lane ^ 1, lane ^ 2, lane ^ 3, lane ^ 4};
-    v4i c[kMfmaChains];
-#pragma unroll
-    for (int j = 0; j < kMfmaChains; ++j) c[j] = v4i{j, 0, 0, 0};
+    const v4i a = {lane, lane * 3, lane * 5, lane * 7};
+    const v4i b = {lane ^ 1, lane ^ 2, lane ^ 3, lane ^ 4};
+    // eight independent chains: each MFMA reads an accumulator written eight
+    // instructions earlier
+    v4i c0 = {0, 0, 0, 0}, c1 = {1, 0, 0, 0}, c2 = {2, 0, 0, 0}, c3 = {3, 0, 0, 0};
+    v4i c4 = {4, 0, 0, 0}, c5 = {5, 0, 0, 0}, c6 = {6, 0, 0, 0}, c7 = {7, 0, 0, 0};
     for (int64_t it = 0; it < iters; ++it) {
-#pragma unroll
-        for (int j = 0; j < kMfmaChains; ++j) c[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c[j], 0, 0, 0);
+        BL_MFMA_INPLACE(c0);
+        BL_MFMA_INPLACE(c1);
+        BL_MFMA_INPLACE(c2);
+        BL_MFMA_INPLACE(c3);
+        BL_MFMA_INPLACE(c4);
+        BL_MFMA_INPLACE(c5);
+        BL_MFMA_INPLACE(c6);
+        BL_MFMA_INPLACE(c7);
     }
-    uint32_t acc = 0;
-#pragma unroll
-    for (int j = 0; j < kMfmaChains; ++j) acc ^= (uint32_t)(c[j][0] ^ c[j][1] ^ c[j][2] ^ c[j][3]);
-    if (acc == 0x9e3779b9u) atomicXor(sink, acc);  // practically never taken; keeps the chain alive
+    const v4i r = c0 ^ c1 ^ c2 ^ c3 ^ c4 ^ c5 ^ c6 ^ c7;
+    const uint32_t acc = (uint32_t)(r[0] ^ r[1] ^ r[2] ^ r[3]);
+    if (acc == 0x9e3779b9u) atomicXor(sink, acc);  // practically never taken; keeps the chains alive
 }
+
+#undef BL_MFMA_INPLACE
 
 int cu_count()
 {
