@@ -119,9 +119,9 @@ bl::SkinnyArgs skinny_gateup(const uint8_t* w_gate, float s_gate, const uint8_t*
     return a;
 }
 
-// True while s records into a graph (or the query fails): the persistent
-// stream kernel needs a cooperative launch, so a capture takes the
-// launch-per-step path (same results).
+// True while s records into a graph (or the query fails). A capture takes the
+// launch-per-step path (same results): a replayed graph may run next to other
+// work that holds CUs, which the persistent kernel needs to itself.
 bool capturing(hipStream_t s)
 {
     hipStreamCaptureStatus st = hipStreamCaptureStatusNone;

@@ -589,7 +589,6 @@ StreamFn stream_fn(int d, int f)
 
 struct DeviceInfo {
     int cus = 0;
-    bool coop = false;
 };
 
 DeviceInfo device_info()
@@ -602,21 +601,31 @@ DeviceInfo device_info()
         DeviceInfo info;
         int v = 0;
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) info.cus = v;
-        v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess) info.coop = v != 0;
         cache[dev] = info;
         have[dev] = true;
     }
     return cache[dev];
 }
 
+// Whether every CU can hold one workgroup of the kernel (registers, LDS, waves).
+bool one_per_cu(StreamFn fn)
+{
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, reinterpret_cast<const void*>(fn), kT, 0) !=
+        hipSuccess)
+        return false;
+    return blocks >= 1;
+}
+
 }  // namespace
 
 bool stream_persistent_fits(int m, int d, int f)
 {
-    if (m != 1 || !stream_fn(d, f)) return false;
+    if (m != 1) return false;
+    const StreamFn fn = stream_fn(d, f);
+    if (!fn) return false;
     const DeviceInfo info = device_info();
-    return info.coop && info.cus >= kGrid;
+    return info.cus >= kGrid && one_per_cu(fn);
 }
 
 int launch_stream_persistent(const uint8_t* weights, const float* scales, const float* gains, const float* z,
@@ -643,10 +652,14 @@ int launch_stream_persistent(const uint8_t* weights, const float* scales, const 
     a.ctrl = ctrl;
     a.n_layers = n_layers;
     a.eps = eps;
-    void* args[] = {&a};
-    const hipError_t e =
-        hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fn), dim3(kGrid), dim3(kT), args, 0, s);
-    return e == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
+    // A plain launch: with at least kGrid CUs that each fit one workgroup, all
+    // kGrid workgroups are resident together on a device that runs nothing
+    // else. Should one not become resident (another queue holding CUs), the
+    // others' waits time out and set the status word: the kernel ends early
+    // and never hangs. (A cooperative launch would make residency a launch
+    // condition, but its runtime state made profiled processes crash at exit.)
+    fn<<<dim3(kGrid), dim3(kT), 0, s>>>(a);
+    return hipGetLastError() == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
 }
 
 size_t stream_ll_words(int d, int f) { return (size_t)2 * d + f + (size_t)kGrid * kFlagStride; }

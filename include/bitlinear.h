@@ -291,10 +291,12 @@ int bitnet_ffn(const float *x, int64_t m, int64_t d, int64_t f,
  *             its first 8 bytes are two uint32 words {phase counter, status}.
  * d and f must be multiples of 64; m >= 1.
  * At m == 1, for the compiled shapes (d, f) = (2560, 10240), (2048, 8192) and
- * (256, 1024) on a device with cooperative launch and at least 256 CUs, the
- * whole stream runs as one persistent kernel, one workgroup per CU, that hands
- * each step's output vector to the next step through flag-tagged words in the
- * workspace.
+ * (256, 1024) on a device with at least 256 CUs that each fit one of its
+ * workgroups, the whole stream runs as one persistent kernel of 256
+ * workgroups, all resident at once, that hands each step's output vector to
+ * the next step through flag-tagged words in the workspace. It needs the CUs
+ * to itself: work running at the same time on other streams can keep a
+ * workgroup from becoming resident, and the call then ends by timeout.
  * Every wait in it is bounded (2 s from the start of that wait, so the bound
  * does not grow with n_layers); on a timeout the kernel stops early and
  * sets status = 1 (status = 2: the phase counter is exhausted after about 2^31
