@@ -342,6 +342,53 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def prefill_ffn_leg(bl, torch, T, dev0, check):
+    """The FFN sub-layer at 2048 tokens (d = 2560, f = 10240): quant of x, the
+    paired gate/up MFMA GEMM with relu(gate)^2 * up in its epilogue, sub-norm +
+    quant of h, down GEMM. 2 M (2 d f + f d) int8 operations per call."""
+    M, d, f = 2048, 2560, 10240
+    gg = [W.rng(W.W_PREFILL, 1, tid) for tid in (W.T_GATE, W.T_UP, W.T_DOWN)]
+    packs = [bl.bitlinear_pack(W.ternary(gx, n, k)) for gx, (n, k) in zip(gg, ((f, d), (f, d), (d, f)))]
+    scales = [float(W.weight_scale(gx)) for gx in gg]
+    pw = [T(pk) for pk in packs]
+    xh = W.activations(W.rng(W.W_PREFILL, 1, W.T_X), M, d, outliers=True)
+    x = T(xh)
+    gn, gs = T(np.ones(d, np.float32)), T(np.ones(f, np.float32))
+    o = torch.empty((M, d), dtype=torch.float32, device=dev0)
+    ws = torch.empty(bl.bitnet_ffn_workspace_bytes(M, d, f), dtype=torch.uint8, device=dev0)
+
+    def call():
+        bl.bitnet_ffn(x, M, d, f, gn, gs, 1e-5, pw[0], scales[0], pw[1], scales[1], pw[2], scales[2], None, o, ws)
+    for _ in range(3):
+        call()
+    iters = 10
+    with Timer() as t:
+        for _ in range(iters):
+            call()
+    ms = t.ms / iters
+    stats = per_call_stats(torch, call, iters)
+    ops = 2.0 * M * (2 * d * f + f * d)
+    tops = ops / (ms * 1e-3) / 1e12
+    res = {"workload": "BitNet-3B FFN at 2048 tokens: quant(x) -> paired gate/up MFMA GEMM with relu(gate)^2 x up "
+                       "epilogue -> sub-norm + quant(h) -> down GEMM", "ms": round(ms, 4), "tops": round(tops, 1),
+           "per_call": stats, "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4), "algorithmic_ops": int(ops)}
+    log(f"prefill FFN: {ms:.4f} ms = {tops:.1f} TOPS")
+    if check:
+        import oracle
+        olib = oracle.load()
+        pick = W.rng(W.W_PREFILL, 2, 1)
+        rows = sorted({0, M - 1} | {int(tt * 128 + pick.integers(0, 128)) for tt in range(M // 128)})
+        opk = [oracle.pack(W.ternary(gx, n, k), olib) for gx, (n, k) in
+               zip([W.rng(W.W_PREFILL, 1, tid) for tid in (W.T_GATE, W.T_UP, W.T_DOWN)], ((f, d), (f, d), (d, f)))]
+        r = oracle.ffn(xh[rows], np.ones(d, np.float32), np.ones(f, np.float32), 1e-5, opk[0], scales[0], opk[1],
+                       scales[1], opk[2], scales[2], olib)
+        got = o.cpu().numpy()[rows]
+        res["parity_sampled_rows"] = {"rows": len(rows),
+                                      "bit_exact": bool(np.array_equal(got.view(np.uint32), r["out"].view(np.uint32)))}
+        log(f"prefill FFN parity on {len(rows)} rows: {res['parity_sampled_rows']}")
+    return res
+
+
 def single_core_oracle():
     """The oracle on one thread: in full for the one-token workloads (2560 -> 2560
     quant + GEMV, the 3B FFN, one 3B stream token), and on a stated slice scaled
@@ -597,6 +644,9 @@ def extra_measurements(bl, torch, T, dev0, check=True):
             got.view(np.uint32), oy.view(np.uint32))), "max_rel_err": float(err.max())}
         log(f"prefill parity on {len(rows)} rows: {out['prefill']['parity_sampled_rows']}")
     del p, x, q, y
+
+    # ---- prefill FFN, 2048 tokens, BitNet-3B shapes ----
+    out["prefill_ffn"] = prefill_ffn_leg(bl, torch, T, dev0, check)
 
     # ---- batched decode, 1.3B, 32 tokens, + LM head argmax ----
     cfg = W.BITNET_1P3B

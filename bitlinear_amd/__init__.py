@@ -266,6 +266,8 @@ def ffn_workspace_view(workspace, m, d, f, segment):
               "h": ((m, f), torch.float32), "q2": ((m, f), torch.int8), "s2": ((m,), torch.float32),
               "qs2": ((m,), torch.int32), "acc_gate": ((m, f), torch.int32), "acc_up": ((m, f), torch.int32),
               "acc_down": ((m, d), torch.int32), "gate": ((m, f), torch.float32), "up": ((m, f), torch.float32)}
+    if segment in ("gate", "up"):
+        raise ValueError(f"workspace segment {segment!r} is reserved and empty")
     shape, dtype = shapes[segment]
     off = bitnet_ffn_workspace_offset(m, d, f, segment)
     nbytes = int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()

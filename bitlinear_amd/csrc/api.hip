@@ -32,10 +32,12 @@ struct Layout {
 
 Layout ffn_layout(int64_t m, int64_t d, int64_t f)
 {
+    // the last two segments (gate, up) are reserved and empty: no path writes
+    // gate or up separately any more
     const size_t sz[BITNET_FFN_WS_COUNT] = {
         (size_t)(m * d),     (size_t)m * 4,     (size_t)m * 4, (size_t)(m * f) * 4,
         (size_t)(m * f),     (size_t)m * 4,     (size_t)m * 4, (size_t)(m * f) * 4,
-        (size_t)(m * f) * 4, (size_t)(m * d) * 4, (size_t)(m * f) * 4, (size_t)(m * f) * 4,
+        (size_t)(m * f) * 4, (size_t)(m * d) * 4, 0, 0,
     };
     Layout l{};
     size_t at = 0;
@@ -172,14 +174,8 @@ int ffn_impl(const float* x, int64_t m, int64_t d, int64_t f, const float* g_ffn
                                              acc_u),
                                true, s);
     } else {
-        float* gate = at<float>(ws, L.off[BITNET_FFN_WS_GATE]);
-        float* up = at<float>(ws, L.off[BITNET_FFN_WS_UP]);
-        rc = bl::launch_gemm(w_gate, s_gate, scale_ptr, F, D, q1, s1, qs1, M, nullptr, gate, F, acc_g, nullptr,
-                             nullptr, s);
-        if (!rc)
-            rc = bl::launch_gemm(w_up, s_up, scale_ptr ? scale_ptr + 1 : nullptr, F, D, q1, s1, qs1, M, nullptr, up, F,
-                                 acc_u, nullptr, nullptr, s);
-        if (!rc) rc = bl::launch_relu2_mul(gate, up, (int64_t)m * f, h, s);
+        // gate and up in one MFMA product with relu(gate)^2 * up in its epilogue
+        rc = bl::launch_gemm_gateup(w_gate, s_gate, w_up, s_up, scale_ptr, F, D, q1, s1, qs1, M, h, acc_g, acc_u, s);
     }
     if (rc) return rc;
     const float* sdp = scale_ptr ? scale_ptr + 2 : nullptr;

@@ -93,17 +93,28 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("" ::: "memory");
 }
 
-template <class C>
+// PAIR mode (the FFN's gate and up projections in one product): n is the
+// number of output columns and every MT-row group of the B tile holds MT/2
+// rows of W_gate followed by the same MT/2 rows of W_up, so in each MFMA
+// output tile lane c (c < MT/2) holds gate and lane c + MT/2 holds up of one
+// output column; the epilogue pairs them with one lane exchange and writes
+// y = relu(gate)^2 * up ("Transformer Block", section "Feed-Forward Network
+// (FFN)"; the fusedGateUpRelu dispatch of "Per-Layer Fused PreparedDispatch
+// Refs"). acc_out / acc_up receive the exact gate / up accumulators.
+template <class C, bool PAIR>
 __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(2))) void gemm_kernel(
     const uint8_t* __restrict__ packed, float w_scale, const float* __restrict__ w_scale_ptr, int n, int k,
     const int8_t* __restrict__ q, const float* __restrict__ act_scale, const int32_t* __restrict__ act_sum, int m,
-    const float* residual, float* y, int ldy, int32_t* __restrict__ acc_out, unsigned long long* __restrict__ keys)
+    const float* residual, float* y, int ldy, int32_t* __restrict__ acc_out, unsigned long long* __restrict__ keys,
+    const uint8_t* __restrict__ packed_up, float up_scale, int32_t* __restrict__ acc_up)
 {
     using M = Mfma<C::MT>;
     constexpr int MT = C::MT;
+    constexpr int HALF = MT / 2;
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][C::BM * C::SA];
     __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][C::BN * C::SB];
     __shared__ float lds_inv[C::BM];
+    __shared__ float lds_inv_up[PAIR ? C::BM : 1];
     __shared__ int lds_qsum[C::BM];
 
     const int tid = threadIdx.x;
@@ -111,15 +122,18 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(2))
     const int wave = tid >> 6;
     const int wm = (wave / C::WAVES_N) * C::WM;  // wave row offset inside the block tile
     const int wn = (wave % C::WAVES_N) * C::WN;  // wave column offset
-    const int n0 = blockIdx.x * C::BN;
+    const int n0 = blockIdx.x * C::BN;           // first B row of the block tile
+    const int c0 = PAIR ? blockIdx.x * (C::BN / 2) : n0;  // first output column
     const int m0 = blockIdx.y * C::BM;
     const size_t kb = (size_t)k / 4;
     const int nk = k / C::BK;
 
     const float ws = w_scale_ptr ? *w_scale_ptr : w_scale;
+    const float ws_up = PAIR ? (w_scale_ptr ? w_scale_ptr[1] : up_scale) : 0.0f;
     for (int r = tid; r < C::BM; r += C::kThreads) {
         const int row = m0 + r;
         lds_inv[r] = row < m ? 1.0f / (act_scale[row] * ws) : 0.0f;
+        if constexpr (PAIR) lds_inv_up[r] = row < m ? 1.0f / (act_scale[row] * ws_up) : 0.0f;
         lds_qsum[r] = row < m ? act_sum[row] : 0;
     }
 
@@ -141,8 +155,17 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(2))
         for (int c = 0; c < C::B_PER_T; ++c) {
             const int chunk = tid + c * C::kThreads;
             const int row = chunk / (C::BK / 64), kg = chunk % (C::BK / 64);
-            const int gcol = (chunk < C::B_CHUNKS && n0 + row < n) ? n0 + row : 0;
-            gb[st][c] = *reinterpret_cast<const uint4*>(packed + (size_t)gcol * kb + k0 / 4 + kg * 16);
+            if constexpr (PAIR) {
+                // B row -> (gate | up, output column); columns past n read row 0
+                const int within = row % MT;
+                const int col = c0 + HALF * (row / MT) + (within % HALF);
+                const int gcol = (chunk < C::B_CHUNKS && col < n) ? col : 0;
+                const uint8_t* src = within < HALF ? packed : packed_up;
+                gb[st][c] = *reinterpret_cast<const uint4*>(src + (size_t)gcol * kb + k0 / 4 + kg * 16);
+            } else {
+                const int gcol = (chunk < C::B_CHUNKS && n0 + row < n) ? n0 + row : 0;
+                gb[st][c] = *reinterpret_cast<const uint4*>(packed + (size_t)gcol * kb + k0 / 4 + kg * 16);
+            }
         }
     };
     auto store_lds = [&](int buf, int st) __attribute__((always_inline)) {
@@ -222,9 +245,42 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(2))
     if (s < nk) k_step(s, 0);
 
     // epilogue: lane holds column lane % MT of each tile, register r the row
-    // M::row(lane, r). An interior tile that only writes y takes a path with
-    // no per-element bounds or pointer checks (they are uniform there; the
-    // general path below unrolls into hundreds of branches).
+    // M::row(lane, r).
+    if constexpr (PAIR) {
+        // lane c < HALF: gate of column c0 + (wn + j MT) / 2 + c; lane c + HALF: its up
+        const int cl = lane % MT;
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i) {
+#pragma unroll
+            for (int r = 0; r < C::NACC; ++r) {
+                const int lrow = wm + i * MT + M::row(lane, r);
+                const int row = m0 + lrow;
+                const int qs = lds_qsum[lrow];
+                const float inv_g = lds_inv[lrow];
+                const float inv_u = lds_inv_up[lrow];
+#pragma unroll
+                for (int j = 0; j < C::TN; ++j) {
+                    const int total = acc[i][j][r] - qs;
+                    const int other = __shfl_xor(total, HALF, 64);
+                    const int col = c0 + (wn + j * MT) / 2 + (cl % HALF);
+                    if (cl < HALF && row < m && col < n) {
+                        const size_t o = (size_t)row * ldy + col;
+                        const float gate = (float)total * inv_g;
+                        const float up = (float)other * inv_u;
+                        const float gp = gate > 0.0f ? gate : 0.0f;
+                        const float g2 = gp * gp;
+                        y[o] = g2 * up;
+                        if (acc_out) acc_out[o] = total;
+                        if (acc_up) acc_up[o] = other;
+                    }
+                }
+            }
+        }
+        return;
+    }
+    // An interior tile that only writes y takes a path with no per-element
+    // bounds or pointer checks (they are uniform there; the general path below
+    // unrolls into hundreds of branches).
     if (y && !residual && !acc_out && !keys && m0 + C::BM <= m && n0 + C::BN <= n) {
         float* yb = y + (size_t)(m0 + wm) * ldy + n0 + wn + (lane % MT);
 #pragma unroll
@@ -293,16 +349,6 @@ __global__ void argmax_finish_kernel(const unsigned long long* keys, int m, int3
     if (i < m) idx[i] = (int32_t)(0xFFFFFFFFu - (uint32_t)(keys[i] & 0xFFFFFFFFull));
 }
 
-__global__ void relu2_mul_kernel(const float* __restrict__ gate, const float* __restrict__ up, int64_t count,
-                                 float* __restrict__ h)
-{
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x) {
-        const float g = gate[i] > 0.0f ? gate[i] : 0.0f;
-        const float g2 = g * g;
-        h[i] = g2 * up[i];
-    }
-}
-
 }  // namespace
 
 int launch_gemm(const uint8_t* packed, float w_scale, const float* w_scale_ptr, int n, int k, const int8_t* q,
@@ -316,12 +362,14 @@ int launch_gemm(const uint8_t* packed, float w_scale, const float* w_scale_ptr, 
     }
     if (m <= 2 * CfgSmall::BM) {
         dim3 grid((n + CfgSmall::BN - 1) / CfgSmall::BN, (m + CfgSmall::BM - 1) / CfgSmall::BM);
-        gemm_kernel<CfgSmall><<<grid, CfgSmall::kThreads, 0, s>>>(packed, w_scale, w_scale_ptr, n, k, q, act_scale,
-                                                                  act_sum, m, residual, y, ldy, acc_out, keys);
+        gemm_kernel<CfgSmall, false><<<grid, CfgSmall::kThreads, 0, s>>>(
+            packed, w_scale, w_scale_ptr, n, k, q, act_scale, act_sum, m, residual, y, ldy, acc_out, keys, nullptr,
+            0.0f, nullptr);
     } else {
         dim3 grid((n + CfgLarge::BN - 1) / CfgLarge::BN, (m + CfgLarge::BM - 1) / CfgLarge::BM);
-        gemm_kernel<CfgLarge><<<grid, CfgLarge::kThreads, 0, s>>>(packed, w_scale, w_scale_ptr, n, k, q, act_scale,
-                                                                  act_sum, m, residual, y, ldy, acc_out, keys);
+        gemm_kernel<CfgLarge, false><<<grid, CfgLarge::kThreads, 0, s>>>(
+            packed, w_scale, w_scale_ptr, n, k, q, act_scale, act_sum, m, residual, y, ldy, acc_out, keys, nullptr,
+            0.0f, nullptr);
     }
     if (hipGetLastError() != hipSuccess) return BL_ERR_LAUNCH;
     if (keys) {
@@ -331,11 +379,22 @@ int launch_gemm(const uint8_t* packed, float w_scale, const float* w_scale_ptr, 
     return BL_OK;
 }
 
-int launch_relu2_mul(const float* gate, const float* up, int64_t count, float* h, hipStream_t s)
+int launch_gemm_gateup(const uint8_t* w_gate, float s_gate, const uint8_t* w_up, float s_up, const float* scale_ptr,
+                       int f, int d, const int8_t* q, const float* act_scale, const int32_t* act_sum, int m, float* h,
+                       int32_t* acc_gate, int32_t* acc_up, hipStream_t s)
 {
-    int64_t blocks = (count + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
-    relu2_mul_kernel<<<(int)blocks, 256, 0, s>>>(gate, up, count, h);
+    // B-row space: 2 f rows (gate and up interleaved by half tiles)
+    if (m <= 2 * CfgSmall::BM) {
+        dim3 grid((2 * f + CfgSmall::BN - 1) / CfgSmall::BN, (m + CfgSmall::BM - 1) / CfgSmall::BM);
+        gemm_kernel<CfgSmall, true><<<grid, CfgSmall::kThreads, 0, s>>>(w_gate, s_gate, scale_ptr, f, d, q, act_scale,
+                                                                        act_sum, m, nullptr, h, f, acc_gate, nullptr,
+                                                                        w_up, s_up, acc_up);
+    } else {
+        dim3 grid((2 * f + CfgLarge::BN - 1) / CfgLarge::BN, (m + CfgLarge::BM - 1) / CfgLarge::BM);
+        gemm_kernel<CfgLarge, true><<<grid, CfgLarge::kThreads, 0, s>>>(w_gate, s_gate, scale_ptr, f, d, q, act_scale,
+                                                                        act_sum, m, nullptr, h, f, acc_gate, nullptr,
+                                                                        w_up, s_up, acc_up);
+    }
     return hipGetLastError() == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
 }
 

@@ -114,8 +114,13 @@ int launch_skinny(const SkinnyArgs& a, bool natural_q, hipStream_t s);
 int skinny_tiles(int n, bool pair);
 int launch_tile_argmax(const unsigned long long* tile_keys, int tiles, int m, int32_t* idx, hipStream_t s);
 
-// h = relu(gate)^2 * up, elementwise.
-int launch_relu2_mul(const float* gate, const float* up, int64_t count, float* h, hipStream_t s);
+// The FFN's gate and up projections as one MFMA GEMM over the stacked weights,
+// with h[m][f] = relu(gate)^2 * up in the epilogue (any m; used above 32
+// tokens). scale_ptr: [s_gate, s_up] or null (then s_gate / s_up).
+int launch_gemm_gateup(const uint8_t* w_gate, float s_gate, const uint8_t* w_up, float s_up, const float* scale_ptr,
+                       int f, int d, const int8_t* q, const float* act_scale, const int32_t* act_sum, int m, float* h,
+                       int32_t* acc_gate, int32_t* acc_up, hipStream_t s);
+
 
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 

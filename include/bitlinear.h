@@ -233,8 +233,10 @@ int bitlinear_gemm_noalloc(const uint8_t *packed, float w_scale, int64_t n, int6
  *                 aligned; holds every intermediate at the offsets given by
  *                 bitnet_ffn_workspace_offset().
  *   flags       : BITNET_FFN_WRITE_ACC also stores acc_gate, acc_up, acc_down.
- * For m <= 8 gate and up run in one launch that streams both weight matrices
- * and applies relu(gate)^2 * up in its epilogue. At m == 1 (d <= 4096, and
+ * gate and up always run in one launch that streams both weight matrices and
+ * applies relu(gate)^2 * up in its epilogue: a GEMV for m <= 8, a skinny MFMA
+ * product for m <= 32, and above that an MFMA GEMM whose B tiles interleave
+ * W_gate and W_up rows, so gate and up of a column meet in one wave. At m == 1 (d <= 4096, and
  * 4096 < f <= 16384 for the second half) each norm + quant runs inside the
  * launch of the product it feeds, so the FFN is two launches; the workspace
  * still receives q1, s1, qs1, h, q2, s2, qs2. Up to 32 tokens each norm + quant
@@ -252,8 +254,8 @@ enum bitnet_ffn_ws_segment {
     BITNET_FFN_WS_ACC_GATE,  /* int32 [m][f] (with BITNET_FFN_WRITE_ACC) */
     BITNET_FFN_WS_ACC_UP,    /* int32 [m][f] (with BITNET_FFN_WRITE_ACC) */
     BITNET_FFN_WS_ACC_DOWN,  /* int32 [m][d] (with BITNET_FFN_WRITE_ACC) */
-    BITNET_FFN_WS_GATE,      /* fp32  [m][f] (used when m > 8) */
-    BITNET_FFN_WS_UP,        /* fp32  [m][f] (used when m > 8) */
+    BITNET_FFN_WS_GATE,      /* reserved, 0 bytes (gate is never stored on its own) */
+    BITNET_FFN_WS_UP,        /* reserved, 0 bytes (up is never stored on its own) */
     BITNET_FFN_WS_COUNT
 };
 size_t bitnet_ffn_workspace_bytes(int64_t m, int64_t d, int64_t f);

@@ -241,7 +241,7 @@ def test_ffn_workspace_layout():
     m, d, f = 3, 2560, 10240
     total = bl.bitnet_ffn_workspace_bytes(m, d, f)
     sizes = {"q1": m * d, "s1": 4 * m, "qs1": 4 * m, "h": 4 * m * f, "q2": m * f, "s2": 4 * m, "qs2": 4 * m,
-             "acc_gate": 4 * m * f, "acc_up": 4 * m * f, "acc_down": 4 * m * d, "gate": 4 * m * f, "up": 4 * m * f}
+             "acc_gate": 4 * m * f, "acc_up": 4 * m * f, "acc_down": 4 * m * d, "gate": 0, "up": 0}
     spans = []
     for seg in bl.FFN_WS_SEGMENTS:
         off = bl.bitnet_ffn_workspace_offset(m, d, f, seg)

@@ -358,9 +358,51 @@ def _ffn_case(bl, olib, m, d, f, seed, with_residual):
 @pytest.mark.parametrize("m,d,f,res", [(1, 64, 128, False), (1, 192, 640, True), (3, 256, 1024, False),
                                         (1, 2560, 10240, False), (8, 640, 2560, True), (12, 320, 640, False),
                                         (40, 256, 512, True), (1, 256, 1024, True), (1, 2048, 8192, True),
-                                        (1, 2560, 10240, True)])
+                                        (1, 2560, 10240, True),
+                                        # above 32 tokens: the paired gate/up MFMA GEMM, with ragged
+                                        # row tiles (32 / 128 rows) and column tiles (128 / 160 columns)
+                                        (33, 256, 1024, False), (64, 128, 1088, True), (65, 256, 1024, True),
+                                        (130, 320, 1088, False), (300, 256, 640, True), (257, 192, 2624, False)])
 def test_ffn(bl, olib, m, d, f, res):
     _ffn_case(bl, olib, m, d, f, m * 1000 + d + f, res)
+
+
+def test_ffn_prefill_full_size_sampled_rows(bl, olib):
+    """The FFN at 2048 tokens with BitNet-3B shapes (d = 2560, f = 10240): the
+    paired gate/up GEMM with relu(gate)^2 * up in its epilogue, the sub-norm +
+    quant of h and the down GEMM. Every intermediate of sampled rows (at least
+    one in every 128-row block tile, plus tile edges) against the oracle's FFN
+    of those rows: q1, s1, sum(q1), the exact gate and up accumulators, h, q2,
+    s2, sum(q2), the exact down accumulators and out (rows are independent)."""
+    import torch
+    m, d, f = 2048, 2560, 10240
+    log(f"ffn full size m={m} d={d} f={f}")
+    g = W.rng(107, 0, 0)
+    tg, tu, td = W.ternary(g, f, d), W.ternary(g, f, d), W.ternary(g, d, f)
+    sg, su, sd = W.weight_scale(g), W.weight_scale(g), W.weight_scale(g)
+    x = W.activations(g, m, d, outliers=True)
+    gn, gs = W.gains(g, d), W.gains(g, f)
+    pg, pu, pd = pack_both(tg, olib), pack_both(tu, olib), pack_both(td, olib)
+    dev = torch_dev()
+    out = torch.empty((m, d), dtype=torch.float32, device=dev)
+    ws = torch.full((bl.bitnet_ffn_workspace_bytes(m, d, f),), 0x5A, dtype=torch.uint8, device=dev)
+    bl.bitnet_ffn(to_dev(x), m, d, f, to_dev(gn), to_dev(gs), 1e-5, to_dev(pg), sg, to_dev(pu), su, to_dev(pd), sd,
+                  None, out, ws, flags=bl.BITNET_FFN_WRITE_ACC)
+    pick = W.rng(107, 1, 1)
+    rows = sorted({0, 127, 128, 1023, 2047} | {int(t * 128 + pick.integers(0, 128)) for t in range(m // 128)})
+    r = oracle.ffn(x[rows], gn, gs, 1e-5, pg, sg, pu, su, pd, sd, olib)
+    view = lambda seg: to_host(bl.ffn_workspace_view(ws, m, d, f, seg))[rows]
+    assert_exact(view("q1"), r["q1"], "q1")
+    assert_exact(view("s1").view(np.uint32), r["s1"].view(np.uint32), "s1 bits")
+    assert_exact(view("qs1"), r["qs1"], "qs1")
+    assert_exact(view("acc_gate"), r["acc_gate"], "acc_gate")
+    assert_exact(view("acc_up"), r["acc_up"], "acc_up")
+    assert_f32(view("h"), r["h"], "h")
+    assert_exact(view("q2"), r["q2"], "q2")
+    assert_exact(view("s2").view(np.uint32), r["s2"].view(np.uint32), "s2 bits")
+    assert_exact(view("qs2"), r["qs2"], "qs2")
+    assert_exact(view("acc_down"), r["acc_down"], "acc_down")
+    assert_f32(to_host(out)[rows], r["out"], "out")
 
 
 # ---- layer stream ------------------------------------------------------------------------------------
