@@ -333,6 +333,8 @@ def main():
                                   "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
         result["parity_first_step"] = {"bit_exact": exact, "max_rel_err_x": rel}
         log(f"oracle: {first_s:.2f}s for one token, {tokens} tokens in {cpu_s:.2f}s; first GPU step bit-exact: {exact}")
+    if not args.no_extra:
+        result["greedy"] = greedy_leg(bl, torch, T, dev0, dev, host_layers if not args.no_cpu else None, L, d, f)
     del host_layers
 
     if not args.no_extra:
@@ -340,6 +342,57 @@ def main():
     if not args.no_cpu:
         result["cpu_single_core"] = single_core_oracle()
     print(json.dumps(result), flush=True)
+
+
+def greedy_leg(bl, torch, T, dev0, dev, host_layers, L, d, f):
+    """Greedy decoding of one BitNet-3B sequence on the device: per step the
+    ternary embedding of the current token, the 32-layer stream, the final
+    norm + quant and the 50000-token LM head with a repetition penalty of 1.1
+    over the history and the greedy choice, which is appended to the history
+    -- bitnet_greedy_step, one submit per token, no host round trip."""
+    vocab, m, cap = W.BITNET_3B["vocab"], 1, 256
+    ge, gh = W.rng(W.W_STREAM, 0, W.T_EMB), W.rng(W.W_STREAM, 0, W.T_HEAD)
+    emb_h, head_h = bl.bitlinear_pack(W.ternary(ge, vocab, d)), bl.bitlinear_pack(W.ternary(gh, vocab, d))
+    s_emb, s_head = float(W.weight_scale(ge)), float(W.weight_scale(gh))
+    emb, head = T(emb_h), T(head_h)
+    gf = T(np.ones(d, np.float32))
+    tok0 = W.rng(W.W_STREAM, 0, W.T_TOKENS).integers(0, vocab, m).astype(np.int32)
+    tokens = T(tok0)
+    hist = torch.zeros((m, cap), dtype=torch.int32, device=dev0)
+    hlen = torch.zeros(m, dtype=torch.int32, device=dev0)
+    x = torch.empty((m, d), dtype=torch.float32, device=dev0)
+    ws = torch.zeros(bl.bitnet_greedy_step_workspace_bytes(m, d, f, vocab), dtype=torch.uint8, device=dev0)
+
+    def step():
+        bl.bitnet_greedy_step(emb, s_emb, dev["weights"], dev["scales"], dev["gains"], dev["z"], L, d, f, 1e-5, gf,
+                              head, s_head, tokens, hist, hlen, 1.1, x, None, ws)
+    n_check = 2
+    for _ in range(n_check):
+        step()
+    torch.cuda.synchronize()
+    first = hist[0, :n_check].cpu().numpy().copy()
+    steps = 40
+    with Timer() as t:
+        for _ in range(steps):
+            step()
+    ms = t.ms / steps
+    stats = per_call_stats(torch, step, 20)
+    wbytes = L * bl.bitnet_layer_bytes(d, f) + vocab * d // 4 + d // 4
+    res = {"workload": "BitNet-3B greedy decoding, 1 sequence: embedding + 32 layers (attention math excluded) + "
+                       "final norm + LM head 2560 -> 50000 with repetition penalty 1.1 + argmax + history append, "
+                       "one bitnet_greedy_step per token", "ms_per_token": round(ms, 4),
+           "tokens_per_s": round(1e3 / ms, 1), "per_step": stats, "weight_bytes_per_token": wbytes,
+           "weight_gbs": round(wbytes / (ms * 1e-3) / 1e9, 1)}
+    if host_layers is not None:
+        import oracle
+        olib = oracle.load()
+        o_tok, o_hist, o_len = tok0.copy(), np.zeros((m, cap), np.int32), np.zeros(m, np.int32)
+        for _ in range(n_check):
+            o_tok, o_hist, o_len, _ = oracle.greedy_step(o_tok, emb_h, s_emb, host_layers, np.ones(d, np.float32),
+                                                         1e-5, head_h, s_head, o_hist, o_len, 1.1, olib)
+        res["parity_first_steps"] = {"steps": n_check, "tokens_match": bool(np.array_equal(first, o_hist[0, :n_check]))}
+    log(f"greedy: {ms:.4f} ms/token ({res.get('parity_first_steps')})")
+    return res
 
 
 def prefill_ffn_leg(bl, torch, T, dev0, check):

@@ -37,6 +37,8 @@ EXPORTS = (
     "bitnet_stream_workspace_bytes", "bitnet_decode_stream",
     "bitlinear_probe_read", "bitlinear_probe_mfma_ops", "bitlinear_probe_mfma_i8",
     "bitlinear_gemm_noalloc", "bitlinear_gemm_noalloc_max_scratch_bytes",
+    "bitnet_embed", "bitnet_greedy_head_workspace_bytes", "bitnet_greedy_head", "bitnet_greedy_step_workspace_bytes",
+    "bitnet_greedy_step",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -86,6 +88,12 @@ _SIGS = {
     "bitnet_decode_stream": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _P, _P, _P, _SZ, _P], _I),
     "bitlinear_gemm_noalloc": ([_P, _F, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P, _P, _P], _I),
     "bitlinear_gemm_noalloc_max_scratch_bytes": ([], _SZ),
+    "bitnet_embed": ([_P, _F, _I64, _I64, _P, _I64, _P, _P], _I),
+    "bitnet_greedy_head_workspace_bytes": ([_I64, _I64], _SZ),
+    "bitnet_greedy_head": ([_P, _F, _I64, _I64, _P, _P, _P, _I64, _P, _I64, _P, _F, _P, _P, _P, _SZ, _P], _I),
+    "bitnet_greedy_step_workspace_bytes": ([_I64, _I64, _I64, _I64], _SZ),
+    "bitnet_greedy_step": ([_P, _F, _I64, _P, _P, _P, _P, _I64, _I64, _I64, _F, _P, _P, _F, _P, _I64, _P, _I64, _P,
+                            _F, _P, _P, _P, _SZ, _P], _I),
     "bitlinear_probe_read": ([_P, _SZ, _P, _P], _I),
     "bitlinear_probe_mfma_ops": ([_I64], _I64),
     "bitlinear_probe_mfma_i8": ([_I64, _P, _P], _I),
@@ -272,6 +280,58 @@ def ffn_workspace_view(workspace, m, d, f, segment):
     off = bitnet_ffn_workspace_offset(m, d, f, segment)
     nbytes = int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()
     return workspace[off:off + nbytes].view(dtype).view(shape)
+
+
+# ---- greedy decoding ------------------------------------------------------------------
+
+def bitnet_embed(table, s_emb, tokens, x, stream=None):
+    """x[r] = ternary embedding row tokens[r] / s_emb (table packed [vocab][d/4])."""
+    vocab = table.shape[0]
+    m, d = x.shape
+    _check(_lib.bitnet_embed(_dev(table, torch.uint8, "table"), float(s_emb), vocab, d,
+                             _dev(tokens, torch.int32, "tokens"), m, _dev(x, torch.float32, "x"), _stream(stream)),
+           "bitnet_embed")
+
+
+def bitnet_greedy_head_workspace_bytes(m, n):
+    return _lib.bitnet_greedy_head_workspace_bytes(m, n)
+
+
+def _hist_args(hist, hist_len):
+    if hist is None:
+        return None, 0, None
+    return _dev(hist, torch.int32, "hist"), hist.shape[1], _dev(hist_len, torch.int32, "hist_len")
+
+
+def bitnet_greedy_head(head, s_head, n, k, q, act_scale, act_sum, m, hist, hist_len, penalty, logits, next_token,
+                       workspace, stream=None):
+    h, stride, hl = _hist_args(hist, hist_len)
+    _check(_lib.bitnet_greedy_head(_dev(head, torch.uint8, "head"), float(s_head), n, k, _dev(q, torch.int8, "q"),
+                                   _dev(act_scale, torch.float32, "act_scale"), _dev(act_sum, torch.int32, "act_sum"),
+                                   m, h, stride, hl, float(penalty), _dev(logits, torch.float32, "logits", True),
+                                   _dev(next_token, torch.int32, "next_token"), _dev(workspace, None, "workspace"),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)),
+           "bitnet_greedy_head")
+
+
+def bitnet_greedy_step_workspace_bytes(m, d, f, vocab):
+    return _lib.bitnet_greedy_step_workspace_bytes(m, d, f, vocab)
+
+
+def bitnet_greedy_step(embed_table, s_emb, weights, scales, gains, z, n_layers, d, f, eps, g_final, head, s_head,
+                       tokens, hist, hist_len, penalty, x, logits, workspace, stream=None):
+    vocab = embed_table.shape[0]
+    m = tokens.numel()
+    h, stride, hl = _hist_args(hist, hist_len)
+    _check(_lib.bitnet_greedy_step(_dev(embed_table, torch.uint8, "embed_table"), float(s_emb), vocab,
+                                   _dev(weights, torch.uint8, "weights"), _dev(scales, torch.float32, "scales"),
+                                   _dev(gains, torch.float32, "gains"), _dev(z, torch.float32, "z"), n_layers, d, f,
+                                   eps, _dev(g_final, torch.float32, "g_final"), _dev(head, torch.uint8, "head"),
+                                   float(s_head), _dev(tokens, torch.int32, "tokens"), m, h, stride, hl,
+                                   float(penalty), _dev(x, torch.float32, "x"),
+                                   _dev(logits, torch.float32, "logits", True), _dev(workspace, None, "workspace"),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)),
+           "bitnet_greedy_step")
 
 
 # ---- roofline probes (measurement tools) -----------------------------------------------

@@ -232,6 +232,69 @@ int gemm_launch(const uint8_t* packed, float w_scale, int64_t n, int64_t k, cons
                 const int32_t* act_sum, int64_t m, const float* residual, float* y, int32_t* acc_out,
                 int32_t* row_argmax, void* workspace, hipStream_t s);
 
+// Greedy-head workspace: the per-sequence penalty bitmaps, then the argmax
+// keys (one per sequence and 32-column tile).
+struct HeadLayout {
+    size_t bits, keys, total;
+};
+
+HeadLayout head_layout(int64_t m, int64_t n)
+{
+    HeadLayout l{};
+    l.bits = 0;
+    l.keys = align_up((size_t)m * (size_t)bl::penalty_words((int)n) * 4, 256);
+    l.total = l.keys + align_up((size_t)m * (size_t)((n + 31) / 32) * 8, 256);
+    return l;
+}
+
+// Greedy-step workspace: the stream's (zero-filled once, then kept), the final
+// norm + quant of x, then the head's.
+struct StepLayout {
+    size_t stream, q, s, qs, head, total;
+};
+
+StepLayout step_layout(int64_t m, int64_t d, int64_t f, int64_t vocab)
+{
+    StepLayout l{};
+    size_t at = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = at;
+        at = align_up(at + bytes, 256);
+        return o;
+    };
+    l.stream = take(stream_layout(m, d, f).total);
+    l.q = take((size_t)(m * d));
+    l.s = take((size_t)m * 4);
+    l.qs = take((size_t)m * 4);
+    l.head = take(head_layout(m, vocab).total);
+    l.total = at;
+    return l;
+}
+
+// The LM head with the repetition penalty and the greedy choice (m <= 32,
+// validated): bitmaps, the skinny product with penalised fp32 keys, the
+// per-token reduction into next.
+int greedy_head_launch(const uint8_t* head, float s_head, int64_t n, int64_t k, const int8_t* q,
+                       const float* act_scale, const int32_t* act_sum, int64_t m, const int32_t* hist,
+                       int64_t hist_stride, const int32_t* hist_len, float penalty, float* logits, int32_t* next,
+                       void* ws, hipStream_t s)
+{
+    const HeadLayout L = head_layout(m, n);
+    uint32_t* bits = at<uint32_t>(ws, L.bits);
+    unsigned long long* keys = at<unsigned long long>(ws, L.keys);
+    int rc = bl::launch_penalty_bits(hist, (int)hist_stride, hist_len, (int)n, (int)m, bits, s);
+    if (rc) return rc;
+    bl::SkinnyArgs a =
+        skinny(head, nullptr, s_head, 1, (int)n, (int)k, q, act_scale, act_sum, (int)m, nullptr, logits, (int)n);
+    a.tile_keys = keys;
+    a.pen_bits = bits;
+    a.pen_words = bl::penalty_words((int)n);
+    a.penalty = penalty;
+    rc = bl::launch_skinny(a, true, s);
+    if (rc) return rc;
+    return bl::launch_tile_argmax(keys, bl::skinny_tiles((int)n, false), (int)m, next, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -524,6 +587,93 @@ int bitnet_decode_stream(const uint8_t* weights, const float* scales, const floa
         if (rc) return rc;
     }
     return BL_OK;
+}
+
+// ---- greedy decoding around the stream ----------------------------------------
+
+int bitnet_embed(const uint8_t* table, float s_emb, int64_t vocab, int64_t d, const int32_t* tokens, int64_t m,
+                 float* x, void* stream)
+{
+    if (!table || !tokens || !x) return BL_ERR_NULL;
+    if (!dim_ok(vocab) || !k_ok(d) || !dim_ok(m) || vocab > 0x7fffffff || d > kMaxGemvK || m > 0x7fffffff)
+        return BL_ERR_SHAPE;
+    if (!aligned(table, 16) || !aligned(tokens, 4) || !aligned(x, 16)) return BL_ERR_ALIGN;
+    if (!(s_emb > 0.0f) || !(s_emb < INFINITY)) return BL_ERR_VALUE;
+    return bl::launch_embed(table, s_emb, (int)vocab, (int)d, tokens, (int)m, x, as_stream(stream));
+}
+
+size_t bitnet_greedy_head_workspace_bytes(int64_t m, int64_t n)
+{
+    if (m <= 0 || n <= 0 || m > kMaxSkinnyM || n > 0x7fffffff) return 0;
+    return head_layout(m, n).total;
+}
+
+int bitnet_greedy_head(const uint8_t* head, float s_head, int64_t n, int64_t k, const int8_t* q,
+                       const float* act_scale, const int32_t* act_sum, int64_t m, const int32_t* hist,
+                       int64_t hist_stride, const int32_t* hist_len, float penalty, float* logits,
+                       int32_t* next_token, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!head || !q || !act_scale || !act_sum || !next_token || !workspace) return BL_ERR_NULL;
+    if (hist_stride > 0 && (!hist || !hist_len)) return BL_ERR_NULL;
+    if (m < 1 || m > kMaxSkinnyM || !dim_ok(n) || n > 0x7fffffff || !k_ok(k) || hist_stride < 0 ||
+        hist_stride > 0x7fffffff)
+        return BL_ERR_SHAPE;
+    if (!aligned(head, 16) || !aligned(q, 16) || !aligned(act_scale, 4) || !aligned(act_sum, 4) ||
+        !aligned(next_token, 4) || (logits && !aligned(logits, 4)) || (hist && !aligned(hist, 4)) ||
+        (hist_len && !aligned(hist_len, 4)) || !aligned(workspace, 256))
+        return BL_ERR_ALIGN;
+    if (!(s_head > 0.0f) || !(s_head < INFINITY) || !(penalty > 0.0f) || !(penalty < INFINITY)) return BL_ERR_VALUE;
+    if (workspace_bytes < bitnet_greedy_head_workspace_bytes(m, n)) return BL_ERR_WORKSPACE;
+    return greedy_head_launch(head, s_head, n, k, q, act_scale, act_sum, m, hist, hist_stride, hist_len, penalty,
+                              logits, next_token, workspace, as_stream(stream));
+}
+
+size_t bitnet_greedy_step_workspace_bytes(int64_t m, int64_t d, int64_t f, int64_t vocab)
+{
+    if (m <= 0 || d <= 0 || f <= 0 || vocab <= 0 || m > kMaxSkinnyM || vocab > 0x7fffffff) return 0;
+    return step_layout(m, d, f, vocab).total;
+}
+
+int bitnet_greedy_step(const uint8_t* embed_table, float s_emb, int64_t vocab, const uint8_t* weights,
+                       const float* scales, const float* gains, const float* z, int64_t n_layers, int64_t d,
+                       int64_t f, float eps, const float* g_final, const uint8_t* head, float s_head, int32_t* tokens,
+                       int64_t m, int32_t* hist, int64_t hist_stride, int32_t* hist_len, float penalty, float* x,
+                       float* logits, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!embed_table || !weights || !scales || !gains || !z || !g_final || !head || !tokens || !x || !workspace)
+        return BL_ERR_NULL;
+    if (hist_stride > 0 && (!hist || !hist_len)) return BL_ERR_NULL;
+    if (m < 1 || m > kMaxSkinnyM || !dim_ok(vocab) || vocab > 0x7fffffff || !dim_ok(n_layers) || !k_ok(d) ||
+        !k_ok(f) || d > kMaxGemvK || f > kMaxGemvK || hist_stride < 0 || hist_stride > 0x7fffffff)
+        return BL_ERR_SHAPE;
+    if (!aligned(embed_table, 16) || !aligned(head, 16) || !aligned(g_final, 16) || !aligned(tokens, 4) ||
+        !aligned(x, 16) || (logits && !aligned(logits, 4)) || (hist && !aligned(hist, 4)) ||
+        (hist_len && !aligned(hist_len, 4)) || !aligned(workspace, 256))
+        return BL_ERR_ALIGN;
+    if (!(s_emb > 0.0f) || !(s_emb < INFINITY) || !(s_head > 0.0f) || !(s_head < INFINITY) || !(penalty > 0.0f) ||
+        !(penalty < INFINITY))
+        return BL_ERR_VALUE;
+    if (workspace_bytes < bitnet_greedy_step_workspace_bytes(m, d, f, vocab)) return BL_ERR_WORKSPACE;
+    const StepLayout L = step_layout(m, d, f, vocab);
+    const hipStream_t s = as_stream(stream);
+    // 1. embedding of the current tokens
+    int rc = bl::launch_embed(embed_table, s_emb, (int)vocab, (int)d, tokens, (int)m, x, s);
+    if (rc) return rc;
+    // 2. the layer stream over x, in place (its own checks run here)
+    rc = bitnet_decode_stream(weights, scales, gains, z, n_layers, m, d, f, eps, x, nullptr,
+                              at<void>(workspace, L.stream), stream_layout(m, d, f).total, stream);
+    if (rc) return rc;
+    // 3. final RMSNorm + quant, 4. penalised LM head + greedy choice into tokens
+    int8_t* qf = at<int8_t>(workspace, L.q);
+    float* sf = at<float>(workspace, L.s);
+    int32_t* qsf = at<int32_t>(workspace, L.qs);
+    rc = bl::launch_quant_act(x, g_final, eps, (int)m, (int)d, qf, sf, qsf, s);
+    if (rc) return rc;
+    rc = greedy_head_launch(head, s_head, vocab, d, qf, sf, qsf, m, hist, hist_stride, hist_len, penalty, logits,
+                            tokens, at<void>(workspace, L.head), s);
+    if (rc) return rc;
+    // 5. the chosen tokens join the histories (the next step embeds them)
+    return bl::launch_append(tokens, (int)m, hist, (int)hist_stride, hist_len, nullptr, s);
 }
 
 }  // extern "C"

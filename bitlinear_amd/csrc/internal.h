@@ -109,6 +109,13 @@ struct SkinnyArgs {
     int32_t* acc0 = nullptr;
     int32_t* acc1 = nullptr;
     unsigned long long* tile_keys = nullptr;
+    // Repetition penalty (LM head only, not with w1 or residual): bit col of
+    // pen_bits[tok * pen_words ...] set means that token's logit of column col
+    // is divided by penalty if positive, else multiplied by it; y (if set)
+    // receives the penalised logits and the argmax keys order fp32 values.
+    const uint32_t* pen_bits = nullptr;
+    int pen_words = 0;
+    float penalty = 1.0f;
 };
 int launch_skinny(const SkinnyArgs& a, bool natural_q, hipStream_t s);
 int skinny_tiles(int n, bool pair);
@@ -121,6 +128,16 @@ int launch_gemm_gateup(const uint8_t* w_gate, float s_gate, const uint8_t* w_up,
                        int f, int d, const int8_t* q, const float* act_scale, const int32_t* act_sum, int m, float* h,
                        int32_t* acc_gate, int32_t* acc_up, hipStream_t s);
 
+
+// Greedy decoding around the stream (greedy.hip). penalty_words(n): 32-bit
+// words of one sequence's bitmap over n vocabulary entries.
+inline int penalty_words(int n) { return (n + 31) / 32; }
+int launch_embed(const uint8_t* table, float s_e, int vocab, int d, const int32_t* tokens, int m, float* x,
+                 hipStream_t s);
+int launch_penalty_bits(const int32_t* hist, int stride, const int32_t* hist_len, int n, int m, uint32_t* bits,
+                        hipStream_t s);
+int launch_append(const int32_t* next, int m, int32_t* hist, int stride, int32_t* hist_len, int32_t* tokens,
+                  hipStream_t s);
 
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 

@@ -189,13 +189,23 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyArgs a)
                 const int col = n0 + 32 * j + lc;
                 if (tok < a.m && col < a.n) {
                     const size_t o = (size_t)tok * a.ldy + col;
-                    if (a.y) {
+                    unsigned long long key;
+                    if (a.pen_bits) {
+                        // the repetition penalty on this token's logit, then an fp32 key
                         float v = (float)tot[j] * (1.0f / (sa * sw[j]));
-                        if (a.residual) v = res[j] + v;
-                        a.y[o] = v;
+                        if ((a.pen_bits[(size_t)tok * a.pen_words + (col >> 5)] >> (col & 31)) & 1u)
+                            v = v > 0.0f ? v / a.penalty : v * a.penalty;
+                        if (a.y) a.y[o] = v;
+                        key = argmax_key_f32(v, col);
+                    } else {
+                        if (a.y) {
+                            float v = (float)tot[j] * (1.0f / (sa * sw[j]));
+                            if (a.residual) v = res[j] + v;
+                            a.y[o] = v;
+                        }
+                        key = argmax_key(tot[j], col);
                     }
                     if (a.acc0) a.acc0[o] = tot[j];
-                    const unsigned long long key = argmax_key(tot[j], col);
                     best = key > best ? key : best;
                 }
             }

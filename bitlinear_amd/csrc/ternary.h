@@ -45,6 +45,17 @@ __device__ __forceinline__ uint4 permute16(const uint4 v)
 
 __device__ __forceinline__ v4i as_v4i(const uint4 v) { return v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w}; }
 
+// Argmax key of an fp32 value: its bits mapped to an unsigned order that
+// matches the float order (-0 taken as +0, so equal values tie), then lower
+// columns first. Non-finite values do not occur.
+__device__ __forceinline__ unsigned long long argmax_key_f32(float v, int col)
+{
+    uint32_t b = __float_as_uint(v);
+    if ((b << 1) == 0u) b = 0u;
+    const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return ((unsigned long long)ord << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)col);
+}
+
 // Argmax key of an exact accumulator: larger totals first, then lower columns.
 __device__ __forceinline__ unsigned long long argmax_key(int total, int col)
 {

@@ -315,6 +315,80 @@ int bitnet_decode_stream(const uint8_t *weights, const float *scales, const floa
                          int64_t n_layers, int64_t m, int64_t d, int64_t f, float eps,
                          float *x, float *qkv, void *workspace, size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------ greedy decoding --- */
+/* The device side of greedy text generation around the BitLinear stream
+ * ("BitNet Model - Complete Inference Pipeline", Hesper API: "Architecture"
+ * -- TQ2_0 embedding, the transformer blocks, final RMSNorm, LM head;
+ * "Text Generation / Greedy Decoding"; "GPU Argmax" -- repetitionPenaltyKernel,
+ * appendPenaltyToken and gpuArgmaxWithPenalty, whose penalty and argmax run in
+ * one submit and return only the token index). */
+
+/* Ternary embedding lookup: x[r][k] = t[tokens[r]][k] / s_emb, with the table
+ * packed like any ternary tensor (uint8 [vocab][d/4], layout above) and one
+ * fp32 scale. A token id outside [0, vocab) gives a zero row (ids are device
+ * data, so they are not checked on the host).
+ *   table  : device uint8 [vocab][d/4], 16-byte aligned.
+ *   tokens : device int32 [m].  x : device fp32 [m][d], 16-byte aligned.
+ * Errors: NULL, SHAPE (d % 64 != 0, d > 32768, vocab or m <= 0), ALIGN,
+ * VALUE (s_emb not > 0 or not finite), LAUNCH. */
+int bitnet_embed(const uint8_t *table, float s_emb, int64_t vocab, int64_t d, const int32_t *tokens,
+                 int64_t m, float *x, void *stream);
+
+/* LM head with repetition penalty and greedy choice, m <= 32 sequences:
+ *   logits[r][c] = dequant(P . q[r]) as bitlinear_gemm computes it;
+ *   every distinct id v in hist[r][0 .. hist_len[r]) with 0 <= v < n has its
+ *   logit l replaced, once, by fl32(l / penalty) if l > 0, else by
+ *   fl32(l * penalty) (ids outside [0, n) are ignored, hist_len[r] is clamped
+ *   to [0, hist_stride]);
+ *   next_token[r] = the lowest c holding the largest penalised logit.
+ * It runs as three launches on the stream: the per-sequence penalty bitmaps,
+ * the skinny MFMA product whose epilogue penalises and forms fp32 argmax keys
+ * (no logits need to be written), and the per-sequence key reduction.
+ *   head, s_head, n, k : the LM head, packed [n][k/4] (n = vocabulary).
+ *   q, act_scale, act_sum : the final-norm quant of the hidden states.
+ *   hist      : device int32 [m][hist_stride] (NULL when hist_stride == 0);
+ *   hist_len  : device int32 [m] (NULL when hist_stride == 0).
+ *   penalty   : > 0 and finite; 1 leaves the logits as they are.
+ *   logits    : device fp32 [m][n] receiving the penalised logits, or NULL.
+ *   next_token: device int32 [m].
+ *   workspace : bitnet_greedy_head_workspace_bytes(m, n) bytes, 256-aligned.
+ * Errors: NULL, SHAPE (m outside [1, 32], ...), ALIGN, VALUE, WORKSPACE, LAUNCH. */
+size_t bitnet_greedy_head_workspace_bytes(int64_t m, int64_t n);
+int bitnet_greedy_head(const uint8_t *head, float s_head, int64_t n, int64_t k,
+                       const int8_t *q, const float *act_scale, const int32_t *act_sum, int64_t m,
+                       const int32_t *hist, int64_t hist_stride, const int32_t *hist_len, float penalty,
+                       float *logits, int32_t *next_token, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/* One greedy decoding step of m <= 32 sequences on the device, with no host
+ * synchronisation and no host round trip, in this order on the stream:
+ *   x = bitnet_embed(tokens)
+ *   x = the layer stream of bitnet_decode_stream over x (stand-in z for attention)
+ *   q = quant(rmsnorm(x, g_final))
+ *   tokens = bitnet_greedy_head(q, hist, hist_len, penalty)     (in place)
+ *   hist[r][hist_len[r]] = tokens[r]; hist_len[r] += 1   (while hist_len < stride)
+ * so the next call continues from the chosen tokens; the host reads tokens or
+ * hist when it wants them (4 bytes per sequence and step).
+ *   embed_table, s_emb, vocab : the embedding ([vocab][d/4]).
+ *   weights, scales, gains, z, n_layers, d, f, eps : as bitnet_decode_stream.
+ *   g_final   : device fp32 [d];  head, s_head : the LM head ([vocab][d/4]).
+ *   tokens    : device int32 [m], the current tokens in, the chosen ones out.
+ *   hist, hist_stride, hist_len, penalty : as bitnet_greedy_head (updated).
+ *   x         : device fp32 [m][d], receives the final hidden states.
+ *   logits    : device fp32 [m][vocab] (penalised) or NULL.
+ *   workspace : bitnet_greedy_step_workspace_bytes(m, d, f, vocab) bytes,
+ *               256-aligned, zero-filled before its first use and then kept
+ *               (it holds the stream's workspace first).
+ * Errors: NULL, SHAPE, ALIGN, VALUE, WORKSPACE, LAUNCH. */
+size_t bitnet_greedy_step_workspace_bytes(int64_t m, int64_t d, int64_t f, int64_t vocab);
+int bitnet_greedy_step(const uint8_t *embed_table, float s_emb, int64_t vocab,
+                       const uint8_t *weights, const float *scales, const float *gains, const float *z,
+                       int64_t n_layers, int64_t d, int64_t f, float eps,
+                       const float *g_final, const uint8_t *head, float s_head,
+                       int32_t *tokens, int64_t m, int32_t *hist, int64_t hist_stride, int32_t *hist_len,
+                       float penalty, float *x, float *logits, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
 /* ------------------------------------------------------- roofline probes --- */
 /* Measurement tools, not part of the method: they give the measured ceilings
  * that throughput is reported against next to the nominal MI355X peaks.

@@ -60,6 +60,8 @@ def load(path=None):
     lib.ref_residual_add.argtypes = [_f32p, _f32p, _i64]
     lib.ref_residual_add.restype = None
     lib.ref_argmax_rows.argtypes = [_i32p, _i64, _i64, _i32p]
+    lib.ref_embed.argtypes = [_u8p, ctypes.c_float, _i64, _i64, _i32p, _i64, _f32p]
+    lib.ref_penalty_argmax.argtypes = [_f32p, _i64, _i64, _i32p, _i64, _i32p, ctypes.c_float, _i32p]
     lib.ref_set_threads.argtypes = [ctypes.c_int]
     lib.ref_set_threads.restype = ctypes.c_int
     if path is None:
@@ -221,6 +223,33 @@ def argmax_rows(acc, lib=None):
     return idx
 
 
+def embed(table, s_e, tokens, d, lib=None):
+    """Ternary embedding lookup: x[r] = t[tokens[r]] / s_e (zero row for an id
+    outside the table). table: packed [vocab][d/4]."""
+    lib = lib or load()
+    table = _c(table, np.uint8)
+    tokens = _c(np.atleast_1d(tokens), np.int32)
+    vocab = table.shape[0]
+    x = np.empty((tokens.size, d), np.float32)
+    _check(lib.ref_embed(_ptr(table, _u8p), ctypes.c_float(s_e), vocab, d, _ptr(tokens, _i32p), tokens.size,
+                         _ptr(x, _f32p)), "embed")
+    return x
+
+
+def penalty_argmax(logits, hist, hist_len, penalty, lib=None):
+    """Repetition penalty over each row's history, then the lowest-index argmax.
+    Returns (idx int32[m], penalised logits). hist: int32 [m][stride]."""
+    lib = lib or load()
+    out = _c(np.atleast_2d(logits), np.float32).copy()
+    m, n = out.shape
+    hist = _c(np.atleast_2d(hist), np.int32)
+    hist_len = _c(np.atleast_1d(hist_len), np.int32)
+    idx = np.empty(m, np.int32)
+    _check(lib.ref_penalty_argmax(_ptr(out, _f32p), m, n, _ptr(hist, _i32p), hist.shape[1], _ptr(hist_len, _i32p),
+                                  ctypes.c_float(penalty), _ptr(idx, _i32p)), "penalty_argmax")
+    return idx, out
+
+
 # --- compositions -------------------------------------------------------------
 
 def ffn(x, norm_gain, sub_norm_gain, eps, w_gate, s_gate, w_up, s_up, w_down, s_down, lib=None):
@@ -282,3 +311,35 @@ def lm_head_argmax(x, g_final, eps, w_head, s_head, lib=None):
     t = unpack(w_head, d, lib)
     acc = matmul_i32(t, q, lib)
     return argmax_rows(acc, lib), acc
+
+
+def greedy_head(x, g_final, eps, w_head, s_head, hist, hist_len, penalty, lib=None):
+    """Final RMSNorm + activation quant, ternary LM head, repetition penalty over
+    each row's history and the greedy choice ("BitNet Model - Complete
+    Inference Pipeline": "Architecture" -- final RMSNorm, LM head, sampling;
+    "GPU Argmax" -- gpuArgmaxWithPenalty). Returns (idx, penalised logits,
+    raw logits)."""
+    x = _c(np.atleast_2d(x), np.float32)
+    d = x.shape[1]
+    q, s, _ = quant_act(x, g_final, eps, lib)
+    logits, _ = bitlinear(w_head, s_head, d, q, s, lib)
+    idx, pen = penalty_argmax(logits, hist, hist_len, penalty, lib)
+    return idx, pen, logits
+
+
+def greedy_step(tokens, table, s_e, layers, g_final, eps, w_head, s_head, hist, hist_len, penalty, lib=None):
+    """One greedy decoding step ("Text Generation / Greedy Decoding"): embed the
+    current tokens, run the layer stream, choose the next tokens with the
+    penalised greedy head, and append them to the histories (a full history
+    is left as it is). Returns (next tokens, new hist, new hist_len, x)."""
+    d = table.shape[1] * 4
+    x = embed(table, s_e, tokens, d, lib)
+    x, _ = chain(x, layers, eps, lib)
+    idx, _, _ = greedy_head(x, g_final, eps, w_head, s_head, hist, hist_len, penalty, lib)
+    hist = np.array(hist, np.int32, copy=True)
+    hist_len = np.array(hist_len, np.int32, copy=True)
+    for r in range(idx.size):
+        if hist_len[r] < hist.shape[1]:
+            hist[r, hist_len[r]] = idx[r]
+            hist_len[r] += 1
+    return idx, hist, hist_len, x

@@ -297,3 +297,64 @@ int ref_argmax_rows(const int32_t *acc, int64_t m, int64_t n, int32_t *idx)
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Ternary embedding lookup ([BN] "Architecture": the embedding layer is TQ2_0
+ * quantized; "Memory Footprint": 50000 x 2560 x 0.25 bytes). Row tokens[r] of
+ * the packed table, dequantized like every ternary tensor, W = t / s_e:
+ * x[r][k] = fl32(t / s_e). A token id outside [0, vocab) gives a zero row.    */
+int ref_embed(const uint8_t *table, float s_e, int64_t vocab, int64_t d, const int32_t *tokens, int64_t m,
+              float *x)
+{
+    if (vocab <= 0 || d <= 0 || m <= 0 || d % 4 != 0) return -2;
+    if (!(s_e > 0.0f)) return -4;
+    int8_t *t = (int8_t *)malloc((size_t)d);
+    if (!t) return -7;
+    int rc = 0;
+    for (int64_t r = 0; r < m && rc == 0; r++) {
+        const int64_t tok = tokens[r];
+        if (tok < 0 || tok >= vocab) {
+            for (int64_t k = 0; k < d; k++) x[r * d + k] = 0.0f;
+            continue;
+        }
+        rc = ref_unpack(table + tok * (d / 4), 1, d, t);
+        for (int64_t k = 0; k < d && rc == 0; k++) x[r * d + k] = (float)t[k] / s_e;
+    }
+    free(t);
+    return rc;
+}
+
+/* Repetition penalty, then the greedy choice ([BN] "GPU Argmax":
+ * repetitionPenaltyKernel penalises the logit of every previous token in
+ * place, gpuArgmaxWithPenalty then takes the argmax; "Text Generation":
+ * repetitionPenalty = 1.1 by default). Per row r, every distinct token id v of
+ * hist[r][0 .. hist_len[r]) with 0 <= v < n has its logit l replaced, once, by
+ * fl32(l / penalty) if l > 0 and by fl32(l * penalty) otherwise; ids outside
+ * [0, n) are ignored. idx[r] = the lowest n holding the largest penalised
+ * logit. logits is updated in place.                                          */
+int ref_penalty_argmax(float *logits, int64_t m, int64_t n, const int32_t *hist, int64_t hist_stride,
+                       const int32_t *hist_len, float penalty, int32_t *idx)
+{
+    if (m <= 0 || n <= 0 || hist_stride < 0) return -2;
+    if (!(penalty > 0.0f)) return -4;
+    unsigned char *seen = (unsigned char *)malloc((size_t)n);
+    if (!seen) return -7;
+    for (int64_t r = 0; r < m; r++) {
+        float *l = logits + r * n;
+        memset(seen, 0, (size_t)n);
+        int64_t len = hist_len ? hist_len[r] : 0;
+        if (len > hist_stride) len = hist_stride;
+        for (int64_t i = 0; i < len; i++) {
+            const int64_t v = hist[r * hist_stride + i];
+            if (v < 0 || v >= n || seen[v]) continue;
+            seen[v] = 1;
+            l[v] = l[v] > 0.0f ? l[v] / penalty : l[v] * penalty;
+        }
+        int64_t best = 0;
+        for (int64_t c = 1; c < n; c++)
+            if (l[c] > l[best]) best = c;
+        idx[r] = (int32_t)best;
+    }
+    free(seen);
+    return 0;
+}

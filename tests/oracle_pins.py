@@ -793,4 +793,92 @@ def pin_residual_exact(o, lib):
         assert Fraction(float(out[i])) == fl32(f32(x[i]) + f32(d[i])), i
 
 
+# --- embedding lookup and the penalised greedy choice --------------------------------------
+
+def pin_embed_closed_form(o, lib):
+    """The ternary embedding returns row tokens[r] of the table dequantized as
+    t / s_e: with s_e = 4 every value is exactly -0.25, 0 or 0.25; with s_e = 37
+    the nonzero values are +-fl32(1/37) (exact rationals); an id outside the
+    table gives a zero row. The rows are checked against the unpacked table the
+    test built (not the oracle's unpack), on a non-square table so a transposed
+    or shifted row fails."""
+    from exact_fp import f32, fl32
+    g = _rng(91)
+    vocab, d = 7, 24
+    t = g.integers(-1, 2, (vocab, d)).astype(np.int8)
+    table = o.pack(t, lib)
+    tokens = np.array([2, 0, 6, -1, 7, 3, 2], np.int32)
+    x = o.embed(table, np.float32(4.0), tokens, d, lib)
+    for r, v in enumerate(tokens):
+        want = t[v].astype(np.float32) * np.float32(0.25) if 0 <= v < vocab else np.zeros(d, np.float32)
+        assert (x[r] == want).all(), (r, v)
+    x = o.embed(table, np.float32(37.0), tokens, d, lib)
+    inv = fl32(Fraction(1) / f32(np.float32(37.0)))
+    for r, v in enumerate(tokens):
+        for k in range(d):
+            want = (int(t[v, k]) * inv) if 0 <= v < vocab else Fraction(0)
+            assert Fraction(float(x[r, k])) == want, (r, k)
+    assert (x[3] == 0).all() and (x[4] == 0).all() and not np.signbit(x[3]).any()
+
+
+def pin_embed_one_hot_rows(o, lib):
+    """Table rows with a single +1 (the rest -1): the lookup of row v has +1/s_e
+    exactly at that column and -1/s_e everywhere else."""
+    vocab, d = 5, 16
+    t = -np.ones((vocab, d), np.int8)
+    cols = [0, 15, 7, 8, 3]
+    for v, c in enumerate(cols):
+        t[v, c] = 1
+    x = o.embed(o.pack(t, lib), np.float32(2.0), np.arange(vocab, dtype=np.int32), d, lib)
+    for v, c in enumerate(cols):
+        want = np.full(d, -0.5, np.float32)
+        want[c] = 0.5
+        assert (x[v] == want).all(), v
+
+
+def _penalty_cases():
+    for row in _read_fixture("penalty_cases.txt"):
+        lg, hist, p, idx, bits, _why = [f.strip() for f in row.split("|")]
+        logits = np.array([float(v) for v in lg.split()], np.float32)
+        h = [int(v) for v in hist.split()]
+        yield logits, h, np.float32(float(p)), int(idx), [int(b, 16) for b in bits.split()]
+
+
+def pin_penalty_golden(o, lib):
+    """Hand-worked penalised greedy choices (tests/golden/penalty_cases.txt): the
+    index and the bits of every penalised logit, one row at a time and all
+    rows at once (each row with its own history, padded history rows and a
+    history length below the stride)."""
+    cases = list(_penalty_cases())
+    for logits, h, p, idx, bits in cases:
+        hist = np.array([h + [0]], np.int32)  # one slot past the length: must be ignored
+        got, pen = o.penalty_argmax(logits.reshape(1, -1), hist, np.array([len(h)], np.int32), p, lib)
+        assert int(got[0]) == idx, (logits, h, p, int(got[0]), idx)
+        assert pen[0].view(np.uint32).tolist() == bits, (logits, h, pen[0])
+
+
+def pin_penalty_rows_are_independent(o, lib):
+    """Several rows at once: row r uses only hist[r][0 .. hist_len[r]); a length
+    beyond the stride is clamped to it."""
+    g = _rng(92)
+    m, n, stride = 5, 40, 6
+    logits = g.standard_normal((m, n)).astype(np.float32)
+    hist = g.integers(-3, n + 3, (m, stride)).astype(np.int32)
+    hist_len = np.array([0, 3, 6, 2, 99], np.int32)
+    idx, pen = o.penalty_argmax(logits, hist, hist_len, np.float32(1.3), lib)
+    for r in range(m):
+        one, pen1 = o.penalty_argmax(logits[r:r + 1], hist[r:r + 1, :min(hist_len[r], stride)],
+                                     np.array([min(hist_len[r], stride)], np.int32), np.float32(1.3), lib)
+        assert idx[r] == one[0] and (pen[r] == pen1[0]).all(), r
+        touched = {int(v) for v in hist[r, :min(hist_len[r], stride)] if 0 <= v < n}
+        for c in range(n):
+            if c not in touched:
+                assert pen[r, c] == logits[r, c]
+            elif logits[r, c] > 0:
+                assert pen[r, c] < logits[r, c]
+            else:
+                assert pen[r, c] <= logits[r, c]
+        assert idx[r] == int(np.argmax(pen[r]))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

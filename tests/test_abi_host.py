@@ -282,3 +282,80 @@ def test_header_states_the_oracle_partial_order():
     assert m, "the header does not state ascending butterfly offsets"
     assert int(m.group(1)) == oracle_partials // 2
     assert "for (int off = 1; off < ORACLE_PARTIALS; off *= 2)" in src
+
+
+def test_embed_checks():
+    f = bl._lib.bitnet_embed
+    ok = dict(t=A, s=40.0, v=100, d=64, tok=A, m=2, x=A)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return f(a["t"], a["s"], a["v"], a["d"], a["tok"], a["m"], a["x"], S)
+
+    assert call(t=None) == bl.BL_ERR_NULL
+    assert call(tok=None) == bl.BL_ERR_NULL
+    assert call(x=None) == bl.BL_ERR_NULL
+    assert call(d=96) == bl.BL_ERR_SHAPE
+    assert call(v=0) == bl.BL_ERR_SHAPE
+    assert call(m=0) == bl.BL_ERR_SHAPE
+    assert call(t=A + 4) == bl.BL_ERR_ALIGN
+    assert call(x=A + 4) == bl.BL_ERR_ALIGN
+    assert call(tok=U) == bl.BL_ERR_ALIGN
+    assert call(s=0.0) == bl.BL_ERR_VALUE
+    assert call(s=float("inf")) == bl.BL_ERR_VALUE
+
+
+def test_greedy_head_checks():
+    f = bl._lib.bitnet_greedy_head
+    m, n = 4, 1000
+    need = bl.bitnet_greedy_head_workspace_bytes(m, n)
+    assert need > 0 and bl.bitnet_greedy_head_workspace_bytes(33, n) == 0
+    ok = dict(h=A, s=40.0, n=n, k=64, q=A, sa=A, qs=A, m=m, hist=A, stride=8, hl=A, p=1.1, lg=None, nx=A, ws=A,
+              wsb=need)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return f(a["h"], a["s"], a["n"], a["k"], a["q"], a["sa"], a["qs"], a["m"], a["hist"], a["stride"], a["hl"],
+                 a["p"], a["lg"], a["nx"], a["ws"], a["wsb"], S)
+
+    assert call(h=None) == bl.BL_ERR_NULL
+    assert call(nx=None) == bl.BL_ERR_NULL
+    assert call(hist=None) == bl.BL_ERR_NULL
+    assert call(hl=None) == bl.BL_ERR_NULL
+    assert call(m=33) == bl.BL_ERR_SHAPE
+    assert call(k=100) == bl.BL_ERR_SHAPE
+    assert call(stride=-1) == bl.BL_ERR_SHAPE
+    assert call(ws=A + 128) == bl.BL_ERR_ALIGN
+    assert call(hist=U) == bl.BL_ERR_ALIGN
+    assert call(p=0.0) == bl.BL_ERR_VALUE
+    assert call(p=float("nan")) == bl.BL_ERR_VALUE
+    assert call(s=-1.0) == bl.BL_ERR_VALUE
+    assert call(wsb=need - 1) == bl.BL_ERR_WORKSPACE
+
+
+def test_greedy_step_checks():
+    f = bl._lib.bitnet_greedy_step
+    m, d, ff, vocab = 2, 64, 128, 500
+    need = bl.bitnet_greedy_step_workspace_bytes(m, d, ff, vocab)
+    assert need >= bl.bitnet_stream_workspace_bytes(m, d, ff)
+    ok = dict(e=A, se=30.0, v=vocab, w=A, sc=A, g=A, z=A, L=2, d=d, f=ff, eps=1e-5, gf=A, h=A, sh=40.0, tok=A, m=m,
+              hist=A, stride=4, hl=A, p=1.1, x=A, lg=None, ws=A, wsb=need)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return f(a["e"], a["se"], a["v"], a["w"], a["sc"], a["g"], a["z"], a["L"], a["d"], a["f"], a["eps"], a["gf"],
+                 a["h"], a["sh"], a["tok"], a["m"], a["hist"], a["stride"], a["hl"], a["p"], a["x"], a["lg"], a["ws"],
+                 a["wsb"], S)
+
+    assert call(e=None) == bl.BL_ERR_NULL
+    assert call(tok=None) == bl.BL_ERR_NULL
+    assert call(z=None) == bl.BL_ERR_NULL
+    assert call(hist=None) == bl.BL_ERR_NULL
+    assert call(m=33) == bl.BL_ERR_SHAPE
+    assert call(d=100) == bl.BL_ERR_SHAPE
+    assert call(L=0) == bl.BL_ERR_SHAPE
+    assert call(x=A + 4) == bl.BL_ERR_ALIGN
+    assert call(ws=A + 16) == bl.BL_ERR_ALIGN
+    assert call(p=-1.0) == bl.BL_ERR_VALUE
+    assert call(se=0.0) == bl.BL_ERR_VALUE
+    assert call(wsb=need - 1) == bl.BL_ERR_WORKSPACE

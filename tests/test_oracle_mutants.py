@@ -67,6 +67,20 @@ C_MUTANTS = [
     ("aq_round_exact_product", "float r = nearbyintf(v);\n            if (r > 127.0f)",
      "float r = (float)nearbyint((double)yr[i] * (double)scale);\n            if (r > 127.0f)"),
     ("aq_div_then_mul", "float v = yr[i] * scale;", "float v = yr[i] / (amax > floor_ ? amax : floor_) * 127.0f;"),
+    # embedding lookup
+    ("emb_no_scale", "x[r * d + k] = (float)t[k] / s_e;", "x[r * d + k] = (float)t[k];"),
+    ("emb_times_scale", "x[r * d + k] = (float)t[k] / s_e;", "x[r * d + k] = (float)t[k] * s_e;"),
+    ("emb_wrong_row", "rc = ref_unpack(table + tok * (d / 4), 1, d, t);",
+     "rc = ref_unpack(table + (tok ^ 1) % vocab * (d / 4), 1, d, t);"),
+    ("emb_negative_zero", "for (int64_t k = 0; k < d; k++) x[r * d + k] = 0.0f;",
+     "for (int64_t k = 0; k < d; k++) x[r * d + k] = -0.0f;"),
+    # repetition penalty and greedy choice
+    ("pen_directions_swapped", "l[v] = l[v] > 0.0f ? l[v] / penalty : l[v] * penalty;",
+     "l[v] = l[v] > 0.0f ? l[v] * penalty : l[v] / penalty;"),
+    ("pen_always_divide", "l[v] = l[v] > 0.0f ? l[v] / penalty : l[v] * penalty;", "l[v] = l[v] / penalty;"),
+    ("pen_every_occurrence", "if (v < 0 || v >= n || seen[v]) continue;", "if (v < 0 || v >= n) continue;"),
+    ("pen_last_tie", "if (l[c] > l[best]) best = c;\n        idx[r]", "if (l[c] >= l[best]) best = c;\n        idx[r]"),
+    ("pen_whole_stride", "int64_t len = hist_len ? hist_len[r] : 0;", "int64_t len = hist_stride;"),
 ]
 
 # Equivalent rewrites, not mutants: they give the same bits on every input, so

@@ -34,6 +34,7 @@ W_GEMV, W_FFN, W_STREAM, W_PREFILL, W_BATCHED = 0, 1, 2, 3, 4
 # Tensor ids within a layer.
 T_Q, T_K, T_V, T_O, T_GATE, T_UP, T_DOWN = range(7)
 T_X, T_Z, T_G_ATTN, T_G_ATTN_SUB, T_G_FFN, T_G_FFN_SUB, T_HEAD, T_G_FINAL = range(7, 15)
+T_EMB, T_TOKENS = 15, 16
 LINEAR_NAMES = ("wq", "wk", "wv", "wo", "wg", "wu", "wd")
 SCALE_NAMES = ("sq", "sk", "sv", "so", "sg", "su", "sd")
 
