@@ -395,6 +395,34 @@ def greedy_leg(bl, torch, T, dev0, dev, host_layers, L, d, f):
     return res
 
 
+def sampling_leg(bl, torch, T, dev0, check):
+    """Top-k (k = 50) and nucleus (p = 0.9) sampling at temperature 0.8 of 32
+    rows of 50000 logits (N(0, 3^2)), with one uniform draw per row."""
+    m, n = 32, W.BITNET_3B["vocab"]
+    g = W.rng(W.W_BATCHED, 5, 0)
+    lh = (g.standard_normal((m, n)) * 3.0).astype(np.float32)
+    uh = g.random(m)
+    logits, u = T(lh), T(uh)
+    tok = torch.empty(m, dtype=torch.int32, device=dev0)
+    ws = torch.empty(bl.bitnet_sample_workspace_bytes(m, n), dtype=torch.uint8, device=dev0)
+    res = {"workload": "32 rows x 50000 logits, temperature 0.8, one draw per row"}
+    for name, fn, param in (("topk_50", bl.bitnet_sample_topk, 50), ("topp_0.9", bl.bitnet_sample_topp, 0.9)):
+        for _ in range(3):
+            fn(logits, param, 0.8, u, tok, ws)
+        iters = 20
+        with Timer() as t:
+            for _ in range(iters):
+                fn(logits, param, 0.8, u, tok, ws)
+        entry = {"us_per_call": round(t.ms / iters * 1e3, 2)}
+        if check:
+            import oracle
+            want = (oracle.sample_topk if name.startswith("topk") else oracle.sample_topp)(lh, param, 0.8, uh)
+            entry["matches_oracle"] = bool(np.array_equal(tok.cpu().numpy(), want))
+        res[name] = entry
+    log(f"sampling: {res}")
+    return res
+
+
 def prefill_ffn_leg(bl, torch, T, dev0, check):
     """The FFN sub-layer at 2048 tokens (d = 2560, f = 10240): quant of x, the
     paired gate/up MFMA GEMM with relu(gate)^2 * up in its epilogue, sub-norm +
@@ -697,6 +725,9 @@ def extra_measurements(bl, torch, T, dev0, check=True):
             got.view(np.uint32), oy.view(np.uint32))), "max_rel_err": float(err.max())}
         log(f"prefill parity on {len(rows)} rows: {out['prefill']['parity_sampled_rows']}")
     del p, x, q, y
+
+    # ---- top-k / nucleus sampling over the vocabulary ----
+    out["sampling"] = sampling_leg(bl, torch, T, dev0, check)
 
     # ---- prefill FFN, 2048 tokens, BitNet-3B shapes ----
     out["prefill_ffn"] = prefill_ffn_leg(bl, torch, T, dev0, check)

@@ -38,7 +38,7 @@ EXPORTS = (
     "bitlinear_probe_read", "bitlinear_probe_mfma_ops", "bitlinear_probe_mfma_i8",
     "bitlinear_gemm_noalloc", "bitlinear_gemm_noalloc_max_scratch_bytes",
     "bitnet_embed", "bitnet_greedy_head_workspace_bytes", "bitnet_greedy_head", "bitnet_greedy_step_workspace_bytes",
-    "bitnet_greedy_step",
+    "bitnet_greedy_step", "bitnet_sample_workspace_bytes", "bitnet_sample_topk", "bitnet_sample_topp",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -94,6 +94,9 @@ _SIGS = {
     "bitnet_greedy_step_workspace_bytes": ([_I64, _I64, _I64, _I64], _SZ),
     "bitnet_greedy_step": ([_P, _F, _I64, _P, _P, _P, _P, _I64, _I64, _I64, _F, _P, _P, _F, _P, _I64, _P, _I64, _P,
                             _F, _P, _P, _P, _SZ, _P], _I),
+    "bitnet_sample_workspace_bytes": ([_I64, _I64], _SZ),
+    "bitnet_sample_topk": ([_P, _I64, _I64, _I64, _F, _P, _P, _P, _SZ, _P], _I),
+    "bitnet_sample_topp": ([_P, _I64, _I64, _F, _F, _P, _P, _P, _SZ, _P], _I),
     "bitlinear_probe_read": ([_P, _SZ, _P, _P], _I),
     "bitlinear_probe_mfma_ops": ([_I64], _I64),
     "bitlinear_probe_mfma_i8": ([_I64, _P, _P], _I),
@@ -332,6 +335,30 @@ def bitnet_greedy_step(embed_table, s_emb, weights, scales, gains, z, n_layers, 
                                    _dev(logits, torch.float32, "logits", True), _dev(workspace, None, "workspace"),
                                    workspace.numel() * workspace.element_size(), _stream(stream)),
            "bitnet_greedy_step")
+
+
+# ---- top-k / nucleus sampling ----------------------------------------------------------
+
+def bitnet_sample_workspace_bytes(m, n):
+    return _lib.bitnet_sample_workspace_bytes(m, n)
+
+
+def bitnet_sample_topk(logits, k, temperature, u, token, workspace, stream=None):
+    """Top-k sampling of each row of logits[m][n] with its uniform u[r] (fp64) in [0, 1)."""
+    m, n = logits.shape
+    _check(_lib.bitnet_sample_topk(_dev(logits, torch.float32, "logits"), m, n, int(k), float(temperature),
+                                   _dev(u, torch.float64, "u"), _dev(token, torch.int32, "token"),
+                                   _dev(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
+                                   _stream(stream)), "bitnet_sample_topk")
+
+
+def bitnet_sample_topp(logits, p, temperature, u, token, workspace, stream=None):
+    """Nucleus (top-p) sampling of each row of logits[m][n] with its uniform u[r] (fp64) in [0, 1)."""
+    m, n = logits.shape
+    _check(_lib.bitnet_sample_topp(_dev(logits, torch.float32, "logits"), m, n, float(p), float(temperature),
+                                   _dev(u, torch.float64, "u"), _dev(token, torch.int32, "token"),
+                                   _dev(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
+                                   _stream(stream)), "bitnet_sample_topp")
 
 
 # ---- roofline probes (measurement tools) -----------------------------------------------

@@ -676,4 +676,48 @@ int bitnet_greedy_step(const uint8_t* embed_table, float s_emb, int64_t vocab, c
     return bl::launch_append(tokens, (int)m, hist, (int)hist_stride, hist_len, nullptr, s);
 }
 
+// ---- top-k and nucleus sampling --------------------------------------------------
+
+size_t bitnet_sample_workspace_bytes(int64_t m, int64_t n)
+{
+    if (m <= 0 || n <= 0 || m > 0x7fffffff || n > 0x7fffffff) return 0;
+    return align_up((size_t)m * (size_t)n * 8, 256);
+}
+
+namespace {
+
+int sample_check(const float* logits, int64_t m, int64_t n, float temperature, const double* u, const int32_t* token,
+                 const void* workspace, size_t workspace_bytes)
+{
+    if (!logits || !u || !token || !workspace) return BL_ERR_NULL;
+    if (!dim_ok(m) || !dim_ok(n) || m > 0x7fffffff || n > 0x7fffffff) return BL_ERR_SHAPE;
+    if (!aligned(logits, 4) || !aligned(u, 8) || !aligned(token, 4) || !aligned(workspace, 256)) return BL_ERR_ALIGN;
+    if (!(temperature > 0.0f) || !(temperature < INFINITY)) return BL_ERR_VALUE;
+    if (workspace_bytes < bitnet_sample_workspace_bytes(m, n)) return BL_ERR_WORKSPACE;
+    return BL_OK;
+}
+
+}  // namespace
+
+int bitnet_sample_topk(const float* logits, int64_t m, int64_t n, int64_t k, float temperature, const double* u,
+                       int32_t* token, void* workspace, size_t workspace_bytes, void* stream)
+{
+    const int rc = sample_check(logits, m, n, temperature, u, token, workspace, workspace_bytes);
+    if (rc != BL_OK) return rc;
+    if (k < 1) return BL_ERR_VALUE;
+    const int kk = (int)std::min<int64_t>(k, n);
+    return bl::launch_sample(false, logits, (int)m, (int)n, kk, 1.0f, temperature, u, token,
+                             static_cast<long long*>(workspace), as_stream(stream));
+}
+
+int bitnet_sample_topp(const float* logits, int64_t m, int64_t n, float p, float temperature, const double* u,
+                       int32_t* token, void* workspace, size_t workspace_bytes, void* stream)
+{
+    const int rc = sample_check(logits, m, n, temperature, u, token, workspace, workspace_bytes);
+    if (rc != BL_OK) return rc;
+    if (!(p > 0.0f) || !(p < INFINITY)) return BL_ERR_VALUE;
+    return bl::launch_sample(true, logits, (int)m, (int)n, 1, p, temperature, u, token,
+                             static_cast<long long*>(workspace), as_stream(stream));
+}
+
 }  // extern "C"

@@ -139,6 +139,11 @@ int launch_penalty_bits(const int32_t* hist, int stride, const int32_t* hist_len
 int launch_append(const int32_t* next, int m, int32_t* hist, int stride, int32_t* hist_len, int32_t* tokens,
                   hipStream_t s);
 
+// Top-k (topp false, k) or nucleus (topp true, p) sampling of m rows of n
+// logits with the caller's uniforms u (sample.hip); wbuf: m * n int64.
+int launch_sample(bool topp, const float* logits, int m, int n, int k, float p, float temperature, const double* u,
+                  int32_t* out, long long* wbuf, hipStream_t s);
+
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 }  // namespace bl

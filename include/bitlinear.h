@@ -389,6 +389,41 @@ int bitnet_greedy_step(const uint8_t *embed_table, float s_emb, int64_t vocab,
                        float penalty, float *x, float *logits, void *workspace, size_t workspace_bytes,
                        void *stream);
 
+/* ------------------------------------------------- top-k / nucleus sampling --- */
+/* Sampling of the next token from m rows of n fp32 logits ("BitNet Model -
+ * Complete Inference Pipeline", section "Text Generation": Top-k Sampling and
+ * Nucleus (Top-p) Sampling; sampleTopK, sampleNucleus). The random numbers are
+ * the caller's: u[r] uniform in [0, 1), one per row (device fp64; values
+ * outside [0, 1) are clamped into the kept set).
+ * Definition (both calls):
+ *   - tokens are taken in sorted order: descending logit, the lower index first
+ *     among equal logits (-0 and +0 are equal);
+ *   - token i weighs w_i = rne(2^40 * E((l_i - l_max) / T)), an exact int64,
+ *     with (l_i - l_max) / T one correctly rounded fp64 division and E the
+ *     fp64 exponential on [-32, 0] given by: k = rne(x * fl64(1/ln2)),
+ *     r = (x - k * H) - k * L (H = 0x1.62e42fee00000p-1, L = 0x1.a39ef35793c76p-33:
+ *     ln2 split into a 32-bit head and a tail), e^r = the Taylor series through
+ *     r^13 / 13! by Horner's rule, scaled by 2^k; E = 0 below -32. Every fp64
+ *     operation rounds on its own;
+ *   - top-k keeps the first min(k, n) tokens; top-p keeps the shortest sorted
+ *     prefix whose weight reaches max(1, min(Z, ceil(fl64(p * Z)))), Z = the total
+ *     weight (the smallest set with probability >= p);
+ *   - with M the kept weight and r = min(M - 1, max(0, floor(fl64(u * M)))), the
+ *     chosen token is the first kept token whose cumulative weight exceeds r.
+ * Each row is one 1024-thread workgroup: weights, then radix selections over
+ * 64-bit (logit, index) keys whose per-digit weight sums are exact integers.
+ *   logits    : device fp32 [m][n] (finite).
+ *   temperature : > 0 and finite.  k >= 1 (k > n keeps all); p > 0 (p >= 1 keeps
+ *               every token of nonzero weight).
+ *   token     : device int32 [m].
+ *   workspace : bitnet_sample_workspace_bytes(m, n) bytes (the weights), 256-aligned.
+ * Errors: NULL, SHAPE, ALIGN, VALUE, WORKSPACE, LAUNCH. */
+size_t bitnet_sample_workspace_bytes(int64_t m, int64_t n);
+int bitnet_sample_topk(const float *logits, int64_t m, int64_t n, int64_t k, float temperature, const double *u,
+                       int32_t *token, void *workspace, size_t workspace_bytes, void *stream);
+int bitnet_sample_topp(const float *logits, int64_t m, int64_t n, float p, float temperature, const double *u,
+                       int32_t *token, void *workspace, size_t workspace_bytes, void *stream);
+
 /* ------------------------------------------------------- roofline probes --- */
 /* Measurement tools, not part of the method: they give the measured ceilings
  * that throughput is reported against next to the nominal MI355X peaks.

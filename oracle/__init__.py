@@ -62,6 +62,10 @@ def load(path=None):
     lib.ref_argmax_rows.argtypes = [_i32p, _i64, _i64, _i32p]
     lib.ref_embed.argtypes = [_u8p, ctypes.c_float, _i64, _i64, _i32p, _i64, _f32p]
     lib.ref_penalty_argmax.argtypes = [_f32p, _i64, _i64, _i32p, _i64, _i32p, ctypes.c_float, _i32p]
+    lib.ref_exp_neg.argtypes = [ctypes.c_double]
+    lib.ref_exp_neg.restype = ctypes.c_double
+    lib.ref_sample.argtypes = [_f32p, _i64, _i64, ctypes.c_int, _i64, ctypes.c_float, ctypes.c_float,
+                               ctypes.POINTER(ctypes.c_double), _i32p]
     lib.ref_set_threads.argtypes = [ctypes.c_int]
     lib.ref_set_threads.restype = ctypes.c_int
     if path is None:
@@ -248,6 +252,34 @@ def penalty_argmax(logits, hist, hist_len, penalty, lib=None):
     _check(lib.ref_penalty_argmax(_ptr(out, _f32p), m, n, _ptr(hist, _i32p), hist.shape[1], _ptr(hist_len, _i32p),
                                   ctypes.c_float(penalty), _ptr(idx, _i32p)), "penalty_argmax")
     return idx, out
+
+
+def exp_neg(x, lib=None):
+    """The sampler's exponential of x in [-32, 0] (0 below -32)."""
+    lib = lib or load()
+    return float(lib.ref_exp_neg(float(x)))
+
+
+def _sample(logits, mode, k, p, temperature, u, lib):
+    lib = lib or load()
+    logits = _c(np.atleast_2d(logits), np.float32)
+    m, n = logits.shape
+    u = _c(np.atleast_1d(u), np.float64)
+    assert u.size == m
+    idx = np.empty(m, np.int32)
+    _check(lib.ref_sample(_ptr(logits, _f32p), m, n, mode, int(k), ctypes.c_float(p), ctypes.c_float(temperature),
+                          u.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), _ptr(idx, _i32p)), "sample")
+    return idx
+
+
+def sample_topk(logits, k, temperature, u, lib=None):
+    """Top-k sampling of each row with its uniform draw u[r] in [0, 1)."""
+    return _sample(logits, 0, k, 1.0, temperature, u, lib)
+
+
+def sample_topp(logits, p, temperature, u, lib=None):
+    """Nucleus (top-p) sampling of each row with its uniform draw u[r] in [0, 1)."""
+    return _sample(logits, 1, 1, p, temperature, u, lib)
 
 
 # --- compositions -------------------------------------------------------------

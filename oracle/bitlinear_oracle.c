@@ -358,3 +358,121 @@ int ref_penalty_argmax(float *logits, int64_t m, int64_t n, const int32_t *hist,
     free(seen);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Top-k and nucleus (top-p) sampling ([BN] "Text Generation": Top-k Sampling,
+ * Nucleus (Top-p) Sampling; sampleTopK / sampleNucleus with a temperature and
+ * a random number generator). The random numbers are inputs: u[r] uniform in
+ * [0, 1), one per row. Readings (the pages give the steps, not the arithmetic):
+ *  - tokens are taken in the pages' sorted order: descending logit, the lower
+ *    index first among equal logits;
+ *  - the softmax weight of token i is e^((l_i - l_max) / T), with the
+ *    exponential below, rounded to a fixed-point integer with 40 fractional
+ *    bits (weights below 2^-41 of the largest become 0), so every sum of
+ *    weights is exact whatever its order;
+ *  - top-k keeps the first min(k, n) tokens of the sorted order;
+ *  - the nucleus is the shortest prefix of the sorted order whose weight
+ *    reaches ceil(p * Z), Z the total weight (the smallest set with cumulative
+ *    probability >= p of sampleNucleus; at least one token);
+ *  - sampling draws r = floor(u * M), M the kept weight, and picks the first
+ *    kept token in sorted order whose cumulative weight exceeds r.            */
+
+/* e^x for x in [-32, 0] in fp64: Cody-Waite range reduction x = k ln2 + r
+ * (ln2 split into a 32-significant-bit head, so k * head is exact, and a
+ * tail), e^r from its Taylor series through r^13 / 13! by Horner's rule
+ * (|r| <= 0.35: truncation below 2^-58), then the exact scaling by 2^k.
+ * Below -32 the result is 0 (it would round to a zero weight anyway).       */
+static const double ORACLE_LN2_HEAD = 0x1.62e42fee00000p-1;
+static const double ORACLE_LN2_TAIL = 0x1.a39ef35793c76p-33;
+static const double ORACLE_INV_LN2 = 0x1.71547652b82fep+0;
+
+double ref_exp_neg(double x)
+{
+    if (x < -32.0) return 0.0;
+    const double k = nearbyint(x * ORACLE_INV_LN2);
+    const double r = (x - k * ORACLE_LN2_HEAD) - k * ORACLE_LN2_TAIL;
+    /* coefficients 1 / j! for j = 13 .. 0 */
+    static const double inv_fact[14] = {1.0,
+                                        1.0,
+                                        1.0 / 2.0,
+                                        1.0 / 6.0,
+                                        1.0 / 24.0,
+                                        1.0 / 120.0,
+                                        1.0 / 720.0,
+                                        1.0 / 5040.0,
+                                        1.0 / 40320.0,
+                                        1.0 / 362880.0,
+                                        1.0 / 3628800.0,
+                                        1.0 / 39916800.0,
+                                        1.0 / 479001600.0,
+                                        1.0 / 6227020800.0};
+    double poly = inv_fact[13];
+    for (int j = 12; j >= 0; j--) poly = poly * r + inv_fact[j];
+    return ldexp(poly, (int)k);
+}
+
+static const float *sample_row_logits;
+
+static int sample_order_cmp(const void *pa, const void *pb)
+{
+    const int64_t a = *(const int64_t *)pa, b = *(const int64_t *)pb;
+    const float la = sample_row_logits[a], lb = sample_row_logits[b];
+    if (la != lb) return la > lb ? -1 : 1;
+    return a < b ? -1 : (a > b ? 1 : 0);
+}
+
+/* mode 0: top-k with k; mode 1: nucleus with p. idx[r] = the sampled token.  */
+int ref_sample(const float *logits, int64_t m, int64_t n, int mode, int64_t k, float p, float temperature,
+               const double *u, int32_t *idx)
+{
+    if (m <= 0 || n <= 0 || (mode != 0 && mode != 1)) return -2;
+    if (!(temperature > 0.0f) || (mode == 0 && k <= 0) || (mode == 1 && !(p > 0.0f))) return -4;
+    int64_t *order = (int64_t *)malloc(sizeof(int64_t) * (size_t)n);
+    int64_t *w = (int64_t *)malloc(sizeof(int64_t) * (size_t)n);
+    if (!order || !w) {
+        free(order);
+        free(w);
+        return -7;
+    }
+    for (int64_t row = 0; row < m; row++) {
+        const float *l = logits + row * n;
+        float lmax = l[0];
+        for (int64_t i = 1; i < n; i++)
+            if (l[i] > lmax) lmax = l[i];
+        int64_t total = 0;
+        for (int64_t i = 0; i < n; i++) {
+            const double x = ((double)l[i] - (double)lmax) / (double)temperature;
+            w[i] = (int64_t)nearbyint(ldexp(ref_exp_neg(x), 40));
+            total += w[i];
+        }
+        for (int64_t i = 0; i < n; i++) order[i] = i;
+        sample_row_logits = l;
+        qsort(order, (size_t)n, sizeof(int64_t), sample_order_cmp);
+        int64_t kept = 0; /* number of kept tokens (a prefix of order) */
+        if (mode == 0) {
+            kept = k < n ? k : n;
+        } else {
+            double tgt = ceil((double)p * (double)total);
+            int64_t target = tgt > (double)total ? total : (int64_t)tgt;
+            if (target < 1) target = 1;
+            int64_t cum = 0;
+            while (kept < n && cum < target) cum += w[order[kept++]];
+        }
+        int64_t mass = 0;
+        for (int64_t j = 0; j < kept; j++) mass += w[order[j]];
+        double rd = floor(u[row] * (double)mass);
+        int64_t r = rd < 0.0 ? 0 : (rd >= (double)mass ? mass - 1 : (int64_t)rd);
+        int64_t cum = 0, chosen = order[0];
+        for (int64_t j = 0; j < kept; j++) {
+            cum += w[order[j]];
+            if (cum > r) {
+                chosen = order[j];
+                break;
+            }
+        }
+        idx[row] = (int32_t)chosen;
+    }
+    free(order);
+    free(w);
+    return 0;
+}

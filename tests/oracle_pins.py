@@ -881,4 +881,111 @@ def pin_penalty_rows_are_independent(o, lib):
         assert idx[r] == int(np.argmax(pen[r]))
 
 
+# --- top-k and nucleus sampling ----------------------------------------------------------------
+
+def pin_sample_exp_vs_library(o, lib):
+    """The sampler's exponential against the C library's (math.exp): within 2
+    fp64 ulps on a grid and on random points of [-32, 0], exactly 1 at 0 and
+    exactly 2^-k at -k ln2 for small k, 0 below -32, and monotone."""
+    import math
+    g = _rng(93)
+    xs = np.concatenate([np.linspace(-32.0, 0.0, 4001), -g.random(2000) * 32.0, -g.random(500) * 1e-6])
+    prev = None
+    for x in np.sort(xs):
+        got = o.exp_neg(float(x), lib)
+        want = math.exp(float(x))
+        assert abs(got - want) <= 2 * abs(want) * 2.0 ** -52, (x, got, want)
+        if prev is not None:
+            assert got >= prev
+        prev = got
+    assert o.exp_neg(0.0, lib) == 1.0
+    assert o.exp_neg(-32.5, lib) == 0.0 and o.exp_neg(-1e9, lib) == 0.0
+
+
+def _grid_counts(o, lib, logits, sampler, n_u):
+    """Tokens drawn for the regular u grid (i + 1/2) / n_u: each token's count
+    divided by n_u is within 1 / n_u of its probability, for any monotone map."""
+    us = (np.arange(n_u) + 0.5) / n_u
+    toks = sampler(np.repeat(logits.reshape(1, -1), n_u, 0), us)
+    return toks, np.bincount(toks, minlength=logits.size) / n_u
+
+
+def pin_sample_topk_distribution(o, lib):
+    """Top-k draws over a regular grid of u reproduce the softmax of the k
+    largest logits at temperature T (probabilities from numpy's exp in fp64),
+    never choose a token outside them, and walk the tokens in descending logit
+    order as u grows."""
+    g = _rng(94)
+    logits = (g.standard_normal(12) * 1.5).astype(np.float32)
+    k, t = 6, 0.8
+    toks, freq = _grid_counts(o, lib, logits, lambda L, U: o.sample_topk(L, k, t, U, lib), 20000)
+    top = np.argsort(-logits.astype(np.float64), kind="stable")[:k]
+    w = np.exp((logits[top].astype(np.float64) - logits.max()) / t)
+    prob = np.zeros(logits.size)
+    prob[top] = w / w.sum()
+    assert np.all(np.abs(freq - prob) <= 1.0 / 20000 + 1e-9), (freq, prob)
+    ranks = {int(tok): r for r, tok in enumerate(top)}
+    seq = [ranks[int(v)] for v in toks]
+    assert all(a <= b for a, b in zip(seq, seq[1:])), "tokens must be walked in sorted order"
+
+
+def pin_sample_topk_special_cases(o, lib):
+    """k = 1 is the greedy choice (numpy's first argmax) for any u; a tiny
+    temperature leaves only the largest logit; two equal logits split [0, 1) at
+    exactly u = 1/2: the weights are 2^40 each, r = floor(u * 2^41), and the
+    lower index is taken while r < 2^40."""
+    g = _rng(95)
+    logits = g.integers(-3, 4, (6, 9)).astype(np.float32)  # many ties
+    for u in (0.0, 0.3, 0.999999):
+        got = o.sample_topk(logits, 1, 1.0, np.full(6, u), lib)
+        assert (got == np.argmax(logits, axis=1)).all()
+    distinct = (g.permutation(9) - 4.0).astype(np.float32).reshape(1, -1)
+    for u in (0.0, 0.5, 0.9999):
+        assert o.sample_topk(distinct, 9, 1e-4, [u], lib)[0] == int(np.argmax(distinct))
+    pair = np.array([[0.25, 2.0, 2.0, -1.0]], np.float32)
+    assert o.sample_topk(pair, 2, 1.0, [0.5 - 2.0 ** -53], lib)[0] == 1
+    assert o.sample_topk(pair, 2, 1.0, [0.5], lib)[0] == 2
+    assert o.sample_topk(pair, 2, 1.0, [0.0], lib)[0] == 1
+
+
+def pin_sample_tie_order(o, lib):
+    """Among equal logits the lower index comes first: it is kept first at the
+    top-k boundary and sampled for the lower u."""
+    l1 = np.array([[1.0, 3.0, 3.0, 2.0]], np.float32)
+    assert o.sample_topk(l1, 2, 1.0, [0.25], lib)[0] == 1 and o.sample_topk(l1, 2, 1.0, [0.75], lib)[0] == 2
+    l2 = np.array([[3.0, 2.0, 2.0, 1.0]], np.float32)
+    reach = {int(o.sample_topk(l2, 2, 1.0, [u], lib)[0]) for u in np.linspace(0.0, 0.999, 200)}
+    assert reach == {0, 1}
+
+
+def pin_sample_nucleus(o, lib):
+    """Nucleus sets from logits ln(1/2), ln(1/4), ln(1/8), ln(1/16), ln(1/16):
+    the smallest sorted prefix whose probability reaches p, the token that
+    crosses p included (p = 0.6 keeps two tokens, where a literal
+    "cumulative <= p" would keep one), p >= 1 keeps every token; draws over a
+    u grid follow the renormalised probabilities of the kept tokens."""
+    probs = np.array([0.5, 0.25, 0.125, 0.0625, 0.0625])
+    order = np.array([3, 0, 4, 1, 2])  # scatter them, so index order is not sorted order
+    logits = np.empty(5, np.float32)
+    logits[order] = np.log(probs).astype(np.float32)
+    for p, kept in ((0.3, 1), (0.6, 2), (0.74, 2), (0.8, 3), (0.9, 4), (1.0, 5)):
+        toks, freq = _grid_counts(o, lib, logits, lambda L, U: o.sample_topp(L, p, 1.0, U, lib), 4000)
+        assert set(np.unique(toks).tolist()) == set(order[:kept].tolist()), (p, np.unique(toks))
+        w = np.exp(logits[order[:kept]].astype(np.float64) - logits.max())
+        want = np.zeros(5)
+        want[order[:kept]] = w / w.sum()
+        assert np.all(np.abs(freq - want) <= 1.0 / 4000 + 1e-9), (p, freq, want)
+
+
+def pin_sample_temperature(o, lib):
+    """Temperature divides the logits: T = 2 flattens two tokens with logits
+    ln(3) and 0 from probabilities 3/4, 1/4 to sqrt(3) / (1 + sqrt(3)) and
+    1 / (1 + sqrt(3))."""
+    logits = np.array([np.log(3.0), 0.0], np.float32)
+    for t in (1.0, 2.0, 0.5):
+        _, freq = _grid_counts(o, lib, logits, lambda L, U: o.sample_topk(L, 2, t, U, lib), 10000)
+        w = np.exp((logits.astype(np.float64) - logits.max()) / t)
+        assert abs(freq[0] - w[0] / w.sum()) <= 1e-4 + 1e-9, (t, freq)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -359,3 +359,27 @@ def test_greedy_step_checks():
     assert call(p=-1.0) == bl.BL_ERR_VALUE
     assert call(se=0.0) == bl.BL_ERR_VALUE
     assert call(wsb=need - 1) == bl.BL_ERR_WORKSPACE
+
+
+def test_sample_checks():
+    m, n = 3, 100
+    need = bl.bitnet_sample_workspace_bytes(m, n)
+    assert need >= m * n * 8
+    for name in ("bitnet_sample_topk", "bitnet_sample_topp"):
+        f = getattr(bl._lib, name)
+        par = 5 if name.endswith("topk") else 0.9
+
+        def call(**kw):
+            a = {**dict(l=A, m=m, n=n, p=par, t=1.0, u=A, tok=A, ws=A, wsb=need), **kw}
+            return f(a["l"], a["m"], a["n"], a["p"], a["t"], a["u"], a["tok"], a["ws"], a["wsb"], S)
+
+        assert call(l=None) == bl.BL_ERR_NULL
+        assert call(u=None) == bl.BL_ERR_NULL
+        assert call(tok=None) == bl.BL_ERR_NULL
+        assert call(m=0) == bl.BL_ERR_SHAPE
+        assert call(n=0) == bl.BL_ERR_SHAPE
+        assert call(u=A + 4) == bl.BL_ERR_ALIGN
+        assert call(ws=A + 8) == bl.BL_ERR_ALIGN
+        assert call(t=0.0) == bl.BL_ERR_VALUE
+        assert call(p=0) == bl.BL_ERR_VALUE
+        assert call(wsb=need - 1) == bl.BL_ERR_WORKSPACE

@@ -81,6 +81,19 @@ C_MUTANTS = [
     ("pen_every_occurrence", "if (v < 0 || v >= n || seen[v]) continue;", "if (v < 0 || v >= n) continue;"),
     ("pen_last_tie", "if (l[c] > l[best]) best = c;\n        idx[r]", "if (l[c] >= l[best]) best = c;\n        idx[r]"),
     ("pen_whole_stride", "int64_t len = hist_len ? hist_len[r] : 0;", "int64_t len = hist_stride;"),
+    # top-k / nucleus sampling
+    ("smp_sort_ascending", "if (la != lb) return la > lb ? -1 : 1;", "if (la != lb) return la < lb ? -1 : 1;"),
+    ("smp_ties_high_first", "return a < b ? -1 : (a > b ? 1 : 0);", "return a > b ? -1 : (a < b ? 1 : 0);"),
+    ("smp_temperature_times", "((double)l[i] - (double)lmax) / (double)temperature;",
+     "((double)l[i] - (double)lmax) * (double)temperature;"),
+    ("smp_nucleus_excludes_crossing", "while (kept < n && cum < target) cum += w[order[kept++]];",
+     "while (kept < n && cum + w[order[kept]] < target) cum += w[order[kept++]];\n            if (kept == 0) kept = 1;"),
+    ("smp_topk_one_more", "kept = k < n ? k : n;", "kept = k < n ? k + 1 : n;"),
+    ("smp_cum_ge", "if (cum > r) {", "if (cum >= r) {"),
+    ("smp_exp_no_tail", "const double r = (x - k * ORACLE_LN2_HEAD) - k * ORACLE_LN2_TAIL;",
+     "const double r = x - k * ORACLE_LN2_HEAD;"),
+    ("smp_exp_short_series", "for (int j = 12; j >= 0; j--) poly = poly * r + inv_fact[j];",
+     "for (int j = 12; j >= 0; j--) poly = poly * r + (j > 7 ? 0.0 : inv_fact[j]);"),
 ]
 
 # Equivalent rewrites, not mutants: they give the same bits on every input, so
