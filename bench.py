@@ -335,6 +335,7 @@ def main():
         log(f"oracle: {first_s:.2f}s for one token, {tokens} tokens in {cpu_s:.2f}s; first GPU step bit-exact: {exact}")
     if not args.no_extra:
         result["greedy"] = greedy_leg(bl, torch, T, dev0, dev, host_layers if not args.no_cpu else None, L, d, f)
+        result["decode_with_attention"] = attention_leg(bl, torch, dev0, dev, L, d, f)
     del host_layers
 
     if not args.no_extra:
@@ -342,6 +343,41 @@ def main():
     if not args.no_cpu:
         result["cpu_single_core"] = single_core_oracle()
     print(json.dumps(result), flush=True)
+
+
+def attention_leg(bl, torch, dev0, dev, L, d, f):
+    """BitNet-3B decode step with attention (bitnet_decode_step, one launch per
+    step): 32 heads of 80, caches of 2048 positions filled with N(0, 1), one
+    sequence at positions 128 and 2047. Bytes per token: the 838,860,800 weight
+    bytes plus the K and V rows read, 2 x 32 layers x 2560 x 4 x (pos + 1)."""
+    heads, hd, max_seq, m = W.BITNET_3B["heads"], d // W.BITNET_3B["heads"], 2048, 1
+    c, s = bl.bitnet_rope_table(10000.0, hd, max_seq)
+    cd, sd = torch.from_numpy(c).to(dev0), torch.from_numpy(s).to(dev0)
+    gen = torch.Generator(device=dev0)
+    gen.manual_seed(2026)
+    kc = torch.randn((L, m, heads, max_seq, hd), generator=gen, device=dev0, dtype=torch.float32)
+    vc = torch.randn((L, m, heads, max_seq, hd), generator=gen, device=dev0, dtype=torch.float32)
+    x = torch.from_numpy(W.activations(W.rng(W.W_STREAM, 998, W.T_X), m, d)).to(dev0)
+    ws = torch.zeros(bl.bitnet_decode_step_workspace_bytes(m, d, f, heads, max_seq), dtype=torch.uint8, device=dev0)
+    res = {"workload": "BitNet-3B decode step with attention: 32 layers x (q/k/v, RoPE + KV-cache append, "
+                       "attention over 0..pos, o, FFN), 1 sequence, 32 heads of 80, launch per step"}
+    for pos in (128, 2047):
+        def step():
+            bl.bitnet_decode_step(dev["weights"], dev["scales"], dev["gains"], L, m, d, f, heads, 1e-5, cd, sd, pos,
+                                  kc, vc, x, None, None, ws)
+        for _ in range(2):
+            step()
+        iters = 10
+        with Timer() as t:
+            for _ in range(iters):
+                step()
+        ms = t.ms / iters
+        nbytes = L * bl.bitnet_layer_bytes(d, f) + 2 * L * d * 4 * (pos + 1)
+        res[f"pos_{pos}"] = {"ms_per_token": round(ms, 4), "bytes_per_token": nbytes,
+                             "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    del kc, vc
+    log(f"decode with attention: {res}")
+    return res
 
 
 def greedy_leg(bl, torch, T, dev0, dev, host_layers, L, d, f):

@@ -39,6 +39,7 @@ EXPORTS = (
     "bitlinear_gemm_noalloc", "bitlinear_gemm_noalloc_max_scratch_bytes",
     "bitnet_embed", "bitnet_greedy_head_workspace_bytes", "bitnet_greedy_head", "bitnet_greedy_step_workspace_bytes",
     "bitnet_greedy_step", "bitnet_sample_workspace_bytes", "bitnet_sample_topk", "bitnet_sample_topp",
+    "bitnet_decode_step_workspace_bytes", "bitnet_decode_step", "bitnet_rope_table",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -97,6 +98,10 @@ _SIGS = {
     "bitnet_sample_workspace_bytes": ([_I64, _I64], _SZ),
     "bitnet_sample_topk": ([_P, _I64, _I64, _I64, _F, _P, _P, _P, _SZ, _P], _I),
     "bitnet_sample_topp": ([_P, _I64, _I64, _F, _F, _P, _P, _P, _SZ, _P], _I),
+    "bitnet_decode_step_workspace_bytes": ([_I64, _I64, _I64, _I64, _I64], _SZ),
+    "bitnet_decode_step": ([_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P,
+                            _SZ, _P], _I),
+    "bitnet_rope_table": ([ctypes.c_double, _I64, _I64, _P, _P], _I),
     "bitlinear_probe_read": ([_P, _SZ, _P, _P], _I),
     "bitlinear_probe_mfma_ops": ([_I64], _I64),
     "bitlinear_probe_mfma_i8": ([_I64, _P, _P], _I),
@@ -283,6 +288,33 @@ def ffn_workspace_view(workspace, m, d, f, segment):
     off = bitnet_ffn_workspace_offset(m, d, f, segment)
     nbytes = int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()
     return workspace[off:off + nbytes].view(dtype).view(shape)
+
+
+# ---- decode step with attention ---------------------------------------------------------
+
+def bitnet_rope_table(base, head_dim, max_pos):
+    """Host: (cos, sin) numpy fp32 [max_pos][head_dim/2] of the rotary embedding."""
+    c = np.empty((max_pos, head_dim // 2), np.float32)
+    s = np.empty((max_pos, head_dim // 2), np.float32)
+    _check(_lib.bitnet_rope_table(float(base), head_dim, max_pos, c.ctypes.data, s.ctypes.data), "bitnet_rope_table")
+    return c, s
+
+
+def bitnet_decode_step_workspace_bytes(m, d, f, n_heads, max_seq):
+    return _lib.bitnet_decode_step_workspace_bytes(m, d, f, n_heads, max_seq)
+
+
+def bitnet_decode_step(weights, scales, gains, n_layers, m, d, f, n_heads, eps, rope_cos, rope_sin, pos, k_cache,
+                       v_cache, x, qkv, attn, workspace, stream=None):
+    max_seq = rope_cos.shape[0]
+    _check(_lib.bitnet_decode_step(_dev(weights, torch.uint8, "weights"), _dev(scales, torch.float32, "scales"),
+                                   _dev(gains, torch.float32, "gains"), n_layers, m, d, f, n_heads, eps,
+                                   _dev(rope_cos, torch.float32, "rope_cos"), _dev(rope_sin, torch.float32, "rope_sin"),
+                                   max_seq, pos, _dev(k_cache, torch.float32, "k_cache"),
+                                   _dev(v_cache, torch.float32, "v_cache"), _dev(x, torch.float32, "x"),
+                                   _dev(qkv, torch.float32, "qkv", True), _dev(attn, torch.float32, "attn", True),
+                                   _dev(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
+                                   _stream(stream)), "bitnet_decode_step")
 
 
 # ---- greedy decoding ------------------------------------------------------------------

@@ -295,6 +295,132 @@ int greedy_head_launch(const uint8_t* head, float s_head, int64_t n, int64_t k, 
     return bl::launch_tile_argmax(keys, bl::skinny_tiles((int)n, false), (int)m, next, s);
 }
 
+// The launch-per-step layer stream (any m). Without attn, the o projection of
+// layer l reads the stand-in z[l]; with attn, it reads the attention output of
+// the layer (RoPE, cache append and attention over positions 0 .. pos after
+// the q/k/v product).
+struct AttnCtx {
+    int heads, max_seq, pos;
+    const float *rope_cos, *rope_sin;
+    float *k_cache, *v_cache;  // [n_layers][m][heads][max_seq][hd]
+    float *q_rot, *part;       // scratch
+    float* attn;               // [n_layers][m][d] or null (then attn_scratch, reused)
+    float* attn_scratch;       // [m][d]
+};
+
+int stream_steps(const uint8_t* weights, const float* scales, const float* gains, const float* z, int64_t n_layers,
+                 int64_t m, int64_t d, int64_t f, float eps, float* x, float* qkv, void* workspace,
+                 const AttnCtx* attn, hipStream_t s)
+{
+    const StreamLayout L = stream_layout(m, d, f);
+    // the o projection's input of layer l: the stand-in, or the layer's attention output
+    auto o_input = [&](int64_t l, float* qkv_l) -> const float* {
+        if (!attn) return z + (size_t)l * m * d;
+        float* out = attn->attn ? attn->attn + (size_t)l * m * d : attn->attn_scratch;
+        const size_t cache_layer = (size_t)m * d * attn->max_seq;  // heads * hd = d per position
+        if (bl::launch_attention(qkv_l, (int)(3 * d), (int)m, (int)d, attn->heads, attn->rope_cos, attn->rope_sin,
+                                 attn->max_seq, attn->pos, attn->k_cache + (size_t)l * cache_layer,
+                                 attn->v_cache + (size_t)l * cache_layer, attn->q_rot, attn->part, out, (int)d, s))
+            return nullptr;
+        return out;
+    };
+    int8_t* qa = at<int8_t>(workspace, L.q_a);
+    float* sa = at<float>(workspace, L.s_a);
+    int32_t* qsa = at<int32_t>(workspace, L.qs_a);
+    int8_t* qo = at<int8_t>(workspace, L.q_o);
+    float* so = at<float>(workspace, L.s_o);
+    int32_t* qso = at<int32_t>(workspace, L.qs_o);
+    void* ffn_ws = at<void>(workspace, L.ffn);
+    const int M = (int)m, D = (int)d, F = (int)f;
+    const size_t blob = bitnet_layer_bytes(d, f);
+    const size_t dd = (size_t)(d * d) / 4, fd = (size_t)(f * d) / 4;
+    const size_t gstride = (size_t)(3 * d + f);
+    if (m > kMaxGemvM && m <= kMaxSkinnyM) {
+        // 9..32 tokens: every projection is one skinny MFMA launch over
+        // activations quantised straight into its operand order
+        const Layout FL = ffn_layout(m, d, f);
+        int8_t* q1 = at<int8_t>(ffn_ws, FL.off[BITNET_FFN_WS_Q1]);
+        float* s1 = at<float>(ffn_ws, FL.off[BITNET_FFN_WS_S1]);
+        int32_t* qs1 = at<int32_t>(ffn_ws, FL.off[BITNET_FFN_WS_QS1]);
+        float* h = at<float>(ffn_ws, FL.off[BITNET_FFN_WS_H]);
+        int8_t* q2 = at<int8_t>(ffn_ws, FL.off[BITNET_FFN_WS_Q2]);
+        float* s2 = at<float>(ffn_ws, FL.off[BITNET_FFN_WS_S2]);
+        int32_t* qs2 = at<int32_t>(ffn_ws, FL.off[BITNET_FFN_WS_QS2]);
+        for (int64_t l = 0; l < n_layers; ++l) {
+            const uint8_t* wl = weights + (size_t)l * blob;
+            const float* sl = scales + 7 * l;
+            const float* gl = gains + l * gstride;
+            float* qkv_l = qkv ? qkv + (size_t)l * m * 3 * d : at<float>(workspace, L.qkv);
+            const uint8_t* wg = wl + 4 * dd;
+            // each norm + quant also pulls the next product's weight lines into the
+            // memory-side cache
+            const uint32_t rd = (uint32_t)(D / 4), rf = (uint32_t)(F / 4);
+            const bl::Prefetch pf_qkv = {{wl, nullptr}, {(uint32_t)(3 * dd), 0u},
+                                         (uint32_t)bl::skinny_rows_per_tile(3 * D, false) * rd};
+            const bl::Prefetch pf_o = {{wl + 3 * dd, nullptr}, {(uint32_t)dd, 0u},
+                                       (uint32_t)bl::skinny_rows_per_tile(D, false) * rd};
+            const bl::Prefetch pf_gu = {{wg, wg + fd}, {(uint32_t)fd, (uint32_t)fd},
+                                        (uint32_t)bl::skinny_rows_per_tile(F, true) * rd};
+            const bl::Prefetch pf_dn = {{wg + 2 * fd, nullptr}, {(uint32_t)fd, 0u},
+                                        (uint32_t)bl::skinny_rows_per_tile(D, false) * rf};
+            int rc = bl::launch_quant_act(x, gl, eps, M, D, qa, sa, qsa, s, true, &pf_qkv);
+            if (!rc)
+                rc = bl::launch_skinny(skinny(wl, sl, 0.0f, D, 3 * D, D, qa, sa, qsa, M, nullptr, qkv_l, 3 * D), false,
+                                       s);
+            const float* o_src = rc ? nullptr : o_input(l, qkv_l);
+            if (!rc && !o_src) rc = BL_ERR_LAUNCH;
+            if (!rc) rc = bl::launch_quant_act(o_src, gl + d, eps, M, D, qo, so, qso, s, true, &pf_o);
+            if (!rc)
+                rc = bl::launch_skinny(skinny(wl + 3 * dd, sl + 3, 0.0f, D, D, D, qo, so, qso, M, x, x, D), false, s);
+            if (!rc) rc = bl::launch_quant_act(x, gl + 2 * d, eps, M, D, q1, s1, qs1, s, true, &pf_gu);
+            if (!rc)
+                rc = bl::launch_skinny(skinny_gateup(wg, 0.0f, wg + fd, 0.0f, sl + 4, F, D, q1, s1, qs1, M, h, nullptr,
+                                                     nullptr),
+                                       false, s);
+            if (!rc) rc = bl::launch_quant_act(h, gl + 3 * d, eps, M, F, q2, s2, qs2, s, true, &pf_dn);
+            if (!rc)
+                rc = bl::launch_skinny(skinny(wg + 2 * fd, sl + 6, 0.0f, D, D, F, q2, s2, qs2, M, x, x, D), false, s);
+            if (rc) return rc;
+        }
+        return BL_OK;
+    }
+    for (int64_t l = 0; l < n_layers; ++l) {
+        const uint8_t* wl = weights + (size_t)l * blob;
+        const float* sl = scales + 7 * l;
+        const float* gl = gains + l * gstride;
+        float* qkv_l = qkv ? qkv + (size_t)l * m * 3 * d : at<float>(workspace, L.qkv);
+        // m <= 8 here: q/k/v and o are GEMV launches over D inputs
+        const uint32_t ch = (uint32_t)bl::gemv_rows_per_block(D) * (uint32_t)(D / 4);
+        const bl::Prefetch pf_qkv = {{wl, nullptr}, {(uint32_t)(3 * dd), 0u}, ch};
+        const bl::Prefetch pf_o = {{wl + 3 * dd, nullptr}, {(uint32_t)dd, 0u}, ch};
+        const bool pre = m <= kMaxGemvM;
+        int rc = bl::launch_quant_act(x, gl, eps, M, D, qa, sa, qsa, s, false, pre ? &pf_qkv : nullptr);
+        if (rc) return rc;
+        if (m <= kMaxGemvM) {
+            const uint8_t* qkv_w[3] = {wl, wl + dd, wl + 2 * dd};
+            rc = bl::launch_gemv_multi(3, qkv_w, sl, D, D, qa, sa, qsa, M, qkv_l, 3 * D, s);
+        } else {
+            for (int j = 0; j < 3 && !rc; ++j)  // column block j of qkv[m][3d]
+                rc = bl::launch_gemm(wl + j * dd, 0.0f, sl + j, D, D, qa, sa, qsa, M, nullptr, qkv_l + (size_t)j * d,
+                                     3 * D, nullptr, nullptr, nullptr, s);
+        }
+        if (rc) return rc;
+        const float* o_src = o_input(l, qkv_l);
+        if (!o_src) return BL_ERR_LAUNCH;
+        rc = bl::launch_quant_act(o_src, gl + d, eps, M, D, qo, so, qso, s, false, pre ? &pf_o : nullptr);
+        if (rc) return rc;
+        if (m <= kMaxGemvM)
+            rc = bl::launch_gemv(wl + 3 * dd, 0.0f, sl + 3, D, D, qo, so, qso, M, x, x, nullptr, s);
+        else
+            rc = bl::launch_gemm(wl + 3 * dd, 0.0f, sl + 3, D, D, qo, so, qso, M, x, x, D, nullptr, nullptr, nullptr, s);
+        if (rc) return rc;
+        rc = ffn_impl(x, m, d, f, gl + 2 * d, gl + 3 * d, eps, wl + 4 * dd, 0.0f, wl + 4 * dd + fd, 0.0f,
+                      wl + 4 * dd + 2 * fd, 0.0f, sl + 4, x, x, ffn_ws, 0, s);
+        if (rc) return rc;
+    }
+    return BL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -496,97 +622,56 @@ int bitnet_decode_stream(const uint8_t* weights, const float* scales, const floa
                                             qkv ? 3 * d : 0, at<void>(workspace, L.ll),
                                             at<uint32_t>(workspace, L.ctrl), s);
     }
-    int8_t* qa = at<int8_t>(workspace, L.q_a);
-    float* sa = at<float>(workspace, L.s_a);
-    int32_t* qsa = at<int32_t>(workspace, L.qs_a);
-    int8_t* qo = at<int8_t>(workspace, L.q_o);
-    float* so = at<float>(workspace, L.s_o);
-    int32_t* qso = at<int32_t>(workspace, L.qs_o);
-    void* ffn_ws = at<void>(workspace, L.ffn);
-    const int M = (int)m, D = (int)d, F = (int)f;
-    const size_t blob = bitnet_layer_bytes(d, f);
-    const size_t dd = (size_t)(d * d) / 4, fd = (size_t)(f * d) / 4;
-    const size_t gstride = (size_t)(3 * d + f);
-    if (m > kMaxGemvM && m <= kMaxSkinnyM) {
-        // 9..32 tokens: every projection is one skinny MFMA launch over
-        // activations quantised straight into its operand order
-        const Layout FL = ffn_layout(m, d, f);
-        int8_t* q1 = at<int8_t>(ffn_ws, FL.off[BITNET_FFN_WS_Q1]);
-        float* s1 = at<float>(ffn_ws, FL.off[BITNET_FFN_WS_S1]);
-        int32_t* qs1 = at<int32_t>(ffn_ws, FL.off[BITNET_FFN_WS_QS1]);
-        float* h = at<float>(ffn_ws, FL.off[BITNET_FFN_WS_H]);
-        int8_t* q2 = at<int8_t>(ffn_ws, FL.off[BITNET_FFN_WS_Q2]);
-        float* s2 = at<float>(ffn_ws, FL.off[BITNET_FFN_WS_S2]);
-        int32_t* qs2 = at<int32_t>(ffn_ws, FL.off[BITNET_FFN_WS_QS2]);
-        for (int64_t l = 0; l < n_layers; ++l) {
-            const uint8_t* wl = weights + (size_t)l * blob;
-            const float* sl = scales + 7 * l;
-            const float* gl = gains + l * gstride;
-            float* qkv_l = qkv ? qkv + (size_t)l * m * 3 * d : at<float>(workspace, L.qkv);
-            const uint8_t* wg = wl + 4 * dd;
-            // each norm + quant also pulls the next product's weight lines into the
-            // memory-side cache
-            const uint32_t rd = (uint32_t)(D / 4), rf = (uint32_t)(F / 4);
-            const bl::Prefetch pf_qkv = {{wl, nullptr}, {(uint32_t)(3 * dd), 0u},
-                                         (uint32_t)bl::skinny_rows_per_tile(3 * D, false) * rd};
-            const bl::Prefetch pf_o = {{wl + 3 * dd, nullptr}, {(uint32_t)dd, 0u},
-                                       (uint32_t)bl::skinny_rows_per_tile(D, false) * rd};
-            const bl::Prefetch pf_gu = {{wg, wg + fd}, {(uint32_t)fd, (uint32_t)fd},
-                                        (uint32_t)bl::skinny_rows_per_tile(F, true) * rd};
-            const bl::Prefetch pf_dn = {{wg + 2 * fd, nullptr}, {(uint32_t)fd, 0u},
-                                        (uint32_t)bl::skinny_rows_per_tile(D, false) * rf};
-            int rc = bl::launch_quant_act(x, gl, eps, M, D, qa, sa, qsa, s, true, &pf_qkv);
-            if (!rc)
-                rc = bl::launch_skinny(skinny(wl, sl, 0.0f, D, 3 * D, D, qa, sa, qsa, M, nullptr, qkv_l, 3 * D), false,
-                                       s);
-            if (!rc) rc = bl::launch_quant_act(z + (size_t)l * m * d, gl + d, eps, M, D, qo, so, qso, s, true, &pf_o);
-            if (!rc)
-                rc = bl::launch_skinny(skinny(wl + 3 * dd, sl + 3, 0.0f, D, D, D, qo, so, qso, M, x, x, D), false, s);
-            if (!rc) rc = bl::launch_quant_act(x, gl + 2 * d, eps, M, D, q1, s1, qs1, s, true, &pf_gu);
-            if (!rc)
-                rc = bl::launch_skinny(skinny_gateup(wg, 0.0f, wg + fd, 0.0f, sl + 4, F, D, q1, s1, qs1, M, h, nullptr,
-                                                     nullptr),
-                                       false, s);
-            if (!rc) rc = bl::launch_quant_act(h, gl + 3 * d, eps, M, F, q2, s2, qs2, s, true, &pf_dn);
-            if (!rc)
-                rc = bl::launch_skinny(skinny(wg + 2 * fd, sl + 6, 0.0f, D, D, F, q2, s2, qs2, M, x, x, D), false, s);
-            if (rc) return rc;
-        }
-        return BL_OK;
-    }
-    for (int64_t l = 0; l < n_layers; ++l) {
-        const uint8_t* wl = weights + (size_t)l * blob;
-        const float* sl = scales + 7 * l;
-        const float* gl = gains + l * gstride;
-        float* qkv_l = qkv ? qkv + (size_t)l * m * 3 * d : at<float>(workspace, L.qkv);
-        // m <= 8 here: q/k/v and o are GEMV launches over D inputs
-        const uint32_t ch = (uint32_t)bl::gemv_rows_per_block(D) * (uint32_t)(D / 4);
-        const bl::Prefetch pf_qkv = {{wl, nullptr}, {(uint32_t)(3 * dd), 0u}, ch};
-        const bl::Prefetch pf_o = {{wl + 3 * dd, nullptr}, {(uint32_t)dd, 0u}, ch};
-        const bool pre = m <= kMaxGemvM;
-        int rc = bl::launch_quant_act(x, gl, eps, M, D, qa, sa, qsa, s, false, pre ? &pf_qkv : nullptr);
-        if (rc) return rc;
-        if (m <= kMaxGemvM) {
-            const uint8_t* qkv_w[3] = {wl, wl + dd, wl + 2 * dd};
-            rc = bl::launch_gemv_multi(3, qkv_w, sl, D, D, qa, sa, qsa, M, qkv_l, 3 * D, s);
-        } else {
-            for (int j = 0; j < 3 && !rc; ++j)  // column block j of qkv[m][3d]
-                rc = bl::launch_gemm(wl + j * dd, 0.0f, sl + j, D, D, qa, sa, qsa, M, nullptr, qkv_l + (size_t)j * d,
-                                     3 * D, nullptr, nullptr, nullptr, s);
-        }
-        if (rc) return rc;
-        rc = bl::launch_quant_act(z + (size_t)l * m * d, gl + d, eps, M, D, qo, so, qso, s, false, pre ? &pf_o : nullptr);
-        if (rc) return rc;
-        if (m <= kMaxGemvM)
-            rc = bl::launch_gemv(wl + 3 * dd, 0.0f, sl + 3, D, D, qo, so, qso, M, x, x, nullptr, s);
-        else
-            rc = bl::launch_gemm(wl + 3 * dd, 0.0f, sl + 3, D, D, qo, so, qso, M, x, x, D, nullptr, nullptr, nullptr, s);
-        if (rc) return rc;
-        rc = ffn_impl(x, m, d, f, gl + 2 * d, gl + 3 * d, eps, wl + 4 * dd, 0.0f, wl + 4 * dd + fd, 0.0f,
-                      wl + 4 * dd + 2 * fd, 0.0f, sl + 4, x, x, ffn_ws, 0, s);
-        if (rc) return rc;
-    }
-    return BL_OK;
+    return stream_steps(weights, scales, gains, z, n_layers, m, d, f, eps, x, qkv, workspace, nullptr, s);
+}
+
+// ---- decode step with attention -------------------------------------------------
+
+size_t bitnet_decode_step_workspace_bytes(int64_t m, int64_t d, int64_t f, int64_t n_heads, int64_t max_seq)
+{
+    if (m <= 0 || d <= 0 || f <= 0 || n_heads <= 0 || max_seq <= 0 || d % n_heads != 0 || max_seq > 0x7fffffff)
+        return 0;
+    const size_t hd = (size_t)(d / n_heads);
+    size_t at = align_up(stream_layout(m, d, f).total, 256);
+    at += align_up((size_t)(m * d) * 4, 256);  // rotated q
+    at += align_up((size_t)(m * d) * 4, 256);  // attention output scratch
+    at += align_up((size_t)m * (size_t)n_heads * (size_t)bl::attn_chunks((int)max_seq) * (hd + 2) * 4, 256);
+    return at;
+}
+
+int bitnet_decode_step(const uint8_t* weights, const float* scales, const float* gains, int64_t n_layers, int64_t m,
+                       int64_t d, int64_t f, int64_t n_heads, float eps, const float* rope_cos, const float* rope_sin,
+                       int64_t max_seq, int64_t pos, float* k_cache, float* v_cache, float* x, float* qkv,
+                       float* attn, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!weights || !scales || !gains || !rope_cos || !rope_sin || !k_cache || !v_cache || !x || !workspace)
+        return BL_ERR_NULL;
+    if (!dim_ok(n_layers) || !dim_ok(m) || !k_ok(d) || !k_ok(f) || d > kMaxGemvK || f > kMaxGemvK ||
+        m > 0x7fffffff || n_heads <= 0 || d % n_heads != 0 || (d / n_heads) % 4 != 0 || d / n_heads > 256 ||
+        max_seq <= 0 || max_seq > 0x7fffffff || pos < 0 || pos >= max_seq)
+        return BL_ERR_SHAPE;
+    if (!aligned(weights, 16) || !aligned(scales, 4) || !aligned(gains, 16) || !aligned(rope_cos, 4) ||
+        !aligned(rope_sin, 4) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(x, 16) ||
+        (qkv && !aligned(qkv, 16)) || (attn && !aligned(attn, 16)) || !aligned(workspace, 256))
+        return BL_ERR_ALIGN;
+    if (workspace_bytes < bitnet_decode_step_workspace_bytes(m, d, f, n_heads, max_seq)) return BL_ERR_WORKSPACE;
+    size_t at_off = align_up(stream_layout(m, d, f).total, 256);
+    AttnCtx ctx;
+    ctx.heads = (int)n_heads;
+    ctx.max_seq = (int)max_seq;
+    ctx.pos = (int)pos;
+    ctx.rope_cos = rope_cos;
+    ctx.rope_sin = rope_sin;
+    ctx.k_cache = k_cache;
+    ctx.v_cache = v_cache;
+    ctx.q_rot = at<float>(workspace, at_off);
+    at_off += align_up((size_t)(m * d) * 4, 256);
+    ctx.attn_scratch = at<float>(workspace, at_off);
+    at_off += align_up((size_t)(m * d) * 4, 256);
+    ctx.part = at<float>(workspace, at_off);
+    ctx.attn = attn;
+    return stream_steps(weights, scales, gains, nullptr, n_layers, m, d, f, eps, x, qkv, workspace, &ctx,
+                        as_stream(stream));
 }
 
 // ---- greedy decoding around the stream ----------------------------------------

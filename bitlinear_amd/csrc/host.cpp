@@ -70,4 +70,23 @@ int bitlinear_weight_quant(const float* w, int64_t n, int64_t k, int8_t* t, floa
     return BL_OK;
 }
 
+// Rotary-embedding table: theta_i = base^(-2i / hd), angle pos * theta_i, cos
+// and sin in fp64, each rounded once to fp32; row pos holds hd / 2 entries.
+int bitnet_rope_table(double base, int64_t head_dim, int64_t max_pos, float* cos_out, float* sin_out)
+{
+    if (!cos_out || !sin_out) return BL_ERR_NULL;
+    if (head_dim <= 0 || head_dim % 2 != 0 || max_pos <= 0) return BL_ERR_SHAPE;
+    if (!(base > 1.0) || !(base < INFINITY)) return BL_ERR_VALUE;
+    const int64_t half = head_dim / 2;
+    for (int64_t i = 0; i < half; ++i) {
+        const double theta = pow(base, -(double)(2 * i) / (double)head_dim);
+        for (int64_t p = 0; p < max_pos; ++p) {
+            const double ang = (double)p * theta;
+            cos_out[p * half + i] = (float)cos(ang);
+            sin_out[p * half + i] = (float)sin(ang);
+        }
+    }
+    return BL_OK;
+}
+
 }  // extern "C"

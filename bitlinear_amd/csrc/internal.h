@@ -144,6 +144,16 @@ int launch_append(const int32_t* next, int m, int32_t* hist, int stride, int32_t
 int launch_sample(bool topp, const float* logits, int m, int n, int k, float p, float temperature, const double* u,
                   int32_t* out, long long* wbuf, hipStream_t s);
 
+// Single-token attention of m sequences at position pos (attn.hip): RoPE of q
+// and k from qkv rows [q | k | v] (row stride ldq), k and v appended to the
+// caches ([m][heads][max_seq][hd]), attention over 0 .. pos into out (row
+// stride ldo). q_rot: m * d floats; part: m * heads * attn_chunks(max_seq) *
+// (hd + 2) floats.
+int attn_chunks(int max_seq);
+int launch_attention(const float* qkv, int ldq, int m, int d, int heads, const float* rope_cos, const float* rope_sin,
+                     int max_seq, int pos, float* k_cache, float* v_cache, float* q_rot, float* part, float* out,
+                     int ldo, hipStream_t s);
+
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 }  // namespace bl

@@ -315,6 +315,50 @@ int bitnet_decode_stream(const uint8_t *weights, const float *scales, const floa
                          int64_t n_layers, int64_t m, int64_t d, int64_t f, float eps,
                          float *x, float *qkv, void *workspace, size_t workspace_bytes, void *stream);
 
+/* -------------------------------------------- decode step with attention --- */
+/* The decoder layer stream of bitnet_decode_stream with real single-token
+ * attention in place of the stand-in z ("BitNet Model - Complete Inference
+ * Pipeline": "KV Cache State", forwardSingleToken; "Transformer Block":
+ * "Forward Pass with KV Cache", forwardWithCache; Config: numHeads, headDim,
+ * ropeBase). m sequences, each with its own cache, at the same position pos.
+ * For each layer l:
+ *   a      = quant(rmsnorm(x, g_attn));  q, k, v = dequant(W . a)  -> qkv[l]
+ *   heads  : head h owns columns h hd .. h hd + hd - 1, hd = d / n_heads;
+ *   RoPE   : in every head of q and k the pairs (x[2i], x[2i+1]) turn by the
+ *            angle pos * theta_i with the table row pos: (a, b) ->
+ *            (fl32(fl32(a c) - fl32(b s)), fl32(fl32(a s) + fl32(b c)));
+ *   cache  : the rotated k and v are written at position pos of layer l;
+ *   attn   = per head softmax(q . K[0..pos]^T / sqrt(hd)) V[0..pos]   -> attn[l]
+ *            (fp32 on the device: scores, expf, sums; not bit-exact, see the
+ *            design notes for the bound);
+ *   x      = x + dequant(W_o . quant(rmsnorm(attn, g_attn_sub)))
+ *   x      = x + ffn(x)
+ *   weights, scales, gains, n_layers, m, d, f, eps : as bitnet_decode_stream.
+ *   n_heads   : d % n_heads == 0, hd % 4 == 0, hd <= 256.
+ *   rope_cos, rope_sin : host-computed tables, device fp32 [max_seq][hd / 2]
+ *               (bitnet_rope_table).
+ *   k_cache, v_cache : device fp32 [n_layers][m][n_heads][max_seq][hd], 16-byte
+ *               aligned; positions 0 .. pos-1 hold earlier steps' entries.
+ *   x         : device fp32 [m][d], updated in place.
+ *   qkv       : device fp32 [n_layers][m][3d] or NULL (q, k, v before RoPE).
+ *   attn      : device fp32 [n_layers][m][d] or NULL (attention outputs).
+ *   workspace : bitnet_decode_step_workspace_bytes(m, d, f, n_heads, max_seq).
+ * It runs one launch per step (the persistent kernel carries no attention).
+ * Errors: NULL, SHAPE (pos outside [0, max_seq), ...), ALIGN, WORKSPACE, LAUNCH. */
+size_t bitnet_decode_step_workspace_bytes(int64_t m, int64_t d, int64_t f, int64_t n_heads, int64_t max_seq);
+int bitnet_decode_step(const uint8_t *weights, const float *scales, const float *gains, int64_t n_layers,
+                       int64_t m, int64_t d, int64_t f, int64_t n_heads, float eps,
+                       const float *rope_cos, const float *rope_sin, int64_t max_seq, int64_t pos,
+                       float *k_cache, float *v_cache, float *x, float *qkv, float *attn,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* Host helper: the rotary-embedding table. theta_i = pow(base, -(2i) / head_dim),
+ * angle = pos * theta_i, cos and sin in fp64, each rounded once to fp32.
+ *   cos_out, sin_out : host fp32 [max_pos][head_dim / 2].
+ * The pages name ropeBase without its value; the usual 10000 is the reading.
+ * Errors: NULL, SHAPE (odd or non-positive head_dim, max_pos <= 0), VALUE (base <= 1). */
+int bitnet_rope_table(double base, int64_t head_dim, int64_t max_pos, float *cos_out, float *sin_out);
+
 /* ------------------------------------------------------ greedy decoding --- */
 /* The device side of greedy text generation around the BitLinear stream
  * ("BitNet Model - Complete Inference Pipeline", Hesper API: "Architecture"

@@ -66,6 +66,10 @@ def load(path=None):
     lib.ref_exp_neg.restype = ctypes.c_double
     lib.ref_sample.argtypes = [_f32p, _i64, _i64, ctypes.c_int, _i64, ctypes.c_float, ctypes.c_float,
                                ctypes.POINTER(ctypes.c_double), _i32p]
+    lib.ref_rope_table.argtypes = [ctypes.c_double, _i64, _i64, _f32p, _f32p]
+    lib.ref_rope_apply.argtypes = [_f32p, _f32p, _f32p, _i64]
+    lib.ref_rope_apply.restype = None
+    lib.ref_attention.argtypes = [_f32p, _f32p, _f32p, _i64, _i64, _i64, _i64, _i64, _f32p]
     lib.ref_set_threads.argtypes = [ctypes.c_int]
     lib.ref_set_threads.restype = ctypes.c_int
     if path is None:
@@ -282,6 +286,42 @@ def sample_topp(logits, p, temperature, u, lib=None):
     return _sample(logits, 1, 1, p, temperature, u, lib)
 
 
+def rope_table(base, hd, max_pos, lib=None):
+    """(cos, sin) fp32 [max_pos][hd/2] of the rotary embedding."""
+    lib = lib or load()
+    c = np.empty((max_pos, hd // 2), np.float32)
+    s = np.empty((max_pos, hd // 2), np.float32)
+    _check(lib.ref_rope_table(float(base), hd, max_pos, _ptr(c, _f32p), _ptr(s, _f32p)), "rope_table")
+    return c, s
+
+
+def rope_apply(x, c_row, s_row, lib=None):
+    """Rotate every head vector of x[..., hd] (fp32, last axis) with one table row."""
+    lib = lib or load()
+    out = _c(x, np.float32).copy()
+    hd = out.shape[-1]
+    c_row = _c(c_row, np.float32)
+    s_row = _c(s_row, np.float32)
+    flat = out.reshape(-1, hd)
+    for v in flat:
+        lib.ref_rope_apply(_ptr(v, _f32p), _ptr(c_row, _f32p), _ptr(s_row, _f32p), hd)
+    return flat.reshape(out.shape)
+
+
+def attention(q, k_cache, v_cache, pos, lib=None):
+    """q [m][H][hd]; caches [m][H][max_seq][hd] -> out [m][H*hd] (fp64 inside)."""
+    lib = lib or load()
+    q = _c(q, np.float32)
+    k_cache = _c(k_cache, np.float32)
+    v_cache = _c(v_cache, np.float32)
+    m, heads, hd = q.shape
+    max_seq = k_cache.shape[2]
+    out = np.empty((m, heads * hd), np.float32)
+    _check(lib.ref_attention(_ptr(q, _f32p), _ptr(k_cache, _f32p), _ptr(v_cache, _f32p), m, heads, hd, max_seq, pos,
+                             _ptr(out, _f32p)), "attention")
+    return out
+
+
 # --- compositions -------------------------------------------------------------
 
 def ffn(x, norm_gain, sub_norm_gain, eps, w_gate, s_gate, w_up, s_up, w_down, s_down, lib=None):
@@ -375,3 +415,32 @@ def greedy_step(tokens, table, s_e, layers, g_final, eps, w_head, s_head, hist, 
             hist[r, hist_len[r]] = idx[r]
             hist_len[r] += 1
     return idx, hist, hist_len, x
+
+
+def layer_attn(x, lw, eps, heads, cos_t, sin_t, k_cache, v_cache, pos, attn_in=None, lib=None):
+    """One decoder layer with attention ("Transformer Block", "Forward Pass with
+    KV Cache"): a = quant(rmsnorm(x, g_attn)); q, k, v = BitLinear(a); q and k
+    rotated for position pos; k, v written to the caches (in place, [m][H][S][hd]);
+    attn = attention over positions 0 .. pos; x += BitLinear_o(quant(rmsnorm(attn,
+    g_attn_sub))); x += ffn(x). attn_in, if given, replaces the computed
+    attention output downstream (to continue from another implementation's
+    floating-point attention). Returns (x_next, qkv [m][3d], attn [m][d])."""
+    x = _c(np.atleast_2d(x), np.float32)
+    m, d = x.shape
+    hd = d // heads
+    a, sa, _ = quant_act(x, lw["g_attn"], eps, lib)
+    yq, _ = bitlinear(lw["wq"], lw["sq"], d, a, sa, lib)
+    yk, _ = bitlinear(lw["wk"], lw["sk"], d, a, sa, lib)
+    yv, _ = bitlinear(lw["wv"], lw["sv"], d, a, sa, lib)
+    q_rot = rope_apply(yq.reshape(m, heads, hd), cos_t[pos], sin_t[pos], lib)
+    k_rot = rope_apply(yk.reshape(m, heads, hd), cos_t[pos], sin_t[pos], lib)
+    k_cache[:, :, pos, :] = k_rot
+    v_cache[:, :, pos, :] = yv.reshape(m, heads, hd)
+    attn = attention(q_rot, k_cache, v_cache, pos, lib)
+    use = attn if attn_in is None else _c(attn_in, np.float32)
+    o_in, so, _ = quant_act(use, lw["g_attn_sub"], eps, lib)
+    yo, _ = bitlinear(lw["wo"], lw["so"], d, o_in, so, lib)
+    x = residual_add(x, yo, lib)
+    f = ffn(x, lw["g_ffn"], lw["g_ffn_sub"], eps, lw["wg"], lw["sg"], lw["wu"], lw["su"], lw["wd"], lw["sd"], lib)
+    x = residual_add(x, f["out"], lib)
+    return x, np.concatenate([yq, yk, yv], axis=1), attn

@@ -476,3 +476,82 @@ int ref_sample(const float *logits, int64_t m, int64_t n, int mode, int64_t k, f
     free(w);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Single-token attention with a KV cache and rotary position embedding
+ * ([BN] "KV Cache State", forwardSingleToken; [TB] "Forward Pass with KV
+ * Cache", forwardWithCache; Config: numHeads, headDim, ropeBase). Readings:
+ * heads h = 0 .. H-1 own columns h * hd .. h * hd + hd - 1 of q, k and v
+ * (hd = d / H, numKVHeads = H); the rotation is RoFormer's: within a head the
+ * pairs (x[2i], x[2i+1]) turn by the angle pos * theta_i, theta_i =
+ * base^(-2i / hd); the rotated k and v of position pos join the cache, and the
+ * head's output is softmax(q . K^T / sqrt(hd)) V over positions 0 .. pos.     */
+
+/* cos / sin table [max_pos][hd / 2]: theta_i = pow(base, -(2 i) / hd) and the
+ * angle pos * theta_i in fp64, cos and sin in fp64, each rounded once to fp32. */
+int ref_rope_table(double base, int64_t hd, int64_t max_pos, float *cos_t, float *sin_t)
+{
+    if (hd <= 0 || hd % 2 != 0 || max_pos <= 0 || !(base > 1.0)) return -2;
+    for (int64_t p = 0; p < max_pos; p++)
+        for (int64_t i = 0; i < hd / 2; i++) {
+            const double theta = pow(base, -(double)(2 * i) / (double)hd);
+            const double ang = (double)p * theta;
+            cos_t[p * (hd / 2) + i] = (float)cos(ang);
+            sin_t[p * (hd / 2) + i] = (float)sin(ang);
+        }
+    return 0;
+}
+
+/* Rotation of one head vector in fp32 with the table row c, s (hd / 2 each):
+ * (a, b) -> (fl32(fl32(a c) - fl32(b s)), fl32(fl32(a s) + fl32(b c))).      */
+void ref_rope_apply(float *x, const float *c, const float *s, int64_t hd)
+{
+    for (int64_t i = 0; i < hd / 2; i++) {
+        const float a = x[2 * i], b = x[2 * i + 1];
+        const float ac = a * c[i], bs = b * s[i], as = a * s[i], bc = b * c[i];
+        x[2 * i] = ac - bs;
+        x[2 * i + 1] = as + bc;
+    }
+}
+
+/* Attention of one query per sequence over cache positions 0 .. pos, in fp64
+ * (scores, softmax, weighted sum), rounded once to fp32.
+ *   q : [m][H][hd] (rotated); k_cache, v_cache : [m][H][max_seq][hd];
+ *   out : [m][H * hd].                                                        */
+int ref_attention(const float *q, const float *k_cache, const float *v_cache, int64_t m, int64_t heads, int64_t hd,
+                  int64_t max_seq, int64_t pos, float *out)
+{
+    if (m <= 0 || heads <= 0 || hd <= 0 || pos < 0 || pos >= max_seq) return -2;
+    double *sc = (double *)malloc(sizeof(double) * (size_t)(pos + 1));
+    double *acc = (double *)malloc(sizeof(double) * (size_t)hd);
+    if (!sc || !acc) {
+        free(sc);
+        free(acc);
+        return -7;
+    }
+    const double scale = 1.0 / sqrt((double)hd);
+    for (int64_t r = 0; r < m; r++)
+        for (int64_t h = 0; h < heads; h++) {
+            const float *qh = q + (r * heads + h) * hd;
+            const float *K = k_cache + ((r * heads + h) * max_seq) * hd;
+            const float *V = v_cache + ((r * heads + h) * max_seq) * hd;
+            double mx = -INFINITY;
+            for (int64_t j = 0; j <= pos; j++) {
+                double dot = 0.0;
+                for (int64_t i = 0; i < hd; i++) dot += (double)qh[i] * (double)K[j * hd + i];
+                sc[j] = dot * scale;
+                if (sc[j] > mx) mx = sc[j];
+            }
+            double den = 0.0;
+            for (int64_t i = 0; i < hd; i++) acc[i] = 0.0;
+            for (int64_t j = 0; j <= pos; j++) {
+                const double e = exp(sc[j] - mx);
+                den += e;
+                for (int64_t i = 0; i < hd; i++) acc[i] += e * (double)V[j * hd + i];
+            }
+            for (int64_t i = 0; i < hd; i++) out[r * heads * hd + h * hd + i] = (float)(acc[i] / den);
+        }
+    free(sc);
+    free(acc);
+    return 0;
+}

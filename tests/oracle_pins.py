@@ -988,4 +988,115 @@ def pin_sample_temperature(o, lib):
         assert abs(freq[0] - w[0] / w.sum()) <= 1e-4 + 1e-9, (t, freq)
 
 
+# --- rotary embedding and single-token attention -----------------------------------------------
+
+def pin_rope_table(o, lib):
+    """The table against numpy's fp64 cos / sin rounded once: position 0 is the
+    identity (cos 1, sin 0), frequency 0 turns by one radian per position,
+    frequency hd/4 by base^(-1/2) radians (1/100 for base 10000), and every
+    entry is fl32 of cos / sin of pos * base^(-2i/hd)."""
+    hd, npos = 80, 40
+    c, s = o.rope_table(10000.0, hd, npos, lib)
+    assert (c[0] == 1.0).all() and (s[0] == 0.0).all()
+    pos = np.arange(npos, dtype=np.float64)
+    assert (c[:, 0] == np.cos(pos).astype(np.float32)).all() and (s[:, 0] == np.sin(pos).astype(np.float32)).all()
+    assert (c[:, hd // 4] == np.cos(pos / 100.0).astype(np.float32)).all()
+    theta = 10000.0 ** (-(2.0 * np.arange(hd // 2)) / hd)
+    ang = pos[:, None] * theta[None, :]
+    assert (c == np.cos(ang).astype(np.float32)).all() and (s == np.sin(ang).astype(np.float32)).all()
+
+
+def pin_rope_rotation(o, lib):
+    """The rotation turns pairs (x[2i], x[2i+1]) of a head vector: a one-hot
+    vector stays within its pair; the four products and the difference / sum
+    round in the stated order (exact rationals); the norm is kept within a few
+    ulps; and q(m) . k(n) depends on m - n only (the defining property), within
+    fp32 rounding."""
+    from exact_fp import f32, fl32
+    hd = 16
+    c, s = o.rope_table(10000.0, hd, 64, lib)
+    for j in range(hd):
+        e = np.zeros(hd, np.float32)
+        e[j] = 1.0
+        r = o.rope_apply(e, c[7], s[7], lib)
+        pair = {2 * (j // 2), 2 * (j // 2) + 1}
+        assert all(r[i] == 0 for i in range(hd) if i not in pair), j
+    g = _rng(96)
+    x = g.standard_normal(hd).astype(np.float32)
+    r = o.rope_apply(x, c[9], s[9], lib)
+    for i in range(hd // 2):
+        a, b, ci, si = f32(x[2 * i]), f32(x[2 * i + 1]), f32(c[9, i]), f32(s[9, i])
+        assert Fraction(float(r[2 * i])) == fl32(fl32(a * ci) - fl32(b * si))
+        assert Fraction(float(r[2 * i + 1])) == fl32(fl32(a * si) + fl32(b * ci))
+    assert abs(np.linalg.norm(r.astype(np.float64)) / np.linalg.norm(x.astype(np.float64)) - 1) < 1e-6
+    q = g.standard_normal(hd).astype(np.float32)
+    k = g.standard_normal(hd).astype(np.float32)
+    dots = []
+    for mpos, npos in ((10, 3), (20, 13), (40, 33)):
+        dots.append(float(o.rope_apply(q, c[mpos], s[mpos], lib).astype(np.float64) @
+                          o.rope_apply(k, c[npos], s[npos], lib).astype(np.float64)))
+    assert max(dots) - min(dots) < 1e-5 * (np.abs(q).sum() * np.abs(k).sum())
+
+
+def pin_attention_closed_forms(o, lib):
+    """Attention over positions 0 .. pos: at pos 0 the output is v_0 exactly;
+    with q = 0 every weight is equal and the output is the mean of v_0 .. v_pos;
+    otherwise it equals softmax(q k^T / sqrt(hd)) V from numpy's fp64 exp,
+    rounded once to fp32 (within one fp32 ulp of that value); heads and
+    sequences use only their own q and cache."""
+    g = _rng(97)
+    m, heads, hd, smax = 2, 3, 8, 10
+    kc = g.standard_normal((m, heads, smax, hd)).astype(np.float32)
+    vc = g.standard_normal((m, heads, smax, hd)).astype(np.float32)
+    q = g.standard_normal((m, heads, hd)).astype(np.float32)
+    out0 = o.attention(q, kc, vc, 0, lib)
+    assert (out0.reshape(m, heads, hd) == vc[:, :, 0, :]).all()
+    outz = o.attention(np.zeros_like(q), kc, vc, 6, lib).reshape(m, heads, hd)
+    assert np.allclose(outz, vc[:, :, :7, :].astype(np.float64).mean(2), rtol=0, atol=1e-6)
+    for pos in (3, 9):
+        out = o.attention(q, kc, vc, pos, lib).reshape(m, heads, hd)
+        for r in range(m):
+            for h in range(heads):
+                sc = kc[r, h, :pos + 1].astype(np.float64) @ q[r, h].astype(np.float64) / np.sqrt(hd)
+                w = np.exp(sc - sc.max())
+                want = (w @ vc[r, h, :pos + 1].astype(np.float64)) / w.sum()
+                ulp = np.spacing(np.abs(want).astype(np.float32)).astype(np.float64)
+                assert np.all(np.abs(out[r, h] - want) <= ulp), (pos, r, h)
+
+
+def pin_layer_attention_position0(o, lib):
+    """At position 0 the attention output is the value vector itself, so the
+    attention layer equals the stand-in layer fed z = v (the o projection then
+    reads quant(rmsnorm(v))), and the caches receive the rotated k (position 0:
+    unrotated) and v."""
+    g = _rng(98)
+    d, f, heads, m = 32, 64, 4, 2
+    lw = _layer_weights(o, lib, g, d, f)
+    x = g.standard_normal((m, d)).astype(np.float32)
+    c, s = o.rope_table(10000.0, d // heads, 4, lib)
+    kc = np.zeros((m, heads, 4, d // heads), np.float32)
+    vc = np.zeros_like(kc)
+    xa, qkv, attn = o.layer_attn(x, lw, 1e-5, heads, c, s, kc, vc, 0, lib=lib)
+    v = qkv[:, 2 * d:]
+    assert (attn == v).all()
+    assert (kc[:, :, 0, :].reshape(m, d) == qkv[:, d:2 * d]).all() and (vc[:, :, 0, :].reshape(m, d) == v).all()
+    lw2 = dict(lw)
+    lw2["z"] = v
+    xs, _ = o.layer(x, lw2, 1e-5, lib)
+    assert (xa == xs).all()
+    # a later position: the cached k is the rotation of the projected k by that
+    # position's table row (first pair of every head, exact rationals), v is
+    # stored as it is
+    from exact_fp import f32, fl32
+    _, qkv3, _ = o.layer_attn(x, lw, 1e-5, heads, c, s, kc, vc, 3, lib=lib)
+    hd = d // heads
+    for r in range(m):
+        for h in range(heads):
+            a, b = f32(qkv3[r, d + h * hd]), f32(qkv3[r, d + h * hd + 1])
+            ci, si = f32(c[3, 0]), f32(s[3, 0])
+            assert Fraction(float(kc[r, h, 3, 0])) == fl32(fl32(a * ci) - fl32(b * si))
+            assert Fraction(float(kc[r, h, 3, 1])) == fl32(fl32(a * si) + fl32(b * ci))
+    assert (vc[:, :, 3, :].reshape(m, d) == qkv3[:, 2 * d:]).all()
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -383,3 +383,44 @@ def test_sample_checks():
         assert call(t=0.0) == bl.BL_ERR_VALUE
         assert call(p=0) == bl.BL_ERR_VALUE
         assert call(wsb=need - 1) == bl.BL_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("base,hd,npos", [(10000.0, 80, 64), (10000.0, 128, 33), (500000.0, 64, 17), (2.5, 2, 5)])
+def test_rope_table_matches_oracle(base, hd, npos, olib):
+    c, s = bl.bitnet_rope_table(base, hd, npos)
+    oc, os_ = oracle.rope_table(base, hd, npos, olib)
+    assert (c.view(np.uint32) == oc.view(np.uint32)).all() and (s.view(np.uint32) == os_.view(np.uint32)).all()
+
+
+def test_rope_table_checks():
+    f = bl._lib.bitnet_rope_table
+    assert f(10000.0, 8, 4, None, A) == bl.BL_ERR_NULL
+    assert f(10000.0, 7, 4, A, A) == bl.BL_ERR_SHAPE
+    assert f(10000.0, 8, 0, A, A) == bl.BL_ERR_SHAPE
+    assert f(1.0, 8, 4, A, A) == bl.BL_ERR_VALUE
+
+
+def test_decode_step_checks():
+    f = bl._lib.bitnet_decode_step
+    m, d, ff, H, S = 1, 256, 512, 4, 64
+    need = bl.bitnet_decode_step_workspace_bytes(m, d, ff, H, S)
+    assert need > bl.bitnet_stream_workspace_bytes(m, d, ff)
+    ok = dict(w=A, sc=A, g=A, L=2, m=m, d=d, f=ff, H=H, eps=1e-5, c=A, s=A, S=S, pos=3, kc=A, vc=A, x=A, qkv=None,
+              at=None, ws=A, wsb=need)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return f(a["w"], a["sc"], a["g"], a["L"], a["m"], a["d"], a["f"], a["H"], a["eps"], a["c"], a["s"], a["S"],
+                 a["pos"], a["kc"], a["vc"], a["x"], a["qkv"], a["at"], a["ws"], a["wsb"], S_)
+
+    S_ = None
+    assert call(kc=None) == bl.BL_ERR_NULL
+    assert call(c=None) == bl.BL_ERR_NULL
+    assert call(pos=S) == bl.BL_ERR_SHAPE
+    assert call(pos=-1) == bl.BL_ERR_SHAPE
+    assert call(H=3) == bl.BL_ERR_SHAPE       # d % H != 0
+    assert call(H=128) == bl.BL_ERR_SHAPE     # hd = 2, not a multiple of 4
+    assert call(H=1, d=512, f=512) == bl.BL_ERR_SHAPE  # hd = 512 > 256
+    assert call(kc=A + 4) == bl.BL_ERR_ALIGN
+    assert call(at=A + 8) == bl.BL_ERR_ALIGN
+    assert call(wsb=need - 1) == bl.BL_ERR_WORKSPACE

@@ -1,0 +1,113 @@
+"""GPU parity of the decode step with attention (bitnet_decode_step) against the
+oracle, through the C ABI.
+
+The device computes attention in fp32 (scores, expf, sums), the oracle in fp64
+from the definition, so the attention outputs are compared within a bound
+derived from fp32 rounding (below). Everything else is integer or follows the
+same fp32 operation order: the oracle continues each layer from the device's
+attention output (oracle.layer_attn(..., attn_in=...)), so q/k/v, the rotated
+caches and the hidden state after every step must match bit for bit.
+
+Bound on one attention output element of a head with scores s_j over
+positions 0 .. pos (u = 2^-24): each fp32 score is within
+e_s = (hd + 4) u max_j sum_i |q_i k_ji| / sqrt(hd) of the exact one; each
+weight e^(s_j - max) is then within a relative 2 e_s + 4 u (expf adds a few
+ulps); the chunked sums add (pos + 1 + 4 * chunks) u relative to
+sum_j e_j |v_j|. With V = max |v| over the head's positions the output is off
+by at most V (2 (2 e_s + 4 u) + (pos + 5 + 4 chunks) u); the test allows
+twice that."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_helpers import assert_exact, log, make_layers, to_dev, to_host, torch_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def bl():
+    import bitlinear_amd
+    return bitlinear_amd
+
+
+def _attn_bound(q_rot, kc, vc, pos, hd):
+    """Per-element bound [m][H][hd] from the oracle's q_rot [m][H][hd] and caches."""
+    u = 2.0 ** -24
+    m, heads = q_rot.shape[:2]
+    chunks = (pos + 1 + 255) // 256
+    bound = np.empty((m, heads, hd))
+    for r in range(m):
+        for h in range(heads):
+            k = kc[r, h, :pos + 1].astype(np.float64)
+            v = vc[r, h, :pos + 1].astype(np.float64)
+            sabs = (np.abs(k) @ np.abs(q_rot[r, h].astype(np.float64))).max() / np.sqrt(hd)
+            e_s = (hd + 4) * u * sabs
+            vmax = np.abs(v).max()
+            bound[r, h, :] = 2 * vmax * (2 * (2 * e_s + 4 * u) + (pos + 5 + 4 * chunks) * u) + 1e-30
+    return bound
+
+
+def _run_steps(bl, olib, n_layers, m, d, f, heads, max_seq, positions, seed, prefill=0):
+    """Decode steps at the given positions (caches optionally prefilled with
+    random entries below prefill), checking every step."""
+    import torch
+    dev = torch_dev()
+    hd = d // heads
+    layers, dw = make_layers(W.W_STREAM, n_layers, d, f, m, olib)
+    g = W.rng(150, seed, 0)
+    x0 = W.activations(g, m, d)
+    c, s = bl.bitnet_rope_table(10000.0, hd, max_seq)
+    kc_h = np.zeros((n_layers, m, heads, max_seq, hd), np.float32)
+    vc_h = np.zeros_like(kc_h)
+    if prefill:
+        kc_h[:, :, :, :prefill] = g.standard_normal((n_layers, m, heads, prefill, hd)).astype(np.float32)
+        vc_h[:, :, :, :prefill] = g.standard_normal((n_layers, m, heads, prefill, hd)).astype(np.float32)
+    kc, vc = to_dev(kc_h), to_dev(vc_h)
+    o_kc, o_vc = kc_h.copy(), vc_h.copy()
+    x = to_dev(x0)
+    xo = x0.copy()
+    qkv = torch.empty((n_layers, m, 3 * d), dtype=torch.float32, device=dev)
+    attn = torch.empty((n_layers, m, d), dtype=torch.float32, device=dev)
+    ws = torch.zeros(bl.bitnet_decode_step_workspace_bytes(m, d, f, heads, max_seq), dtype=torch.uint8, device=dev)
+    cd, sd = to_dev(c), to_dev(s)
+    worst = 0.0
+    for pos in positions:
+        log(f"decode step m={m} d={d} heads={heads} pos={pos}")
+        bl.bitnet_decode_step(dw["weights"], dw["scales"], dw["gains"], n_layers, m, d, f, heads, 1e-5, cd, sd, pos,
+                              kc, vc, x, qkv, attn, ws)
+        g_qkv, g_attn = to_host(qkv), to_host(attn)
+        for l, lw in enumerate(layers):
+            xn, o_qkv, o_attn = oracle.layer_attn(xo, lw, 1e-5, heads, c, s, o_kc[l], o_vc[l], pos,
+                                                  attn_in=g_attn[l], lib=olib)
+            assert_exact(g_qkv[l].view(np.uint32), o_qkv.view(np.uint32), f"qkv bits, layer {l}, pos {pos}")
+            q_rot = oracle.rope_apply(o_qkv[:, :d].reshape(m, heads, hd), c[pos], s[pos], olib)
+            bound = _attn_bound(q_rot, o_kc[l], o_vc[l], pos, hd).reshape(m, d)
+            err = np.abs(g_attn[l].astype(np.float64) - o_attn.astype(np.float64))
+            assert np.all(err <= bound), f"attention beyond bound at layer {l}, pos {pos}: {(err / bound).max()}"
+            worst = max(worst, float((err / bound).max()))
+            xo = xn
+        assert_exact(to_host(kc).view(np.uint32), o_kc.view(np.uint32), f"k cache bits, pos {pos}")
+        assert_exact(to_host(vc).view(np.uint32), o_vc.view(np.uint32), f"v cache bits, pos {pos}")
+        assert_exact(to_host(x).view(np.uint32), xo.view(np.uint32), f"hidden state bits, pos {pos}")
+    log(f"  largest attention error / bound: {worst:.3g}")
+
+
+@pytest.mark.parametrize("m", [1, 3, 12, 40])
+def test_decode_steps_from_position_0(bl, olib, m):
+    """Six consecutive steps from an empty cache; 1, 3, 12 and 40 sequences take
+    the GEMV, skinny and GEMM paths of the layer stream."""
+    _run_steps(bl, olib, 2, m, 256, 1024, 4, 64, list(range(6)), seed=m)
+
+
+def test_decode_step_long_context(bl, olib):
+    """Positions 700 .. 702 over a prefilled cache: three 256-position chunks
+    are combined."""
+    _run_steps(bl, olib, 2, 2, 256, 512, 2, 1024, [700, 701, 702], seed=9, prefill=700)
+
+
+def test_decode_step_bitnet_3b_shapes(bl, olib):
+    """BitNet-3B shapes (d = 2560, 32 heads of 80, f = 10240), two layers, one
+    sequence at position 300 over a prefilled cache, then position 301."""
+    _run_steps(bl, olib, 2, 1, 2560, 10240, 32, 512, [300, 301], seed=10, prefill=300)

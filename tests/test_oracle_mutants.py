@@ -92,6 +92,15 @@ C_MUTANTS = [
     ("smp_cum_ge", "if (cum > r) {", "if (cum >= r) {"),
     ("smp_exp_no_tail", "const double r = (x - k * ORACLE_LN2_HEAD) - k * ORACLE_LN2_TAIL;",
      "const double r = x - k * ORACLE_LN2_HEAD;"),
+    # rotary embedding and attention
+    ("rope_sign", "x[2 * i + 1] = as + bc;", "x[2 * i + 1] = bc - as;"),
+    ("rope_theta_half", "const double theta = pow(base, -(double)(2 * i) / (double)hd);",
+     "const double theta = pow(base, -(double)(i) / (double)hd);"),
+    ("attn_no_scale", "sc[j] = dot * scale;", "sc[j] = dot;"),
+    ("attn_drops_current", "for (int64_t j = 0; j <= pos; j++) {\n                const double e",
+     "for (int64_t j = 0; j < pos; j++) {\n                const double e"),
+    ("attn_head0_keys", "const float *K = k_cache + ((r * heads + h) * max_seq) * hd;",
+     "const float *K = k_cache + ((r * heads) * max_seq) * hd;"),
     ("smp_exp_short_series", "for (int j = 12; j >= 0; j--) poly = poly * r + inv_fact[j];",
      "for (int j = 12; j >= 0; j--) poly = poly * r + (j > 7 ? 0.0 : inv_fact[j]);"),
 ]
@@ -115,6 +124,8 @@ PY_MUTANTS = [
     ("layer_ffn_from_old_x", "    f = ffn(x, lw[\"g_ffn\"]", "    f = ffn(x - yo, lw[\"g_ffn\"]"),
     ("layer_q_uses_wk", "yq, _ = bitlinear(lw[\"wq\"], lw[\"sq\"], d, a, sa, lib)",
      "yq, _ = bitlinear(lw[\"wk\"], lw[\"sq\"], d, a, sa, lib)"),
+    ("attn_layer_k_unrotated", "k_cache[:, :, pos, :] = k_rot", "k_cache[:, :, pos, :] = yk.reshape(m, heads, hd)"),
+    ("attn_layer_v_rotated", "v_cache[:, :, pos, :] = yv.reshape(m, heads, hd)", "v_cache[:, :, pos, :] = k_rot"),
 ]
 
 
