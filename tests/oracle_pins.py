@@ -1097,6 +1097,13 @@ def pin_layer_attention_position0(o, lib):
             assert Fraction(float(kc[r, h, 3, 0])) == fl32(fl32(a * ci) - fl32(b * si))
             assert Fraction(float(kc[r, h, 3, 1])) == fl32(fl32(a * si) + fl32(b * ci))
     assert (vc[:, :, 3, :].reshape(m, d) == qkv3[:, 2 * d:]).all()
+    # q, k, v are the three projections of quant(rmsnorm(x, g_attn)), in that
+    # order (numpy's int64 product with the unpacked weights, then the scale)
+    a, sa, _ = o.quant_act(x, lw["g_attn"], 1e-5, lib)
+    for blk, (wn, sn) in enumerate((("wq", "sq"), ("wk", "sk"), ("wv", "sv"))):
+        acc = a.astype(np.int64) @ o.unpack(lw[wn], d, lib).astype(np.int64).T
+        got = qkv3[:, blk * d:(blk + 1) * d].astype(np.float64) * sa[:, None].astype(np.float64) * float(lw[sn])
+        assert (np.round(got) == acc).all(), wn
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

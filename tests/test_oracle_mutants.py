@@ -118,12 +118,33 @@ PY_MUTANTS = [
     ("ffn_up_uses_gate_w", "up, acc_up = bitlinear(w_up, s_up, d, q1, s1, lib)",
      "up, acc_up = bitlinear(w_gate, s_up, d, q1, s1, lib)"),
     ("ffn_no_norm", "q1, s1, qs1 = quant_act(x, norm_gain, eps, lib)", "q1, s1, qs1 = quant_act(x, None, eps, lib)"),
-    ("layer_no_residual_o", "    x = residual_add(x, yo, lib)\n", "    x = x\n"),
+    ("layer_no_residual_o",
+     "quant_act(lw[\"z\"], lw[\"g_attn_sub\"], eps, lib)\n    yo, _ = bitlinear(lw[\"wo\"], lw[\"so\"], d, o_in, so, lib)\n"
+     "    x = residual_add(x, yo, lib)\n",
+     "quant_act(lw[\"z\"], lw[\"g_attn_sub\"], eps, lib)\n    yo, _ = bitlinear(lw[\"wo\"], lw[\"so\"], d, o_in, so, lib)\n"
+     "    x = x\n"),
     ("layer_o_reads_x", "o_in, so, _ = quant_act(lw[\"z\"], lw[\"g_attn_sub\"], eps, lib)",
      "o_in, so, _ = quant_act(x, lw[\"g_attn_sub\"], eps, lib)"),
-    ("layer_ffn_from_old_x", "    f = ffn(x, lw[\"g_ffn\"]", "    f = ffn(x - yo, lw[\"g_ffn\"]"),
-    ("layer_q_uses_wk", "yq, _ = bitlinear(lw[\"wq\"], lw[\"sq\"], d, a, sa, lib)",
-     "yq, _ = bitlinear(lw[\"wk\"], lw[\"sq\"], d, a, sa, lib)"),
+    ("layer_ffn_from_old_x",
+     "quant_act(lw[\"z\"], lw[\"g_attn_sub\"], eps, lib)\n    yo, _ = bitlinear(lw[\"wo\"], lw[\"so\"], d, o_in, so, lib)\n"
+     "    x = residual_add(x, yo, lib)\n    f = ffn(x, lw[\"g_ffn\"]",
+     "quant_act(lw[\"z\"], lw[\"g_attn_sub\"], eps, lib)\n    yo, _ = bitlinear(lw[\"wo\"], lw[\"so\"], d, o_in, so, lib)\n"
+     "    x = residual_add(x, yo, lib)\n    f = ffn(x - yo, lw[\"g_ffn\"]"),
+    ("attn_layer_no_residual_o",
+     "o_in, so, _ = quant_act(use, lw[\"g_attn_sub\"], eps, lib)\n    yo, _ = bitlinear(lw[\"wo\"], lw[\"so\"], d, o_in, so, lib)\n"
+     "    x = residual_add(x, yo, lib)\n",
+     "o_in, so, _ = quant_act(use, lw[\"g_attn_sub\"], eps, lib)\n    yo, _ = bitlinear(lw[\"wo\"], lw[\"so\"], d, o_in, so, lib)\n"
+     "    x = x\n"),
+    ("attn_layer_o_reads_x", "o_in, so, _ = quant_act(use, lw[\"g_attn_sub\"], eps, lib)",
+     "o_in, so, _ = quant_act(x, lw[\"g_attn_sub\"], eps, lib)"),
+    ("layer_q_uses_wk", "    d = x.shape[1]\n    a, sa, _ = quant_act(x, lw[\"g_attn\"], eps, lib)\n"
+     "    yq, _ = bitlinear(lw[\"wq\"], lw[\"sq\"], d, a, sa, lib)",
+     "    d = x.shape[1]\n    a, sa, _ = quant_act(x, lw[\"g_attn\"], eps, lib)\n"
+     "    yq, _ = bitlinear(lw[\"wk\"], lw[\"sq\"], d, a, sa, lib)"),
+    ("attn_layer_q_uses_wk", "    hd = d // heads\n    a, sa, _ = quant_act(x, lw[\"g_attn\"], eps, lib)\n"
+     "    yq, _ = bitlinear(lw[\"wq\"], lw[\"sq\"], d, a, sa, lib)",
+     "    hd = d // heads\n    a, sa, _ = quant_act(x, lw[\"g_attn\"], eps, lib)\n"
+     "    yq, _ = bitlinear(lw[\"wk\"], lw[\"sq\"], d, a, sa, lib)"),
     ("attn_layer_k_unrotated", "k_cache[:, :, pos, :] = k_rot", "k_cache[:, :, pos, :] = yk.reshape(m, heads, hd)"),
     ("attn_layer_v_rotated", "v_cache[:, :, pos, :] = yv.reshape(m, heads, hd)", "v_cache[:, :, pos, :] = k_rot"),
 ]
