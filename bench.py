@@ -346,10 +346,11 @@ def main():
 
 
 def attention_leg(bl, torch, dev0, dev, L, d, f):
-    """BitNet-3B decode step with attention (bitnet_decode_step, one launch per
-    step): 32 heads of 80, caches of 2048 positions filled with N(0, 1), one
-    sequence at positions 128 and 2047. Bytes per token: the 838,860,800 weight
-    bytes plus the K and V rows read, 2 x 32 layers x 2560 x 4 x (pos + 1)."""
+    """BitNet-3B decode step with attention (bitnet_decode_step; one sequence,
+    so the whole step is one persistent launch): 32 heads of 80, caches of 2048
+    positions filled with N(0, 1), at positions 128 and 2047. Bytes per token:
+    the 838,860,800 weight bytes plus the K and V rows read,
+    2 x 32 layers x 2560 x 4 x (pos + 1)."""
     heads, hd, max_seq, m = W.BITNET_3B["heads"], d // W.BITNET_3B["heads"], 2048, 1
     c, s = bl.bitnet_rope_table(10000.0, hd, max_seq)
     cd, sd = torch.from_numpy(c).to(dev0), torch.from_numpy(s).to(dev0)
@@ -360,7 +361,7 @@ def attention_leg(bl, torch, dev0, dev, L, d, f):
     x = torch.from_numpy(W.activations(W.rng(W.W_STREAM, 998, W.T_X), m, d)).to(dev0)
     ws = torch.zeros(bl.bitnet_decode_step_workspace_bytes(m, d, f, heads, max_seq), dtype=torch.uint8, device=dev0)
     res = {"workload": "BitNet-3B decode step with attention: 32 layers x (q/k/v, RoPE + KV-cache append, "
-                       "attention over 0..pos, o, FFN), 1 sequence, 32 heads of 80, launch per step"}
+                       "attention over 0..pos, o, FFN), 1 sequence, 32 heads of 80, one persistent launch per token"}
     for pos in (128, 2047):
         def step():
             bl.bitnet_decode_step(dev["weights"], dev["scales"], dev["gains"], L, m, d, f, heads, 1e-5, cd, sd, pos,
@@ -372,6 +373,9 @@ def attention_leg(bl, torch, dev0, dev, L, d, f):
             for _ in range(iters):
                 step()
         ms = t.ms / iters
+        status = int(ws[4:8].view(torch.int32).item())
+        if status != 0:
+            raise RuntimeError(f"decode step status word {status}: the persistent kernel gave up; timing is void")
         nbytes = L * bl.bitnet_layer_bytes(d, f) + 2 * L * d * 4 * (pos + 1)
         res[f"pos_{pos}"] = {"ms_per_token": round(ms, 4), "bytes_per_token": nbytes,
                              "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}

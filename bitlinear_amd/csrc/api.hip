@@ -616,11 +616,11 @@ int bitnet_decode_stream(const uint8_t* weights, const float* scales, const floa
     if (workspace_bytes < bitnet_stream_workspace_bytes(m, d, f)) return BL_ERR_WORKSPACE;
     const hipStream_t s = as_stream(stream);
     const StreamLayout L = stream_layout(m, d, f);
-    if (bl::stream_persistent_fits((int)m, (int)d, (int)f) && !capturing(s)) {
+    if (bl::stream_persistent_fits((int)m, (int)d, (int)f, nullptr) && !capturing(s)) {
         float* qkv_out = qkv ? qkv : at<float>(workspace, L.qkv);
         return bl::launch_stream_persistent(weights, scales, gains, z, (int)n_layers, (int)d, (int)f, eps, x, qkv_out,
                                             qkv ? 3 * d : 0, at<void>(workspace, L.ll),
-                                            at<uint32_t>(workspace, L.ctrl), s);
+                                            at<uint32_t>(workspace, L.ctrl), nullptr, s);
     }
     return stream_steps(weights, scales, gains, z, n_layers, m, d, f, eps, x, qkv, workspace, nullptr, s);
 }
@@ -635,7 +635,8 @@ size_t bitnet_decode_step_workspace_bytes(int64_t m, int64_t d, int64_t f, int64
     size_t at = align_up(stream_layout(m, d, f).total, 256);
     at += align_up((size_t)(m * d) * 4, 256);  // rotated q
     at += align_up((size_t)(m * d) * 4, 256);  // attention output scratch
-    at += align_up((size_t)m * (size_t)n_heads * (size_t)bl::attn_chunks((int)max_seq) * (hd + 2) * 4, 256);
+    // chunk partials: fp32 for the launch path, epoch-tagged 8-byte words for the persistent one
+    at += align_up((size_t)m * (size_t)n_heads * (size_t)bl::attn_chunks((int)max_seq) * (hd + 2) * 8, 256);
     return at;
 }
 
@@ -655,6 +656,20 @@ int bitnet_decode_step(const uint8_t* weights, const float* scales, const float*
         (qkv && !aligned(qkv, 16)) || (attn && !aligned(attn, 16)) || !aligned(workspace, 256))
         return BL_ERR_ALIGN;
     if (workspace_bytes < bitnet_decode_step_workspace_bytes(m, d, f, n_heads, max_seq)) return BL_ERR_WORKSPACE;
+    const hipStream_t s = as_stream(stream);
+    const size_t part_off = align_up(stream_layout(m, d, f).total, 256) + 2 * align_up((size_t)(m * d) * 4, 256);
+    {
+        // one sequence: the whole step as one persistent launch
+        const bl::StreamAttn pa = {(int)n_heads, (int)max_seq, (int)pos, rope_cos, rope_sin, k_cache, v_cache, attn,
+                                   at<void>(workspace, part_off)};
+        if (bl::stream_persistent_fits((int)m, (int)d, (int)f, &pa) && !capturing(s)) {
+            const StreamLayout L = stream_layout(m, d, f);
+            float* qkv_out = qkv ? qkv : at<float>(workspace, L.qkv);
+            return bl::launch_stream_persistent(weights, scales, gains, nullptr, (int)n_layers, (int)d, (int)f, eps, x,
+                                                qkv_out, qkv ? 3 * d : 0, at<void>(workspace, L.ll),
+                                                at<uint32_t>(workspace, L.ctrl), &pa, s);
+        }
+    }
     size_t at_off = align_up(stream_layout(m, d, f).total, 256);
     AttnCtx ctx;
     ctx.heads = (int)n_heads;
@@ -670,8 +685,7 @@ int bitnet_decode_step(const uint8_t* weights, const float* scales, const float*
     at_off += align_up((size_t)(m * d) * 4, 256);
     ctx.part = at<float>(workspace, at_off);
     ctx.attn = attn;
-    return stream_steps(weights, scales, gains, nullptr, n_layers, m, d, f, eps, x, qkv, workspace, &ctx,
-                        as_stream(stream));
+    return stream_steps(weights, scales, gains, nullptr, n_layers, m, d, f, eps, x, qkv, workspace, &ctx, s);
 }
 
 // ---- greedy decoding around the stream ----------------------------------------

@@ -76,12 +76,21 @@ int launch_gemm(const uint8_t* packed, float w_scale, const float* w_scale_ptr, 
 
 // Persistent one-token layer stream (stream.hip). fits() tells whether the
 // shapes and the device suit it; ll_region holds stream_ll_words(d, f) 64-bit
-// words and ctrl two 32-bit words, all zero before the first call.
-bool stream_persistent_fits(int m, int d, int f);
+// words and ctrl two 32-bit words, all zero before the first call. With attn
+// the stand-in z is unused and every layer runs single-token attention with
+// RoPE and the caches of one sequence ([n_layers][heads][max_seq][hd]).
+struct StreamAttn {
+    int heads, max_seq, pos;
+    const float *rope_cos, *rope_sin;  // full tables [max_seq][hd / 2]
+    float *k_cache, *v_cache;
+    float* attn;  // [n_layers][d] or null
+    void* part;   // 8-byte words [heads][ceil(max_seq / 256)][hd + 2]
+};
+bool stream_persistent_fits(int m, int d, int f, const StreamAttn* attn);
 size_t stream_ll_words(int d, int f);
 int launch_stream_persistent(const uint8_t* weights, const float* scales, const float* gains, const float* z,
                              int n_layers, int d, int f, float eps, float* x, float* qkv, long long qkv_stride,
-                             void* ll_region, uint32_t* ctrl, hipStream_t s);
+                             void* ll_region, uint32_t* ctrl, const StreamAttn* attn, hipStream_t s);
 
 // Skinny MFMA products for m <= 32 tokens (skinny.hip). Without w1:
 // y[m][n] = [residual +] (acc - act_sum) / (act_scale * s_w), with s_w =

@@ -9,7 +9,10 @@
 //                                                                     f row pairs, K = d
 //   P4  x''      = x' + BitLinear_down(quant(rmsnorm(h, g_ffn_sub)))  d rows, K = f
 // P2 waits for every workgroup to finish P1, as the o projection waits for
-// attention over all heads in the full model.
+// attention over all heads in the full model. The kernels with ATTN (a decode
+// step of one sequence) run that attention: P1 publishes q, k, v, a phase PA
+// computes single-token attention with RoPE and the KV caches, and P2 waits
+// for its published output instead of the stand-in z.
 //
 // At one token every step is a short weight stream (1.6 to 13 MB) whose input
 // is a vector produced by all CUs in the step before. Launching a kernel per
@@ -69,6 +72,8 @@
 // start of that wait (s_memrealtime, 100 MHz) and by a shared status word; a
 // workgroup that gives up sets the status, every other one sees it and leaves,
 // so the grid always drains.
+#include <type_traits>
+
 #include "internal.h"
 #include "prefetch.h"
 #include "wave.h"
@@ -120,6 +125,16 @@ struct StreamArgs {
     uint32_t* ctrl;              // [0] epoch base, [1] status
     int n_layers;
     float eps;
+    // attention (the kernels with ATTN only)
+    uint32_t* qq;                // q, k, v (published by P1), two copies of 3d words
+    uint32_t* ao;                // attention output (published by PA), two copies of d words
+    const float* rope_cos;       // row pos of the rotary table [hd / 2]
+    const float* rope_sin;
+    float* k_cache;              // [n_layers][heads][max_seq][hd]
+    float* v_cache;
+    float* attn;                 // [n_layers][d] or null
+    unsigned long long* apart;   // per head and chunk: epoch-tagged [max, sum, hd weighted sums]
+    int heads, hd, max_seq, pos, chunks_max;
 };
 
 __device__ __forceinline__ void ll_store(unsigned long long* p, float v, uint32_t e)
@@ -396,7 +411,279 @@ __device__ __forceinline__ void dots(const uint4* wr, const uint8_t* q, const ui
     if (tile >= 0) flush();
 }
 
-template <int D, int F>
+// ---- single-token attention inside the stream --------------------------------
+// Phase PA of the kernels with ATTN ("Transformer Block", "Forward Pass with
+// KV Cache"; "BitNet Model - Complete Inference Pipeline", "KV Cache State").
+// Positions 0 .. pos of a head split into chunks of 256; G = 256 / heads
+// workgroups serve each head, workgroup (h, split) taking the chunks
+// c = split, split + G, ... Each waits for the 3 hd published words of q, k
+// and v of its head, turns q and k by RoPE (the one holding position pos also
+// appends k and v to the caches), and per chunk forms the scores
+// q . k_j / sqrt(hd) (one thread per position), the chunk's maximum and sum of
+// e^(s - max), and the weighted sums of v (512 / hd groups of hd threads, each
+// group over every (512 / hd)-th position, then the groups in order). Split 0
+// merges the chunks by rescaling with e^(max_c - max), as the launch path's
+// merge kernel does, and publishes the head's output for P2. Scores,
+// exponentials and sums are fp32.
+constexpr int kAttnChunk = 256;
+constexpr int kMaxAttnChunks = 32;  // max_seq <= 8192
+constexpr int kMaxHd = 256;
+
+struct AttnShared {
+    __attribute__((aligned(16))) float q[kMaxHd];  // rotated q, rotated k and v of position pos
+    __attribute__((aligned(16))) float k[kMaxHd];
+    __attribute__((aligned(16))) float v[kMaxHd];
+    float e[kAttnChunk];                    // e^(s_j - max) of the chunk's positions
+    float part[kT];                         // per-group partial sums of the weighted values
+    float red[kT / 64];
+    float chunk[kMaxAttnChunks][kMaxHd + 2];  // per chunk: max, sum, weighted sums
+};
+struct NoAttnShared {};
+
+__device__ __forceinline__ float block_max_f(float v, float* red)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v = wave_max(v);
+    __syncthreads();  // red is free
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    float m = red[0];
+#pragma unroll
+    for (int i = 1; i < kT / 64; ++i) m = fmaxf(m, red[i]);
+    return m;
+}
+
+__device__ __forceinline__ float block_sum_f(float v, float* red)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    __syncthreads();
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    float s = red[0];
+#pragma unroll
+    for (int i = 1; i < kT / 64; ++i) s += red[i];
+    return s;
+}
+
+// Attention work of workgroup (h, split) in layer l: head h's chunks c with
+// c % G == split (G workgroups per head). The workgroup that holds position
+// pos (the last chunk) appends k and v to the caches. Split 0 merges: its own
+// chunks' partials stay in LDS, the others' arrive as epoch-tagged words
+// (epoch E2, so no copy needs clearing), and it publishes the head's output.
+// False (for the whole workgroup) when a wait gave up. D: the model width (q,
+// k, v are the 3 consecutive D-word rows of qq). The cache rows are not
+// prefetched: a wave's loads complete in order, so a prefetch issued before
+// the wait for q, k, v, or at the start of the layer, only delayed that wait
+// (measured slower at positions 128 and 2047).
+template <int D>
+__device__ bool attention_split(const StreamArgs& a, int l, int h, int split, int G, uint32_t E2,
+                                const uint32_t* qq_cur, uint32_t* ao_cur, uint32_t* ao_old, AttnShared& s)
+{
+    const int t = threadIdx.x;
+    const int hd = a.hd, half = hd / 2, pos = a.pos;
+    const int nch = (pos + kAttnChunk) / kAttnChunk;
+    const int last = (nch - 1) % G;  // the split that holds position pos
+    const float* kbase = a.k_cache + ((size_t)l * a.heads + h) * a.max_seq * hd;
+    const float* vbase = a.v_cache + ((size_t)l * a.heads + h) * a.max_seq * hd;
+    // the 3 hd words of this head: q, then k, then v
+    const int n = 3 * hd;
+    const long long t_start = (long long)__builtin_amdgcn_s_memrealtime();
+    uint32_t w[2];
+    bool failed = false;
+    for (int spin = 0;; ++spin) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int u = min(t + kT * i, n - 1);
+            const int seg = u / hd;
+            w[i] = __hip_atomic_load(qq_cur + seg * D + h * hd + (u - seg * hd), __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (w[0] != 0u && w[1] != 0u) break;
+        if ((spin & 15) == 15 &&
+            (status_load(a.ctrl) != 0 || (long long)__builtin_amdgcn_s_memrealtime() - t_start > kTimeoutTicks)) {
+            failed = true;
+            break;
+        }
+        __builtin_amdgcn_s_sleep(3);
+    }
+    if (__syncthreads_or(failed ? 1 : 0)) {
+        if (t == 0) __hip_atomic_fetch_or(a.ctrl + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return false;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int u = t + kT * i;
+        if (u < n) {
+            // q, k, v are (acc - sum q) / (s_a s_w) with a positive divisor and so
+            // never -0.0: the word -0.0 is the published +0.0
+            const float x = w[i] == 0x80000000u ? 0.0f : __uint_as_float(w[i]);
+            const int seg = u / hd, i_ = u - seg * hd;
+            (seg == 0 ? s.q : seg == 1 ? s.k : s.v)[i_] = x;
+        }
+    }
+    __syncthreads();
+    // RoPE of q and k (each thread its own pair); the split of the last chunk
+    // writes k and v at position pos of the caches
+    if (t < half) {
+        const float c = a.rope_cos[t], sn = a.rope_sin[t];
+        {
+            const float x0 = s.q[2 * t], x1 = s.q[2 * t + 1];
+            const float ac = x0 * c, bs = x1 * sn, as = x0 * sn, bc = x1 * c;
+            s.q[2 * t] = ac - bs;
+            s.q[2 * t + 1] = as + bc;
+        }
+        {
+            const float x0 = s.k[2 * t], x1 = s.k[2 * t + 1];
+            const float ac = x0 * c, bs = x1 * sn, as = x0 * sn, bc = x1 * c;
+            s.k[2 * t] = ac - bs;
+            s.k[2 * t + 1] = as + bc;
+        }
+        if (split == last) {
+            float* krow = a.k_cache + (((size_t)l * a.heads + h) * a.max_seq + pos) * hd;
+            float* vrow = a.v_cache + (((size_t)l * a.heads + h) * a.max_seq + pos) * hd;
+            krow[2 * t] = s.k[2 * t];
+            krow[2 * t + 1] = s.k[2 * t + 1];
+            vrow[2 * t] = s.v[2 * t];
+            vrow[2 * t + 1] = s.v[2 * t + 1];
+        }
+    }
+    __syncthreads();
+    const float scale = 1.0f / sqrtf((float)hd);
+    const int groups = kT / hd, g = t / hd, gi = t - g * hd;
+    for (int c = split; c < nch; c += G) {
+        const int j0 = c * kAttnChunk, cnt = min(kAttnChunk, pos + 1 - j0);
+        float sc = -INFINITY;
+        if (t < cnt) {
+            float dot = 0.0f;
+            if (j0 + t < pos) {
+                // a cache row: the loads of four 16-byte pieces go out together
+                const float* kj = kbase + (size_t)(j0 + t) * hd;
+                int i = 0;
+                for (; i + 16 <= hd; i += 16) {
+                    float4 kv[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) kv[u] = *reinterpret_cast<const float4*>(kj + i + 4 * u);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        dot += s.q[i + 4 * u] * kv[u].x;
+                        dot += s.q[i + 4 * u + 1] * kv[u].y;
+                        dot += s.q[i + 4 * u + 2] * kv[u].z;
+                        dot += s.q[i + 4 * u + 3] * kv[u].w;
+                    }
+                }
+                for (; i < hd; i += 4) {
+                    const float4 kv = *reinterpret_cast<const float4*>(kj + i);
+                    dot += s.q[i] * kv.x;
+                    dot += s.q[i + 1] * kv.y;
+                    dot += s.q[i + 2] * kv.z;
+                    dot += s.q[i + 3] * kv.w;
+                }
+            } else {
+                // position pos, from LDS: its cache row is being written now
+                for (int i = 0; i < hd; ++i) dot += s.q[i] * s.k[i];
+            }
+            sc = dot * scale;
+        }
+        const float mx = block_max_f(sc, s.red);
+        if (t < kAttnChunk) s.e[t] = t < cnt ? expf(sc - mx) : 0.0f;
+        const float sum = block_sum_f(t < cnt ? s.e[t] : 0.0f, s.red);  // its barriers also publish e[]
+        if (g < groups) {
+            // positions j0 + jj, jj = g, g + groups, ... ascending: cache rows in
+            // batches of eight independent loads, then position pos (always the
+            // last one) from LDS
+            // batches of 16 with the next batch's loads issued before the
+            // current one is summed
+            const int lim = min(cnt, pos - j0);
+            const int mine = lim > g ? (lim - g + groups - 1) / groups : 0;  // my cache rows
+            const size_t step = (size_t)groups * hd;
+            const float* vp = vbase + (size_t)(j0 + g) * hd + gi;
+            constexpr int B = 16;
+            float va[B], vb[B];
+#pragma unroll
+            for (int u = 0; u < B; ++u) va[u] = u < mine ? vp[(size_t)u * step] : 0.0f;
+            float acc = 0.0f;
+            for (int k0 = 0; k0 < mine; k0 += B) {
+#pragma unroll
+                for (int u = 0; u < B; ++u) vb[u] = k0 + B + u < mine ? vp[(size_t)(k0 + B + u) * step] : 0.0f;
+#pragma unroll
+                for (int u = 0; u < B; ++u)
+                    if (k0 + u < mine) acc += s.e[g + (k0 + u) * groups] * va[u];
+#pragma unroll
+                for (int u = 0; u < B; ++u) va[u] = vb[u];
+            }
+            const int jj = g + mine * groups;  // my first position not in the cache loop
+            if (jj == pos - j0 && jj < cnt) acc += s.e[jj] * s.v[gi];  // pos lies in this chunk
+            s.part[g * hd + gi] = acc;
+        }
+        __syncthreads();
+        float* cp = s.chunk[split == 0 ? c : 0];
+        if (t < hd) {
+            float acc = 0.0f;
+            for (int q = 0; q < groups; ++q) acc += s.part[q * hd + t];
+            cp[2 + t] = acc;
+        }
+        if (t == 0) {
+            cp[0] = mx;
+            cp[1] = sum;
+        }
+        if (split != 0) {
+            // publish the chunk's partials: [max, sum, hd weighted sums]
+            __syncthreads();
+            unsigned long long* dst = a.apart + ((size_t)h * a.chunks_max + c) * (hd + 2);
+            if (t < hd + 2) ll_store(dst + t, cp[t], E2);
+        }
+        // the next chunk's first writes (e[], part[], the chunk slot) follow two barriers
+    }
+    if (split != 0) return true;
+    // split 0: the other chunks' partials, then the merge and the head's output
+    const int others = nch - (nch + G - 1) / G;  // chunks held by splits 1 .. G-1
+    if (others > 0) {
+        const int nw = others * (hd + 2);
+        const long long t0 = (long long)__builtin_amdgcn_s_memrealtime();
+        bool bad = false;
+        for (int spin = 0;; ++spin) {
+            bool ready = true;
+            for (int u = t; u < nw; u += kT) {
+                // u-th word of the chunks c % G != 0, in chunk order
+                const int oc = u / (hd + 2), wi = u - oc * (hd + 2);
+                const int c = oc + oc / (G - 1) + 1;
+                const unsigned long long v = ll_load(a.apart + ((size_t)h * a.chunks_max + c) * (hd + 2) + wi);
+                if ((uint32_t)(v >> 32) != E2) {
+                    ready = false;
+                } else {
+                    s.chunk[c][wi] = __uint_as_float((uint32_t)v);
+                }
+            }
+            if (__syncthreads_and(ready ? 1 : 0)) break;
+            if ((spin & 15) == 15 && (status_load(a.ctrl) != 0 ||
+                                      (long long)__builtin_amdgcn_s_memrealtime() - t0 > kTimeoutTicks)) {
+                bad = true;
+            }
+            if (__syncthreads_or(bad ? 1 : 0)) {
+                if (t == 0) __hip_atomic_fetch_or(a.ctrl + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                return false;
+            }
+            __builtin_amdgcn_s_sleep(3);
+        }
+    }
+    __syncthreads();
+    if (t < hd) {
+        float mx = -INFINITY;
+        for (int c = 0; c < nch; ++c) mx = fmaxf(mx, s.chunk[c][0]);
+        float den = 0.0f, acc = 0.0f;
+        for (int c = 0; c < nch; ++c) den += s.chunk[c][1] * expf(s.chunk[c][0] - mx);
+        for (int c = 0; c < nch; ++c) acc += s.chunk[c][2 + t] * expf(s.chunk[c][0] - mx);
+        const float out = acc / den;
+        val_store(ao_cur + h * hd + t, out);
+        val_clear(ao_old + h * hd + t);
+        if (a.attn) a.attn[(size_t)l * D + h * hd + t] = out;
+    }
+    return true;
+}
+
+template <int D, int F, bool ATTN>
 __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
 {
     using S1 = Step<3 * D, D, 1>;  // q, k, v stacked
@@ -409,6 +696,7 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
     constexpr size_t blob = 4 * dd + 3 * fd;
 
     __shared__ Shared sh;
+    __shared__ std::conditional_t<ATTN, AttnShared, NoAttnShared> ash;
     const int w = blockIdx.x, t = threadIdx.x;
 
     const uint32_t base = __hip_atomic_load(a.ctrl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -445,7 +733,7 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
         load_strided<D>(a.gains + (size_t)l * (3 * D + F), g1);
         // P2's gains and stand-in input (its norm + quant follows the wait for P1)
         load_strided<D>(a.gains + (size_t)l * (3 * D + F) + D, g2);
-        load_strided<D>(a.z + (size_t)l * D, zv);
+        if constexpr (!ATTN) load_strided<D>(a.z + (size_t)l * D, zv);
     };
     auto fetch3 = [&](int l) {
         const uint8_t* W = a.weights + (size_t)l * blob + 4 * dd + (size_t)r3 * (D / 4);
@@ -475,7 +763,7 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
         prefetch_span<S4::R * (F / 4)>(a.weights + (size_t)l * blob + 4 * dd + 2 * fd + (size_t)r2 * (F / 4), trash);
     };
     for (int l = 0; l < a.n_layers; ++l) {
-        const uint32_t E = base + 4u * (uint32_t)l;
+        [[maybe_unused]] const uint32_t E = base + 4u * (uint32_t)l;
         float sw[7];  // this layer's weight scales
 #pragma unroll
         for (int i = 0; i < 7; ++i) sw[i] = a.scales[7 * l + i];
@@ -489,6 +777,10 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
         uint32_t* xb_old = a.xb + (cp ^ 1) * D;
         uint32_t* hh_cur = a.hh + cp * F;
         uint32_t* hh_old = a.hh + (cp ^ 1) * F;
+        uint32_t* qq_cur = a.qq + cp * 3 * D;
+        uint32_t* qq_old = a.qq + (cp ^ 1) * 3 * D;
+        uint32_t* ao_cur = a.ao + cp * D;
+        uint32_t* ao_old = a.ao + (cp ^ 1) * D;
 
         // ---- P1: q, k, v ----
         {
@@ -506,23 +798,48 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
             if (e1) {
                 const int row = r1 + t, mat = row / D;
                 const float inv = 1.0f / (s_a * (mat == 0 ? sw[0] : (mat == 1 ? sw[1] : sw[2])));
-                qkv[row] = (float)(sh.acc[t] - qsum) * inv;
+                const float val = (float)(sh.acc[t] - qsum) * inv;
+                qkv[row] = val;
+                if constexpr (ATTN) {
+                    val_store(qq_cur + row, val);
+                    val_clear(qq_old + row);
+                }
             }
-            if (t == 0) ll_store(a.done + kFlagStride * w, 0.0f, E + 1);
+            if constexpr (!ATTN) {
+                if (t == 0) ll_store(a.done + kFlagStride * w, 0.0f, E + 1);
+            }
+        }
+        // ---- PA: attention, G = 256 / heads workgroups per head ----
+        if constexpr (ATTN) {
+            const int G = kGrid / a.heads, nch = (a.pos + kAttnChunk) / kAttnChunk;
+            if (w < a.heads * G && w % G < nch &&
+                !attention_split<D>(a, l, w / G, w % G, G, E + 2, qq_cur, ao_cur, ao_old, ash))
+                return;
         }
         // ---- P2: o projection of the stand-in z, residual ----
         {
             // z stands in for the attention output, which exists only once
             // every workgroup has finished P1: its norm + quant follows the wait
             if (t < S2::R) sh.acc[t] = 0;
-            float fl[1];
             fetch2(l);
-            if (!poll_vec<kGrid, kFlagStride>(a.done, E + 1, fl, a.ctrl)) return;
+            float ov[ND];
+            if constexpr (ATTN) {
+                // the attention output of every head (each head's inputs came
+                // from P1 rows of many workgroups, so every workgroup has
+                // published P1, and read the base, by now)
+                if (!poll_val<D>(ao_cur, ov, a.ctrl)) return;
+            } else {
+                float fl[1];
+                if (!poll_vec<kGrid, kFlagStride>(a.done, E + 1, fl, a.ctrl)) return;
+            }
             pf3(l);
             if (l == 0 && w == 0 && t == 0)  // every workgroup has read the base by now
                 __hip_atomic_store(a.ctrl, base + 4u * (uint32_t)a.n_layers, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
-            norm_quant<D>(zv, g2, a.eps, sh, s_a, qsum);
+            if constexpr (ATTN)
+                norm_quant<D>(ov, g2, a.eps, sh, s_a, qsum);
+            else
+                norm_quant<D>(zv, g2, a.eps, sh, s_a, qsum);
             dots<S2>(w2, sh.q, sh.zero, sh.acc);
             __syncthreads();
             if (e2) {
@@ -579,11 +896,11 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
 using StreamFn = void (*)(StreamArgs);
 
 // Shapes with a compiled kernel: BitNet-3B, BitNet-1.3B and a small test shape.
-StreamFn stream_fn(int d, int f)
+StreamFn stream_fn(int d, int f, bool attn)
 {
-    if (d == 2560 && f == 10240) return stream_kernel<2560, 10240>;
-    if (d == 2048 && f == 8192) return stream_kernel<2048, 8192>;
-    if (d == 256 && f == 1024) return stream_kernel<256, 1024>;
+    if (d == 2560 && f == 10240) return attn ? stream_kernel<2560, 10240, true> : stream_kernel<2560, 10240, false>;
+    if (d == 2048 && f == 8192) return attn ? stream_kernel<2048, 8192, true> : stream_kernel<2048, 8192, false>;
+    if (d == 256 && f == 1024) return attn ? stream_kernel<256, 1024, true> : stream_kernel<256, 1024, false>;
     return nullptr;
 }
 
@@ -619,10 +936,13 @@ bool one_per_cu(StreamFn fn)
 
 }  // namespace
 
-bool stream_persistent_fits(int m, int d, int f)
+bool stream_persistent_fits(int m, int d, int f, const StreamAttn* attn)
 {
     if (m != 1) return false;
-    const StreamFn fn = stream_fn(d, f);
+    if (attn && (attn->heads < 1 || attn->heads > kGrid || d % attn->heads != 0 || (d / attn->heads) % 4 != 0 ||
+                 d / attn->heads > kMaxHd || attn->max_seq > kMaxAttnChunks * kAttnChunk))
+        return false;
+    const StreamFn fn = stream_fn(d, f, attn != nullptr);
     if (!fn) return false;
     const DeviceInfo info = device_info();
     return info.cus >= kGrid && one_per_cu(fn);
@@ -630,9 +950,9 @@ bool stream_persistent_fits(int m, int d, int f)
 
 int launch_stream_persistent(const uint8_t* weights, const float* scales, const float* gains, const float* z,
                              int n_layers, int d, int f, float eps, float* x, float* qkv, long long qkv_stride,
-                             void* ll_region, uint32_t* ctrl, hipStream_t s)
+                             void* ll_region, uint32_t* ctrl, const StreamAttn* attn, hipStream_t s)
 {
-    const StreamFn fn = stream_fn(d, f);
+    const StreamFn fn = stream_fn(d, f, attn != nullptr);
     if (!fn) return BL_ERR_SHAPE;
     StreamArgs a;
     a.weights = weights;
@@ -649,9 +969,29 @@ int launch_stream_persistent(const uint8_t* weights, const float* scales, const 
     a.xa = vec;
     a.xb = vec + 2 * d;
     a.hh = vec + 4 * d;
+    a.qq = vec + 4 * d + 2 * f;
+    a.ao = vec + 10 * d + 2 * f;
     a.ctrl = ctrl;
     a.n_layers = n_layers;
     a.eps = eps;
+    a.rope_cos = a.rope_sin = nullptr;
+    a.k_cache = a.v_cache = a.attn = nullptr;
+    a.apart = nullptr;
+    a.heads = a.hd = a.max_seq = a.pos = a.chunks_max = 0;
+    if (attn) {
+        const int hd = d / attn->heads;
+        a.rope_cos = attn->rope_cos + (size_t)attn->pos * (hd / 2);
+        a.rope_sin = attn->rope_sin + (size_t)attn->pos * (hd / 2);
+        a.k_cache = attn->k_cache;
+        a.v_cache = attn->v_cache;
+        a.attn = attn->attn;
+        a.heads = attn->heads;
+        a.hd = hd;
+        a.max_seq = attn->max_seq;
+        a.pos = attn->pos;
+        a.apart = static_cast<unsigned long long*>(attn->part);
+        a.chunks_max = (attn->max_seq + kAttnChunk - 1) / kAttnChunk;
+    }
     // A plain launch: with at least kGrid CUs that each fit one workgroup, all
     // kGrid workgroups are resident together on a device that runs nothing
     // else. Should one not become resident (another queue holding CUs), the
@@ -662,6 +1002,8 @@ int launch_stream_persistent(const uint8_t* weights, const float* scales, const 
     return hipGetLastError() == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
 }
 
-size_t stream_ll_words(int d, int f) { return (size_t)2 * d + f + (size_t)kGrid * kFlagStride; }
+// 8-byte words: the flags, then two copies each of x (twice), h, q/k/v and the
+// attention output as 4-byte words
+size_t stream_ll_words(int d, int f) { return (size_t)6 * d + f + (size_t)kGrid * kFlagStride; }
 
 }  // namespace bl

@@ -342,8 +342,21 @@ int bitnet_decode_stream(const uint8_t *weights, const float *scales, const floa
  *   x         : device fp32 [m][d], updated in place.
  *   qkv       : device fp32 [n_layers][m][3d] or NULL (q, k, v before RoPE).
  *   attn      : device fp32 [n_layers][m][d] or NULL (attention outputs).
- *   workspace : bitnet_decode_step_workspace_bytes(m, d, f, n_heads, max_seq).
- * It runs one launch per step (the persistent kernel carries no attention).
+ *   workspace : bitnet_decode_step_workspace_bytes(m, d, f, n_heads, max_seq)
+ *               bytes, 256-aligned, zero-filled before its first use and then
+ *               kept between calls (its first 8 bytes are the stream's
+ *               {phase counter, status} words).
+ * At m == 1, for the persistent kernel's shapes and device (as in
+ * bitnet_decode_stream) with n_heads <= 256 and max_seq <= 8192, the whole
+ * step is one persistent launch: q, k and v are published like the stream's
+ * other vectors, workgroup h < n_heads computes head h (RoPE, cache append,
+ * attention over positions 0 .. pos in chunks of 256 merged by rescaling),
+ * and the o projection waits for the published attention output. Its timeout
+ * and status rules are those of bitnet_decode_stream. Otherwise (and while the
+ * stream is being captured into a graph) it runs one launch per step: RoPE and
+ * append, one workgroup per (sequence, head, 256 positions), a merge launch.
+ * Both compute the same fp32 attention arithmetic up to the order of the
+ * weighted sums, within the same bound.
  * Errors: NULL, SHAPE (pos outside [0, max_seq), ...), ALIGN, WORKSPACE, LAUNCH. */
 size_t bitnet_decode_step_workspace_bytes(int64_t m, int64_t d, int64_t f, int64_t n_heads, int64_t max_seq);
 int bitnet_decode_step(const uint8_t *weights, const float *scales, const float *gains, int64_t n_layers,

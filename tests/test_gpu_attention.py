@@ -21,7 +21,7 @@ import pytest
 
 import oracle
 import workloads as W
-from gpu_helpers import assert_exact, log, make_layers, to_dev, to_host, torch_dev
+from gpu_helpers import assert_exact, log, make_layers, stream_ctrl, to_dev, to_host, torch_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -91,6 +91,7 @@ def _run_steps(bl, olib, n_layers, m, d, f, heads, max_seq, positions, seed, pre
         assert_exact(to_host(kc).view(np.uint32), o_kc.view(np.uint32), f"k cache bits, pos {pos}")
         assert_exact(to_host(vc).view(np.uint32), o_vc.view(np.uint32), f"v cache bits, pos {pos}")
         assert_exact(to_host(x).view(np.uint32), xo.view(np.uint32), f"hidden state bits, pos {pos}")
+    assert stream_ctrl(ws)[1] == 0, "stream status word"
     log(f"  largest attention error / bound: {worst:.3g}")
 
 
@@ -109,5 +110,25 @@ def test_decode_step_long_context(bl, olib):
 
 def test_decode_step_bitnet_3b_shapes(bl, olib):
     """BitNet-3B shapes (d = 2560, 32 heads of 80, f = 10240), two layers, one
-    sequence at position 300 over a prefilled cache, then position 301."""
+    sequence at position 300 over a prefilled cache, then position 301 (one
+    sequence: the persistent kernel, two 256-position chunks)."""
     _run_steps(bl, olib, 2, 1, 2560, 10240, 32, 512, [300, 301], seed=10, prefill=300)
+
+
+def test_decode_step_persistent_long_context(bl, olib):
+    """One sequence (the persistent kernel) at positions 700 .. 702 over a
+    prefilled cache: three chunks merged inside one head's workgroup; then
+    position 1023 (the cache's last slot, four chunks) and position 0 again
+    (one position)."""
+    _run_steps(bl, olib, 2, 1, 256, 1024, 2, 1024, [700, 701, 702, 1023, 0], seed=11, prefill=700)
+
+
+def test_decode_step_persistent_heads_of_4(bl, olib):
+    """One sequence with 64 heads of 4 values (the smallest head), positions 0 .. 2."""
+    _run_steps(bl, olib, 2, 1, 256, 1024, 64, 64, [0, 1, 2], seed=12)
+
+
+def test_decode_step_bitnet_1p3b_shapes(bl, olib):
+    """BitNet-1.3B shapes (d = 2048, 16 heads of 128, f = 8192), two layers, one
+    sequence at positions 255 and 256 (one chunk, then two)."""
+    _run_steps(bl, olib, 2, 1, 2048, 8192, 16, 512, [255, 256], seed=13, prefill=255)
