@@ -463,6 +463,34 @@ def sampling_leg(bl, torch, T, dev0, check):
     return res
 
 
+def vendor_int8_gemm(torch, dev0, q, t_rows):
+    """Context for the prefill GEMM: the library int8 GEMM of this PyTorch build
+    (torch._int_mm, hipBLASLt on ROCm) on the same M x K activations against an
+    int8 [N][K] weight matrix (ternary values, one byte each), y = q . W^T in
+    int32. Not the same product (no 2-bit weights, no dequant), the same MFMA
+    work."""
+    M, K = q.shape
+    gen = torch.Generator(device=dev0)
+    gen.manual_seed(7)
+    wt = torch.randint(-1, 2, (t_rows, K), generator=gen, device=dev0, dtype=torch.int8)
+    try:
+        def call():
+            return torch._int_mm(q, wt.t())
+        for _ in range(3):
+            call()
+        iters = 20
+        with Timer() as tv:
+            for _ in range(iters):
+                call()
+        ms = tv.ms / iters
+        res = {"call": "torch._int_mm(q [M][K] int8, W^T) with W [N][K] int8", "ms": round(ms, 4),
+               "tops": round(2.0 * M * t_rows * K / (ms * 1e-3) / 1e12, 1)}
+    except Exception as ex:  # an op this build lacks is reported, not fatal
+        res = {"call": "torch._int_mm", "error": str(ex)[:200]}
+    del wt
+    return res
+
+
 def prefill_ffn_leg(bl, torch, T, dev0, check):
     """The FFN sub-layer at 2048 tokens (d = 2560, f = 10240): quant of x, the
     paired gate/up MFMA GEMM with relu(gate)^2 * up in its epilogue, sub-norm +
@@ -749,6 +777,8 @@ def extra_measurements(bl, torch, T, dev0, check=True):
                                    "frac": round(tops / INT8_PEAK_TOPS, 4), "algorithmic_ops": int(ops),
                                    "traffic": None}}
     log(f"prefill: GEMM {gemm_ms:.4f} ms = {out['prefill']['gemm_tops']} TOPS")
+    out["prefill"]["vendor_int8_gemm"] = vendor_int8_gemm(torch, dev0, q, t_rows=N)
+    log(f"prefill: vendor int8 GEMM on the same shape: {out['prefill']['vendor_int8_gemm']}")
     if check:
         # the timed call's y against the oracle: one random row in every
         # 128-row block tile, plus the first and last rows, every column

@@ -789,7 +789,8 @@ int sample_check(const float* logits, int64_t m, int64_t n, float temperature, c
                  const void* workspace, size_t workspace_bytes)
 {
     if (!logits || !u || !token || !workspace) return BL_ERR_NULL;
-    if (!dim_ok(m) || !dim_ok(n) || m > 0x7fffffff || n > 0x7fffffff) return BL_ERR_SHAPE;
+    // n < 2^23: a total weight of n tokens of at most 2^40 each fits in an int64
+    if (!dim_ok(m) || !dim_ok(n) || m > 0x7fffffff || n >= (int64_t)1 << 23) return BL_ERR_SHAPE;
     if (!aligned(logits, 4) || !aligned(u, 8) || !aligned(token, 4) || !aligned(workspace, 256)) return BL_ERR_ALIGN;
     if (!(temperature > 0.0f) || !(temperature < INFINITY)) return BL_ERR_VALUE;
     if (workspace_bytes < bitnet_sample_workspace_bytes(m, n)) return BL_ERR_WORKSPACE;

@@ -17,9 +17,19 @@
 //             cumulative weight exceeds r is chosen.
 // Nothing is sorted. Each "first token in sorted order whose cumulative
 // weight reaches a target" is found by a most-significant-digit radix
-// selection over the keys, 8 bits per pass: a pass sums the (exact, int64)
-// weights of the candidates per digit value in LDS, and one wave finds the
-// digit at which the running total crosses the target.
+// selection over the keys in six digits (12, 10, 10, 11, 11, 10 bits): a
+// level sums the (exact, int64) weights and the counts of the candidates per
+// digit value in LDS, and the workgroup finds the digit at which the running
+// total crosses the target with one prefix scan. The first level's sums come
+// from the pass that computes the weights and serve both selections; the
+// twelve-bit first digit (sign, exponent, three mantissa bits of the logit)
+// spreads logits of a few units over many bins, which keeps the LDS atomics
+// of that pass from piling onto a handful of addresses. Once a level's
+// candidates number at most 2048, the pass that reads them also copies their
+// keys and weights into LDS, and the deeper levels (and the second selection,
+// while its candidates are among them) run from that list. The kept weight M
+// is read off the first selection (the weight above the kept boundary plus
+// the boundary token's own).
 //
 // The exponential is written out here (fp64, valid on [-32, 0]): Cody-Waite
 // range reduction x = k ln2 + r with ln2 split into a 32-significant-bit head
@@ -69,12 +79,33 @@ __device__ __forceinline__ unsigned long long sort_key(float l, int i)
     return ((unsigned long long)ord << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)i);
 }
 
+// Radix digits of the key from the top: 12 bits (sign, exponent and three
+// mantissa bits of the logit, so that logits of a few units spread over many
+// bins), then 10, 10, 11, 11, 10.
+constexpr int kLevels = 6;
+__device__ __forceinline__ int digit_width(int lv) { return lv == 0 ? 12 : (lv == 3 || lv == 4) ? 11 : 10; }
+__device__ __forceinline__ int digit_shift(int lv)
+{
+    return lv == 0 ? 52 : lv == 1 ? 42 : lv == 2 ? 32 : lv == 3 ? 21 : lv == 4 ? 10 : 0;
+}
+constexpr int kBins0 = 4096;  // first level
+constexpr int kBins = 2048;   // deeper levels
+constexpr int kCap = 2048;    // candidates held in LDS
+constexpr int kB = 8;         // logits per thread whose loads a pass issues together
+
 struct Shared {
-    unsigned long long hist[256];
-    long long red[kWaves];
+    unsigned long long h0w[kBins0];  // first level over all tokens: weight sums
+    unsigned int h0c[kBins0];        //                               counts
+    unsigned long long hw[kBins];    // deeper levels
+    unsigned int hc[kBins];
+    unsigned long long ck[kCap];     // the candidate list: keys
+    long long cw[kCap];              //                     weights
+    long long red[kWaves][3];
     float redf[kWaves];
+    unsigned int ncand;
     int sel_digit;
-    long long sel_above;
+    long long sel_above_t, sel_above_w, sel_bin_w;
+    unsigned int sel_above_c, sel_bin_c;
 };
 
 __device__ __forceinline__ long long wave_sum_i64(long long v)
@@ -90,11 +121,11 @@ __device__ long long block_sum_i64(long long v, Shared& sh)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     v = wave_sum_i64(v);
     __syncthreads();  // sh.red is free
-    if (lane == 0) sh.red[wave] = v;
+    if (lane == 0) sh.red[wave][0] = v;
     __syncthreads();
     long long t = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) t += sh.red[w];
+    for (int w = 0; w < kWaves; ++w) t += sh.red[w][0];
     return t;
 }
 
@@ -111,65 +142,166 @@ __device__ float block_max(float v, Shared& sh)
     return t;
 }
 
+// Exclusive prefix sums over the workgroup (threads in order) of three int64s.
+__device__ void block_excl3(long long (&v)[3], Shared& sh)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    long long inc[3] = {v[0], v[1], v[2]};
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const long long o = __shfl_up(inc[j], off, 64);
+            if (lane >= off) inc[j] += o;
+        }
+    }
+    __syncthreads();  // sh.red is free
+    if (lane == 63) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j) sh.red[wave][j] = inc[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        long long before = 0;
+        for (int w = 0; w < wave; ++w) before += sh.red[w][j];
+        v[j] = before + inc[j] - v[j];
+    }
+}
+
+// Result of a selection: the key, and the weight and count of the tokens
+// above it, and its own weight.
+struct Pick {
+    unsigned long long key;
+    long long above_w, own_w;
+};
+
 // The largest key kappa whose tokens with keys >= kappa weigh at least target
 // (unit weights when COUNT): the token at which the cumulative weight, in
-// sorted order, first reaches target. Needs 1 <= target <= the total weight.
+// sorted order, first reaches target. Needs 1 <= target <= the total. Level 0
+// reads the first-level histogram built with the weights; a deeper level sums
+// its candidates (the tokens matching the digits chosen so far) per digit in
+// LDS, exact in any order, read from the candidate list when it holds them
+// all, else from the logits and weights -- the pass that finds at most kCap
+// candidates also copies them into the list.
 template <bool COUNT>
-__device__ unsigned long long select_key(const float* __restrict__ l, const long long* __restrict__ w, int n,
-                                         long long target, Shared& sh)
+__device__ Pick select_key(const float* __restrict__ l, const long long* __restrict__ w, int n, long long target,
+                           Shared& sh, unsigned long long& lmask, unsigned long long& lprefix)
 {
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int t = threadIdx.x;
     unsigned long long prefix = 0, mask = 0;
-    long long above = 0;  // weight of the keys above the candidates
-    for (int level = 7; level >= 0; --level) {
-        const int shift = 8 * level;
-        if (t < 256) sh.hist[t] = 0ull;
-        __syncthreads();
-        for (int i = t; i < n; i += kT) {
-            const unsigned long long key = sort_key(l[i], i);
-            if ((key & mask) == prefix) {
-                const long long wi = COUNT ? 1 : w[i];
-                if (wi != 0) atomicAdd(&sh.hist[(key >> shift) & 255ull], (unsigned long long)wi);
+    long long above_t = 0, above_w = 0;
+    unsigned int above_c = 0;
+    unsigned int cand = 0xFFFFFFFFu;  // candidates at this level (unknown at level 0)
+    Pick out{0ull, 0, 0};
+    for (int lv = 0; lv < kLevels; ++lv) {
+        const int width = digit_width(lv), shift = digit_shift(lv), bins = 1 << width;
+        const unsigned long long dmask = (unsigned long long)(bins - 1);
+        const unsigned long long* hw = lv == 0 ? sh.h0w : sh.hw;
+        const unsigned int* hc = lv == 0 ? sh.h0c : sh.hc;
+        if (lv > 0) {
+            for (int i = t; i < bins; i += kT) {
+                sh.hw[i] = 0ull;
+                sh.hc[i] = 0u;
             }
-        }
-        __syncthreads();
-        if (wave == 0) {
-            // lane l holds digits 255 - 4 l .. 252 - 4 l (descending)
-            long long b[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = (long long)sh.hist[255 - 4 * lane - j];
-            const long long s4 = b[0] + b[1] + b[2] + b[3];
-            long long incl = s4;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const long long v = __shfl_up(incl, off, 64);
-                if (lane >= off) incl += v;
-            }
-            long long run = above + (incl - s4);
-            int found = -1;
-            long long before = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (found < 0 && run + b[j] >= target) {
-                    found = 255 - 4 * lane - j;
-                    before = run;
+            const bool in_list = (mask & lmask) == lmask && (prefix & lmask) == lprefix;
+            const bool fill = !in_list && cand <= (unsigned int)kCap;
+            if (fill && t == 0) sh.ncand = 0u;
+            __syncthreads();
+            if (in_list) {
+                const int nc = (int)sh.ncand;
+                for (int i = t; i < nc; i += kT) {
+                    const unsigned long long key = sh.ck[i];
+                    if ((key & mask) == prefix) {
+                        const int d = (int)((key >> shift) & dmask);
+                        atomicAdd(&sh.hw[d], (unsigned long long)sh.cw[i]);
+                        atomicAdd(&sh.hc[d], 1u);
+                    }
                 }
-                run += b[j];
+            } else {
+                // batches of kB logits per thread, their loads issued together
+                for (int i0 = t; i0 < n; i0 += kB * kT) {
+                    float lv[kB];
+#pragma unroll
+                    for (int u = 0; u < kB; ++u) lv[u] = i0 + u * kT < n ? l[i0 + u * kT] : 0.0f;
+                    unsigned long long key[kB];
+                    long long wv[kB];
+#pragma unroll
+                    for (int u = 0; u < kB; ++u) {
+                        const int i = i0 + u * kT;
+                        key[u] = sort_key(lv[u], i);
+                        const bool hit = i < n && (key[u] & mask) == prefix;
+                        wv[u] = hit ? w[i] : -1;  // -1: not a candidate (weights are >= 0)
+                    }
+#pragma unroll
+                    for (int u = 0; u < kB; ++u) {
+                        if (wv[u] >= 0) {
+                            const int d = (int)((key[u] >> shift) & dmask);
+                            atomicAdd(&sh.hw[d], (unsigned long long)wv[u]);
+                            atomicAdd(&sh.hc[d], 1u);
+                            if (fill) {
+                                const unsigned int slot = atomicAdd(&sh.ncand, 1u);
+                                sh.ck[slot] = key[u];
+                                sh.cw[slot] = wv[u];
+                            }
+                        }
+                    }
+                }
+                if (fill) {
+                    lmask = mask;
+                    lprefix = prefix;
+                }
             }
-            const unsigned long long ballot = __ballot(found >= 0);
-            const int first = ballot ? __ffsll((long long)ballot) - 1 : 0;
-            if (lane == first) {
-                sh.sel_digit = found < 0 ? 0 : found;  // found exists when target is in range
-                sh.sel_above = before;
+            __syncthreads();
+        }
+        // the digit at which the running total (digits in descending order)
+        // reaches target; thread t scans bins - 1 - per t .. bins - per (t + 1)
+        const int per = bins / kT;
+        long long s[3] = {0, 0, 0};  // target units, weight, count
+        for (int j = 0; j < per; ++j) {
+            const int d = bins - 1 - per * t - j;
+            const long long bw = (long long)hw[d], bc = (long long)hc[d];
+            s[0] += COUNT ? bc : bw;
+            s[1] += bw;
+            s[2] += bc;
+        }
+        const long long mine = s[0];
+        block_excl3(s, sh);
+        if (above_t + s[0] < target && above_t + s[0] + mine >= target) {
+            long long rt = above_t + s[0], rw = above_w + s[1];
+            long long rc = (long long)above_c + s[2];
+            for (int j = 0; j < per; ++j) {
+                const int d = bins - 1 - per * t - j;
+                const long long bw = (long long)hw[d], bc = (long long)hc[d];
+                const long long bt = COUNT ? bc : bw;
+                if (rt + bt >= target) {
+                    sh.sel_digit = d;
+                    sh.sel_above_t = rt;
+                    sh.sel_above_w = rw;
+                    sh.sel_above_c = (unsigned int)rc;
+                    sh.sel_bin_w = bw;
+                    sh.sel_bin_c = (unsigned int)bc;
+                    break;
+                }
+                rt += bt;
+                rw += bw;
+                rc += bc;
             }
         }
         __syncthreads();
-        prefix |= (unsigned long long)sh.sel_digit << shift;
-        mask |= 255ull << shift;
-        above = sh.sel_above;
-        __syncthreads();  // every thread has read the selection before the next clear
+        const int d = sh.sel_digit;
+        prefix |= (unsigned long long)d << shift;
+        mask |= dmask << shift;
+        above_t = sh.sel_above_t;
+        above_w = sh.sel_above_w;
+        above_c = sh.sel_above_c;
+        cand = sh.sel_bin_c;
+        out.own_w = sh.sel_bin_w;  // at the last level: the one token with this key
+        __syncthreads();  // every thread has read the selection before it is written again
     }
-    return prefix;
+    out.key = prefix;
+    out.above_w = above_w;
+    return out;
 }
 
 template <bool TOPP>
@@ -182,38 +314,63 @@ __global__ __launch_bounds__(kT) void sample_kernel(const float* __restrict__ lo
     const float* l = logits + (size_t)row * n;
     long long* w = wbuf + (size_t)row * n;
 
+    for (int i = t; i < kBins0; i += kT) {
+        sh.h0w[i] = 0ull;
+        sh.h0c[i] = 0u;
+    }
     float lm = -INFINITY;
-    for (int i = t; i < n; i += kT) lm = fmaxf(lm, l[i]);
-    const float lmax = block_max(lm, sh);
+    for (int i0 = t; i0 < n; i0 += kB * kT) {
+        float lv[kB];
+#pragma unroll
+        for (int u = 0; u < kB; ++u) lv[u] = i0 + u * kT < n ? l[i0 + u * kT] : -INFINITY;
+#pragma unroll
+        for (int u = 0; u < kB; ++u) lm = fmaxf(lm, lv[u]);
+    }
+    const float lmax = block_max(lm, sh);  // its barrier also publishes the cleared bins
 
+    // weights, their total and the first-level histogram in one pass
     long long part = 0;
-    for (int i = t; i < n; i += kT) {
-        const double x = ((double)l[i] - (double)lmax) / (double)temp;
-        const long long q = (long long)rint(ldexp(exp_neg(x), 40));
-        w[i] = q;
-        part += q;
+    for (int i0 = t; i0 < n; i0 += kB * kT) {
+        float lv[kB];
+#pragma unroll
+        for (int u = 0; u < kB; ++u) lv[u] = i0 + u * kT < n ? l[i0 + u * kT] : 0.0f;
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            const int i = i0 + u * kT;
+            if (i < n) {
+                const double x = ((double)lv[u] - (double)lmax) / (double)temp;
+                const long long q = (long long)rint(ldexp(exp_neg(x), 40));
+                w[i] = q;
+                part += q;
+                const int d = (int)(sort_key(lv[u], i) >> 52);
+                atomicAdd(&sh.h0w[d], (unsigned long long)q);
+                atomicAdd(&sh.h0c[d], 1u);
+            }
+        }
     }
-    const long long total = block_sum_i64(part, sh);  // its barriers also publish w to the workgroup
+    const long long total = block_sum_i64(part, sh);  // its barriers also publish w and the bins
 
-    unsigned long long kappa;
+    unsigned long long lmask = ~0ull, lprefix = 0ull;  // the candidate list: empty
+    Pick kept;
     if (TOPP) {
+        // min(Z, ceil(p Z)) compared exactly: fl64(Z) may round above Z, and a
+        // target above Z would have no crossing digit
         const double tg = ceil((double)p * (double)total);
-        long long target = tg > (double)total ? total : (long long)tg;
+        long long target = tg < 9.0e18 ? (long long)tg : total;
+        if (target > total) target = total;
         if (target < 1) target = 1;
-        kappa = select_key<false>(l, w, n, target, sh);
+        kept = select_key<false>(l, w, n, target, sh, lmask, lprefix);
     } else {
-        kappa = select_key<true>(l, w, n, k < n ? k : n, sh);
+        kept = select_key<true>(l, w, n, k < n ? k : n, sh, lmask, lprefix);
     }
-    long long kept = 0;
-    for (int i = t; i < n; i += kT)
-        if (sort_key(l[i], i) >= kappa) kept += w[i];
-    const long long mass = block_sum_i64(kept, sh);
+    // the kept tokens (keys >= kappa) weigh the tokens above kappa plus kappa's own
+    const long long mass = kept.above_w + kept.own_w;
     const double rd = floor(u[row] * (double)mass);
     const long long r = rd < 0.0 ? 0 : (rd >= (double)mass ? mass - 1 : (long long)rd);
     // the kept tokens are a prefix of the sorted order, so the first token
     // whose cumulative weight reaches r + 1 (<= mass) is a kept one
-    const unsigned long long chosen = select_key<false>(l, w, n, r + 1, sh);
-    if (t == 0) out[row] = (int32_t)(0xFFFFFFFFu - (uint32_t)(chosen & 0xFFFFFFFFull));
+    const Pick chosen = select_key<false>(l, w, n, r + 1, sh, lmask, lprefix);
+    if (t == 0) out[row] = (int32_t)(0xFFFFFFFFu - (uint32_t)(chosen.key & 0xFFFFFFFFull));
 }
 
 }  // namespace

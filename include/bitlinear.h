@@ -469,7 +469,8 @@ int bitnet_greedy_step(const uint8_t *embed_table, float s_emb, int64_t vocab,
  *     chosen token is the first kept token whose cumulative weight exceeds r.
  * Each row is one 1024-thread workgroup: weights, then radix selections over
  * 64-bit (logit, index) keys whose per-digit weight sums are exact integers.
- *   logits    : device fp32 [m][n] (finite).
+ *   logits    : device fp32 [m][n] (finite), 1 <= n < 2^23 (so the total
+ *               weight, at most n 2^40, fits in an int64).
  *   temperature : > 0 and finite.  k >= 1 (k > n keeps all); p > 0 (p >= 1 keeps
  *               every token of nonzero weight).
  *   token     : device int32 [m].

@@ -378,6 +378,7 @@ def test_sample_checks():
         assert call(tok=None) == bl.BL_ERR_NULL
         assert call(m=0) == bl.BL_ERR_SHAPE
         assert call(n=0) == bl.BL_ERR_SHAPE
+        assert call(n=1 << 23, wsb=1 << 40) == bl.BL_ERR_SHAPE  # the total weight would not fit an int64
         assert call(u=A + 4) == bl.BL_ERR_ALIGN
         assert call(ws=A + 8) == bl.BL_ERR_ALIGN
         assert call(t=0.0) == bl.BL_ERR_VALUE
