@@ -195,16 +195,21 @@ def probe_peaks(bl, torch, dev0):
         best = max(best, nb / (t.ms * 1e-3) / 1e9)
     del buf
     iters = 20000
-    bl.bitlinear_probe_mfma_i8(100, sink)
-    best_ops = 0.0
-    for _ in range(3):
-        with Timer() as t:
-            ops = bl.bitlinear_probe_mfma_i8(iters, sink)
-        best_ops = max(best_ops, ops / (t.ms * 1e-3) / 1e12)
+    tops = {}
+    for name, fn in (("int8_mfma_tops", bl.bitlinear_probe_mfma_i8),
+                     ("int8_mfma_tops_dense", bl.bitlinear_probe_mfma_i8_dense)):
+        fn(100, sink)
+        best_ops = 0.0
+        for _ in range(3):
+            with Timer() as t:
+                ops = fn(iters, sink)
+            best_ops = max(best_ops, ops / (t.ms * 1e-3) / 1e12)
+        tops[name] = round(best_ops, 1)
     torch.cuda.synchronize()
-    return {"hbm_read_gbs": round(best, 1), "int8_mfma_tops": round(best_ops, 1),
+    return {"hbm_read_gbs": round(best, 1), **tops,
             "how": "bitlinear_probe_read over 4 GiB (best of 5); bitlinear_probe_mfma_i8, 2 waves per SIMD x "
-                   "8 independent v_mfma_i32_16x16x64_i8 chains (best of 3)"}
+                   "8 independent v_mfma_i32_16x16x64_i8 chains on one pair of small operands (best of 3); "
+                   "bitlinear_probe_mfma_i8_dense, the same with each chain on its own random operand bytes"}
 
 
 def main():
@@ -303,7 +308,8 @@ def main():
              else "bitnet_decode_stream launches of one token")
     achieved = weight_bytes / (ev_ms_per_step * 1e-3) / 1e9
     peaks = probe_peaks(bl, torch, dev0)
-    log(f"probes: HBM read {peaks['hbm_read_gbs']} GB/s, int8 MFMA {peaks['int8_mfma_tops']} TOP/s")
+    log(f"probes: HBM read {peaks['hbm_read_gbs']} GB/s, int8 MFMA {peaks['int8_mfma_tops']} TOP/s "
+        f"({peaks['int8_mfma_tops_dense']} on random operands)")
     result["roofline"] = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                           "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                           "traffic": traffic_bytes("stream_3b"),
@@ -339,7 +345,7 @@ def main():
     del host_layers
 
     if not args.no_extra:
-        result.update(extra_measurements(bl, torch, T, dev0, check=not args.no_cpu))
+        result.update(extra_measurements(bl, torch, T, dev0, check=not args.no_cpu, peaks=peaks))
     if not args.no_cpu:
         result["cpu_single_core"] = single_core_oracle()
     print(json.dumps(result), flush=True)
@@ -631,7 +637,7 @@ def graph_ms(torch, calls, outputs):
     return t.ms, same
 
 
-def extra_measurements(bl, torch, T, dev0, check=True):
+def extra_measurements(bl, torch, T, dev0, check=True, peaks=None):
     out = {}
     # ---- single BitLinear decode GEMV 2560 -> 2560 (quant + GEMV), weights rotated
     # over > 512 MiB of copies so that they stream from HBM, not the 256 MB MALL ----
@@ -776,6 +782,11 @@ def extra_measurements(bl, torch, T, dev0, check=True):
                                    "achieved": round(tops, 1), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
                                    "frac": round(tops / INT8_PEAK_TOPS, 4), "algorithmic_ops": int(ops),
                                    "traffic": None}}
+    if peaks:
+        # the measured ceiling with operands like a GEMM's (random bytes, changing every MFMA)
+        dense = peaks["int8_mfma_tops_dense"]
+        out["prefill"]["roofline"]["probe_peak_dense"] = dense
+        out["prefill"]["roofline"]["frac_of_probe_dense"] = round(tops / dense, 4)
     log(f"prefill: GEMM {gemm_ms:.4f} ms = {out['prefill']['gemm_tops']} TOPS")
     out["prefill"]["vendor_int8_gemm"] = vendor_int8_gemm(torch, dev0, q, t_rows=N)
     log(f"prefill: vendor int8 GEMM on the same shape: {out['prefill']['vendor_int8_gemm']}")

@@ -35,7 +35,7 @@ EXPORTS = (
     "bitlinear_quant_act", "bitlinear_gemv", "bitlinear_forward", "bitlinear_gemm_workspace_bytes", "bitlinear_gemm",
     "bitnet_ffn_workspace_bytes", "bitnet_ffn_workspace_offset", "bitnet_ffn", "bitnet_layer_bytes",
     "bitnet_stream_workspace_bytes", "bitnet_decode_stream",
-    "bitlinear_probe_read", "bitlinear_probe_mfma_ops", "bitlinear_probe_mfma_i8",
+    "bitlinear_probe_read", "bitlinear_probe_mfma_ops", "bitlinear_probe_mfma_i8", "bitlinear_probe_mfma_i8_dense",
     "bitlinear_gemm_noalloc", "bitlinear_gemm_noalloc_max_scratch_bytes",
     "bitnet_embed", "bitnet_greedy_head_workspace_bytes", "bitnet_greedy_head", "bitnet_greedy_step_workspace_bytes",
     "bitnet_greedy_step", "bitnet_sample_workspace_bytes", "bitnet_sample_topk", "bitnet_sample_topp",
@@ -105,6 +105,7 @@ _SIGS = {
     "bitlinear_probe_read": ([_P, _SZ, _P, _P], _I),
     "bitlinear_probe_mfma_ops": ([_I64], _I64),
     "bitlinear_probe_mfma_i8": ([_I64, _P, _P], _I),
+    "bitlinear_probe_mfma_i8_dense": ([_I64, _P, _P], _I),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -407,4 +408,11 @@ def bitlinear_probe_mfma_i8(iters, sink, stream=None):
     """int8 MFMA-only probe; returns the int8 operations of the call."""
     _check(_lib.bitlinear_probe_mfma_i8(int(iters), _dev(sink, torch.int32, "sink"), _stream(stream)),
            "bitlinear_probe_mfma_i8")
+    return _lib.bitlinear_probe_mfma_ops(int(iters))
+
+
+def bitlinear_probe_mfma_i8_dense(iters, sink, stream=None):
+    """int8 MFMA-only probe on random-looking, changing operands; returns the int8 operations of the call."""
+    _check(_lib.bitlinear_probe_mfma_i8_dense(int(iters), _dev(sink, torch.int32, "sink"), _stream(stream)),
+           "bitlinear_probe_mfma_i8_dense")
     return _lib.bitlinear_probe_mfma_ops(int(iters))

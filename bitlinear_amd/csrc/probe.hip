@@ -56,26 +56,53 @@ constexpr int kMfmaChains = 8;
 // One MFMA accumulating in place: the compiler's own form of a loop-carried
 // accumulator is moved between registers every iteration, which the probe
 // would then measure instead of the matrix cores.
-#define BL_MFMA_INPLACE(c) asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b))
+#define BL_MFMA_INPLACE(c, a, b) asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b))
 
+// A 32-bit mix of x (the murmur3 finaliser), for operand bytes that look random.
+__device__ __forceinline__ int mix32(uint32_t x)
+{
+    x ^= x >> 16;
+    x *= 0x85ebca6bu;
+    x ^= x >> 13;
+    x *= 0xc2b2ae35u;
+    x ^= x >> 16;
+    return (int)x;
+}
+
+// DENSE = false: one operand pair of small values (mostly zero bytes) for every
+// MFMA. DENSE = true: each chain its own pair of random-looking bytes, so
+// consecutive MFMAs see different operands with every bit toggling, as in a
+// GEMM on real data; the matrix cores then draw more power and the clock can
+// drop, which this form measures.
+template <bool DENSE>
 __global__ __launch_bounds__(kMfmaThreads) void mfma_probe_kernel(int64_t iters, uint32_t* sink)
 {
     const int lane = threadIdx.x & 63;
-    const v4i a = {lane, lane * 3, lane * 5, lane * 7};
-    const v4i b = {lane ^ 1, lane ^ 2, lane ^ 3, lane ^ 4};
+    v4i a[8], b[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if (DENSE) {
+            const uint32_t s = (uint32_t)(blockIdx.x * 4096 + threadIdx.x * 16 + j * 2);
+            a[j] = v4i{mix32(8 * s), mix32(8 * s + 1), mix32(8 * s + 2), mix32(8 * s + 3)};
+            b[j] = v4i{mix32(8 * s + 4), mix32(8 * s + 5), mix32(8 * s + 6), mix32(8 * s + 7)};
+        } else {
+            a[j] = v4i{lane, lane * 3, lane * 5, lane * 7};
+            b[j] = v4i{lane ^ 1, lane ^ 2, lane ^ 3, lane ^ 4};
+        }
+    }
     // eight independent chains: each MFMA reads an accumulator written eight
     // instructions earlier
     v4i c0 = {0, 0, 0, 0}, c1 = {1, 0, 0, 0}, c2 = {2, 0, 0, 0}, c3 = {3, 0, 0, 0};
     v4i c4 = {4, 0, 0, 0}, c5 = {5, 0, 0, 0}, c6 = {6, 0, 0, 0}, c7 = {7, 0, 0, 0};
     for (int64_t it = 0; it < iters; ++it) {
-        BL_MFMA_INPLACE(c0);
-        BL_MFMA_INPLACE(c1);
-        BL_MFMA_INPLACE(c2);
-        BL_MFMA_INPLACE(c3);
-        BL_MFMA_INPLACE(c4);
-        BL_MFMA_INPLACE(c5);
-        BL_MFMA_INPLACE(c6);
-        BL_MFMA_INPLACE(c7);
+        BL_MFMA_INPLACE(c0, a[0], b[0]);
+        BL_MFMA_INPLACE(c1, a[1], b[1]);
+        BL_MFMA_INPLACE(c2, a[2], b[2]);
+        BL_MFMA_INPLACE(c3, a[3], b[3]);
+        BL_MFMA_INPLACE(c4, a[4], b[4]);
+        BL_MFMA_INPLACE(c5, a[5], b[5]);
+        BL_MFMA_INPLACE(c6, a[6], b[6]);
+        BL_MFMA_INPLACE(c7, a[7], b[7]);
     }
     const v4i r = c0 ^ c1 ^ c2 ^ c3 ^ c4 ^ c5 ^ c6 ^ c7;
     const uint32_t acc = (uint32_t)(r[0] ^ r[1] ^ r[2] ^ r[3]);
@@ -121,7 +148,8 @@ int64_t bitlinear_probe_mfma_ops(int64_t iters)
     return (int64_t)cus * 8 * iters * bl::kMfmaChains * 32768;
 }
 
-int bitlinear_probe_mfma_i8(int64_t iters, uint32_t* sink, void* stream)
+namespace {
+int probe_mfma(bool dense, int64_t iters, uint32_t* sink, void* stream)
 {
     if (!sink) return BL_ERR_NULL;
     if (iters <= 0 || iters > ((int64_t)1 << 40)) return BL_ERR_SHAPE;
@@ -129,8 +157,23 @@ int bitlinear_probe_mfma_i8(int64_t iters, uint32_t* sink, void* stream)
     const int cus = bl::cu_count();
     if (cus <= 0) return BL_ERR_DEVICE;
     // two waves per SIMD: 8 waves per CU, as 2 workgroups of 4 waves
-    bl::mfma_probe_kernel<<<cus * 2, bl::kMfmaThreads, 0, reinterpret_cast<hipStream_t>(stream)>>>(iters, sink);
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (dense)
+        bl::mfma_probe_kernel<true><<<cus * 2, bl::kMfmaThreads, 0, s>>>(iters, sink);
+    else
+        bl::mfma_probe_kernel<false><<<cus * 2, bl::kMfmaThreads, 0, s>>>(iters, sink);
     return hipGetLastError() == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
+}
+}  // namespace
+
+int bitlinear_probe_mfma_i8(int64_t iters, uint32_t* sink, void* stream)
+{
+    return probe_mfma(false, iters, sink, stream);
+}
+
+int bitlinear_probe_mfma_i8_dense(int64_t iters, uint32_t* sink, void* stream)
+{
+    return probe_mfma(true, iters, sink, stream);
 }
 
 }  // extern "C"

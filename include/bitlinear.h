@@ -496,11 +496,17 @@ int bitlinear_probe_read(const void *buf, size_t bytes, uint32_t *sink, void *st
 /* bitlinear_probe_mfma_i8: every wave (two per SIMD on every CU) issues
  * iters x 8 independent v_mfma_i32_16x16x64_i8 on register operands and
  * nothing else; *sink (device uint32) is touched only to keep the results
- * alive. bitlinear_probe_mfma_ops(iters) is the number of int8 operations
- * (2 per multiply-add) one call performs on the current device (0 on error).
+ * alive. The operands are one pair of small values (mostly zero bytes).
+ * bitlinear_probe_mfma_i8_dense: the same with each of the 8 chains on its
+ * own pair of random-looking operand bytes, so consecutive MFMAs see
+ * different, fully toggling operands as a GEMM on real data does (the matrix
+ * cores draw more power, and the clock may drop).
+ * bitlinear_probe_mfma_ops(iters) is the number of int8 operations (2 per
+ * multiply-add) one call of either performs on the current device (0 on error).
  * Errors: NULL, SHAPE (iters <= 0 or > 2^40), ALIGN, DEVICE, LAUNCH. */
 int64_t bitlinear_probe_mfma_ops(int64_t iters);
 int bitlinear_probe_mfma_i8(int64_t iters, uint32_t *sink, void *stream);
+int bitlinear_probe_mfma_i8_dense(int64_t iters, uint32_t *sink, void *stream);
 
 #ifdef __cplusplus
 }
