@@ -123,6 +123,13 @@ def test_decode_step_persistent_long_context(bl, olib):
     _run_steps(bl, olib, 2, 1, 256, 1024, 2, 1024, [700, 701, 702, 1023, 0], seed=11, prefill=700)
 
 
+def test_decode_step_one_sequence_long_cache_launch_path(bl, olib):
+    """One sequence with a cache of 8448 positions, beyond the persistent
+    kernel's 8192: the launch-per-step path at m = 1, positions 8200 and 8447
+    (33 chunks of 256) over a prefilled cache."""
+    _run_steps(bl, olib, 1, 1, 256, 1024, 2, 8448, [8200, 8447], seed=14, prefill=8200)
+
+
 def test_decode_step_persistent_heads_of_4(bl, olib):
     """One sequence with 64 heads of 4 values (the smallest head), positions 0 .. 2."""
     _run_steps(bl, olib, 2, 1, 256, 1024, 64, 64, [0, 1, 2], seed=12)

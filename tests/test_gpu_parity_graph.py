@@ -144,8 +144,9 @@ def test_graph_layer_stream_and_head(bl, olib, m):
 
 def test_graph_one_token_stream(bl, olib):
     """One token of a shape with a persistent kernel: the eager call runs the
-    persistent kernel, the captured one the launch-per-step path (a cooperative
-    launch is not recorded); the replays must equal the eager result bit for bit."""
+    persistent kernel, the captured one the launch-per-step path (the library
+    does not record the persistent launch, whose waits span the whole grid);
+    the replays must equal the eager result bit for bit."""
     import torch
     dev = torch.device("cuda", 0)
     n_layers, d, f, m = 2, 256, 1024, 1
@@ -161,3 +162,38 @@ def test_graph_one_token_stream(bl, olib):
                                 ws)
 
     _replay_check(torch, calls, [x, qkv], lambda: x.copy_(x0))
+
+
+def test_graph_decode_step_two_sequences(bl, olib):
+    """The decode step with attention for two sequences (launch per step both
+    eagerly and captured): RoPE, the cache append at pos, attention over the
+    prefilled caches, o and the FFN; every replay equals the eager call."""
+    import torch
+    dev = torch.device("cuda", 0)
+    n_layers, d, f, m, heads, max_seq, pos = 2, 256, 1024, 2, 4, 64, 9
+    hd = d // heads
+    log("graph decode step, two sequences")
+    layers, dw = make_layers(W.W_STREAM, n_layers, d, f, m, olib)
+    g = W.rng(160, 0, 0)
+    x0 = to_dev(W.activations(g, m, d))
+    x = x0.clone()
+    kc = to_dev(g.standard_normal((n_layers, m, heads, max_seq, hd)).astype(np.float32))
+    vc = to_dev(g.standard_normal((n_layers, m, heads, max_seq, hd)).astype(np.float32))
+    c, s_ = bl.bitnet_rope_table(10000.0, hd, max_seq)
+    cd, sd = to_dev(c), to_dev(s_)
+    qkv = torch.empty((n_layers, m, 3 * d), dtype=torch.float32, device=dev)
+    attn = torch.empty((n_layers, m, d), dtype=torch.float32, device=dev)
+    ws = torch.zeros(bl.bitnet_decode_step_workspace_bytes(m, d, f, heads, max_seq), dtype=torch.uint8, device=dev)
+
+    def calls():
+        bl.bitnet_decode_step(dw["weights"], dw["scales"], dw["gains"], n_layers, m, d, f, heads, 1e-5, cd, sd, pos,
+                              kc, vc, x, qkv, attn, ws)
+
+    kc0, vc0 = kc.clone(), vc.clone()
+
+    def reset():  # the caches back to their state before the step
+        x.copy_(x0)
+        kc.copy_(kc0)
+        vc.copy_(vc0)
+
+    _replay_check(torch, calls, [x, qkv, attn, kc, vc], reset)
