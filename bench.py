@@ -384,7 +384,8 @@ def attention_leg(bl, torch, dev0, dev, L, d, f):
             raise RuntimeError(f"decode step status word {status}: the persistent kernel gave up; timing is void")
         nbytes = L * bl.bitnet_layer_bytes(d, f) + 2 * L * d * 4 * (pos + 1)
         res[f"pos_{pos}"] = {"ms_per_token": round(ms, 4), "bytes_per_token": nbytes,
-                             "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+                             "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                             "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     del kc, vc
     log(f"decode with attention: {res}")
     return res
@@ -696,6 +697,29 @@ def extra_measurements(bl, torch, T, dev0, check=True, peaks=None):
                    "us_per_call_quant_then_gemv": round(ms2 * 1e3, 3),
                    "us_per_call_quant_then_gemv_graph": round(gms2 * 1e3, 3)}
     del pw
+    # For context: the same GEMV kernel streaming a long matrix (2560 -> 163840,
+    # 104,857,600 packed bytes) in one launch, where the launch and first-load
+    # latency that bound the 1.6 MB call are amortised.
+    nl = 64 * d
+    gl = torch.Generator(device=dev0)
+    gl.manual_seed(11)
+    valid = torch.tensor([sum(((v // 3 ** j) % 3) << (2 * j) for j in range(4)) for v in range(81)],
+                         dtype=torch.uint8, device=dev0)
+    pl = valid[torch.randint(0, 81, (nl * d // 4,), generator=gl, device=dev0)]
+    yl = torch.empty((1, nl), dtype=torch.float32, device=dev0)
+    bl.bitlinear_quant_act(x1, None, 1e-5, q1, s1, qs1)
+    for _ in range(3):
+        bl.bitlinear_gemv(pl, sw, nl, d, q1, s1, qs1, 1, None, yl)
+    with Timer() as tl:
+        for _ in range(10):
+            bl.bitlinear_gemv(pl, sw, nl, d, q1, s1, qs1, 1, None, yl)
+    lms = tl.ms / 10
+    out["gemv"]["long_matrix"] = {"shape": f"1 token, K={d} -> N={nl}", "packed_bytes": nl * d // 4,
+                                  "us_per_call": round(lms * 1e3, 2),
+                                  "weight_gbs": round(nl * d / 4 / (lms * 1e-3) / 1e9, 1),
+                                  "frac_hbm": round(nl * d / 4 / (lms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    log(f"gemv over a long matrix: {out['gemv']['long_matrix']}")
+    del pl, yl
     # ---- BitNet-3B FFN at one token, weights rotated over 27 copies (531 MB) ----
     f = 10240
     gg = [W.rng(W.W_FFN, 0, tid) for tid in (W.T_GATE, W.T_UP, W.T_DOWN)]
