@@ -636,7 +636,9 @@ size_t bitnet_decode_step_workspace_bytes(int64_t m, int64_t d, int64_t f, int64
     at += align_up((size_t)(m * d) * 4, 256);  // rotated q
     at += align_up((size_t)(m * d) * 4, 256);  // attention output scratch
     // chunk partials: fp32 for the launch path, epoch-tagged 8-byte words for the persistent one
-    at += align_up((size_t)m * (size_t)n_heads * (size_t)bl::attn_chunks((int)max_seq) * (hd + 2) * 8, 256);
+    // (which cuts short contexts into up to 32 chunks)
+    const size_t chunks = std::max<size_t>((size_t)bl::attn_chunks((int)max_seq), (size_t)bl::kStreamAttnMaxChunks);
+    at += align_up((size_t)m * (size_t)n_heads * chunks * (hd + 2) * 8, 256);
     return at;
 }
 

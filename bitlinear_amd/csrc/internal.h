@@ -79,12 +79,13 @@ int launch_gemm(const uint8_t* packed, float w_scale, const float* w_scale_ptr, 
 // words and ctrl two 32-bit words, all zero before the first call. With attn
 // the stand-in z is unused and every layer runs single-token attention with
 // RoPE and the caches of one sequence ([n_layers][heads][max_seq][hd]).
+constexpr int kStreamAttnMaxChunks = 32;  // chunk partials per head the persistent attention keeps
 struct StreamAttn {
     int heads, max_seq, pos;
     const float *rope_cos, *rope_sin;  // full tables [max_seq][hd / 2]
     float *k_cache, *v_cache;
     float* attn;  // [n_layers][d] or null
-    void* part;   // 8-byte words [heads][ceil(max_seq / 256)][hd + 2]
+    void* part;   // 8-byte words [heads][kStreamAttnMaxChunks][hd + 2]
 };
 bool stream_persistent_fits(int m, int d, int f, const StreamAttn* attn);
 size_t stream_ll_words(int d, int f);

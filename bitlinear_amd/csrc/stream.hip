@@ -414,8 +414,8 @@ __device__ __forceinline__ void dots(const uint4* wr, const uint8_t* q, const ui
 // ---- single-token attention inside the stream --------------------------------
 // Phase PA of the kernels with ATTN ("Transformer Block", "Forward Pass with
 // KV Cache"; "BitNet Model - Complete Inference Pipeline", "KV Cache State").
-// Positions 0 .. pos of a head split into chunks of 256; G = 256 / heads
-// workgroups serve each head, workgroup (h, split) taking the chunks
+// Positions 0 .. pos of a head split into chunks (attn_chunk_len); G = 256 /
+// heads workgroups serve each head, workgroup (h, split) taking the chunks
 // c = split, split + G, ... Each waits for the 3 hd published words of q, k
 // and v of its head, turns q and k by RoPE (the one holding position pos also
 // appends k and v to the caches), and per chunk forms the scores
@@ -426,8 +426,23 @@ __device__ __forceinline__ void dots(const uint4* wr, const uint8_t* q, const ui
 // merge kernel does, and publishes the head's output for P2. Scores,
 // exponentials and sums are fp32.
 constexpr int kAttnChunk = 256;
-constexpr int kMaxAttnChunks = 32;  // max_seq <= 8192
+constexpr int kMaxAttnChunks = kStreamAttnMaxChunks;  // 32: max_seq <= 8192
 constexpr int kMaxHd = 256;
+
+// Positions per chunk for position pos and G workgroups per head: 256, unless
+// there are at least two such chunks but fewer than the head's workgroups;
+// then the positions are cut into up to min(G, 32) chunks of a multiple of 8,
+// so that every workgroup pulls a share of the cache rows (one CU alone
+// streams them at a few tens of GB/s). A single chunk is not cut: the merge
+// of several would add a hand-over that costs more than the split saves.
+__device__ __forceinline__ int attn_chunk_len(int pos, int G)
+{
+    const int gm = min(G, kMaxAttnChunks);
+    const int n256 = (pos + kAttnChunk) / kAttnChunk;
+    if (n256 < 2 || n256 >= gm) return kAttnChunk;
+    const int len = (((pos + gm) / gm) + 7) & ~7;  // ceil((pos + 1) / gm), up to a multiple of 8
+    return max(len, 16);
+}
 
 struct AttnShared {
     __attribute__((aligned(16))) float q[kMaxHd];  // rotated q, rotated k and v of position pos
@@ -483,7 +498,8 @@ __device__ bool attention_split(const StreamArgs& a, int l, int h, int split, in
 {
     const int t = threadIdx.x;
     const int hd = a.hd, half = hd / 2, pos = a.pos;
-    const int nch = (pos + kAttnChunk) / kAttnChunk;
+    const int len = attn_chunk_len(pos, G);
+    const int nch = (pos + len) / len;
     const int last = (nch - 1) % G;  // the split that holds position pos
     const float* kbase = a.k_cache + ((size_t)l * a.heads + h) * a.max_seq * hd;
     const float* vbase = a.v_cache + ((size_t)l * a.heads + h) * a.max_seq * hd;
@@ -553,7 +569,7 @@ __device__ bool attention_split(const StreamArgs& a, int l, int h, int split, in
     const float scale = 1.0f / sqrtf((float)hd);
     const int groups = kT / hd, g = t / hd, gi = t - g * hd;
     for (int c = split; c < nch; c += G) {
-        const int j0 = c * kAttnChunk, cnt = min(kAttnChunk, pos + 1 - j0);
+        const int j0 = c * len, cnt = min(len, pos + 1 - j0);
         float sc = -INFINITY;
         if (t < cnt) {
             float dot = 0.0f;
@@ -811,7 +827,7 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
         }
         // ---- PA: attention, G = 256 / heads workgroups per head ----
         if constexpr (ATTN) {
-            const int G = kGrid / a.heads, nch = (a.pos + kAttnChunk) / kAttnChunk;
+            const int G = kGrid / a.heads, len = attn_chunk_len(a.pos, G), nch = (a.pos + len) / len;
             if (w < a.heads * G && w % G < nch &&
                 !attention_split<D>(a, l, w / G, w % G, G, E + 2, qq_cur, ao_cur, ao_old, ash))
                 return;
@@ -990,7 +1006,7 @@ int launch_stream_persistent(const uint8_t* weights, const float* scales, const 
         a.max_seq = attn->max_seq;
         a.pos = attn->pos;
         a.apart = static_cast<unsigned long long*>(attn->part);
-        a.chunks_max = (attn->max_seq + kAttnChunk - 1) / kAttnChunk;
+        a.chunks_max = kMaxAttnChunks;
     }
     // A plain launch: with at least kGrid CUs that each fit one workgroup, all
     // kGrid workgroups are resident together on a device that runs nothing

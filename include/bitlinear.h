@@ -349,9 +349,12 @@ int bitnet_decode_stream(const uint8_t *weights, const float *scales, const floa
  * At m == 1, for the persistent kernel's shapes and device (as in
  * bitnet_decode_stream) with n_heads <= 256 and max_seq <= 8192, the whole
  * step is one persistent launch: q, k and v are published like the stream's
- * other vectors, workgroup h < n_heads computes head h (RoPE, cache append,
- * attention over positions 0 .. pos in chunks of 256 merged by rescaling),
- * and the o projection waits for the published attention output. Its timeout
+ * other vectors, 256 / n_heads workgroups per head split its positions
+ * 0 .. pos into chunks (256 positions, or, while that leaves workgroups of
+ * the head idle, up to 32 shorter chunks of at least 16), and the head's first
+ * workgroup merges the chunks by rescaling (RoPE and the cache append are done
+ * by the workgroup holding pos); the o projection waits for the published
+ * attention output. Its timeout
  * and status rules are those of bitnet_decode_stream. Otherwise (and while the
  * stream is being captured into a graph) it runs one launch per step: RoPE and
  * append, one workgroup per (sequence, head, 256 positions), a merge launch.

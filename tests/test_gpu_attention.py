@@ -13,7 +13,8 @@ positions 0 .. pos (u = 2^-24): each fp32 score is within
 e_s = (hd + 4) u max_j sum_i |q_i k_ji| / sqrt(hd) of the exact one; each
 weight e^(s_j - max) is then within a relative 2 e_s + 4 u (expf adds a few
 ulps); the chunked sums add (pos + 1 + 4 * chunks) u relative to
-sum_j e_j |v_j|. With V = max |v| over the head's positions the output is off
+sum_j e_j |v_j|, chunks being the number of chunks merged (256 positions
+each, or up to min(256 / heads, 32) shorter ones in the persistent kernel). With V = max |v| over the head's positions the output is off
 by at most V (2 (2 e_s + 4 u) + (pos + 5 + 4 chunks) u); the test allows
 twice that."""
 import numpy as np
@@ -36,7 +37,10 @@ def _attn_bound(q_rot, kc, vc, pos, hd):
     """Per-element bound [m][H][hd] from the oracle's q_rot [m][H][hd] and caches."""
     u = 2.0 ** -24
     m, heads = q_rot.shape[:2]
-    chunks = (pos + 1 + 255) // 256
+    # chunks merged: 256-position chunks, or (the persistent kernel, when a head
+    # has fewer of those than workgroups) up to min(256 / heads, 32) shorter ones
+    n256 = (pos + 1 + 255) // 256
+    chunks = max(n256, min(256 // heads, 32)) if n256 >= 2 else 1
     bound = np.empty((m, heads, hd))
     for r in range(m):
         for h in range(heads):
