@@ -424,6 +424,29 @@ def test_decode_stream(bl, olib, n_layers, m, d, f):
     assert_f32(x, ox, "x after the stream")
 
 
+def test_decode_stream_absmax_not_at_largest_product(bl, olib):
+    """Layer 0's input and attention gains from tests/crafted.py: the element
+    with the largest exact |x g| is not the one with the largest rounded |y|.
+    The persistent kernel first takes the absmax from the largest product and
+    must notice the larger |y| and quantize again; q/k/v and x must match the
+    oracle bit for bit."""
+    from crafted import absmax_flip
+    from gpu_helpers import make_layers, run_stream, stream_ctrl
+    n_layers, d, f = 2, 256, 1024
+    log("stream with the absmax away from the largest product")
+    layers, dev = make_layers(W.W_STREAM, n_layers, d, f, 1, olib)
+    x, g = absmax_flip(d)
+    layers[0]["g_attn"] = g
+    dev["gains"][0, :d] = to_dev(g)
+    x0 = x[None, :]
+    gx, gqkv, ws = run_stream(dev, n_layers, 1, d, f, 1e-5, x0)
+    assert stream_ctrl(ws)[1] == 0, "stream status word"
+    ox, oqkv = oracle.chain(x0, layers, 1e-5, olib)
+    for l in range(n_layers):
+        assert_f32(gqkv[l], oqkv[l], f"qkv layer {l}")
+    assert_f32(gx, ox, "x after the stream")
+
+
 @pytest.mark.parametrize("d,f", [(256, 1024), (2560, 10240)])
 def test_decode_stream_all_zero_vectors(bl, olib, d, f):
     """x = 0 and z = 0: every vector the persistent kernel hands over (x, x
