@@ -79,6 +79,10 @@ struct Mfma<16> {
 // The four waves split the columns (128 x 80 each, 8 x 5 tiles of 16x16x64),
 // so every packed weight column is unpacked by one wave only.
 using CfgLarge = Cfg<128, 320, 1, 4, 64, 16>;
+// Large M with few columns (fewer than two 128 x 320 tiles per CU, e.g. the FFN's
+// down projection 2048 x 10240 -> 2560: 128 tiles): 128 x 160 tiles, 2 x 2
+// waves of 64 x 80, twice the tiles (measured 90 against 125 us there).
+using CfgMid = Cfg<128, 160, 2, 2, 64, 16>;
 // Small M (up to 64 tokens; fewer run the skinny kernels): 32 x 256 tiles.
 using CfgSmall = Cfg<32, 256, 1, 4, 64, 32>;
 
@@ -363,6 +367,11 @@ int launch_gemm(const uint8_t* packed, float w_scale, const float* w_scale_ptr, 
     if (m <= 2 * CfgSmall::BM) {
         dim3 grid((n + CfgSmall::BN - 1) / CfgSmall::BN, (m + CfgSmall::BM - 1) / CfgSmall::BM);
         gemm_kernel<CfgSmall, false><<<grid, CfgSmall::kThreads, 0, s>>>(
+            packed, w_scale, w_scale_ptr, n, k, q, act_scale, act_sum, m, residual, y, ldy, acc_out, keys, nullptr,
+            0.0f, nullptr);
+    } else if ((int64_t)cdiv(n, CfgLarge::BN) * cdiv(m, CfgLarge::BM) < 2 * 256) {
+        dim3 grid((n + CfgMid::BN - 1) / CfgMid::BN, (m + CfgMid::BM - 1) / CfgMid::BM);
+        gemm_kernel<CfgMid, false><<<grid, CfgMid::kThreads, 0, s>>>(
             packed, w_scale, w_scale_ptr, n, k, q, act_scale, act_sum, m, residual, y, ldy, acc_out, keys, nullptr,
             0.0f, nullptr);
     } else {
