@@ -419,29 +419,45 @@ __device__ __forceinline__ void dots(const uint4* wr, const uint8_t* q, const ui
 // c = split, split + G, ... Each waits for the 3 hd published words of q, k
 // and v of its head, turns q and k by RoPE (the one holding position pos also
 // appends k and v to the caches), and per chunk forms the scores
-// q . k_j / sqrt(hd) (one thread per position), the chunk's maximum and sum of
-// e^(s - max), and the weighted sums of v (512 / hd groups of hd threads, each
-// group over every (512 / hd)-th position, then the groups in order). Split 0
-// merges the chunks by rescaling with e^(max_c - max), as the launch path's
-// merge kernel does, and publishes the head's output for P2. Scores,
-// exponentials and sums are fp32.
+// q . k_j / sqrt(hd), the chunk's maximum and sum of e^(s - max), and the
+// weighted sums of v (512 / (hd / 4) groups of hd / 4 threads, a thread
+// holding four columns, each group over every (512 / (hd / 4))-th position,
+// then the groups in order). A score is the sum, in
+// order, of the dot products of q and k_j over the hd / 4 runs of four
+// values. Split 0 merges the chunks by rescaling with e^(max_c - max), as the
+// launch path's merge kernel does, and publishes the head's output for P2.
+// Scores, exponentials and sums are fp32.
+//
+// One CU pulls cache rows from HBM at only a few tens of GB/s, so the rows of
+// a head are spread over all of its workgroups (attn_chunk_len), and each
+// workgroup issues a chunk's K and V loads together, right after the wait for
+// q, k and v, as float4s: K in row-major order (thread t takes t, t + 512,
+// ...), V in the layout of the weighted sums (indices past the chunk's rows
+// are clamped to its last row, so that every load is unconditional). The
+// barriers between the loads and their use wait for LDS only (__syncthreads
+// would also wait for the loads in flight).
 constexpr int kAttnChunk = 256;
+constexpr int kAttnMinChunk = 16;
+constexpr int kAttnCutFrom = 224;  // positions 0 .. pos with pos below this are one chunk
 constexpr int kMaxAttnChunks = kStreamAttnMaxChunks;  // 32: max_seq <= 8192
 constexpr int kMaxHd = 256;
+constexpr int kAttnKB = 8;   // K float4s per thread and round: 204 positions of hd = 80
+constexpr int kAttnVB = 7;   // V float4s per thread and round: 175 positions of hd = 80
+// (larger rounds spill registers)
 
-// Positions per chunk for position pos and G workgroups per head: 256, unless
-// there are at least two such chunks but fewer than the head's workgroups;
-// then the positions are cut into up to min(G, 32) chunks of a multiple of 8,
-// so that every workgroup pulls a share of the cache rows (one CU alone
-// streams them at a few tens of GB/s). A single chunk is not cut: the merge
-// of several would add a hand-over that costs more than the split saves.
+// Positions per chunk for position pos and G workgroups per head: 256 once a
+// head has at least min(G, 32) such chunks; below that the positions are cut
+// into up to min(G, 32) chunks of a multiple of 8, at least 16, so that every
+// workgroup of the head pulls a share of the cache rows -- except up to 224
+// positions, which stay one chunk: there the merge's hand-over costs more
+// than the split saves.
 __device__ __forceinline__ int attn_chunk_len(int pos, int G)
 {
     const int gm = min(G, kMaxAttnChunks);
     const int n256 = (pos + kAttnChunk) / kAttnChunk;
-    if (n256 < 2 || n256 >= gm) return kAttnChunk;
+    if (n256 >= gm || pos < kAttnCutFrom) return kAttnChunk;
     const int len = (((pos + gm) / gm) + 7) & ~7;  // ceil((pos + 1) / gm), up to a multiple of 8
-    return max(len, 16);
+    return max(len, kAttnMinChunk);
 }
 
 struct AttnShared {
@@ -449,19 +465,30 @@ struct AttnShared {
     __attribute__((aligned(16))) float k[kMaxHd];
     __attribute__((aligned(16))) float v[kMaxHd];
     float e[kAttnChunk];                    // e^(s_j - max) of the chunk's positions
-    float part[kT];                         // per-group partial sums of the weighted values
+    float kp[kAttnChunk * (kMaxHd / 4)];    // q . k over each run of four values, row-major
+    __attribute__((aligned(16))) float part[4 * kT];  // per-group partial sums of the weighted values
     float red[kT / 64];
     float chunk[kMaxAttnChunks][kMaxHd + 2];  // per chunk: max, sum, weighted sums
 };
 struct NoAttnShared {};
 
+// Workgroup barrier for LDS: this wave's LDS accesses complete, then
+// s_barrier; global loads in flight stay in flight.
+__device__ __forceinline__ void lds_sync()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unconstrained
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ float block_max_f(float v, float* red)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     v = wave_max(v);
-    __syncthreads();  // red is free
+    lds_sync();  // red is free
     if (lane == 0) red[wave] = v;
-    __syncthreads();
+    lds_sync();
     float m = red[0];
 #pragma unroll
     for (int i = 1; i < kT / 64; ++i) m = fmaxf(m, red[i]);
@@ -473,9 +500,9 @@ __device__ __forceinline__ float block_sum_f(float v, float* red)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    __syncthreads();
+    lds_sync();
     if (lane == 0) red[wave] = v;
-    __syncthreads();
+    lds_sync();
     float s = red[0];
 #pragma unroll
     for (int i = 1; i < kT / 64; ++i) s += red[i];
@@ -488,21 +515,45 @@ __device__ __forceinline__ float block_sum_f(float v, float* red)
 // chunks' partials stay in LDS, the others' arrive as epoch-tagged words
 // (epoch E2, so no copy needs clearing), and it publishes the head's output.
 // False (for the whole workgroup) when a wait gave up. D: the model width (q,
-// k, v are the 3 consecutive D-word rows of qq). The cache rows are not
-// prefetched: a wave's loads complete in order, so a prefetch issued before
-// the wait for q, k, v, or at the start of the layer, only delayed that wait
-// (measured slower at positions 128 and 2047).
+// k, v are the 3 consecutive D-word rows of qq).
 template <int D>
 __device__ bool attention_split(const StreamArgs& a, int l, int h, int split, int G, uint32_t E2,
                                 const uint32_t* qq_cur, uint32_t* ao_cur, uint32_t* ao_old, AttnShared& s)
 {
     const int t = threadIdx.x;
-    const int hd = a.hd, half = hd / 2, pos = a.pos;
+    const int hd = a.hd, half = hd / 2, pos = a.pos, h4 = hd / 4;
     const int len = attn_chunk_len(pos, G);
     const int nch = (pos + len) / len;
     const int last = (nch - 1) % G;  // the split that holds position pos
     const float* kbase = a.k_cache + ((size_t)l * a.heads + h) * a.max_seq * hd;
     const float* vbase = a.v_cache + ((size_t)l * a.heads + h) * a.max_seq * hd;
+    // V: thread (g, c4v) takes float4 column c4v of positions g, g + groups, ...
+    const int groups = kT / h4, g = t / h4, c4v = t - g * h4;
+    const size_t vstep = (size_t)groups * h4;  // float4s between a thread's V positions
+
+    // One round of a chunk's cache rows (lim >= 1 rows from position j0): K
+    // float4s f0 + t + 512 i, V positions g + groups (u0 + u) of float4 column
+    // c4v, indices clamped to the last row (threads without V positions read
+    // row j0).
+    float4 kr[kAttnKB];
+    float4 vr[kAttnVB];
+    auto load_k = [&](int j0, int lim, int f0) {
+        const float4* kb4 = reinterpret_cast<const float4*>(kbase + (size_t)j0 * hd);
+        const int nf = lim * (hd / 4);
+#pragma unroll
+        for (int i = 0; i < kAttnKB; ++i) kr[i] = kb4[min(f0 + t + kT * i, nf - 1)];
+    };
+    auto load_v = [&](int j0, int lim, int u0) {
+        const bool has = g < groups && lim > g;  // else: row j0 only
+        const int mine = has ? (lim - g + groups - 1) / groups : 1;
+        const float4* vp = reinterpret_cast<const float4*>(vbase + (size_t)(j0 + (has ? g : 0)) * hd) + c4v;
+#pragma unroll
+        for (int u = 0; u < kAttnVB; ++u) vr[u] = vp[(size_t)min(u0 + u, mine - 1) * vstep];
+    };
+
+    // RoPE factors first: loads complete in issue order, so a load issued after
+    // the cache rows' would wait for all of them
+    const float rc = t < half ? a.rope_cos[t] : 0.0f, rsn = t < half ? a.rope_sin[t] : 0.0f;
     // the 3 hd words of this head: q, then k, then v
     const int n = 3 * hd;
     const long long t_start = (long long)__builtin_amdgcn_s_memrealtime();
@@ -528,6 +579,14 @@ __device__ bool attention_split(const StreamArgs& a, int l, int h, int split, in
         if (t == 0) __hip_atomic_fetch_or(a.ctrl + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return false;
     }
+    {
+        // the first chunk's rows do not depend on this step's q, k, v
+        const int lim = min(len, pos - split * len);
+        if (lim > 0) {
+            load_k(split * len, lim, 0);
+            load_v(split * len, lim, 0);
+        }
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int u = t + kT * i;
@@ -539,11 +598,11 @@ __device__ bool attention_split(const StreamArgs& a, int l, int h, int split, in
             (seg == 0 ? s.q : seg == 1 ? s.k : s.v)[i_] = x;
         }
     }
-    __syncthreads();
+    lds_sync();
     // RoPE of q and k (each thread its own pair); the split of the last chunk
     // writes k and v at position pos of the caches
     if (t < half) {
-        const float c = a.rope_cos[t], sn = a.rope_sin[t];
+        const float c = rc, sn = rsn;
         {
             const float x0 = s.q[2 * t], x1 = s.q[2 * t + 1];
             const float ac = x0 * c, bs = x1 * sn, as = x0 * sn, bc = x1 * c;
@@ -565,80 +624,85 @@ __device__ bool attention_split(const StreamArgs& a, int l, int h, int split, in
             vrow[2 * t + 1] = s.v[2 * t + 1];
         }
     }
-    __syncthreads();
+    lds_sync();
     const float scale = 1.0f / sqrtf((float)hd);
-    const int groups = kT / hd, g = t / hd, gi = t - g * hd;
+    // run of float4 f = t + 512 i within its row: f mod h4, advanced by 512 mod h4 per i
+    const int c4_first = t % h4, c4_step = kT % h4;
     for (int c = split; c < nch; c += G) {
         const int j0 = c * len, cnt = min(len, pos + 1 - j0);
+        const int lim = min(len, pos - j0);  // cache rows of the chunk (position pos is not one)
+        const int nf = lim * h4;
+        if (c != split && lim > 0) {
+            load_k(j0, lim, 0);
+            load_v(j0, lim, 0);
+        }
+        // q . k over each run of four values of the cache rows
+        int c4 = c4_first;
+        for (int f0 = 0; f0 < nf; f0 += kT * kAttnKB) {
+            if (f0 > 0) load_k(j0, lim, f0);
+#pragma unroll
+            for (int i = 0; i < kAttnKB; ++i) {
+                const int f = f0 + t + kT * i;
+                if (f < nf) {
+                    const float4 qv = *reinterpret_cast<const float4*>(s.q + 4 * c4);
+                    s.kp[f] = ((qv.x * kr[i].x + qv.y * kr[i].y) + qv.z * kr[i].z) + qv.w * kr[i].w;
+                }
+                c4 += c4_step;
+                if (c4 >= h4) c4 -= h4;
+            }
+        }
+        if (lim < cnt && t < h4) {
+            // position pos (row lim of the chunk), from LDS: its cache row is being written now
+            const float4 qv = *reinterpret_cast<const float4*>(s.q + 4 * t);
+            const float4 kv = *reinterpret_cast<const float4*>(s.k + 4 * t);
+            s.kp[nf + t] = ((qv.x * kv.x + qv.y * kv.y) + qv.z * kv.z) + qv.w * kv.w;
+        }
+        lds_sync();
         float sc = -INFINITY;
         if (t < cnt) {
             float dot = 0.0f;
-            if (j0 + t < pos) {
-                // a cache row: the loads of four 16-byte pieces go out together
-                const float* kj = kbase + (size_t)(j0 + t) * hd;
-                int i = 0;
-                for (; i + 16 <= hd; i += 16) {
-                    float4 kv[4];
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) kv[u] = *reinterpret_cast<const float4*>(kj + i + 4 * u);
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        dot += s.q[i + 4 * u] * kv[u].x;
-                        dot += s.q[i + 4 * u + 1] * kv[u].y;
-                        dot += s.q[i + 4 * u + 2] * kv[u].z;
-                        dot += s.q[i + 4 * u + 3] * kv[u].w;
-                    }
-                }
-                for (; i < hd; i += 4) {
-                    const float4 kv = *reinterpret_cast<const float4*>(kj + i);
-                    dot += s.q[i] * kv.x;
-                    dot += s.q[i + 1] * kv.y;
-                    dot += s.q[i + 2] * kv.z;
-                    dot += s.q[i + 3] * kv.w;
-                }
-            } else {
-                // position pos, from LDS: its cache row is being written now
-                for (int i = 0; i < hd; ++i) dot += s.q[i] * s.k[i];
-            }
+            const float* pr = s.kp + t * h4;
+#pragma unroll 8
+            for (int m = 0; m < h4; ++m) dot += pr[m];
             sc = dot * scale;
         }
         const float mx = block_max_f(sc, s.red);
         if (t < kAttnChunk) s.e[t] = t < cnt ? expf(sc - mx) : 0.0f;
         const float sum = block_sum_f(t < cnt ? s.e[t] : 0.0f, s.red);  // its barriers also publish e[]
-        if (g < groups) {
-            // positions j0 + jj, jj = g, g + groups, ... ascending: cache rows in
-            // batches of eight independent loads, then position pos (always the
-            // last one) from LDS
-            // batches of 16 with the next batch's loads issued before the
-            // current one is summed
-            const int lim = min(cnt, pos - j0);
-            const int mine = lim > g ? (lim - g + groups - 1) / groups : 0;  // my cache rows
-            const size_t step = (size_t)groups * hd;
-            const float* vp = vbase + (size_t)(j0 + g) * hd + gi;
-            constexpr int B = 16;
-            float va[B], vb[B];
+        // positions j0 + jj, jj = g, g + groups, ... ascending: the cache rows,
+        // then position pos (always the last one) from LDS
+        const int mine = (g < groups && lim > g) ? (lim - g + groups - 1) / groups : 0;
+        float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        for (int u0 = 0; u0 < mine; u0 += kAttnVB) {
+            if (u0 > 0) load_v(j0, lim, u0);
 #pragma unroll
-            for (int u = 0; u < B; ++u) va[u] = u < mine ? vp[(size_t)u * step] : 0.0f;
-            float acc = 0.0f;
-            for (int k0 = 0; k0 < mine; k0 += B) {
-#pragma unroll
-                for (int u = 0; u < B; ++u) vb[u] = k0 + B + u < mine ? vp[(size_t)(k0 + B + u) * step] : 0.0f;
-#pragma unroll
-                for (int u = 0; u < B; ++u)
-                    if (k0 + u < mine) acc += s.e[g + (k0 + u) * groups] * va[u];
-#pragma unroll
-                for (int u = 0; u < B; ++u) va[u] = vb[u];
-            }
-            const int jj = g + mine * groups;  // my first position not in the cache loop
-            if (jj == pos - j0 && jj < cnt) acc += s.e[jj] * s.v[gi];  // pos lies in this chunk
-            s.part[g * hd + gi] = acc;
+            for (int u = 0; u < kAttnVB; ++u)
+                if (u0 + u < mine) {
+                    const float e = s.e[g + (u0 + u) * groups];
+                    acc.x += e * vr[u].x;
+                    acc.y += e * vr[u].y;
+                    acc.z += e * vr[u].z;
+                    acc.w += e * vr[u].w;
+                }
         }
-        __syncthreads();
+        if (g < groups) {
+            const int jj = g + mine * groups;  // my first position not in the cache rows
+            if (jj == pos - j0 && jj < cnt) {  // pos lies in this chunk
+                const float e = s.e[jj];
+                const float4 vv = *reinterpret_cast<const float4*>(s.v + 4 * c4v);
+                acc.x += e * vv.x;
+                acc.y += e * vv.y;
+                acc.z += e * vv.z;
+                acc.w += e * vv.w;
+            }
+            *reinterpret_cast<float4*>(s.part + g * hd + 4 * c4v) = acc;
+        }
+        lds_sync();
         float* cp = s.chunk[split == 0 ? c : 0];
         if (t < hd) {
-            float acc = 0.0f;
-            for (int q = 0; q < groups; ++q) acc += s.part[q * hd + t];
-            cp[2 + t] = acc;
+            float acc2 = 0.0f;
+            for (int q = 0; q < groups; ++q) acc2 += s.part[q * hd + t];
+            cp[2 + t] = acc2;
         }
         if (t == 0) {
             cp[0] = mx;
@@ -646,30 +710,45 @@ __device__ bool attention_split(const StreamArgs& a, int l, int h, int split, in
         }
         if (split != 0) {
             // publish the chunk's partials: [max, sum, hd weighted sums]
-            __syncthreads();
+            lds_sync();
             unsigned long long* dst = a.apart + ((size_t)h * a.chunks_max + c) * (hd + 2);
             if (t < hd + 2) ll_store(dst + t, cp[t], E2);
         }
-        // the next chunk's first writes (e[], part[], the chunk slot) follow two barriers
+        // the next chunk's first writes (kp[], e[], part[], the chunk slot) follow
+        // at least one barrier after this chunk's last reads of them
     }
     if (split != 0) return true;
     // split 0: the other chunks' partials, then the merge and the head's output
     const int others = nch - (nch + G - 1) / G;  // chunks held by splits 1 .. G-1
     if (others > 0) {
+        // word u of the chunks c % G != 0, in chunk order; each round issues
+        // all of its loads before it checks any
         const int nw = others * (hd + 2);
+        constexpr int kMW = 4;
         const long long t0 = (long long)__builtin_amdgcn_s_memrealtime();
         bool bad = false;
         for (int spin = 0;; ++spin) {
             bool ready = true;
-            for (int u = t; u < nw; u += kT) {
-                // u-th word of the chunks c % G != 0, in chunk order
-                const int oc = u / (hd + 2), wi = u - oc * (hd + 2);
-                const int c = oc + oc / (G - 1) + 1;
-                const unsigned long long v = ll_load(a.apart + ((size_t)h * a.chunks_max + c) * (hd + 2) + wi);
-                if ((uint32_t)(v >> 32) != E2) {
-                    ready = false;
-                } else {
-                    s.chunk[c][wi] = __uint_as_float((uint32_t)v);
+            for (int u0 = 0; u0 < nw; u0 += kT * kMW) {
+                unsigned long long v[kMW];
+#pragma unroll
+                for (int i = 0; i < kMW; ++i) {
+                    const int u = min(u0 + t + kT * i, nw - 1);
+                    const int oc = u / (hd + 2), wi = u - oc * (hd + 2);
+                    const int c = oc + oc / (G - 1) + 1;
+                    v[i] = ll_load(a.apart + ((size_t)h * a.chunks_max + c) * (hd + 2) + wi);
+                }
+#pragma unroll
+                for (int i = 0; i < kMW; ++i) {
+                    const int u = u0 + t + kT * i;
+                    if (u < nw) {
+                        const int oc = u / (hd + 2), wi = u - oc * (hd + 2);
+                        const int c = oc + oc / (G - 1) + 1;
+                        if ((uint32_t)(v[i] >> 32) != E2)
+                            ready = false;
+                        else
+                            s.chunk[c][wi] = __uint_as_float((uint32_t)v[i]);
+                    }
                 }
             }
             if (__syncthreads_and(ready ? 1 : 0)) break;

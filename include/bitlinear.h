@@ -359,7 +359,7 @@ int bitnet_decode_stream(const uint8_t *weights, const float *scales, const floa
  * stream is being captured into a graph) it runs one launch per step: RoPE and
  * append, one workgroup per (sequence, head, 256 positions), a merge launch.
  * Both compute the same fp32 attention arithmetic up to the order of the
- * weighted sums, within the same bound.
+ * terms of the scores and of the weighted sums, within the same bound.
  * Errors: NULL, SHAPE (pos outside [0, max_seq), ...), ALIGN, WORKSPACE, LAUNCH. */
 size_t bitnet_decode_step_workspace_bytes(int64_t m, int64_t d, int64_t f, int64_t n_heads, int64_t max_seq);
 int bitnet_decode_step(const uint8_t *weights, const float *scales, const float *gains, int64_t n_layers,

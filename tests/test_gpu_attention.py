@@ -14,7 +14,9 @@ e_s = (hd + 4) u max_j sum_i |q_i k_ji| / sqrt(hd) of the exact one; each
 weight e^(s_j - max) is then within a relative 2 e_s + 4 u (expf adds a few
 ulps); the chunked sums add (pos + 1 + 4 * chunks) u relative to
 sum_j e_j |v_j|, chunks being the number of chunks merged (256 positions
-each, or up to min(256 / heads, 32) shorter ones in the persistent kernel). With V = max |v| over the head's positions the output is off
+each, or up to min(256 / heads, 32) shorter ones in the persistent kernel;
+the bound takes the larger count). With V = max |v| over the head's
+positions the output is off
 by at most V (2 (2 e_s + 4 u) + (pos + 5 + 4 chunks) u); the test allows
 twice that."""
 import numpy as np
@@ -40,7 +42,7 @@ def _attn_bound(q_rot, kc, vc, pos, hd):
     # chunks merged: 256-position chunks, or (the persistent kernel, when a head
     # has fewer of those than workgroups) up to min(256 / heads, 32) shorter ones
     n256 = (pos + 1 + 255) // 256
-    chunks = max(n256, min(256 // heads, 32)) if n256 >= 2 else 1
+    chunks = max(n256, min(256 // heads, 32))
     bound = np.empty((m, heads, hd))
     for r in range(m):
         for h in range(heads):
@@ -143,3 +145,11 @@ def test_decode_step_bitnet_1p3b_shapes(bl, olib):
     """BitNet-1.3B shapes (d = 2048, 16 heads of 128, f = 8192), two layers, one
     sequence at positions 255 and 256 (one chunk, then two)."""
     _run_steps(bl, olib, 2, 1, 2048, 8192, 16, 512, [255, 256], seed=13, prefill=255)
+
+
+def test_decode_step_persistent_short_chunks(bl, olib):
+    """One sequence with 32 heads of 8 values (8 workgroups per head): at
+    position 15 the 16 positions form one chunk; at 16 a chunk of 16 cache
+    rows and one holding only the new position; at 17 and 47 two and three
+    chunks of 16, merged by the head's first workgroup."""
+    _run_steps(bl, olib, 2, 1, 256, 1024, 32, 64, [15, 16, 17, 47], seed=15, prefill=15)
