@@ -19,8 +19,10 @@
 // weight reaches a target" is found by a most-significant-digit radix
 // selection over the keys in six digits (12, 10, 10, 11, 11, 10 bits): a
 // level sums the (exact, int64) weights and the counts of the candidates per
-// digit value in LDS, and the workgroup finds the digit at which the running
-// total crosses the target with one prefix scan. The first level's sums come
+// digit value in LDS; each wave totals a block of digit values, and one wave
+// finds the block and then the digit at which the running total crosses the
+// target (lane prefix sums by DPP row shifts and broadcasts; the sums are
+// integers, so their order does not matter). The first level's sums come
 // from the pass that computes the weights and serve both selections; the
 // twelve-bit first digit (sign, exponent, three mantissa bits of the logit)
 // spreads logits of a few units over many bins, which keeps the LDS atomics
@@ -142,31 +144,27 @@ __device__ float block_max(float v, Shared& sh)
     return t;
 }
 
-// Exclusive prefix sums over the workgroup (threads in order) of three int64s.
-__device__ void block_excl3(long long (&v)[3], Shared& sh)
+// Lane i receives lane i - n's value of its row of 16 (n = 1, 2, 4, 8), or a
+// row broadcast (lane 15 into rows 1 and 3, then lane 31 into rows 2 and 3);
+// 0 where there is none. Integer sums, exact in any order.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ long long dpp64(long long v)
 {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    long long inc[3] = {v[0], v[1], v[2]};
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-#pragma unroll
-        for (int j = 0; j < 3; ++j) {
-            const long long o = __shfl_up(inc[j], off, 64);
-            if (lane >= off) inc[j] += o;
-        }
-    }
-    __syncthreads();  // sh.red is free
-    if (lane == 63) {
-#pragma unroll
-        for (int j = 0; j < 3; ++j) sh.red[wave][j] = inc[j];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-        long long before = 0;
-        for (int w = 0; w < wave; ++w) before += sh.red[w][j];
-        v[j] = before + inc[j] - v[j];
-    }
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(unsigned int)(unsigned long long)v, CTRL, ROW_MASK, 0xF, true);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)((unsigned long long)v >> 32), CTRL, ROW_MASK, 0xF, true);
+    return (long long)(((unsigned long long)(unsigned int)hi << 32) | (unsigned long long)(unsigned int)lo);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ long long lane_scan(long long v)
+{
+    v += dpp64<0x111, 0xF>(v);  // row_shr:1
+    v += dpp64<0x112, 0xF>(v);  // row_shr:2
+    v += dpp64<0x114, 0xF>(v);  // row_shr:4
+    v += dpp64<0x118, 0xF>(v);  // row_shr:8
+    v += dpp64<0x142, 0xA>(v);  // row_bcast:15
+    v += dpp64<0x143, 0xC>(v);  // row_bcast:31
+    return v;
 }
 
 // Result of a selection: the key, and the weight and count of the tokens
@@ -188,7 +186,7 @@ template <bool COUNT>
 __device__ Pick select_key(const float* __restrict__ l, const long long* __restrict__ w, int n, long long target,
                            Shared& sh, unsigned long long& lmask, unsigned long long& lprefix)
 {
-    const int t = threadIdx.x;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     unsigned long long prefix = 0, mask = 0;
     long long above_t = 0, above_w = 0;
     unsigned int above_c = 0;
@@ -255,37 +253,59 @@ __device__ Pick select_key(const float* __restrict__ l, const long long* __restr
             __syncthreads();
         }
         // the digit at which the running total (digits in descending order)
-        // reaches target; thread t scans bins - 1 - per t .. bins - per (t + 1)
-        const int per = bins / kT;
-        long long s[3] = {0, 0, 0};  // target units, weight, count
-        for (int j = 0; j < per; ++j) {
-            const int d = bins - 1 - per * t - j;
-            const long long bw = (long long)hw[d], bc = (long long)hc[d];
-            s[0] += COUNT ? bc : bw;
-            s[1] += bw;
-            s[2] += bc;
-        }
-        const long long mine = s[0];
-        block_excl3(s, sh);
-        if (above_t + s[0] < target && above_t + s[0] + mine >= target) {
-            long long rt = above_t + s[0], rw = above_w + s[1];
-            long long rc = (long long)above_c + s[2];
-            for (int j = 0; j < per; ++j) {
-                const int d = bins - 1 - per * t - j;
+        // reaches target. Wave w totals the block of bins / 16 digits
+        // bins - 1 - w B .. bins - (w + 1) B (lane j its digits j, j + 64, ...
+        // of the block); wave 0 then finds the block where the total crosses
+        // target, and the digit inside it 64 digits at a time.
+        const int B = bins / kWaves;
+        {
+            long long s0 = 0, s1 = 0, s2 = 0;  // target units, weight, count
+            for (int i = lane; i < B; i += 64) {
+                const int d = bins - 1 - B * wave - i;
                 const long long bw = (long long)hw[d], bc = (long long)hc[d];
+                s0 += COUNT ? bc : bw;
+                s1 += bw;
+                s2 += bc;
+            }
+            s0 = lane_scan(s0);
+            s1 = lane_scan(s1);
+            s2 = lane_scan(s2);
+            if (lv == 0) __syncthreads();  // sh.red is free (the total's reduction read it last)
+            if (lane == 63) {
+                sh.red[wave][0] = s0;
+                sh.red[wave][1] = s1;
+                sh.red[wave][2] = s2;
+            }
+        }
+        __syncthreads();
+        if (wave == 0) {
+            const long long b0 = lane < kWaves ? sh.red[lane][0] : 0, b1 = lane < kWaves ? sh.red[lane][1] : 0;
+            const long long b2 = lane < kWaves ? sh.red[lane][2] : 0;
+            const long long i0 = lane_scan(b0), i1 = lane_scan(b1), i2 = lane_scan(b2);
+            const bool cross = lane < kWaves && above_t + i0 - b0 < target && above_t + i0 >= target;
+            // one block (1 <= target <= total); block 0 should there be none
+            const int W = max(__ffsll((unsigned long long)__ballot(cross)) - 1, 0);
+            long long rt = above_t + __shfl(i0 - b0, W, 64), rw = above_w + __shfl(i1 - b1, W, 64);
+            long long rc = (long long)above_c + __shfl(i2 - b2, W, 64);
+            for (int i0b = 0; i0b < B; i0b += 64) {
+                const int i = i0b + lane;
+                const int d = bins - 1 - B * W - i;
+                const long long bw = i < B ? (long long)hw[d] : 0, bc = i < B ? (long long)hc[d] : 0;
                 const long long bt = COUNT ? bc : bw;
-                if (rt + bt >= target) {
+                const long long f0 = lane_scan(bt), f1 = lane_scan(bw), f2 = lane_scan(bc);
+                const bool hit = i < B && rt + f0 - bt < target && rt + f0 >= target;
+                if (hit) {
                     sh.sel_digit = d;
-                    sh.sel_above_t = rt;
-                    sh.sel_above_w = rw;
-                    sh.sel_above_c = (unsigned int)rc;
+                    sh.sel_above_t = rt + f0 - bt;
+                    sh.sel_above_w = rw + f1 - bw;
+                    sh.sel_above_c = (unsigned int)(rc + f2 - bc);
                     sh.sel_bin_w = bw;
                     sh.sel_bin_c = (unsigned int)bc;
-                    break;
                 }
-                rt += bt;
-                rw += bw;
-                rc += bc;
+                if (__ballot(hit)) break;
+                rt += __shfl(f0, 63, 64);
+                rw += __shfl(f1, 63, 64);
+                rc += __shfl(f2, 63, 64);
             }
         }
         __syncthreads();
