@@ -223,29 +223,48 @@ __device__ Pick select_key(const float* __restrict__ l, const long long* __restr
 #pragma unroll
                     for (int u = 0; u < kB; ++u) lv[u] = i0 + u * kT < n ? l[i0 + u * kT] : 0.0f;
                     unsigned long long key[kB];
-                    long long wv[kB];
 #pragma unroll
-                    for (int u = 0; u < kB; ++u) {
-                        const int i = i0 + u * kT;
-                        key[u] = sort_key(lv[u], i);
-                        const bool hit = i < n && (key[u] & mask) == prefix;
-                        wv[u] = hit ? w[i] : -1;  // -1: not a candidate (weights are >= 0)
-                    }
+                    for (int u = 0; u < kB; ++u) key[u] = sort_key(lv[u], i0 + u * kT);
+                    if (fill) {
+                        // the candidates (at most kCap) go to the list with their
+                        // index; their weights are gathered below in one round
 #pragma unroll
-                    for (int u = 0; u < kB; ++u) {
-                        if (wv[u] >= 0) {
-                            const int d = (int)((key[u] >> shift) & dmask);
-                            atomicAdd(&sh.hw[d], (unsigned long long)wv[u]);
-                            atomicAdd(&sh.hc[d], 1u);
-                            if (fill) {
+                        for (int u = 0; u < kB; ++u) {
+                            const int i = i0 + u * kT;
+                            if (i < n && (key[u] & mask) == prefix) {
                                 const unsigned int slot = atomicAdd(&sh.ncand, 1u);
                                 sh.ck[slot] = key[u];
-                                sh.cw[slot] = wv[u];
+                                sh.cw[slot] = i;
+                            }
+                        }
+                    } else {
+                        long long wv[kB];
+#pragma unroll
+                        for (int u = 0; u < kB; ++u) {
+                            const int i = i0 + u * kT;
+                            const bool hit = i < n && (key[u] & mask) == prefix;
+                            wv[u] = hit ? w[i] : -1;  // -1: not a candidate (weights are >= 0)
+                        }
+#pragma unroll
+                        for (int u = 0; u < kB; ++u) {
+                            if (wv[u] >= 0) {
+                                const int d = (int)((key[u] >> shift) & dmask);
+                                atomicAdd(&sh.hw[d], (unsigned long long)wv[u]);
+                                atomicAdd(&sh.hc[d], 1u);
                             }
                         }
                     }
                 }
                 if (fill) {
+                    __syncthreads();
+                    const int nc = (int)sh.ncand;
+                    for (int i = t; i < nc; i += kT) {
+                        const long long wv = w[(int)sh.cw[i]];
+                        sh.cw[i] = wv;
+                        const int d = (int)((sh.ck[i] >> shift) & dmask);
+                        atomicAdd(&sh.hw[d], (unsigned long long)wv);
+                        atomicAdd(&sh.hc[d], 1u);
+                    }
                     lmask = mask;
                     lprefix = prefix;
                 }
