@@ -26,6 +26,7 @@ constexpr uint32_t kCodeMask = 0x03030303u;
 constexpr int kMaxChunksPerLane = 8;
 constexpr int kFwdMaxK = 4096;         // longest row of the one-wave quant + GEMV
 constexpr int kFwdBlockMaxK = 16384;   // ... and of the 512-thread form
+constexpr int kFwdBlockGrid = 256;     // workgroups of the 512-thread form: one per CU
 
 // 4x4 byte transpose of 16 activations a[0..15] (given as 4 dwords, natural
 // order) into the order the shifted code masks produce: out[j] holds
@@ -259,17 +260,18 @@ __global__ __launch_bounds__(64) void fwd_kernel(const float* __restrict__ x, co
 // fwd_kernel for rows longer than one wave can hold (4096 < k <= 512 NPT): a
 // 512-thread workgroup quantizes x with the workgroup quant of the quant kernel
 // (block_quant_compute: same operations, same order, so every workgroup holds
-// the same q, s_a and sum(q)) into LDS, then each wave runs one row with all 64
-// lanes. Optional residual (may alias y) and exact accumulators, as gemv_kernel.
+// the same q, s_a and sum(q)) into LDS, then its waves run its rpb consecutive
+// rows (wave w rows w, w + 8, ...) with all 64 lanes each. Optional residual
+// (may alias y) and exact accumulators, as gemv_kernel.
 template <int NPT, bool kNorm>
 __global__ __launch_bounds__(512) void fwd_block_kernel(const float* __restrict__ x, const float* __restrict__ gain,
                                                         float eps, const uint8_t* __restrict__ packed, float w_scale,
                                                         const float* __restrict__ w_scale_ptr, int n, int k,
                                                         const float* residual, float* y, int32_t* __restrict__ acc_out,
                                                         int8_t* __restrict__ q_out, float* __restrict__ scale_out,
-                                                        int32_t* __restrict__ sum_out)
+                                                        int32_t* __restrict__ sum_out, int rpb)
 {
-    constexpr int L = 64, RW = 8;                // a row per wave, 8 per workgroup
+    constexpr int L = 64, RW = 8;                // a row per wave at a time
     constexpr int CPL = (8 * NPT + L - 1) / L;   // chunks per lane: k <= 512 NPT
     static_assert(CPL <= kMaxChunksPerLane && 512 * NPT <= kFwdBlockMaxK, "row size");
     __shared__ __attribute__((aligned(16))) int8_t qs[512 * NPT];
@@ -281,8 +283,9 @@ __global__ __launch_bounds__(512) void fwd_block_kernel(const float* __restrict_
     float xv[NPT], gv[NPT];
     block_quant_load<kNorm, NPT>(x, gain, k, xv, gv);  // first: a wave's loads complete in issue order
     uint4 w[kMaxChunksPerLane];
-    int base = blockIdx.x * RW;
-    load_row_fixed<L, CPL>(packed + (size_t)min(base + wave, n - 1) * row_bytes, lane, chunks, w);
+    const int r1 = min(blockIdx.x * rpb + rpb, n);  // this workgroup's rows end here
+    int row = blockIdx.x * rpb + wave;
+    load_row_fixed<L, CPL>(packed + (size_t)min(row, n - 1) * row_bytes, lane, chunks, w);
     __builtin_amdgcn_sched_barrier(0);  // keep the weight loads ahead of the quant
     float s_a;
     int qsum;
@@ -306,18 +309,17 @@ __global__ __launch_bounds__(512) void fwd_block_kernel(const float* __restrict_
     const float ws = w_scale_ptr ? *w_scale_ptr : w_scale;
     const float inv = 1.0f / (s_a * ws);
     for (;;) {
-        const int row = base + wave;
         const int acc = group_sum<L>(dot_row_one<L, CPL>(w, lane, chunks, qreg));
-        if (row < n && lane == 0) {
+        if (row < r1 && lane == 0) {
             const int total = acc - qsum;
             float v = (float)total * inv;
             if (residual) v = residual[row] + v;
             y[row] = v;
             if (acc_out) acc_out[row] = total;
         }
-        base += gridDim.x * RW;
-        if (base >= n) break;
-        load_row_fixed<L, CPL>(packed + (size_t)min(base + wave, n - 1) * row_bytes, lane, chunks, w);
+        row += RW;
+        if (row >= r1) break;
+        load_row_fixed<L, CPL>(packed + (size_t)row * row_bytes, lane, chunks, w);
     }
 }
 
@@ -417,37 +419,40 @@ __global__ __launch_bounds__(64) void gateup_kernel(const uint8_t* __restrict__ 
 }
 
 // gateup_kernel for one token with the [RMSNorm +] quant of its input fused
-// in, as fwd_kernel does for a single matrix: every workgroup quantizes x into
-// LDS itself while its first gate and up rows stream in.
-template <int V, bool kNorm>
-__global__ __launch_bounds__(64) void fwd_gateup_kernel(const float* __restrict__ x, const float* __restrict__ gain,
-                                                        float eps, const uint8_t* __restrict__ w_gate, float s_gate,
-                                                        const uint8_t* __restrict__ w_up, float s_up,
-                                                        const float* __restrict__ scale_ptr, int f, int d,
-                                                        float* __restrict__ h, int8_t* __restrict__ q_out,
-                                                        float* __restrict__ scale_out, int32_t* __restrict__ sum_out,
-                                                        int32_t* __restrict__ acc_gate, int32_t* __restrict__ acc_up)
+// in, one 512-thread workgroup per CU: it quantizes x once with the workgroup
+// quant (block_quant_compute: the same q, s_a and sum(q) as the quant kernel)
+// into LDS while its first gate and up rows stream in, and its 8 waves run its
+// rpb consecutive rows, 8 lanes per row (wave w takes rows w, w + 8, ... of
+// the block): x is read once per CU.
+template <int NPT, bool kNorm>
+__global__ __launch_bounds__(512) void fwd_gateup_block_kernel(
+    const float* __restrict__ x, const float* __restrict__ gain, float eps, const uint8_t* __restrict__ w_gate,
+    float s_gate, const uint8_t* __restrict__ w_up, float s_up, const float* __restrict__ scale_ptr, int f, int d,
+    float* __restrict__ h, int8_t* __restrict__ q_out, float* __restrict__ scale_out, int32_t* __restrict__ sum_out,
+    int32_t* __restrict__ acc_gate, int32_t* __restrict__ acc_up, int rpb)
 {
-    constexpr int L = 8, R = 64 / L;
-    static_assert(64 * 4 * V <= kFwdMaxK, "row held in LDS");
-    __shared__ __attribute__((aligned(16))) int8_t qs[kFwdMaxK];
-    const int lane = threadIdx.x;
+    constexpr int L = 8, R = 64 / L;   // 8 lanes per row, 8 rows per wave at a time
+    constexpr int CPL = NPT;           // chunks per lane: d <= 512 NPT, 8 NPT chunks over 8 lanes
+    static_assert(CPL <= kMaxChunksPerLane, "row size");
+    __shared__ __attribute__((aligned(16))) int8_t qs[512 * NPT];
+    __shared__ BlockQuantShared sh;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane / L, j = lane % L;
     const int chunks = d / 64;
     const size_t row_bytes = (size_t)d / 4;
 
-    float4 xv[V], gv[V];
-    wave_quant_load<kNorm, V>(x, gain, d, lane, xv, gv);  // first: see fwd_kernel
-    constexpr int CPL = (V + 1) / 2;  // chunks per lane: d <= 256 V
+    float xv[NPT], gv[NPT];
+    block_quant_load<kNorm, NPT>(x, gain, d, xv, gv);  // first: a wave's loads complete in issue order
     uint4 wg[kMaxChunksPerLane], wu[kMaxChunksPerLane];
-    int base = blockIdx.x * R;
-    load_row_fixed<L, CPL>(w_gate + (size_t)min(base + g, f - 1) * row_bytes, j, chunks, wg);
-    load_row_fixed<L, CPL>(w_up + (size_t)min(base + g, f - 1) * row_bytes, j, chunks, wu);
+    const int r1 = min(blockIdx.x * rpb + rpb, f);  // this workgroup's rows end here
+    int row = blockIdx.x * rpb + wave + 8 * g;      // 8 waves x 8 groups: 64 rows at a time
+    // slots past the block's last row load that row again (from cache), not another block's
+    load_row_fixed<L, CPL>(w_gate + (size_t)min(row, r1 - 1) * row_bytes, j, chunks, wg);
+    load_row_fixed<L, CPL>(w_up + (size_t)min(row, r1 - 1) * row_bytes, j, chunks, wu);
     __builtin_amdgcn_sched_barrier(0);  // keep the weight loads ahead of the quant
     float s_a;
     int qsum;
-    wave_quant_compute<kNorm, false, V>(xv, gv, eps, d, lane, qs, s_a, qsum);
-    __syncthreads();  // q complete in LDS
+    block_quant_compute<kNorm, false, NPT>(xv, gv, eps, d, qs, sh, s_a, qsum);  // ends with a barrier
 
     uint32_t qreg[kMaxChunksPerLane][16];
 #pragma unroll
@@ -457,9 +462,9 @@ __global__ __launch_bounds__(64) void fwd_gateup_kernel(const float* __restrict_
     }
     if (blockIdx.x == 0) {
         if (q_out)
-            for (int i = lane; i < d / 16; i += 64)
+            for (int i = threadIdx.x; i < d / 16; i += 512)
                 reinterpret_cast<uint4*>(q_out)[i] = reinterpret_cast<const uint4*>(qs)[i];
-        if (lane == 0) {
+        if (threadIdx.x == 0) {
             if (scale_out) *scale_out = s_a;
             if (sum_out) *sum_out = qsum;
         }
@@ -467,10 +472,9 @@ __global__ __launch_bounds__(64) void fwd_gateup_kernel(const float* __restrict_
     const float sg = scale_ptr ? scale_ptr[0] : s_gate;
     const float su = scale_ptr ? scale_ptr[1] : s_up;
     for (;;) {
-        const int row = base + g;
         const int ag = group_sum<L>(dot_row_one<L, CPL>(wg, j, chunks, qreg));
         const int au = group_sum<L>(dot_row_one<L, CPL>(wu, j, chunks, qreg));
-        if (row < f && j == 0) {
+        if (row < r1 && j == 0) {
             const int tg = ag - qsum, tu = au - qsum;
             const float gate = (float)tg * (1.0f / (s_a * sg));
             const float up = (float)tu * (1.0f / (s_a * su));
@@ -480,10 +484,11 @@ __global__ __launch_bounds__(64) void fwd_gateup_kernel(const float* __restrict_
             if (acc_gate) acc_gate[row] = tg;
             if (acc_up) acc_up[row] = tu;
         }
-        base += gridDim.x * R;
-        if (base >= f) break;
-        load_row_fixed<L, CPL>(w_gate + (size_t)min(base + g, f - 1) * row_bytes, j, chunks, wg);
-        load_row_fixed<L, CPL>(w_up + (size_t)min(base + g, f - 1) * row_bytes, j, chunks, wu);
+        // the next 64 rows of the block; the wave stops when none of its rows is left
+        row += 64;
+        if (__builtin_amdgcn_readfirstlane(row - 8 * g) >= r1) break;
+        load_row_fixed<L, CPL>(w_gate + (size_t)min(row, r1 - 1) * row_bytes, j, chunks, wg);
+        load_row_fixed<L, CPL>(w_up + (size_t)min(row, r1 - 1) * row_bytes, j, chunks, wu);
     }
 }
 
@@ -576,11 +581,12 @@ int launch_fwd_block(const float* x, const float* gain, float eps, const uint8_t
                      int8_t* q_out, float* scale_out, int32_t* sum_out, hipStream_t s)
 {
     if (!fwd_block_fits(1, k)) return BL_ERR_SHAPE;
-    const int grid = (n + 7) / 8 < 8192 ? (n + 7) / 8 : 8192;
+    // one workgroup per CU, each on a block of consecutive rows (it reads x once)
+    const int rpb = (n + kFwdBlockGrid - 1) / kFwdBlockGrid, grid = (n + rpb - 1) / rpb;
     const int per = (k + 511) / 512;  // values per thread
 #define BL_FWDB(N, G)                                                                                              \
     fwd_block_kernel<N, G><<<grid, 512, 0, s>>>(x, gain, eps, packed, w_scale, w_scale_ptr, n, k, residual, y, acc_out, \
-                                                q_out, scale_out, sum_out)
+                                                q_out, scale_out, sum_out, rpb)
 #define BL_FWDB_N(N)      \
     if (gain)             \
         BL_FWDB(N, true); \
@@ -634,29 +640,32 @@ int launch_fwd_gateup(const float* x, const float* gain, float eps, const uint8_
                       hipStream_t s)
 {
     if (!fwd_fits(1, d)) return BL_ERR_SHAPE;
-    const int grid = grid_for(f, 8);
-    const int v = (d / 4 + 63) / 64;
-#define BL_FWDGU(V, N)                                                                                       \
-    fwd_gateup_kernel<V, N><<<grid, 64, 0, s>>>(x, gain, eps, w_gate, s_gate, w_up, s_up, scale_ptr, f, d, h, \
-                                                q_out, scale_out, sum_out, acc_gate, acc_up)
-#define BL_FWDGU_V(V)       \
-    if (gain)               \
-        BL_FWDGU(V, true);  \
-    else                    \
-        BL_FWDGU(V, false)
-    if (v <= 2) {
-        BL_FWDGU_V(2);
-    } else if (v <= 4) {
-        BL_FWDGU_V(4);
-    } else if (v <= 8) {
-        BL_FWDGU_V(8);
-    } else if (v <= 10) {
-        BL_FWDGU_V(10);
-    } else {
-        BL_FWDGU_V(16);
+    {
+        // one 512-thread workgroup per CU on a block of consecutive rows
+        const int rpb = (f + kFwdBlockGrid - 1) / kFwdBlockGrid, grid = (f + rpb - 1) / rpb;
+        const int npt = (d + 511) / 512;
+#define BL_FWDGUB(NPT, N)                                                                                            \
+    fwd_gateup_block_kernel<NPT, N><<<grid, 512, 0, s>>>(x, gain, eps, w_gate, s_gate, w_up, s_up, scale_ptr, f, d, h, \
+                                                        q_out, scale_out, sum_out, acc_gate, acc_up, rpb)
+#define BL_FWDGUB_N(NPT)      \
+    if (gain)                 \
+        BL_FWDGUB(NPT, true); \
+    else                      \
+        BL_FWDGUB(NPT, false)
+        if (npt <= 1) {
+            BL_FWDGUB_N(1);
+        } else if (npt <= 2) {
+            BL_FWDGUB_N(2);
+        } else if (npt <= 4) {
+            BL_FWDGUB_N(4);
+        } else if (npt <= 5) {
+            BL_FWDGUB_N(5);
+        } else {
+            BL_FWDGUB_N(8);
+        }
+#undef BL_FWDGUB_N
+#undef BL_FWDGUB
     }
-#undef BL_FWDGU_V
-#undef BL_FWDGU
     return hipGetLastError() == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
 }
 
