@@ -80,9 +80,12 @@ struct Mfma<16> {
 // so every packed weight column is unpacked by one wave only.
 using CfgLarge = Cfg<128, 320, 1, 4, 64, 16>;
 // Large M with few columns (fewer than two 128 x 320 tiles per CU, e.g. the FFN's
-// down projection 2048 x 10240 -> 2560: 128 tiles): 128 x 160 tiles, 2 x 2
-// waves of 64 x 80, twice the tiles (measured 90 against 125 us there).
-using CfgMid = Cfg<128, 160, 2, 2, 64, 16>;
+// down projection 2048 x 10240 -> 2560: 128 tiles): 64 x 160 tiles, 2 x 2
+// waves of 32 x 80, 128-deep K steps (half the barriers per K), four times the
+// tiles -- measured 69 us there, against 90 us for 128 x 160 tiles with 64-deep
+// steps and 125 us for 128 x 320. Rows of K % 128 == 64 take the 64-deep form.
+using CfgMid = Cfg<64, 160, 2, 2, 128, 16>;
+using CfgMid64 = Cfg<128, 160, 2, 2, 64, 16>;
 // Small M (up to 64 tokens; fewer run the skinny kernels): 32 x 256 tiles.
 using CfgSmall = Cfg<32, 256, 1, 4, 64, 32>;
 
@@ -369,9 +372,14 @@ int launch_gemm(const uint8_t* packed, float w_scale, const float* w_scale_ptr, 
         gemm_kernel<CfgSmall, false><<<grid, CfgSmall::kThreads, 0, s>>>(
             packed, w_scale, w_scale_ptr, n, k, q, act_scale, act_sum, m, residual, y, ldy, acc_out, keys, nullptr,
             0.0f, nullptr);
-    } else if ((int64_t)cdiv(n, CfgLarge::BN) * cdiv(m, CfgLarge::BM) < 2 * 256) {
+    } else if ((int64_t)cdiv(n, CfgLarge::BN) * cdiv(m, CfgLarge::BM) < 2 * 256 && k % CfgMid::BK == 0) {
         dim3 grid((n + CfgMid::BN - 1) / CfgMid::BN, (m + CfgMid::BM - 1) / CfgMid::BM);
         gemm_kernel<CfgMid, false><<<grid, CfgMid::kThreads, 0, s>>>(
+            packed, w_scale, w_scale_ptr, n, k, q, act_scale, act_sum, m, residual, y, ldy, acc_out, keys, nullptr,
+            0.0f, nullptr);
+    } else if ((int64_t)cdiv(n, CfgLarge::BN) * cdiv(m, CfgLarge::BM) < 2 * 256) {
+        dim3 grid((n + CfgMid64::BN - 1) / CfgMid64::BN, (m + CfgMid64::BM - 1) / CfgMid64::BM);
+        gemm_kernel<CfgMid64, false><<<grid, CfgMid64::kThreads, 0, s>>>(
             packed, w_scale, w_scale_ptr, n, k, q, act_scale, act_sum, m, residual, y, ldy, acc_out, keys, nullptr,
             0.0f, nullptr);
     } else {

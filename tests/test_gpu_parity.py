@@ -187,12 +187,14 @@ def test_gemv(bl, olib, n, k, m):
 
 # m <= 32 runs the skinny kernels (one or two 32-row tiles per wave, K split
 # over up to 16 waves, ragged K tails); larger m the tiled GEMM: 32 x 256 tiles
-# up to 64 tokens, above that 128 x 320 tiles, or 128 x 160 ones while the
-# 128 x 320 tiling would give fewer than 512 tiles ((2100, 10000): 544 tiles of
-# 128 x 320, ragged in both directions).
+# up to 64 tokens, above that 128 x 320 tiles, or, while the 128 x 320 tiling
+# would give fewer than 512 tiles, 64 x 160 tiles with 128-deep K steps (K a
+# multiple of 128: (130, 200, 640), (257, 2560, 1024)) or 128 x 160 tiles with
+# 64-deep ones ((200, 700, 320)); (2100, 10000): 544 tiles of 128 x 320, ragged
+# in both directions.
 GEMM_CASES = [(1, 16, 64), (5, 100, 192), (32, 2048, 2048), (130, 200, 640), (256, 384, 2560), (37, 2560, 10240),
               (300, 129, 128), (32, 8192, 2048), (64, 50000, 2048), (32, 50000, 2048), (17, 16448, 320),
-              (9, 33, 4160), (24, 700, 8448), (2100, 10000, 64)]
+              (9, 33, 4160), (24, 700, 8448), (2100, 10000, 64), (257, 2560, 1024), (200, 700, 320)]
 
 
 @pytest.mark.parametrize("m,n,k", GEMM_CASES)
@@ -265,7 +267,8 @@ def test_gemm_prefill_full_size_sampled_rows(bl, olib):
 # shapes where interior tiles take it and edge tiles the general one, for both
 # block-tile configurations (m <= 64 and m > 64).
 GEMM_Y_ONLY_CASES = [(256, 640, 256), (300, 1000, 320), (129, 330, 2560), (64, 512, 128), (65, 700, 192),
-                     (40, 257, 64), (2048, 640, 64), (2100, 10000, 64), (2048, 2560, 640)]
+                     (40, 257, 64), (2048, 640, 64), (2100, 10000, 64), (2048, 2560, 640), (257, 2560, 1024),
+                     (1000, 2500, 1152)]
 
 
 @pytest.mark.parametrize("m,n,k", GEMM_Y_ONLY_CASES)
