@@ -145,9 +145,16 @@ def _host(a, dtype, name):
     return a.ctypes.data
 
 
+# The current stream's raw handle straight from torch's C layer (0.1 us), not
+# through a Stream object (about 3 us a call), when this torch build has it.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(stream):
     if stream is not None:
         return stream
+    if _raw_stream is not None:
+        return _raw_stream(torch.cuda.current_device())
     return torch.cuda.current_stream().cuda_stream
 
 
