@@ -29,7 +29,10 @@
 // of that pass from piling onto a handful of addresses. Once a level's
 // candidates number at most 2048, the pass that reads them also copies their
 // keys and weights into LDS, and the deeper levels (and the second selection,
-// while its candidates are among them) run from that list. The kept weight M
+// while its candidates are among them) run from that list; the first
+// selection's second level copies every token whose first digit is at least
+// the chosen one, when they fit, so that the draw (always a kept token) runs
+// from the list too. The kept weight M
 // is read off the first selection (the weight above the kept boundary plus
 // the boundary token's own).
 //
@@ -184,7 +187,8 @@ struct Pick {
 // candidates also copies them into the list.
 template <bool COUNT>
 __device__ Pick select_key(const float* __restrict__ l, const long long* __restrict__ w, int n, long long target,
-                           Shared& sh, unsigned long long& lmask, unsigned long long& lprefix)
+                           Shared& sh, unsigned long long& lmask, unsigned long long& lprefix, int& lfloor,
+                           bool first)
 {
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     unsigned long long prefix = 0, mask = 0;
@@ -202,8 +206,15 @@ __device__ Pick select_key(const float* __restrict__ l, const long long* __restr
                 sh.hw[i] = 0ull;
                 sh.hc[i] = 0u;
             }
-            const bool in_list = (mask & lmask) == lmask && (prefix & lmask) == lprefix;
-            const bool fill = !in_list && cand <= (unsigned int)kCap;
+            // the list holds every token whose first digit is at least lfloor
+            // (lfloor >= 0), or every token matching lprefix under lmask
+            const bool in_list = lfloor >= 0 ? (int)(prefix >> 52) >= lfloor
+                                             : (mask & lmask) == lmask && (prefix & lmask) == lprefix;
+            // the first selection's second level keeps every token at or above
+            // its first digit when they fit: the draw is among them
+            const bool fill_floor = !in_list && first && lv == 1 && above_c + cand <= (unsigned int)kCap;
+            const bool fill = !in_list && (fill_floor || cand <= (unsigned int)kCap);
+            const unsigned long long floor_key = prefix & (0xFFFull << 52);
             if (fill && t == 0) sh.ncand = 0u;
             __syncthreads();
             if (in_list) {
@@ -226,12 +237,12 @@ __device__ Pick select_key(const float* __restrict__ l, const long long* __restr
 #pragma unroll
                     for (int u = 0; u < kB; ++u) key[u] = sort_key(lv[u], i0 + u * kT);
                     if (fill) {
-                        // the candidates (at most kCap) go to the list with their
+                        // the kept tokens (at most kCap) go to the list with their
                         // index; their weights are gathered below in one round
 #pragma unroll
                         for (int u = 0; u < kB; ++u) {
                             const int i = i0 + u * kT;
-                            if (i < n && (key[u] & mask) == prefix) {
+                            if (i < n && (fill_floor ? key[u] >= floor_key : (key[u] & mask) == prefix)) {
                                 const unsigned int slot = atomicAdd(&sh.ncand, 1u);
                                 sh.ck[slot] = key[u];
                                 sh.cw[slot] = i;
@@ -261,12 +272,16 @@ __device__ Pick select_key(const float* __restrict__ l, const long long* __restr
                     for (int i = t; i < nc; i += kT) {
                         const long long wv = w[(int)sh.cw[i]];
                         sh.cw[i] = wv;
-                        const int d = (int)((sh.ck[i] >> shift) & dmask);
-                        atomicAdd(&sh.hw[d], (unsigned long long)wv);
-                        atomicAdd(&sh.hc[d], 1u);
+                        const unsigned long long key = sh.ck[i];
+                        if ((key & mask) == prefix) {  // this level's candidates
+                            const int d = (int)((key >> shift) & dmask);
+                            atomicAdd(&sh.hw[d], (unsigned long long)wv);
+                            atomicAdd(&sh.hc[d], 1u);
+                        }
                     }
                     lmask = mask;
                     lprefix = prefix;
+                    lfloor = fill_floor ? (int)(prefix >> 52) : -1;
                 }
             }
             __syncthreads();
@@ -390,6 +405,7 @@ __global__ __launch_bounds__(kT) void sample_kernel(const float* __restrict__ lo
     const long long total = block_sum_i64(part, sh);  // its barriers also publish w and the bins
 
     unsigned long long lmask = ~0ull, lprefix = 0ull;  // the candidate list: empty
+    int lfloor = -1;
     Pick kept;
     if (TOPP) {
         // min(Z, ceil(p Z)) compared exactly: fl64(Z) may round above Z, and a
@@ -398,9 +414,9 @@ __global__ __launch_bounds__(kT) void sample_kernel(const float* __restrict__ lo
         long long target = tg < 9.0e18 ? (long long)tg : total;
         if (target > total) target = total;
         if (target < 1) target = 1;
-        kept = select_key<false>(l, w, n, target, sh, lmask, lprefix);
+        kept = select_key<false>(l, w, n, target, sh, lmask, lprefix, lfloor, true);
     } else {
-        kept = select_key<true>(l, w, n, k < n ? k : n, sh, lmask, lprefix);
+        kept = select_key<true>(l, w, n, k < n ? k : n, sh, lmask, lprefix, lfloor, true);
     }
     // the kept tokens (keys >= kappa) weigh the tokens above kappa plus kappa's own
     const long long mass = kept.above_w + kept.own_w;
@@ -408,7 +424,7 @@ __global__ __launch_bounds__(kT) void sample_kernel(const float* __restrict__ lo
     const long long r = rd < 0.0 ? 0 : (rd >= (double)mass ? mass - 1 : (long long)rd);
     // the kept tokens are a prefix of the sorted order, so the first token
     // whose cumulative weight reaches r + 1 (<= mass) is a kept one
-    const Pick chosen = select_key<false>(l, w, n, r + 1, sh, lmask, lprefix);
+    const Pick chosen = select_key<false>(l, w, n, r + 1, sh, lmask, lprefix, lfloor, false);
     if (t == 0) out[row] = (int32_t)(0xFFFFFFFFu - (uint32_t)(chosen.key & 0xFFFFFFFFull));
 }
 
