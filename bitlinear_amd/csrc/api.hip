@@ -781,8 +781,8 @@ int bitnet_greedy_step(const uint8_t* embed_table, float s_emb, int64_t vocab, c
 
 size_t bitnet_sample_workspace_bytes(int64_t m, int64_t n)
 {
-    if (m <= 0 || n <= 0 || m > 0x7fffffff || n > 0x7fffffff) return 0;
-    return align_up((size_t)m * (size_t)n * 8, 256);
+    if (m <= 0 || n <= 0 || m > 0x7fffffff || n >= (int64_t)1 << 23) return 0;
+    return bl::sample_workspace_bytes((int)m, (int)n);
 }
 
 namespace {
@@ -808,8 +808,7 @@ int bitnet_sample_topk(const float* logits, int64_t m, int64_t n, int64_t k, flo
     if (rc != BL_OK) return rc;
     if (k < 1) return BL_ERR_VALUE;
     const int kk = (int)std::min<int64_t>(k, n);
-    return bl::launch_sample(false, logits, (int)m, (int)n, kk, 1.0f, temperature, u, token,
-                             static_cast<long long*>(workspace), as_stream(stream));
+    return bl::launch_sample(false, logits, (int)m, (int)n, kk, 1.0f, temperature, u, token, workspace, as_stream(stream));
 }
 
 int bitnet_sample_topp(const float* logits, int64_t m, int64_t n, float p, float temperature, const double* u,
@@ -818,8 +817,7 @@ int bitnet_sample_topp(const float* logits, int64_t m, int64_t n, float p, float
     const int rc = sample_check(logits, m, n, temperature, u, token, workspace, workspace_bytes);
     if (rc != BL_OK) return rc;
     if (!(p > 0.0f) || !(p < INFINITY)) return BL_ERR_VALUE;
-    return bl::launch_sample(true, logits, (int)m, (int)n, 1, p, temperature, u, token,
-                             static_cast<long long*>(workspace), as_stream(stream));
+    return bl::launch_sample(true, logits, (int)m, (int)n, 1, p, temperature, u, token, workspace, as_stream(stream));
 }
 
 }  // extern "C"

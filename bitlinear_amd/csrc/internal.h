@@ -150,9 +150,11 @@ int launch_append(const int32_t* next, int m, int32_t* hist, int stride, int32_t
                   hipStream_t s);
 
 // Top-k (topp false, k) or nucleus (topp true, p) sampling of m rows of n
-// logits with the caller's uniforms u (sample.hip); wbuf: m * n int64.
+// logits with the caller's uniforms u (sample.hip); workspace:
+// sample_workspace_bytes(m, n) bytes, 256-aligned.
+size_t sample_workspace_bytes(int m, int n);
 int launch_sample(bool topp, const float* logits, int m, int n, int k, float p, float temperature, const double* u,
-                  int32_t* out, long long* wbuf, hipStream_t s);
+                  int32_t* out, void* workspace, hipStream_t s);
 
 // Single-token attention of m sequences at position pos (attn.hip): RoPE of q
 // and k from qkv rows [q | k | v] (row stride ldq), k and v appended to the

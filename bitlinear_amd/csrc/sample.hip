@@ -23,7 +23,9 @@
 // finds the block and then the digit at which the running total crosses the
 // target (lane prefix sums by DPP row shifts and broadcasts; the sums are
 // integers, so their order does not matter). The first level's sums come
-// from the pass that computes the weights and serve both selections; the
+// from the launch that computes the weights (up to 64 workgroups per row, each
+// on a slice, their histograms and totals added into the row's by exact
+// integer atomics) and serve both selections; the
 // twelve-bit first digit (sign, exponent, three mantissa bits of the logit)
 // spreads logits of a few units over many bins, which keeps the LDS atomics
 // of that pass from piling onto a handful of addresses. Once a level's
@@ -42,6 +44,8 @@
 // by Horner's rule, then the exact scaling by 2^k. Every operation is a single
 // IEEE-rounded fp64 operation (no contraction), so its value does not depend
 // on the hardware's own exp.
+#include <algorithm>
+
 #include "internal.h"
 
 namespace bl {
@@ -120,32 +124,7 @@ __device__ __forceinline__ long long wave_sum_i64(long long v)
     return v;
 }
 
-// Workgroup sum of an int64 (exact), returned to every thread.
-__device__ long long block_sum_i64(long long v, Shared& sh)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    v = wave_sum_i64(v);
-    __syncthreads();  // sh.red is free
-    if (lane == 0) sh.red[wave][0] = v;
-    __syncthreads();
-    long long t = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) t += sh.red[w][0];
-    return t;
-}
 
-__device__ float block_max(float v, Shared& sh)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    if (lane == 0) sh.redf[wave] = v;
-    __syncthreads();
-    float t = sh.redf[0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) t = fmaxf(t, sh.redf[w]);
-    return t;
-}
 
 // Lane i receives lane i - n's value of its row of 16 (n = 1, 2, 4, 8), or a
 // row broadcast (lane 15 into rows 1 and 3, then lane 31 into rows 2 and 3);
@@ -358,40 +337,82 @@ __device__ Pick select_key(const float* __restrict__ l, const long long* __restr
     return out;
 }
 
-template <bool TOPP>
-__global__ __launch_bounds__(kT) void sample_kernel(const float* __restrict__ logits, int n, int k, float p, float temp,
-                                                    const double* __restrict__ u, int32_t* __restrict__ out,
-                                                    long long* __restrict__ wbuf)
+// ---- the row maximum, the weights and the first-level histogram over P
+// workgroups per row (P = splits: a slice of about n / P tokens each) -----------
+// The fp64 weights (about fifty fp64 instructions per token) dominate a row;
+// spread over P CUs they take a P-th of the time. Maxima and the integer sums
+// are exact in any order, so the result does not depend on P.
+constexpr int kMaxSplits = 64;
+
+struct SampleWs {
+    float* maxp;                // [m][kMaxSplits] slice maxima
+    unsigned long long* h0w;    // [m][kBins0] first-level weight sums
+    unsigned int* h0c;          // [m][kBins0] first-level counts
+    long long* total;           // [m] total weight
+};
+
+// Slice maxima; each workgroup also zeroes its share of its row's histogram.
+__global__ __launch_bounds__(256) void sample_max_kernel(const float* __restrict__ logits, int n, int splits,
+                                                         SampleWs ws)
 {
-    __shared__ Shared sh;
-    const int row = blockIdx.x, t = threadIdx.x;
+    __shared__ float red[4];
+    const int row = blockIdx.x / splits, sp = blockIdx.x - row * splits, t = threadIdx.x;
+    const int per = (n + splits - 1) / splits, i0 = sp * per, i1 = min(i0 + per, n);
+    const float* l = logits + (size_t)row * n;
+    float lm = -INFINITY;
+    for (int i = i0 + t; i < i1; i += 256) lm = fmaxf(lm, l[i]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) lm = fmaxf(lm, __shfl_xor(lm, off, 64));
+    if ((t & 63) == 0) red[t >> 6] = lm;
+    __syncthreads();
+    if (t == 0) ws.maxp[(size_t)row * kMaxSplits + sp] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const int bper = (kBins0 + splits - 1) / splits, b0 = sp * bper, b1 = min(b0 + bper, kBins0);
+    for (int b = b0 + t; b < b1; b += 256) {
+        ws.h0w[(size_t)row * kBins0 + b] = 0ull;
+        ws.h0c[(size_t)row * kBins0 + b] = 0u;
+    }
+    if (sp == 0 && t == 0) ws.total[row] = 0;
+}
+
+__device__ __forceinline__ float row_max(const SampleWs& ws, int row, int splits)
+{
+    float m = -INFINITY;
+    for (int j = 0; j < splits; ++j) m = fmaxf(m, ws.maxp[(size_t)row * kMaxSplits + j]);
+    return m;
+}
+
+struct WeightsShared {
+    unsigned long long h0w[kBins0];
+    unsigned int h0c[kBins0];
+    long long red[kWaves];
+};
+
+// A slice's weights (stored), its first-level histogram (in LDS, then added to
+// the row's) and its total weight.
+__global__ __launch_bounds__(kT) void sample_weights_kernel(const float* __restrict__ logits, int n, int splits,
+                                                            float temp, long long* __restrict__ wbuf, SampleWs ws)
+{
+    __shared__ WeightsShared sh;
+    const int row = blockIdx.x / splits, sp = blockIdx.x - row * splits, t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    const int per = (n + splits - 1) / splits, i0 = sp * per, i1 = min(i0 + per, n);
     const float* l = logits + (size_t)row * n;
     long long* w = wbuf + (size_t)row * n;
-
     for (int i = t; i < kBins0; i += kT) {
         sh.h0w[i] = 0ull;
         sh.h0c[i] = 0u;
     }
-    float lm = -INFINITY;
-    for (int i0 = t; i0 < n; i0 += kB * kT) {
-        float lv[kB];
-#pragma unroll
-        for (int u = 0; u < kB; ++u) lv[u] = i0 + u * kT < n ? l[i0 + u * kT] : -INFINITY;
-#pragma unroll
-        for (int u = 0; u < kB; ++u) lm = fmaxf(lm, lv[u]);
-    }
-    const float lmax = block_max(lm, sh);  // its barrier also publishes the cleared bins
-
-    // weights, their total and the first-level histogram in one pass
+    const float lmax = row_max(ws, row, splits);
+    __syncthreads();
     long long part = 0;
-    for (int i0 = t; i0 < n; i0 += kB * kT) {
+    for (int ib = i0 + t; ib < i1; ib += kB * kT) {
         float lv[kB];
 #pragma unroll
-        for (int u = 0; u < kB; ++u) lv[u] = i0 + u * kT < n ? l[i0 + u * kT] : 0.0f;
+        for (int u = 0; u < kB; ++u) lv[u] = ib + u * kT < i1 ? l[ib + u * kT] : 0.0f;
 #pragma unroll
         for (int u = 0; u < kB; ++u) {
-            const int i = i0 + u * kT;
-            if (i < n) {
+            const int i = ib + u * kT;
+            if (i < i1) {
                 const double x = ((double)lv[u] - (double)lmax) / (double)temp;
                 const long long q = (long long)rint(ldexp(exp_neg(x), 40));
                 w[i] = q;
@@ -402,7 +423,38 @@ __global__ __launch_bounds__(kT) void sample_kernel(const float* __restrict__ lo
             }
         }
     }
-    const long long total = block_sum_i64(part, sh);  // its barriers also publish w and the bins
+    part = wave_sum_i64(part);
+    if (lane == 0) sh.red[wave] = part;
+    __syncthreads();
+    if (t == 0) {
+        long long tot = 0;
+        for (int j = 0; j < kWaves; ++j) tot += sh.red[j];
+        atomicAdd(reinterpret_cast<unsigned long long*>(ws.total + row), (unsigned long long)tot);
+    }
+    for (int b = t; b < kBins0; b += kT) {
+        const unsigned int c = sh.h0c[b];
+        if (c) {
+            atomicAdd(ws.h0w + (size_t)row * kBins0 + b, sh.h0w[b]);
+            atomicAdd(ws.h0c + (size_t)row * kBins0 + b, c);
+        }
+    }
+}
+
+template <bool TOPP>
+__global__ __launch_bounds__(kT) void sample_kernel(const float* __restrict__ logits, int n, int splits, int k,
+                                                    float p, const double* __restrict__ u, int32_t* __restrict__ out,
+                                                    long long* __restrict__ wbuf, SampleWs ws)
+{
+    __shared__ Shared sh;
+    const int row = blockIdx.x, t = threadIdx.x;
+    const float* l = logits + (size_t)row * n;
+    const long long* w = wbuf + (size_t)row * n;
+    for (int i = t; i < kBins0; i += kT) {
+        sh.h0w[i] = ws.h0w[(size_t)row * kBins0 + i];
+        sh.h0c[i] = ws.h0c[(size_t)row * kBins0 + i];
+    }
+    const long long total = ws.total[row];
+    __syncthreads();
 
     unsigned long long lmask = ~0ull, lprefix = 0ull;  // the candidate list: empty
     int lfloor = -1;
@@ -430,13 +482,40 @@ __global__ __launch_bounds__(kT) void sample_kernel(const float* __restrict__ lo
 
 }  // namespace
 
-int launch_sample(bool topp, const float* logits, int m, int n, int k, float p, float temperature, const double* u,
-                  int32_t* out, long long* wbuf, hipStream_t s)
+// Workspace of launch_sample: the weights, then the slice maxima, the first-level
+// histograms and the totals (each part 256-aligned).
+size_t sample_workspace_bytes(int m, int n)
 {
+    auto al = [](size_t b) { return (b + 255) / 256 * 256; };
+    return al((size_t)m * n * 8) + al((size_t)m * kMaxSplits * 4) + al((size_t)m * kBins0 * 8) +
+           al((size_t)m * kBins0 * 4) + al((size_t)m * 8);
+}
+
+int launch_sample(bool topp, const float* logits, int m, int n, int k, float p, float temperature, const double* u,
+                  int32_t* out, void* workspace, hipStream_t s)
+{
+    auto al = [](size_t b) { return (b + 255) / 256 * 256; };
+    char* base = static_cast<char*>(workspace);
+    long long* wbuf = reinterpret_cast<long long*>(base);
+    size_t off = al((size_t)m * n * 8);
+    SampleWs ws;
+    ws.maxp = reinterpret_cast<float*>(base + off);
+    off += al((size_t)m * kMaxSplits * 4);
+    ws.h0w = reinterpret_cast<unsigned long long*>(base + off);
+    off += al((size_t)m * kBins0 * 8);
+    ws.h0c = reinterpret_cast<unsigned int*>(base + off);
+    off += al((size_t)m * kBins0 * 4);
+    ws.total = reinterpret_cast<long long*>(base + off);
+    // workgroups per row: the rows over about 256 CUs, at least 1024 tokens each
+    int splits = std::max(1, std::min(kMaxSplits, 256 / std::max(m, 1)));
+    splits = std::max(1, std::min(splits, (n + kT - 1) / kT));
+    const int g = m * splits;
+    sample_max_kernel<<<g, 256, 0, s>>>(logits, n, splits, ws);
+    sample_weights_kernel<<<g, kT, 0, s>>>(logits, n, splits, temperature, wbuf, ws);
     if (topp)
-        sample_kernel<true><<<m, kT, 0, s>>>(logits, n, k, p, temperature, u, out, wbuf);
+        sample_kernel<true><<<m, kT, 0, s>>>(logits, n, splits, k, p, u, out, wbuf, ws);
     else
-        sample_kernel<false><<<m, kT, 0, s>>>(logits, n, k, p, temperature, u, out, wbuf);
+        sample_kernel<false><<<m, kT, 0, s>>>(logits, n, splits, k, p, u, out, wbuf, ws);
     return hipGetLastError() == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
 }
 

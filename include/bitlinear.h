@@ -470,14 +470,18 @@ int bitnet_greedy_step(const uint8_t *embed_table, float s_emb, int64_t vocab,
  *     weight (the smallest set with probability >= p);
  *   - with M the kept weight and r = min(M - 1, max(0, floor(fl64(u * M)))), the
  *     chosen token is the first kept token whose cumulative weight exceeds r.
- * Each row is one 1024-thread workgroup: weights, then radix selections over
- * 64-bit (logit, index) keys whose per-digit weight sums are exact integers.
+ * Three launches on the stream: the row maxima (per slice), the weights and
+ * first-level histograms (up to 64 workgroups per row, 256 in all, merged by
+ * exact integer atomics), then one 1024-thread workgroup per row for the radix
+ * selections over 64-bit (logit, index) keys whose per-digit weight sums are
+ * exact integers.
  *   logits    : device fp32 [m][n] (finite), 1 <= n < 2^23 (so the total
  *               weight, at most n 2^40, fits in an int64).
  *   temperature : > 0 and finite.  k >= 1 (k > n keeps all); p > 0 (p >= 1 keeps
  *               every token of nonzero weight).
  *   token     : device int32 [m].
- *   workspace : bitnet_sample_workspace_bytes(m, n) bytes (the weights), 256-aligned.
+ *   workspace : bitnet_sample_workspace_bytes(m, n) bytes (the weights, slice maxima,
+ *               histograms and totals), 256-aligned; no contents carried between calls.
  * Errors: NULL, SHAPE, ALIGN, VALUE, WORKSPACE, LAUNCH. */
 size_t bitnet_sample_workspace_bytes(int64_t m, int64_t n);
 int bitnet_sample_topk(const float *logits, int64_t m, int64_t n, int64_t k, float temperature, const double *u,
