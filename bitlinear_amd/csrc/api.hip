@@ -272,17 +272,20 @@ StepLayout step_layout(int64_t m, int64_t d, int64_t f, int64_t vocab)
 }
 
 // The LM head with the repetition penalty and the greedy choice (m <= 32,
-// validated): bitmaps, the skinny product with penalised fp32 keys, the
-// per-token reduction into next.
+// validated): bitmaps (unless bits_ready: the caller built them in the head's
+// workspace), the skinny product with penalised fp32 keys, the per-token
+// reduction into next -- which, given app_hist, also appends next to the
+// histories.
 int greedy_head_launch(const uint8_t* head, float s_head, int64_t n, int64_t k, const int8_t* q,
                        const float* act_scale, const int32_t* act_sum, int64_t m, const int32_t* hist,
                        int64_t hist_stride, const int32_t* hist_len, float penalty, float* logits, int32_t* next,
-                       void* ws, hipStream_t s)
+                       void* ws, hipStream_t s, bool bits_ready = false, int32_t* app_hist = nullptr,
+                       int32_t* app_len = nullptr)
 {
     const HeadLayout L = head_layout(m, n);
     uint32_t* bits = at<uint32_t>(ws, L.bits);
     unsigned long long* keys = at<unsigned long long>(ws, L.keys);
-    int rc = bl::launch_penalty_bits(hist, (int)hist_stride, hist_len, (int)n, (int)m, bits, s);
+    int rc = bits_ready ? BL_OK : bl::launch_penalty_bits(hist, (int)hist_stride, hist_len, (int)n, (int)m, bits, s);
     if (rc) return rc;
     bl::SkinnyArgs a =
         skinny(head, nullptr, s_head, 1, (int)n, (int)k, q, act_scale, act_sum, (int)m, nullptr, logits, (int)n);
@@ -292,7 +295,8 @@ int greedy_head_launch(const uint8_t* head, float s_head, int64_t n, int64_t k, 
     a.penalty = penalty;
     rc = bl::launch_skinny(a, true, s);
     if (rc) return rc;
-    return bl::launch_tile_argmax(keys, bl::skinny_tiles((int)n, false), (int)m, next, s);
+    return bl::launch_tile_argmax(keys, bl::skinny_tiles((int)n, false), (int)m, next, s, app_hist, (int)hist_stride,
+                                  app_len);
 }
 
 // The launch-per-step layer stream (any m). Without attn, the o projection of
@@ -757,8 +761,11 @@ int bitnet_greedy_step(const uint8_t* embed_table, float s_emb, int64_t vocab, c
     if (workspace_bytes < bitnet_greedy_step_workspace_bytes(m, d, f, vocab)) return BL_ERR_WORKSPACE;
     const StepLayout L = step_layout(m, d, f, vocab);
     const hipStream_t s = as_stream(stream);
-    // 1. embedding of the current tokens
-    int rc = bl::launch_embed(embed_table, s_emb, (int)vocab, (int)d, tokens, (int)m, x, s);
+    // 1. embedding of the current tokens; the same launch builds the head's
+    // penalty bitmaps (the histories do not change before the head reads them)
+    const bl::PenaltyRows pen = {hist, (int)hist_stride, hist_len,
+                                 at<uint32_t>(at<void>(workspace, L.head), head_layout(m, vocab).bits)};
+    int rc = bl::launch_embed(embed_table, s_emb, (int)vocab, (int)d, tokens, (int)m, x, s, &pen);
     if (rc) return rc;
     // 2. the layer stream over x, in place (its own checks run here)
     rc = bitnet_decode_stream(weights, scales, gains, z, n_layers, m, d, f, eps, x, nullptr,
@@ -770,11 +777,11 @@ int bitnet_greedy_step(const uint8_t* embed_table, float s_emb, int64_t vocab, c
     int32_t* qsf = at<int32_t>(workspace, L.qs);
     rc = bl::launch_quant_act(x, g_final, eps, (int)m, (int)d, qf, sf, qsf, s);
     if (rc) return rc;
-    rc = greedy_head_launch(head, s_head, vocab, d, qf, sf, qsf, m, hist, hist_stride, hist_len, penalty, logits,
-                            tokens, at<void>(workspace, L.head), s);
-    if (rc) return rc;
-    // 5. the chosen tokens join the histories (the next step embeds them)
-    return bl::launch_append(tokens, (int)m, hist, (int)hist_stride, hist_len, nullptr, s);
+    // 5. the chosen tokens join the histories (the next step embeds them): in the
+    // launch that reduces the head's keys
+    return greedy_head_launch(head, s_head, vocab, d, qf, sf, qsf, m, hist, hist_stride, hist_len, penalty, logits,
+                              tokens, at<void>(workspace, L.head), s, true, hist_stride > 0 ? hist : nullptr,
+                              hist_stride > 0 ? hist_len : nullptr);
 }
 
 // ---- top-k and nucleus sampling --------------------------------------------------

@@ -16,18 +16,42 @@ namespace {
 
 constexpr int kEmbedThreads = 256;
 
+// Per sequence r: clear its bitmap of words 32-bit words, then set the bit of
+// every history id in [0, n) (hist_len clamped to [0, stride]). All threads
+// of the workgroup (kThreads of them) take part.
+template <int kThreads>
+__device__ __forceinline__ void penalty_bits_row(int r, const int32_t* __restrict__ hist, int stride,
+                                                 const int32_t* __restrict__ hist_len, int n, int words,
+                                                 uint32_t* __restrict__ bits)
+{
+    uint32_t* b = bits + (size_t)r * words;
+    for (int i = threadIdx.x; i < words; i += kThreads) b[i] = 0u;
+    __syncthreads();  // the clears are done before any bit is set
+    int len = stride > 0 ? hist_len[r] : 0;
+    len = len < 0 ? 0 : (len > stride ? stride : len);
+    for (int i = threadIdx.x; i < len; i += kThreads) {
+        const int v = hist[(size_t)r * stride + i];
+        if (v >= 0 && v < n) atomicOr(b + (v >> 5), 1u << (v & 31));
+    }
+}
+
 // Row tokens[r] of the packed table, dequantized: t / s_e, i.e. +inv, -inv or
 // +0 with inv = fl32(1 / s_e) (the correctly rounded quotient of +-1 by s_e is
 // +-inv). Each thread expands one 16-byte chunk (64 values) per step. A token
-// outside [0, vocab) gives a zero row.
+// outside [0, vocab) gives a zero row. With bits, the same workgroup also
+// builds sequence r's penalty bitmap (the history does not change before the
+// LM head reads it), which saves the head a launch.
 __global__ __launch_bounds__(kEmbedThreads) void embed_kernel(const uint8_t* __restrict__ table, float s_e,
                                                               int vocab, int d, const int32_t* __restrict__ tokens,
-                                                              float* __restrict__ x)
+                                                              float* __restrict__ x, const int32_t* __restrict__ hist,
+                                                              int stride, const int32_t* __restrict__ hist_len,
+                                                              int words, uint32_t* __restrict__ bits)
 {
     const int r = blockIdx.x;
     const int tok = tokens[r];
     float* xr = x + (size_t)r * d;
     const int chunks = d / 64;
+    if (bits) penalty_bits_row<kEmbedThreads>(r, hist, stride, hist_len, vocab, words, bits);
     if (tok < 0 || tok >= vocab) {
         for (int i = threadIdx.x; i < d / 4; i += kEmbedThreads)
             reinterpret_cast<float4*>(xr)[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -54,22 +78,11 @@ __global__ __launch_bounds__(kEmbedThreads) void embed_kernel(const uint8_t* __r
     }
 }
 
-// Per sequence r: clear its bitmap of words 32-bit words, then set the bit of
-// every history id in [0, n) (hist_len clamped to [0, stride]).
 __global__ __launch_bounds__(256) void penalty_bits_kernel(const int32_t* __restrict__ hist, int stride,
                                                            const int32_t* __restrict__ hist_len, int n, int words,
                                                            uint32_t* __restrict__ bits)
 {
-    const int r = blockIdx.x;
-    uint32_t* b = bits + (size_t)r * words;
-    for (int i = threadIdx.x; i < words; i += 256) b[i] = 0u;
-    __syncthreads();  // the clears are done before any bit is set
-    int len = stride > 0 ? hist_len[r] : 0;
-    len = len < 0 ? 0 : (len > stride ? stride : len);
-    for (int i = threadIdx.x; i < len; i += 256) {
-        const int v = hist[(size_t)r * stride + i];
-        if (v >= 0 && v < n) atomicOr(b + (v >> 5), 1u << (v & 31));
-    }
+    penalty_bits_row<256>(blockIdx.x, hist, stride, hist_len, n, words, bits);
 }
 
 // After the choice: hist[r][hist_len[r]] = next[r] and hist_len[r] + 1 while
@@ -93,9 +106,11 @@ __global__ void append_kernel(const int32_t* __restrict__ next, int m, int32_t* 
 }  // namespace
 
 int launch_embed(const uint8_t* table, float s_e, int vocab, int d, const int32_t* tokens, int m, float* x,
-                 hipStream_t s)
+                 hipStream_t s, const PenaltyRows* pen)
 {
-    embed_kernel<<<m, kEmbedThreads, 0, s>>>(table, s_e, vocab, d, tokens, x);
+    embed_kernel<<<m, kEmbedThreads, 0, s>>>(table, s_e, vocab, d, tokens, x, pen ? pen->hist : nullptr,
+                                             pen ? pen->stride : 0, pen ? pen->hist_len : nullptr,
+                                             penalty_words(vocab), pen ? pen->bits : nullptr);
     return hipGetLastError() == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
 }
 

@@ -129,7 +129,11 @@ struct SkinnyArgs {
 };
 int launch_skinny(const SkinnyArgs& a, bool natural_q, hipStream_t s);
 int skinny_tiles(int n, bool pair);
-int launch_tile_argmax(const unsigned long long* tile_keys, int tiles, int m, int32_t* idx, hipStream_t s);
+// Per token the column of the largest key; with hist, the chosen token is
+// also appended to its sequence's history (hist[r][hist_len[r]], hist_len[r]
+// + 1, while there is room).
+int launch_tile_argmax(const unsigned long long* tile_keys, int tiles, int m, int32_t* idx, hipStream_t s,
+                       int32_t* hist = nullptr, int stride = 0, int32_t* hist_len = nullptr);
 
 // The FFN's gate and up projections as one MFMA GEMM over the stacked weights,
 // with h[m][f] = relu(gate)^2 * up in the epilogue (any m; used above 32
@@ -142,8 +146,16 @@ int launch_gemm_gateup(const uint8_t* w_gate, float s_gate, const uint8_t* w_up,
 // Greedy decoding around the stream (greedy.hip). penalty_words(n): 32-bit
 // words of one sequence's bitmap over n vocabulary entries.
 inline int penalty_words(int n) { return (n + 31) / 32; }
+// The penalty bitmaps of the sequences' histories (bits: m rows of
+// penalty_words(vocab) words), built by launch_embed's workgroups when given.
+struct PenaltyRows {
+    const int32_t* hist;
+    int stride;
+    const int32_t* hist_len;
+    uint32_t* bits;
+};
 int launch_embed(const uint8_t* table, float s_e, int vocab, int d, const int32_t* tokens, int m, float* x,
-                 hipStream_t s);
+                 hipStream_t s, const PenaltyRows* pen = nullptr);
 int launch_penalty_bits(const int32_t* hist, int stride, const int32_t* hist_len, int n, int m, uint32_t* bits,
                         hipStream_t s);
 int launch_append(const int32_t* next, int m, int32_t* hist, int stride, int32_t* hist_len, int32_t* tokens,

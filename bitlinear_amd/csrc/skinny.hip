@@ -254,8 +254,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyArgs a)
 }
 
 // Per token, the largest of the workgroups' keys; its low word gives the column.
+// With hist, the chosen column also joins the token's history.
 __global__ __launch_bounds__(256) void tile_argmax_kernel(const unsigned long long* __restrict__ keys, int tiles,
-                                                          int32_t* __restrict__ idx)
+                                                          int32_t* __restrict__ idx, int32_t* __restrict__ hist,
+                                                          int stride, int32_t* __restrict__ hist_len)
 {
     __shared__ unsigned long long wbest[4];
     const int tok = blockIdx.x;
@@ -274,7 +276,15 @@ __global__ __launch_bounds__(256) void tile_argmax_kernel(const unsigned long lo
     if (threadIdx.x == 0) {
 #pragma unroll
         for (int w = 1; w < 4; ++w) best = wbest[w] > best ? wbest[w] : best;
-        idx[tok] = (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
+        const int32_t c = (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
+        idx[tok] = c;
+        if (hist && hist_len) {
+            const int len = hist_len[tok];
+            if (len >= 0 && len < stride) {
+                hist[(size_t)tok * stride + len] = c;
+                hist_len[tok] = len + 1;
+            }
+        }
     }
 }
 
@@ -339,9 +349,10 @@ int launch_skinny(const SkinnyArgs& a, bool natural_q, hipStream_t s)
     return natural_q ? launch_nb<1, false, true>(a, s) : launch_nb<1, false, false>(a, s);
 }
 
-int launch_tile_argmax(const unsigned long long* tile_keys, int tiles, int m, int32_t* idx, hipStream_t s)
+int launch_tile_argmax(const unsigned long long* tile_keys, int tiles, int m, int32_t* idx, hipStream_t s,
+                       int32_t* hist, int stride, int32_t* hist_len)
 {
-    tile_argmax_kernel<<<m, 256, 0, s>>>(tile_keys, tiles, idx);
+    tile_argmax_kernel<<<m, 256, 0, s>>>(tile_keys, tiles, idx, hist, stride, hist_len);
     return hipGetLastError() == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
 }
 
