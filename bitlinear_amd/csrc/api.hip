@@ -287,6 +287,14 @@ int greedy_head_launch(const uint8_t* head, float s_head, int64_t n, int64_t k, 
     unsigned long long* keys = at<unsigned long long>(ws, L.keys);
     int rc = bits_ready ? BL_OK : bl::launch_penalty_bits(hist, (int)hist_stride, hist_len, (int)n, (int)m, bits, s);
     if (rc) return rc;
+    if (m == 1) {
+        // one token: a GEMV streams the head at the GEMV's rate
+        int tiles = 0;
+        rc = bl::launch_head_gemv(head, s_head, (int)n, (int)k, q, act_scale, act_sum, bits, penalty, logits, keys,
+                                  (int)((n + 31) / 32), &tiles, s);
+        if (rc) return rc;
+        return bl::launch_tile_argmax(keys, tiles, 1, next, s, app_hist, (int)hist_stride, app_len);
+    }
     bl::SkinnyArgs a =
         skinny(head, nullptr, s_head, 1, (int)n, (int)k, q, act_scale, act_sum, (int)m, nullptr, logits, (int)n);
     a.tile_keys = keys;

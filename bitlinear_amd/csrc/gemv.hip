@@ -17,12 +17,12 @@
 // subtracted once per row. The partial sums are reduced across the L lanes with
 // xor shuffles, and the group's first lane applies the single fp32 rescale.
 #include "internal.h"
+#include "ternary.h"
 #include "wave_quant.h"
 
 namespace bl {
 namespace {
 
-constexpr uint32_t kCodeMask = 0x03030303u;
 constexpr int kMaxChunksPerLane = 8;
 constexpr int kFwdMaxK = 4096;         // longest row of the one-wave quant + GEMV
 constexpr int kFwdBlockMaxK = 16384;   // ... and of the 512-thread form
@@ -191,6 +191,57 @@ __global__ __launch_bounds__(64) void gemv_kernel(const uint8_t* __restrict__ pa
             }
         }
     }
+}
+
+// ---- the LM head of one token with the repetition penalty and greedy keys ---
+// gemv_kernel's product with the greedy head's epilogue ("BitNet Model -
+// Complete Inference Pipeline", "GPU Argmax": repetition penalty, then the
+// argmax): the logit (acc - sum q) / (s_a s_w) of a column whose bit is set in
+// the penalty bitmap becomes l / penalty if positive, else l * penalty; each
+// workgroup writes the largest fp32 argmax key of its columns to tile_keys
+// (reduced by tile_argmax_kernel), and the logits to y if given. One token:
+// the weights stream at the GEMV's rate, where the MFMA skinny product uses one
+// of its 32 rows.
+template <int L>
+__global__ __launch_bounds__(64) void head_gemv_kernel(const uint8_t* __restrict__ packed, float w_scale, int n, int k,
+                                                       const int8_t* __restrict__ q,
+                                                       const float* __restrict__ act_scale,
+                                                       const int32_t* __restrict__ act_sum,
+                                                       const uint32_t* __restrict__ pen_bits, float penalty,
+                                                       float* __restrict__ y, unsigned long long* __restrict__ tile_keys)
+{
+    constexpr int R = 64 / L;
+    const int lane = threadIdx.x;
+    const int g = lane / L, j = lane % L;
+    const int chunks = k / 64;
+    const size_t row_bytes = (size_t)k / 4;
+    uint32_t qreg[kMaxChunksPerLane][16];
+    load_qreg<L, 1>(q, j, chunks, qreg);
+    const float inv = 1.0f / (act_scale[0] * w_scale);
+    const int qs = act_sum[0];
+    unsigned long long best = 0;
+    for (int base = blockIdx.x * R; base < n; base += gridDim.x * R) {
+        const int row = base + g;
+        const bool valid = row < n;
+        uint4 w[kMaxChunksPerLane];
+        load_row<L>(packed + (size_t)row * row_bytes, valid, j, chunks, w);
+        int acc[1];
+        dot_row<L, 1>(w, j, chunks, q, k, qreg, acc);
+        acc[0] = group_sum<L>(acc[0]);
+        if (valid && j == 0) {
+            float v = (float)(acc[0] - qs) * inv;
+            if (pen_bits && ((pen_bits[row >> 5] >> (row & 31)) & 1u)) v = v > 0.0f ? v / penalty : v * penalty;
+            if (y) y[row] = v;
+            const unsigned long long key = argmax_key_f32(v, row);
+            best = key > best ? key : best;
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const unsigned long long other = __shfl_xor(best, off, 64);
+        best = other > best ? other : best;
+    }
+    if (lane == 0) tile_keys[blockIdx.x] = best;
 }
 
 // ---- [RMSNorm +] quant + GEMV of one token in one launch -------------------
@@ -548,6 +599,27 @@ int launch_gemv(const uint8_t* packed, float w_scale, const float* w_scale_ptr, 
                                             y, acc_out)
     BL_DISPATCH_L(BL_LAUNCH)
 #undef BL_LAUNCH
+    return hipGetLastError() == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
+}
+
+int launch_head_gemv(const uint8_t* packed, float w_scale, int n, int k, const int8_t* q, const float* act_scale,
+                     const int32_t* act_sum, const uint32_t* pen_bits, float penalty, float* y,
+                     unsigned long long* tile_keys, int max_tiles, int* tiles, hipStream_t s)
+{
+    const int lanes = pick_lanes(k);
+    int grid = grid_for(n, lanes);
+    if (grid > max_tiles) grid = max_tiles;
+    *tiles = grid;
+#define BL_HEAD(LV)                                                                                          \
+    head_gemv_kernel<LV><<<grid, 64, 0, s>>>(packed, w_scale, n, k, q, act_scale, act_sum, pen_bits, penalty, y, \
+                                             tile_keys)
+    switch (lanes) {
+    case 8: BL_HEAD(8); break;
+    case 16: BL_HEAD(16); break;
+    case 32: BL_HEAD(32); break;
+    default: BL_HEAD(64); break;
+    }
+#undef BL_HEAD
     return hipGetLastError() == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
 }
 

@@ -129,6 +129,13 @@ struct SkinnyArgs {
 };
 int launch_skinny(const SkinnyArgs& a, bool natural_q, hipStream_t s);
 int skinny_tiles(int n, bool pair);
+// The LM head of one token (m == 1) with the repetition penalty (pen_bits: the
+// sequence's bitmap, or null) as a GEMV: each of the *tiles (<= max_tiles)
+// workgroups writes its largest penalised fp32 argmax key to tile_keys, and
+// the logits go to y if given (gemv.hip).
+int launch_head_gemv(const uint8_t* packed, float w_scale, int n, int k, const int8_t* q, const float* act_scale,
+                     const int32_t* act_sum, const uint32_t* pen_bits, float penalty, float* y,
+                     unsigned long long* tile_keys, int max_tiles, int* tiles, hipStream_t s);
 // Per token the column of the largest key; with hist, the chosen token is
 // also appended to its sequence's history (hist[r][hist_len[r]], hist_len[r]
 // + 1, while there is room).

@@ -402,8 +402,9 @@ int bitnet_embed(const uint8_t *table, float s_emb, int64_t vocab, int64_t d, co
  *   to [0, hist_stride]);
  *   next_token[r] = the lowest c holding the largest penalised logit.
  * It runs as three launches on the stream: the per-sequence penalty bitmaps,
- * the skinny MFMA product whose epilogue penalises and forms fp32 argmax keys
- * (no logits need to be written), and the per-sequence key reduction.
+ * the product whose epilogue penalises and forms fp32 argmax keys (no logits
+ * need to be written; one sequence: a GEMV, several: the skinny MFMA
+ * product), and the per-sequence key reduction.
  *   head, s_head, n, k : the LM head, packed [n][k/4] (n = vocabulary).
  *   q, act_scale, act_sum : the final-norm quant of the hidden states.
  *   hist      : device int32 [m][hist_stride] (NULL when hist_stride == 0);

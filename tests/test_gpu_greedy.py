@@ -79,8 +79,10 @@ def _head_case(bl, olib, m, n, k, stride, penalty, seed, ties=False):
 
 @pytest.mark.parametrize("m,n,k,stride,penalty", [(1, 50000, 2560, 64, 1.1), (32, 50000, 2048, 48, 1.1),
                                                    (7, 3000, 256, 5, 1.3), (3, 257, 64, 0, 1.1),
-                                                   (32, 1000, 128, 200, 1.0), (5, 999, 192, 9, 2.0)])
+                                                   (32, 1000, 128, 200, 1.0), (5, 999, 192, 9, 2.0),
+                                                   (1, 999, 192, 0, 1.1), (1, 7, 64, 3, 2.0)])
 def test_greedy_head(bl, olib, m, n, k, stride, penalty):
+    """m = 1 runs the head as a GEMV, larger m as the MFMA skinny product."""
     _head_case(bl, olib, m, n, k, stride, penalty, seed=m + n)
 
 
@@ -88,8 +90,9 @@ def test_greedy_head_ties_and_flips(bl, olib):
     """Duplicated weight rows give equal logits; with the first of each pair in
     the history the penalty must move the choice, and with penalty 1 the lower
     index must win."""
-    for penalty in (1.1, 1.0, 2.0):
-        _head_case(bl, olib, 16, 640, 128, 8, penalty, seed=7, ties=True)
+    for m in (16, 1):  # 1: the GEMV form of the head
+        for penalty in (1.1, 1.0, 2.0):
+            _head_case(bl, olib, m, 640, 128, 8, penalty, seed=7, ties=True)
 
 
 def _step_inputs(bl, olib, d, f, n_layers, vocab, m, seed):
