@@ -51,10 +51,27 @@ Layout ffn_layout(int64_t m, int64_t d, int64_t f)
 
 // Stream workspace: control words {epoch, status} and the published vectors of
 // the persistent one-token kernel, then a (q, s, qs) for d, o_in for d, the
-// FFN workspace and the q/k/v scratch of the launch-per-step path.
+// FFN workspace, the q/k/v scratch of the launch-per-step path and the K-split
+// partial sums of its down product at 9..32 tokens.
 struct StreamLayout {
-    size_t ctrl, ll, q_a, s_a, qs_a, q_o, s_o, qs_o, ffn, qkv, total;
+    size_t ctrl, ll, q_a, s_a, qs_a, q_o, s_o, qs_o, ffn, qkv, part, total;
 };
+
+constexpr int kMaxKSplit = 4;
+
+// K split of the down product (d rows, K = f) at 9..32 tokens: its d / 32
+// tiles alone would occupy a quarter of the CUs at d = 2048, each workgroup
+// pulling all 32 x f activation bytes; split so that tiles x parts still fits
+// one workgroup per CU and every part is a whole number of 128-input steps.
+// (The o product, K = d, gains less from a split than its reducer then costs.)
+int batched_ksplit(int64_t d, int64_t f)
+{
+    const int64_t tiles = (d + 31) / 32;
+    if (d > 8192) return 1;  // the reducing quant holds 16 values per thread at most
+    for (int ks = kMaxKSplit; ks > 1; ks /= 2)
+        if (tiles * ks <= 256 && f % (128 * ks) == 0) return ks;
+    return 1;
+}
 
 StreamLayout stream_layout(int64_t m, int64_t d, int64_t f)
 {
@@ -75,6 +92,7 @@ StreamLayout stream_layout(int64_t m, int64_t d, int64_t f)
     l.qs_o = take((size_t)m * 4);
     l.ffn = take(ffn_layout(m, d, f).total);
     l.qkv = take((size_t)(m * 3 * d) * 4);
+    l.part = take((size_t)(kMaxKSplit * m * d) * 4);
     l.total = at;
     return l;
 }
@@ -107,6 +125,16 @@ bl::SkinnyArgs skinny(const uint8_t* w, const float* w_scale_ptr, float w_scale,
     a.ldy = ldy;
     a.acc0 = acc;
     return a;
+}
+
+// The product as ks partial sums over K (no epilogue: the next norm + quant
+// finishes it with the residual, launch_quant_reduce).
+void split_k(bl::SkinnyArgs& a, int32_t* part, int ks)
+{
+    a.residual = nullptr;
+    a.y = nullptr;
+    a.part = part;
+    a.ksplit = ks;
 }
 
 // The fused gate/up of f rows over d inputs: h[m][f] = relu(gate)^2 * up.
@@ -358,6 +386,8 @@ int stream_steps(const uint8_t* weights, const float* scales, const float* gains
         int8_t* q2 = at<int8_t>(ffn_ws, FL.off[BITNET_FFN_WS_Q2]);
         float* s2 = at<float>(ffn_ws, FL.off[BITNET_FFN_WS_S2]);
         int32_t* qs2 = at<int32_t>(ffn_ws, FL.off[BITNET_FFN_WS_QS2]);
+        int32_t* part = at<int32_t>(workspace, L.part);
+        const int ks = batched_ksplit(d, f);
         for (int64_t l = 0; l < n_layers; ++l) {
             const uint8_t* wl = weights + (size_t)l * blob;
             const float* sl = scales + 7 * l;
@@ -375,7 +405,12 @@ int stream_steps(const uint8_t* weights, const float* scales, const float* gains
                                         (uint32_t)bl::skinny_rows_per_tile(F, true) * rd};
             const bl::Prefetch pf_dn = {{wg + 2 * fd, nullptr}, {(uint32_t)fd, 0u},
                                         (uint32_t)bl::skinny_rows_per_tile(D, false) * rf};
-            int rc = bl::launch_quant_act(x, gl, eps, M, D, qa, sa, qsa, s, true, &pf_qkv);
+            // x after the previous layer's down product: finished by this norm +
+            // quant when that product was split (every layer but the last)
+            int rc = l > 0 && ks > 1
+                         ? bl::launch_quant_reduce(x, gl, eps, M, D, part, ks, qs2, s2, sl - 7 + 6, qa, sa, qsa, s,
+                                                   &pf_qkv)
+                         : bl::launch_quant_act(x, gl, eps, M, D, qa, sa, qsa, s, true, &pf_qkv);
             if (!rc)
                 rc = bl::launch_skinny(skinny(wl, sl, 0.0f, D, 3 * D, D, qa, sa, qsa, M, nullptr, qkv_l, 3 * D), false,
                                        s);
@@ -390,8 +425,13 @@ int stream_steps(const uint8_t* weights, const float* scales, const float* gains
                                                      nullptr),
                                        false, s);
             if (!rc) rc = bl::launch_quant_act(h, gl + 3 * d, eps, M, F, q2, s2, qs2, s, true, &pf_dn);
-            if (!rc)
-                rc = bl::launch_skinny(skinny(wg + 2 * fd, sl + 6, 0.0f, D, D, F, q2, s2, qs2, M, x, x, D), false, s);
+            if (!rc) {
+                // down: partial sums per K part, finished by the next layer's
+                // norm + quant; the last layer writes x itself
+                bl::SkinnyArgs adn = skinny(wg + 2 * fd, sl + 6, 0.0f, D, D, F, q2, s2, qs2, M, x, x, D);
+                if (ks > 1 && l + 1 < n_layers) split_k(adn, part, ks);
+                rc = bl::launch_skinny(adn, false, s);
+            }
             if (rc) return rc;
         }
         return BL_OK;

@@ -23,6 +23,13 @@ struct Prefetch;
 int launch_quant_act(const float* x, const float* gain, float eps, int m, int k, int8_t* q,
                      float* act_scale, int32_t* act_sum, hipStream_t s, bool perm16 = false,
                      const Prefetch* pf = nullptr);
+// RMSNorm + quant (perm16 order) of x[m][k] after first finishing the K-split
+// product whose ksplit (2 or 4) partial sums part[ksplit][m][k] it adds up:
+// x += dequant(sum - qs_in, sa_in, *sw) in that product's epilogue order, x is
+// written back, then quantized as launch_quant_act does. k <= 8192.
+int launch_quant_reduce(float* x, const float* gain, float eps, int m, int k, const int32_t* part, int ksplit,
+                        const int32_t* qs_in, const float* sa_in, const float* sw, int8_t* q, float* act_scale,
+                        int32_t* act_sum, hipStream_t s, const Prefetch* pf);
 
 // Weight rows read by workgroup b of a GEMV-family launch over k inputs (rows
 // [b R, (b + 1) R) of the stacked matrices), and by workgroup b of a skinny
@@ -126,6 +133,13 @@ struct SkinnyArgs {
     const uint32_t* pen_bits = nullptr;
     int pen_words = 0;
     float penalty = 1.0f;
+    // K split over workgroups (one matrix, not with w1, the head or the
+    // epilogue outputs): with part set, workgroup (tile, p) of ksplit covers
+    // inputs [p k / ksplit, (p + 1) k / ksplit) and writes its exact sums of
+    // codes x q, sum(q) not yet removed, to part[(p m + tok) n + col]; the
+    // reader adds the ksplit partials (quant_reduce).
+    int32_t* part = nullptr;
+    int ksplit = 1;
 };
 int launch_skinny(const SkinnyArgs& a, bool natural_q, hipStream_t s);
 int skinny_tiles(int n, bool pair);

@@ -151,6 +151,68 @@ __global__ __launch_bounds__(kThreads) void quant_act_reg_kernel(const float* __
     }
 }
 
+// The norm + quant launch behind a product whose K was split over KS
+// workgroups (SkinnyArgs::part): it first finishes that product for its row.
+// Element i: acc = the KS partial sums of codes x q added up (exact, any order)
+// minus sum(q) of the product's input, y = fl(fl(acc) * fl(1 / fl(s_a s_w))),
+// x = fl(x + y) -- the operations, in the order, of the product's own
+// epilogue with a residual -- and x is written back; the row then goes
+// through the same register-resident norm + quant as quant_act_reg_kernel.
+struct ReduceIn {
+    const int32_t* part;  // [KS][rows][k]
+    const int32_t* qs;    // sum(q) per row of the product's input
+    const float* sa;      // s_a per row of the product's input
+    const float* sw;      // the product's weight scale (device)
+};
+
+template <int NPT, int KS>
+__global__ __launch_bounds__(kThreads) void quant_reduce_kernel(float* __restrict__ x, const float* __restrict__ gain,
+                                                                float eps, int k, ReduceIn rin,
+                                                                int8_t* __restrict__ q, float* __restrict__ act_scale,
+                                                                int32_t* __restrict__ act_sum, int rows, Prefetch pf)
+{
+    const int row = blockIdx.x;
+    if (row >= rows) {  // the whole workgroup: no barrier is skipped
+        __shared__ uint32_t trash[64];
+        prefetch_chunks(pf, row, row - rows, (int)gridDim.x - rows, kThreads, (uint32_t)(uintptr_t)&trash[0]);
+        return;
+    }
+    __shared__ BlockQuantShared sh;
+    const int t = threadIdx.x;
+    float* xr = x + (size_t)row * k;
+    float xv[NPT], gv[NPT];
+    int acc[NPT];
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+        const int i = min(t + j * kThreads, k - 1);
+        xv[j] = xr[i];
+        gv[j] = gain[i];
+        acc[j] = 0;
+#pragma unroll
+        for (int p = 0; p < KS; ++p) acc[j] += rin.part[((size_t)p * rows + row) * k + i];
+    }
+    const float inv = 1.0f / (rin.sa[row] * *rin.sw);
+    const int qs = rin.qs[row];
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+        const int i = t + j * kThreads;
+        if (i < k) {
+            xv[j] = xv[j] + (float)(acc[j] - qs) * inv;
+            xr[i] = xv[j];
+        } else {
+            xv[j] = 0.0f;
+            gv[j] = 0.0f;
+        }
+    }
+    float scale;
+    int total;
+    block_quant_compute<true, true, NPT>(xv, gv, eps, k, q + (size_t)row * k, sh, scale, total);
+    if (t == 0) {
+        act_scale[row] = scale;
+        act_sum[row] = total;
+    }
+}
+
 // One wave per row, for rows of up to 64 * 4 * V values (wave_quant_row).
 template <bool kNorm, bool kPerm, int V>
 __global__ __launch_bounds__(256) void quant_act_wave_kernel(const float* __restrict__ x,
@@ -229,15 +291,12 @@ void launch_kind(const float* x, const float* gain, float eps, int m, int k, int
 #undef BL_QREG
 }
 
-}  // namespace
-
-int launch_quant_act(const float* x, const float* gain, float eps, int m, int k, int8_t* q, float* act_scale,
-                     int32_t* act_sum, hipStream_t s, bool perm16, const Prefetch* pf)
+// One extra workgroup per chunk of the next launch (a multiple of 8, at most
+// 256); spans that are not 4-byte aligned are not prefetched.
+Prefetch prefetch_plan(const Prefetch* pf, int& pf_blocks)
 {
-    // one extra workgroup per chunk of the next launch (a multiple of 8, at
-    // most 256); spans that are not 4-byte aligned are not prefetched
     Prefetch p = {{nullptr, nullptr}, {0u, 0u}, 0u};
-    int pf_blocks = 0;
+    pf_blocks = 0;
     if (pf && pf->chunk && (pf->chunk & 3) == 0) {
         for (int i = 0; i < 2; ++i)
             if (pf->p[i] && pf->bytes[i] && (reinterpret_cast<uintptr_t>(pf->p[i]) & 3) == 0 && (pf->bytes[i] & 3) == 0) {
@@ -249,6 +308,45 @@ int launch_quant_act(const float* x, const float* gain, float eps, int m, int k,
         const uint64_t chunks = (top + p.chunk - 1) / p.chunk;
         pf_blocks = (int)std::min<uint64_t>(256, (chunks + 7) / 8 * 8);
     }
+    return p;
+}
+
+}  // namespace
+
+int launch_quant_reduce(float* x, const float* gain, float eps, int m, int k, const int32_t* part, int ksplit,
+                        const int32_t* qs_in, const float* sa_in, const float* sw, int8_t* q, float* act_scale,
+                        int32_t* act_sum, hipStream_t s, const Prefetch* pf)
+{
+    int pf_blocks;
+    const Prefetch p = prefetch_plan(pf, pf_blocks);
+    const ReduceIn rin = {part, qs_in, sa_in, sw};
+    const int per = (k + kThreads - 1) / kThreads;  // values per thread
+    const dim3 grid(m + pf_blocks);
+#define BL_QRED(N, KS) \
+    quant_reduce_kernel<N, KS><<<grid, kThreads, 0, s>>>(x, gain, eps, k, rin, q, act_scale, act_sum, m, p)
+    if (ksplit == 2 && per <= 4)
+        BL_QRED(4, 2);
+    else if (ksplit == 2 && per <= 8)
+        BL_QRED(8, 2);
+    else if (ksplit == 2 && per <= 16)
+        BL_QRED(16, 2);
+    else if (ksplit == 4 && per <= 4)
+        BL_QRED(4, 4);
+    else if (ksplit == 4 && per <= 8)
+        BL_QRED(8, 4);
+    else if (ksplit == 4 && per <= 16)
+        BL_QRED(16, 4);
+    else
+        return BL_ERR_SHAPE;
+#undef BL_QRED
+    return hipGetLastError() == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
+}
+
+int launch_quant_act(const float* x, const float* gain, float eps, int m, int k, int8_t* q, float* act_scale,
+                     int32_t* act_sum, hipStream_t s, bool perm16, const Prefetch* pf)
+{
+    int pf_blocks;
+    const Prefetch p = prefetch_plan(pf, pf_blocks);
     if (perm16) {
         if (gain)
             launch_kind<true, true>(x, gain, eps, m, k, q, act_scale, act_sum, s, p, pf_blocks);

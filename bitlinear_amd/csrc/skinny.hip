@@ -61,22 +61,29 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyArgs a)
     const int lane = threadIdx.x & 63;
     const int S = blockDim.x >> 6;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int n0 = blockIdx.x * COLS;
+    // K split: workgroup b takes part b mod ksplit of tile b / ksplit, so the
+    // workgroups of one part run on the same XCDs and share its activations in L2
+    const bool split = a.part != nullptr;
+    const int kp = split ? (int)blockIdx.x % a.ksplit : 0;
+    const int tile = split ? (int)blockIdx.x / a.ksplit : (int)blockIdx.x;
+    const int kr = split ? a.k / a.ksplit : a.k;  // inputs of this workgroup, from kp * kr
+    const int n0 = tile * COLS;
     const int lc = lane & 31, h = lane >> 5;
     const size_t kb = (size_t)a.k / 4;
     const uint8_t* wr[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
         const int row = min(PAIR ? n0 + lc : n0 + 32 * j + lc, a.n - 1);
-        wr[j] = (PAIR && j == 1 ? a.w1 : a.w0) + (size_t)row * kb + 16 * h;
+        wr[j] = (PAIR && j == 1 ? a.w1 : a.w0) + (size_t)row * kb + (size_t)(kp * kr) / 4 + 16 * h;
     }
     // row-contiguous activation loads: lane l of load u reads 16 bytes of token 8 u + l / 8
     const int c8 = lane & 7;
     const int8_t* ar[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) ar[u] = a.q + (size_t)min(8 * u + (lane >> 3), a.m - 1) * a.k + 16 * c8;
+    for (int u = 0; u < 4; ++u)
+        ar[u] = a.q + (size_t)min(8 * u + (lane >> 3), a.m - 1) * a.k + (size_t)kp * kr + 16 * c8;
     int8_t* stage = reinterpret_cast<int8_t*>(red + NB * 16 * 64) + wave * kStageA;
-    const int nss = (a.k + 127) / 128;  // the last may be partial
+    const int nss = (kr + 127) / 128;  // the last may be partial
 
     for (int i = threadIdx.x; i < NB * 16 * 64; i += blockDim.x) red[i] = 0;
 
@@ -84,7 +91,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyArgs a)
     // wave has at most kPreSlots slots (16 / S): they travel in the same trip.
     int pre_qs[kPreSlots];
     float pre_sa[kPreSlots], pre_sw[kPreSlots][NB], pre_res[kPreSlots][NB];
-    if (S * kPreSlots >= 16) {
+    if (S * kPreSlots >= 16 && !split) {
 #pragma unroll
         for (int i = 0; i < kPreSlots; ++i) {
             const int r = min(wave + S * i, 15);  // slots past 15 load slot 15 again (unused)
@@ -121,12 +128,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyArgs a)
             for (int j = 0; j < NB; ++j) o[i].w[j] = z;
 #pragma unroll
             for (int u = 0; u < 4; ++u) o[i].a[u] = z;
-            // k is a multiple of 64, so a lane's 64 weights are all in range or none
-            if (ss * 128 + 64 * h < a.k) {
+            // kr is a multiple of 64, so a lane's 64 weights are all in range or none
+            if (ss * 128 + 64 * h < kr) {
 #pragma unroll
                 for (int j = 0; j < NB; ++j) o[i].w[j] = *reinterpret_cast<const uint4*>(wr[j] + (size_t)ss * 32);
             }
-            if (ss * 128 + 16 * c8 < a.k) {
+            if (ss * 128 + 16 * c8 < kr) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u) o[i].a[u] = *reinterpret_cast<const uint4*>(ar[u] + (size_t)ss * 128);
             }
@@ -162,6 +169,15 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyArgs a)
     }
     __syncthreads();
 
+    if (split) {  // uniform: the part's raw totals, no epilogue
+        for (int r = wave; r < 16; r += S) {
+            const int tok = tile_row(lane, r);
+            const int col = n0 + lc;
+            if (tok < a.m && col < a.n)
+                a.part[((size_t)kp * a.m + tok) * a.n + col] = red[r * 64 + lane];
+        }
+        return;
+    }
     const int tiles = gridDim.x;
     // Epilogue of slot r (C row 4 b + r of the tile, see tile_row) with the
     // slot's per-token and per-column inputs.
@@ -315,10 +331,11 @@ int launch_nb(const SkinnyArgs& a, hipStream_t s)
     constexpr int cols = PAIR ? 32 : 32 * NB;
     constexpr int kw_max = NB == 1 ? 4 : 2;
     const int tiles = (a.n + cols - 1) / cols;
+    const int parts = a.part ? a.ksplit : 1;
     // More workgroups than CUs (the LM head): at most 8 waves each, so two fit
     // on a CU (LDS and registers) and the grid runs in fewer rounds.
-    const Split sp = pick_split(a.k, kw_max, tiles > 256 ? kMaxWaves / 2 : kMaxWaves);
-    const dim3 grid(tiles), block(64 * sp.waves);
+    const Split sp = pick_split(a.k / parts, kw_max, tiles * parts > 256 ? kMaxWaves / 2 : kMaxWaves);
+    const dim3 grid(tiles * parts), block(64 * sp.waves);
     const size_t lds = (size_t)NB * 16 * 64 * sizeof(int) + (size_t)sp.waves * kStageA;
     if (sp.kw == 1)
         skinny_kernel<NB, PAIR, 1, NAT><<<grid, block, lds, s>>>(a);
@@ -344,6 +361,10 @@ int skinny_rows_per_tile(int n, bool pair) { return pair || !two_tiles(n) ? 32 :
 
 int launch_skinny(const SkinnyArgs& a, bool natural_q, hipStream_t s)
 {
+    if (a.part) {  // K split: one matrix of 32-row tiles, each part a whole number of 64-input chunks
+        if (a.w1 || two_tiles(a.n) || a.ksplit < 1 || a.k % (64 * a.ksplit) != 0) return BL_ERR_SHAPE;
+        return natural_q ? launch_nb<1, false, true>(a, s) : launch_nb<1, false, false>(a, s);
+    }
     if (a.w1) return natural_q ? launch_nb<2, true, true>(a, s) : launch_nb<2, true, false>(a, s);
     if (two_tiles(a.n)) return natural_q ? launch_nb<2, false, true>(a, s) : launch_nb<2, false, false>(a, s);
     return natural_q ? launch_nb<1, false, true>(a, s) : launch_nb<1, false, false>(a, s);

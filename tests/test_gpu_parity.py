@@ -416,8 +416,13 @@ def test_ffn_prefill_full_size_sampled_rows(bl, olib):
 @pytest.mark.parametrize("n_layers,m,d,f", [(2, 1, 128, 512), (3, 2, 256, 640), (3, 1, 256, 1024),
                                             (2, 1, 2560, 10240), (2, 1, 2048, 8192), (2, 12, 192, 384),
                                             (2, 9, 320, 1088), (2, 25, 512, 1536), (2, 32, 2048, 8192),
+                                            (3, 32, 256, 1024), (2, 16, 2560, 10240),
                                             (2, 33, 256, 512), (1, 16, 256, 8448)])
 def test_decode_stream(bl, olib, n_layers, m, d, f):
+    """The layer stream against oracle.chain. At 9..32 tokens the down
+    product of every layer but the last splits K over 2 or 4 workgroups where
+    d and f allow it (f = 1536, 8192, 1024: 4 parts; 2560 x 10240: 2; f = 384
+    and 1088: none), and the next layer's norm + quant finishes it."""
     from gpu_helpers import make_layers, run_stream, stream_ctrl
     log(f"stream layers={n_layers} m={m} d={d} f={f}")
     layers, dev = make_layers(W.W_STREAM, n_layers, d, f, m, olib)
