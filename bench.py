@@ -840,7 +840,7 @@ def extra_measurements(bl, torch, T, dev0, check=True, peaks=None):
     # ---- batched decode, 1.3B, 32 tokens, + LM head argmax ----
     cfg = W.BITNET_1P3B
     L, d, f, m, V = cfg["layers"], cfg["dim"], cfg["ffn"], 32, cfg["vocab"]
-    dev, _ = build_stream(bl, W.W_BATCHED, L, d, f, m, T)
+    dev, host_b = build_stream(bl, W.W_BATCHED, L, d, f, m, T)
     gh = W.rng(W.W_BATCHED, 0, W.T_HEAD)
     head = T(bl.bitlinear_pack(W.ternary(gh, V, d)))
     sh = W.weight_scale(gh)
@@ -858,6 +858,28 @@ def extra_measurements(bl, torch, T, dev0, check=True, peaks=None):
         run_stream_step(bl, dev, L, m, d, f, xb, qkv, ws)
         bl.bitlinear_quant_act(xb, gfin, 1e-5, qf, sf, qsf)
         bl.bitlinear_gemm(head, sh, V, d, qf, sf, qsf, m, None, None, None, idx, wsh)
+
+    # parity of the first stream step on sampled tokens: every row goes through
+    # the layers on its own (per-token norms, products and stand-in), so the
+    # oracle runs the chosen rows alone, bit for bit
+    batched_check = None
+    if check:
+        import oracle
+        olib = oracle.load()
+        x_in = xb.cpu().numpy().copy()
+        run_stream_step(bl, dev, L, m, d, f, xb, qkv, ws)
+        x_gpu, qkv_gpu = xb.cpu().numpy(), qkv.cpu().numpy()
+        rows = [0, m - 1]
+        exact = True
+        for r in rows:
+            lr = [dict(lw, z=lw["z"][r:r + 1]) for lw in host_b]
+            ox, oqkv = oracle.chain(x_in[r:r + 1], lr, 1e-5, olib)
+            exact = exact and bool(np.array_equal(ox.view(np.uint32), x_gpu[r:r + 1].view(np.uint32)))
+            exact = exact and all(np.array_equal(oqkv[l].view(np.uint32), qkv_gpu[l, r:r + 1].view(np.uint32))
+                                  for l in range(L))
+        batched_check = {"tokens": rows, "bit_exact": exact}
+        xb.copy_(T(x_in))
+    del host_b
 
     for _ in range(2):
         batched_step()
@@ -883,6 +905,7 @@ def extra_measurements(bl, torch, T, dev0, check=True, peaks=None):
                       "ms_per_step_graph": round(gms, 4),
                       "weight_gbs_graph": round(bytes_b / (gms * 1e-3) / 1e9, 1),
                       "graph_matches_eager": gsame, "per_step": batched_stats,
+                      "parity_first_step": batched_check,
                       "roofline": {"kernel": "the step's launches (skinny MFMA products, quant, LM head argmax)",
                                    "bound": "hbm", "achieved": round(bytes_b / (ms_b * 1e-3) / 1e9, 1),
                                    "peak": HBM_PEAK_GBS, "unit": "GB/s",
