@@ -7,8 +7,9 @@
 //     sequence are set in a per-sequence bitmap over the vocabulary, which the
 //     LM-head epilogue (skinny.hip) reads to penalise those logits before it
 //     forms its argmax keys, so penalty and argmax take one pass and no logits
-//     need to be written;
-//   - appending the chosen token to each sequence's history on the device.
+//     need to be written. The embedding launch of a greedy step builds these
+//     bitmaps too, and the argmax key reduction (skinny.hip) appends the
+//     chosen token to each sequence's history on the device.
 #include "internal.h"
 
 namespace bl {
@@ -85,24 +86,6 @@ __global__ __launch_bounds__(256) void penalty_bits_kernel(const int32_t* __rest
     penalty_bits_row<256>(blockIdx.x, hist, stride, hist_len, n, words, bits);
 }
 
-// After the choice: hist[r][hist_len[r]] = next[r] and hist_len[r] + 1 while
-// the history has room; tokens[r] = next[r] (if given).
-__global__ void append_kernel(const int32_t* __restrict__ next, int m, int32_t* __restrict__ hist, int stride,
-                              int32_t* __restrict__ hist_len, int32_t* __restrict__ tokens)
-{
-    const int r = blockIdx.x * blockDim.x + threadIdx.x;
-    if (r >= m) return;
-    const int32_t t = next[r];
-    if (hist && hist_len) {
-        const int len = hist_len[r];
-        if (len >= 0 && len < stride) {
-            hist[(size_t)r * stride + len] = t;
-            hist_len[r] = len + 1;
-        }
-    }
-    if (tokens) tokens[r] = t;
-}
-
 }  // namespace
 
 int launch_embed(const uint8_t* table, float s_e, int vocab, int d, const int32_t* tokens, int m, float* x,
@@ -118,13 +101,6 @@ int launch_penalty_bits(const int32_t* hist, int stride, const int32_t* hist_len
                         hipStream_t s)
 {
     penalty_bits_kernel<<<m, 256, 0, s>>>(hist, stride, hist_len, n, penalty_words(n), bits);
-    return hipGetLastError() == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
-}
-
-int launch_append(const int32_t* next, int m, int32_t* hist, int stride, int32_t* hist_len, int32_t* tokens,
-                  hipStream_t s)
-{
-    append_kernel<<<(m + 63) / 64, 64, 0, s>>>(next, m, hist, stride, hist_len, tokens);
     return hipGetLastError() == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
 }
 

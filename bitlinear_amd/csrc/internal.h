@@ -179,8 +179,6 @@ int launch_embed(const uint8_t* table, float s_e, int vocab, int d, const int32_
                  hipStream_t s, const PenaltyRows* pen = nullptr);
 int launch_penalty_bits(const int32_t* hist, int stride, const int32_t* hist_len, int n, int m, uint32_t* bits,
                         hipStream_t s);
-int launch_append(const int32_t* next, int m, int32_t* hist, int stride, int32_t* hist_len, int32_t* tokens,
-                  hipStream_t s);
 
 // Top-k (topp false, k) or nucleus (topp true, p) sampling of m rows of n
 // logits with the caller's uniforms u (sample.hip); workspace:

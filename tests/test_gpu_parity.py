@@ -416,7 +416,7 @@ def test_ffn_prefill_full_size_sampled_rows(bl, olib):
 @pytest.mark.parametrize("n_layers,m,d,f", [(2, 1, 128, 512), (3, 2, 256, 640), (3, 1, 256, 1024),
                                             (2, 1, 2560, 10240), (2, 1, 2048, 8192), (2, 12, 192, 384),
                                             (2, 9, 320, 1088), (2, 25, 512, 1536), (2, 32, 2048, 8192),
-                                            (3, 32, 256, 1024), (2, 16, 2560, 10240),
+                                            (3, 32, 256, 1024), (3, 9, 256, 1024), (2, 16, 2560, 10240),
                                             (2, 33, 256, 512), (1, 16, 256, 8448)])
 def test_decode_stream(bl, olib, n_layers, m, d, f):
     """The layer stream against oracle.chain. At 9..32 tokens the down
