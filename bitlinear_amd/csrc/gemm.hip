@@ -23,6 +23,7 @@
 // a 64-bit atomicMax, so equal accumulators resolve to the lowest n.
 #include "internal.h"
 #include "ternary.h"
+#include "wave.h"
 
 namespace bl {
 namespace {
@@ -256,6 +257,33 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(2))
     if constexpr (PAIR) {
         // lane c < HALF: gate of column c0 + (wn + j MT) / 2 + c; lane c + HALF: its up
         const int cl = lane % MT;
+        if (!acc_out && !acc_up && m0 + C::BM <= m && c0 + C::BN / 2 <= n) {
+            // An interior tile that only writes y: no per-element bounds or
+            // pointer checks (the lanes of gate columns store)
+            float* yb = y + (size_t)(m0 + wm) * ldy + c0 + wn / 2 + cl;
+#pragma unroll
+            for (int i = 0; i < C::TM; ++i) {
+#pragma unroll
+                for (int r = 0; r < C::NACC; ++r) {
+                    const int lrow = wm + i * MT + M::row(lane, r);
+                    const int qs = lds_qsum[lrow];
+                    const float inv_g = lds_inv[lrow];
+                    const float inv_u = lds_inv_up[lrow];
+                    float* yr = yb + (size_t)(i * MT + M::row(lane, r)) * ldy;
+#pragma unroll
+                    for (int j = 0; j < C::TN; ++j) {
+                        const int total = acc[i][j][r] - qs;
+                        const int other = xor_lane<HALF>(total);
+                        const float gate = (float)total * inv_g;
+                        const float up = (float)other * inv_u;
+                        const float gp = gate > 0.0f ? gate : 0.0f;
+                        const float g2 = gp * gp;
+                        if (cl < HALF) yr[j * HALF] = g2 * up;
+                    }
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < C::TM; ++i) {
 #pragma unroll
@@ -268,7 +296,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
                 for (int j = 0; j < C::TN; ++j) {
                     const int total = acc[i][j][r] - qs;
-                    const int other = __shfl_xor(total, HALF, 64);
+                    const int other = xor_lane<HALF>(total);
                     const int col = c0 + (wn + j * MT) / 2 + (cl % HALF);
                     if (cl < HALF && row < m && col < n) {
                         const size_t o = (size_t)row * ldy + col;

@@ -329,9 +329,13 @@ def test_gemm_residual_and_stride(bl, olib, m):
 
 # ---- FFN -----------------------------------------------------------------------------------------
 
-def _ffn_case(bl, olib, m, d, f, seed, with_residual):
+def _ffn_case(bl, olib, m, d, f, seed, with_residual, write_acc=True):
+    """One bitnet_ffn call against oracle.ffn, every intermediate of the
+    workspace; without write_acc the accumulators are not written (above 64
+    tokens the gate/up GEMM's interior tiles then store h with no per-element
+    checks) and everything else is compared."""
     import torch
-    log(f"ffn m={m} d={d} f={f}")
+    log(f"ffn m={m} d={d} f={f} write_acc={write_acc}")
     g = W.rng(105, seed, 0)
     tg, tu, td = W.ternary(g, f, d), W.ternary(g, f, d), W.ternary(g, d, f)
     sg, su, sd = W.weight_scale(g), W.weight_scale(g), W.weight_scale(g)
@@ -344,19 +348,22 @@ def _ffn_case(bl, olib, m, d, f, seed, with_residual):
     # the workspace's content on entry is unspecified: start from garbage
     ws = torch.full((bl.bitnet_ffn_workspace_bytes(m, d, f),), 0x5A, dtype=torch.uint8, device=dev)
     bl.bitnet_ffn(to_dev(x), m, d, f, to_dev(gn), to_dev(gs), 1e-5, to_dev(pg), sg, to_dev(pu), su, to_dev(pd), sd,
-                  to_dev(res) if res is not None else None, out, ws, flags=bl.BITNET_FFN_WRITE_ACC)
+                  to_dev(res) if res is not None else None, out, ws,
+                  flags=bl.BITNET_FFN_WRITE_ACC if write_acc else 0)
     r = oracle.ffn(x, gn, gs, 1e-5, pg, sg, pu, su, pd, sd, olib)
     view = lambda seg: to_host(bl.ffn_workspace_view(ws, m, d, f, seg))
     assert_exact(view("q1"), r["q1"], "q1")
     assert_exact(view("s1").view(np.uint32), r["s1"].view(np.uint32), "s1 bits")
     assert_exact(view("qs1"), r["qs1"], "qs1")
-    assert_exact(view("acc_gate"), r["acc_gate"], "acc_gate")
-    assert_exact(view("acc_up"), r["acc_up"], "acc_up")
+    if write_acc:
+        assert_exact(view("acc_gate"), r["acc_gate"], "acc_gate")
+        assert_exact(view("acc_up"), r["acc_up"], "acc_up")
     assert_f32(view("h"), r["h"], "h")
     assert_exact(view("q2"), r["q2"], "q2")
     assert_exact(view("s2").view(np.uint32), r["s2"].view(np.uint32), "s2 bits")
     assert_exact(view("qs2"), r["qs2"], "qs2")
-    assert_exact(view("acc_down"), r["acc_down"], "acc_down")
+    if write_acc:
+        assert_exact(view("acc_down"), r["acc_down"], "acc_down")
     want = r["out"] if res is None else oracle.residual_add(res, r["out"], olib)
     assert_f32(to_host(out), want, "out")
 
@@ -373,16 +380,27 @@ def test_ffn(bl, olib, m, d, f, res):
     _ffn_case(bl, olib, m, d, f, m * 1000 + d + f, res)
 
 
-def test_ffn_prefill_full_size_sampled_rows(bl, olib):
+@pytest.mark.parametrize("m,d,f,res", [(40, 256, 512, True), (64, 256, 1024, False), (65, 256, 1024, True),
+                                        (130, 320, 1088, False), (300, 256, 640, True), (257, 192, 2624, False),
+                                        (512, 512, 2048, False)])
+def test_ffn_without_accumulators(bl, olib, m, d, f, res):
+    """Above 64 tokens without BITNET_FFN_WRITE_ACC: interior gate/up tiles take
+    the epilogue without per-element checks, edge tiles the general one."""
+    _ffn_case(bl, olib, m, d, f, m * 1000 + d + f + 7, res, write_acc=False)
+
+
+@pytest.mark.parametrize("write_acc", [True, False])
+def test_ffn_prefill_full_size_sampled_rows(bl, olib, write_acc):
     """The FFN at 2048 tokens with BitNet-3B shapes (d = 2560, f = 10240): the
     paired gate/up GEMM with relu(gate)^2 * up in its epilogue, the sub-norm +
     quant of h and the down GEMM. Every intermediate of sampled rows (at least
     one in every 128-row block tile, plus tile edges) against the oracle's FFN
     of those rows: q1, s1, sum(q1), the exact gate and up accumulators, h, q2,
-    s2, sum(q2), the exact down accumulators and out (rows are independent)."""
+    s2, sum(q2), the exact down accumulators and out (rows are independent).
+    Without the accumulators (the benchmark's call) everything else again."""
     import torch
     m, d, f = 2048, 2560, 10240
-    log(f"ffn full size m={m} d={d} f={f}")
+    log(f"ffn full size m={m} d={d} f={f} write_acc={write_acc}")
     g = W.rng(107, 0, 0)
     tg, tu, td = W.ternary(g, f, d), W.ternary(g, f, d), W.ternary(g, d, f)
     sg, su, sd = W.weight_scale(g), W.weight_scale(g), W.weight_scale(g)
@@ -393,7 +411,7 @@ def test_ffn_prefill_full_size_sampled_rows(bl, olib):
     out = torch.empty((m, d), dtype=torch.float32, device=dev)
     ws = torch.full((bl.bitnet_ffn_workspace_bytes(m, d, f),), 0x5A, dtype=torch.uint8, device=dev)
     bl.bitnet_ffn(to_dev(x), m, d, f, to_dev(gn), to_dev(gs), 1e-5, to_dev(pg), sg, to_dev(pu), su, to_dev(pd), sd,
-                  None, out, ws, flags=bl.BITNET_FFN_WRITE_ACC)
+                  None, out, ws, flags=bl.BITNET_FFN_WRITE_ACC if write_acc else 0)
     pick = W.rng(107, 1, 1)
     rows = sorted({0, 127, 128, 1023, 2047} | {int(t * 128 + pick.integers(0, 128)) for t in range(m // 128)})
     r = oracle.ffn(x[rows], gn, gs, 1e-5, pg, sg, pu, su, pd, sd, olib)
@@ -401,13 +419,15 @@ def test_ffn_prefill_full_size_sampled_rows(bl, olib):
     assert_exact(view("q1"), r["q1"], "q1")
     assert_exact(view("s1").view(np.uint32), r["s1"].view(np.uint32), "s1 bits")
     assert_exact(view("qs1"), r["qs1"], "qs1")
-    assert_exact(view("acc_gate"), r["acc_gate"], "acc_gate")
-    assert_exact(view("acc_up"), r["acc_up"], "acc_up")
+    if write_acc:
+        assert_exact(view("acc_gate"), r["acc_gate"], "acc_gate")
+        assert_exact(view("acc_up"), r["acc_up"], "acc_up")
     assert_f32(view("h"), r["h"], "h")
     assert_exact(view("q2"), r["q2"], "q2")
     assert_exact(view("s2").view(np.uint32), r["s2"].view(np.uint32), "s2 bits")
     assert_exact(view("qs2"), r["qs2"], "qs2")
-    assert_exact(view("acc_down"), r["acc_down"], "acc_down")
+    if write_acc:
+        assert_exact(view("acc_down"), r["acc_down"], "acc_down")
     assert_f32(to_host(out)[rows], r["out"], "out")
 
 
