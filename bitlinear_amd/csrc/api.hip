@@ -819,17 +819,30 @@ int bitnet_greedy_step(const uint8_t* embed_table, float s_emb, int64_t vocab, c
     rc = bitnet_decode_stream(weights, scales, gains, z, n_layers, m, d, f, eps, x, nullptr,
                               at<void>(workspace, L.stream), stream_layout(m, d, f).total, stream);
     if (rc) return rc;
-    // 3. final RMSNorm + quant, 4. penalised LM head + greedy choice into tokens
+    // 3. final RMSNorm + quant, 4. penalised LM head + greedy choice into tokens,
+    // 5. the chosen tokens join the histories (the next step embeds them): in the
+    // launch that reduces the head's keys
+    int32_t* app_hist = hist_stride > 0 ? hist : nullptr;
+    int32_t* app_len = hist_stride > 0 ? hist_len : nullptr;
+    if (m == 1 && bl::fwd_fits(1, (int)d)) {
+        // one sequence: the final norm + quant runs inside the head's launch
+        const HeadLayout HL = head_layout(m, vocab);
+        void* hws = at<void>(workspace, L.head);
+        int tiles = 0;
+        rc = bl::launch_head_block(x, g_final, eps, head, s_head, (int)vocab, (int)d, at<uint32_t>(hws, HL.bits),
+                                   penalty, logits, at<unsigned long long>(hws, HL.keys), (int)((vocab + 31) / 32),
+                                   &tiles, s);
+        if (rc) return rc;
+        return bl::launch_tile_argmax(at<unsigned long long>(hws, HL.keys), tiles, 1, tokens, s, app_hist,
+                                      (int)hist_stride, app_len);
+    }
     int8_t* qf = at<int8_t>(workspace, L.q);
     float* sf = at<float>(workspace, L.s);
     int32_t* qsf = at<int32_t>(workspace, L.qs);
     rc = bl::launch_quant_act(x, g_final, eps, (int)m, (int)d, qf, sf, qsf, s);
     if (rc) return rc;
-    // 5. the chosen tokens join the histories (the next step embeds them): in the
-    // launch that reduces the head's keys
     return greedy_head_launch(head, s_head, vocab, d, qf, sf, qsf, m, hist, hist_stride, hist_len, penalty, logits,
-                              tokens, at<void>(workspace, L.head), s, true, hist_stride > 0 ? hist : nullptr,
-                              hist_stride > 0 ? hist_len : nullptr);
+                              tokens, at<void>(workspace, L.head), s, true, app_hist, app_len);
 }
 
 // ---- top-k and nucleus sampling --------------------------------------------------

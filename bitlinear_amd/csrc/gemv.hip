@@ -244,6 +244,88 @@ __global__ __launch_bounds__(64) void head_gemv_kernel(const uint8_t* __restrict
     if (lane == 0) tile_keys[blockIdx.x] = best;
 }
 
+// head_gemv_kernel with the final RMSNorm + quant of the token fused in, one
+// 512-thread workgroup per CU on a block of rpb consecutive rows: the
+// workgroup quantizes x once with the workgroup quant (block_quant_compute:
+// the same q, s_a and sum(q) as the quant kernel) into LDS while its first
+// rows stream in; its 8 waves then take 64 rows at a time, 8 lanes per row
+// (wave w rows w, w + 8, ... of each 64), with the next 64 rows' loads issued
+// before the current ones' dot products. Each workgroup writes the largest
+// fp32 argmax key of its rows to tile_keys[blockIdx.x].
+template <int NPT>
+__global__ __launch_bounds__(512) void head_block_kernel(const float* __restrict__ x, const float* __restrict__ gain,
+                                                         float eps, const uint8_t* __restrict__ packed, float w_scale,
+                                                         int n, int k, const uint32_t* __restrict__ pen_bits,
+                                                         float penalty, float* __restrict__ y,
+                                                         unsigned long long* __restrict__ tile_keys, int rpb)
+{
+    constexpr int L = 8;
+    constexpr int CPL = NPT;  // chunks per lane: k <= 512 NPT, 8 NPT chunks over 8 lanes
+    static_assert(CPL <= kMaxChunksPerLane, "row size");
+    __shared__ __attribute__((aligned(16))) int8_t qs[512 * NPT];
+    __shared__ BlockQuantShared sh;
+    __shared__ unsigned long long wbest[8];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane / L, j = lane % L;
+    const int chunks = k / 64;
+    const size_t row_bytes = (size_t)k / 4;
+
+    float xv[NPT], gv[NPT];
+    block_quant_load<true, NPT>(x, gain, k, xv, gv);  // first: a wave's loads complete in issue order
+    const int r1 = min(blockIdx.x * rpb + rpb, n);     // this workgroup's rows end here
+    int row = blockIdx.x * rpb + wave + 8 * g;
+    // slots past the block's last row load that row again (from cache), not another block's
+    uint4 wa[kMaxChunksPerLane], wb[kMaxChunksPerLane];
+    load_row_fixed<L, CPL>(packed + (size_t)min(row, r1 - 1) * row_bytes, j, chunks, wa);
+    load_row_fixed<L, CPL>(packed + (size_t)min(row + 64, r1 - 1) * row_bytes, j, chunks, wb);
+    __builtin_amdgcn_sched_barrier(0);  // keep the weight loads ahead of the quant
+    float s_a;
+    int qsum;
+    block_quant_compute<true, false, NPT>(xv, gv, eps, k, qs, sh, s_a, qsum);  // ends with a barrier
+
+    uint32_t qreg[kMaxChunksPerLane][16];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const int ch = j + c * L;
+        if (ch < chunks) load_q_chunk(qs, ch, qreg[c]);
+    }
+    const float inv = 1.0f / (s_a * w_scale);
+    unsigned long long best = 0;
+    auto emit = [&](int acc, int r) __attribute__((always_inline)) {
+        if (r < r1 && j == 0) {
+            float v = (float)(acc - qsum) * inv;
+            if (pen_bits && ((pen_bits[r >> 5] >> (r & 31)) & 1u)) v = v > 0.0f ? v / penalty : v * penalty;
+            if (y) y[r] = v;
+            const unsigned long long key = argmax_key_f32(v, r);
+            best = key > best ? key : best;
+        }
+    };
+    // two register sets in turn: the loads of the rows after next go out
+    // before the dot products of the current ones
+    for (;;) {
+        emit(group_sum<L>(dot_row_one<L, CPL>(wa, j, chunks, qreg)), row);
+        row += 64;
+        if (__builtin_amdgcn_readfirstlane(row - 8 * g) >= r1) break;
+        load_row_fixed<L, CPL>(packed + (size_t)min(row + 64, r1 - 1) * row_bytes, j, chunks, wa);
+        emit(group_sum<L>(dot_row_one<L, CPL>(wb, j, chunks, qreg)), row);
+        row += 64;
+        if (__builtin_amdgcn_readfirstlane(row - 8 * g) >= r1) break;
+        load_row_fixed<L, CPL>(packed + (size_t)min(row + 64, r1 - 1) * row_bytes, j, chunks, wb);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const unsigned long long other = __shfl_xor(best, off, 64);
+        best = other > best ? other : best;
+    }
+    if (lane == 0) wbest[wave] = best;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int w = 1; w < 8; ++w) best = wbest[w] > best ? wbest[w] : best;
+        tile_keys[blockIdx.x] = best;
+    }
+}
+
 // ---- [RMSNorm +] quant + GEMV of one token in one launch -------------------
 // Every workgroup (one wave) quantizes the whole input row itself with the
 // one-wave quant (wave_quant_row: the same operations in the same order as
@@ -620,6 +702,33 @@ int launch_head_gemv(const uint8_t* packed, float w_scale, int n, int k, const i
     default: BL_HEAD(64); break;
     }
 #undef BL_HEAD
+    return hipGetLastError() == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
+}
+
+int launch_head_block(const float* x, const float* gain, float eps, const uint8_t* packed, float w_scale, int n,
+                      int k, const uint32_t* pen_bits, float penalty, float* y, unsigned long long* tile_keys,
+                      int max_tiles, int* tiles, hipStream_t s)
+{
+    if (!fwd_fits(1, k) || n < 1) return BL_ERR_SHAPE;
+    // one 512-thread workgroup per CU on a block of consecutive rows
+    const int grid_max = max_tiles < kFwdBlockGrid ? max_tiles : kFwdBlockGrid;
+    const int rpb = (n + grid_max - 1) / grid_max, grid = (n + rpb - 1) / rpb;
+    *tiles = grid;
+    const int npt = (k + 511) / 512;
+#define BL_HEADB(NPT)                                                                                       \
+    head_block_kernel<NPT><<<grid, 512, 0, s>>>(x, gain, eps, packed, w_scale, n, k, pen_bits, penalty, y, \
+                                                tile_keys, rpb)
+    if (npt <= 1)
+        BL_HEADB(1);
+    else if (npt <= 2)
+        BL_HEADB(2);
+    else if (npt <= 4)
+        BL_HEADB(4);
+    else if (npt <= 5)
+        BL_HEADB(5);
+    else
+        BL_HEADB(8);
+#undef BL_HEADB
     return hipGetLastError() == hipSuccess ? BL_OK : BL_ERR_LAUNCH;
 }
 

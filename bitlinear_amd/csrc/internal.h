@@ -150,6 +150,12 @@ int skinny_tiles(int n, bool pair);
 int launch_head_gemv(const uint8_t* packed, float w_scale, int n, int k, const int8_t* q, const float* act_scale,
                      const int32_t* act_sum, const uint32_t* pen_bits, float penalty, float* y,
                      unsigned long long* tile_keys, int max_tiles, int* tiles, hipStream_t s);
+// launch_head_gemv with the final RMSNorm(gain, eps) + quant of the token x
+// fused in (k <= 4096): one 512-thread workgroup per CU on a block of rows,
+// each writing one key (*tiles <= min(max_tiles, 256) of them).
+int launch_head_block(const float* x, const float* gain, float eps, const uint8_t* packed, float w_scale, int n,
+                      int k, const uint32_t* pen_bits, float penalty, float* y, unsigned long long* tile_keys,
+                      int max_tiles, int* tiles, hipStream_t s);
 // Per token the column of the largest key; with hist, the chosen token is
 // also appended to its sequence's history (hist[r][hist_len[r]], hist_len[r]
 // + 1, while there is room).

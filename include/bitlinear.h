@@ -429,7 +429,11 @@ int bitnet_greedy_head(const uint8_t *head, float s_head, int64_t n, int64_t k,
  *   tokens = bitnet_greedy_head(q, hist, hist_len, penalty)     (in place)
  *   hist[r][hist_len[r]] = tokens[r]; hist_len[r] += 1   (while hist_len < stride)
  * so the next call continues from the chosen tokens; the host reads tokens or
- * hist when it wants them (4 bytes per sequence and step).
+ * hist when it wants them (4 bytes per sequence and step). The embedding
+ * launch also builds the penalty bitmaps, and the launch that reduces the
+ * head's argmax keys appends the tokens; for one sequence with d <= 4096 the
+ * final norm + quant runs inside the head's launch (one workgroup per CU on
+ * a block of head rows), so the step is four launches besides the stream's.
  *   embed_table, s_emb, vocab : the embedding ([vocab][d/4]).
  *   weights, scales, gains, z, n_layers, d, f, eps : as bitnet_decode_stream.
  *   g_final   : device fp32 [d];  head, s_head : the LM head ([vocab][d/4]).

@@ -143,3 +143,41 @@ def test_greedy_step_loop(bl, olib, m, d, f, n_layers, vocab, stride, steps):
         assert_exact(to_host(got_tokens[i]), o_tok, f"tokens, step {i}")
     assert_exact(to_host(hist), o_hist, "histories")
     assert_exact(to_host(hist_len), o_len, "history lengths")
+
+
+@pytest.mark.parametrize("d,f,vocab", [(2560, 10240, 50000), (192, 384, 999)])
+def test_greedy_step_one_sequence_logits(bl, olib, d, f, vocab):
+    """One sequence: the final norm + quant runs inside the head's launch (one
+    workgroup per CU on a block of head rows; 999 columns leave a short last
+    block). Three steps with the penalised logits requested; tokens, hidden
+    states, histories and every penalised logit against the oracle."""
+    import torch
+    m, n_layers, stride, steps = 1, 2, 16, 3
+    log(f"greedy one sequence d={d} f={f} vocab={vocab}")
+    inp = _step_inputs(bl, olib, d, f, n_layers, vocab, m, seed=77)
+    dev = torch_dev()
+    dw = inp["dev"]
+    tokens = to_dev(inp["tokens"])
+    hist = torch.zeros((m, stride), dtype=torch.int32, device=dev)
+    hist_len = torch.zeros(m, dtype=torch.int32, device=dev)
+    x = torch.empty((m, d), dtype=torch.float32, device=dev)
+    logits = torch.empty((m, vocab), dtype=torch.float32, device=dev)
+    ws = torch.zeros(bl.bitnet_greedy_step_workspace_bytes(m, d, f, vocab), dtype=torch.uint8, device=dev)
+    emb, head, gf = to_dev(inp["emb"]), to_dev(inp["head"]), to_dev(inp["g_final"])
+    o_tok = inp["tokens"].copy()
+    o_hist = np.zeros((m, stride), np.int32)
+    o_len = np.zeros(m, np.int32)
+    for step in range(steps):
+        bl.bitnet_greedy_step(emb, inp["s_emb"], dw["weights"], dw["scales"], dw["gains"], dw["z"], n_layers, d, f,
+                              1e-5, gf, head, inp["s_head"], tokens, hist, hist_len, 1.1, x, logits, ws)
+        o_x = oracle.embed(inp["emb"], inp["s_emb"], o_tok, d, olib)
+        o_x, _ = oracle.chain(o_x, inp["layers"], 1e-5, olib)
+        _, o_pen, _ = oracle.greedy_head(o_x, inp["g_final"], 1e-5, inp["head"], inp["s_head"], o_hist, o_len, 1.1,
+                                         olib)
+        o_tok, o_hist, o_len, _ = oracle.greedy_step(o_tok, inp["emb"], inp["s_emb"], inp["layers"], inp["g_final"],
+                                                     1e-5, inp["head"], inp["s_head"], o_hist, o_len, 1.1, olib)
+        assert_exact(to_host(x).view(np.uint32), o_x.view(np.uint32), f"hidden state bits, step {step}")
+        assert_exact(to_host(logits).view(np.uint32), o_pen.view(np.uint32), f"penalised logits, step {step}")
+        assert_exact(to_host(tokens), o_tok, f"tokens, step {step}")
+    assert_exact(to_host(hist), o_hist, "histories")
+    assert_exact(to_host(hist_len), o_len, "history lengths")
