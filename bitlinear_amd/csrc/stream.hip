@@ -469,6 +469,7 @@ struct AttnShared {
     __attribute__((aligned(16))) float part[4 * kT];  // per-group partial sums of the weighted values
     float red[kT / 64];
     float chunk[kMaxAttnChunks][kMaxHd + 2];  // per chunk: max, sum, weighted sums
+    uint32_t vote;  // the epoch of a phase whose q/k/v wait failed (0 at kernel start)
 };
 struct NoAttnShared {};
 
@@ -554,38 +555,48 @@ __device__ bool attention_split(const StreamArgs& a, int l, int h, int split, in
     // RoPE factors first: loads complete in issue order, so a load issued after
     // the cache rows' would wait for all of them
     const float rc = t < half ? a.rope_cos[t] : 0.0f, rsn = t < half ? a.rope_sin[t] : 0.0f;
-    // the 3 hd words of this head: q, then k, then v
+    // the 3 hd words of this head: q, then k, then v. The waves that hold none
+    // of them issue their loads of the first chunk's cache rows (which do not
+    // depend on this step's q, k, v) before the wait; the polling waves after
+    // it, since a poll issued behind those loads would wait for them. The
+    // failure vote is an LDS word read after the next LDS-only barrier, which
+    // unlike __syncthreads leaves the early loads in flight.
     const int n = 3 * hd;
+    const bool poller = (t >> 6) * 64 < n;  // uniform in a wave
+    const int lim0 = min(len, pos - split * len);
+    if (!poller && lim0 > 0) {
+        load_k(split * len, lim0, 0);
+        load_v(split * len, lim0, 0);
+    }
     const long long t_start = (long long)__builtin_amdgcn_s_memrealtime();
-    uint32_t w[2];
+    uint32_t w[2] = {0u, 0u};
     bool failed = false;
-    for (int spin = 0;; ++spin) {
+    if (poller) {
+        for (int spin = 0;; ++spin) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int u = min(t + kT * i, n - 1);
-            const int seg = u / hd;
-            w[i] = __hip_atomic_load(qq_cur + seg * D + h * hd + (u - seg * hd), __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
+            for (int i = 0; i < 2; ++i) {
+                const int u = min(t + kT * i, n - 1);
+                const int seg = u / hd;
+                w[i] = __hip_atomic_load(qq_cur + seg * D + h * hd + (u - seg * hd), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+            }
+            if (w[0] != 0u && w[1] != 0u) break;
+            if ((spin & 15) == 15 &&
+                (status_load(a.ctrl) != 0 ||
+                 (long long)__builtin_amdgcn_s_memrealtime() - t_start > kTimeoutTicks)) {
+                failed = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(3);
         }
-        if (w[0] != 0u && w[1] != 0u) break;
-        if ((spin & 15) == 15 &&
-            (status_load(a.ctrl) != 0 || (long long)__builtin_amdgcn_s_memrealtime() - t_start > kTimeoutTicks)) {
-            failed = true;
-            break;
-        }
-        __builtin_amdgcn_s_sleep(3);
     }
-    if (__syncthreads_or(failed ? 1 : 0)) {
-        if (t == 0) __hip_atomic_fetch_or(a.ctrl + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return false;
+    if (failed) {
+        s.vote = E2;
+        __hip_atomic_fetch_or(a.ctrl + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    {
-        // the first chunk's rows do not depend on this step's q, k, v
-        const int lim = min(len, pos - split * len);
-        if (lim > 0) {
-            load_k(split * len, lim, 0);
-            load_v(split * len, lim, 0);
-        }
+    if (poller && lim0 > 0) {
+        load_k(split * len, lim0, 0);
+        load_v(split * len, lim0, 0);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -599,6 +610,7 @@ __device__ bool attention_split(const StreamArgs& a, int l, int h, int split, in
         }
     }
     lds_sync();
+    if (s.vote == E2) return false;  // a poller's wait failed (uniform: one LDS word)
     // RoPE of q and k (each thread its own pair); the split of the last chunk
     // writes k and v at position pos of the caches
     if (t < half) {
@@ -805,6 +817,9 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
     // epilogue thread t < R owns row t of the step
     const bool e1 = t < S1::R, e2 = t < S2::R, e3 = t < S3::R;
     if (t < 16) reinterpret_cast<uint32_t*>(sh.zero)[t] = 0u;  // visible after the first barrier
+    if constexpr (ATTN) {
+        if (t == 0) ash.vote = 0u;  // likewise, long before the first attention phase
+    }
 
     float xres = e2 ? a.x[r2 + t] : 0.0f;  // residual x of this workgroup's rows
     float s_a;
