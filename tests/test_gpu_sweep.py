@@ -7,7 +7,9 @@ up), so every run checks the same cases; together they cross the launch
 choices of each entry point (one wave or a workgroup per row, GEMV lanes per
 row, skinny / 32 x 256 / 64 x 160 / 128 x 160 / 128 x 320 tiles, ragged row
 and column tiles, K tails, the K-split down product of the batched stream)
-at sizes the fixed cases of the other files do not name."""
+at sizes the fixed cases of the other files do not name, and the samplers over
+row counts and lengths that split the rows' passes over 1 to 64 workgroups
+with ragged slices."""
 import numpy as np
 import pytest
 
@@ -39,6 +41,9 @@ FWD_SWEEP = _cases(_G.integers(1, 6000, 8), _w64(1, 256, 8), _G.integers(0, 2, 8
 GEMM_SWEEP = _cases(_tokens(1, 300, 18), _G.integers(1, 3000, 18), _w64(1, 64, 18), np.arange(18) % 3)
 FFN_SWEEP = _cases(_tokens(1, 300, 8), _w64(1, 16, 8), _w64(2, 48, 8), _G.integers(0, 2, 8))
 STREAM_SWEEP = _cases(_G.integers(1, 3, 6), _tokens(1, 40, 6), _w64(1, 8, 6), _w64(2, 24, 6))
+# sampling: rows, row length, top-k (k) or nucleus (p in thousandths), temperature in tenths
+SAMPLE_SWEEP = _cases(_tokens(1, 300, 12), _tokens(1, 60000, 12), _G.integers(0, 2, 12), _G.integers(1, 1000, 12),
+                      _G.integers(3, 25, 12))
 
 
 @pytest.fixture(scope="module")
@@ -181,3 +186,25 @@ def test_sweep_stream(bl, olib, n_layers, m, d, f):
     for l in range(n_layers):
         assert_f32(qkv[l], oqkv[l], f"qkv layer {l}")
     assert_f32(x, ox, "x after the stream")
+
+
+@pytest.mark.parametrize("m,n,topp,param,temp10", SAMPLE_SWEEP)
+def test_sweep_sample(bl, olib, m, n, topp, param, temp10):
+    import torch
+    temp = temp10 / 10.0
+    g = W.rng(145, m, n)
+    logits = (g.standard_normal((m, n)) * g.uniform(0.5, 4.0)).astype(np.float32)
+    u = g.random(m)
+    log(f"sweep sample m={m} n={n} {'topp' if topp else 'topk'} {param} T={temp}")
+    dev = torch_dev()
+    tok = torch.full((m,), -1, dtype=torch.int32, device=dev)
+    ws = torch.empty(bl.bitnet_sample_workspace_bytes(m, n), dtype=torch.uint8, device=dev)
+    ud = torch.from_numpy(np.ascontiguousarray(u, np.float64)).to(dev)
+    if topp:
+        p = param / 1000.0
+        bl.bitnet_sample_topp(to_dev(logits), p, temp, ud, tok, ws)
+        want = oracle.sample_topp(logits, p, temp, u, olib)
+    else:
+        bl.bitnet_sample_topk(to_dev(logits), param, temp, ud, tok, ws)
+        want = oracle.sample_topk(logits, param, temp, u, olib)
+    assert_exact(to_host(tok), want, "sampled tokens")
