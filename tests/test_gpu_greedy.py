@@ -145,12 +145,15 @@ def test_greedy_step_loop(bl, olib, m, d, f, n_layers, vocab, stride, steps):
     assert_exact(to_host(hist_len), o_len, "history lengths")
 
 
-@pytest.mark.parametrize("d,f,vocab", [(2560, 10240, 50000), (192, 384, 999)])
+@pytest.mark.parametrize("d,f,vocab", [(2560, 10240, 50000), (192, 384, 999), (64, 128, 1), (64, 128, 7),
+                                        (128, 256, 33), (256, 512, 8193), (4096, 8192, 300)])
 def test_greedy_step_one_sequence_logits(bl, olib, d, f, vocab):
     """One sequence: the final norm + quant runs inside the head's launch (one
-    workgroup per CU on a block of head rows; 999 columns leave a short last
-    block). Three steps with the penalised logits requested; tokens, hidden
-    states, histories and every penalised logit against the oracle."""
+    workgroup per CU on a block of head rows; 999 and 8193 columns leave a
+    short last block, 1 to 33 columns give blocks of one row; d from 64, one
+    value per thread, to 4096, eight). Three steps with the penalised logits
+    requested; tokens, hidden states, histories and every penalised logit
+    against the oracle."""
     import torch
     m, n_layers, stride, steps = 1, 2, 16, 3
     log(f"greedy one sequence d={d} f={f} vocab={vocab}")
