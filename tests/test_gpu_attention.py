@@ -153,3 +153,30 @@ def test_decode_step_persistent_short_chunks(bl, olib):
     rows and one holding only the new position; at 17 and 47 two and three
     chunks of 16, merged by the head's first workgroup."""
     _run_steps(bl, olib, 2, 1, 256, 1024, 32, 64, [15, 16, 17, 47], seed=15, prefill=15)
+
+
+def _random_attention_cases(n):
+    """Seeded (m, d, heads, max_seq, pos) with hd = d / heads from 4 to 128."""
+    g = np.random.default_rng(31337)
+    cases = []
+    while len(cases) < n:
+        heads = int(g.choice([2, 4, 8, 16, 32, 64]))
+        hd = int(g.choice([4, 8, 16, 32, 64, 80, 128]))
+        d = heads * hd
+        if d % 64 or d > 2560 or heads > 256:
+            continue
+        m = int(g.choice([1, 1, 1, 2, 3]))
+        max_seq = int(g.integers(2, 2048))
+        pos = int(g.integers(0, max_seq))
+        cases.append((m, d, heads, max_seq, pos))
+    return cases
+
+
+@pytest.mark.parametrize("m,d,heads,max_seq,pos", _random_attention_cases(10))
+def test_decode_step_random_shapes(bl, olib, m, d, heads, max_seq, pos):
+    """One decode step at a random position over a prefilled cache, for seeded
+    head counts, head sizes (4 .. 128), sequence counts and cache lengths: the
+    persistent kernel's chunking (one chunk, shorter chunks over a head's
+    workgroups, 256-position chunks) at one sequence, the launch-per-step path
+    at several."""
+    _run_steps(bl, olib, 1, m, d, 4 * d, heads, max_seq, [pos], seed=200 + pos, prefill=pos)
