@@ -155,6 +155,45 @@ def test_decode_step_persistent_short_chunks(bl, olib):
     _run_steps(bl, olib, 2, 1, 256, 1024, 32, 64, [15, 16, 17, 47], seed=15, prefill=15)
 
 
+def test_decode_step_long_run_repeatable(bl, olib):
+    """200 consecutive steps (positions 700 .. 899 over a prefilled cache of
+    1024) of two layers of the 3B shape on one sequence, the persistent kernel,
+    run twice from the same caches and input: the hidden states of every step
+    and the caches at the end agree bit for bit between the two runs (the
+    attention hand-overs leave no trace of timing in the results), and the
+    status word stays clear. Each step's values against the oracle are the
+    business of the tests above."""
+    import torch
+    n_layers, m, d, f, heads, max_seq, first, steps = 2, 1, 2560, 10240, 32, 1024, 700, 200
+    hd = d // heads
+    log(f"decode step long run d={d} heads={heads} positions {first}..{first + steps - 1}")
+    _, dw = make_layers(W.W_STREAM, n_layers, d, f, m, olib)
+    g = W.rng(150, 16, 0)
+    x0 = W.activations(g, m, d)
+    kc_h = np.zeros((n_layers, m, heads, max_seq, hd), np.float32)
+    vc_h = np.zeros_like(kc_h)
+    kc_h[:, :, :, :first] = g.standard_normal((n_layers, m, heads, first, hd)).astype(np.float32)
+    vc_h[:, :, :, :first] = g.standard_normal((n_layers, m, heads, first, hd)).astype(np.float32)
+    c, s = bl.bitnet_rope_table(10000.0, hd, max_seq)
+    cd, sd = to_dev(c), to_dev(s)
+    dev = torch_dev()
+    runs = []
+    for run in range(2):
+        kc, vc, x = to_dev(kc_h), to_dev(vc_h), to_dev(x0)
+        ws = torch.zeros(bl.bitnet_decode_step_workspace_bytes(m, d, f, heads, max_seq), dtype=torch.uint8,
+                         device=dev)
+        seq = torch.empty((steps, d), dtype=torch.float32, device=dev)
+        for i in range(steps):
+            bl.bitnet_decode_step(dw["weights"], dw["scales"], dw["gains"], n_layers, m, d, f, heads, 1e-5, cd, sd,
+                                  first + i, kc, vc, x, None, None, ws)
+            seq[i] = x[0]
+        assert stream_ctrl(ws)[1] == 0, f"stream status word, run {run}"
+        runs.append((to_host(seq), to_host(kc), to_host(vc)))
+    for name, a, b in zip(("hidden states", "k cache", "v cache"), runs[0], runs[1]):
+        assert_exact(a.view(np.uint32), b.view(np.uint32), f"{name} of the two runs")
+    assert np.all(np.isfinite(runs[0][0]))
+
+
 def _random_attention_cases(n):
     """Seeded (m, d, heads, max_seq, pos) with hd = d / heads from 4 to 128."""
     g = np.random.default_rng(31337)

@@ -522,3 +522,39 @@ def test_decode_stream_repeated_calls(bl, olib, d, f):
         assert_f32(gx, x, f"x after call {call}")
         x = gx
     assert epoch == 3 * 4 * n_layers, "one-token calls of these shapes run the persistent kernel"
+
+
+def test_decode_stream_long_run_repeatable(bl, olib):
+    """400 consecutive tokens through one workspace on the full grid of the
+    persistent kernel (2 layers of the 3B shape), run twice from the same input:
+    the two runs' sequences of hidden states agree bit for bit (no hand-over
+    leaves a trace of timing in the results), the status word stays clear, and
+    sampled calls match the oracle on their own input."""
+    import torch
+    from gpu_helpers import make_layers, new_stream_workspace, stream_ctrl
+    n_layers, d, f, calls, checked = 2, 2560, 10240, 400, (0, 199, 399)
+    log(f"stream long run layers={n_layers} d={d} f={f} calls={calls}")
+    layers, dev = make_layers(W.W_STREAM, n_layers, d, f, 1, olib)
+    x0 = W.activations(W.rng(W.W_STREAM, 996, W.T_X), 1, d)
+    qkv = torch.empty((n_layers, 1, 3 * d), dtype=torch.float32, device=torch_dev())
+    runs = []
+    for run in range(2):
+        ws = new_stream_workspace(1, d, f)
+        x = to_dev(x0)
+        seq = torch.empty((calls, d), dtype=torch.float32, device=torch_dev())
+        inputs = {}
+        for c in range(calls):
+            if c in checked:
+                inputs[c] = to_host(x)
+            bl.bitnet_decode_stream(dev["weights"], dev["scales"], dev["gains"], dev["z"], n_layers, 1, d, f, 1e-5,
+                                    x, qkv, ws)
+            seq[c] = x[0]
+        epoch, status = stream_ctrl(ws)
+        assert status == 0, f"stream status word, run {run}"
+        assert epoch == calls * 4 * n_layers
+        out = to_host(seq)
+        for c in checked:
+            want, _ = oracle.chain(inputs[c], layers, 1e-5, olib)
+            assert_f32(out[c:c + 1], want, f"run {run} call {c}")
+        runs.append(out)
+    assert_exact(runs[0].view(np.uint32), runs[1].view(np.uint32), "hidden states of the two runs")
