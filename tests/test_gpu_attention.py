@@ -129,6 +129,23 @@ def test_decode_step_persistent_long_context(bl, olib):
     _run_steps(bl, olib, 2, 1, 256, 1024, 2, 1024, [700, 701, 702, 1023, 0], seed=11, prefill=700)
 
 
+@pytest.mark.parametrize("d,f,heads", [(2560, 10240, 32), (256, 1024, 2)])
+def test_decode_step_persistent_longest_cache(bl, olib, d, f, heads):
+    """One sequence with the persistent kernel's largest cache, 8192 positions,
+    at positions 8190 and 8191 over a prefilled cache: the full 32 chunks of 256,
+    four per workgroup of a head at the 3B shape (32 heads of 80), one per
+    workgroup for 32 of the 128 workgroups of a head of 128 values."""
+    _run_steps(bl, olib, 2, 1, d, f, heads, 8192, [8190, 8191], seed=17, prefill=8190)
+
+
+@pytest.mark.parametrize("m", [1, 3])
+def test_decode_step_largest_head(bl, olib, m):
+    """Heads of 256 values, the largest accepted (d = 512, 2 heads), at positions
+    300 and 301 over a prefilled cache: one sequence in the persistent kernel
+    (19 chunks of 16 positions), three through the launch-per-step kernels."""
+    _run_steps(bl, olib, 2, m, 512, 1024, 2, 600, [300, 301], seed=18, prefill=300)
+
+
 def test_decode_step_one_sequence_long_cache_launch_path(bl, olib):
     """One sequence with a cache of 8448 positions, beyond the persistent
     kernel's 8192: the launch-per-step path at m = 1, positions 8200 and 8447
