@@ -564,7 +564,7 @@ __global__ __launch_bounds__(512) void fwd_gateup_block_kernel(
     float* __restrict__ h, int8_t* __restrict__ q_out, float* __restrict__ scale_out, int32_t* __restrict__ sum_out,
     int32_t* __restrict__ acc_gate, int32_t* __restrict__ acc_up, int rpb)
 {
-    constexpr int L = 8, R = 64 / L;   // 8 lanes per row, 8 rows per wave at a time
+    constexpr int L = 8;               // 8 lanes per row, 8 rows per wave at a time
     constexpr int CPL = NPT;           // chunks per lane: d <= 512 NPT, 8 NPT chunks over 8 lanes
     static_assert(CPL <= kMaxChunksPerLane, "row size");
     __shared__ __attribute__((aligned(16))) int8_t qs[512 * NPT];
