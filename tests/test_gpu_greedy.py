@@ -109,12 +109,15 @@ def _step_inputs(bl, olib, d, f, n_layers, vocab, m, seed):
 
 @pytest.mark.parametrize("m,d,f,n_layers,vocab,stride,steps", [(1, 256, 1024, 2, 3000, 8, 4),
                                                                 (4, 256, 1024, 2, 3000, 3, 4),
-                                                                (12, 256, 1024, 2, 1500, 16, 3)])
+                                                                (12, 256, 1024, 2, 1500, 16, 3),
+                                                                (1, 2560, 10240, 2, 50000, 64, 12)])
 def test_greedy_step_loop(bl, olib, m, d, f, n_layers, vocab, stride, steps):
     """Several greedy steps on the device with no host round trip in between,
     against the oracle's greedy_step applied as often (the chosen tokens, the
     histories and the final hidden states of every step). A history of 3 slots
-    fills up and then stays as it is."""
+    fills up and then stays as it is. The last case runs twelve tokens of two
+    3B-shape layers and the 50000-token head: the persistent stream and the
+    block form of the LM head with the penalty."""
     import torch
     log(f"greedy step loop m={m} d={d} f={f} layers={n_layers} vocab={vocab} steps={steps}")
     inp = _step_inputs(bl, olib, d, f, n_layers, vocab, m, seed=m)
