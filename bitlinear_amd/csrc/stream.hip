@@ -250,11 +250,19 @@ __device__ __forceinline__ void load_strided(const float* src, float* out)
         if (t + kT * i >= N) out[i] = 0.0f;
 }
 
-__device__ __forceinline__ int quant_one(float y, float scale)
+// The code rne(fl32(y * scale)) from one more fp32 add: the rounded product
+// plus 1.5 * 2^23 lands in [2^23, 2^24), where consecutive floats are one
+// apart, so the add rounds it to an integer, to nearest even as rintf does; the
+// bit pattern is then 0x4B400000 + code, whose low byte is the code's int8 byte.
+// With scale = 127 / max(absmax, 1e-5) no |y * scale| exceeds 127 (1 + 2^-23),
+// so the quantizer's clamp to [-128, 127] never acts and is left out. (The
+// library builds with -ffp-contract=off: the product is rounded on its own.)
+__device__ __forceinline__ uint32_t quant_bits(float y, float scale)
 {
-    const float r = rintf(y * scale);
-    return (int)fminf(fmaxf(r, -128.0f), 127.0f);
+    const float p = y * scale;
+    return __float_as_uint(p + 12582912.0f);
 }
+constexpr uint32_t kQuantBias = 0x4B400000u;  // bit pattern of 1.5 * 2^23
 
 // Byte position of activation k in LDS: within each 64 values, the 16 bytes at
 // 16 j hold k = 16 g + 4 i + j at byte 4 g + i (the order of the B operand
@@ -326,9 +334,9 @@ __device__ void norm_quant(const float* v, const float* g, float eps, Shared& sh
     for (int i = 0; i < NI; ++i) {
         const int k = t + kT * i;
         if (k < N) {
-            const int qv = quant_one(y[i], scale);
-            sum += qv;
-            sh.q[q_pos(k)] = (uint8_t)(qv & 0xff);
+            const uint32_t qb = quant_bits(y[i], scale);
+            sum += (int)(qb - kQuantBias);
+            sh.q[q_pos(k)] = (uint8_t)qb;
         }
     }
     sum = wave_sum(sum);
