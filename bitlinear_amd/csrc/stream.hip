@@ -798,6 +798,18 @@ __device__ bool attention_split(const StreamArgs& a, int l, int h, int split, in
     return true;
 }
 
+// With ON, keeps v computed where this stands: an empty asm that claims to
+// read and write it, so the compiler does not sink the computation (a
+// correctly rounded division) into an epilogue behind the next barrier, where
+// it would sit on the path to the published words; placed before the dot
+// products, it overlaps them. The form with attention, whose registers are at
+// the limit, came out slower with it and leaves it off.
+template <bool ON, class T>
+__device__ __forceinline__ void pin(T& v)
+{
+    if constexpr (ON) asm volatile("" : "+v"(v));
+}
+
 template <int D, int F, bool ATTN>
 __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
 {
@@ -911,11 +923,14 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
                 return;
             }
             norm_quant<D>(v, g1, a.eps, sh, s_a, qsum);
+            const int mat1 = (r1 + t) / D;
+            float inv = 1.0f / (s_a * (mat1 == 0 ? sw[0] : (mat1 == 1 ? sw[1] : sw[2])));
+            pin<!ATTN>(inv);
+            pin<!ATTN>(qsum);
             dots<S1>(w1, sh.q, sh.zero, sh.acc);
             __syncthreads();
             if (e1) {
-                const int row = r1 + t, mat = row / D;
-                const float inv = 1.0f / (s_a * (mat == 0 ? sw[0] : (mat == 1 ? sw[1] : sw[2])));
+                const int row = r1 + t;
                 const float val = (float)(sh.acc[t] - qsum) * inv;
                 qkv[row] = val;
                 if constexpr (ATTN) {
@@ -958,10 +973,12 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
                 norm_quant<D>(ov, g2, a.eps, sh, s_a, qsum);
             else
                 norm_quant<D>(zv, g2, a.eps, sh, s_a, qsum);
+            float inv = 1.0f / (s_a * sw[3]);
+            pin<!ATTN>(inv);
+            pin<!ATTN>(qsum);
             dots<S2>(w2, sh.q, sh.zero, sh.acc);
             __syncthreads();
             if (e2) {
-                const float inv = 1.0f / (s_a * sw[3]);
                 xres = xres + (float)(sh.acc[t] - qsum) * inv;
                 val_store(xb_cur + r2 + t, xres);
                 val_clear(xb_old + r2 + t);
@@ -979,11 +996,15 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
             pf4(l);
             if (l + 1 < a.n_layers) pf1o(l + 1);
             norm_quant<D>(v, g3, a.eps, sh, s_a, qsum);
+            float inv_g = 1.0f / (s_a * sw[4]), inv_u = 1.0f / (s_a * sw[5]);
+            pin<!ATTN>(inv_g);
+            pin<!ATTN>(inv_u);
+            pin<!ATTN>(qsum);
             dots<S3>(w3, sh.q, sh.zero, sh.acc);
             __syncthreads();
             if (e3) {
-                const float gate = (float)(sh.acc[t] - qsum) * (1.0f / (s_a * sw[4]));
-                const float up = (float)(sh.acc[S3::R + t] - qsum) * (1.0f / (s_a * sw[5]));
+                const float gate = (float)(sh.acc[t] - qsum) * inv_g;
+                const float up = (float)(sh.acc[S3::R + t] - qsum) * inv_u;
                 const float gp = gate > 0.0f ? gate : 0.0f;
                 const float g2v = gp * gp;
                 val_store(hh_cur + r3 + t, g2v * up);
@@ -998,10 +1019,12 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
             if (!poll_val<F>(hh_cur, v, a.ctrl)) return;
             if (l + 1 < a.n_layers) pf1q(l + 1);
             norm_quant<F>(v, g4, a.eps, sh, s_a, qsum);
+            float inv = 1.0f / (s_a * sw[6]);
+            pin<!ATTN>(inv);
+            pin<!ATTN>(qsum);
             dots<S4>(w4, sh.q, sh.zero, sh.acc);
             __syncthreads();
             if (e2) {
-                const float inv = 1.0f / (s_a * sw[6]);
                 xres = xres + (float)(sh.acc[t] - qsum) * inv;
                 val_store(xa_out + r2 + t, xres);
                 val_clear(xa_in + r2 + t);
