@@ -169,12 +169,38 @@ __device__ __forceinline__ uint32_t status_load(const uint32_t* ctrl)
     return __hip_atomic_load(ctrl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Workgroup barrier for LDS: this wave's LDS accesses complete, then
+// s_barrier; global loads in flight stay in flight.
+__device__ __forceinline__ void lds_sync()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unconstrained
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Workgroup-wide OR of failed with one barrier: lane 0 of each wave stores its
+// wave's ballot in its own word of vote[kT / 64], and every thread reads all
+// of them after the barrier. The words are written again only at the next
+// wait, which lies behind further barriers (the norm + quant's), so no thread
+// can read a later vote.
+__device__ __forceinline__ bool block_any(bool failed, uint32_t* vote)
+{
+    const uint32_t wv = __ballot(failed) != 0ull ? 1u : 0u;
+    if ((threadIdx.x & 63) == 0) vote[threadIdx.x >> 6] = wv;
+    lds_sync();
+    uint32_t any = 0u;
+#pragma unroll
+    for (int i = 0; i < kT / 64; ++i) any |= vote[i];
+    return any != 0u;
+}
+
 // Loads the words k = t, t + 512, ... < N of buf until every one carries epoch
 // e (all loads of a round are issued before any is checked); v receives the
 // fp32 payloads. Returns false, for the whole workgroup, on a timeout (2 s from
 // the start of this wait) or when another workgroup gave up.
 template <int N, int STRIDE = 1>
-__device__ bool poll_vec(const unsigned long long* buf, uint32_t e, float* v, uint32_t* ctrl)
+__device__ bool poll_vec(const unsigned long long* buf, uint32_t e, float* v, uint32_t* ctrl, uint32_t* vote)
 {
     constexpr int NI = cdiv(N, kT);
     const int t = threadIdx.x;
@@ -199,7 +225,7 @@ __device__ bool poll_vec(const unsigned long long* buf, uint32_t e, float* v, ui
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i) v[i] = (t + kT * i < N) ? __uint_as_float((uint32_t)w[i]) : 0.0f;
-    if (__syncthreads_or(failed ? 1 : 0)) {
+    if (block_any(failed, vote)) {
         if (t == 0) __hip_atomic_fetch_or(ctrl + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return false;
     }
@@ -208,7 +234,7 @@ __device__ bool poll_vec(const unsigned long long* buf, uint32_t e, float* v, ui
 
 // As poll_vec for a published fp32 vector: repeats until no word reads 0.
 template <int N>
-__device__ bool poll_val(const uint32_t* buf, float* v, uint32_t* ctrl)
+__device__ bool poll_val(const uint32_t* buf, float* v, uint32_t* ctrl, uint32_t* vote)
 {
     constexpr int NI = cdiv(N, kT);
     const int t = threadIdx.x;
@@ -232,7 +258,7 @@ __device__ bool poll_val(const uint32_t* buf, float* v, uint32_t* ctrl)
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i) v[i] = (t + kT * i < N) ? __uint_as_float(w[i]) : 0.0f;
-    if (__syncthreads_or(failed ? 1 : 0)) {
+    if (block_any(failed, vote)) {
         if (t == 0) __hip_atomic_fetch_or(ctrl + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return false;
     }
@@ -280,6 +306,7 @@ struct Shared {
     int red_i[kT / 64];
     int acc[128];  // per-row accumulators of a step (gate rows, then up rows)
     uint32_t trash[64];  // written by the L2 prefetch loads, never read
+    uint32_t vote[kT / 64];  // per-wave failure votes of a wait
 };
 
 // Every 128-byte line of [p, p + BYTES), one per thread. BYTES is a multiple
@@ -480,16 +507,6 @@ struct AttnShared {
     uint32_t vote;  // the epoch of a phase whose q/k/v wait failed (0 at kernel start)
 };
 struct NoAttnShared {};
-
-// Workgroup barrier for LDS: this wave's LDS accesses complete, then
-// s_barrier; global loads in flight stay in flight.
-__device__ __forceinline__ void lds_sync()
-{
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unconstrained
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
 
 __device__ __forceinline__ float block_max_f(float v, float* red)
 {
@@ -919,7 +936,7 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
             float v[ND];
             if (l == 0) {
                 load_strided<D>(a.x, v);
-            } else if (!poll_val<D>(xa_in, v, a.ctrl)) {
+            } else if (!poll_val<D>(xa_in, v, a.ctrl, sh.vote)) {
                 return;
             }
             norm_quant<D>(v, g1, a.eps, sh, s_a, qsum);
@@ -960,10 +977,10 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
                 // the attention output of every head (each head's inputs came
                 // from P1 rows of many workgroups, so every workgroup has
                 // published P1, and read the base, by now)
-                if (!poll_val<D>(ao_cur, ov, a.ctrl)) return;
+                if (!poll_val<D>(ao_cur, ov, a.ctrl, sh.vote)) return;
             } else {
                 float fl[1];
-                if (!poll_vec<kGrid, kFlagStride>(a.done, E + 1, fl, a.ctrl)) return;
+                if (!poll_vec<kGrid, kFlagStride>(a.done, E + 1, fl, a.ctrl, sh.vote)) return;
             }
             pf3(l);
             if (l == 0 && w == 0 && t == 0)  // every workgroup has read the base by now
@@ -992,7 +1009,7 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
             }
             fetch3(l);
             float v[ND];
-            if (!poll_val<D>(xb_cur, v, a.ctrl)) return;
+            if (!poll_val<D>(xb_cur, v, a.ctrl, sh.vote)) return;
             pf4(l);
             if (l + 1 < a.n_layers) pf1o(l + 1);
             norm_quant<D>(v, g3, a.eps, sh, s_a, qsum);
@@ -1016,7 +1033,7 @@ __global__ __launch_bounds__(kT) void stream_kernel(StreamArgs a)
             if (t < S4::R) sh.acc[t] = 0;
             fetch4(l);
             float v[NF];
-            if (!poll_val<F>(hh_cur, v, a.ctrl)) return;
+            if (!poll_val<F>(hh_cur, v, a.ctrl, sh.vote)) return;
             if (l + 1 < a.n_layers) pf1q(l + 1);
             norm_quant<F>(v, g4, a.eps, sh, s_a, qsum);
             float inv = 1.0f / (s_a * sw[6]);
