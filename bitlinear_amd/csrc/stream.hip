@@ -505,6 +505,7 @@ struct AttnShared {
     float red[kT / 64];
     float chunk[kMaxAttnChunks][kMaxHd + 2];  // per chunk: max, sum, weighted sums
     uint32_t vote;  // the epoch of a phase whose q/k/v wait failed (0 at kernel start)
+    uint32_t merge_vote[2][kT / 64];  // per-wave flags of the merge wait's rounds, by round parity
 };
 struct NoAttnShared {};
 
@@ -763,7 +764,6 @@ __device__ bool attention_split(const StreamArgs& a, int l, int h, int split, in
         const int nw = others * (hd + 2);
         constexpr int kMW = 4;
         const long long t0 = (long long)__builtin_amdgcn_s_memrealtime();
-        bool bad = false;
         for (int spin = 0;; ++spin) {
             bool ready = true;
             for (int u0 = 0; u0 < nw; u0 += kT * kMW) {
@@ -788,12 +788,22 @@ __device__ bool attention_split(const StreamArgs& a, int l, int h, int split, in
                     }
                 }
             }
-            if (__syncthreads_and(ready ? 1 : 0)) break;
-            if ((spin & 15) == 15 && (status_load(a.ctrl) != 0 ||
-                                      (long long)__builtin_amdgcn_s_memrealtime() - t0 > kTimeoutTicks)) {
-                bad = true;
-            }
-            if (__syncthreads_or(bad ? 1 : 0)) {
+            // one vote per round, bit 0: a word not yet written, bit 1: gave up.
+            // Lane 0 of each wave stores its wave's flags in this round's words
+            // (alternating by round: a wave writes a round's words again only
+            // after the next round's barrier, which every wave reaches after
+            // reading them); all ready ends the wait even if a thread gave up.
+            const bool gave_up = (spin & 15) == 15 && (status_load(a.ctrl) != 0 ||
+                                 (long long)__builtin_amdgcn_s_memrealtime() - t0 > kTimeoutTicks);
+            uint32_t* words = s.merge_vote[spin & 1];
+            const uint32_t wf = (__ballot(!ready) != 0ull ? 1u : 0u) | (__ballot(gave_up) != 0ull ? 2u : 0u);
+            if ((t & 63) == 0) words[t >> 6] = wf;
+            lds_sync();
+            uint32_t any = 0u;
+#pragma unroll
+            for (int i = 0; i < kT / 64; ++i) any |= words[i];
+            if (!(any & 1u)) break;
+            if (any & 2u) {
                 if (t == 0) __hip_atomic_fetch_or(a.ctrl + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 return false;
             }
